@@ -1,0 +1,435 @@
+"""fp64 CPU oracle for the NAtS-L hybrid attention layer (forward and decode step).
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import this module:
+only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg use it.
+It shares no code with the HIP library and imports nothing from it.
+
+Pages cited (all from gist.science):
+  [NL]  "Technische Samenvatting: Neural Attention Search Linear (NAtS-L)"
+        (Dutch summary of arXiv 2602.03681)
+  [DE]  "Neural Attention Search Linear: Towards Adaptive Token-Level Hybrid
+        Attention Models" (German explainer of the same paper; its
+        "Technisches Resümee" repeats [NL])
+  [SA]  "Technische Samenvatting: Een Systematische Analyse van Hybride
+        Lineaire Aandacht" (Dutch summary of arXiv 2507.06457)
+
+What the layer computes (plain definitions, no chunkwise algebra):
+  * route:   the sequence is cut into chunks of C = 64 tokens ([DE] "Die
+             Chunking-Strategie"); each chunk is mean-pooled and passed through
+             a linear layer that yields one score per operation type; the
+             highest score picks the operation ([NL] Kernmechanismen 1).
+  * softmax: plain causal softmax attention whose key set is the tokens of
+             earlier softmax-routed chunks plus the causal prefix of the
+             query's own chunk ([NL] Kernmechanismen 3: both correlations are
+             computed inside every chunk; only the selected operation's KV is
+             kept).
+  * GDN:     the gated delta rule run token by token; at the end of every
+             chunk the state is kept if the chunk was routed to the linear
+             operation and restored to its chunk-start value otherwise
+             ([NL] Kernmechanismen 3, "pseudo-update" then reset/rollback).
+             Gated DeltaNet itself is only named on the pages; the recurrence
+             used is the published gated delta rule, gating plus a delta rule
+             that erases stale content ([SA] Methodologie, generation 3, and
+             Belangrijkste Resultaten 3, "Gecontroleerd Vergeten").
+  * merge:   each branch output is RMS-normalised and the two are summed with
+             weights produced from Q ([NL] Kernmechanismen 4).
+
+Readings where the pages are silent (each is also listed in the design doc):
+  route column 0 = softmax, column 1 = linear; an exact tie goes to softmax;
+  the router pools the layer input x; the decay alpha and write strength beta
+  are per (b, h, t) scalars; S is key-major [Dk, Dv]; o_t = S_t^T q_t with no
+  extra scale; the softmax scale defaults to 1/sqrt(Dk); RMSNorm has eps
+  inside the square root and no mean subtraction; mixing weights are
+  softmax(q_t . W_mix) with column 0 weighting the softmax branch.
+
+Every function works in float64 on whatever values it is handed; callers pass
+the exact (already bf16-rounded where applicable) values the GPU receives.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+SM = 0   # route id of the softmax operation
+LIN = 1  # route id of the Gated DeltaNet operation
+CHUNK = 64  # [DE] "Die Chunking-Strategie": a stack of 64 notes is one chunk
+
+
+def _f64(a):
+    return None if a is None else np.asarray(a, dtype=np.float64)
+
+
+def group_of_head(h: int, H: int, G: int) -> int:
+    """Route group used by head h.  G = 1 shares one route per chunk across
+    all heads; G = H routes every head on its own."""
+    return h // (H // G)
+
+
+# ---------------------------------------------------------------------------
+# Router  ([NL] Kernmechanismen 1; [DE] Chunking-Strategie / Verkehrspolizist)
+# ---------------------------------------------------------------------------
+def route_scores(x, w_score, b_score=None, chunk=CHUNK, groups=1):
+    """Attention Score Layer: mean-pool every chunk of x, apply a linear layer.
+
+    x        [B, L, d]      layer input (only complete chunks are scored)
+    w_score  [d, 2*groups]  columns (2g, 2g+1) = (softmax, linear) of group g
+    b_score  [2*groups] or None
+    returns  scores [B, groups, Nc, 2]
+    """
+    x = _f64(x)
+    w = _f64(w_score)
+    B, L, d = x.shape
+    nc = L // chunk
+    pooled = x[:, : nc * chunk].reshape(B, nc, chunk, d).mean(axis=2)  # [B,Nc,d]
+    s = pooled @ w  # [B, Nc, 2G]
+    if b_score is not None:
+        s = s + _f64(b_score)
+    return s.reshape(B, nc, groups, 2).transpose(0, 2, 1, 3).copy()
+
+
+def route_from_scores(scores):
+    """The operation with the highest score wins; an exact tie goes to the
+    softmax operation (column 0), the first-maximum rule of argmax."""
+    return np.where(scores[..., SM] >= scores[..., LIN], SM, LIN).astype(np.int32)
+
+
+def route(x, w_score, b_score=None, chunk=CHUNK, groups=1):
+    """Returns (route [B,G,Nc] int32, margin [B,G,Nc] = s_softmax - s_linear)."""
+    s = route_scores(x, w_score, b_score, chunk, groups)
+    return route_from_scores(s), s[..., SM] - s[..., LIN]
+
+
+def compact(route_bgc):
+    """Index list of softmax-routed chunks, the prefill form of the softmax
+    branch's retained KV ([NL] Kernmechanismen 3: only the selected
+    operation's KV values are kept).
+
+    returns sel_idx [B,G,Nc] (ascending SM chunk ids, padded with -1) and
+            nsel_before [B,G,Nc+1] (number of SM chunks before chunk c)."""
+    r = np.asarray(route_bgc)
+    B, G, nc = r.shape
+    sel = np.full((B, G, nc), -1, dtype=np.int32)
+    nsb = np.zeros((B, G, nc + 1), dtype=np.int32)
+    for b in range(B):
+        for g in range(G):
+            ids = [c for c in range(nc) if r[b, g, c] == SM]
+            sel[b, g, : len(ids)] = ids
+            cnt = 0
+            for c in range(nc):
+                nsb[b, g, c] = cnt
+                cnt += int(r[b, g, c] == SM)
+            nsb[b, g, nc] = cnt
+    return sel, nsb
+
+
+# ---------------------------------------------------------------------------
+# Softmax branch  ([NL] Kernmechanismen 3)
+# ---------------------------------------------------------------------------
+def key_mask(route_c, L, chunk=CHUNK):
+    """Boolean [L, L] mask M[t, s]: key s is visible to query t iff s <= t and
+    (s is in t's own chunk, or s's chunk was routed to softmax).  route_c has
+    one entry per chunk (a trailing partial chunk needs none: its own route
+    never affects its outputs)."""
+    t = np.arange(L)[:, None]
+    s = np.arange(L)[None, :]
+    cs, ct = s // chunk, t // chunk
+    rc = np.asarray(route_c)
+    rs = np.where(cs < len(rc), rc[np.minimum(cs, len(rc) - 1)], LIN)
+    return (s <= t) & ((cs == ct) | (rs == SM))
+
+
+def softmax_branch(q, k, v, route_bgc, scale=None, chunk=CHUNK, with_lse=False):
+    """Naive masked two-pass softmax attention, one 64-row query block at a
+    time (rows are independent, so blocking changes nothing).
+
+    q, k [B,H,L,Dk]; v [B,H,L,Dv]; route_bgc [B,G,Nc] -> o_sm [B,H,L,Dv]
+    (and the natural-log logsumexp [B,H,L] of the scaled scores if asked)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, L, Dk = q.shape
+    G = route_bgc.shape[1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(Dk)
+    o = np.zeros(v.shape[:3] + (v.shape[3],))
+    lse = np.zeros((B, H, L))
+    for b in range(B):
+        for g in range(G):
+            heads = [h for h in range(H) if group_of_head(h, H, G) == g]
+            mask = key_mask(route_bgc[b, g], L, chunk)
+            for t0 in range(0, L, chunk):
+                t1 = min(L, t0 + chunk)
+                m = mask[t0:t1, :t1]  # keys past the block end are never visible
+                z = scale * np.einsum("hqd,hkd->hqk", q[b, heads, t0:t1], k[b, heads, :t1])
+                z = np.where(m[None], z, -np.inf)
+                zmax = z.max(axis=-1, keepdims=True)
+                p = np.exp(z - zmax)
+                den = p.sum(axis=-1, keepdims=True)
+                o[b, heads, t0:t1] = np.einsum("hqk,hkd->hqd", p, v[b, heads, :t1]) / den
+                lse[b, heads, t0:t1] = (zmax + np.log(den))[..., 0]
+    return (o, lse) if with_lse else o
+
+
+def softmax_branch_bruteforce(q, k, v, route_bgc, scale=None, chunk=CHUNK):
+    """Brute-force twin: for every query, list its visible keys explicitly and
+    take a softmax over that list.  Tiny inputs only."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, L, Dk = q.shape
+    G = route_bgc.shape[1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(Dk)
+    o = np.zeros(v.shape)
+    for b in range(B):
+        for h in range(H):
+            r = route_bgc[b, group_of_head(h, H, G)]
+            for t in range(L):
+                keys = [s for s in range(t + 1)
+                        if s // chunk == t // chunk or r[s // chunk] == SM]
+                z = np.array([scale * float(q[b, h, t] @ k[b, h, s]) for s in keys])
+                p = np.exp(z - z.max())
+                p /= p.sum()
+                o[b, h, t] = sum(pi * v[b, h, s] for pi, s in zip(p, keys))
+    return o
+
+
+# ---------------------------------------------------------------------------
+# Gated DeltaNet branch  ([NL] Kernmechanismen 3; [SA] generation 3)
+# ---------------------------------------------------------------------------
+def gdn_token_update(S, k_t, v_t, a_t, b_t):
+    """One gated delta-rule step on key-major states S [..., Dk, Dv]:
+        S <- a_t * (S - b_t * k_t (k_t^T S)) + b_t * k_t v_t^T
+    (decay the state, erase what key k_t currently retrieves, write v_t)."""
+    kS = np.einsum("...k,...kv->...v", k_t, S)
+    a = np.asarray(a_t)[..., None, None]
+    b = np.asarray(b_t)[..., None, None]
+    return a * (S - b * k_t[..., :, None] * kS[..., None, :]) + b * k_t[..., :, None] * v_t[..., None, :]
+
+
+def gdn_readout(S, q_t):
+    """o_t = S_t^T q_t."""
+    return np.einsum("...kv,...k->...v", S, q_t)
+
+
+def gdn_branch(q, k, v, alpha, beta, route_bgc, S_init=None, chunk=CHUNK):
+    """Per-token gated delta rule with per-chunk rollback.
+
+    For every chunk the state starts from the carried state, is pseudo-updated
+    token by token (every token reads out after its own update), and at the
+    chunk's end is kept only if the chunk was routed to the linear operation.
+
+    q, k [B,H,L,Dk]; v [B,H,L,Dv]; alpha, beta [B,H,L]; route [B,G,Nc]
+    returns o_gdn [B,H,L,Dv], S_final [B,H,Dk,Dv] (the carried state)."""
+    q, k, v, alpha, beta = map(_f64, (q, k, v, alpha, beta))
+    B, H, L, Dk = q.shape
+    Dv = v.shape[3]
+    G = route_bgc.shape[1]
+    carry = np.zeros((B, H, Dk, Dv)) if S_init is None else _f64(S_init).copy()
+    gidx = np.array([group_of_head(h, H, G) for h in range(H)])
+    o = np.zeros((B, H, L, Dv))
+    for c0 in range(0, L, chunk):
+        c = c0 // chunk
+        S = carry.copy()
+        for t in range(c0, min(L, c0 + chunk)):
+            S = gdn_token_update(S, k[:, :, t], v[:, :, t], alpha[:, :, t], beta[:, :, t])
+            o[:, :, t] = gdn_readout(S, q[:, :, t])
+        if c0 + chunk <= L:  # only a complete chunk has a route and can commit
+            keep = route_bgc[:, gidx, c] == LIN  # [B, H]
+            carry = np.where(keep[:, :, None, None], S, carry)
+    return o, carry
+
+
+def gdn_branch_bruteforce(q, k, v, alpha, beta, route_bgc, S_init=None, chunk=CHUNK):
+    """Brute-force twin of gdn_branch: for every token t, rerun the recurrence
+    from S_init over exactly the tokens whose writes survive (all tokens of
+    linear-routed chunks before t's chunk, in order) followed by t's own chunk
+    up to t.  Tiny inputs only."""
+    q, k, v, alpha, beta = map(_f64, (q, k, v, alpha, beta))
+    B, H, L, Dk = q.shape
+    Dv = v.shape[3]
+    G = route_bgc.shape[1]
+    o = np.zeros((B, H, L, Dv))
+    for b in range(B):
+        for h in range(H):
+            r = route_bgc[b, group_of_head(h, H, G)]
+            S0 = np.zeros((Dk, Dv)) if S_init is None else _f64(S_init)[b, h]
+            for t in range(L):
+                ct = t // chunk
+                toks = [s for s in range(ct * chunk) if r[s // chunk] == LIN]
+                toks += list(range(ct * chunk, t + 1))
+                S = S0.copy()
+                for s in toks:
+                    S = gdn_token_update(S, k[b, h, s], v[b, h, s], alpha[b, h, s], beta[b, h, s])
+                o[b, h, t] = gdn_readout(S, q[b, h, t])
+    return o
+
+
+# ---------------------------------------------------------------------------
+# Output merging  ([NL] Kernmechanismen 4)
+# ---------------------------------------------------------------------------
+def rmsnorm(o, gain=None, eps=1e-6):
+    o = _f64(o)
+    n = o / np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + eps)
+    return n if gain is None else n * _f64(gain)
+
+
+def mix_weights(q, w_mix):
+    """softmax over the two logits q_t . W_mix[:, 0] (softmax) and
+    q_t . W_mix[:, 1] (linear).  w_mix is [Dk, 2] shared by all heads or
+    [H, Dk, 2] per head."""
+    q = _f64(q)
+    w = _f64(w_mix)
+    if w.ndim == 2:
+        z = q @ w
+    else:
+        z = np.einsum("bhtk,hkj->bhtj", q, w)
+    z = z - z.max(axis=-1, keepdims=True)
+    e = np.exp(z)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def merge(q, o_sm, o_gdn, w_mix, g_sm=None, g_lin=None, eps=1e-6):
+    """returns out, n_sm, n_lin, weights [.., 2]"""
+    n_sm = rmsnorm(o_sm, g_sm, eps)
+    n_lin = rmsnorm(o_gdn, g_lin, eps)
+    w = mix_weights(q, w_mix)
+    out = w[..., 0:1] * n_sm + w[..., 1:2] * n_lin
+    return out, n_sm, n_lin, w
+
+
+# ---------------------------------------------------------------------------
+# Whole layer forward
+# ---------------------------------------------------------------------------
+def forward(x, q, k, v, alpha, beta, w_score, w_mix, b_score=None, g_sm=None, g_lin=None,
+            route_override=None, S_init=None, scale=None, eps=1e-6, groups=1, chunk=CHUNK):
+    """Router -> softmax branch, GDN branch -> merge.  Returns a dict with
+    route, margin, o_sm, o_gdn, S_final, n_sm, n_lin, out."""
+    if route_override is None:
+        r, margin = route(x, w_score, b_score, chunk, groups)
+    else:
+        r, margin = np.asarray(route_override, dtype=np.int32), None
+    o_sm = softmax_branch(q, k, v, r, scale, chunk)
+    o_gdn, S_final = gdn_branch(q, k, v, alpha, beta, r, S_init, chunk)
+    out, n_sm, n_lin, w = merge(q, o_sm, o_gdn, w_mix, g_sm, g_lin, eps)
+    return dict(route=r, margin=margin, o_sm=o_sm, o_gdn=o_gdn, S_final=S_final,
+                n_sm=n_sm, n_lin=n_lin, weights=w, out=out)
+
+
+# ---------------------------------------------------------------------------
+# Decode  (the two hidden states of [NL] Kernmechanismen 3, kept online)
+# ---------------------------------------------------------------------------
+def empty_cache(B, H, D, d_model, cap, groups=1):
+    return dict(k=np.zeros((B, H, cap, D)), v=np.zeros((B, H, cap, D)),
+                n_committed=np.zeros((B, groups), np.int64), n_open=np.zeros((B, groups), np.int64),
+                S_carry=np.zeros((B, H, D, D)), S_work=np.zeros((B, H, D, D)),
+                x_sum=np.zeros((B, groups, d_model)), err=0)
+
+
+def build_cache(x, k, v, alpha, beta, w_score, b_score=None, cap=None, groups=1, S_init=None,
+                chunk=CHUNK):
+    """Decode cache after a prefix of n = x.shape[1] tokens (any n):
+       softmax-routed complete chunks keep their KV (compacted, in order),
+       the open (incomplete) chunk's tokens sit after them, S_carry is the
+       state after the committed linear chunks, S_work the open chunk's
+       pseudo-updated state, x_sum the open chunk's sum of x."""
+    x, k, v, alpha, beta = map(_f64, (x, k, v, alpha, beta))
+    B, n, d = x.shape
+    H, D = k.shape[1], k.shape[3]
+    G = groups
+    nc_full = n // chunk
+    r, _ = route(x[:, : nc_full * chunk], w_score, b_score, chunk, G) if nc_full else (
+        np.zeros((B, G, 0), np.int32), None)
+    if cap is None:
+        cap = n + chunk
+    cache = empty_cache(B, H, D, d, cap, G)
+    if S_init is not None:
+        cache["S_carry"][:] = _f64(S_init)
+    for b in range(B):
+        for g in range(G):
+            heads = [h for h in range(H) if group_of_head(h, H, G) == g]
+            pos = 0
+            for c in range(nc_full):
+                if r[b, g, c] == SM:
+                    sl = slice(c * chunk, (c + 1) * chunk)
+                    cache["k"][b, heads, pos:pos + chunk] = k[b, heads, sl]
+                    cache["v"][b, heads, pos:pos + chunk] = v[b, heads, sl]
+                    pos += chunk
+            n_open = n - nc_full * chunk
+            cache["k"][b, heads, pos:pos + n_open] = k[b, heads, nc_full * chunk:]
+            cache["v"][b, heads, pos:pos + n_open] = v[b, heads, nc_full * chunk:]
+            cache["n_committed"][b, g] = pos
+            cache["n_open"][b, g] = n_open
+            cache["x_sum"][b, g] = x[b, nc_full * chunk:].sum(axis=0)
+    # states: rerun the per-token rule with rollback over the prefix
+    carry = np.zeros((B, H, D, D)) if S_init is None else _f64(S_init).copy()
+    gidx = np.array([group_of_head(h, H, G) for h in range(H)])
+    for c in range(nc_full):
+        S = carry.copy()
+        for t in range(c * chunk, (c + 1) * chunk):
+            S = gdn_token_update(S, k[:, :, t], v[:, :, t], alpha[:, :, t], beta[:, :, t])
+        keep = r[:, gidx, c] == LIN
+        carry = np.where(keep[:, :, None, None], S, carry)
+    S = carry.copy()
+    for t in range(nc_full * chunk, n):
+        S = gdn_token_update(S, k[:, :, t], v[:, :, t], alpha[:, :, t], beta[:, :, t])
+    cache["S_carry"] = carry
+    cache["S_work"] = S if n > nc_full * chunk else np.zeros_like(S)
+    return cache
+
+
+def decode_step(cache, x, q, k, v, alpha, beta, w_score, w_mix, b_score=None, g_sm=None, g_lin=None,
+                scale=None, eps=1e-6, chunk=CHUNK):
+    """One new token per sequence against the decode cache.
+
+    x [B,d]; q, k, v [B,H,D]; alpha, beta [B,H].  Returns (out [B,H,D],
+    dict of branch values, new cache).  The new token joins the open chunk:
+    it attends to the committed softmax chunks, the open chunk's earlier
+    tokens and itself; the GDN state is pseudo-updated from S_carry (first
+    token of a chunk) or S_work.  When the chunk completes it is routed; a
+    softmax route commits its KV, a linear route commits its state."""
+    x, q, k, v, alpha, beta = map(_f64, (x, q, k, v, alpha, beta))
+    c = {key: (val.copy() if isinstance(val, np.ndarray) else val) for key, val in cache.items()}
+    B, H, D = q.shape
+    G = c["n_open"].shape[1]
+    cap = c["k"].shape[2]
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    o_sm = np.zeros((B, H, D))
+    o_gdn = np.zeros((B, H, D))
+    for b in range(B):
+        for h in range(H):
+            g = group_of_head(h, H, G)
+            nco, nop = int(c["n_committed"][b, g]), int(c["n_open"][b, g])
+            S_src = c["S_carry"][b, h] if nop == 0 else c["S_work"][b, h]
+            S_new = gdn_token_update(S_src, k[b, h], v[b, h], alpha[b, h], beta[b, h])
+            c["S_work"][b, h] = S_new
+            o_gdn[b, h] = gdn_readout(S_new, q[b, h])
+            n = nco + nop
+            keys = np.concatenate([c["k"][b, h, :n], k[b, h][None]], axis=0)
+            vals = np.concatenate([c["v"][b, h, :n], v[b, h][None]], axis=0)
+            z = scale * (keys @ q[b, h])
+            p = np.exp(z - z.max())
+            o_sm[b, h] = (p @ vals) / p.sum()
+            if n < cap:
+                c["k"][b, h, n] = k[b, h]
+                c["v"][b, h, n] = v[b, h]
+            else:
+                c["err"] = 1
+    out, n_sm, n_lin, w = merge(q[:, :, None], o_sm[:, :, None], o_gdn[:, :, None], w_mix,
+                                g_sm, g_lin, eps)
+    routes = np.full((B, G), -1, np.int32)
+    for b in range(B):
+        for g in range(G):
+            c["x_sum"][b, g] += x[b]
+            c["n_open"][b, g] += 1
+            if c["n_open"][b, g] == chunk:
+                s = (c["x_sum"][b, g] / chunk) @ _f64(w_score)[:, 2 * g:2 * g + 2]
+                if b_score is not None:
+                    s = s + _f64(b_score)[2 * g:2 * g + 2]
+                rt = SM if s[0] >= s[1] else LIN
+                routes[b, g] = rt
+                heads = [h for h in range(H) if group_of_head(h, H, G) == g]
+                if rt == SM:
+                    c["n_committed"][b, g] += chunk
+                else:
+                    c["S_carry"][b, heads] = c["S_work"][b, heads]
+                c["n_open"][b, g] = 0
+                c["x_sum"][b, g] = 0.0
+    return out[:, :, 0], dict(o_sm=o_sm, o_gdn=o_gdn, n_sm=n_sm[:, :, 0], n_lin=n_lin[:, :, 0],
+                              weights=w[:, :, 0], routes=routes), c
