@@ -1,0 +1,264 @@
+/*
+ * natsl.h -- C ABI of the NAtS-L hybrid attention layer for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The layer (gist.science, "Technische Samenvatting: Neural Attention Search
+ * Linear (NAtS-L)", section Kernmechanismen, items 1-4; the German
+ * "Technisches Resümee" of the same paper repeats it):
+ *   1. the sequence is split into chunks of 64 tokens ("Die Chunking-
+ *      Strategie" in the German explainer); an Attention Score Layer (mean-
+ *      pool of the chunk, then a linear layer) scores each chunk for the two
+ *      operation types and the highest score picks the chunk's operation:
+ *      softmax attention or Gated DeltaNet;
+ *   3. both operations are computed inside every chunk; at the chunk's end
+ *      only the selected operation keeps the chunk (softmax keeps its KV,
+ *      Gated DeltaNet keeps its state update; the other rolls back to the
+ *      chunk start);
+ *   4. both outputs are RMS-normalised and mixed with weights derived from Q.
+ *
+ * Conventions shared by every entry point:
+ *   - every tensor pointer is a DEVICE pointer owned by the caller; the
+ *     library never allocates, frees or synchronises device memory;
+ *   - scratch memory is a caller-provided workspace whose size comes from
+ *     natsl_workspace_size(); it must be 256-byte aligned;
+ *   - every call is asynchronous on the caller's stream (natsl_forward may
+ *     fork work onto one library-owned helper stream of default priority and
+ *     joins it back before returning; the join is an event wait, not a host
+ *     synchronisation);
+ *   - every call validates its arguments on the host BEFORE enqueueing any
+ *     work; on failure nothing is enqueued, a status != NATSL_OK is
+ *     returned and natsl_last_error() (thread-local) describes the problem;
+ *   - a failed HIP launch returns NATSL_ERR_DEVICE;
+ *   - results are bit-identical from run to run (no float atomics);
+ *   - tensors are dense row-major with the shapes given; io tensors (x, q, k,
+ *     v, out) hold the io dtype of natsl_dims, alpha/beta/weights are fp32;
+ *   - supported: Dk == Dv in {64, 128}, chunk == 64, L % 64 == 0, L >= 64,
+ *     route_groups G in {1, H}, d_model % 8 == 0.  B == 0 is a no-op that
+ *     succeeds after the dims check (tensor pointers may then be NULL).
+ *   - route ids: 0 = softmax attention, 1 = Gated DeltaNet (linear).
+ */
+#ifndef NATSL_H
+#define NATSL_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NATSL_OK = 0,
+  NATSL_ERR_INVALID_ARG = 1,  /* null pointer, bad size, inconsistent dims */
+  NATSL_ERR_UNSUPPORTED = 2,  /* valid but outside what v1 implements      */
+  NATSL_ERR_WORKSPACE = 3,    /* workspace missing, misaligned or too small */
+  NATSL_ERR_DEVICE = 4,       /* a HIP call or kernel launch failed         */
+  NATSL_ERR_CAPACITY = 5      /* host-visible capacity problem (decode)     */
+} natsl_status;
+
+typedef enum { NATSL_F32 = 0, NATSL_BF16 = 1 } natsl_dtype;
+
+enum { NATSL_ROUTE_SOFTMAX = 0, NATSL_ROUTE_LINEAR = 1 };
+
+/* entry ids for natsl_workspace_size */
+enum {
+  NATSL_ENTRY_ROUTE = 0,
+  NATSL_ENTRY_GDN_CHUNK = 1,
+  NATSL_ENTRY_SOFTMAX_MASKED = 2,
+  NATSL_ENTRY_MERGE = 3,
+  NATSL_ENTRY_FORWARD = 4,
+  NATSL_ENTRY_DECODE_STEP = 5
+};
+
+typedef struct {
+  int32_t B, H, L;        /* batch, heads, sequence length (decode: L unused) */
+  int32_t Dk, Dv;         /* head dims (Dk == Dv in v1)                        */
+  int32_t d_model;        /* width of the router input x                       */
+  int32_t chunk;          /* must be 64                                        */
+  int32_t route_groups;   /* G: 1 = one route per chunk shared by all heads,
+                             H = one route per head                            */
+  natsl_dtype io;         /* dtype of x, q, k, v, out (and the decode cache)   */
+  float sm_scale;         /* softmax scale; <= 0 selects 1/sqrt(Dk)            */
+  float rms_eps;          /* RMSNorm epsilon (added inside the sqrt); <= 0
+                             selects 1e-6                                      */
+} natsl_dims;
+
+/* Library version (major*10000 + minor*100 + patch). */
+int natsl_version(void);
+
+/* Description of the last failure on the calling thread ("" if none). */
+const char* natsl_last_error(void);
+
+/* Workspace bytes the given entry point needs for these dims (0 if none).
+ * Pure host computation. */
+natsl_status natsl_workspace_size(int entry, const natsl_dims* dims, size_t* bytes);
+
+/*
+ * Router (Kernmechanismen 1): for every (b, chunk c) pool x over the chunk's
+ * 64 tokens (mean), score it with W_score and b_score, and pick the op with
+ * the higher score (an exact tie picks softmax).  Then compact: list the
+ * softmax-routed chunks per (b, g) in ascending order (the prefill form of the
+ * retained softmax KV, Kernmechanismen 3).
+ *   x            [B, L, d_model] io dtype (may be NULL when route_in is given)
+ *   w_score      [d_model, 2G] fp32; columns (2g, 2g+1) = (softmax, linear)
+ *   b_score      [2G] fp32 or NULL (zero bias)
+ *   route_in     [B, G, Nc] int32 or NULL: forced routes (skips scoring)
+ *   route_out    [B, G, Nc] int32   (may alias route_in)
+ *   sel_idx      [B, G, Nc] int32   ascending softmax chunk ids, -1 padded
+ *   nsel_before  [B, G, Nc+1] int32 softmax chunks before chunk c (exclusive)
+ *   scores       [B, G, Nc, 2] fp32 or NULL
+ * Reduction order is fixed, so routes are deterministic.
+ */
+natsl_status natsl_route(const natsl_dims* dims, const void* x, const float* w_score,
+                         const float* b_score, const int32_t* route_in, int32_t* route_out,
+                         int32_t* sel_idx, int32_t* nsel_before, float* scores,
+                         hipStream_t stream);
+
+/*
+ * Gated DeltaNet branch with per-chunk rollback (Kernmechanismen 3): the
+ * gated delta rule S_t = a_t (S_{t-1} - b_t k_t (k_t^T S_{t-1})) + b_t k_t v_t^T,
+ * o_t = S_t^T q_t, pseudo-updated through every chunk; the state is carried
+ * past a chunk only when route == linear, otherwise it returns to the chunk
+ * start.  Computed chunkwise (UT transform per chunk, then a state scan).
+ *   q, k         [B, H, L, Dk] io dtype;  v [B, H, L, Dv] io dtype
+ *   alpha, beta  [B, H, L] fp32 (decay in (0, 1], write strength)
+ *   route        [B, G, Nc] int32
+ *   S_init       [B, H, Dk, Dv] fp32 key-major, or NULL (zero state)
+ *   o_gdn        [B, H, L, Dv] of o_dtype
+ *   S_final      [B, H, Dk, Dv] fp32 carried state after the last chunk, or NULL
+ *   ws           workspace of natsl_workspace_size(NATSL_ENTRY_GDN_CHUNK)
+ */
+natsl_status natsl_gdn_chunk(const natsl_dims* dims, const void* q, const void* k, const void* v,
+                             const float* alpha, const float* beta, const int32_t* route,
+                             const float* S_init, void* o_gdn, natsl_dtype o_dtype,
+                             float* S_final, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Softmax branch (Kernmechanismen 3): causal softmax attention in which a
+ * query of chunk c sees the tokens of the softmax-routed chunks before c plus
+ * the causal prefix of chunk c itself (whatever chunk c's own route is).
+ *   q, k [B, H, L, Dk], v [B, H, L, Dv] io dtype
+ *   sel_idx, nsel_before  as produced by natsl_route
+ *   o_sm [B, H, L, Dv] of o_dtype
+ *   lse  [B, H, L] fp32 natural-log logsumexp of the scaled scores, or NULL
+ * No workspace is needed (ws may be NULL, ws_bytes 0).
+ */
+natsl_status natsl_softmax_masked(const natsl_dims* dims, const void* q, const void* k,
+                                  const void* v, const int32_t* sel_idx,
+                                  const int32_t* nsel_before, void* o_sm, natsl_dtype o_dtype,
+                                  float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Output merging (Kernmechanismen 4): per (b, h, t)
+ *   n_x = o_x / sqrt(mean(o_x^2) + eps) * g_x      for x in {sm, lin}
+ *   (w_sm, w_lin) = softmax(q_t . W_mix[:, 0], q_t . W_mix[:, 1])
+ *   out = w_sm * n_sm + w_lin * n_lin
+ *   q [B, H, L, Dk] io dtype; o_sm, o_gdn [B, H, L, Dv] branch_dtype
+ *   w_mix [Dk, 2] fp32 (+ h * w_mix_head_stride floats for head h;
+ *         stride 0 = shared by all heads)
+ *   g_sm, g_lin [Dv] fp32 or NULL (ones);  out [B, H, L, Dv] io dtype
+ */
+natsl_status natsl_merge(const natsl_dims* dims, const void* q, const void* o_sm, const void* o_gdn,
+                         natsl_dtype branch_dtype, const float* w_mix, int64_t w_mix_head_stride,
+                         const float* g_sm, const float* g_lin, void* out, hipStream_t stream);
+
+typedef struct {
+  const void* x;               /* [B, L, d_model] io (NULL if route_override) */
+  const void* q;               /* [B, H, L, Dk] io                            */
+  const void* k;               /* [B, H, L, Dk] io                            */
+  const void* v;               /* [B, H, L, Dv] io                            */
+  const float* alpha;          /* [B, H, L]                                   */
+  const float* beta;           /* [B, H, L]                                   */
+  const float* w_score;        /* [d_model, 2G] (NULL if route_override)      */
+  const float* b_score;        /* [2G] or NULL                                */
+  const float* w_mix;          /* [Dk, 2] (+ head stride)                     */
+  int64_t w_mix_head_stride;   /* 0 = shared                                  */
+  const float* g_sm;           /* [Dv] or NULL                                */
+  const float* g_lin;          /* [Dv] or NULL                                */
+  const int32_t* route_override; /* [B, G, Nc] or NULL                        */
+  const float* S_init;         /* [B, H, Dk, Dv] or NULL                      */
+  natsl_dtype branch_dtype;    /* dtype of the intermediate branch outputs    */
+  int32_t* route_out;          /* [B, G, Nc] or NULL                          */
+  float* scores_out;           /* [B, G, Nc, 2] or NULL                       */
+  void* o_sm_dbg;              /* [B, H, L, Dv] branch_dtype or NULL: raw
+                                  softmax branch output                       */
+  void* o_gdn_dbg;             /* [B, H, L, Dv] branch_dtype or NULL: raw
+                                  Gated DeltaNet branch output                */
+  float* S_final;              /* [B, H, Dk, Dv] or NULL                      */
+  void* out;                   /* [B, H, L, Dv] io                            */
+} natsl_forward_args;
+
+/*
+ * Whole layer forward: route + compaction, Gated DeltaNet branch and softmax
+ * branch (run concurrently), merge.  ws from NATSL_ENTRY_FORWARD.
+ */
+natsl_status natsl_forward(const natsl_dims* dims, const natsl_forward_args* args, void* ws,
+                           size_t ws_bytes, hipStream_t stream);
+
+typedef struct {
+  void* k_cache;               /* [B, H, cap, Dk] io: compacted KV             */
+  void* v_cache;               /* [B, H, cap, Dv] io                           */
+  int32_t cap;                 /* rows per (b, h)                              */
+  int32_t* n_committed;        /* [B, G] rows of committed softmax chunks      */
+  int32_t* n_open;             /* [B] tokens of the open (incomplete) chunk    */
+  float* S_carry;              /* [B, H, Dk, Dv] state after committed chunks  */
+  float* S_work;               /* [B, H, Dk, Dv] open chunk's pseudo-updated   */
+  float* x_sum;                /* [B, d_model] sum of x over the open chunk    */
+  int32_t* err_flag;           /* [1]: set to 1 when a row would exceed cap    */
+} natsl_decode_cache;
+
+typedef struct {
+  const void* x;               /* [B, d_model] io                              */
+  const void* q;               /* [B, H, Dk] io                                */
+  const void* k;               /* [B, H, Dk] io                                */
+  const void* v;               /* [B, H, Dv] io                                */
+  const float* alpha;          /* [B, H]                                       */
+  const float* beta;           /* [B, H]                                       */
+  const float* w_score;        /* [d_model, 2G]                                */
+  const float* b_score;        /* [2G] or NULL                                 */
+  const float* w_mix;          /* [Dk, 2] (+ head stride)                      */
+  int64_t w_mix_head_stride;
+  const float* g_sm;           /* [Dv] or NULL                                 */
+  const float* g_lin;          /* [Dv] or NULL                                 */
+  void* out;                   /* [B, H, Dv] io                                */
+  int32_t* route_out;          /* [B, G] or NULL: -1 no chunk completed this
+                                  step, else the completed chunk's route       */
+  float* o_sm_dbg;             /* [B, H, Dv] fp32 or NULL                      */
+  float* o_gdn_dbg;            /* [B, H, Dv] fp32 or NULL                      */
+} natsl_decode_args;
+
+/*
+ * One decode step: every sequence appends one token to its open chunk.
+ * Softmax over the committed softmax chunks' rows, the open chunk's earlier
+ * rows and the new token; the Gated DeltaNet state is pseudo-updated from
+ * S_carry (first token of a chunk) or S_work.  When the open chunk reaches
+ * 64 tokens it is routed from x_sum / 64: softmax commits its 64 rows
+ * (n_committed += 64), linear commits its state (S_carry <- S_work) and its
+ * rows are dropped.  The new row is written at index n_committed + n_open;
+ * if that index is >= cap the row is not written and *err_flag is set to 1
+ * (checked by the caller after the step; counters still advance).
+ * ws from NATSL_ENTRY_DECODE_STEP (depends on cap via dims->L: pass
+ * dims->L = cap).
+ */
+natsl_status natsl_decode_step(const natsl_dims* dims, const natsl_decode_cache* cache,
+                               const natsl_decode_args* args, void* ws, size_t ws_bytes,
+                               hipStream_t stream);
+
+/*
+ * Kernel timing for measurement: when enabled, every kernel the library
+ * launches is bracketed by HIP events on the stream it runs on.
+ * natsl_profile_read synchronises those events and returns, for the kernel
+ * named `name`, the number of recorded launches and their summed duration
+ * in milliseconds since the last reset.  Names: "route", "compact",
+ * "gdn_prep", "gdn_scan", "softmax_masked", "merge", "decode_route",
+ * "decode_gdn", "decode_attn", "decode_combine", "decode_commit".
+ */
+natsl_status natsl_profile_enable(int on);
+natsl_status natsl_profile_reset(void);
+natsl_status natsl_profile_read(const char* name, int* count, double* total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NATSL_H */

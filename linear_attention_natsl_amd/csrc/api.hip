@@ -1,0 +1,544 @@
+// C ABI of the NAtS-L hybrid layer: argument validation (before anything is
+// enqueued), workspace carving, dtype / head-dim dispatch, the prefill
+// fork-join (Gated DeltaNet on a helper stream, softmax on the caller's
+// stream), and optional per-kernel event timing.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/natsl.h"
+#include "kernels.hpp"
+
+using namespace natsl;
+
+namespace {
+
+thread_local std::string g_err;
+
+natsl_status fail(natsl_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+natsl_status fail(natsl_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+natsl_status ok() {
+  g_err.clear();
+  return NATSL_OK;
+}
+natsl_status dev_fail(hipError_t e, const char* where) {
+  return fail(NATSL_ERR_DEVICE, "%s: %s", where, hipGetErrorString(e));
+}
+
+size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// ---------------------------------------------------------------- timing ----
+const char* kKernelNames[KID_COUNT] = {"route",        "compact",       "gdn_prep",   "gdn_scan",
+                                       "softmax_masked", "merge",       "decode_route", "decode_gdn",
+                                       "decode_attn",  "decode_combine", "decode_commit"};
+struct ProfRec {
+  int kid;
+  hipEvent_t a, b;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRec> g_prof_pool;  // created on enable
+size_t g_prof_used = 0;
+int g_prof_open[KID_COUNT];         // index of the record whose start was recorded
+
+void prof_hook(int kid, hipStream_t st, int phase) {
+  if (!g_prof_on) return;
+  if (phase == 0) {
+    if (g_prof_used >= g_prof_pool.size()) {
+      g_prof_open[kid] = -1;
+      return;
+    }
+    ProfRec& r = g_prof_pool[g_prof_used];
+    r.kid = kid;
+    g_prof_open[kid] = (int)g_prof_used++;
+    (void)hipEventRecord(r.a, st);
+  } else if (g_prof_open[kid] >= 0) {
+    (void)hipEventRecord(g_prof_pool[g_prof_open[kid]].b, st);
+  }
+}
+void (*prof_fn())(int, hipStream_t, int) { return g_prof_on ? prof_hook : nullptr; }
+
+// ------------------------------------------------------------ helper stream ----
+struct DevCtx {
+  bool init = false;
+  hipStream_t aux = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr, prep = nullptr;
+};
+std::mutex g_ctx_mu;
+DevCtx g_ctx[64];
+
+natsl_status get_ctx(DevCtx** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return dev_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(NATSL_ERR_UNSUPPORTED, "device ordinal %d", dev);
+  std::lock_guard<std::mutex> lk(g_ctx_mu);
+  DevCtx& c = g_ctx[dev];
+  if (!c.init) {
+    if ((e = hipStreamCreateWithFlags(&c.aux, hipStreamNonBlocking)) != hipSuccess)
+      return dev_fail(e, "hipStreamCreateWithFlags");
+    if ((e = hipEventCreateWithFlags(&c.fork, hipEventDisableTiming)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&c.join, hipEventDisableTiming)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&c.prep, hipEventDisableTiming)) != hipSuccess)
+      return dev_fail(e, "hipEventCreateWithFlags");
+    c.init = true;
+  }
+  *out = &c;
+  return NATSL_OK;
+}
+
+// ------------------------------------------------------------ validation ----
+natsl_status check_dims(const natsl_dims* d, bool need_L, bool need_dmodel) {
+  if (!d) return fail(NATSL_ERR_INVALID_ARG, "dims is NULL");
+  if (d->B < 0 || d->H < 1) return fail(NATSL_ERR_INVALID_ARG, "bad B=%d / H=%d", d->B, d->H);
+  if (d->io != NATSL_F32 && d->io != NATSL_BF16) return fail(NATSL_ERR_INVALID_ARG, "bad io dtype %d", (int)d->io);
+  if (d->chunk != 64) return fail(NATSL_ERR_UNSUPPORTED, "chunk must be 64 (got %d)", d->chunk);
+  if (d->Dk != d->Dv) return fail(NATSL_ERR_UNSUPPORTED, "Dk (%d) != Dv (%d)", d->Dk, d->Dv);
+  if (d->Dk != 64 && d->Dk != 128) return fail(NATSL_ERR_UNSUPPORTED, "head dim %d not in {64, 128}", d->Dk);
+  if (d->route_groups != 1 && d->route_groups != d->H)
+    return fail(NATSL_ERR_UNSUPPORTED, "route_groups %d not in {1, H=%d}", d->route_groups, d->H);
+  if (need_L) {
+    if (d->L < 64 || d->L % 64 != 0) return fail(NATSL_ERR_UNSUPPORTED, "L=%d must be a positive multiple of 64", d->L);
+    if ((int64_t)d->B * d->H * d->L > ((int64_t)1 << 31) - 1)
+      return fail(NATSL_ERR_UNSUPPORTED, "B*H*L too large");
+  }
+  if (need_dmodel) {
+    if (d->d_model < 8 || d->d_model % 8 != 0 || d->d_model > 65536)
+      return fail(NATSL_ERR_UNSUPPORTED, "d_model=%d must be a multiple of 8 in [8, 65536]", d->d_model);
+  }
+  return NATSL_OK;
+}
+#define NEED(p, name) \
+  if (!(p)) return fail(NATSL_ERR_INVALID_ARG, "%s is NULL", name)
+#define CHECK(x)                                \
+  do {                                          \
+    natsl_status _s = (x);                      \
+    if (_s != NATSL_OK) return _s;              \
+  } while (0)
+
+float eff_scale(const natsl_dims* d) { return d->sm_scale > 0.f ? d->sm_scale : 1.0f / sqrtf((float)d->Dk); }
+float eff_eps(const natsl_dims* d) { return d->rms_eps > 0.f ? d->rms_eps : 1e-6f; }
+int nchunks(const natsl_dims* d) { return d->L / 64; }
+
+struct FwdWs {
+  int32_t *route, *sel, *nsb;
+  void *o_sm, *o_gdn, *gdn;
+};
+size_t fwd_ws(const natsl_dims* d, natsl_dtype branch, FwdWs* w, void* base) {
+  const int64_t nc = nchunks(d), BG = (int64_t)d->B * d->route_groups;
+  const size_t bsz = (size_t)d->B * d->H * d->L * d->Dv * (branch == NATSL_BF16 ? 2 : 4);
+  size_t off = 0;
+  auto take = [&](size_t n) {
+    size_t o = off;
+    off += al256(n);
+    return o;
+  };
+  const size_t o_r = take(BG * nc * 4), o_s = take(BG * nc * 4), o_n = take(BG * (nc + 1) * 4);
+  const size_t o_sm = take(bsz), o_gd = take(bsz);
+  const size_t o_gdn = take(gdn_ws_bytes(d->io == NATSL_BF16, d->Dk, (int64_t)d->B * d->H * nc));
+  if (w) {
+    char* p = (char*)base;
+    w->route = (int32_t*)(p + o_r);
+    w->sel = (int32_t*)(p + o_s);
+    w->nsb = (int32_t*)(p + o_n);
+    w->o_sm = p + o_sm;
+    w->o_gdn = p + o_gd;
+    w->gdn = p + o_gdn;
+  }
+  return off;
+}
+
+natsl_status check_ws(void* ws, size_t have, size_t need) {
+  if (need == 0) return NATSL_OK;
+  if (!ws) return fail(NATSL_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
+  if (((uintptr_t)ws & 255) != 0) return fail(NATSL_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (have < need) return fail(NATSL_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", have, need);
+  return NATSL_OK;
+}
+
+// --------------------------------------------------------------- launches ----
+hipError_t do_route(const natsl_dims* d, const void* x, const float* w, const float* b,
+                    const int32_t* route_in, int32_t* route_out, int32_t* sel, int32_t* nsb,
+                    float* scores, hipStream_t st) {
+  const int nc = nchunks(d), G = d->route_groups;
+  auto prof = prof_fn();
+  hipError_t e = hipSuccess;
+  const int32_t* rsrc = route_in;
+  if (!route_in) {
+    if (prof) prof(KID_ROUTE, st, 0);
+    if (d->io == NATSL_BF16)
+      e = launch_route<bf16>((const bf16*)x, w, b, d->B, d->L, d->d_model, G, route_out, scores, st);
+    else
+      e = launch_route<float>((const float*)x, w, b, d->B, d->L, d->d_model, G, route_out, scores, st);
+    if (e != hipSuccess) return e;
+    if (prof) prof(KID_ROUTE, st, 1);
+    rsrc = route_out;
+  }
+  if (prof) prof(KID_COMPACT, st, 0);
+  e = launch_compact(rsrc, route_out, d->B, G, nc, sel, nsb, st);
+  if (e != hipSuccess) return e;
+  if (prof) prof(KID_COMPACT, st, 1);
+  return hipSuccess;
+}
+
+template <typename T, typename To>
+hipError_t do_softmax_t(const natsl_dims* d, const void* q, const void* k, const void* v,
+                        const int32_t* sel, const int32_t* nsb, void* o, float* lse, hipStream_t st) {
+  if (d->Dk == 64)
+    return launch_softmax_masked<T, To, 64>((const T*)q, (const T*)k, (const T*)v, sel, nsb, (To*)o, lse,
+                                            d->B, d->H, d->L, d->route_groups, eff_scale(d), st);
+  return launch_softmax_masked<T, To, 128>((const T*)q, (const T*)k, (const T*)v, sel, nsb, (To*)o, lse,
+                                           d->B, d->H, d->L, d->route_groups, eff_scale(d), st);
+}
+hipError_t do_softmax(const natsl_dims* d, const void* q, const void* k, const void* v, const int32_t* sel,
+                      const int32_t* nsb, void* o, natsl_dtype od, float* lse, hipStream_t st) {
+  auto prof = prof_fn();
+  if (prof) prof(KID_SOFTMAX, st, 0);
+  hipError_t e;
+  if (d->io == NATSL_BF16)
+    e = od == NATSL_BF16 ? do_softmax_t<bf16, bf16>(d, q, k, v, sel, nsb, o, lse, st)
+                         : do_softmax_t<bf16, float>(d, q, k, v, sel, nsb, o, lse, st);
+  else
+    e = od == NATSL_BF16 ? do_softmax_t<float, bf16>(d, q, k, v, sel, nsb, o, lse, st)
+                         : do_softmax_t<float, float>(d, q, k, v, sel, nsb, o, lse, st);
+  if (e == hipSuccess && prof) prof(KID_SOFTMAX, st, 1);
+  return e;
+}
+
+template <typename T, typename To>
+hipError_t do_gdn_t(const natsl_dims* d, const void* q, const void* k, const void* v, const float* a,
+                    const float* b, const int32_t* route, const float* S0, void* o, float* Sf, void* ws,
+                    hipStream_t st) {
+  DevCtx* c = nullptr;
+  hipEvent_t ev = nullptr;
+  if (get_ctx(&c) == NATSL_OK) ev = c->prep;
+  if (d->Dk == 64)
+    return launch_gdn<T, To, 64>((const T*)q, (const T*)k, (const T*)v, a, b, route, S0, (To*)o, Sf, ws,
+                                 d->B, d->H, d->L, d->route_groups, st, st, ev, prof_fn());
+  return launch_gdn<T, To, 128>((const T*)q, (const T*)k, (const T*)v, a, b, route, S0, (To*)o, Sf, ws,
+                                d->B, d->H, d->L, d->route_groups, st, st, ev, prof_fn());
+}
+hipError_t do_gdn(const natsl_dims* d, const void* q, const void* k, const void* v, const float* a,
+                  const float* b, const int32_t* route, const float* S0, void* o, natsl_dtype od, float* Sf,
+                  void* ws, hipStream_t st) {
+  if (d->io == NATSL_BF16)
+    return od == NATSL_BF16 ? do_gdn_t<bf16, bf16>(d, q, k, v, a, b, route, S0, o, Sf, ws, st)
+                            : do_gdn_t<bf16, float>(d, q, k, v, a, b, route, S0, o, Sf, ws, st);
+  return od == NATSL_BF16 ? do_gdn_t<float, bf16>(d, q, k, v, a, b, route, S0, o, Sf, ws, st)
+                          : do_gdn_t<float, float>(d, q, k, v, a, b, route, S0, o, Sf, ws, st);
+}
+
+template <typename Tq, typename Tb>
+hipError_t do_merge_t(const natsl_dims* d, const void* q, const void* osm, const void* ogd, const float* wm,
+                      int64_t hs, const float* gs, const float* gl, void* out, hipStream_t st) {
+  if (d->Dk == 64)
+    return launch_merge<Tq, Tb, 64>((const Tq*)q, (const Tb*)osm, (const Tb*)ogd, wm, hs, gs, gl, (Tq*)out,
+                                    d->B, d->H, d->L, eff_eps(d), st);
+  return launch_merge<Tq, Tb, 128>((const Tq*)q, (const Tb*)osm, (const Tb*)ogd, wm, hs, gs, gl, (Tq*)out,
+                                   d->B, d->H, d->L, eff_eps(d), st);
+}
+hipError_t do_merge(const natsl_dims* d, const void* q, const void* osm, const void* ogd, natsl_dtype bd,
+                    const float* wm, int64_t hs, const float* gs, const float* gl, void* out, hipStream_t st) {
+  auto prof = prof_fn();
+  if (prof) prof(KID_MERGE, st, 0);
+  hipError_t e;
+  if (d->io == NATSL_BF16)
+    e = bd == NATSL_BF16 ? do_merge_t<bf16, bf16>(d, q, osm, ogd, wm, hs, gs, gl, out, st)
+                         : do_merge_t<bf16, float>(d, q, osm, ogd, wm, hs, gs, gl, out, st);
+  else
+    e = bd == NATSL_BF16 ? do_merge_t<float, bf16>(d, q, osm, ogd, wm, hs, gs, gl, out, st)
+                         : do_merge_t<float, float>(d, q, osm, ogd, wm, hs, gs, gl, out, st);
+  if (e == hipSuccess && prof) prof(KID_MERGE, st, 1);
+  return e;
+}
+
+}  // namespace
+
+extern "C" {
+
+int natsl_version(void) { return 100; }
+
+const char* natsl_last_error(void) { return g_err.c_str(); }
+
+natsl_status natsl_workspace_size(int entry, const natsl_dims* dims, size_t* bytes) {
+  if (!bytes) return fail(NATSL_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = 0;
+  switch (entry) {
+    case NATSL_ENTRY_ROUTE:
+    case NATSL_ENTRY_SOFTMAX_MASKED:
+    case NATSL_ENTRY_MERGE:
+      CHECK(check_dims(dims, true, false));
+      return ok();
+    case NATSL_ENTRY_GDN_CHUNK:
+      CHECK(check_dims(dims, true, false));
+      *bytes = gdn_ws_bytes(dims->io == NATSL_BF16, dims->Dk, (int64_t)dims->B * dims->H * nchunks(dims));
+      return ok();
+    case NATSL_ENTRY_FORWARD:
+      CHECK(check_dims(dims, true, false));
+      *bytes = fwd_ws(dims, NATSL_F32, nullptr, nullptr);  // fp32 branches: the larger of the two
+      return ok();
+    case NATSL_ENTRY_DECODE_STEP:
+      CHECK(check_dims(dims, false, false));
+      if (dims->L < 1) return fail(NATSL_ERR_INVALID_ARG, "decode: dims->L must hold the cache capacity");
+      *bytes = decode_ws_bytes(dims->B, dims->H, dims->route_groups, dims->Dk, dims->L);
+      return ok();
+    default:
+      return fail(NATSL_ERR_INVALID_ARG, "unknown entry id %d", entry);
+  }
+}
+
+natsl_status natsl_route(const natsl_dims* dims, const void* x, const float* w_score, const float* b_score,
+                         const int32_t* route_in, int32_t* route_out, int32_t* sel_idx, int32_t* nsel_before,
+                         float* scores, hipStream_t stream) {
+  CHECK(check_dims(dims, true, route_in == nullptr));
+  if (dims->B == 0) return ok();  // empty batch: nothing to do, pointers may be NULL
+  if (!route_in) {
+    NEED(x, "x");
+    NEED(w_score, "w_score");
+  }
+  NEED(route_out, "route_out");
+  NEED(sel_idx, "sel_idx");
+  NEED(nsel_before, "nsel_before");
+  hipError_t e = do_route(dims, x, w_score, b_score, route_in, route_out, sel_idx, nsel_before, scores, stream);
+  if (e != hipSuccess) return dev_fail(e, "natsl_route");
+  return ok();
+}
+
+natsl_status natsl_gdn_chunk(const natsl_dims* dims, const void* q, const void* k, const void* v,
+                             const float* alpha, const float* beta, const int32_t* route, const float* S_init,
+                             void* o_gdn, natsl_dtype o_dtype, float* S_final, void* ws, size_t ws_bytes,
+                             hipStream_t stream) {
+  CHECK(check_dims(dims, true, false));
+  if (dims->B == 0) return ok();  // empty batch: nothing to do, pointers may be NULL
+  NEED(q, "q");
+  NEED(k, "k");
+  NEED(v, "v");
+  NEED(alpha, "alpha");
+  NEED(beta, "beta");
+  NEED(route, "route");
+  NEED(o_gdn, "o_gdn");
+  if (o_dtype != NATSL_F32 && o_dtype != NATSL_BF16) return fail(NATSL_ERR_INVALID_ARG, "bad o_dtype");
+  size_t need = 0;
+  natsl_workspace_size(NATSL_ENTRY_GDN_CHUNK, dims, &need);
+  CHECK(check_ws(ws, ws_bytes, need));
+  hipError_t e = do_gdn(dims, q, k, v, alpha, beta, route, S_init, o_gdn, o_dtype, S_final, ws, stream);
+  if (e != hipSuccess) return dev_fail(e, "natsl_gdn_chunk");
+  return ok();
+}
+
+natsl_status natsl_softmax_masked(const natsl_dims* dims, const void* q, const void* k, const void* v,
+                                  const int32_t* sel_idx, const int32_t* nsel_before, void* o_sm,
+                                  natsl_dtype o_dtype, float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  CHECK(check_dims(dims, true, false));
+  if (dims->B == 0) return ok();  // empty batch: nothing to do, pointers may be NULL
+  NEED(q, "q");
+  NEED(k, "k");
+  NEED(v, "v");
+  NEED(sel_idx, "sel_idx");
+  NEED(nsel_before, "nsel_before");
+  NEED(o_sm, "o_sm");
+  if (o_dtype != NATSL_F32 && o_dtype != NATSL_BF16) return fail(NATSL_ERR_INVALID_ARG, "bad o_dtype");
+  hipError_t e = do_softmax(dims, q, k, v, sel_idx, nsel_before, o_sm, o_dtype, lse, stream);
+  if (e != hipSuccess) return dev_fail(e, "natsl_softmax_masked");
+  return ok();
+}
+
+natsl_status natsl_merge(const natsl_dims* dims, const void* q, const void* o_sm, const void* o_gdn,
+                         natsl_dtype branch_dtype, const float* w_mix, int64_t w_mix_head_stride,
+                         const float* g_sm, const float* g_lin, void* out, hipStream_t stream) {
+  CHECK(check_dims(dims, true, false));
+  if (dims->B == 0) return ok();  // empty batch: nothing to do, pointers may be NULL
+  NEED(q, "q");
+  NEED(o_sm, "o_sm");
+  NEED(o_gdn, "o_gdn");
+  NEED(w_mix, "w_mix");
+  NEED(out, "out");
+  if (branch_dtype != NATSL_F32 && branch_dtype != NATSL_BF16) return fail(NATSL_ERR_INVALID_ARG, "bad branch dtype");
+  if (w_mix_head_stride < 0) return fail(NATSL_ERR_INVALID_ARG, "negative w_mix head stride");
+  hipError_t e = do_merge(dims, q, o_sm, o_gdn, branch_dtype, w_mix, w_mix_head_stride, g_sm, g_lin, out, stream);
+  if (e != hipSuccess) return dev_fail(e, "natsl_merge");
+  return ok();
+}
+
+natsl_status natsl_forward(const natsl_dims* dims, const natsl_forward_args* a, void* ws, size_t ws_bytes,
+                           hipStream_t stream) {
+  CHECK(check_dims(dims, true, a && !a->route_override));
+  if (dims->B == 0) return ok();  // empty batch: nothing to do, pointers may be NULL
+  NEED(a, "args");
+  NEED(a->q, "q");
+  NEED(a->k, "k");
+  NEED(a->v, "v");
+  NEED(a->alpha, "alpha");
+  NEED(a->beta, "beta");
+  NEED(a->w_mix, "w_mix");
+  NEED(a->out, "out");
+  if (!a->route_override) {
+    NEED(a->x, "x");
+    NEED(a->w_score, "w_score");
+  }
+  if (a->branch_dtype != NATSL_F32 && a->branch_dtype != NATSL_BF16)
+    return fail(NATSL_ERR_INVALID_ARG, "bad branch dtype");
+  if (a->w_mix_head_stride < 0) return fail(NATSL_ERR_INVALID_ARG, "negative w_mix head stride");
+  FwdWs w;
+  const size_t need = fwd_ws(dims, a->branch_dtype, nullptr, nullptr);
+  CHECK(check_ws(ws, ws_bytes, need));
+  fwd_ws(dims, a->branch_dtype, &w, ws);
+  DevCtx* ctx = nullptr;
+  CHECK(get_ctx(&ctx));
+  int32_t* route = a->route_out ? a->route_out : w.route;
+  void* o_sm = a->o_sm_dbg ? a->o_sm_dbg : w.o_sm;
+  void* o_gd = a->o_gdn_dbg ? a->o_gdn_dbg : w.o_gdn;
+  hipError_t e = do_route(dims, a->x, a->w_score, a->b_score, a->route_override, route, w.sel, w.nsb,
+                          a->scores_out, stream);
+  if (e != hipSuccess) return dev_fail(e, "natsl_forward/route");
+  // fork: Gated DeltaNet branch on the helper stream, softmax on the caller's
+  if ((e = hipEventRecord(ctx->fork, stream)) != hipSuccess) return dev_fail(e, "hipEventRecord");
+  if ((e = hipStreamWaitEvent(ctx->aux, ctx->fork, 0)) != hipSuccess) return dev_fail(e, "hipStreamWaitEvent");
+  e = do_gdn(dims, a->q, a->k, a->v, a->alpha, a->beta, route, a->S_init, o_gd, a->branch_dtype, a->S_final,
+             w.gdn, ctx->aux);
+  if (e != hipSuccess) return dev_fail(e, "natsl_forward/gdn");
+  e = do_softmax(dims, a->q, a->k, a->v, w.sel, w.nsb, o_sm, a->branch_dtype, nullptr, stream);
+  if (e != hipSuccess) return dev_fail(e, "natsl_forward/softmax");
+  if ((e = hipEventRecord(ctx->join, ctx->aux)) != hipSuccess) return dev_fail(e, "hipEventRecord");
+  if ((e = hipStreamWaitEvent(stream, ctx->join, 0)) != hipSuccess) return dev_fail(e, "hipStreamWaitEvent");
+  e = do_merge(dims, a->q, o_sm, o_gd, a->branch_dtype, a->w_mix, a->w_mix_head_stride, a->g_sm, a->g_lin, a->out,
+               stream);
+  if (e != hipSuccess) return dev_fail(e, "natsl_forward/merge");
+  return ok();
+}
+
+natsl_status natsl_decode_step(const natsl_dims* dims, const natsl_decode_cache* c, const natsl_decode_args* a,
+                               void* ws, size_t ws_bytes, hipStream_t stream) {
+  CHECK(check_dims(dims, false, true));
+  if (dims->B == 0) return ok();  // empty batch: nothing to do, pointers may be NULL
+  NEED(c, "cache");
+  NEED(a, "args");
+  NEED(c->k_cache, "k_cache");
+  NEED(c->v_cache, "v_cache");
+  NEED(c->n_committed, "n_committed");
+  NEED(c->n_open, "n_open");
+  NEED(c->S_carry, "S_carry");
+  NEED(c->S_work, "S_work");
+  NEED(c->x_sum, "x_sum");
+  NEED(c->err_flag, "err_flag");
+  if (c->cap < 1) return fail(NATSL_ERR_INVALID_ARG, "cache capacity %d", c->cap);
+  NEED(a->x, "x");
+  NEED(a->q, "q");
+  NEED(a->k, "k");
+  NEED(a->v, "v");
+  NEED(a->alpha, "alpha");
+  NEED(a->beta, "beta");
+  NEED(a->w_score, "w_score");
+  NEED(a->w_mix, "w_mix");
+  NEED(a->out, "out");
+  if (a->w_mix_head_stride < 0) return fail(NATSL_ERR_INVALID_ARG, "negative w_mix head stride");
+  const size_t need = decode_ws_bytes(dims->B, dims->H, dims->route_groups, dims->Dk, c->cap);
+  CHECK(check_ws(ws, ws_bytes, need));
+  DecodeLaunch L;
+  L.B = dims->B;
+  L.H = dims->H;
+  L.G = dims->route_groups;
+  L.d = dims->d_model;
+  L.cap = c->cap;
+  L.scale = eff_scale(dims);
+  L.eps = eff_eps(dims);
+  L.x = a->x;
+  L.q = a->q;
+  L.k = a->k;
+  L.v = a->v;
+  L.alpha = a->alpha;
+  L.beta = a->beta;
+  L.w_score = a->w_score;
+  L.b_score = a->b_score;
+  L.w_mix = a->w_mix;
+  L.w_mix_hs = a->w_mix_head_stride;
+  L.g_sm = a->g_sm;
+  L.g_lin = a->g_lin;
+  L.k_cache = c->k_cache;
+  L.v_cache = c->v_cache;
+  L.n_committed = c->n_committed;
+  L.n_open = c->n_open;
+  L.err_flag = c->err_flag;
+  L.route_out = a->route_out;
+  L.S_carry = c->S_carry;
+  L.S_work = c->S_work;
+  L.x_sum = c->x_sum;
+  L.out = a->out;
+  L.o_sm_dbg = a->o_sm_dbg;
+  L.o_gdn_dbg = a->o_gdn_dbg;
+  hipError_t e;
+  auto prof = prof_fn();
+  if (dims->io == NATSL_BF16)
+    e = dims->Dk == 64 ? launch_decode<bf16, 64>(L, ws, stream, prof) : launch_decode<bf16, 128>(L, ws, stream, prof);
+  else
+    e = dims->Dk == 64 ? launch_decode<float, 64>(L, ws, stream, prof) : launch_decode<float, 128>(L, ws, stream, prof);
+  if (e != hipSuccess) return dev_fail(e, "natsl_decode_step");
+  return ok();
+}
+
+natsl_status natsl_profile_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (on && g_prof_pool.empty()) {
+    g_prof_pool.resize(8192);
+    for (auto& r : g_prof_pool) {
+      hipError_t e;
+      if ((e = hipEventCreate(&r.a)) != hipSuccess || (e = hipEventCreate(&r.b)) != hipSuccess) {
+        g_prof_pool.clear();
+        return dev_fail(e, "hipEventCreate");
+      }
+    }
+  }
+  g_prof_on = on != 0;
+  g_prof_used = 0;
+  return ok();
+}
+
+natsl_status natsl_profile_reset(void) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_used = 0;
+  return ok();
+}
+
+natsl_status natsl_profile_read(const char* name, int* count, double* total_ms) {
+  NEED(name, "name");
+  NEED(count, "count");
+  NEED(total_ms, "total_ms");
+  int kid = -1;
+  for (int i = 0; i < KID_COUNT; ++i)
+    if (strcmp(name, kKernelNames[i]) == 0) kid = i;
+  if (kid < 0) return fail(NATSL_ERR_INVALID_ARG, "unknown kernel name '%s'", name);
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  int n = 0;
+  double tot = 0.0;
+  for (size_t i = 0; i < g_prof_used; ++i) {
+    const ProfRec& r = g_prof_pool[i];
+    if (r.kid != kid) continue;
+    hipError_t e = hipEventSynchronize(r.b);
+    if (e != hipSuccess) return dev_fail(e, "hipEventSynchronize");
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, r.a, r.b);
+    if (e != hipSuccess) return dev_fail(e, "hipEventElapsedTime");
+    tot += ms;
+    ++n;
+  }
+  *count = n;
+  *total_ms = tot;
+  return ok();
+}
+
+}  // extern "C"

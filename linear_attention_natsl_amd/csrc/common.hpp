@@ -1,0 +1,135 @@
+// Device helpers shared by the NAtS-L kernels (gfx950 / CDNA4).
+//
+// Matrix products use 16x16 MFMA tiles with a 32-deep contraction step:
+//   bf16: one v_mfma_f32_16x16x32_bf16 per step (8 bf16 per lane per operand)
+//   fp32: eight v_mfma_f32_16x16x4_f32 per step (one fp32 per lane each)
+// A lane l (g = l / 16, c = l % 16) holds, for a step,
+//   A operand: row c of the 16x32 A tile, 8 contraction indices kmap(g, 0..7)
+//   B operand: column c of the 32x16 B tile, the same 8 contraction indices
+// and the fp32 accumulator holds C[4g + i][c], i = 0..3.
+// Any bijective kmap works as long as A and B use the same one, because the
+// hardware pairs A's and B's values by (lane group, slot).  Two maps are used:
+//   KMAP_ROW: kmap(g, j) = 8g + j            (contiguous: 16 B of a row)
+//   KMAP_ACC: kmap(g, j) = 4g + j      (j<4)  (the layout an accumulator has:
+//             kmap(g, j) = 16 + 4g + j-4 (j>=4) two stacked 16-row C tiles)
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace natsl {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int CHUNK = 64;
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+
+// One lane's share of an MFMA operand for one 32-deep step.
+template <typename T> struct Frag;
+template <> struct Frag<bf16> { bf16x8 v; };
+template <> struct Frag<float> { float v[8]; };
+
+__device__ __forceinline__ void mma(f32x4& c, const Frag<bf16>& a, const Frag<bf16>& b) {
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, c, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x4& c, const Frag<float>& a, const Frag<float>& b) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[j], b.v[j], c, 0, 0, 0);
+}
+
+template <typename T> __device__ __forceinline__ T frag_get(const Frag<T>& f, int j);
+template <> __device__ __forceinline__ bf16 frag_get<bf16>(const Frag<bf16>& f, int j) { return f.v[j]; }
+template <> __device__ __forceinline__ float frag_get<float>(const Frag<float>& f, int j) { return f.v[j]; }
+__device__ __forceinline__ void frag_set(Frag<bf16>& f, int j, float x) { f.v[j] = (bf16)x; }
+__device__ __forceinline__ void frag_set(Frag<float>& f, int j, float x) { f.v[j] = x; }
+
+// 8 contiguous elements (16 B bf16 / 32 B fp32) <-> Frag
+template <typename T> __device__ __forceinline__ Frag<T> load8(const T* p);
+template <> __device__ __forceinline__ Frag<bf16> load8<bf16>(const bf16* p) {
+  Frag<bf16> f;
+  f.v = *reinterpret_cast<const bf16x8*>(p);
+  return f;
+}
+template <> __device__ __forceinline__ Frag<float> load8<float>(const float* p) {
+  Frag<float> f;
+  f32x4 a = *reinterpret_cast<const f32x4*>(p);
+  f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+  f.v[0] = a[0]; f.v[1] = a[1]; f.v[2] = a[2]; f.v[3] = a[3];
+  f.v[4] = b[0]; f.v[5] = b[1]; f.v[6] = b[2]; f.v[7] = b[3];
+  return f;
+}
+template <typename T> __device__ __forceinline__ void store8(T* p, const Frag<T>& f);
+template <> __device__ __forceinline__ void store8<bf16>(bf16* p, const Frag<bf16>& f) {
+  *reinterpret_cast<bf16x8*>(p) = f.v;
+}
+template <> __device__ __forceinline__ void store8<float>(float* p, const Frag<float>& f) {
+  f32x4 a = {f.v[0], f.v[1], f.v[2], f.v[3]};
+  f32x4 b = {f.v[4], f.v[5], f.v[6], f.v[7]};
+  *reinterpret_cast<f32x4*>(p) = a;
+  *reinterpret_cast<f32x4*>(p + 4) = b;
+}
+
+// 4 contiguous elements <-> floats
+template <typename T> __device__ __forceinline__ void load4f(const T* p, float* o);
+template <> __device__ __forceinline__ void load4f<bf16>(const bf16* p, float* o) {
+  bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+  o[0] = (float)v[0]; o[1] = (float)v[1]; o[2] = (float)v[2]; o[3] = (float)v[3];
+}
+template <> __device__ __forceinline__ void load4f<float>(const float* p, float* o) {
+  f32x4 v = *reinterpret_cast<const f32x4*>(p);
+  o[0] = v[0]; o[1] = v[1]; o[2] = v[2]; o[3] = v[3];
+}
+template <typename T> __device__ __forceinline__ void store4f(T* p, const float* o);
+template <> __device__ __forceinline__ void store4f<bf16>(bf16* p, const float* o) {
+  bf16x4 v = {(bf16)o[0], (bf16)o[1], (bf16)o[2], (bf16)o[3]};
+  *reinterpret_cast<bf16x4*>(p) = v;
+}
+template <> __device__ __forceinline__ void store4f<float>(float* p, const float* o) {
+  f32x4 v = {o[0], o[1], o[2], o[3]};
+  *reinterpret_cast<f32x4*>(p) = v;
+}
+
+// 8 contiguous elements -> floats
+template <typename T> __device__ __forceinline__ void load8f(const T* p, float* o) {
+  Frag<T> f = load8<T>(p);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) o[j] = to_f32(frag_get<T>(f, j));
+}
+
+__device__ __forceinline__ int kmap_acc(int g, int j) { return (j < 4) ? (4 * g + j) : (16 + 4 * g + (j - 4)); }
+
+// "Key-group" LDS layout for an operand whose contraction index runs over
+// tokens (rows of a row-major [64 x D] tile): element (tok, col) is stored at
+//   ((tok / 4) * D + swz(col)) * 4 + tok % 4
+// so the 4 tokens 4kg..4kg+3 of one column are contiguous (one 8-byte bf16 /
+// 16-byte fp32 read).  swz permutes columns inside each group of 16 so that
+// 16 lanes reading 16 consecutive columns, or 16 lanes writing columns
+// 8m + i (m = 0..15), hit distinct bank groups.
+__device__ __forceinline__ int kg_swz(int col) {
+  const int hi = col >> 4;
+  return (col & ~15) | ((col ^ hi) & 15);
+}
+template <int D> __device__ __forceinline__ int kg_index(int kg, int col) {
+  return (kg * D + kg_swz(col)) * 4;
+}
+
+// Wave-level helpers (wave64).
+__device__ __forceinline__ float wave_max_xor(float v, int mask) {
+  return fmaxf(v, __shfl_xor(v, mask, 64));
+}
+__device__ __forceinline__ float wave_sum_xor(float v, int mask) { return v + __shfl_xor(v, mask, 64); }
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+}  // namespace natsl

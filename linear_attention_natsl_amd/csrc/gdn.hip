@@ -1,0 +1,555 @@
+// Gated DeltaNet branch with per-chunk rollback.
+//
+// "Technische Samenvatting: Neural Attention Search Linear (NAtS-L)",
+// Kernmechanismen 3: the model keeps a hidden state for the linear operation,
+// pseudo-updates it through every chunk, and resets it to the chunk start when
+// the chunk was not routed to the linear operation.  The recurrence itself is
+// the gated delta rule (Gated DeltaNet is named in Kernmechanismen 1; the
+// "Systematische Analyse van Hybride Lineaire Aandacht" summary describes this
+// family as data-dependent gating plus a delta rule that erases stale content):
+//   S_t = a_t (S_{t-1} - b_t k_t (k_t^T S_{t-1})) + b_t k_t v_t^T,  o_t = S_t^T q_t.
+//
+// Chunkwise form (exact up to rounding) for a chunk starting from state S0,
+// with g_r = sum_{i<=r} log a_i and gamma_r = exp(g_r):
+//   A = strict_tril(exp(g_r - g_i) k_r.k_i),  T = (I + diag(b) A)^-1
+//   W = T diag(b gamma) K,  U~ = T diag(b) V,  U = U~ - W S0
+//   P = tril(exp(g_r - g_i) q_r.k_i),  O = diag(gamma) Q S0 + P U
+//   S_end = gamma_C S0 + K~^T U,  K~ = diag(exp(g_C - g_i)) K
+// S_end replaces S0 only for linear-routed chunks (rollback otherwise).
+//
+// Two kernels:
+//   k_gdn_prep  one workgroup per (b, h, chunk), fully parallel: K K^T and
+//               Q K^T on MFMA, the 64x64 unit-lower-triangular inverse T in
+//               LDS (fp32: 16x16 diagonal blocks by forward substitution, then
+//               block rows), T diag(b) V and T diag(b gamma) K on MFMA; writes
+//               -W, U~, K~^T, P and gamma in exactly the per-lane fragment
+//               order the scan consumes (every scan load is 16 B per lane,
+//               1 KiB contiguous per wave).
+//   k_gdn_scan  one workgroup per (b, h, 32-column slice of Dv), sequential
+//               over chunks.  Columns of S evolve independently under the
+//               delta rule, so slicing Dv needs no communication.  The fp32
+//               master state lives in registers, a bf16 copy in LDS feeds the
+//               MFMAs; the next chunk's operands are loaded while the current
+//               chunk is computed.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace natsl {
+
+template <typename T, int D>
+struct GdnCfg {
+  static constexpr int KP = D + 16 / (int)sizeof(T);   // row-layout pitch (elements)
+  static constexpr int PP = CHUNK + 16 / (int)sizeof(T);
+  static constexpr int LTP = CHUNK + 1;                 // fp32 pitch of L / T
+  static constexpr int KF = D / 32;
+  static constexpr int NT = D / 16;                     // 16-wide column tiles of D
+  // LDS layout of the prep kernel (bytes)
+  static constexpr int OFF_KS = 0;
+  static constexpr int OFF_KG = OFF_KS + CHUNK * KP * (int)sizeof(T);
+  static constexpr int OFF_VG = OFF_KG + CHUNK * D * (int)sizeof(T);
+  static constexpr int OFF_LT = OFF_VG + CHUNK * D * (int)sizeof(T);
+  static constexpr int OFF_RS = OFF_LT + CHUNK * LTP * 4;
+  static constexpr int OFF_PS = OFF_RS + 3 * 16 * 17 * 4;
+  static constexpr int OFF_GL = OFF_PS + ((CHUNK * PP * (int)sizeof(T) + 15) / 16) * 16;
+  static constexpr int PREP_LDS = OFF_GL + 4 * CHUNK * 4;
+  // per chunk-head workspace (elements)
+  static constexpr int64_t WN = (int64_t)CHUNK * D;   // T
+  static constexpr int64_t UT = (int64_t)CHUNK * D;   // float
+  static constexpr int64_t KT = (int64_t)D * CHUNK;   // T
+  static constexpr int64_t PM = (int64_t)CHUNK * CHUNK;  // T
+  static constexpr int64_t GM = 80;                   // float: gamma[64], gamma_C at 64
+};
+
+size_t gdn_ws_bytes(int io_is_bf16, int D, int64_t nch) {
+  const size_t ts = io_is_bf16 ? 2 : 4;
+  const size_t per = (size_t)CHUNK * D * ts + (size_t)CHUNK * D * 4 + (size_t)D * CHUNK * ts +
+                     (size_t)CHUNK * CHUNK * ts + 80 * 4;
+  return per * (size_t)nch + 5 * 256;
+}
+
+template <typename T, int D>
+struct GdnWs {
+  T* wn;
+  float* ut;
+  T* kt;
+  T* pm;
+  float* gm;
+};
+
+template <typename T, int D>
+static GdnWs<T, D> carve(void* ws, int64_t nch) {
+  using C = GdnCfg<T, D>;
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  char* p = (char*)ws;
+  GdnWs<T, D> w;
+  w.wn = (T*)p; p += al(C::WN * nch * sizeof(T));
+  w.ut = (float*)p; p += al(C::UT * nch * sizeof(float));
+  w.kt = (T*)p; p += al(C::KT * nch * sizeof(T));
+  w.pm = (T*)p; p += al(C::PM * nch * sizeof(T));
+  w.gm = (float*)p;
+  return w;
+}
+
+template <typename T> __device__ __forceinline__ Frag<T> ld4x2(const T* p0, const T* p1);
+template <> __device__ __forceinline__ Frag<bf16> ld4x2<bf16>(const bf16* p0, const bf16* p1) {
+  bf16x4 a = *reinterpret_cast<const bf16x4*>(p0);
+  bf16x4 b = *reinterpret_cast<const bf16x4*>(p1);
+  Frag<bf16> f;
+  f.v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return f;
+}
+template <> __device__ __forceinline__ Frag<float> ld4x2<float>(const float* p0, const float* p1) {
+  f32x4 a = *reinterpret_cast<const f32x4*>(p0);
+  f32x4 b = *reinterpret_cast<const f32x4*>(p1);
+  Frag<float> f;
+  f.v[0] = a[0]; f.v[1] = a[1]; f.v[2] = a[2]; f.v[3] = a[3];
+  f.v[4] = b[0]; f.v[5] = b[1]; f.v[6] = b[2]; f.v[7] = b[3];
+  return f;
+}
+template <typename T> __device__ __forceinline__ void st4(T* p, float a, float b, float c, float d);
+template <> __device__ __forceinline__ void st4<bf16>(bf16* p, float a, float b, float c, float d) {
+  bf16x4 v = {(bf16)a, (bf16)b, (bf16)c, (bf16)d};
+  *reinterpret_cast<bf16x4*>(p) = v;
+}
+template <> __device__ __forceinline__ void st4<float>(float* p, float a, float b, float c, float d) {
+  f32x4 v = {a, b, c, d};
+  *reinterpret_cast<f32x4*>(p) = v;
+}
+
+// ---------------------------------------------------------------- prep ----
+template <typename T, int D>
+__global__ void __launch_bounds__(256, 2)
+    k_gdn_prep(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+               const float* __restrict__ alpha, const float* __restrict__ beta, GdnWs<T, D> ws,
+               int L) {
+  using C = GdnCfg<T, D>;
+  extern __shared__ __align__(16) unsigned char lds[];
+  T* Ks = (T*)(lds + C::OFF_KS);
+  T* Kg = (T*)(lds + C::OFF_KG);
+  T* Vg = (T*)(lds + C::OFF_VG);
+  float* LT = (float*)(lds + C::OFF_LT);
+  float* Rs = (float*)(lds + C::OFF_RS);
+  T* Ps = (T*)(lds + C::OFF_PS);
+  float* gl = (float*)(lds + C::OFF_GL);  // cumulative log decay
+  float* bl = gl + CHUNK;                 // beta
+  float* gbl = bl + CHUNK;                // beta * gamma
+  float* ekl = gbl + CHUNK;               // exp(g_C - g)
+
+  const int nc = L / CHUNK;
+  const int64_t ch = blockIdx.x;
+  const int64_t bh = ch / nc;
+  const int cc = (int)(ch % nc);
+  const int64_t tok0 = bh * L + (int64_t)cc * CHUNK;  // row index into [B*H*L]
+  const int t = threadIdx.x, lane = lane_id(), w = wave_id();
+  const int g = lane >> 4, c = lane & 15;
+
+  // cumulative log decay (wave 0), beta
+  if (w == 0) {
+    const float a = alpha[tok0 + lane];
+    float s = logf(a);
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float o = __shfl_up(s, off, 64);
+      if (lane >= off) s += o;
+    }
+    const float gC = __shfl(s, 63, 64);
+    const float bt = beta[tok0 + lane];
+    gl[lane] = s;
+    bl[lane] = bt;
+    gbl[lane] = bt * expf(s);
+    ekl[lane] = expf(gC - s);
+    ws.gm[ch * C::GM + lane] = expf(s);
+    if (lane == 0) ws.gm[ch * C::GM + 64] = expf(gC);
+  }
+  // K -> row layout and key-group layout, V -> key-group layout
+  const T* kc = k + tok0 * D;
+  const T* vc = v + tok0 * D;
+  for (int e = t; e < CHUNK * D / 8; e += 256) {
+    const int row = e / (D / 8), col = (e % (D / 8)) * 8;
+    store8<T>(Ks + row * C::KP + col, load8<T>(kc + row * D + col));
+  }
+  for (int task = t; task < (CHUNK / 4) * (D / 8); task += 256) {
+    const int kg = task / (D / 8), col = (task % (D / 8)) * 8;
+    Frag<T> kr[4], vr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      kr[i] = load8<T>(kc + (4 * kg + i) * D + col);
+      vr[i] = load8<T>(vc + (4 * kg + i) * D + col);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      st4<T>(Kg + kg_index<D>(kg, col + j), to_f32(frag_get<T>(kr[0], j)), to_f32(frag_get<T>(kr[1], j)),
+             to_f32(frag_get<T>(kr[2], j)), to_f32(frag_get<T>(kr[3], j)));
+      st4<T>(Vg + kg_index<D>(kg, col + j), to_f32(frag_get<T>(vr[0], j)), to_f32(frag_get<T>(vr[1], j)),
+             to_f32(frag_get<T>(vr[2], j)), to_f32(frag_get<T>(vr[3], j)));
+    }
+  }
+  Frag<T> qa[C::KF];
+#pragma unroll
+  for (int ks = 0; ks < C::KF; ++ks) qa[ks] = load8<T>(q + (tok0 + 16 * w + c) * D + 32 * ks + 8 * g);
+  __syncthreads();
+
+  // K K^T and Q K^T rows 16w .. 16w+15
+  f32x4 akk[4], aqk[4];
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) {
+    akk[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    aqk[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int ks = 0; ks < C::KF; ++ks) {
+    const Frag<T> ak = load8<T>(Ks + (16 * w + c) * C::KP + 32 * ks + 8 * g);
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      const Frag<T> bk = load8<T>(Ks + (16 * ct + c) * C::KP + 32 * ks + 8 * g);
+      mma(akk[ct], ak, bk);
+      mma(aqk[ct], qa[ks], bk);
+    }
+  }
+  // L = diag(beta) strict_tril(Gamma . KK^T) -> LT (fp32); P = tril(Gamma . QK^T) -> Ps
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * w + 4 * g + i, col = 16 * ct + c;
+      const float e = (col <= r) ? expf(gl[r] - gl[col]) : 0.f;
+      LT[r * C::LTP + col] = (col < r) ? bl[r] * e * akk[ct][i] : 0.f;
+      Ps[r * C::PP + col] = from_f32<T>((col <= r) ? e * aqk[ct][i] : 0.f);
+    }
+  __syncthreads();
+
+  // P fragments (A operand of P U in the scan; contraction over tokens, KMAP_ACC)
+#pragma unroll
+  for (int k2 = 0; k2 < 2; ++k2) {
+    const T* row = Ps + (16 * w + c) * C::PP + 32 * k2 + 4 * g;
+    store8<T>(ws.pm + ((ch * 4 + w) * 2 + k2) * 512 + lane * 8, ld4x2<T>(row, row + 16));
+  }
+
+  // T = (I + L)^-1, in place.  (a) 16x16 diagonal blocks: lane j of wave w
+  // solves column j of block w by forward substitution.
+  if (lane < 16) {
+    const int j = lane, o = 16 * w;
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float acc = (r == j) ? 1.f : 0.f;
+#pragma unroll
+      for (int i = 0; i < r; ++i) acc -= LT[(o + r) * C::LTP + o + i] * x[i];
+      x[r] = acc;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) LT[(o + r) * C::LTP + o + j] = x[r];
+  }
+  __syncthreads();
+  // (b) block rows a = 1..3:  T_ab = -T_aa * sum_{b<=m<a} L_am T_mb
+  {
+    const int rr = t >> 4, col = t & 15;
+    for (int a = 1; a < 4; ++a) {
+      for (int bb = 0; bb < a; ++bb) {
+        float acc = 0.f;
+        for (int m = bb; m < a; ++m) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            acc += LT[(16 * a + rr) * C::LTP + 16 * m + i] * LT[(16 * m + i) * C::LTP + 16 * bb + col];
+        }
+        Rs[(bb * 16 + rr) * 17 + col] = acc;
+      }
+      __syncthreads();
+      for (int bb = 0; bb < a; ++bb) {
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          acc += LT[(16 * a + rr) * C::LTP + 16 * a + i] * Rs[(bb * 16 + i) * 17 + col];
+        LT[(16 * a + rr) * C::LTP + 16 * bb + col] = -acc;
+      }
+      __syncthreads();
+    }
+  }
+
+  // U~ = T diag(b) V and W = T diag(b gamma) K, rows 16w .. 16w+15
+  f32x4 ut[C::NT], wa[C::NT];
+#pragma unroll
+  for (int n = 0; n < C::NT; ++n) {
+    ut[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    wa[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int k2 = 0; k2 < 2; ++k2) {
+    Frag<T> a1, a2;
+    const float* trow = LT + (16 * w + c) * C::LTP;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int tk = 32 * k2 + kmap_acc(g, j);
+      const float tv = trow[tk];
+      frag_set(a1, j, tv * bl[tk]);
+      frag_set(a2, j, tv * gbl[tk]);
+    }
+#pragma unroll
+    for (int n = 0; n < C::NT; ++n) {
+      const Frag<T> bv = ld4x2<T>(Vg + kg_index<D>(8 * k2 + g, 16 * n + c),
+                                  Vg + kg_index<D>(8 * k2 + 4 + g, 16 * n + c));
+      const Frag<T> bk = ld4x2<T>(Kg + kg_index<D>(8 * k2 + g, 16 * n + c),
+                                  Kg + kg_index<D>(8 * k2 + 4 + g, 16 * n + c));
+      mma(ut[n], a1, bv);
+      mma(wa[n], a2, bk);
+    }
+  }
+  // U~ in accumulator order (the scan uses it as the C operand): [rt][n][lane][4]
+#pragma unroll
+  for (int n = 0; n < C::NT; ++n)
+    *reinterpret_cast<f32x4*>(ws.ut + ((ch * 4 + w) * C::NT + n) * 256 + lane * 4) = ut[n];
+  // -W -> Ks (row layout) -> A fragments with contraction over d (KMAP_ROW)
+#pragma unroll
+  for (int n = 0; n < C::NT; ++n)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Ks[(16 * w + 4 * g + i) * C::KP + 16 * n + c] = from_f32<T>(-wa[n][i]);
+  // K~^T fragments: rows = d, contraction over tokens (KMAP_ACC), scaled by exp(g_C - g)
+  for (int f = w; f < C::NT * 2; f += 4) {
+    const int n = f >> 1, k2 = f & 1;
+    const Frag<T> kk = ld4x2<T>(Kg + kg_index<D>(8 * k2 + g, 16 * n + c),
+                                Kg + kg_index<D>(8 * k2 + 4 + g, 16 * n + c));
+    Frag<T> o;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) frag_set(o, j, to_f32(frag_get<T>(kk, j)) * ekl[32 * k2 + kmap_acc(g, j)]);
+    store8<T>(ws.kt + ((ch * C::NT + n) * 2 + k2) * 512 + lane * 8, o);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int ks = 0; ks < C::KF; ++ks)
+    store8<T>(ws.wn + ((ch * 4 + w) * C::KF + ks) * 512 + lane * 8,
+              load8<T>(Ks + (16 * w + c) * C::KP + 32 * ks + 8 * g));
+}
+
+// ---------------------------------------------------------------- scan ----
+template <typename T, int D, int DVT>
+struct ScanOps {
+  static constexpr int KF = D / 32;
+  static constexpr int NV = DVT / 16;
+  static constexpr int DTW = D / 64;  // 16-row d tiles of the state per wave
+  Frag<T> wn[KF];
+  f32x4 ut[NV];
+  Frag<T> qa[KF];
+  Frag<T> pa[2];
+  Frag<T> kt[DTW][2];
+  f32x4 gam;
+  float gC;
+  int route;
+};
+
+template <typename T, int D, int DVT>
+__device__ __forceinline__ void scan_load(ScanOps<T, D, DVT>& op, const GdnWs<T, D>& ws,
+                                          const T* qh, const int32_t* rt, int64_t bh, int nc,
+                                          int cc, int nv0) {
+  using C = GdnCfg<T, D>;
+  using O = ScanOps<T, D, DVT>;
+  const int lane = lane_id(), w = wave_id();
+  const int g = lane >> 4, c = lane & 15;
+  const int64_t ch = bh * nc + cc;
+#pragma unroll
+  for (int ks = 0; ks < O::KF; ++ks) {
+    op.wn[ks] = load8<T>(ws.wn + ((ch * 4 + w) * C::KF + ks) * 512 + lane * 8);
+    op.qa[ks] = load8<T>(qh + ((int64_t)cc * CHUNK + 16 * w + c) * D + 32 * ks + 8 * g);
+  }
+#pragma unroll
+  for (int n = 0; n < O::NV; ++n)
+    op.ut[n] = *reinterpret_cast<const f32x4*>(ws.ut + ((ch * 4 + w) * C::NT + nv0 + n) * 256 + lane * 4);
+#pragma unroll
+  for (int k2 = 0; k2 < 2; ++k2) op.pa[k2] = load8<T>(ws.pm + ((ch * 4 + w) * 2 + k2) * 512 + lane * 8);
+#pragma unroll
+  for (int x = 0; x < O::DTW; ++x)
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+      op.kt[x][k2] = load8<T>(ws.kt + ((ch * C::NT + w * O::DTW + x) * 2 + k2) * 512 + lane * 8);
+  op.gam = *reinterpret_cast<const f32x4*>(ws.gm + ch * C::GM + 16 * w + 4 * g);
+  op.gC = ws.gm[ch * C::GM + 64];
+  op.route = rt[cc];
+}
+
+template <typename T, typename To, int D, int DVT>
+__global__ void __launch_bounds__(256, 1)
+    k_gdn_scan(const T* __restrict__ q, const int32_t* __restrict__ route, GdnWs<T, D> ws,
+               const float* __restrict__ S_init, To* __restrict__ o_gdn, float* __restrict__ S_final,
+               int H, int L, int G) {
+  using O = ScanOps<T, D, DVT>;
+  constexpr int SPP = D + 16 / (int)sizeof(T);  // pitch of the transposed bf16 state [dv][dk]
+  __shared__ __align__(16) T Sp[2][DVT * SPP];
+  __shared__ __align__(16) T Up[(CHUNK / 4) * DVT * 4];
+
+  const int nc = L / CHUNK;
+  const int nvt = D / DVT;
+  const int total = (int)gridDim.x;
+  const int BH = total / nvt;
+  int logical = blockIdx.x;
+  if ((BH & 7) == 0) logical = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
+  const int64_t bh = logical / nvt;
+  const int vt = logical % nvt;
+  const int b = (int)(bh / H), h = (int)(bh % H);
+  const int grp = (G == 1) ? 0 : h;
+  const int32_t* rt = route + ((int64_t)b * G + grp) * nc;
+  const int nv0 = vt * (DVT / 16);
+  const int dv0 = vt * DVT;
+  const T* qh = q + bh * L * D;
+  To* oh = o_gdn + bh * L * D;
+
+  const int lane = lane_id(), w = wave_id();
+  const int g = lane >> 4, c = lane & 15;
+
+  // fp32 master state: rows d = 16 (w*DTW + x) + 4g + i, columns dv0 + 16n + c
+  f32x4 sm[O::DTW][O::NV];
+#pragma unroll
+  for (int x = 0; x < O::DTW; ++x)
+#pragma unroll
+    for (int n = 0; n < O::NV; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int dk = 16 * (w * O::DTW + x) + 4 * g + i;
+        sm[x][n][i] = S_init ? S_init[(bh * D + dk) * D + dv0 + 16 * n + c] : 0.f;
+      }
+  int sb = 0;
+  auto write_state = [&](int buf) {
+#pragma unroll
+    for (int x = 0; x < O::DTW; ++x)
+#pragma unroll
+      for (int n = 0; n < O::NV; ++n)
+        st4<T>(&Sp[buf][(16 * n + c) * SPP + 16 * (w * O::DTW + x) + 4 * g], sm[x][n][0], sm[x][n][1],
+               sm[x][n][2], sm[x][n][3]);
+  };
+  write_state(0);
+  __syncthreads();
+
+  auto step = [&](const ScanOps<T, D, DVT>& op, int cc) {
+    // S fragments (B operand, contraction over d): shared by U and Q S
+    Frag<T> bs[O::KF][O::NV];
+#pragma unroll
+    for (int ks = 0; ks < O::KF; ++ks)
+#pragma unroll
+      for (int n = 0; n < O::NV; ++n) bs[ks][n] = load8<T>(&Sp[sb][(16 * n + c) * SPP + 32 * ks + 8 * g]);
+    f32x4 u[O::NV], oa[O::NV];
+#pragma unroll
+    for (int n = 0; n < O::NV; ++n) {
+      u[n] = op.ut[n];
+      oa[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int ks = 0; ks < O::KF; ++ks)
+#pragma unroll
+      for (int n = 0; n < O::NV; ++n) {
+        mma(u[n], op.wn[ks], bs[ks][n]);   // U = U~ - W S
+        mma(oa[n], op.qa[ks], bs[ks][n]);  // Q S
+      }
+#pragma unroll
+    for (int n = 0; n < O::NV; ++n) {
+      st4<T>(&Up[kg_index<DVT>(4 * w + g, 16 * n + c)], u[n][0], u[n][1], u[n][2], u[n][3]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) oa[n][i] *= op.gam[i];
+    }
+    __syncthreads();
+    Frag<T> bu[2][O::NV];
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+      for (int n = 0; n < O::NV; ++n)
+        bu[k2][n] = ld4x2<T>(&Up[kg_index<DVT>(8 * k2 + g, 16 * n + c)],
+                             &Up[kg_index<DVT>(8 * k2 + 4 + g, 16 * n + c)]);
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+      for (int n = 0; n < O::NV; ++n) mma(oa[n], op.pa[k2], bu[k2][n]);  // + P U
+#pragma unroll
+    for (int n = 0; n < O::NV; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        oh[((int64_t)cc * CHUNK + 16 * w + 4 * g + i) * D + dv0 + 16 * n + c] = from_f32<To>(oa[n][i]);
+    if (op.route == 1) {  // linear-routed: commit S <- gamma_C S + K~^T U
+#pragma unroll
+      for (int x = 0; x < O::DTW; ++x)
+#pragma unroll
+        for (int n = 0; n < O::NV; ++n) {
+          f32x4 acc = sm[x][n] * op.gC;
+#pragma unroll
+          for (int k2 = 0; k2 < 2; ++k2) mma(acc, op.kt[x][k2], bu[k2][n]);
+          sm[x][n] = acc;
+        }
+      write_state(sb ^ 1);
+      sb ^= 1;
+    }
+    __syncthreads();
+  };
+
+  ScanOps<T, D, DVT> opA, opB;
+  scan_load<T, D, DVT>(opA, ws, qh, rt, bh, nc, 0, nv0);
+  for (int cc = 0; cc < nc; cc += 2) {
+    if (cc + 1 < nc) scan_load<T, D, DVT>(opB, ws, qh, rt, bh, nc, cc + 1, nv0);
+    step(opA, cc);
+    if (cc + 1 < nc) {
+      if (cc + 2 < nc) scan_load<T, D, DVT>(opA, ws, qh, rt, bh, nc, cc + 2, nv0);
+      step(opB, cc + 1);
+    }
+  }
+  if (S_final) {
+#pragma unroll
+    for (int x = 0; x < O::DTW; ++x)
+#pragma unroll
+      for (int n = 0; n < O::NV; ++n)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int dk = 16 * (w * O::DTW + x) + 4 * g + i;
+          S_final[(bh * D + dk) * D + dv0 + 16 * n + c] = sm[x][n][i];
+        }
+  }
+}
+
+template <typename T, typename To, int D>
+hipError_t launch_gdn(const T* q, const T* k, const T* v, const float* alpha, const float* beta,
+                      const int32_t* route, const float* S_init, To* o_gdn, float* S_final, void* wsp,
+                      int B, int H, int L, int G, hipStream_t st_prep, hipStream_t st_scan,
+                      hipEvent_t prep_done, void (*prof)(int, hipStream_t, int)) {
+  using C = GdnCfg<T, D>;
+  constexpr int DVT = 32;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)k_gdn_prep<T, D>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::PREP_LDS);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int nc = L / CHUNK;
+  const int64_t nch = (int64_t)B * H * nc;
+  GdnWs<T, D> ws = carve<T, D>(wsp, nch);
+  if (prof) prof(KID_GDN_PREP, st_prep, 0);
+  hipLaunchKernelGGL((k_gdn_prep<T, D>), dim3((unsigned)nch), dim3(256), C::PREP_LDS, st_prep, q, k, v,
+                     alpha, beta, ws, L);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (prof) prof(KID_GDN_PREP, st_prep, 1);
+  if (st_scan != st_prep) {
+    e = hipEventRecord(prep_done, st_prep);
+    if (e != hipSuccess) return e;
+    e = hipStreamWaitEvent(st_scan, prep_done, 0);
+    if (e != hipSuccess) return e;
+  }
+  if (prof) prof(KID_GDN_SCAN, st_scan, 0);
+  hipLaunchKernelGGL((k_gdn_scan<T, To, D, DVT>), dim3((unsigned)(B * H * (D / DVT))), dim3(256), 0,
+                     st_scan, q, route, ws, S_init, o_gdn, S_final, H, L, G);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (prof) prof(KID_GDN_SCAN, st_scan, 1);
+  return hipSuccess;
+}
+
+#define INST(T, To, D)                                                                            \
+  template hipError_t launch_gdn<T, To, D>(const T*, const T*, const T*, const float*, const float*, \
+                                           const int32_t*, const float*, To*, float*, void*, int,  \
+                                           int, int, int, hipStream_t, hipStream_t, hipEvent_t,     \
+                                           void (*)(int, hipStream_t, int));
+INST(float, float, 64)
+INST(float, float, 128)
+INST(float, bf16, 64)
+INST(float, bf16, 128)
+INST(bf16, float, 64)
+INST(bf16, float, 128)
+INST(bf16, bf16, 64)
+INST(bf16, bf16, 128)
+#undef INST
+
+}  // namespace natsl

@@ -1,0 +1,68 @@
+// Host-side launch helpers of the NAtS-L kernels (internal to the library).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace natsl {
+
+typedef __bf16 bf16;
+
+// kernel ids for the optional launch timing
+enum {
+  KID_ROUTE = 0,
+  KID_COMPACT,
+  KID_GDN_PREP,
+  KID_GDN_SCAN,
+  KID_SOFTMAX,
+  KID_MERGE,
+  KID_DECODE_ROUTE,
+  KID_DECODE_GDN,
+  KID_DECODE_ATTN,
+  KID_DECODE_COMBINE,
+  KID_DECODE_COMMIT,
+  KID_COUNT
+};
+
+template <typename T>
+hipError_t launch_route(const T* x, const float* w, const float* bsc, int B, int L, int d, int G,
+                        int32_t* route_out, float* scores, hipStream_t st);
+hipError_t launch_compact(const int32_t* route_in, int32_t* route_out, int B, int G, int nc,
+                          int32_t* sel_idx, int32_t* nsel_before, hipStream_t st);
+
+template <typename Tq, typename Tb, int D>
+hipError_t launch_merge(const Tq* q, const Tb* o_sm, const Tb* o_gdn, const float* w_mix, int64_t hs,
+                        const float* g_sm, const float* g_lin, Tq* out, int B, int H, int L,
+                        float eps, hipStream_t st);
+
+template <typename T, typename To, int D>
+hipError_t launch_softmax_masked(const T* q, const T* k, const T* v, const int32_t* sel_idx,
+                                 const int32_t* nsel_before, To* o_sm, float* lse, int B, int H,
+                                 int L, int G, float scale, hipStream_t st);
+
+size_t gdn_ws_bytes(int io_is_bf16, int D, int64_t nch);
+template <typename T, typename To, int D>
+hipError_t launch_gdn(const T* q, const T* k, const T* v, const float* alpha, const float* beta,
+                      const int32_t* route, const float* S_init, To* o_gdn, float* S_final, void* ws,
+                      int B, int H, int L, int G, hipStream_t st_prep, hipStream_t st_scan,
+                      hipEvent_t prep_done, void (*prof)(int, hipStream_t, int));
+
+struct DecodeLaunch {
+  int B, H, G, d, cap;
+  float scale, eps;
+  const void *x, *q, *k, *v;
+  const float *alpha, *beta, *w_score, *b_score, *w_mix;
+  int64_t w_mix_hs;
+  const float *g_sm, *g_lin;
+  void *k_cache, *v_cache;
+  int32_t *n_committed, *n_open, *err_flag, *route_out;
+  float *S_carry, *S_work, *x_sum;
+  void* out;
+  float *o_sm_dbg, *o_gdn_dbg;
+};
+size_t decode_ws_bytes(int B, int H, int G, int D, int cap);
+template <typename T, int D>
+hipError_t launch_decode(const DecodeLaunch& a, void* ws, hipStream_t st,
+                         void (*prof)(int, hipStream_t, int));
+
+}  // namespace natsl

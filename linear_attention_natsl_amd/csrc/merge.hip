@@ -1,0 +1,95 @@
+// Output merging: "Technische Samenvatting: Neural Attention Search Linear
+// (NAtS-L)", Kernmechanismen 4 -- each branch output is RMS-normalised and the
+// two are added with weights generated from the query.
+//   n_x = o_x / sqrt(mean(o_x^2) + eps) * g_x,  (w_sm, w_lin) = softmax(q W_mix),
+//   out = w_sm n_sm + w_lin n_lin.
+// Bandwidth-bound: D/8 lanes per token, 8 elements per lane (16-byte bf16
+// loads), reductions across the token's lanes with xor shuffles.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace natsl {
+
+template <typename Tq, typename Tb, typename To, int D>
+__global__ void __launch_bounds__(256) k_merge(const Tq* __restrict__ q, const Tb* __restrict__ o_sm,
+                                               const Tb* __restrict__ o_gdn,
+                                               const float* __restrict__ w_mix, int64_t wmix_hs,
+                                               const float* __restrict__ g_sm,
+                                               const float* __restrict__ g_lin, To* __restrict__ out,
+                                               int H, int L, float eps, int64_t ntok) {
+  constexpr int LPT = D / 8;  // lanes per token
+  const int64_t gtid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t tok = gtid / LPT;
+  const int sub = (int)(gtid % LPT);
+  const bool valid = tok < ntok;
+  const int64_t t = valid ? tok : 0;
+  const int h = (int)((t / L) % H);
+  const int col = sub * 8;
+  float qv[8], a[8], b[8];
+  load8f<Tq>(q + t * D + col, qv);
+  load8f<Tb>(o_sm + t * D + col, a);
+  load8f<Tb>(o_gdn + t * D + col, b);
+  const float* wm = w_mix + (int64_t)h * wmix_hs;
+  float ssa = 0.f, ssb = 0.f, z0 = 0.f, z1 = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    ssa += a[j] * a[j];
+    ssb += b[j] * b[j];
+    z0 += qv[j] * wm[(col + j) * 2];
+    z1 += qv[j] * wm[(col + j) * 2 + 1];
+  }
+#pragma unroll
+  for (int m = LPT / 2; m >= 1; m >>= 1) {
+    ssa = wave_sum_xor(ssa, m);
+    ssb = wave_sum_xor(ssb, m);
+    z0 = wave_sum_xor(z0, m);
+    z1 = wave_sum_xor(z1, m);
+  }
+  const float ra = 1.0f / sqrtf(ssa * (1.0f / D) + eps);
+  const float rb = 1.0f / sqrtf(ssb * (1.0f / D) + eps);
+  const float zm = fmaxf(z0, z1);
+  const float e0 = expf(z0 - zm), e1 = expf(z1 - zm);
+  const float inv = 1.0f / (e0 + e1);
+  const float w0 = e0 * inv * ra, w1 = e1 * inv * rb;
+  float o[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float gs = g_sm ? g_sm[col + j] : 1.f;
+    const float gl = g_lin ? g_lin[col + j] : 1.f;
+    o[j] = w0 * a[j] * gs + w1 * b[j] * gl;
+  }
+  if (valid) {
+    Frag<To> f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) frag_set(f, j, o[j]);
+    store8<To>(out + t * D + col, f);
+  }
+}
+
+template <typename Tq, typename Tb, int D>
+hipError_t launch_merge(const Tq* q, const Tb* o_sm, const Tb* o_gdn, const float* w_mix, int64_t hs,
+                        const float* g_sm, const float* g_lin, Tq* out, int B, int H, int L,
+                        float eps, hipStream_t st) {
+  const int64_t ntok = (int64_t)B * H * L;
+  const int64_t threads = ntok * (D / 8);
+  const int64_t blocks = (threads + 255) / 256;
+  hipLaunchKernelGGL((k_merge<Tq, Tb, Tq, D>), dim3((unsigned)blocks), dim3(256), 0, st, q, o_sm,
+                     o_gdn, w_mix, hs, g_sm, g_lin, out, H, L, eps, ntok);
+  return hipGetLastError();
+}
+
+#define INST(Tq, Tb, D)                                                                          \
+  template hipError_t launch_merge<Tq, Tb, D>(const Tq*, const Tb*, const Tb*, const float*,     \
+                                              int64_t, const float*, const float*, Tq*, int, int, \
+                                              int, float, hipStream_t);
+INST(float, float, 64)
+INST(float, float, 128)
+INST(float, bf16, 64)
+INST(float, bf16, 128)
+INST(bf16, float, 64)
+INST(bf16, float, 128)
+INST(bf16, bf16, 64)
+INST(bf16, bf16, 128)
+#undef INST
+
+}  // namespace natsl

@@ -1,0 +1,114 @@
+// Router and compaction.
+//
+// Router: "Technische Samenvatting: Neural Attention Search Linear (NAtS-L)",
+// Kernmechanismen 1 -- every 64-token chunk is mean-pooled and scored by a
+// linear layer, one score per operation; the higher score picks the chunk's
+// operation (ties: softmax, the first maximum).
+// Compaction: Kernmechanismen 3 -- only the softmax-routed chunks' KV is kept
+// for the softmax operation; in prefill that is an ordered index list.
+//
+// The router is bandwidth-bound: one pass over x.  One workgroup per (b, c)
+// streams the chunk's 64 x d values with 16-byte loads (each thread owns 8
+// columns), sums in fp32 in a fixed order, stores the mean in LDS, and the
+// four waves form the 2G dot products with W_score (fixed-order wave
+// reductions), so the result is deterministic.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace natsl {
+
+template <typename T>
+__global__ void __launch_bounds__(256) k_route(const T* __restrict__ x, const float* __restrict__ w,
+                                               const float* __restrict__ bsc, int L, int d, int G,
+                                               int nc, int32_t* __restrict__ route_out,
+                                               float* __restrict__ scores) {
+  extern __shared__ float s_mean[];  // [d]
+  const int c = blockIdx.x, b = blockIdx.y;
+  const T* xc = x + ((int64_t)b * L + (int64_t)c * CHUNK) * d;
+  for (int col0 = threadIdx.x * 8; col0 < d; col0 += 256 * 8) {
+    float acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+#pragma unroll 8
+    for (int r = 0; r < CHUNK; ++r) {
+      float v[8];
+      load8f<T>(xc + (int64_t)r * d + col0, v);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] += v[j];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s_mean[col0 + j] = acc[j] * (1.0f / CHUNK);
+  }
+  __syncthreads();
+  const int lane = lane_id(), wv = wave_id();
+  for (int o = wv; o < 2 * G; o += 4) {
+    float p = 0.f;
+    for (int j = lane; j < d; j += 64) p += s_mean[j] * w[(int64_t)j * 2 * G + o];
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) p = wave_sum_xor(p, m);
+    if (bsc) p += bsc[o];
+    if (lane == 0) s_mean[d + o] = p;  // scores live after the mean
+  }
+  __syncthreads();
+  for (int gg = threadIdx.x; gg < G; gg += 256) {
+    const float s0 = s_mean[d + 2 * gg], s1 = s_mean[d + 2 * gg + 1];
+    const int64_t idx = ((int64_t)b * G + gg) * nc + c;
+    route_out[idx] = (s0 >= s1) ? 0 : 1;
+    if (scores) {
+      scores[idx * 2] = s0;
+      scores[idx * 2 + 1] = s1;
+    }
+  }
+}
+
+// One wave per (b, g): ordered list of softmax chunks and exclusive prefix counts.
+__global__ void __launch_bounds__(64) k_compact(const int32_t* __restrict__ route_in,
+                                                int32_t* __restrict__ route_out, int nc,
+                                                int32_t* __restrict__ sel_idx,
+                                                int32_t* __restrict__ nsel_before) {
+  const int bg = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int32_t* r = route_in + (int64_t)bg * nc;
+  int32_t* ro = route_out + (int64_t)bg * nc;
+  int32_t* sel = sel_idx + (int64_t)bg * nc;
+  int32_t* nsb = nsel_before + (int64_t)bg * (nc + 1);
+  int base = 0;
+  for (int c0 = 0; c0 < nc; c0 += 64) {
+    const int c = c0 + lane;
+    const int rv = (c < nc) ? r[c] : 1;
+    const bool is_sm = (c < nc) && (rv == 0);
+    const uint64_t mask = __ballot(is_sm);
+    const int before = __popcll(mask & ((1ull << lane) - 1ull));
+    if (c < nc) {
+      if (ro != r) ro[c] = rv;
+      nsb[c] = base + before;
+      if (is_sm) sel[base + before] = c;
+    }
+    base += __popcll(mask);
+  }
+  for (int c = base + lane; c < nc; c += 64) sel[c] = -1;
+  if (lane == 0) nsb[nc] = base;
+}
+
+template <typename T>
+hipError_t launch_route(const T* x, const float* w, const float* bsc, int B, int L, int d, int G,
+                        int32_t* route_out, float* scores, hipStream_t st) {
+  const int nc = L / CHUNK;
+  const size_t lds = (size_t)(d + 2 * G) * sizeof(float);
+  hipLaunchKernelGGL(k_route<T>, dim3(nc, B), dim3(256), lds, st, x, w, bsc, L, d, G, nc, route_out,
+                     scores);
+  return hipGetLastError();
+}
+template hipError_t launch_route<float>(const float*, const float*, const float*, int, int, int, int,
+                                        int32_t*, float*, hipStream_t);
+template hipError_t launch_route<bf16>(const bf16*, const float*, const float*, int, int, int, int,
+                                       int32_t*, float*, hipStream_t);
+
+hipError_t launch_compact(const int32_t* route_in, int32_t* route_out, int B, int G, int nc,
+                          int32_t* sel_idx, int32_t* nsel_before, hipStream_t st) {
+  hipLaunchKernelGGL(k_compact, dim3(B * G), dim3(64), 0, st, route_in, route_out, nc, sel_idx,
+                     nsel_before);
+  return hipGetLastError();
+}
+
+}  // namespace natsl

@@ -1,0 +1,337 @@
+// Softmax branch: "Technische Samenvatting: Neural Attention Search Linear
+// (NAtS-L)", Kernmechanismen 3 -- inside every chunk both correlations are
+// computed, and the softmax operation keeps only the KV of the chunks routed to
+// it.  A query of chunk c therefore attends to the tokens of the softmax chunks
+// before c (the compacted list sel_idx[0 .. nsel_before[c])) plus the causal
+// prefix of its own chunk.
+//
+// Flash-style online softmax on MFMA (gfx950, wave64):
+//   * one workgroup = 4 waves = 128 queries (two chunks c0 = 2p, c1 = 2p + 1);
+//     wave w owns queries 32w .. 32w+31 of the block;
+//   * the key loop walks the compacted chunk list, then c0, then c1; every key
+//     tile is exactly one 64-token chunk (contiguous 16 KiB bf16 rows, so the
+//     gather through sel_idx costs nothing in coalescing);
+//   * per tile a wave is FULL (all keys visible), DIAG (causal mask inside its
+//     own chunk) or SKIP (c1's queries and c0's tile when c0 is linear-routed;
+//     c0's queries never see c1);
+//   * S^T = K Q^T with K from LDS (A operand) and Q held in registers
+//     (B operand); its accumulator layout (lane = query, 4 keys per lane) is
+//     directly the B operand of O^T = V^T P^T, so P never leaves registers and
+//     the per-query rescale is lane-local;
+//   * V is stored in LDS in the key-group layout (4 keys of one column in 8
+//     bytes, swizzled) that the A operand of V^T needs;
+//   * K/V tiles are double-buffered: the next tile's global loads are in flight
+//     while the current tile is computed;
+//   * blocks are issued longest-first (later query chunks see more keys), and
+//     on the 8 XCDs every XCD serves a fixed set of heads so the K/V tiles those
+//     blocks stream stay in that XCD's L2.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace natsl {
+
+template <typename T, int D>
+struct SmCfg {
+  static constexpr int KP = D + 16 / (int)sizeof(T);   // K row pitch (elements), 16 B pad
+  static constexpr int KTILE = CHUNK * KP;              // elements
+  static constexpr int VTILE = (CHUNK / 4) * D * 4;     // elements (key-group layout)
+  static constexpr int BUF = KTILE + VTILE;
+  static constexpr int LDS_BYTES = 2 * BUF * (int)sizeof(T);
+  static constexpr int KF = D / 32;                     // contraction steps over D
+  static constexpr int KLOADS = (CHUNK * D / 8) / 256;  // 8-element K loads per thread
+  static constexpr int VTASKS = (CHUNK / 4) * (D / 8);  // (key group, 8 columns) tasks
+  static constexpr int VT = (VTASKS + 255) / 256;
+};
+
+template <typename T> __device__ __forceinline__ Frag<T> load4x2(const T* p0, const T* p1);
+template <> __device__ __forceinline__ Frag<bf16> load4x2<bf16>(const bf16* p0, const bf16* p1) {
+  bf16x4 a = *reinterpret_cast<const bf16x4*>(p0);
+  bf16x4 b = *reinterpret_cast<const bf16x4*>(p1);
+  Frag<bf16> f;
+  f.v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return f;
+}
+template <> __device__ __forceinline__ Frag<float> load4x2<float>(const float* p0, const float* p1) {
+  f32x4 a = *reinterpret_cast<const f32x4*>(p0);
+  f32x4 b = *reinterpret_cast<const f32x4*>(p1);
+  Frag<float> f;
+  f.v[0] = a[0]; f.v[1] = a[1]; f.v[2] = a[2]; f.v[3] = a[3];
+  f.v[4] = b[0]; f.v[5] = b[1]; f.v[6] = b[2]; f.v[7] = b[3];
+  return f;
+}
+
+// store 4 elements (one per token of a key group) for one column
+template <typename T> __device__ __forceinline__ void store_col4(T* p, T a, T b, T c, T d);
+template <> __device__ __forceinline__ void store_col4<bf16>(bf16* p, bf16 a, bf16 b, bf16 c, bf16 d) {
+  bf16x4 v = {a, b, c, d};
+  *reinterpret_cast<bf16x4*>(p) = v;
+}
+template <> __device__ __forceinline__ void store_col4<float>(float* p, float a, float b, float c, float d) {
+  f32x4 v = {a, b, c, d};
+  *reinterpret_cast<f32x4*>(p) = v;
+}
+
+template <typename T, int D>
+struct TileRegs {
+  Frag<T> k[SmCfg<T, D>::KLOADS];
+  Frag<T> v[SmCfg<T, D>::VT][4];
+};
+
+template <typename T, int D>
+__device__ __forceinline__ void tile_gload(TileRegs<T, D>& r, const T* kbase, const T* vbase) {
+  using C = SmCfg<T, D>;
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < C::KLOADS; ++i) {
+    const int e = t + 256 * i;
+    const int row = e / (D / 8), col = (e % (D / 8)) * 8;
+    r.k[i] = load8<T>(kbase + row * D + col);
+  }
+#pragma unroll
+  for (int i = 0; i < C::VT; ++i) {
+    const int task = t + 256 * i;
+    if (task < C::VTASKS) {
+      const int kg = task / (D / 8), col = (task % (D / 8)) * 8;
+#pragma unroll
+      for (int tk = 0; tk < 4; ++tk) r.v[i][tk] = load8<T>(vbase + (4 * kg + tk) * D + col);
+    }
+  }
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void tile_sstore(const TileRegs<T, D>& r, T* buf) {
+  using C = SmCfg<T, D>;
+  const int t = threadIdx.x;
+  T* ks = buf;
+  T* vs = buf + C::KTILE;
+#pragma unroll
+  for (int i = 0; i < C::KLOADS; ++i) {
+    const int e = t + 256 * i;
+    const int row = e / (D / 8), col = (e % (D / 8)) * 8;
+    store8<T>(ks + row * C::KP + col, r.k[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < C::VT; ++i) {
+    const int task = t + 256 * i;
+    if (task < C::VTASKS) {
+      const int kg = task / (D / 8), col = (task % (D / 8)) * 8;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        store_col4<T>(vs + kg_index<D>(kg, col + j), frag_get<T>(r.v[i][0], j),
+                      frag_get<T>(r.v[i][1], j), frag_get<T>(r.v[i][2], j),
+                      frag_get<T>(r.v[i][3], j));
+    }
+  }
+}
+
+enum { MODE_SKIP = 0, MODE_FULL = 1, MODE_DIAG = 2 };
+
+template <typename T, typename To, int D>
+__global__ void __launch_bounds__(256, 2)
+    k_softmax_masked(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+                     const int32_t* __restrict__ sel_idx, const int32_t* __restrict__ nsel_before,
+                     To* __restrict__ o_sm, float* __restrict__ lse, int H, int L, int G,
+                     float scale_log2) {
+  using C = SmCfg<T, D>;
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  T* smem = reinterpret_cast<T*>(smem_raw);
+
+  const int nc = L / CHUNK;
+  const int nb = (nc + 1) / 2;
+  const int BH = (int)(gridDim.x / nb);
+  const int p = blockIdx.x;
+  int qblk, bh;
+  if ((BH & 7) == 0) {
+    const int xcd = p & 7, slot = p >> 3, hpx = BH >> 3;
+    qblk = nb - 1 - slot / hpx;
+    bh = (slot % hpx) * 8 + xcd;
+  } else {
+    qblk = nb - 1 - p / BH;
+    bh = p % BH;
+  }
+  const int b = bh / H, h = bh % H;
+  const int grp = (G == 1) ? 0 : h;
+  const int32_t* sel = sel_idx + ((int64_t)b * G + grp) * nc;
+  const int32_t* nsbp = nsel_before + ((int64_t)b * G + grp) * (nc + 1);
+  const int c0 = 2 * qblk, c1 = c0 + 1;
+  const bool has_c1 = c1 < nc;
+  const int nsb = nsbp[c0];
+  const bool c0_sm = nsbp[c0 + 1] > nsb;
+  const int ntiles = nsb + 1 + (has_c1 ? 1 : 0);
+
+  const int lane = lane_id(), w = wave_id();
+  const int g = lane >> 4, c = lane & 15;
+  const bool my_c1 = w >= 2;
+  const bool active = !my_c1 || has_c1;
+  const int64_t head_off = (int64_t)bh * L * D;
+  const T* qh = q + head_off;
+  const T* kh = k + head_off;
+  const T* vh = v + head_off;
+
+  // Q fragments: B operand of S^T = K Q^T (column = query, rows = d)
+  Frag<T> qf[2][C::KF];
+  const int qtok0 = c0 * CHUNK + 32 * w;
+#pragma unroll
+  for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+    for (int ks = 0; ks < C::KF; ++ks) {
+      if (active) qf[qs][ks] = load8<T>(qh + (int64_t)(qtok0 + 16 * qs + c) * D + 32 * ks + 8 * g);
+      else qf[qs][ks] = load8<T>(qh + 32 * ks + 8 * g);  // any in-bounds row; unused
+    }
+
+  f32x4 o[D / 16][2];
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) o[dt][qs] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[2] = {-INFINITY, -INFINITY};
+  float l_run[2] = {0.f, 0.f};
+
+  auto tile_chunk = [&](int it) -> int { return it < nsb ? sel[it] : (it == nsb ? c0 : c1); };
+
+  TileRegs<T, D> pre;
+  {
+    const int kc = tile_chunk(0);
+    tile_gload<T, D>(pre, kh + (int64_t)kc * CHUNK * D, vh + (int64_t)kc * CHUNK * D);
+    tile_sstore<T, D>(pre, smem);
+  }
+  __syncthreads();
+
+  const int qrow_base = 32 * (w & 1);  // query row inside its own chunk, minus 16qs + c
+  for (int it = 0; it < ntiles; ++it) {
+    const bool more = it + 1 < ntiles;
+    if (more) {
+      const int kc = tile_chunk(it + 1);
+      tile_gload<T, D>(pre, kh + (int64_t)kc * CHUNK * D, vh + (int64_t)kc * CHUNK * D);
+    }
+    int mode;
+    if (it < nsb) mode = MODE_FULL;
+    else if (it == nsb) mode = my_c1 ? (c0_sm ? MODE_FULL : MODE_SKIP) : MODE_DIAG;
+    else mode = my_c1 ? MODE_DIAG : MODE_SKIP;
+    if (!active) mode = MODE_SKIP;
+
+    if (mode != MODE_SKIP) {
+      const T* ks_lds = smem + (it & 1) * C::BUF;
+      const T* vs_lds = ks_lds + C::KTILE;
+      f32x4 s[4][2];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int qs = 0; qs < 2; ++qs) s[kt][qs] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < C::KF; ++ks)
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          const Frag<T> a = load8<T>(ks_lds + (16 * kt + c) * C::KP + 32 * ks + 8 * g);
+#pragma unroll
+          for (int qs = 0; qs < 2; ++qs) mma(s[kt][qs], a, qf[qs][ks]);
+        }
+
+      Frag<T> pf[2][2];
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs) {
+        const int qrow = qrow_base + 16 * qs + c;
+        float mt = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float z = s[kt][qs][i] * scale_log2;
+            if (mode == MODE_DIAG && (16 * kt + 4 * g + i) > qrow) z = -INFINITY;
+            s[kt][qs][i] = z;
+            mt = fmaxf(mt, z);
+          }
+        mt = wave_max_xor(mt, 16);
+        mt = wave_max_xor(mt, 32);
+        const float m_new = fmaxf(m_run[qs], mt);
+        const float alpha = exp2f(m_run[qs] - m_new);
+        m_run[qs] = m_new;
+        float ls = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float pv = exp2f(s[kt][qs][i] - m_new);
+            s[kt][qs][i] = pv;
+            ls += pv;
+          }
+        l_run[qs] = l_run[qs] * alpha + ls;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) o[dt][qs] *= alpha;
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            frag_set(pf[qs][k2], j, s[2 * k2][qs][j]);
+            frag_set(pf[qs][k2], 4 + j, s[2 * k2 + 1][qs][j]);
+          }
+      }
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          const Frag<T> a = load4x2<T>(vs_lds + kg_index<D>(8 * k2 + g, 16 * dt + c),
+                                       vs_lds + kg_index<D>(8 * k2 + 4 + g, 16 * dt + c));
+#pragma unroll
+          for (int qs = 0; qs < 2; ++qs) mma(o[dt][qs], a, pf[qs][k2]);
+        }
+    }
+    if (more) tile_sstore<T, D>(pre, smem + ((it + 1) & 1) * C::BUF);
+    __syncthreads();
+  }
+
+  if (!active) return;
+#pragma unroll
+  for (int qs = 0; qs < 2; ++qs) {
+    float lt = l_run[qs];
+    lt = wave_sum_xor(lt, 16);
+    lt = wave_sum_xor(lt, 32);
+    const float inv = 1.0f / lt;
+    const int64_t tok = qtok0 + 16 * qs + c;
+    To* orow = o_sm + head_off + tok * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      float vals[4] = {o[dt][qs][0] * inv, o[dt][qs][1] * inv, o[dt][qs][2] * inv,
+                       o[dt][qs][3] * inv};
+      store4f<To>(orow + 16 * dt + 4 * g, vals);
+    }
+    if (lse && g == 0) lse[(int64_t)bh * L + tok] = (m_run[qs] + log2f(lt)) * LN2;
+  }
+}
+
+template <typename T, typename To, int D>
+hipError_t launch_softmax_masked(const T* q, const T* k, const T* v, const int32_t* sel_idx,
+                                 const int32_t* nsel_before, To* o_sm, float* lse, int B, int H,
+                                 int L, int G, float scale, hipStream_t st) {
+  using C = SmCfg<T, D>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)k_softmax_masked<T, To, D>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int nc = L / CHUNK;
+  const int nb = (nc + 1) / 2;
+  const int64_t grid = (int64_t)B * H * nb;
+  hipLaunchKernelGGL((k_softmax_masked<T, To, D>), dim3((unsigned)grid), dim3(256), C::LDS_BYTES,
+                     st, q, k, v, sel_idx, nsel_before, o_sm, lse, H, L, G, scale * LOG2E);
+  return hipGetLastError();
+}
+
+#define INST(T, To, D)                                                                         \
+  template hipError_t launch_softmax_masked<T, To, D>(const T*, const T*, const T*,            \
+                                                      const int32_t*, const int32_t*, To*,     \
+                                                      float*, int, int, int, int, float,       \
+                                                      hipStream_t);
+INST(float, float, 64)
+INST(float, float, 128)
+INST(float, bf16, 64)
+INST(float, bf16, 128)
+INST(bf16, float, 64)
+INST(bf16, float, 128)
+INST(bf16, bf16, 64)
+INST(bf16, bf16, 128)
+#undef INST
+
+}  // namespace natsl

@@ -137,12 +137,24 @@ def key_mask(route_c, L, chunk=CHUNK):
     return (s <= t) & ((cs == ct) | (rs == SM))
 
 
-def softmax_branch(q, k, v, route_bgc, scale=None, chunk=CHUNK, with_lse=False):
+def block_mask(route_c, t0, t1, chunk=CHUNK):
+    """Rows t0..t1-1 of key_mask, restricted to keys 0..t1-1."""
+    t = np.arange(t0, t1)[:, None]
+    s = np.arange(t1)[None, :]
+    cs, ct = s // chunk, t // chunk
+    rc = np.asarray(route_c)
+    rs = np.where(cs < len(rc), rc[np.minimum(cs, len(rc) - 1)], LIN)
+    return (s <= t) & ((cs == ct) | (rs == SM))
+
+
+def softmax_branch(q, k, v, route_bgc, scale=None, chunk=CHUNK, with_lse=False, query_blocks=None):
     """Naive masked two-pass softmax attention, one 64-row query block at a
     time (rows are independent, so blocking changes nothing).
 
     q, k [B,H,L,Dk]; v [B,H,L,Dv]; route_bgc [B,G,Nc] -> o_sm [B,H,L,Dv]
-    (and the natural-log logsumexp [B,H,L] of the scaled scores if asked)."""
+    (and the natural-log logsumexp [B,H,L] of the scaled scores if asked).
+    query_blocks, if given, lists the 64-row query blocks to compute; the
+    other rows are left at zero (used to sample very long sequences)."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, H, L, Dk = q.shape
     G = route_bgc.shape[1]
@@ -153,10 +165,10 @@ def softmax_branch(q, k, v, route_bgc, scale=None, chunk=CHUNK, with_lse=False):
     for b in range(B):
         for g in range(G):
             heads = [h for h in range(H) if group_of_head(h, H, G) == g]
-            mask = key_mask(route_bgc[b, g], L, chunk)
-            for t0 in range(0, L, chunk):
+            blocks = range(0, L, chunk) if query_blocks is None else [c * chunk for c in query_blocks]
+            for t0 in blocks:
                 t1 = min(L, t0 + chunk)
-                m = mask[t0:t1, :t1]  # keys past the block end are never visible
+                m = block_mask(route_bgc[b, g], t0, t1, chunk)  # keys past t1 are never visible
                 z = scale * np.einsum("hqd,hkd->hqk", q[b, heads, t0:t1], k[b, heads, :t1])
                 z = np.where(m[None], z, -np.inf)
                 zmax = z.max(axis=-1, keepdims=True)

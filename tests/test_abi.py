@@ -1,0 +1,172 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/natsl.h declares, and rejects bad arguments with the documented
+status before anything is enqueued (the fake device pointers used here are
+never dereferenced because validation fails first)."""
+import ctypes as C
+import os
+import re
+import threading
+
+import pytest
+
+import linear_attention_natsl_amd as N
+
+ROOT = os.path.abspath(os.path.join(os.path.dirname(__file__), ".."))
+HDR = os.path.join(ROOT, "include", "natsl.h")
+FAKE = 0x10000  # stands in for a device pointer; never dereferenced
+
+# Every call below must fail validation before anything is enqueued.  As a
+# safety net these fake-pointer tests never run where a GPU is visible.
+pytestmark = pytest.mark.skipif(
+    __import__("torch").cuda.is_available(), reason="fake-pointer validation tests run without a GPU only")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(N.LIB_PATH):
+        from linear_attention_natsl_amd import build
+        build.build()
+    return N.lib()
+
+
+def declared():
+    src = open(HDR).read()
+    return sorted(set(re.findall(r"^\s*(?:natsl_status|int|const char\*)\s+(natsl_\w+)\s*\(", src, re.M)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(L, n), f"{n} not exported"
+    assert set(names) == set(N.EXPORTS)
+
+
+def test_version(L):
+    assert N.version() == 100
+
+
+def good(io=N.BF16):
+    return N.dims(2, 4, 256, 128, 256, io)
+
+
+@pytest.mark.parametrize("mut,status", [
+    (lambda d: setattr(d, "chunk", 32), 2),
+    (lambda d: setattr(d, "Dv", 64), 2),
+    (lambda d: (setattr(d, "Dk", 96), setattr(d, "Dv", 96)), 2),
+    (lambda d: setattr(d, "L", 100), 2),
+    (lambda d: setattr(d, "L", 0), 2),
+    (lambda d: setattr(d, "route_groups", 3), 2),
+    (lambda d: setattr(d, "H", 0), 1),
+    (lambda d: setattr(d, "B", -1), 1),
+    (lambda d: setattr(d, "io", 7), 1),
+])
+def test_dims_validation(L, mut, status):
+    d = good()
+    mut(d)
+    n = C.c_size_t(0)
+    assert L.natsl_workspace_size(N.ENTRY_FORWARD, C.byref(d), C.byref(n)) == status
+    assert L.natsl_last_error()
+
+
+def test_route_validation(L):
+    d = good()
+    # x, w_score, b_score, route_in(NULL), route_out, sel_idx, nsel_before, scores, stream
+    args = [FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, None]
+    assert L.natsl_route(None, *args) == 1
+    bad = list(args)
+    bad[0] = None  # x without route_in
+    assert L.natsl_route(C.byref(d), *bad) == 1 and b"x" in L.natsl_last_error()
+    d.d_model = 12  # router input width must be a multiple of 8
+    assert L.natsl_route(C.byref(d), *args) == 2
+    d.d_model = 256
+    bad = list(args)
+    bad[5] = None  # sel_idx
+    assert L.natsl_route(C.byref(d), *bad) == 1 and b"sel_idx" in L.natsl_last_error()
+    bad[3] = FAKE  # forced routes still need the outputs
+    assert L.natsl_route(C.byref(d), *bad) == 1
+
+
+def test_gdn_workspace_checks(L):
+    d = good()
+    need = N.workspace_size(N.ENTRY_GDN_CHUNK, d)
+    assert need > 0
+    base = [C.byref(d)] + [FAKE] * 8 + [N.F32, None]
+    assert L.natsl_gdn_chunk(*base, None, need, None) == 3
+    assert L.natsl_gdn_chunk(*base, FAKE + 8, need, None) == 3  # misaligned
+    assert L.natsl_gdn_chunk(*base, FAKE, need - 1, None) == 3
+    assert b"too small" in L.natsl_last_error()
+    b2 = list(base)
+    b2[6] = None  # route (base = dims, q, k, v, alpha, beta, route, S_init, o_gdn, o_dtype, S_final)
+    assert L.natsl_gdn_chunk(*b2, FAKE, need, None) == 1
+    b3 = list(base)
+    b3[9] = 5  # bad o_dtype
+    assert L.natsl_gdn_chunk(*b3, FAKE, need, None) == 1
+
+
+def test_softmax_and_merge_validation(L):
+    d = good()
+    assert L.natsl_softmax_masked(C.byref(d), FAKE, FAKE, FAKE, None, FAKE, FAKE, 0, None, None, 0, None) == 1
+    assert L.natsl_softmax_masked(C.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 9, None, None, 0, None) == 1
+    assert L.natsl_merge(C.byref(d), FAKE, FAKE, FAKE, 0, None, 0, None, None, FAKE, None) == 1
+    assert L.natsl_merge(C.byref(d), FAKE, FAKE, FAKE, 0, FAKE, -2, None, None, FAKE, None) == 1
+
+
+def test_forward_validation(L):
+    d = good()
+    a = N.ForwardArgs()
+    assert L.natsl_forward(C.byref(d), None, FAKE, 1 << 30, None) == 1
+    a.q = a.k = a.v = a.alpha = a.beta = a.w_mix = a.out = FAKE
+    assert L.natsl_forward(C.byref(d), C.byref(a), FAKE, 1 << 30, None) == 1  # no x, no override
+    a.route_override = FAKE
+    need = N.workspace_size(N.ENTRY_FORWARD, d)
+    assert L.natsl_forward(C.byref(d), C.byref(a), FAKE, need // 4, None) == 3
+    a.branch_dtype = 3
+    assert L.natsl_forward(C.byref(d), C.byref(a), FAKE, need, None) == 1
+
+
+def test_decode_validation(L):
+    d = good()
+    c = N.DecodeCache()
+    a = N.DecodeArgs()
+    assert L.natsl_decode_step(C.byref(d), C.byref(c), C.byref(a), None, 0, None) == 1
+    for f in ("k_cache", "v_cache", "n_committed", "n_open", "S_carry", "S_work", "x_sum", "err_flag"):
+        setattr(c, f, FAKE)
+    c.cap = 0
+    assert L.natsl_decode_step(C.byref(d), C.byref(c), C.byref(a), None, 0, None) == 1
+    c.cap = 1024
+    for f in ("x", "q", "k", "v", "alpha", "beta", "w_score", "w_mix", "out"):
+        setattr(a, f, FAKE)
+    assert L.natsl_decode_step(C.byref(d), C.byref(c), C.byref(a), None, 0, None) == 3
+    d2 = N.dims(2, 4, 1024, 128, 256, N.BF16)
+    need = N.workspace_size(N.ENTRY_DECODE_STEP, d2)
+    assert need > 0
+    assert L.natsl_decode_step(C.byref(d), C.byref(c), C.byref(a), FAKE, need - 256, None) == 3
+
+
+def test_workspace_sizes_monotone(L):
+    prev = 0
+    for Lq in (64, 128, 1024, 4096):
+        n = N.workspace_size(N.ENTRY_FORWARD, N.dims(1, 16, Lq, 128, 2048, N.BF16))
+        assert n > prev
+        prev = n
+    a = N.workspace_size(N.ENTRY_GDN_CHUNK, N.dims(1, 16, 4096, 128, 2048, N.BF16))
+    b = N.workspace_size(N.ENTRY_GDN_CHUNK, N.dims(2, 16, 4096, 128, 2048, N.BF16))
+    assert b > a
+    assert N.workspace_size(N.ENTRY_SOFTMAX_MASKED, N.dims(1, 16, 4096, 128, 2048, N.BF16)) == 0
+
+
+def test_last_error_is_thread_local(L):
+    L.natsl_route(None, *([None] * 9))
+    assert L.natsl_last_error() != b""
+    seen = []
+    t = threading.Thread(target=lambda: seen.append(L.natsl_last_error()))
+    t.start()
+    t.join()
+    assert seen == [b""]
+
+
+def test_binding_rejects_without_gpu_tensor():
+    import torch
+    with pytest.raises(ValueError):
+        N._p(torch.zeros(3), name="x")

@@ -1,0 +1,380 @@
+"""GPU parity: the HIP library, called through its C ABI, against the fp64
+oracle on the same seeded inputs.
+
+Bars: routes bit-exact; fp32 workloads max abs <= 1e-4 on out and on each
+RMS-normalised branch; bf16 workloads max abs <= 3e-2 on RMS-normalised
+outputs (out, n_sm, n_lin).  Full-size workloads are compared on sampled
+heads / query blocks that the oracle computes one by one.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import linear_attention_natsl_amd as N
+import oracle as O
+import workloads as W
+from tests.gpu_util import (TOL_BF16, TOL_F32, dev, dev_bits, host, maxerr, oracle_head, prefill_tensors,
+                            rmsn, rows_of_blocks)
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def io_code(inp):
+    return N.BF16 if inp["io"] == "bf16" else N.F32
+
+
+def run_forward(inp, wl_d, B, H, L, D, route_override=None, branch=None, groups=1, S_init=None):
+    t = prefill_tensors(inp)
+    dm = N.dims(B, H, L, D, wl_d, io_code(inp), groups=groups)
+    ro = None if route_override is None else dev(np.ascontiguousarray(route_override, dtype=np.int32))
+    Si = None if S_init is None else dev(S_init.astype(np.float32))
+    f = N.Forward(dm, branch_dtype=branch, debug=True, want_state=True)
+    f(t["x"] if route_override is None else None, t["q"], t["k"], t["v"], t["alpha"], t["beta"],
+      t["w_score"] if route_override is None else None, t["w_mix"], b_score=t["b_score"] if route_override is None else None,
+      g_sm=t["g_sm"], g_lin=t["g_lin"], route_override=ro, S_init=Si)
+    torch.cuda.synchronize()
+    return f
+
+
+# ------------------------------------------------------------------ router ----
+@pytest.mark.parametrize("name", ["tiny", "prefill", "long"])
+def test_route_full_size_bitexact(name):
+    wl = W.WORKLOADS[name]
+    inp = W.make_prefill(wl)
+    say(f"[route] {name} B={wl.B} L={wl.L} d={wl.d}")
+    r_ref, margin = O.route(inp["x"], inp["w_score"], inp["b_score"])
+    sel_ref, nsb_ref = O.compact(r_ref)
+    dm = N.dims(wl.B, wl.H, wl.L, wl.D, wl.d, io_code(inp))
+    r, sel, nsb, sc = N.route(dm, dev(inp["x"], inp["io"]), dev(inp["w_score"]), dev(inp["b_score"]))
+    torch.cuda.synchronize()
+    assert np.array_equal(r.cpu().numpy(), r_ref)
+    assert np.array_equal(sel.cpu().numpy(), sel_ref)
+    assert np.array_equal(nsb.cpu().numpy(), nsb_ref)
+    s_ref = O.route_scores(inp["x"], inp["w_score"], inp["b_score"])
+    assert maxerr(host(sc), s_ref) < 1e-5
+
+
+def test_route_tie_and_forced():
+    """Equal score columns tie exactly on the GPU too (same fp32 sums) and go
+    to softmax; a forced route is copied and compacted."""
+    wl = W.WORKLOADS["tiny"]
+    inp = W.make_prefill(wl)
+    w = np.repeat(inp["w_score"][:, :1], 2, axis=1).copy()
+    dm = N.dims(1, 1, 256, 64, 64, N.F32)
+    r, _, nsb, _ = N.route(dm, dev(inp["x"]), dev(w))
+    assert (r.cpu().numpy() == 0).all() and nsb.cpu().numpy()[0, 0, -1] == 4
+    forced = np.array([[[1, 0, 1, 0]]], np.int32)
+    r2, sel2, nsb2, _ = N.route(dm, None, None, route_in=dev(forced))
+    assert np.array_equal(r2.cpu().numpy(), forced)
+    assert sel2.cpu().numpy()[0, 0].tolist() == [1, 3, -1, -1]
+    assert nsb2.cpu().numpy()[0, 0].tolist() == [0, 0, 1, 1, 2]
+
+
+def test_route_groups_per_head():
+    """route_groups = H: every head has its own score columns."""
+    r0 = np.random.default_rng(7)
+    B, H, L, d = 2, 4, 512, 64
+    x = r0.standard_normal((B, L, d)).astype(np.float32)
+    w = r0.normal(0, 0.3, (d, 2 * H)).astype(np.float32)
+    r_ref, m = O.route(x, w, groups=H)
+    assert np.abs(m).min() > 1e-4
+    dm = N.dims(B, H, L, 64, d, N.F32, groups=H)
+    r, sel, nsb, _ = N.route(dm, dev(x), dev(w))
+    assert np.array_equal(r.cpu().numpy(), r_ref)
+    assert np.array_equal(nsb.cpu().numpy(), O.compact(r_ref)[1])
+
+
+# ---------------------------------------------------------------- branches ----
+def small_case(io="f32", B=1, H=2, L=640, D=64, seed=11, alpha=(0.9, 0.999), q_scale=1.0, sm_frac=0.5):
+    base = W.WORKLOADS["tiny"] if io == "f32" else W.WORKLOADS["prefill"]
+    wl = W.Workload("case", io, B, H, L, D, 64 if io == "f32" else base.d, "iid", seed)
+    return wl, W.make_prefill(wl, alpha_range=alpha, q_scale=q_scale, routing="iid", sm_frac=sm_frac)
+
+
+@pytest.mark.parametrize("io,D,L,q_scale", [("f32", 64, 256, 1.0), ("f32", 64, 576, 8.0), ("f32", 128, 320, 1.0),
+                                            ("bf16", 128, 640, 1.0), ("bf16", 128, 576, 8.0), ("bf16", 64, 448, 1.0)])
+def test_softmax_masked_parity(io, D, L, q_scale):
+    """Odd chunk counts exercise the single-chunk last block; q x 8 gives
+    sharp attention where one wrongly masked key shows."""
+    wl, inp = small_case(io, B=2, H=2, L=L, D=D, q_scale=q_scale)
+    say(f"[softmax] io={io} D={D} L={L} qs={q_scale}")
+    r = np.broadcast_to(inp["plan"], (2, 1, L // 64)).copy()
+    sel, nsb = O.compact(r)
+    dm = N.dims(2, 2, L, D, wl.d, io_code(inp))
+    o, lse = N.softmax_masked(dm, dev(inp["q"], io), dev(inp["k"], io), dev(inp["v"], io), dev(sel), dev(nsb),
+                              want_lse=True)
+    torch.cuda.synchronize()
+    ref, lse_ref = O.softmax_branch(inp["q"], inp["k"], inp["v"], r, with_lse=True)
+    tol = TOL_F32 if io == "f32" else TOL_BF16
+    e = maxerr(rmsn(host(o)), rmsn(ref))
+    say(f"  n_sm err {e:.3e}  raw {maxerr(host(o), ref):.3e}  lse {maxerr(host(lse), lse_ref):.3e}")
+    assert e <= tol
+    assert maxerr(host(lse), lse_ref) <= (1e-4 if io == "f32" else 2e-2)
+
+
+@pytest.mark.parametrize("io,D,L,alpha", [("f32", 64, 256, (0.9, 0.999)), ("f32", 64, 640, (0.995, 1.0)),
+                                          ("f32", 128, 320, (0.9, 0.999)), ("bf16", 128, 640, (0.9, 0.999)),
+                                          ("bf16", 128, 640, (0.995, 1.0)), ("bf16", 64, 448, (0.9, 0.999))])
+def test_gdn_chunk_parity(io, D, L, alpha):
+    """alpha ~ U(0.995, 1) keeps old state alive so a rollback bug several
+    chunks back still shows; a nonzero initial state checks S_init."""
+    wl, inp = small_case(io, B=2, H=2, L=L, D=D, alpha=alpha, seed=12)
+    say(f"[gdn] io={io} D={D} L={L} alpha={alpha}")
+    r = np.broadcast_to(inp["plan"], (2, 1, L // 64)).copy()
+    S0 = (np.random.default_rng(3).standard_normal((2, 2, D, D)) / np.sqrt(D)).astype(np.float32)
+    dm = N.dims(2, 2, L, D, wl.d, io_code(inp))
+    o, Sf = N.gdn_chunk(dm, dev(inp["q"], io), dev(inp["k"], io), dev(inp["v"], io), dev(inp["alpha"]),
+                        dev(inp["beta"]), dev(r), S_init=dev(S0))
+    torch.cuda.synchronize()
+    ref, Sref = O.gdn_branch(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], r, S_init=S0)
+    tol = TOL_F32 if io == "f32" else TOL_BF16
+    e = maxerr(rmsn(host(o)), rmsn(ref))
+    es = maxerr(host(Sf), Sref) / max(1.0, np.abs(Sref).max())
+    say(f"  n_lin err {e:.3e} raw {maxerr(host(o), ref):.3e}  S_final rel {es:.3e}")
+    assert e <= tol
+    assert es <= (1e-4 if io == "f32" else 3e-2)
+
+
+@pytest.mark.parametrize("io,branch,D", [("f32", "f32", 64), ("bf16", "bf16", 128), ("bf16", "f32", 128),
+                                         ("f32", "bf16", 128)])
+def test_merge_parity(io, branch, D):
+    rng = np.random.default_rng(5)
+    B, H, L = 2, 3, 128
+    q = rng.standard_normal((B, H, L, D)).astype(np.float32)
+    a = (rng.standard_normal((B, H, L, D)) * 3).astype(np.float32)
+    b = (rng.standard_normal((B, H, L, D)) * 0.1).astype(np.float32)
+    if io == "bf16":
+        q = W.round_bf16(q)
+    if branch == "bf16":
+        a, b = W.round_bf16(a), W.round_bf16(b)
+    w_mix = rng.normal(0, 0.3, (H, D, 2)).astype(np.float32)
+    gs = rng.uniform(0.5, 1.5, D).astype(np.float32)
+    gl = rng.uniform(0.5, 1.5, D).astype(np.float32)
+    dm = N.dims(B, H, L, D, 64, N.BF16 if io == "bf16" else N.F32)
+    say(f"[merge] io={io} branch={branch} D={D}")
+    out = N.merge(dm, dev(q, io), dev(a, branch), dev(b, branch), dev(w_mix), w_mix_head_stride=2 * D,
+                  g_sm=dev(gs), g_lin=dev(gl))
+    torch.cuda.synchronize()
+    ref, _, _, _ = O.merge(q, a, b, w_mix, gs, gl)
+    e = maxerr(host(out), ref)
+    say(f"  out err {e:.3e}")
+    assert e <= (TOL_F32 if io == "f32" else 2e-2)
+
+
+# ----------------------------------------------------------------- forward ----
+def test_forward_tiny_fp32():
+    wl = W.WORKLOADS["tiny"]
+    inp = W.make_prefill(wl)
+    say("[forward] tiny fp32")
+    f = run_forward(inp, wl.d, wl.B, wl.H, wl.L, wl.D)
+    ref = O.forward(inp["x"], inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["w_score"],
+                    inp["w_mix"], b_score=inp["b_score"], g_sm=inp["g_sm"], g_lin=inp["g_lin"])
+    assert np.array_equal(f.route.cpu().numpy(), ref["route"])
+    eo = maxerr(host(f.out), ref["out"])
+    es = maxerr(rmsn(host(f.o_sm)), ref["n_sm"])
+    el = maxerr(rmsn(host(f.o_gdn)), ref["n_lin"])
+    say(f"  out {eo:.3e} n_sm {es:.3e} n_lin {el:.3e}")
+    assert max(eo, es, el) <= TOL_F32
+
+
+@pytest.mark.parametrize("kind", ["sm", "lin"])
+def test_forward_forced_routes_small(kind):
+    """All-softmax must be full causal attention; all-linear pure Gated
+    DeltaNet (both pinned in the oracle tests)."""
+    wl, inp = small_case("bf16", B=2, H=2, L=512, D=128, seed=21)
+    r = W.forced_routes(2, 8, kind)
+    say(f"[forward] forced {kind}")
+    f = run_forward(inp, wl.d, 2, 2, 512, 128, route_override=r)
+    ref = O.forward(None, inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], None, inp["w_mix"],
+                    route_override=r, g_sm=inp["g_sm"], g_lin=inp["g_lin"])
+    eo = maxerr(host(f.out), ref["out"])
+    es = maxerr(rmsn(host(f.o_sm)), ref["n_sm"])
+    el = maxerr(rmsn(host(f.o_gdn)), ref["n_lin"])
+    say(f"  out {eo:.3e} n_sm {es:.3e} n_lin {el:.3e}")
+    assert max(eo, es, el) <= TOL_BF16
+
+
+def test_forward_edge_shapes():
+    """L = 64 (one chunk), an odd chunk count, B = 0 (no-op), and G = H."""
+    for (B, H, L, G) in [(1, 1, 64, 1), (3, 2, 192, 1), (2, 4, 320, 4)]:
+        wl, inp = small_case("f32", B=B, H=H, L=L, D=64, seed=31 + L)
+        say(f"[forward] edge B={B} H={H} L={L} G={G}")
+        if G == 1:
+            r = np.broadcast_to(inp["plan"], (B, 1, L // 64)).copy()
+        else:
+            r = (np.random.default_rng(L).random((B, G, L // 64)) < 0.5).astype(np.int32)
+        f = run_forward(inp, wl.d, B, H, L, 64, route_override=r, groups=G)
+        ref = O.forward(None, inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], None, inp["w_mix"],
+                        route_override=r, groups=G)
+        e = maxerr(host(f.out), ref["out"])
+        say(f"  out err {e:.3e}")
+        assert e <= TOL_F32
+    dm = N.dims(0, 2, 128, 64, 64, N.F32)
+    z = torch.empty(0, 2, 128, 64, device="cuda")
+    out = N.softmax_masked(dm, z, z, z, torch.empty(0, 1, 2, dtype=torch.int32, device="cuda"),
+                           torch.empty(0, 1, 3, dtype=torch.int32, device="cuda"))[0]
+    assert out.numel() == 0
+
+
+def test_forward_deterministic():
+    wl, inp = small_case("bf16", B=1, H=4, L=1024, D=128, seed=41)
+    r = np.broadcast_to(inp["plan"], (1, 1, 16)).copy()
+    say("[forward] determinism")
+    f1 = run_forward(inp, wl.d, 1, 4, 1024, 128, route_override=r)
+    o1 = f1.out.clone()
+    f2 = run_forward(inp, wl.d, 1, 4, 1024, 128, route_override=r)
+    assert torch.equal(o1, f2.out)
+
+
+# --------------------------------------------------------- full-size sampled ----
+def full_forward_check(name, heads, query_blocks=None, route_kind=None):
+    wl = W.WORKLOADS[name]
+    inp = W.make_prefill(wl)
+    r_ref = W.forced_routes(wl.B, wl.nc, route_kind) if route_kind else O.route(inp["x"], inp["w_score"],
+                                                                                 inp["b_score"])[0]
+    say(f"[forward] full {name} {route_kind or ''} B={wl.B} H={wl.H} L={wl.L}")
+    f = run_forward(inp, wl.d, wl.B, wl.H, wl.L, wl.D, route_override=r_ref if route_kind else None)
+    if not route_kind:
+        assert np.array_equal(f.route.cpu().numpy(), r_ref)
+    worst = 0.0
+    for (b, h) in heads:
+        ref = oracle_head(inp, b, h, r_ref[b], query_blocks=query_blocks)
+        rows = slice(None) if query_blocks is None else rows_of_blocks(query_blocks)
+        out = host(f.out[b, h])
+        eo = maxerr(out[rows], ref["out"][rows])
+        es = maxerr(rmsn(host(f.o_sm[b, h]))[rows], ref["n_sm"][rows])
+        el = maxerr(rmsn(host(f.o_gdn[b, h])), ref["n_lin"])
+        say(f"  (b={b},h={h}) out {eo:.3e} n_sm {es:.3e} n_lin {el:.3e}")
+        worst = max(worst, eo, es, el)
+    assert worst <= TOL_BF16
+
+
+def test_forward_prefill_full_sampled():
+    full_forward_check("prefill", heads=[(0, 0), (1, 7), (3, 15)])
+
+
+def test_forward_long_full_sampled():
+    blocks = [0, 1, 100, 255, 256, 300, 400, 477, 510, 511]
+    full_forward_check("long", heads=[(0, 5)], query_blocks=blocks)
+
+
+@pytest.mark.parametrize("kind", ["sm", "lin"])
+def test_forward_degen_full_sampled(kind):
+    blocks = [0, 1, 63, 64, 127] if kind == "sm" else None
+    full_forward_check("degen", heads=[(0, 0), (1, 9)], query_blocks=blocks, route_kind=kind)
+
+
+# ------------------------------------------------------------------ decode ----
+def load_state(cache, B, H, D, d, io, groups=1):
+    st = N.DecodeState(B, H, D, d, cache["k"].shape[2], groups=groups,
+                       io=torch.bfloat16 if io == "bf16" else torch.float32)
+    if cache["k"].dtype == np.uint16:
+        st.k.copy_(dev_bits(cache["k"]))
+        st.v.copy_(dev_bits(cache["v"]))
+    else:
+        st.k.copy_(dev(cache["k"].astype(np.float32), io))
+        st.v.copy_(dev(cache["v"].astype(np.float32), io))
+    st.n_committed.copy_(dev(np.asarray(cache["n_committed"], np.int32).reshape(B, groups)))
+    st.n_open.copy_(dev(np.asarray(cache["n_open"], np.int32).reshape(B, -1)[:, 0].copy()))
+    st.S_carry.copy_(dev(cache["S_carry"].astype(np.float32)))
+    st.S_work.copy_(dev(cache["S_work"].astype(np.float32)))
+    xs = np.asarray(cache["x_sum"], np.float32).reshape(B, -1, d)[:, 0]
+    st.x_sum.copy_(dev(np.ascontiguousarray(xs)))
+    return st
+
+
+@pytest.mark.parametrize("io,D", [("f32", 64), ("bf16", 128)])
+def test_decode_steps_match_oracle(io, D):
+    """Prefix of 100 tokens, then 150 decode steps one at a time, crossing
+    chunk completions of both routes; every step's output and the final
+    counters and states against the oracle's decode."""
+    B, H, L = 2, 2, 256
+    wl, inp = small_case(io, B=B, H=H, L=L, D=D, seed=51, sm_frac=0.5)
+    d = wl.d
+    n0 = 100
+    say(f"[decode] steps io={io} D={D}")
+    cache = O.build_cache(inp["x"][:, :n0], inp["k"][:, :, :n0], inp["v"][:, :, :n0], inp["alpha"][:, :, :n0],
+                          inp["beta"][:, :, :n0], inp["w_score"], cap=L + 64)
+    st = load_state(cache, B, H, D, d, io)
+    dm = N.dims(B, H, L, D, d, N.BF16 if io == "bf16" else N.F32)
+    dec = N.Decode(dm, st, debug=True)
+    t = prefill_tensors(inp)
+    tol = TOL_F32 if io == "f32" else TOL_BF16
+    worst = 0.0
+    seen = set()
+    for tok in range(n0, L):
+        args = [t["x"][:, tok].contiguous(), t["q"][:, :, tok].contiguous(), t["k"][:, :, tok].contiguous(),
+                t["v"][:, :, tok].contiguous(), t["alpha"][:, :, tok].contiguous(),
+                t["beta"][:, :, tok].contiguous(), t["w_score"], t["w_mix"]]
+        dec(*args)
+        out_ref, br, cache = O.decode_step(cache, inp["x"][:, tok], inp["q"][:, :, tok], inp["k"][:, :, tok],
+                                           inp["v"][:, :, tok], inp["alpha"][:, :, tok], inp["beta"][:, :, tok],
+                                           inp["w_score"], inp["w_mix"])
+        torch.cuda.synchronize()
+        routes = dec.route.cpu().numpy()
+        assert np.array_equal(routes, br["routes"]), f"tok {tok}"
+        seen.update(int(x) for x in routes.ravel() if x >= 0)
+        e = max(maxerr(host(dec.out), out_ref), maxerr(rmsn(host(dec.o_sm)), br["n_sm"]),
+                maxerr(rmsn(host(dec.o_gdn)), br["n_lin"]))
+        worst = max(worst, e)
+        assert e <= tol, f"tok {tok}: err {e}"
+    say(f"  worst err {worst:.3e}, routes seen {seen}")
+    assert seen == {0, 1}
+    assert np.array_equal(st.n_committed.cpu().numpy(), cache["n_committed"].astype(np.int32))
+    assert np.array_equal(st.n_open.cpu().numpy(), cache["n_open"][:, 0].astype(np.int32))
+    assert maxerr(host(st.S_carry), cache["S_carry"]) <= (1e-4 if io == "f32" else 1e-2)
+    assert int(st.err.item()) == 0
+
+
+def test_decode_full_sampled():
+    """The decode workload at full size (B=64, ~8192 cached rows per head),
+    one step; sampled sequences against the oracle."""
+    wl = W.WORKLOADS["decode"]
+    cache, new = W.make_decode(wl)
+    B, H, D, d = wl.B, wl.H, wl.D, wl.d
+    say(f"[decode] full B={B} cap={cache['k'].shape[2]}")
+    st = load_state(cache, B, H, D, d, "bf16")
+    dm = N.dims(B, H, 1, D, d, N.BF16)
+    dec = N.Decode(dm, st, debug=True)
+    args = [dev(new["x"], "bf16"), dev(new["q"], "bf16"), dev(new["k"], "bf16"), dev(new["v"], "bf16"),
+            dev(new["alpha"]), dev(new["beta"]), dev(new["w_score"]), dev(new["w_mix"])]
+    dec(*args)
+    torch.cuda.synchronize()
+    for b in (0, 17, 63):
+        sub = dict(k=W.bits_to_f32(cache["k"][b:b + 1]), v=W.bits_to_f32(cache["v"][b:b + 1]),
+                   n_committed=cache["n_committed"][b:b + 1], n_open=cache["n_open"][b:b + 1],
+                   S_carry=cache["S_carry"][b:b + 1], S_work=cache["S_work"][b:b + 1],
+                   x_sum=cache["x_sum"][b:b + 1], err=0)
+        out_ref, br, _ = O.decode_step(sub, new["x"][b:b + 1], new["q"][b:b + 1], new["k"][b:b + 1],
+                                       new["v"][b:b + 1], new["alpha"][b:b + 1], new["beta"][b:b + 1],
+                                       new["w_score"], new["w_mix"])
+        e = max(maxerr(host(dec.out[b:b + 1]), out_ref), maxerr(rmsn(host(dec.o_sm[b:b + 1])), br["n_sm"]),
+                maxerr(rmsn(host(dec.o_gdn[b:b + 1])), br["n_lin"]))
+        say(f"  b={b} err {e:.3e}")
+        assert e <= TOL_BF16
+    n = int(cache["n_committed"][0, 0])
+    assert torch.equal(st.k[0, :, n], args[2][0])
+    assert (st.n_open.cpu().numpy() == 1).all()
+
+
+def test_decode_capacity_flag():
+    """A full cache sets err_flag and writes nothing past its end."""
+    B, H, D, d, cap = 1, 2, 64, 64, 128
+    st = N.DecodeState(B, H, D, d, cap, io=torch.float32)
+    st.n_committed.fill_(128)
+    dm = N.dims(B, H, 1, D, d, N.F32)
+    dec = N.Decode(dm, st)
+    rng = np.random.default_rng(0)
+    mk = lambda *s: dev(rng.standard_normal(s).astype(np.float32))
+    dec(mk(B, d), mk(B, H, D), mk(B, H, D), mk(B, H, D), dev(np.full((B, H), 0.9, np.float32)),
+        dev(np.full((B, H), 0.5, np.float32)), mk(d, 2), mk(D, 2))
+    torch.cuda.synchronize()
+    assert int(st.err.item()) == 1
+    assert torch.isfinite(dec.out).all()

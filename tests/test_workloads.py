@@ -81,5 +81,6 @@ def test_decode_workload_small():
     assert ((nc % 64) == 0).all() and (nc >= 64 * 120).all() and (nc <= 64 * 136).all()
     for b in range(4):
         n = int(nc[b])
-        np.testing.assert_allclose(np.linalg.norm(cache["k"][b, :, :n], axis=-1), 1.0, atol=1e-2)
+        kk = W.bits_to_f32(cache["k"][b, :, :n])
+        np.testing.assert_allclose(np.linalg.norm(kk, axis=-1), 1.0, atol=1e-2)
         assert (cache["k"][b, :, n:] == 0).all()

@@ -21,6 +21,7 @@ normalisation) to bf16 with round-to-nearest-even.
 """
 from __future__ import annotations
 
+import os
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -68,6 +69,16 @@ def round_bf16(a):
     bias = np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
     r = ((u + bias) & np.uint32(0xFFFF0000)).astype(np.uint32)
     return r.view(np.float32)
+
+
+def bf16_bits(a):
+    """bf16 bit patterns (uint16) of float32 values already rounded to bf16."""
+    return (np.ascontiguousarray(a, dtype=np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def bits_to_f32(u):
+    """float32 values of bf16 bit patterns."""
+    return (np.asarray(u, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
 def _streams(seed, n=12):
@@ -198,7 +209,8 @@ def make_decode(wl: Workload, seed=None, B=None, H=None, cap=None, n_open=0):
     K and N(0,1) V per head); rows of an open chunk (n_open tokens) follow
     them.  S_carry (and S_work) ~ N(0, 1/Dk) fp32; x_sum = sum of n_open
     N(0,1) rows (0 when n_open = 0).  New x, q, k, v, alpha, beta use the
-    prefill distributions."""
+    prefill distributions.  The cache rows k, v are returned as bf16 bit
+    patterns (uint16); bits_to_f32 gives their values."""
     seed = wl.seed if seed is None else seed
     rs = _streams(seed)
     B = wl.B if B is None else B
@@ -209,12 +221,19 @@ def make_decode(wl: Workload, seed=None, B=None, H=None, cap=None, n_open=0):
     n_committed = (CHUNK * n_sel).astype(np.int32)
     if cap is None:
         cap = CHUNK * int(e["nsel_hi"]) + CHUNK
-    kc = np.zeros((B, H, cap, D), np.float32)
-    vc = np.zeros((B, H, cap, D), np.float32)
-    for b in range(B):
+    kc = np.zeros((B, H, cap, D), np.uint16)  # bf16 bit patterns
+    vc = np.zeros((B, H, cap, D), np.uint16)
+    seq_seeds = np.random.SeedSequence([seed, 4]).spawn(B)  # one stream per sequence
+
+    def fill(b):
+        r = np.random.Generator(np.random.PCG64(seq_seeds[b]))
         n = int(n_committed[b]) + n_open
-        kc[b, :, :n] = round_bf16(_unit_rows(rs[4].standard_normal(size=(H, n, D), dtype=np.float32)))
-        vc[b, :, :n] = round_bf16(rs[5].standard_normal(size=(H, n, D), dtype=np.float32))
+        kc[b, :, :n] = bf16_bits(round_bf16(_unit_rows(r.standard_normal(size=(H, n, D), dtype=np.float32))))
+        vc[b, :, :n] = bf16_bits(round_bf16(r.standard_normal(size=(H, n, D), dtype=np.float32)))
+
+    import concurrent.futures as cf
+    with cf.ThreadPoolExecutor(min(16, os.cpu_count() or 4)) as ex:
+        list(ex.map(fill, range(B)))
     S_carry = (rs[6].standard_normal(size=(B, H, D, D), dtype=np.float32) / np.sqrt(D)).astype(np.float32)
     S_work = (rs[7].standard_normal(size=(B, H, D, D), dtype=np.float32) / np.sqrt(D)).astype(np.float32)
     x_sum = np.zeros((B, 1, d), np.float32)
