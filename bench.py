@@ -1,0 +1,277 @@
+"""Benchmark of the NAtS-L hybrid layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long] [--no-cpu] [--no-decode]
+
+A step is one full prefill forward of the layer (router + compaction, Gated
+DeltaNet branch, softmax branch, merge) over the "long" workload
+(B=1, H=16, L=32768, D=128, d_model=2048, bf16, 25% softmax chunks in 3
+bursts + 32 singles).  Inputs are resident in HBM before timing starts; W
+untimed warm-up steps, then K timed steps between device synchronisations.
+
+The decode step (B=64, H=16, ~8192 cached rows per head) is measured in the
+same run and reported under "decode".
+
+roofline: the dominant kernel of each phase, timed live with HIP events that
+the library records around its own launches (on the stream each kernel runs
+on) during the timed region:
+  prefill  softmax_masked, MFMA-bound: algorithmic FLOPs 4*D*(visible pairs)
+           of the realised routes / average launch time, against 2.5 PFLOP/s
+           dense bf16;
+  decode   decode_attn, HBM-bound: the cached K/V bytes it must read / average
+           launch time, against 8 TB/s.
+cpu_baseline: the fp64 oracle on a bounded sample (one head: router on all
+chunks, Gated DeltaNet on all tokens, softmax on every 8th query block), the
+per-head time scaled to all heads.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def sm_pairs(route_bgc, H, chunk=64):
+    """Visible (query, key) pairs of the softmax branch for realised routes:
+    every query sees the earlier softmax chunks in full and its own chunk
+    causally."""
+    r = np.asarray(route_bgc)
+    B, G, nc = r.shape
+    total = 0
+    for b in range(B):
+        for g in range(G):
+            is_sm = (r[b, g] == 0).astype(np.int64)
+            nsb = np.concatenate([[0], np.cumsum(is_sm)[:-1]])
+            per_head = int((chunk * chunk * nsb).sum()) + nc * chunk * (chunk + 1) // 2
+            total += per_head * (H // G)
+    return total
+
+
+def gdn_flops(B, H, nc, n_lin, D, chunk=64):
+    """Chunkwise Gated DeltaNet work: per chunk-head 10 C^2 D + 4 C D^2, plus
+    2 C D^2 for every committed (linear) chunk (the C^3 solve is excluded)."""
+    return B * H * (nc * (10 * chunk * chunk * D + 4 * chunk * D * D)) + H * n_lin * 2 * chunk * D * D
+
+
+def source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "linear_attention_natsl_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counters_traffic(kernel, workload, src_hash, launches_bytes_hint=None):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when it is missing or the kernel source changed since."""
+    p = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        c = json.load(f)
+    if c.get("source_hash") != src_hash:
+        return None
+    return c.get("hbm_bytes_per_launch")
+
+
+def time_prefill(args, N, W, O):
+    import torch
+    wl = W.WORKLOADS[args.workload]
+    inp = W.make_prefill(wl)
+    dev = torch.device("cuda:0")
+    io_t = torch.bfloat16 if inp["io"] == "bf16" else torch.float32
+    t = {k: torch.from_numpy(np.ascontiguousarray(inp[k])).to(dev).to(io_t) for k in ("x", "q", "k", "v")}
+    for k in ("alpha", "beta", "w_score", "w_mix", "b_score", "g_sm", "g_lin"):
+        t[k] = torch.from_numpy(np.ascontiguousarray(inp[k])).to(dev)
+    dm = N.dims(wl.B, wl.H, wl.L, wl.D, wl.d, N.BF16 if inp["io"] == "bf16" else N.F32)
+    fwd = N.Forward(dm, device=dev)
+    call = lambda: fwd(t["x"], t["q"], t["k"], t["v"], t["alpha"], t["beta"], t["w_score"], t["w_mix"],
+                       b_score=t["b_score"], g_sm=t["g_sm"], g_lin=t["g_lin"])
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    N.profile_enable(True)
+    N.profile_reset()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        call()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    kernels = {}
+    for name in ("route", "compact", "gdn_prep", "gdn_scan", "softmax_masked", "merge"):
+        n, ms = N.profile_read(name)
+        kernels[name] = dict(launches=n, avg_us=round(1000.0 * ms / max(n, 1), 2))
+    N.profile_enable(False)
+    route = fwd.route.cpu().numpy()
+    ref_route = O.route(inp["x"], inp["w_score"], inp["b_score"])[0] if args.check_route else None
+    pairs = sm_pairs(route, wl.H)
+    f_sm = 4 * wl.D * pairs
+    n_lin = int((route == 1).sum())
+    f_gdn = gdn_flops(wl.B, wl.H, wl.nc, n_lin, wl.D)
+    ms_step = 1000.0 * dt / args.steps
+    tok_s = wl.B * wl.L / (dt / args.steps)
+    sm_us = kernels["softmax_masked"]["avg_us"]
+    achieved = f_sm / (sm_us * 1e-6) / 1e12
+    traffic = counters_traffic("softmax_masked", args.workload, source_hash("softmax_masked.hip", "common.hpp"))
+    res = dict(
+        metric="hybrid-layer prefill tokens/sec + % bf16 MFMA peak; decode-step % HBM peak",
+        value=round(tok_s, 1), unit="tokens/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
+        ms_per_step=round(ms_step, 4), higher_is_better=True, scaling="weak", vs_baseline=None,
+        dtype="bf16" if inp["io"] == "bf16" else "f32", data="synthetic",
+        config=dict(workload=f"{args.workload} prefill: B={wl.B} H={wl.H} L={wl.L} D={wl.D} d_model={wl.d}, "
+                    f"chunk 64, {inp['io']} io / fp32 accumulate",
+                    B=wl.B, H=wl.H, L=wl.L, D=wl.D, d_model=wl.d, seed=wl.seed,
+                    softmax_chunk_fraction=round(float((route == 0).mean()), 4),
+                    route_matches_oracle=None if ref_route is None else bool(np.array_equal(route, ref_route)),
+                    parallelism="single GPU"),
+        roofline=dict(bound="mfma", kernel="softmax_masked", achieved=round(achieved, 1), peak=PEAK_BF16_TFLOPS,
+                      unit="TFLOP/s", frac=round(achieved / PEAK_BF16_TFLOPS, 4), traffic=traffic,
+                      flops_per_launch=f_sm, avg_launch_us=sm_us),
+        layer=dict(flops_softmax=f_sm, flops_gdn=f_gdn,
+                   layer_tflops=round((f_sm + f_gdn) / (dt / args.steps) / 1e12, 1),
+                   layer_frac_of_mfma_peak=round((f_sm + f_gdn) / (dt / args.steps) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                   kernels=kernels),
+    )
+    return res, inp, route
+
+
+def time_decode(args, N, W):
+    import torch
+    wl = W.WORKLOADS["decode"]
+    cache, new = W.make_decode(wl)
+    dev = torch.device("cuda:0")
+    B, H, D, d = wl.B, wl.H, wl.D, wl.d
+    cap = cache["k"].shape[2]
+    st = N.DecodeState(B, H, D, d, cap, io=torch.bfloat16, device=dev)
+    bits = lambda u: torch.from_numpy(np.ascontiguousarray(u).view(np.int16)).to(dev).view(torch.bfloat16)
+    st.k.copy_(bits(cache["k"]))
+    st.v.copy_(bits(cache["v"]))
+    st.n_committed.copy_(torch.from_numpy(cache["n_committed"].astype(np.int32)).to(dev))
+    st.n_open.copy_(torch.from_numpy(cache["n_open"][:, 0].astype(np.int32)).to(dev))
+    st.S_carry.copy_(torch.from_numpy(cache["S_carry"]).to(dev))
+    st.S_work.copy_(torch.from_numpy(cache["S_work"]).to(dev))
+    del cache
+    dm = N.dims(B, H, 1, D, d, N.BF16)
+    dec = N.Decode(dm, st, device=dev)
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(torch.bfloat16)
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    a = [bf(new["x"]), bf(new["q"]), bf(new["k"]), bf(new["v"]), f32(new["alpha"]), f32(new["beta"]),
+         f32(new["w_score"]), f32(new["w_mix"])]
+    rows0 = (st.n_committed[:, 0] + st.n_open).cpu().numpy().astype(np.int64)
+    steps, warm = args.decode_steps, 3
+    for _ in range(warm):
+        dec(*a)
+    torch.cuda.synchronize()
+    rows_start = (st.n_committed[:, 0] + st.n_open).cpu().numpy().astype(np.int64)
+    N.profile_enable(True)
+    N.profile_reset()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        dec(*a)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    kernels = {}
+    for name in ("decode_route", "decode_gdn", "decode_attn", "decode_combine", "decode_commit"):
+        n, ms = N.profile_read(name)
+        kernels[name] = dict(launches=n, avg_us=round(1000.0 * ms / max(n, 1), 2))
+    N.profile_enable(False)
+    assert int(st.err.item()) == 0
+    # rows read per step: step i reads rows_start + i cached rows per (b, h)
+    mean_rows = float((rows_start[:, None] + np.arange(steps)[None, :]).mean())
+    kv_bytes = B * H * mean_rows * 2 * D * 2
+    step_bytes = kv_bytes + B * H * (2 * D * 2 + 2 * D * D * 4 + 4 * D * 2) + B * d * (2 + 8)
+    attn_us = kernels["decode_attn"]["avg_us"]
+    achieved = kv_bytes / (attn_us * 1e-6) / 1e9
+    traffic = counters_traffic("decode_attn", "decode", source_hash("decode.hip", "common.hpp"))
+    return dict(
+        workload=f"decode: B={B} H={H} D={D} d_model={d}, ~{rows0.mean():.0f} cached rows per head, bf16 cache",
+        value=round(B / (dt / steps), 1), unit="tokens/s", steps=steps, warmup=warm,
+        ms_per_step=round(1000.0 * dt / steps, 4),
+        step_bytes=int(step_bytes), step_hbm_frac=round(step_bytes / (dt / steps) / 1e9 / PEAK_HBM_GBS, 4),
+        roofline=dict(bound="hbm", kernel="decode_attn", achieved=round(achieved, 1), peak=PEAK_HBM_GBS,
+                      unit="GB/s", frac=round(achieved / PEAK_HBM_GBS, 4), traffic=traffic,
+                      bytes_per_launch=int(kv_bytes), avg_launch_us=attn_us),
+        kernels=kernels)
+
+
+def cpu_baseline(W, O, inp, route, workload):
+    """The oracle as it stands, on head 0 of the prefill workload: router on
+    all chunks, Gated DeltaNet over every token, softmax on every 8th 64-row
+    query block; scaled to the whole job."""
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    wl = W.WORKLOADS[workload]
+    sl = lambda a: a[:, :1]
+    t0 = time.perf_counter()
+    r, _ = O.route(inp["x"], inp["w_score"], inp["b_score"])
+    t_route = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    o_gdn, _ = O.gdn_branch(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(inp["alpha"]), sl(inp["beta"]), r)
+    t_gdn = time.perf_counter() - t0
+    blocks = list(range(0, wl.nc, 8))
+    t0 = time.perf_counter()
+    o_sm = O.softmax_branch(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), r, query_blocks=blocks)
+    t_sm = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    O.merge(sl(inp["q"]), o_sm, o_gdn, inp["w_mix"])
+    t_merge = time.perf_counter() - t0
+    per_head = t_gdn + t_sm * (wl.nc / len(blocks)) + t_merge
+    total = t_route + wl.H * per_head
+    return dict(value=round(wl.B * wl.L / total, 2), unit="tokens/s", cores=int(cores), kind="oracle",
+                sample=f"{workload}: head 0 of {wl.H}; router on all {wl.nc} chunks ({t_route:.2f}s), Gated DeltaNet "
+                       f"on all {wl.L} tokens ({t_gdn:.2f}s), softmax on {len(blocks)} of {wl.nc} query blocks "
+                       f"({t_sm:.2f}s), merge ({t_merge:.2f}s); per-head time scaled by {wl.nc // len(blocks)} for "
+                       f"the softmax and by {wl.H} heads",
+                seconds_measured=round(t_route + t_gdn + t_sm + t_merge, 2))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="long", choices=["long", "prefill", "degen"])
+    ap.add_argument("--decode-steps", type=int, default=50)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--check-route", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(shard over (batch, head) with one process per GPU; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import linear_attention_natsl_amd as N
+    import workloads as W
+    import oracle as O
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    N.lib()
+    res, inp, route = time_prefill(args, N, W, O)
+    print(f"prefill: {res['ms_per_step']} ms/step, {res['value']:.0f} tok/s, softmax "
+          f"{res['roofline']['frac']*100:.1f}% of MFMA peak", file=sys.stderr, flush=True)
+    if not args.no_decode:
+        res["decode"] = time_decode(args, N, W)
+        print(f"decode: {res['decode']['ms_per_step']} ms/step, attn {res['decode']['roofline']['frac']*100:.1f}% "
+              f"of HBM peak", file=sys.stderr, flush=True)
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(W, O, inp, route, args.workload)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

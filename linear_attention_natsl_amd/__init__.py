@@ -223,7 +223,9 @@ class Forward:
     def __init__(self, dm: Dims, device="cuda", branch_dtype=None, debug=False, want_state=False):
         self.dm = dm
         io_t = torch.bfloat16 if dm.io == BF16 else torch.float32
-        self.branch_dtype = branch_dtype if branch_dtype is not None else io_t
+        # fp32 branch intermediates by default: bf16 storage would add its own
+        # rounding to both RMS-normalised branches
+        self.branch_dtype = branch_dtype if branch_dtype is not None else torch.float32
         self.ws_bytes = workspace_size(ENTRY_FORWARD, dm)
         self.ws = workspace(self.ws_bytes, device)
         shp = (dm.B, dm.H, dm.L, dm.Dv)

@@ -218,27 +218,27 @@ hipError_t do_softmax(const natsl_dims* d, const void* q, const void* k, const v
   return e;
 }
 
+// The chunk prep runs on st_prep; the scan runs on st_scan (after an event
+// wait when the two differ).
 template <typename T, typename To>
 hipError_t do_gdn_t(const natsl_dims* d, const void* q, const void* k, const void* v, const float* a,
                     const float* b, const int32_t* route, const float* S0, void* o, float* Sf, void* ws,
-                    hipStream_t st) {
-  DevCtx* c = nullptr;
-  hipEvent_t ev = nullptr;
-  if (get_ctx(&c) == NATSL_OK) ev = c->prep;
+                    hipStream_t st_prep, hipStream_t st_scan, hipEvent_t ev) {
   if (d->Dk == 64)
     return launch_gdn<T, To, 64>((const T*)q, (const T*)k, (const T*)v, a, b, route, S0, (To*)o, Sf, ws,
-                                 d->B, d->H, d->L, d->route_groups, st, st, ev, prof_fn());
+                                 d->B, d->H, d->L, d->route_groups, st_prep, st_scan, ev, prof_fn());
   return launch_gdn<T, To, 128>((const T*)q, (const T*)k, (const T*)v, a, b, route, S0, (To*)o, Sf, ws,
-                                d->B, d->H, d->L, d->route_groups, st, st, ev, prof_fn());
+                                d->B, d->H, d->L, d->route_groups, st_prep, st_scan, ev, prof_fn());
 }
 hipError_t do_gdn(const natsl_dims* d, const void* q, const void* k, const void* v, const float* a,
                   const float* b, const int32_t* route, const float* S0, void* o, natsl_dtype od, float* Sf,
-                  void* ws, hipStream_t st) {
+                  void* ws, hipStream_t st_prep, hipStream_t st_scan = nullptr, hipEvent_t ev = nullptr) {
+  if (!st_scan) st_scan = st_prep;
   if (d->io == NATSL_BF16)
-    return od == NATSL_BF16 ? do_gdn_t<bf16, bf16>(d, q, k, v, a, b, route, S0, o, Sf, ws, st)
-                            : do_gdn_t<bf16, float>(d, q, k, v, a, b, route, S0, o, Sf, ws, st);
-  return od == NATSL_BF16 ? do_gdn_t<float, bf16>(d, q, k, v, a, b, route, S0, o, Sf, ws, st)
-                          : do_gdn_t<float, float>(d, q, k, v, a, b, route, S0, o, Sf, ws, st);
+    return od == NATSL_BF16 ? do_gdn_t<bf16, bf16>(d, q, k, v, a, b, route, S0, o, Sf, ws, st_prep, st_scan, ev)
+                            : do_gdn_t<bf16, float>(d, q, k, v, a, b, route, S0, o, Sf, ws, st_prep, st_scan, ev);
+  return od == NATSL_BF16 ? do_gdn_t<float, bf16>(d, q, k, v, a, b, route, S0, o, Sf, ws, st_prep, st_scan, ev)
+                          : do_gdn_t<float, float>(d, q, k, v, a, b, route, S0, o, Sf, ws, st_prep, st_scan, ev);
 }
 
 template <typename Tq, typename Tb>
@@ -406,11 +406,11 @@ natsl_status natsl_forward(const natsl_dims* dims, const natsl_forward_args* a, 
   hipError_t e = do_route(dims, a->x, a->w_score, a->b_score, a->route_override, route, w.sel, w.nsb,
                           a->scores_out, stream);
   if (e != hipSuccess) return dev_fail(e, "natsl_forward/route");
-  // fork: Gated DeltaNet branch on the helper stream, softmax on the caller's
-  if ((e = hipEventRecord(ctx->fork, stream)) != hipSuccess) return dev_fail(e, "hipEventRecord");
-  if ((e = hipStreamWaitEvent(ctx->aux, ctx->fork, 0)) != hipSuccess) return dev_fail(e, "hipStreamWaitEvent");
+  // The chunk prep (fully parallel, bandwidth-bound) runs alone on the caller's
+  // stream; then the state scan (one workgroup per (b, h, Dv slice), latency-
+  // bound) forks onto the helper stream and overlaps the softmax branch.
   e = do_gdn(dims, a->q, a->k, a->v, a->alpha, a->beta, route, a->S_init, o_gd, a->branch_dtype, a->S_final,
-             w.gdn, ctx->aux);
+             w.gdn, stream, ctx->aux, ctx->prep);
   if (e != hipSuccess) return dev_fail(e, "natsl_forward/gdn");
   e = do_softmax(dims, a->q, a->k, a->v, w.sel, w.nsb, o_sm, a->branch_dtype, nullptr, stream);
   if (e != hipSuccess) return dev_fail(e, "natsl_forward/softmax");

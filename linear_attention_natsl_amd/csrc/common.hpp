@@ -109,18 +109,21 @@ template <typename T> __device__ __forceinline__ void load8f(const T* p, float* 
 __device__ __forceinline__ int kmap_acc(int g, int j) { return (j < 4) ? (4 * g + j) : (16 + 4 * g + (j - 4)); }
 
 // "Key-group" LDS layout for an operand whose contraction index runs over
-// tokens (rows of a row-major [64 x D] tile): element (tok, col) is stored at
-//   ((tok / 4) * D + swz(col)) * 4 + tok % 4
+// tokens (rows of a row-major [64 x NCOL] tile): element (tok, col) is stored at
+//   ((tok / 4) * RL + swz(col)) * 4 + tok % 4,   RL = kg_row<T, NCOL>
 // so the 4 tokens 4kg..4kg+3 of one column are contiguous (one 8-byte bf16 /
 // 16-byte fp32 read).  swz permutes columns inside each group of 16 so that
 // 16 lanes reading 16 consecutive columns, or 16 lanes writing columns
-// 8m + i (m = 0..15), hit distinct bank groups.
+// 8m + i (m = 0..15), hit distinct banks; each key-group row is padded by
+// 128 bytes so that the next 16 lanes (the next key group) land on the other
+// half of the 64 banks.
+template <typename T, int NCOL> constexpr int kg_row() { return NCOL + 32 / (int)sizeof(T); }
 __device__ __forceinline__ int kg_swz(int col) {
   const int hi = col >> 4;
   return (col & ~15) | ((col ^ hi) & 15);
 }
-template <int D> __device__ __forceinline__ int kg_index(int kg, int col) {
-  return (kg * D + kg_swz(col)) * 4;
+template <int RL> __device__ __forceinline__ int kg_index(int kg, int col) {
+  return (kg * RL + kg_swz(col)) * 4;
 }
 
 // Wave-level helpers (wave64).
@@ -128,6 +131,15 @@ __device__ __forceinline__ float wave_max_xor(float v, int mask) {
   return fmaxf(v, __shfl_xor(v, mask, 64));
 }
 __device__ __forceinline__ float wave_sum_xor(float v, int mask) { return v + __shfl_xor(v, mask, 64); }
+
+// Workgroup barrier that orders LDS only: waits for this wave's LDS accesses
+// and meets the other waves, but leaves global loads in flight (a plain
+// __syncthreads() also drains outstanding global loads, which would defeat
+// prefetching the next step's operands).  The memory clobber keeps the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }

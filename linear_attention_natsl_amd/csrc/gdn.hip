@@ -22,15 +22,20 @@
 //               Q K^T on MFMA, the 64x64 unit-lower-triangular inverse T in
 //               LDS (fp32: 16x16 diagonal blocks by forward substitution, then
 //               block rows), T diag(b) V and T diag(b gamma) K on MFMA; writes
-//               -W, U~, K~^T, P and gamma in exactly the per-lane fragment
-//               order the scan consumes (every scan load is 16 B per lane,
-//               1 KiB contiguous per wave).
+//               -W, U~, K^T, P and the per-token decays in exactly the
+//               per-lane fragment order the scan consumes (every scan load is
+//               16 B per lane, 1 KiB contiguous per wave).  T diag(b) and
+//               T diag(b gamma) are split into bf16 hi + lo parts for their
+//               products, and P is stored as hi + lo, so neither is rounded to
+//               bf16 precision; K^T stays exact (its exp(g_C - g) scale is
+//               applied to U in fp32 by the scan).
 //   k_gdn_scan  one workgroup per (b, h, 32-column slice of Dv), sequential
 //               over chunks.  Columns of S evolve independently under the
 //               delta rule, so slicing Dv needs no communication.  The fp32
 //               master state lives in registers, a bf16 copy in LDS feeds the
 //               MFMAs; the next chunk's operands are loaded while the current
-//               chunk is computed.
+//               chunk is computed (the barriers order LDS only, so those loads
+//               stay in flight across them).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -45,25 +50,29 @@ struct GdnCfg {
   static constexpr int NT = D / 16;                     // 16-wide column tiles of D
   // LDS layout of the prep kernel (bytes)
   static constexpr int OFF_KS = 0;
+  static constexpr int RL = kg_row<T, D>();             // padded key-group row (columns)
   static constexpr int OFF_KG = OFF_KS + CHUNK * KP * (int)sizeof(T);
-  static constexpr int OFF_VG = OFF_KG + CHUNK * D * (int)sizeof(T);
-  static constexpr int OFF_LT = OFF_VG + CHUNK * D * (int)sizeof(T);
-  static constexpr int OFF_RS = OFF_LT + CHUNK * LTP * 4;
-  static constexpr int OFF_PS = OFF_RS + 3 * 16 * 17 * 4;
-  static constexpr int OFF_GL = OFF_PS + ((CHUNK * PP * (int)sizeof(T) + 15) / 16) * 16;
+  static constexpr int OFF_VG = OFF_KG + 16 * RL * 4 * (int)sizeof(T);
+  static constexpr int OFF_LT = OFF_VG + 16 * RL * 4 * (int)sizeof(T);
+  // P staging (before the inverse) and the inverse's block scratch (during it)
+  // share one region
+  static constexpr int OFF_PS = OFF_LT + CHUNK * LTP * 4;
+  static constexpr int OFF_RS = OFF_PS;
+  static constexpr int PS_BYTES = ((CHUNK * PP * (int)sizeof(T) + 15) / 16) * 16;
+  static constexpr int OFF_GL = OFF_PS + (PS_BYTES > 3 * 16 * 17 * 4 ? PS_BYTES : 3 * 16 * 17 * 4);
   static constexpr int PREP_LDS = OFF_GL + 4 * CHUNK * 4;
   // per chunk-head workspace (elements)
   static constexpr int64_t WN = (int64_t)CHUNK * D;   // T
   static constexpr int64_t UT = (int64_t)CHUNK * D;   // float
   static constexpr int64_t KT = (int64_t)D * CHUNK;   // T
-  static constexpr int64_t PM = (int64_t)CHUNK * CHUNK;  // T
-  static constexpr int64_t GM = 80;                   // float: gamma[64], gamma_C at 64
+  static constexpr int64_t PM = 2 * (int64_t)CHUNK * CHUNK;  // T: hi and lo parts
+  static constexpr int64_t GM = 144;  // float: gamma[64], gamma_C at 64, exp(g_C - g)[64] at 80
 };
 
 size_t gdn_ws_bytes(int io_is_bf16, int D, int64_t nch) {
   const size_t ts = io_is_bf16 ? 2 : 4;
   const size_t per = (size_t)CHUNK * D * ts + (size_t)CHUNK * D * 4 + (size_t)D * CHUNK * ts +
-                     (size_t)CHUNK * CHUNK * ts + 80 * 4;
+                     2 * (size_t)CHUNK * CHUNK * ts + 144 * 4;
   return per * (size_t)nch + 5 * 256;
 }
 
@@ -159,6 +168,7 @@ __global__ void __launch_bounds__(256, 2)
     gbl[lane] = bt * expf(s);
     ekl[lane] = expf(gC - s);
     ws.gm[ch * C::GM + lane] = expf(s);
+    ws.gm[ch * C::GM + 80 + lane] = expf(gC - s);
     if (lane == 0) ws.gm[ch * C::GM + 64] = expf(gC);
   }
   // K -> row layout and key-group layout, V -> key-group layout
@@ -178,9 +188,9 @@ __global__ void __launch_bounds__(256, 2)
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      st4<T>(Kg + kg_index<D>(kg, col + j), to_f32(frag_get<T>(kr[0], j)), to_f32(frag_get<T>(kr[1], j)),
+      st4<T>(Kg + kg_index<C::RL>(kg, col + j), to_f32(frag_get<T>(kr[0], j)), to_f32(frag_get<T>(kr[1], j)),
              to_f32(frag_get<T>(kr[2], j)), to_f32(frag_get<T>(kr[3], j)));
-      st4<T>(Vg + kg_index<D>(kg, col + j), to_f32(frag_get<T>(vr[0], j)), to_f32(frag_get<T>(vr[1], j)),
+      st4<T>(Vg + kg_index<C::RL>(kg, col + j), to_f32(frag_get<T>(vr[0], j)), to_f32(frag_get<T>(vr[1], j)),
              to_f32(frag_get<T>(vr[2], j)), to_f32(frag_get<T>(vr[3], j)));
     }
   }
@@ -214,15 +224,30 @@ __global__ void __launch_bounds__(256, 2)
       const int r = 16 * w + 4 * g + i, col = 16 * ct + c;
       const float e = (col <= r) ? expf(gl[r] - gl[col]) : 0.f;
       LT[r * C::LTP + col] = (col < r) ? bl[r] * e * akk[ct][i] : 0.f;
-      Ps[r * C::PP + col] = from_f32<T>((col <= r) ? e * aqk[ct][i] : 0.f);
+      const float pv = (col <= r) ? e * aqk[ct][i] : 0.f;
+      const T ph = from_f32<T>(pv);
+      aqk[ct][i] = pv - to_f32(ph);  // the part bf16 could not hold
+      Ps[r * C::PP + col] = ph;
     }
   __syncthreads();
 
-  // P fragments (A operand of P U in the scan; contraction over tokens, KMAP_ACC)
+  // P fragments (A operand of P U in the scan; contraction over tokens, KMAP_ACC): hi part
 #pragma unroll
   for (int k2 = 0; k2 < 2; ++k2) {
     const T* row = Ps + (16 * w + c) * C::PP + 32 * k2 + 4 * g;
-    store8<T>(ws.pm + ((ch * 4 + w) * 2 + k2) * 512 + lane * 8, ld4x2<T>(row, row + 16));
+    store8<T>(ws.pm + (((ch * 4 + w) * 2 + k2) * 2 + 0) * 512 + lane * 8, ld4x2<T>(row, row + 16));
+  }
+  __syncthreads();
+  // lo part (zero for fp32 io)
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Ps[(16 * w + 4 * g + i) * C::PP + 16 * ct + c] = from_f32<T>(aqk[ct][i]);
+  __syncthreads();
+#pragma unroll
+  for (int k2 = 0; k2 < 2; ++k2) {
+    const T* row = Ps + (16 * w + c) * C::PP + 32 * k2 + 4 * g;
+    store8<T>(ws.pm + (((ch * 4 + w) * 2 + k2) * 2 + 1) * 512 + lane * 8, ld4x2<T>(row, row + 16));
   }
 
   // T = (I + L)^-1, in place.  (a) 16x16 diagonal blocks: lane j of wave w
@@ -273,25 +298,33 @@ __global__ void __launch_bounds__(256, 2)
     ut[n] = f32x4{0.f, 0.f, 0.f, 0.f};
     wa[n] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  constexpr bool SPLIT = sizeof(T) == 2;  // bf16 operands: add the rounding remainder
 #pragma unroll
   for (int k2 = 0; k2 < 2; ++k2) {
-    Frag<T> a1, a2;
+    Frag<T> a1, a2, a1l, a2l;
     const float* trow = LT + (16 * w + c) * C::LTP;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int tk = 32 * k2 + kmap_acc(g, j);
       const float tv = trow[tk];
-      frag_set(a1, j, tv * bl[tk]);
-      frag_set(a2, j, tv * gbl[tk]);
+      const float x1 = tv * bl[tk], x2 = tv * gbl[tk];
+      frag_set(a1, j, x1);
+      frag_set(a2, j, x2);
+      frag_set(a1l, j, x1 - to_f32(frag_get<T>(a1, j)));
+      frag_set(a2l, j, x2 - to_f32(frag_get<T>(a2, j)));
     }
 #pragma unroll
     for (int n = 0; n < C::NT; ++n) {
-      const Frag<T> bv = ld4x2<T>(Vg + kg_index<D>(8 * k2 + g, 16 * n + c),
-                                  Vg + kg_index<D>(8 * k2 + 4 + g, 16 * n + c));
-      const Frag<T> bk = ld4x2<T>(Kg + kg_index<D>(8 * k2 + g, 16 * n + c),
-                                  Kg + kg_index<D>(8 * k2 + 4 + g, 16 * n + c));
+      const Frag<T> bv = ld4x2<T>(Vg + kg_index<C::RL>(8 * k2 + g, 16 * n + c),
+                                  Vg + kg_index<C::RL>(8 * k2 + 4 + g, 16 * n + c));
+      const Frag<T> bk = ld4x2<T>(Kg + kg_index<C::RL>(8 * k2 + g, 16 * n + c),
+                                  Kg + kg_index<C::RL>(8 * k2 + 4 + g, 16 * n + c));
       mma(ut[n], a1, bv);
       mma(wa[n], a2, bk);
+      if (SPLIT) {
+        mma(ut[n], a1l, bv);
+        mma(wa[n], a2l, bk);
+      }
     }
   }
   // U~ in accumulator order (the scan uses it as the C operand): [rt][n][lane][4]
@@ -303,15 +336,12 @@ __global__ void __launch_bounds__(256, 2)
   for (int n = 0; n < C::NT; ++n)
 #pragma unroll
     for (int i = 0; i < 4; ++i) Ks[(16 * w + 4 * g + i) * C::KP + 16 * n + c] = from_f32<T>(-wa[n][i]);
-  // K~^T fragments: rows = d, contraction over tokens (KMAP_ACC), scaled by exp(g_C - g)
+  // K^T fragments: rows = d, contraction over tokens (KMAP_ACC); exact copies
+  // of K (the exp(g_C - g) row scale is applied to U by the scan)
   for (int f = w; f < C::NT * 2; f += 4) {
     const int n = f >> 1, k2 = f & 1;
-    const Frag<T> kk = ld4x2<T>(Kg + kg_index<D>(8 * k2 + g, 16 * n + c),
-                                Kg + kg_index<D>(8 * k2 + 4 + g, 16 * n + c));
-    Frag<T> o;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) frag_set(o, j, to_f32(frag_get<T>(kk, j)) * ekl[32 * k2 + kmap_acc(g, j)]);
-    store8<T>(ws.kt + ((ch * C::NT + n) * 2 + k2) * 512 + lane * 8, o);
+    store8<T>(ws.kt + ((ch * C::NT + n) * 2 + k2) * 512 + lane * 8,
+              ld4x2<T>(Kg + kg_index<C::RL>(8 * k2 + g, 16 * n + c), Kg + kg_index<C::RL>(8 * k2 + 4 + g, 16 * n + c)));
   }
   __syncthreads();
 #pragma unroll
@@ -329,9 +359,10 @@ struct ScanOps {
   Frag<T> wn[KF];
   f32x4 ut[NV];
   Frag<T> qa[KF];
-  Frag<T> pa[2];
+  Frag<T> pa[2][2];  // [k2][hi, lo]
   Frag<T> kt[DTW][2];
-  f32x4 gam;
+  f32x4 gam;  // gamma of the wave's 4 rows
+  f32x4 ek;   // exp(g_C - g) of the wave's 4 rows
   float gC;
   int route;
 };
@@ -354,18 +385,30 @@ __device__ __forceinline__ void scan_load(ScanOps<T, D, DVT>& op, const GdnWs<T,
   for (int n = 0; n < O::NV; ++n)
     op.ut[n] = *reinterpret_cast<const f32x4*>(ws.ut + ((ch * 4 + w) * C::NT + nv0 + n) * 256 + lane * 4);
 #pragma unroll
-  for (int k2 = 0; k2 < 2; ++k2) op.pa[k2] = load8<T>(ws.pm + ((ch * 4 + w) * 2 + k2) * 512 + lane * 8);
+  for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+    for (int hl = 0; hl < 2; ++hl) op.pa[k2][hl] = load8<T>(ws.pm + (((ch * 4 + w) * 2 + k2) * 2 + hl) * 512 + lane * 8);
 #pragma unroll
   for (int x = 0; x < O::DTW; ++x)
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2)
       op.kt[x][k2] = load8<T>(ws.kt + ((ch * C::NT + w * O::DTW + x) * 2 + k2) * 512 + lane * 8);
   op.gam = *reinterpret_cast<const f32x4*>(ws.gm + ch * C::GM + 16 * w + 4 * g);
+  op.ek = *reinterpret_cast<const f32x4*>(ws.gm + ch * C::GM + 80 + 16 * w + 4 * g);
   op.gC = ws.gm[ch * C::GM + 64];
   op.route = rt[cc];
 }
 
-template <typename T, typename To, int D, int DVT>
+// The scan keeps global stores out of its chunk loop: on this GPU loads and
+// stores share one completion counter, and while both kinds are outstanding
+// a wait for a load can only be a wait for everything, which would drain the
+// operand prefetch every chunk.  Outputs therefore go to an LDS ring of
+// OUT_RING chunks that is flushed to memory (followed by one full wait)
+// every OUT_RING chunks; between flushes only loads are in flight and the
+// prefetch of NS - 1 chunks ahead stays in flight across chunks.
+constexpr int OUT_RING = 8;
+
+template <typename T, typename To, int D, int DVT, int NS>
 __global__ void __launch_bounds__(256, 1)
     k_gdn_scan(const T* __restrict__ q, const int32_t* __restrict__ route, GdnWs<T, D> ws,
                const float* __restrict__ S_init, To* __restrict__ o_gdn, float* __restrict__ S_final,
@@ -373,7 +416,11 @@ __global__ void __launch_bounds__(256, 1)
   using O = ScanOps<T, D, DVT>;
   constexpr int SPP = D + 16 / (int)sizeof(T);  // pitch of the transposed bf16 state [dv][dk]
   __shared__ __align__(16) T Sp[2][DVT * SPP];
-  __shared__ __align__(16) T Up[(CHUNK / 4) * DVT * 4];
+  constexpr int URL = kg_row<T, DVT>();
+  __shared__ __align__(16) To Ob[OUT_RING * CHUNK * DVT];  // output ring
+  __shared__ __align__(16) T Up[(CHUNK / 4) * URL * 4];   // U (B operand of P U)
+  __shared__ __align__(16) T Ue[(CHUNK / 4) * URL * 4];   // exp(g_C - g) U (of K^T U)
+  constexpr bool SPLIT = sizeof(T) == 2;
 
   const int nc = L / CHUNK;
   const int nvt = D / DVT;
@@ -415,8 +462,12 @@ __global__ void __launch_bounds__(256, 1)
                sm[x][n][2], sm[x][n][3]);
   };
   write_state(0);
-  __syncthreads();
+  lds_barrier();
 
+  // One chunk.  Branch-free: for a softmax-routed chunk the state update runs
+  // with decay 1 and a zero scaled U, which leaves S bit-identical (x*1 + 0),
+  // so every prefetched operand is consumed unconditionally (a use inside a
+  // branch lets the compiler sink the load into it, defeating the prefetch).
   auto step = [&](const ScanOps<T, D, DVT>& op, int cc) {
     // S fragments (B operand, contraction over d): shared by U and Q S
     Frag<T> bs[O::KF][O::NV];
@@ -437,55 +488,101 @@ __global__ void __launch_bounds__(256, 1)
         mma(u[n], op.wn[ks], bs[ks][n]);   // U = U~ - W S
         mma(oa[n], op.qa[ks], bs[ks][n]);  // Q S
       }
+    const bool lin = op.route == 1;
+    const float gce = lin ? op.gC : 1.f;
+    f32x4 eks;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) eks[i] = lin ? op.ek[i] : 0.f;
 #pragma unroll
     for (int n = 0; n < O::NV; ++n) {
-      st4<T>(&Up[kg_index<DVT>(4 * w + g, 16 * n + c)], u[n][0], u[n][1], u[n][2], u[n][3]);
+      st4<T>(&Up[kg_index<URL>(4 * w + g, 16 * n + c)], u[n][0], u[n][1], u[n][2], u[n][3]);
+      st4<T>(&Ue[kg_index<URL>(4 * w + g, 16 * n + c)], u[n][0] * eks[0], u[n][1] * eks[1], u[n][2] * eks[2],
+             u[n][3] * eks[3]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) oa[n][i] *= op.gam[i];
     }
-    __syncthreads();
-    Frag<T> bu[2][O::NV];
+    lds_barrier();
+    Frag<T> bu[2][O::NV], be[2][O::NV];
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
-      for (int n = 0; n < O::NV; ++n)
-        bu[k2][n] = ld4x2<T>(&Up[kg_index<DVT>(8 * k2 + g, 16 * n + c)],
-                             &Up[kg_index<DVT>(8 * k2 + 4 + g, 16 * n + c)]);
+      for (int n = 0; n < O::NV; ++n) {
+        bu[k2][n] = ld4x2<T>(&Up[kg_index<URL>(8 * k2 + g, 16 * n + c)], &Up[kg_index<URL>(8 * k2 + 4 + g, 16 * n + c)]);
+        be[k2][n] = ld4x2<T>(&Ue[kg_index<URL>(8 * k2 + g, 16 * n + c)], &Ue[kg_index<URL>(8 * k2 + 4 + g, 16 * n + c)]);
+      }
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
-      for (int n = 0; n < O::NV; ++n) mma(oa[n], op.pa[k2], bu[k2][n]);  // + P U
+      for (int n = 0; n < O::NV; ++n) {
+        mma(oa[n], op.pa[k2][0], bu[k2][n]);  // + P U
+        if (SPLIT) mma(oa[n], op.pa[k2][1], bu[k2][n]);
+      }
+    To* ob = Ob + (cc % OUT_RING) * CHUNK * DVT;
 #pragma unroll
     for (int n = 0; n < O::NV; ++n)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        oh[((int64_t)cc * CHUNK + 16 * w + 4 * g + i) * D + dv0 + 16 * n + c] = from_f32<To>(oa[n][i]);
-    if (op.route == 1) {  // linear-routed: commit S <- gamma_C S + K~^T U
+      for (int i = 0; i < 4; ++i) ob[(16 * w + 4 * g + i) * DVT + 16 * n + c] = from_f32<To>(oa[n][i]);
+    // S <- gamma_C S + K^T diag(exp(g_C - g)) U   (linear-routed), else S unchanged
 #pragma unroll
-      for (int x = 0; x < O::DTW; ++x)
+    for (int x = 0; x < O::DTW; ++x)
 #pragma unroll
-        for (int n = 0; n < O::NV; ++n) {
-          f32x4 acc = sm[x][n] * op.gC;
+      for (int n = 0; n < O::NV; ++n) {
+        f32x4 acc = sm[x][n] * gce;
 #pragma unroll
-          for (int k2 = 0; k2 < 2; ++k2) mma(acc, op.kt[x][k2], bu[k2][n]);
-          sm[x][n] = acc;
-        }
-      write_state(sb ^ 1);
-      sb ^= 1;
+        for (int k2 = 0; k2 < 2; ++k2) mma(acc, op.kt[x][k2], be[k2][n]);
+        sm[x][n] = acc;
+      }
+    write_state(sb ^ 1);
+    sb ^= 1;
+    lds_barrier();
+  };
+  // Output ring -> memory for chunks c_first .. c_last, then one full wait so
+  // that no store stays outstanding next to the operand loads.
+  auto flush = [&](int c_first, int c_last) {
+    const int rows = (c_last - c_first + 1) * CHUNK;
+    constexpr int PER = 16 / (int)sizeof(To);  // elements per 16-byte store
+    for (int e = threadIdx.x; e < rows * (DVT / PER); e += 256) {
+      const int r = e / (DVT / PER), cl = (e % (DVT / PER)) * PER;
+      const To* src = Ob + ((c_first % OUT_RING) * CHUNK + r) * DVT + cl;
+      To* dst = oh + ((int64_t)c_first * CHUNK + r) * D + dv0 + cl;
+      *reinterpret_cast<f32x4*>(dst) = *reinterpret_cast<const f32x4*>(src);
     }
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   };
 
-  ScanOps<T, D, DVT> opA, opB;
-  scan_load<T, D, DVT>(opA, ws, qh, rt, bh, nc, 0, nv0);
-  for (int cc = 0; cc < nc; cc += 2) {
-    if (cc + 1 < nc) scan_load<T, D, DVT>(opB, ws, qh, rt, bh, nc, cc + 1, nv0);
-    step(opA, cc);
-    if (cc + 1 < nc) {
-      if (cc + 2 < nc) scan_load<T, D, DVT>(opA, ws, qh, rt, bh, nc, cc + 2, nv0);
-      step(opB, cc + 1);
+  // NS operand sets rotate: the loads for chunk c + NS - 1 are issued before
+  // chunk c is computed (clamped to the last chunk near the end; the extra
+  // loads are harmless).  Main loop: OUT_RING chunks per iteration, no
+  // branches but the loop itself; then a generic tail.
+  static_assert(OUT_RING % NS == 0, "ring must hold whole operand rotations");
+  ScanOps<T, D, DVT> ops[NS];
+#pragma unroll
+  for (int j = 0; j < NS - 1; ++j) scan_load<T, D, DVT>(ops[j], ws, qh, rt, bh, nc, min(j, nc - 1), nv0);
+  int c0 = 0;
+  for (; c0 + OUT_RING <= nc; c0 += OUT_RING) {
+#pragma unroll
+    for (int j = 0; j < OUT_RING; ++j) {
+      scan_load<T, D, DVT>(ops[(j + NS - 1) % NS], ws, qh, rt, bh, nc, min(c0 + j + NS - 1, nc - 1), nv0);
+      __builtin_amdgcn_sched_barrier(0);
+      step(ops[j % NS], c0 + j);
     }
+    flush(c0, c0 + OUT_RING - 1);
   }
+  // tail (fewer than OUT_RING chunks): ops[0 .. NS-2] hold chunks c0 .. c0+NS-2
+  for (int cc = c0; cc < nc; ++cc) {
+    const int j = cc - c0;
+    ScanOps<T, D, DVT> cur;
+    if (j < NS - 1) {
+      // pick the already-loaded set (j is small and runtime: select by copy)
+#pragma unroll
+      for (int jj = 0; jj < NS - 1; ++jj)
+        if (jj == j) cur = ops[jj];
+    } else {
+      scan_load<T, D, DVT>(cur, ws, qh, rt, bh, nc, cc, nv0);
+    }
+    step(cur, cc);
+  }
+  if (c0 < nc) flush(c0, nc - 1);
   if (S_final) {
 #pragma unroll
     for (int x = 0; x < O::DTW; ++x)
@@ -506,6 +603,7 @@ hipError_t launch_gdn(const T* q, const T* k, const T* v, const float* alpha, co
                       hipEvent_t prep_done, void (*prof)(int, hipStream_t, int)) {
   using C = GdnCfg<T, D>;
   constexpr int DVT = 32;
+  constexpr int SCAN_NS = sizeof(T) == 2 ? 4 : 2;  // operand sets in flight in the scan
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)k_gdn_prep<T, D>,
@@ -529,7 +627,7 @@ hipError_t launch_gdn(const T* q, const T* k, const T* v, const float* alpha, co
     if (e != hipSuccess) return e;
   }
   if (prof) prof(KID_GDN_SCAN, st_scan, 0);
-  hipLaunchKernelGGL((k_gdn_scan<T, To, D, DVT>), dim3((unsigned)(B * H * (D / DVT))), dim3(256), 0,
+  hipLaunchKernelGGL((k_gdn_scan<T, To, D, DVT, SCAN_NS>), dim3((unsigned)(B * H * (D / DVT))), dim3(256), 0,
                      st_scan, q, route, ws, S_init, o_gdn, S_final, H, L, G);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -34,7 +34,8 @@ template <typename T, int D>
 struct SmCfg {
   static constexpr int KP = D + 16 / (int)sizeof(T);   // K row pitch (elements), 16 B pad
   static constexpr int KTILE = CHUNK * KP;              // elements
-  static constexpr int VTILE = (CHUNK / 4) * D * 4;     // elements (key-group layout)
+  static constexpr int VRL = kg_row<T, D>();            // padded key-group row (columns)
+  static constexpr int VTILE = (CHUNK / 4) * VRL * 4;   // elements (key-group layout)
   static constexpr int BUF = KTILE + VTILE;
   static constexpr int LDS_BYTES = 2 * BUF * (int)sizeof(T);
   static constexpr int KF = D / 32;                     // contraction steps over D
@@ -117,7 +118,7 @@ __device__ __forceinline__ void tile_sstore(const TileRegs<T, D>& r, T* buf) {
       const int kg = task / (D / 8), col = (task % (D / 8)) * 8;
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        store_col4<T>(vs + kg_index<D>(kg, col + j), frag_get<T>(r.v[i][0], j),
+        store_col4<T>(vs + kg_index<C::VRL>(kg, col + j), frag_get<T>(r.v[i][0], j),
                       frag_get<T>(r.v[i][1], j), frag_get<T>(r.v[i][2], j),
                       frag_get<T>(r.v[i][3], j));
     }
@@ -125,6 +126,7 @@ __device__ __forceinline__ void tile_sstore(const TileRegs<T, D>& r, T* buf) {
 }
 
 enum { MODE_SKIP = 0, MODE_FULL = 1, MODE_DIAG = 2 };
+constexpr float RESCALE_TH = 8.0f;  // log2 units
 
 template <typename T, typename To, int D>
 __global__ void __launch_bounds__(256, 2)
@@ -227,37 +229,48 @@ __global__ void __launch_bounds__(256, 2)
           for (int qs = 0; qs < 2; ++qs) mma(s[kt][qs], a, qf[qs][ks]);
         }
 
+      // Online softmax in log2 units.  The running max only moves when a
+      // row's tile max exceeds it by more than RESCALE_TH, so p = 2^(s - m)
+      // stays <= 2^RESCALE_TH (exact enough in fp32 and bf16) and the O
+      // rescale (D/16 x 4 multiplies per row block) is skipped for most
+      // tiles; the final division by the matching row sum is unaffected.
       Frag<T> pf[2][2];
 #pragma unroll
       for (int qs = 0; qs < 2; ++qs) {
         const int qrow = qrow_base + 16 * qs + c;
-        float mt = -INFINITY;
+        if (mode == MODE_DIAG) {
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
+          for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float z = s[kt][qs][i] * scale_log2;
-            if (mode == MODE_DIAG && (16 * kt + 4 * g + i) > qrow) z = -INFINITY;
-            s[kt][qs][i] = z;
-            mt = fmaxf(mt, z);
-          }
+            for (int i = 0; i < 4; ++i)
+              if ((16 * kt + 4 * g + i) > qrow) s[kt][qs][i] = -INFINITY;
+        }
+        float mt = fmaxf(fmaxf(s[0][qs][0], s[0][qs][1]), fmaxf(s[0][qs][2], s[0][qs][3]));
+#pragma unroll
+        for (int kt = 1; kt < 4; ++kt)
+          mt = fmaxf(mt, fmaxf(fmaxf(s[kt][qs][0], s[kt][qs][1]), fmaxf(s[kt][qs][2], s[kt][qs][3])));
         mt = wave_max_xor(mt, 16);
         mt = wave_max_xor(mt, 32);
-        const float m_new = fmaxf(m_run[qs], mt);
-        const float alpha = exp2f(m_run[qs] - m_new);
-        m_run[qs] = m_new;
+        mt *= scale_log2;  // scale > 0: max commutes with scaling
+        if (__ballot(mt > m_run[qs] + RESCALE_TH) != 0) {
+          const float m_new = fmaxf(m_run[qs], mt);
+          const float alpha = __builtin_amdgcn_exp2f(m_run[qs] - m_new);  // 0 on the first tile
+          m_run[qs] = m_new;
+          l_run[qs] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < D / 16; ++dt) o[dt][qs] *= alpha;
+        }
+        const float nm = -m_run[qs];
         float ls = 0.f;
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float pv = exp2f(s[kt][qs][i] - m_new);
+            const float pv = __builtin_amdgcn_exp2f(fmaf(s[kt][qs][i], scale_log2, nm));
             s[kt][qs][i] = pv;
             ls += pv;
           }
-        l_run[qs] = l_run[qs] * alpha + ls;
-#pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) o[dt][qs] *= alpha;
+        l_run[qs] += ls;
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
@@ -270,8 +283,8 @@ __global__ void __launch_bounds__(256, 2)
       for (int dt = 0; dt < D / 16; ++dt)
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
-          const Frag<T> a = load4x2<T>(vs_lds + kg_index<D>(8 * k2 + g, 16 * dt + c),
-                                       vs_lds + kg_index<D>(8 * k2 + 4 + g, 16 * dt + c));
+          const Frag<T> a = load4x2<T>(vs_lds + kg_index<C::VRL>(8 * k2 + g, 16 * dt + c),
+                                       vs_lds + kg_index<C::VRL>(8 * k2 + 4 + g, 16 * dt + c));
 #pragma unroll
           for (int qs = 0; qs < 2; ++qs) mma(o[dt][qs], a, pf[qs][k2]);
         }
@@ -299,11 +312,271 @@ __global__ void __launch_bounds__(256, 2)
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// bf16, D = 128: deep-pipelined variant.
+//
+// Measured on the kernel above, a tile costs ~9.4k cycles of which ~5.3k are
+// spent issuing and waiting for the next tile's global loads: every block of
+// a head streams the same K/V chunks in lockstep, so each tile is an L2 miss
+// for someone and one tile of prefetch cannot cover it.  Here the K/V tiles
+// go straight from global memory into a 4-stage LDS ring
+// (global_load_lds_dwordx4, no register staging) three tiles ahead.  Rows are
+// stored contiguously with a 16-byte-chunk XOR swizzle (the direct loads fill
+// 1 KiB of LDS per wave instruction, so rows cannot be padded):
+//   K: chunk q of row r at slot q ^ (r & 15)        (conflict-free A reads)
+//   V: chunk q of row r at slot q ^ ((r & 7) << 1)  (conflict-free transposed reads)
+// V stays row-major; the A operand of O^T = V^T P^T (4 keys of one column per
+// 8 bytes) comes from ds_read_b64_tr_b16, which transposes 4 x 4 blocks of
+// 16-bit values across each group of 16 lanes.
+// One workgroup = 8 waves = 4 chunks; waves 2m and 2m+1 own the 64 queries of
+// chunk c0 + m (32 each), so register use matches the kernel above.
+constexpr int SM2_STAGES = 4;
+constexpr int SM2_TILE_BYTES = 2 * CHUNK * 128 * 2;  // K + V, bf16, D = 128
+constexpr int SM2_LDS = SM2_STAGES * SM2_TILE_BYTES + 4 * 1024;  // + sel list (up to 1024 chunks)
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int sm2_kslot(int r, int q) { return q ^ (r & 15); }
+__device__ __forceinline__ int sm2_vslot(int r, int q) { return q ^ ((r & 7) << 1); }
+
+// 16-byte global -> LDS load of this lane to lds_wave_base + 16 * lane.  Issued
+// from inline assembly so that the compiler's wait insertion, which cannot tell
+// the ring stages apart, does not drain the whole ring before every LDS read;
+// the kernel waits for these loads itself (wait_vm + lds_barrier).
+__device__ __forceinline__ void gload_lds16(const void* gptr, const void* lds_wave_base) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_wave_base);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(base), "v"(gptr) : "memory", "m0");
+}
+
+// s_waitcnt with vmcnt = n (expcnt / lgkmcnt not waited); n in {0, 4, 8}
+__device__ __forceinline__ void wait_vm(int n) {
+  if (n >= 8) __builtin_amdgcn_s_waitcnt(0x0F78);
+  else if (n >= 4) __builtin_amdgcn_s_waitcnt(0x0F74);
+  else __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
+template <typename To>
+__global__ void __launch_bounds__(512, 1)
+    k_softmax_v2(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+                 const int32_t* __restrict__ sel_idx, const int32_t* __restrict__ nsel_before,
+                 To* __restrict__ o_sm, float* __restrict__ lse, int H, int L, int G, float scale_log2) {
+  constexpr int D = 128;
+  extern __shared__ __align__(16) unsigned char lds[];
+  int32_t* sel_l = reinterpret_cast<int32_t*>(lds + SM2_STAGES * SM2_TILE_BYTES);
+
+  const int nc = L / CHUNK;
+  const int nb = (nc + 3) / 4;
+  const int BH = (int)(gridDim.x / nb);
+  const int p = blockIdx.x;
+  int qblk, bh;
+  if ((BH & 7) == 0) {
+    const int xcd = p & 7, slot = p >> 3, hpx = BH >> 3;
+    qblk = nb - 1 - slot / hpx;
+    bh = (slot % hpx) * 8 + xcd;
+  } else {
+    qblk = nb - 1 - p / BH;
+    bh = p % BH;
+  }
+  const int b = bh / H, h = bh % H;
+  const int grp = (G == 1) ? 0 : h;
+  const int32_t* sel = sel_idx + ((int64_t)b * G + grp) * nc;
+  const int32_t* nsbp = nsel_before + ((int64_t)b * G + grp) * (nc + 1);
+  const int c0 = 4 * qblk;
+  const int nown = min(4, nc - c0);
+  const int nsb = nsbp[c0];
+  const int ntiles = nsb + nown;
+  int sm_bits = 0;
+  for (int j = 0; j < nown; ++j) sm_bits |= (nsbp[c0 + j + 1] > nsbp[c0 + j]) ? (1 << j) : 0;
+
+  const int lane = lane_id(), w = wave_id();
+  const int g = lane >> 4, c = lane & 15;
+  const int mch = w >> 1;            // chunk of this wave within the block
+  const bool active = mch < nown;
+  const int64_t head_off = (int64_t)bh * L * D;
+  const bf16* kh = k + head_off;
+  const bf16* vh = v + head_off;
+
+  // tile list in LDS (keeps its reads out of the vector-memory counter)
+  for (int i = threadIdx.x; i < nsb; i += 512) sel_l[i] = sel[i];
+  for (int i = threadIdx.x; i < nown; i += 512) sel_l[nsb + i] = c0 + i;
+
+  Frag<bf16> qf[2][4];
+  const int qtok0 = (c0 + (active ? mch : 0)) * CHUNK + 32 * (w & 1);
+#pragma unroll
+  for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qf[qs][ks] = load8<bf16>(q + head_off + (int64_t)(qtok0 + 16 * qs + c) * D + 32 * ks + 8 * g);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): nothing of ours outstanding before the ring starts
+  __syncthreads();
+
+  // tile `it` -> stage it % STAGES: 2 K + 2 V 16-byte loads per thread
+  auto issue = [&](int it) {
+    const int kc = sel_l[it];
+    unsigned char* st = lds + (it % SM2_STAGES) * SM2_TILE_BYTES;
+    const bf16* kg = kh + (int64_t)kc * CHUNK * D;
+    const bf16* vg = vh + (int64_t)kc * CHUNK * D;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int e0 = w * 128 + i * 64;  // first 16-byte chunk of this wave instruction
+      const int e = e0 + lane, r = e >> 4, sl = e & 15;
+      gload_lds16(kg + r * D + sm2_kslot(r, sl) * 8, st + e0 * 16);
+      gload_lds16(vg + r * D + sm2_vslot(r, sl) * 8, st + CHUNK * D * 2 + e0 * 16);
+    }
+  };
+
+  f32x4 o[D / 16][2];
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) o[dt][qs] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[2] = {-INFINITY, -INFINITY};
+  float l_run[2] = {0.f, 0.f};
+
+#pragma unroll
+  for (int j = 0; j < SM2_STAGES - 1; ++j)
+    if (j < ntiles) issue(j);
+
+  const int qrow_base = 32 * (w & 1);
+  for (int it = 0; it < ntiles; ++it) {
+    wait_vm(4 * (min(it + SM2_STAGES - 2, ntiles - 1) - it));  // this tile's loads have landed
+    lds_barrier();                                              // ... for every wave
+    if (it + SM2_STAGES - 1 < ntiles) issue(it + SM2_STAGES - 1);  // into the stage read last iteration
+
+    int mode;
+    if (it < nsb) {
+      mode = MODE_FULL;
+    } else {
+      const int j = it - nsb;
+      mode = (j == mch) ? MODE_DIAG : (j < mch && ((sm_bits >> j) & 1)) ? MODE_FULL : MODE_SKIP;
+    }
+    if (!active) mode = MODE_SKIP;
+    if (mode == MODE_SKIP) continue;
+
+    const unsigned char* st = lds + (it % SM2_STAGES) * SM2_TILE_BYTES;
+    const bf16* ks_l = reinterpret_cast<const bf16*>(st);
+    const unsigned char* vs_l = st + CHUNK * D * 2;
+    f32x4 s[4][2];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs) s[kt][qs] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const int r = 16 * kt + c;
+        const Frag<bf16> a = load8<bf16>(ks_l + r * D + sm2_kslot(r, 4 * ks + g) * 8);
+#pragma unroll
+        for (int qs = 0; qs < 2; ++qs) mma(s[kt][qs], a, qf[qs][ks]);
+      }
+
+    Frag<bf16> pf[2][2];
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
+      const int qrow = qrow_base + 16 * qs + c;
+      if (mode == MODE_DIAG) {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if ((16 * kt + 4 * g + i) > qrow) s[kt][qs][i] = -INFINITY;
+      }
+      float mt = fmaxf(fmaxf(s[0][qs][0], s[0][qs][1]), fmaxf(s[0][qs][2], s[0][qs][3]));
+#pragma unroll
+      for (int kt = 1; kt < 4; ++kt)
+        mt = fmaxf(mt, fmaxf(fmaxf(s[kt][qs][0], s[kt][qs][1]), fmaxf(s[kt][qs][2], s[kt][qs][3])));
+      mt = wave_max_xor(mt, 16);
+      mt = wave_max_xor(mt, 32);
+      mt *= scale_log2;
+      if (__ballot(mt > m_run[qs] + RESCALE_TH) != 0) {
+        const float m_new = fmaxf(m_run[qs], mt);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[qs] - m_new);
+        m_run[qs] = m_new;
+        l_run[qs] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) o[dt][qs] *= alpha;
+      }
+      const float nm = -m_run[qs];
+      float ls = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float pv = __builtin_amdgcn_exp2f(fmaf(s[kt][qs][i], scale_log2, nm));
+          s[kt][qs][i] = pv;
+          ls += pv;
+        }
+      l_run[qs] += ls;
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          frag_set(pf[qs][k2], j, s[2 * k2][qs][j]);
+          frag_set(pf[qs][k2], 4 + j, s[2 * k2 + 1][qs][j]);
+        }
+    }
+    // V^T fragments by transposed reads: lane c of group g reads row
+    // 32 k2 + 4 g + c / 4 (+16 for the second half), columns 16 dt + 4 (c % 4) .. +3
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      const int colq = (16 * dt + 4 * (c & 3)) >> 3;  // 16-byte chunk of the 4 columns
+      const int half = ((c & 3) & 1) * 8;            // byte offset inside it
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        const int r0 = 32 * k2 + 4 * g + (c >> 2), r1 = r0 + 16;
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4i16*)(vs_l + r0 * 256 + sm2_vslot(r0, colq) * 16 + half));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4i16*)(vs_l + r1 * 256 + sm2_vslot(r1, colq) * 16 + half));
+        Frag<bf16> a;
+        a.v = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int qs = 0; qs < 2; ++qs) mma(o[dt][qs], a, pf[qs][k2]);
+      }
+    }
+  }
+
+  if (!active) return;
+#pragma unroll
+  for (int qs = 0; qs < 2; ++qs) {
+    float lt = l_run[qs];
+    lt = wave_sum_xor(lt, 16);
+    lt = wave_sum_xor(lt, 32);
+    const float inv = 1.0f / lt;
+    const int64_t tok = qtok0 + 16 * qs + c;
+    To* orow = o_sm + head_off + tok * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      float vals[4] = {o[dt][qs][0] * inv, o[dt][qs][1] * inv, o[dt][qs][2] * inv, o[dt][qs][3] * inv};
+      store4f<To>(orow + 16 * dt + 4 * g, vals);
+    }
+    if (lse && g == 0) lse[(int64_t)bh * L + tok] = (m_run[qs] + log2f(lt)) * LN2;
+  }
+}
+
 template <typename T, typename To, int D>
 hipError_t launch_softmax_masked(const T* q, const T* k, const T* v, const int32_t* sel_idx,
                                  const int32_t* nsel_before, To* o_sm, float* lse, int B, int H,
                                  int L, int G, float scale, hipStream_t st) {
   using C = SmCfg<T, D>;
+  if constexpr (sizeof(T) == 2 && D == 128) {
+    static bool attr2 = false;
+    if (!attr2) {
+      hipError_t e = hipFuncSetAttribute((const void*)k_softmax_v2<To>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         SM2_LDS);
+      if (e != hipSuccess) return e;
+      attr2 = true;
+    }
+    const int nc = L / CHUNK;
+    if (nc <= 1024) {
+      const int64_t grid = (int64_t)B * H * ((nc + 3) / 4);
+      hipLaunchKernelGGL(k_softmax_v2<To>, dim3((unsigned)grid), dim3(512), SM2_LDS, st, (const bf16*)q,
+                         (const bf16*)k, (const bf16*)v, sel_idx, nsel_before, o_sm, lse, H, L, G, scale * LOG2E);
+      return hipGetLastError();
+    }
+  }
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)k_softmax_masked<T, To, D>,
