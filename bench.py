@@ -72,7 +72,7 @@ def source_hash(*names):
 def counters_traffic(kernel, workload, src_hash, launches_bytes_hint=None):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or
     None when it is missing or the kernel source changed since."""
-    p = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.json")
+    p = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.txt")
     if not os.path.exists(p):
         return None
     with open(p) as f:
@@ -248,6 +248,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--check-route", action="store_true")
+    ap.add_argument("--profile-copy", action="store_true",
+                    help="first run a plain 256 MiB read + 256 MiB write elementwise kernel three times, "
+                         "the known-size reference for scaling FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -261,6 +264,13 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     N.lib()
+    if args.profile_copy:
+        a = torch.ones(64 * 2 ** 20, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            torch.mul(a, 2.0, out=b)
+        torch.cuda.synchronize()
+        del a, b
     res, inp, route = time_prefill(args, N, W, O)
     print(f"prefill: {res['ms_per_step']} ms/step, {res['value']:.0f} tok/s, softmax "
           f"{res['roofline']['frac']*100:.1f}% of MFMA peak", file=sys.stderr, flush=True)
