@@ -75,7 +75,7 @@ void (*prof_fn())(int, hipStream_t, int) { return g_prof_on ? prof_hook : nullpt
 struct DevCtx {
   bool init = false;
   hipStream_t aux = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr, prep = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr, routed = nullptr;
 };
 std::mutex g_ctx_mu;
 DevCtx g_ctx[64];
@@ -92,7 +92,7 @@ natsl_status get_ctx(DevCtx** out) {
       return dev_fail(e, "hipStreamCreateWithFlags");
     if ((e = hipEventCreateWithFlags(&c.fork, hipEventDisableTiming)) != hipSuccess ||
         (e = hipEventCreateWithFlags(&c.join, hipEventDisableTiming)) != hipSuccess ||
-        (e = hipEventCreateWithFlags(&c.prep, hipEventDisableTiming)) != hipSuccess)
+        (e = hipEventCreateWithFlags(&c.routed, hipEventDisableTiming)) != hipSuccess)
       return dev_fail(e, "hipEventCreateWithFlags");
     c.init = true;
   }
@@ -223,22 +223,25 @@ hipError_t do_softmax(const natsl_dims* d, const void* q, const void* k, const v
 template <typename T, typename To>
 hipError_t do_gdn_t(const natsl_dims* d, const void* q, const void* k, const void* v, const float* a,
                     const float* b, const int32_t* route, const float* S0, void* o, float* Sf, void* ws,
-                    hipStream_t st_prep, hipStream_t st_scan, hipEvent_t ev) {
+                    hipStream_t st_prep, hipStream_t st_scan, hipEvent_t ev, hipEvent_t dep) {
   if (d->Dk == 64)
     return launch_gdn<T, To, 64>((const T*)q, (const T*)k, (const T*)v, a, b, route, S0, (To*)o, Sf, ws,
-                                 d->B, d->H, d->L, d->route_groups, st_prep, st_scan, ev, prof_fn());
+                                 d->B, d->H, d->L, d->route_groups, st_prep, st_scan, ev, dep, prof_fn());
   return launch_gdn<T, To, 128>((const T*)q, (const T*)k, (const T*)v, a, b, route, S0, (To*)o, Sf, ws,
-                                d->B, d->H, d->L, d->route_groups, st_prep, st_scan, ev, prof_fn());
+                                d->B, d->H, d->L, d->route_groups, st_prep, st_scan, ev, dep, prof_fn());
 }
+// st_prep / st_scan: streams of the chunk prep and of the scan (an event orders
+// them when they differ); dep: an event the scan waits for (the routes), or null
 hipError_t do_gdn(const natsl_dims* d, const void* q, const void* k, const void* v, const float* a,
                   const float* b, const int32_t* route, const float* S0, void* o, natsl_dtype od, float* Sf,
-                  void* ws, hipStream_t st_prep, hipStream_t st_scan = nullptr, hipEvent_t ev = nullptr) {
+                  void* ws, hipStream_t st_prep, hipStream_t st_scan = nullptr, hipEvent_t ev = nullptr,
+                  hipEvent_t dep = nullptr) {
   if (!st_scan) st_scan = st_prep;
   if (d->io == NATSL_BF16)
-    return od == NATSL_BF16 ? do_gdn_t<bf16, bf16>(d, q, k, v, a, b, route, S0, o, Sf, ws, st_prep, st_scan, ev)
-                            : do_gdn_t<bf16, float>(d, q, k, v, a, b, route, S0, o, Sf, ws, st_prep, st_scan, ev);
-  return od == NATSL_BF16 ? do_gdn_t<float, bf16>(d, q, k, v, a, b, route, S0, o, Sf, ws, st_prep, st_scan, ev)
-                          : do_gdn_t<float, float>(d, q, k, v, a, b, route, S0, o, Sf, ws, st_prep, st_scan, ev);
+    return od == NATSL_BF16 ? do_gdn_t<bf16, bf16>(d, q, k, v, a, b, route, S0, o, Sf, ws, st_prep, st_scan, ev, dep)
+                            : do_gdn_t<bf16, float>(d, q, k, v, a, b, route, S0, o, Sf, ws, st_prep, st_scan, ev, dep);
+  return od == NATSL_BF16 ? do_gdn_t<float, bf16>(d, q, k, v, a, b, route, S0, o, Sf, ws, st_prep, st_scan, ev, dep)
+                          : do_gdn_t<float, float>(d, q, k, v, a, b, route, S0, o, Sf, ws, st_prep, st_scan, ev, dep);
 }
 
 template <typename Tq, typename Tb>
@@ -403,14 +406,18 @@ natsl_status natsl_forward(const natsl_dims* dims, const natsl_forward_args* a, 
   int32_t* route = a->route_out ? a->route_out : w.route;
   void* o_sm = a->o_sm_dbg ? a->o_sm_dbg : w.o_sm;
   void* o_gd = a->o_gdn_dbg ? a->o_gdn_dbg : w.o_gdn;
-  hipError_t e = do_route(dims, a->x, a->w_score, a->b_score, a->route_override, route, w.sel, w.nsb,
-                          a->scores_out, stream);
+  // Fork: the helper stream waits for the caller's stream (inputs ready) and
+  // runs the chunk prep, which does not depend on the routes, while the caller's
+  // stream routes; the scan then waits for the routes.  The softmax branch runs
+  // on the caller's stream meanwhile; the merge waits for both.
+  hipError_t e;
+  if ((e = hipEventRecord(ctx->fork, stream)) != hipSuccess) return dev_fail(e, "hipEventRecord");
+  if ((e = hipStreamWaitEvent(ctx->aux, ctx->fork, 0)) != hipSuccess) return dev_fail(e, "hipStreamWaitEvent");
+  e = do_route(dims, a->x, a->w_score, a->b_score, a->route_override, route, w.sel, w.nsb, a->scores_out, stream);
   if (e != hipSuccess) return dev_fail(e, "natsl_forward/route");
-  // The chunk prep (fully parallel, bandwidth-bound) runs alone on the caller's
-  // stream; then the state scan (one workgroup per (b, h, Dv slice), latency-
-  // bound) forks onto the helper stream and overlaps the softmax branch.
+  if ((e = hipEventRecord(ctx->routed, stream)) != hipSuccess) return dev_fail(e, "hipEventRecord");
   e = do_gdn(dims, a->q, a->k, a->v, a->alpha, a->beta, route, a->S_init, o_gd, a->branch_dtype, a->S_final,
-             w.gdn, stream, ctx->aux, ctx->prep);
+             w.gdn, ctx->aux, ctx->aux, nullptr, ctx->routed);
   if (e != hipSuccess) return dev_fail(e, "natsl_forward/gdn");
   e = do_softmax(dims, a->q, a->k, a->v, w.sel, w.nsb, o_sm, a->branch_dtype, nullptr, stream);
   if (e != hipSuccess) return dev_fail(e, "natsl_forward/softmax");

@@ -600,7 +600,7 @@ template <typename T, typename To, int D>
 hipError_t launch_gdn(const T* q, const T* k, const T* v, const float* alpha, const float* beta,
                       const int32_t* route, const float* S_init, To* o_gdn, float* S_final, void* wsp,
                       int B, int H, int L, int G, hipStream_t st_prep, hipStream_t st_scan,
-                      hipEvent_t prep_done, void (*prof)(int, hipStream_t, int)) {
+                      hipEvent_t prep_done, hipEvent_t scan_dep, void (*prof)(int, hipStream_t, int)) {
   using C = GdnCfg<T, D>;
   constexpr int DVT = 32;
   constexpr int SCAN_NS = sizeof(T) == 2 ? 4 : 2;  // operand sets in flight in the scan
@@ -626,6 +626,10 @@ hipError_t launch_gdn(const T* q, const T* k, const T* v, const float* alpha, co
     e = hipStreamWaitEvent(st_scan, prep_done, 0);
     if (e != hipSuccess) return e;
   }
+  if (scan_dep) {  // the routes come from another stream
+    e = hipStreamWaitEvent(st_scan, scan_dep, 0);
+    if (e != hipSuccess) return e;
+  }
   if (prof) prof(KID_GDN_SCAN, st_scan, 0);
   hipLaunchKernelGGL((k_gdn_scan<T, To, D, DVT, SCAN_NS>), dim3((unsigned)(B * H * (D / DVT))), dim3(256), 0,
                      st_scan, q, route, ws, S_init, o_gdn, S_final, H, L, G);
@@ -639,7 +643,7 @@ hipError_t launch_gdn(const T* q, const T* k, const T* v, const float* alpha, co
   template hipError_t launch_gdn<T, To, D>(const T*, const T*, const T*, const float*, const float*, \
                                            const int32_t*, const float*, To*, float*, void*, int,  \
                                            int, int, int, hipStream_t, hipStream_t, hipEvent_t,     \
-                                           void (*)(int, hipStream_t, int));
+                                           hipEvent_t, void (*)(int, hipStream_t, int));
 INST(float, float, 64)
 INST(float, float, 128)
 INST(float, bf16, 64)

@@ -45,7 +45,7 @@ template <typename T, typename To, int D>
 hipError_t launch_gdn(const T* q, const T* k, const T* v, const float* alpha, const float* beta,
                       const int32_t* route, const float* S_init, To* o_gdn, float* S_final, void* ws,
                       int B, int H, int L, int G, hipStream_t st_prep, hipStream_t st_scan,
-                      hipEvent_t prep_done, void (*prof)(int, hipStream_t, int));
+                      hipEvent_t prep_done, hipEvent_t scan_dep, void (*prof)(int, hipStream_t, int));
 
 struct DecodeLaunch {
   int B, H, G, d, cap;

@@ -29,14 +29,21 @@ __global__ void __launch_bounds__(256) k_merge(const Tq* __restrict__ q, const T
   load8f<Tq>(q + t * D + col, qv);
   load8f<Tb>(o_sm + t * D + col, a);
   load8f<Tb>(o_gdn + t * D + col, b);
-  const float* wm = w_mix + (int64_t)h * wmix_hs;
+  // the lane's 8 rows of W_mix [D, 2] are 16 consecutive floats
+  const f32x4* wm4 = reinterpret_cast<const f32x4*>(w_mix + (int64_t)h * wmix_hs + col * 2);
+  float wm[16];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const f32x4 t4 = wm4[j];
+    wm[4 * j] = t4[0]; wm[4 * j + 1] = t4[1]; wm[4 * j + 2] = t4[2]; wm[4 * j + 3] = t4[3];
+  }
   float ssa = 0.f, ssb = 0.f, z0 = 0.f, z1 = 0.f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     ssa += a[j] * a[j];
     ssb += b[j] * b[j];
-    z0 += qv[j] * wm[(col + j) * 2];
-    z1 += qv[j] * wm[(col + j) * 2 + 1];
+    z0 += qv[j] * wm[2 * j];
+    z1 += qv[j] * wm[2 * j + 1];
   }
 #pragma unroll
   for (int m = LPT / 2; m >= 1; m >>= 1) {
@@ -51,13 +58,18 @@ __global__ void __launch_bounds__(256) k_merge(const Tq* __restrict__ q, const T
   const float e0 = expf(z0 - zm), e1 = expf(z1 - zm);
   const float inv = 1.0f / (e0 + e1);
   const float w0 = e0 * inv * ra, w1 = e1 * inv * rb;
+  float gs[8], gl[8];
+  if (g_sm) load8f<float>(g_sm + col, gs);
+  else
+#pragma unroll
+    for (int j = 0; j < 8; ++j) gs[j] = 1.f;
+  if (g_lin) load8f<float>(g_lin + col, gl);
+  else
+#pragma unroll
+    for (int j = 0; j < 8; ++j) gl[j] = 1.f;
   float o[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const float gs = g_sm ? g_sm[col + j] : 1.f;
-    const float gl = g_lin ? g_lin[col + j] : 1.f;
-    o[j] = w0 * a[j] * gs + w1 * b[j] * gl;
-  }
+  for (int j = 0; j < 8; ++j) o[j] = w0 * a[j] * gs[j] + w1 * b[j] * gl[j];
   if (valid) {
     Frag<To> f;
 #pragma unroll
