@@ -62,10 +62,13 @@ def gdn_flops(B, H, nc, n_lin, D, chunk=64):
 
 
 def source_hash(*names):
+    """Hash of the kernel sources and of the compiler flags they are built with."""
+    from linear_attention_natsl_amd import build as B
     h = hashlib.sha256()
     for n in names:
         with open(os.path.join(ROOT, "linear_attention_natsl_amd", "csrc", n), "rb") as f:
             h.update(f.read())
+        h.update(" ".join(B.FLAGS[:-1] + B.FILE_FLAGS.get(n, [])).encode())
     return h.hexdigest()[:16]
 
 
@@ -82,6 +85,22 @@ def counters_traffic(kernel, workload, src_hash, launches_bytes_hint=None):
     return c.get("hbm_bytes_per_launch")
 
 
+SETTLE_S = 0.3
+
+
+def settle(fn, seconds=SETTLE_S):
+    """Runs fn untimed for `seconds`: the GPU's clocks take tens of milliseconds
+    of sustained load to leave their idle state (the first forward steps of a
+    cold GPU run up to 30% slower), and the timed steps should see the steady
+    state a serving or training loop sees."""
+    import torch
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+
+
 def time_prefill(args, N, W, O):
     import torch
     wl = W.WORKLOADS[args.workload]
@@ -95,6 +114,7 @@ def time_prefill(args, N, W, O):
     fwd = N.Forward(dm, device=dev)
     call = lambda: fwd(t["x"], t["q"], t["k"], t["v"], t["alpha"], t["beta"], t["w_score"], t["w_mix"],
                        b_score=t["b_score"], g_sm=t["g_sm"], g_lin=t["g_lin"])
+    settle(call)
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
@@ -168,6 +188,17 @@ def time_decode(args, N, W):
          f32(new["w_score"]), f32(new["w_mix"])]
     rows0 = (st.n_committed[:, 0] + st.n_open).cpu().numpy().astype(np.int64)
     steps, warm = args.decode_steps, 3
+    # settle the clocks with bursts of steps, each followed by a restore of the
+    # counters and states (the cache rows the burst appended are rewritten by
+    # the timed steps), so the cache never grows past its capacity
+    saved = [x.clone() for x in (st.n_committed, st.n_open, st.S_carry, st.S_work, st.x_sum, st.err)]
+
+    def burst():
+        for _ in range(32):
+            dec(*a)
+        for x, y in zip((st.n_committed, st.n_open, st.S_carry, st.S_work, st.x_sum, st.err), saved):
+            x.copy_(y)
+    settle(burst)
     for _ in range(warm):
         dec(*a)
     torch.cuda.synchronize()
@@ -241,8 +272,8 @@ def cpu_baseline(W, O, inp, route, workload):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long", choices=["long", "prefill", "degen"])
     ap.add_argument("--decode-steps", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true")
