@@ -141,6 +141,44 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// 16-byte global -> LDS load of this lane to lds_wave_base + 16 * lane (the
+// wave writes 1 KiB of LDS contiguously).  Issued from inline assembly so that
+// the compiler's wait insertion, which cannot tell ring stages apart, does not
+// drain every outstanding load before each LDS read; kernels that use it wait
+// for these loads themselves (wait_vm, then a barrier for the other waves).
+__device__ __forceinline__ void gload_lds16(const void* gptr, const void* lds_wave_base) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_wave_base);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(base), "v"(gptr) : "memory", "m0");
+}
+// The same with a wave-uniform 64-bit base in SGPRs and a 32-bit lane offset
+// (one VGPR per distinct offset pattern instead of a 64-bit address per load).
+// readfirstlane returns int: both halves are zero-extended before they are
+// joined, a sign-extended low half would corrupt the high one.
+__device__ __forceinline__ void gload_lds16_s(const void* gbase, uint32_t voff, const void* lds_wave_base) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_wave_base);
+  const uint64_t gp = (uint64_t)(uintptr_t)gbase;
+  const uint32_t ghi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(gp >> 32));
+  const uint32_t glo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)gp);
+  const uint64_t gs = ((uint64_t)ghi << 32) | (uint64_t)glo;
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(base), "v"(voff), "s"(gs)
+               : "memory", "m0");
+}
+// s_waitcnt with vmcnt = n (expcnt / lgkmcnt not waited); n in {0, 4, 8}
+__device__ __forceinline__ void wait_vm(int n) {
+  if (n >= 8) __builtin_amdgcn_s_waitcnt(0x0F78);
+  else if (n >= 4) __builtin_amdgcn_s_waitcnt(0x0F74);
+  else __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+// Hides a wave-uniform value from the optimiser.  A ring stage offset is one
+// of a few values; left visible, the compiler precomputes the addresses of
+// every stage and keeps them all live.
+__device__ __forceinline__ int opaque_sgpr(int x) {
+  x = __builtin_amdgcn_readfirstlane(x);
+  asm volatile("" : "+s"(x));
+  return x;
+}
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 

@@ -125,6 +125,10 @@ template <> __device__ __forceinline__ void st4<float>(float* p, float a, float 
   *reinterpret_cast<f32x4*>(p) = v;
 }
 
+// The scan runs one workgroup per head for bf16 with D = 128, and one per
+// (head, 32-column slice) otherwise; the two read -W in different orders.
+template <typename T, int D> constexpr bool scan_head_form() { return sizeof(T) == 2 && D == 128; }
+
 // ---------------------------------------------------------------- prep ----
 template <typename T, int D>
 __global__ void __launch_bounds__(256, 2)
@@ -344,10 +348,14 @@ __global__ void __launch_bounds__(256, 2)
               ld4x2<T>(Kg + kg_index<C::RL>(8 * k2 + g, 16 * n + c), Kg + kg_index<C::RL>(8 * k2 + 4 + g, 16 * n + c)));
   }
   __syncthreads();
+  // the head-per-workgroup scan (bf16, D = 128) packs its state B operand
+  // straight from accumulators, so -W uses the accumulator-shaped map there
 #pragma unroll
-  for (int ks = 0; ks < C::KF; ++ks)
+  for (int ks = 0; ks < C::KF; ++ks) {
+    const T* row = Ks + (16 * w + c) * C::KP + 32 * ks;
     store8<T>(ws.wn + ((ch * 4 + w) * C::KF + ks) * 512 + lane * 8,
-              load8<T>(Ks + (16 * w + c) * C::KP + 32 * ks + 8 * g));
+              scan_head_form<T, D>() ? ld4x2<T>(row + 4 * g, row + 16 + 4 * g) : load8<T>(row + 8 * g));
+  }
 }
 
 // ---------------------------------------------------------------- scan ----
@@ -596,6 +604,336 @@ __global__ void __launch_bounds__(256, 1)
   }
 }
 
+// --------------------------------------------------- scan, head form ----
+// bf16, D = 128: NSPLIT workgroups of NW waves per (b, h).  Wave w of part p
+// owns the state columns dv0 .. dv0 + 16 NV - 1, dv0 = 16 NV (NW p + w)
+// (NV = 128 / (16 NW NSPLIT) column tiles, all 128 rows) and runs the whole
+// chunk recurrence for them in registers: columns
+// of S evolve independently, so the waves never exchange state, and the
+// dependency chain of a chunk (S -> U = U~ - W S -> S' = gamma_C S +
+// K^T diag(exp(g_C - g)) U) has no barrier and no LDS round trip.  The state's
+// B operand (contraction over d) is packed from the fp32 accumulators directly
+// (accumulator-shaped map, which is how the chunk prep writes -W for this
+// form); U's B operand (contraction over tokens) likewise.
+// The operands every wave needs (-W, Q, P hi + lo, K^T: 64 KiB, plus the
+// decays) go through a 2-stage LDS ring by direct global -> LDS loads issued
+// one chunk ahead; each wave loads its own U~ columns into registers one chunk
+// ahead.  All loads of a chunk, and the output stores of the previous one, are
+// issued a whole chunk before the single vmcnt(0) wait at the top of the next
+// chunk.
+constexpr int SCH_WN = 0;              // -W fragments [rt 4][ks 4][lane][8]
+constexpr int SCH_Q = 16384;           // Q rows, 16-byte chunk q of row r at slot q ^ (r & 15)
+constexpr int SCH_PM = 2 * 16384;      // P fragments [rt 4][k2 2][hi, lo][lane][8]
+constexpr int SCH_KT = 3 * 16384;      // K^T fragments [dt 8][k2 2][lane][8]
+constexpr int SCH_GM = 4 * 16384;      // gamma[64], gamma_C at 64, exp(g_C - g)[64] at 80 (fp32)
+constexpr int SCH_STAGE = SCH_GM + 576;
+constexpr int SCH_ROUTE = 2 * SCH_STAGE;
+constexpr int SCH_NW = 4;              // waves per workgroup
+constexpr int SCH_NSPLIT = 2;          // workgroups per head
+// (every wave reads all 64 KiB of shared operands from LDS per chunk, so LDS
+// traffic per CU grows with the waves per workgroup: two workgroups of four
+// waves per head halve it against one of eight, at the price of loading the
+// shared operands twice from L2)
+
+__device__ __forceinline__ Frag<bf16> pack_acc2(const f32x4& a, const f32x4& b) {
+  Frag<bf16> f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    f.v[j] = (bf16)a[j];
+    f.v[4 + j] = (bf16)b[j];
+  }
+  return f;
+}
+
+// (launch bounds of two waves per SIMD cap the wave at 256 VGPRs, so that the
+// compiler keeps the matrix products in their VGPR form: with 512 registers it
+// moves the accumulators to AGPRs and copies them back and forth for every
+// VALU touch of the state)
+template <typename To, int NW, int NSPLIT>
+__global__ void __launch_bounds__(64 * NW, 8 / NW)
+    k_gdn_scan_head(const bf16* __restrict__ q, const int32_t* __restrict__ route, GdnWs<bf16, 128> ws,
+                    const float* __restrict__ S_init, To* __restrict__ o_gdn, float* __restrict__ S_final,
+                    int H, int L, int G) {
+  constexpr int D = 128;
+  constexpr int NV = D / (16 * NW * NSPLIT);  // 16-column state tiles per wave
+  static_assert(NV >= 1 && NW >= 4, "the Q swizzle assumes 4 KiB-aligned load groups");
+  constexpr int NB = 16 / NW;        // 1 KiB blocks of each 16 KiB operand per wave
+  using C = GdnCfg<bf16, D>;
+  extern __shared__ __align__(16) unsigned char lds[];
+  int32_t* rl = reinterpret_cast<int32_t*>(lds + SCH_ROUTE);
+
+  const int nc = L / CHUNK;
+  const int64_t bh = blockIdx.x / NSPLIT;
+  const int part = (int)(blockIdx.x % NSPLIT);
+  const int b = (int)(bh / H), h = (int)(bh % H);
+  const int grp = (G == 1) ? 0 : h;
+  const int32_t* rt_g = route + ((int64_t)b * G + grp) * nc;
+  const bf16* qh = q + bh * L * D;
+  To* oh = o_gdn + bh * L * D;
+  const int lane = lane_id(), w = wave_id();
+  const int g = lane >> 4, c = lane & 15;
+  const int dv0 = 16 * NV * (NW * part + w);
+  const int nt0 = NV * (NW * part + w);  // first 16-column tile of this wave
+
+  for (int i = threadIdx.x; i < nc; i += 64 * NW) rl[i] = rt_g[i];
+
+  // fp32 state: rows d = 16 dt + 4g + i, columns dv0 + 16 nn + c
+  f32x4 sm[8][NV];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+    for (int nn = 0; nn < NV; ++nn) sm[dt][nn] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (S_init) {
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int nn = 0; nn < NV; ++nn)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sm[dt][nn][i] = S_init[(bh * D + 16 * dt + 4 * g + i) * D + dv0 + 16 * nn + c];
+  }
+
+  // chunk cc's shared operands -> stage st.  Wave w loads the 1 KiB blocks
+  // NW i + w of each 16 KiB operand; for Q, LDS position e = 64 blk + lane
+  // holds 16-byte chunk (e & 15) ^ (r & 15) of row r = e / 16, and r & 15 does
+  // not depend on i
+  const uint32_t off_lin = (uint32_t)(w * 1024 + lane * 16);
+  const int qr = 4 * w + (lane >> 4);
+  const uint32_t off_q = (uint32_t)(w * 1024 + (lane >> 4) * 256 + (((lane & 15) ^ (qr & 15)) * 16));
+  // part 0: -W, 1: Q, 2: P, 3: K^T and the decays
+  auto load_stage = [&](int cc, int st, int part) {
+    const int64_t ch = bh * nc + cc;
+    unsigned char* sb = lds + opaque_sgpr(st * SCH_STAGE);
+    const unsigned char* src;
+    uint32_t off = off_lin;
+    int dst;
+    if (part == 0) {
+      src = reinterpret_cast<const unsigned char*>(ws.wn + ch * C::WN);
+      dst = SCH_WN;
+    } else if (part == 1) {
+      src = reinterpret_cast<const unsigned char*>(qh + (int64_t)cc * CHUNK * D);
+      off = off_q;
+      dst = SCH_Q;
+    } else if (part == 2) {
+      src = reinterpret_cast<const unsigned char*>(ws.pm + ch * C::PM);
+      dst = SCH_PM;
+    } else {
+      src = reinterpret_cast<const unsigned char*>(ws.kt + ch * C::KT);
+      dst = SCH_KT;
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) gload_lds16_s(src + i * NW * 1024, off, sb + dst + (NW * i + w) * 1024);
+    if (part == 3 && w == 0 && lane < 36)  // 576 bytes of decays
+      gload_lds16_s(ws.gm + ch * C::GM, (uint32_t)(lane * 16), sb + SCH_GM);
+  };
+  // this wave's U~ columns of chunk cc, accumulator order [rt][nn]
+  // (uniform base + 32-bit lane offset: the compiler can use the SGPR-base
+  // forms and needs no 64-bit address per load or store)
+  const uint32_t ut_off = (uint32_t)(nt0 * 256 + lane * 4);
+  auto load_ut = [&](int cc, f32x4 (&u)[4][NV]) {
+    const float* ub = ws.ut + (bh * nc + cc) * 4 * C::NT * 256;
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int nn = 0; nn < NV; ++nn)
+        u[rt][nn] = *reinterpret_cast<const f32x4*>(ub + (ut_off + (uint32_t)((rt * C::NT + nn) * 256)));
+  };
+  const uint32_t o_off = (uint32_t)(4 * g * D + dv0 + c);
+  auto store_o = [&](int cc, const f32x4 (&o)[4][NV]) {
+    To* ob = oh + (int64_t)cc * CHUNK * D;
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int nn = 0; nn < NV; ++nn)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ob[o_off + (uint32_t)((16 * rt + i) * D + 16 * nn)] = from_f32<To>(o[rt][nn][i]);
+  };
+
+  // Operand fragments from LDS are read one group ahead of the products that
+  // use them (sched_barrier fences pin that order: left free, the scheduler
+  // hoists every read of the chunk and runs out of registers; fenced without a
+  // lead, every group waits out the LDS latency).
+  struct FragA { Frag<bf16> w[4], q[4]; };  // -W and Q for one 16-token row tile, all 4 d steps
+  auto read_a = [&](const unsigned char* sb, int rt, FragA& f) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      f.w[ks] = load8<bf16>(reinterpret_cast<const bf16*>(sb + SCH_WN + ((rt * 4 + ks) * 64 + lane) * 16));
+      // Q row 16 rt + c, columns 32 ks + 4g .. +3 and 32 ks + 16 + 4g .. +3
+      const unsigned char* qrow = sb + SCH_Q + (16 * rt + c) * 256;
+      const int q1 = 4 * ks + (g >> 1), q2 = q1 + 2, half = (g & 1) * 8;
+      f.q[ks] = ld4x2<bf16>(reinterpret_cast<const bf16*>(qrow + ((q1 ^ c) * 16) + half),
+                            reinterpret_cast<const bf16*>(qrow + ((q2 ^ c) * 16) + half));
+    }
+  };
+  struct FragP { Frag<bf16> p[2][2][2]; };  // P for two row tiles: [tile][k2][hi, lo]
+  auto read_p = [&](const unsigned char* sb, int rt0, FragP& f) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+        for (int hl = 0; hl < 2; ++hl)
+          f.p[t][k2][hl] = load8<bf16>(
+              reinterpret_cast<const bf16*>(sb + SCH_PM + ((((rt0 + t) * 2 + k2) * 2 + hl) * 64 + lane) * 16));
+  };
+  struct FragK { Frag<bf16> k[4][2]; };  // K^T for four d tiles: [tile][k2]
+  auto read_k = [&](const unsigned char* sb, int dt0, FragK& f) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2)
+        f.k[t][k2] = load8<bf16>(reinterpret_cast<const bf16*>(sb + SCH_KT + (((dt0 + t) * 2 + k2) * 64 + lane) * 16));
+  };
+  auto fence = []() { __builtin_amdgcn_sched_barrier(0); };
+
+  // chunk cc from stage st: u holds its U~ on entry (U afterwards), u_nxt
+  // receives the next chunk's U~; o_prev holds the previous chunk's outputs on
+  // entry (stored here, a whole chunk before the wait that covers the stores)
+  // and o receives this chunk's
+  auto step = [&](int cc, int st, f32x4 (&u)[4][NV], f32x4 (&u_nxt)[4][NV], f32x4 (&o)[4][NV],
+                  f32x4 (&o_prev)[4][NV]) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this chunk's loads (and older stores) are done
+    lds_barrier();                       // ... for every wave; every wave is done with chunk cc - 1
+    // pin this chunk's U~ ahead of the next chunk's loads
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int nn = 0; nn < NV; ++nn) asm volatile("" : "+v"(u[rt][nn]));
+    if (cc > 0) store_o(cc - 1, o_prev);  // outputs of chunk cc - 1
+    // The next chunk's loads are spread over this one: a CU moves only a few
+    // tens of bytes per clock from L2, and issuing all ~96 KiB at once stalls
+    // the wave for the whole transfer instead of overlapping it with compute.
+    const bool more = cc + 1 < nc;
+    if (more) load_stage(cc + 1, st ^ 1, 0);
+    const unsigned char* sb = lds + opaque_sgpr(st * SCH_STAGE);
+    const float* gm = reinterpret_cast<const float*>(sb + SCH_GM);
+    const bool lin = rl[cc] == 1;
+
+    // state B operand, contraction over d
+    Frag<bf16> bs[4][NV];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int nn = 0; nn < NV; ++nn) bs[ks][nn] = pack_acc2(sm[2 * ks][nn], sm[2 * ks + 1][nn]);
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int nn = 0; nn < NV; ++nn) o[rt][nn] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // U = U~ - W S  and  Q S, one row tile per group
+    FragA fa[2];
+    FragP fp[2];
+    read_a(sb, 0, fa[0]);
+    fence();
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      if (rt < 3) read_a(sb, rt + 1, fa[(rt + 1) & 1]);
+      else read_p(sb, 0, fp[0]);
+      if (more && rt == 1) load_stage(cc + 1, st ^ 1, 1);
+      if (more && rt == 3) load_stage(cc + 1, st ^ 1, 2);
+      fence();
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int nn = 0; nn < NV; ++nn) {
+          mma(u[rt][nn], fa[rt & 1].w[ks], bs[ks][nn]);
+          mma(o[rt][nn], fa[rt & 1].q[ks], bs[ks][nn]);
+        }
+      fence();
+    }
+    // branch-free rollback: a softmax-routed chunk updates with decay 1 and a
+    // zero scaled U, which leaves S bit-identical
+    const float gce = lin ? gm[64] : 1.f;
+    Frag<bf16> bu[2][NV], be[2][NV];
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      const f32x4 ek0 = *reinterpret_cast<const f32x4*>(gm + 80 + 32 * k2 + 4 * g);
+      const f32x4 ek1 = *reinterpret_cast<const f32x4*>(gm + 80 + 32 * k2 + 16 + 4 * g);
+#pragma unroll
+      for (int nn = 0; nn < NV; ++nn) {
+        bu[k2][nn] = pack_acc2(u[2 * k2][nn], u[2 * k2 + 1][nn]);
+        f32x4 e0, e1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          e0[i] = lin ? u[2 * k2][nn][i] * ek0[i] : 0.f;
+          e1[i] = lin ? u[2 * k2 + 1][nn][i] * ek1[i] : 0.f;
+        }
+        be[k2][nn] = pack_acc2(e0, e1);
+      }
+    }
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      const f32x4 gam = *reinterpret_cast<const f32x4*>(gm + 16 * rt + 4 * g);
+#pragma unroll
+      for (int nn = 0; nn < NV; ++nn) o[rt][nn] *= gam;
+    }
+    // O += P U  (P as hi + lo), two row tiles per group
+    FragK fk[2];
+#pragma unroll
+    for (int gp = 0; gp < 2; ++gp) {
+      if (gp == 0) read_p(sb, 2, fp[1]);
+      else read_k(sb, 0, fk[0]);
+      if (more && gp == 1) {
+        load_stage(cc + 1, st ^ 1, 3);
+        load_ut(cc + 1, u_nxt);
+      }
+      fence();
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+          for (int hl = 0; hl < 2; ++hl)
+#pragma unroll
+            for (int nn = 0; nn < NV; ++nn) mma(o[2 * gp + t][nn], fp[gp].p[t][k2][hl], bu[k2][nn]);
+      fence();
+    }
+    // S <- gamma_C S + K^T diag(exp(g_C - g)) U, four d tiles per group
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int nn = 0; nn < NV; ++nn) sm[dt][nn] *= gce;
+#pragma unroll
+    for (int gk = 0; gk < 2; ++gk) {
+      if (gk == 0) read_k(sb, 4, fk[1]);
+      fence();
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+          for (int nn = 0; nn < NV; ++nn) mma(sm[4 * gk + t][nn], fk[gk].k[t][k2], be[k2][nn]);
+      fence();
+    }
+  };
+
+  f32x4 utA[4][NV], utB[4][NV], oA[4][NV], oB[4][NV];
+#pragma unroll
+  for (int part = 0; part < 4; ++part) load_stage(0, 0, part);
+  load_ut(0, utA);
+  int cc = 0;
+  for (; cc + 2 <= nc; cc += 2) {
+    step(cc, 0, utA, utB, oA, oB);
+    step(cc + 1, 1, utB, utA, oB, oA);
+  }
+  const bool odd = cc < nc;
+  if (odd) step(cc, 0, utA, utB, oA, oB);
+  // outputs of the last chunk
+  if (odd)
+    store_o(nc - 1, oA);
+  else
+    store_o(nc - 1, oB);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // no load may still be in flight into LDS at the end
+  if (S_final) {
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int nn = 0; nn < NV; ++nn)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          S_final[(bh * D + 16 * dt + 4 * g + i) * D + dv0 + 16 * nn + c] = sm[dt][nn][i];
+  }
+}
+
 template <typename T, typename To, int D>
 hipError_t launch_gdn(const T* q, const T* k, const T* v, const float* alpha, const float* beta,
                       const int32_t* route, const float* S_init, To* o_gdn, float* S_final, void* wsp,
@@ -631,8 +969,24 @@ hipError_t launch_gdn(const T* q, const T* k, const T* v, const float* alpha, co
     if (e != hipSuccess) return e;
   }
   if (prof) prof(KID_GDN_SCAN, st_scan, 0);
-  hipLaunchKernelGGL((k_gdn_scan<T, To, D, DVT, SCAN_NS>), dim3((unsigned)(B * H * (D / DVT))), dim3(256), 0,
-                     st_scan, q, route, ws, S_init, o_gdn, S_final, H, L, G);
+  if constexpr (scan_head_form<T, D>()) {
+    static bool attr_head = false;
+    if (!attr_head) {
+      e = hipFuncSetAttribute((const void*)k_gdn_scan_head<To, SCH_NW, SCH_NSPLIT>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, SCH_ROUTE + 4096);
+      if (e != hipSuccess) return e;
+      attr_head = true;
+    }
+    if (nc > 1024) return hipErrorInvalidValue;
+    const size_t lds = SCH_ROUTE + ((size_t)nc * 4 + 255) / 256 * 256;
+    hipLaunchKernelGGL((k_gdn_scan_head<To, SCH_NW, SCH_NSPLIT>), dim3((unsigned)(B * H * SCH_NSPLIT)), dim3(64 * SCH_NW),
+                       lds, st_scan,
+                       (const bf16*)q,
+                       route, ws, S_init, o_gdn, S_final, H, L, G);
+  } else {
+    hipLaunchKernelGGL((k_gdn_scan<T, To, D, DVT, SCAN_NS>), dim3((unsigned)(B * H * (D / DVT))), dim3(256), 0,
+                       st_scan, q, route, ws, S_init, o_gdn, S_final, H, L, G);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (prof) prof(KID_GDN_SCAN, st_scan, 1);

@@ -340,23 +340,6 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ int sm2_kslot(int r, int q) { return q ^ (r & 15); }
 __device__ __forceinline__ int sm2_vslot(int r, int q) { return q ^ ((r & 7) << 1); }
 
-// 16-byte global -> LDS load of this lane to lds_wave_base + 16 * lane.  Issued
-// from inline assembly so that the compiler's wait insertion, which cannot tell
-// the ring stages apart, does not drain the whole ring before every LDS read;
-// the kernel waits for these loads itself (wait_vm + lds_barrier).
-__device__ __forceinline__ void gload_lds16(const void* gptr, const void* lds_wave_base) {
-  const uint32_t base = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_wave_base);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(base), "v"(gptr) : "memory", "m0");
-}
-
-// s_waitcnt with vmcnt = n (expcnt / lgkmcnt not waited); n in {0, 4, 8}
-__device__ __forceinline__ void wait_vm(int n) {
-  if (n >= 8) __builtin_amdgcn_s_waitcnt(0x0F78);
-  else if (n >= 4) __builtin_amdgcn_s_waitcnt(0x0F74);
-  else __builtin_amdgcn_s_waitcnt(0x0F70);
-}
-
 template <typename To>
 __global__ void __launch_bounds__(512, 1)
     k_softmax_v2(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
