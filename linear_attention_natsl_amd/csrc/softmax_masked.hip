@@ -455,43 +455,47 @@ __global__ void __launch_bounds__(512, 1)
         for (int qs = 0; qs < 2; ++qs) mma(s[kt][qs], a, qf[qs][ks]);
       }
 
-    Frag<bf16> pf[2][2];
+    if (mode == MODE_DIAG) {
 #pragma unroll
-    for (int qs = 0; qs < 2; ++qs) {
-      const int qrow = qrow_base + 16 * qs + c;
-      if (mode == MODE_DIAG) {
+      for (int qs = 0; qs < 2; ++qs)
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            if ((16 * kt + 4 * g + i) > qrow) s[kt][qs][i] = -INFINITY;
-      }
-      float mt = fmaxf(fmaxf(s[0][qs][0], s[0][qs][1]), fmaxf(s[0][qs][2], s[0][qs][3]));
+            if ((16 * kt + 4 * g + i) > qrow_base + 16 * qs + c) s[kt][qs][i] = -INFINITY;
+    }
+    // tile max per query (its 4 lane groups hold 16 keys each), one rescale
+    // decision for the wave
+    float mt[2];
+    bool up = false;
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
+      float x = fmaxf(fmaxf(s[0][qs][0], s[0][qs][1]), fmaxf(s[0][qs][2], s[0][qs][3]));
 #pragma unroll
       for (int kt = 1; kt < 4; ++kt)
-        mt = fmaxf(mt, fmaxf(fmaxf(s[kt][qs][0], s[kt][qs][1]), fmaxf(s[kt][qs][2], s[kt][qs][3])));
-      mt = wave_max_xor(mt, 16);
-      mt = wave_max_xor(mt, 32);
-      mt *= scale_log2;
-      if (__ballot(mt > m_run[qs] + RESCALE_TH) != 0) {
-        const float m_new = fmaxf(m_run[qs], mt);
+        x = fmaxf(x, fmaxf(fmaxf(s[kt][qs][0], s[kt][qs][1]), fmaxf(s[kt][qs][2], s[kt][qs][3])));
+      mt[qs] = group4_max(x) * scale_log2;
+      up |= mt[qs] > m_run[qs] + RESCALE_TH;
+    }
+    if (__ballot(up) != 0) {
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs) {
+        const float m_new = fmaxf(m_run[qs], mt[qs]);
         const float alpha = __builtin_amdgcn_exp2f(m_run[qs] - m_new);
         m_run[qs] = m_new;
         l_run[qs] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) o[dt][qs] *= alpha;
       }
+    }
+    Frag<bf16> pf[2][2];
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
       const float nm = -m_run[qs];
-      float ls = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float pv = __builtin_amdgcn_exp2f(fmaf(s[kt][qs][i], scale_log2, nm));
-          s[kt][qs][i] = pv;
-          ls += pv;
-        }
-      l_run[qs] += ls;
+        for (int i = 0; i < 4; ++i) s[kt][qs][i] = __builtin_amdgcn_exp2f(fmaf(s[kt][qs][i], scale_log2, nm));
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
@@ -499,6 +503,16 @@ __global__ void __launch_bounds__(512, 1)
           frag_set(pf[qs][k2], j, s[2 * k2][qs][j]);
           frag_set(pf[qs][k2], 4 + j, s[2 * k2 + 1][qs][j]);
         }
+      // row sum of the bf16 weights the product uses, two per dot2 (fp32 accumulate)
+      float ls = l_run[qs];
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bf16x2 pr = {pf[qs][k2].v[2 * j], pf[qs][k2].v[2 * j + 1]};
+          ls = __builtin_amdgcn_fdot2_f32_bf16(pr, bf16x2{(bf16)1.f, (bf16)1.f}, ls, false);
+        }
+      l_run[qs] = ls;
     }
     // V^T fragments by transposed reads: lane c of group g reads row
     // 32 k2 + 4 g + c / 4 (+16 for the second half), columns 16 dt + 4 (c % 4) .. +3
@@ -524,9 +538,7 @@ __global__ void __launch_bounds__(512, 1)
   if (!active) return;
 #pragma unroll
   for (int qs = 0; qs < 2; ++qs) {
-    float lt = l_run[qs];
-    lt = wave_sum_xor(lt, 16);
-    lt = wave_sum_xor(lt, 32);
+    const float lt = group4_sum(l_run[qs]);
     const float inv = 1.0f / lt;
     const int64_t tok = qtok0 + 16 * qs + c;
     To* orow = o_sm + head_off + tok * D;
