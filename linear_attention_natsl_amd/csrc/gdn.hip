@@ -156,9 +156,30 @@ __global__ void __launch_bounds__(256, 2)
   const int t = threadIdx.x, lane = lane_id(), w = wave_id();
   const int g = lane >> 4, c = lane & 15;
 
+  // Every global load of the chunk is issued first (one memory latency
+  // instead of one per copy loop): thread t loads key group kg = t / (D / 8)
+  // (rows 4kg .. 4kg+3) of K and V at columns col .. col+7, plus its Q
+  // fragments; wave 0 also loads alpha and beta.
+  constexpr int TASKS = (CHUNK / 4) * (D / 8);
+  static_assert(TASKS <= 256, "one task per thread");
+  const T* kc = k + tok0 * D;
+  const T* vc = v + tok0 * D;
+  const int kg = t / (D / 8), col = (t % (D / 8)) * 8;
+  Frag<T> kr[4], vr[4];
+  if (t < TASKS) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      kr[i] = load8<T>(kc + (4 * kg + i) * D + col);
+      vr[i] = load8<T>(vc + (4 * kg + i) * D + col);
+    }
+  }
+  Frag<T> qa[C::KF];
+#pragma unroll
+  for (int ks = 0; ks < C::KF; ++ks) qa[ks] = load8<T>(q + (tok0 + 16 * w + c) * D + 32 * ks + 8 * g);
   // cumulative log decay (wave 0), beta
   if (w == 0) {
     const float a = alpha[tok0 + lane];
+    const float bt = beta[tok0 + lane];
     float s = logf(a);
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -166,7 +187,6 @@ __global__ void __launch_bounds__(256, 2)
       if (lane >= off) s += o;
     }
     const float gC = __shfl(s, 63, 64);
-    const float bt = beta[tok0 + lane];
     gl[lane] = s;
     bl[lane] = bt;
     gbl[lane] = bt * expf(s);
@@ -176,20 +196,9 @@ __global__ void __launch_bounds__(256, 2)
     if (lane == 0) ws.gm[ch * C::GM + 64] = expf(gC);
   }
   // K -> row layout and key-group layout, V -> key-group layout
-  const T* kc = k + tok0 * D;
-  const T* vc = v + tok0 * D;
-  for (int e = t; e < CHUNK * D / 8; e += 256) {
-    const int row = e / (D / 8), col = (e % (D / 8)) * 8;
-    store8<T>(Ks + row * C::KP + col, load8<T>(kc + row * D + col));
-  }
-  for (int task = t; task < (CHUNK / 4) * (D / 8); task += 256) {
-    const int kg = task / (D / 8), col = (task % (D / 8)) * 8;
-    Frag<T> kr[4], vr[4];
+  if (t < TASKS) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      kr[i] = load8<T>(kc + (4 * kg + i) * D + col);
-      vr[i] = load8<T>(vc + (4 * kg + i) * D + col);
-    }
+    for (int i = 0; i < 4; ++i) store8<T>(Ks + (4 * kg + i) * C::KP + col, kr[i]);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       st4<T>(Kg + kg_index<C::RL>(kg, col + j), to_f32(frag_get<T>(kr[0], j)), to_f32(frag_get<T>(kr[1], j)),
@@ -198,9 +207,6 @@ __global__ void __launch_bounds__(256, 2)
              to_f32(frag_get<T>(vr[2], j)), to_f32(frag_get<T>(vr[3], j)));
     }
   }
-  Frag<T> qa[C::KF];
-#pragma unroll
-  for (int ks = 0; ks < C::KF; ++ks) qa[ks] = load8<T>(q + (tok0 + 16 * w + c) * D + 32 * ks + 8 * g);
   __syncthreads();
 
   // K K^T and Q K^T rows 16w .. 16w+15
@@ -335,7 +341,7 @@ __global__ void __launch_bounds__(256, 2)
 #pragma unroll
   for (int n = 0; n < C::NT; ++n)
     *reinterpret_cast<f32x4*>(ws.ut + ((ch * 4 + w) * C::NT + n) * 256 + lane * 4) = ut[n];
-  // -W -> Ks (row layout) -> A fragments with contraction over d (KMAP_ROW)
+  // -W -> Ks (row layout) -> A fragments with contraction over d
 #pragma unroll
   for (int n = 0; n < C::NT; ++n)
 #pragma unroll
