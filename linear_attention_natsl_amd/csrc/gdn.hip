@@ -142,7 +142,6 @@ __global__ void __launch_bounds__(256, 2)
   T* Vg = (T*)(lds + C::OFF_VG);
   float* LT = (float*)(lds + C::OFF_LT);
   float* Rs = (float*)(lds + C::OFF_RS);
-  T* Ps = (T*)(lds + C::OFF_PS);
   float* gl = (float*)(lds + C::OFF_GL);  // cumulative log decay
   float* bl = gl + CHUNK;                 // beta
   float* gbl = bl + CHUNK;                // beta * gamma
@@ -209,12 +208,15 @@ __global__ void __launch_bounds__(256, 2)
   }
   __syncthreads();
 
-  // K K^T and Q K^T rows 16w .. 16w+15
-  f32x4 akk[4], aqk[4];
+  // K K^T rows 16w .. 16w+15, and P^T = K Q^T for the queries 16w .. 16w+15:
+  // the transposed product leaves P's A fragments for the scan (row = query,
+  // contraction over keys, accumulator-shaped map) directly in the
+  // accumulators, with no LDS round trip
+  f32x4 akk[4], apt[4];
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) {
     akk[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-    aqk[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    apt[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 #pragma unroll
   for (int ks = 0; ks < C::KF; ++ks) {
@@ -223,42 +225,40 @@ __global__ void __launch_bounds__(256, 2)
     for (int ct = 0; ct < 4; ++ct) {
       const Frag<T> bk = load8<T>(Ks + (16 * ct + c) * C::KP + 32 * ks + 8 * g);
       mma(akk[ct], ak, bk);
-      mma(aqk[ct], qa[ks], bk);
+      mma(apt[ct], bk, qa[ks]);
     }
   }
-  // L = diag(beta) strict_tril(Gamma . KK^T) -> LT (fp32); P = tril(Gamma . QK^T) -> Ps
+  // L = diag(beta) strict_tril(Gamma . KK^T) -> LT (fp32)
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * w + 4 * g + i, col = 16 * ct + c;
-      const float e = (col <= r) ? expf(gl[r] - gl[col]) : 0.f;
-      LT[r * C::LTP + col] = (col < r) ? bl[r] * e * akk[ct][i] : 0.f;
-      const float pv = (col <= r) ? e * aqk[ct][i] : 0.f;
-      const T ph = from_f32<T>(pv);
-      aqk[ct][i] = pv - to_f32(ph);  // the part bf16 could not hold
-      Ps[r * C::PP + col] = ph;
+      LT[r * C::LTP + col] = (col < r) ? bl[r] * expf(gl[r] - gl[col]) * akk[ct][i] : 0.f;
     }
-  __syncthreads();
-
-  // P fragments (A operand of P U in the scan; contraction over tokens, KMAP_ACC): hi part
+  // P = tril(Gamma . QK^T): apt[ct][i] is (query 16w + c, key 16ct + 4g + i); the
+  // fragment of key half k2 holds keys 32k2 + 4g + j and 32k2 + 16 + 4g + j,
+  // split into a bf16 part and the remainder bf16 could not hold (zero for fp32)
+  {
+    Frag<T> ph[2], pl[2];
+    const int r = 16 * w + c;
 #pragma unroll
-  for (int k2 = 0; k2 < 2; ++k2) {
-    const T* row = Ps + (16 * w + c) * C::PP + 32 * k2 + 4 * g;
-    store8<T>(ws.pm + (((ch * 4 + w) * 2 + k2) * 2 + 0) * 512 + lane * 8, ld4x2<T>(row, row + 16));
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int col = 16 * ct + 4 * g + i;
+        const float pv = (col <= r) ? expf(gl[r] - gl[col]) * apt[ct][i] : 0.f;
+        const int k2 = ct >> 1, j = (ct & 1) * 4 + i;
+        frag_set(ph[k2], j, pv);
+        frag_set(pl[k2], j, pv - to_f32(frag_get<T>(ph[k2], j)));
+      }
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      store8<T>(ws.pm + (((ch * 4 + w) * 2 + k2) * 2 + 0) * 512 + lane * 8, ph[k2]);
+      store8<T>(ws.pm + (((ch * 4 + w) * 2 + k2) * 2 + 1) * 512 + lane * 8, pl[k2]);
+    }
   }
   __syncthreads();
-  // lo part (zero for fp32 io)
-#pragma unroll
-  for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) Ps[(16 * w + 4 * g + i) * C::PP + 16 * ct + c] = from_f32<T>(aqk[ct][i]);
-  __syncthreads();
-#pragma unroll
-  for (int k2 = 0; k2 < 2; ++k2) {
-    const T* row = Ps + (16 * w + c) * C::PP + 32 * k2 + 4 * g;
-    store8<T>(ws.pm + (((ch * 4 + w) * 2 + k2) * 2 + 1) * 512 + lane * 8, ld4x2<T>(row, row + 16));
-  }
 
   // T = (I + L)^-1, in place.  (a) 16x16 diagonal blocks: lane j of wave w
   // solves column j of block w by forward substitution.
@@ -330,10 +330,14 @@ __global__ void __launch_bounds__(256, 2)
       const Frag<T> bk = ld4x2<T>(Kg + kg_index<C::RL>(8 * k2 + g, 16 * n + c),
                                   Kg + kg_index<C::RL>(8 * k2 + 4 + g, 16 * n + c));
       mma(ut[n], a1, bv);
-      mma(wa[n], a2, bk);
-      if (SPLIT) {
-        mma(ut[n], a1l, bv);
-        mma(wa[n], a2l, bk);
+      if (SPLIT) mma(ut[n], a1l, bv);
+      if constexpr (scan_head_form<T, D>()) {
+        // W^T = K^T (T diag(b gamma))^T: wa[n][i] is W(token 16w + c, d 16n + 4g + i)
+        mma(wa[n], bk, a2);
+        if (SPLIT) mma(wa[n], bk, a2l);
+      } else {
+        mma(wa[n], a2, bk);
+        if (SPLIT) mma(wa[n], a2l, bk);
       }
     }
   }
@@ -341,11 +345,27 @@ __global__ void __launch_bounds__(256, 2)
 #pragma unroll
   for (int n = 0; n < C::NT; ++n)
     *reinterpret_cast<f32x4*>(ws.ut + ((ch * 4 + w) * C::NT + n) * 256 + lane * 4) = ut[n];
-  // -W -> Ks (row layout) -> A fragments with contraction over d
+  // -W -> A fragments with contraction over d.  Head form: straight from the
+  // transposed accumulators (d 32 ks + 4g + j from tile 2 ks, d 32 ks + 16 +
+  // 4g + j from tile 2 ks + 1); otherwise through Ks (row layout, 8
+  // contiguous d per lane)
+  if constexpr (scan_head_form<T, D>()) {
 #pragma unroll
-  for (int n = 0; n < C::NT; ++n)
+    for (int ks = 0; ks < C::KF; ++ks) {
+      Frag<T> f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) Ks[(16 * w + 4 * g + i) * C::KP + 16 * n + c] = from_f32<T>(-wa[n][i]);
+      for (int j = 0; j < 4; ++j) {
+        frag_set(f, j, -wa[2 * ks][j]);
+        frag_set(f, 4 + j, -wa[2 * ks + 1][j]);
+      }
+      store8<T>(ws.wn + ((ch * 4 + w) * C::KF + ks) * 512 + lane * 8, f);
+    }
+  } else {
+#pragma unroll
+    for (int n = 0; n < C::NT; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Ks[(16 * w + 4 * g + i) * C::KP + 16 * n + c] = from_f32<T>(-wa[n][i]);
+  }
   // K^T fragments: rows = d, contraction over tokens (KMAP_ACC); exact copies
   // of K (the exp(g_C - g) row scale is applied to U by the scan)
   for (int f = w; f < C::NT * 2; f += 4) {
@@ -353,14 +373,12 @@ __global__ void __launch_bounds__(256, 2)
     store8<T>(ws.kt + ((ch * C::NT + n) * 2 + k2) * 512 + lane * 8,
               ld4x2<T>(Kg + kg_index<C::RL>(8 * k2 + g, 16 * n + c), Kg + kg_index<C::RL>(8 * k2 + 4 + g, 16 * n + c)));
   }
-  __syncthreads();
-  // the head-per-workgroup scan (bf16, D = 128) packs its state B operand
-  // straight from accumulators, so -W uses the accumulator-shaped map there
+  if constexpr (!scan_head_form<T, D>()) {
+    __syncthreads();
 #pragma unroll
-  for (int ks = 0; ks < C::KF; ++ks) {
-    const T* row = Ks + (16 * w + c) * C::KP + 32 * ks;
-    store8<T>(ws.wn + ((ch * 4 + w) * C::KF + ks) * 512 + lane * 8,
-              scan_head_form<T, D>() ? ld4x2<T>(row + 4 * g, row + 16 + 4 * g) : load8<T>(row + 8 * g));
+    for (int ks = 0; ks < C::KF; ++ks)
+      store8<T>(ws.wn + ((ch * 4 + w) * C::KF + ks) * 512 + lane * 8,
+                load8<T>(Ks + (16 * w + c) * C::KP + 32 * ks + 8 * g));
   }
 }
 
