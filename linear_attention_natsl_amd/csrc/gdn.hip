@@ -687,8 +687,18 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW)
   int32_t* rl = reinterpret_cast<int32_t*>(lds + SCH_ROUTE);
 
   const int nc = L / CHUNK;
-  const int64_t bh = blockIdx.x / NSPLIT;
-  const int part = (int)(blockIdx.x % NSPLIT);
+  // the NSPLIT workgroups of a head go to one XCD (workgroup p runs on XCD
+  // p % 8), so the second reads the shared operands from that XCD's L2
+  int64_t bh;
+  int part;
+  if (((gridDim.x / NSPLIT) & 7) == 0) {
+    const int x = blockIdx.x & 7, r = blockIdx.x >> 3;
+    part = r % NSPLIT;
+    bh = (int64_t)(r / NSPLIT) * 8 + x;
+  } else {
+    bh = blockIdx.x / NSPLIT;
+    part = (int)(blockIdx.x % NSPLIT);
+  }
   const int b = (int)(bh / H), h = (int)(bh % H);
   const int grp = (G == 1) ? 0 : h;
   const int32_t* rt_g = route + ((int64_t)b * G + grp) * nc;
