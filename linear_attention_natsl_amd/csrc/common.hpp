@@ -132,6 +132,20 @@ __device__ __forceinline__ float wave_max_xor(float v, int mask) {
   return fmaxf(v, __shfl_xor(v, mask, 64));
 }
 __device__ __forceinline__ float wave_sum_xor(float v, int mask) { return v + __shfl_xor(v, mask, 64); }
+// Sum over aligned groups of N = 8 or 16 lanes, in registers (DPP), result in
+// every lane of the group: quad xor 1, quad xor 2, then the half-row mirror
+// (lane i <-> 7 - i pairs the two quads of each 8) and, for 16, the row
+// mirror (i <-> 15 - i pairs the two halves).
+template <int N>
+__device__ __forceinline__ float dpp_group_sum(float x) {
+  static_assert(N == 8 || N == 16, "groups of 8 or 16 lanes");
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));   // quad_perm 1,0,3,2
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));   // quad_perm 2,3,0,1
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, true));  // row_half_mirror
+  if (N == 16)
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, true));  // row_mirror
+  return x;
+}
 // max / sum over the 4 lanes c, c + 16, c + 32, c + 48 (the 4 lane groups of
 // an MFMA accumulator column), with the gfx950 row swaps instead of LDS
 // permutes: permlane16_swap pairs rows 0-1 and 2-3, permlane32_swap rows 0-2
@@ -148,6 +162,8 @@ __device__ __forceinline__ float group4_sum(float x) {
   auto r2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r2[0]) + __uint_as_float(r2[1]);
 }
+// sum over the whole wave, in registers: rows of 16 by DPP, then the 4 rows
+__device__ __forceinline__ float wave_sum64(float x) { return group4_sum(dpp_group_sum<16>(x)); }
 
 // Workgroup barrier that orders LDS only: waits for this wave's LDS accesses
 // and meets the other waves, but leaves global loads in flight (a plain

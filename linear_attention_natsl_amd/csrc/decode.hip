@@ -60,8 +60,7 @@ __global__ void __launch_bounds__(256) k_decode_route(const T* __restrict__ x, c
   for (int o = wv; o < 2 * G; o += 4) {
     float p = 0.f;
     for (int j = lane; j < d; j += 64) p += s_mean[j] * w[(int64_t)j * 2 * G + o];
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) p = wave_sum_xor(p, m);
+    p = wave_sum64(p);
     if (bsc) p += bsc[o];
     if (lane == 0) s_mean[d + o] = p;
   }
@@ -130,8 +129,8 @@ __global__ void __launch_bounds__(256) k_decode_gdn(const T* __restrict__ q, con
   }
 }
 
-constexpr int DEC_SPLIT = 512;  // cached rows per workgroup
-constexpr int DEC_UNROLL = 8;   // rows per lane group in flight
+constexpr int DEC_SPLIT = 1024;  // cached rows per workgroup
+constexpr int DEC_UNROLL = 16;   // rows per lane group in flight
 
 template <typename T, int D>
 __global__ void __launch_bounds__(256) k_decode_attn(const T* __restrict__ q, const T* __restrict__ kc,
@@ -179,8 +178,7 @@ __global__ void __launch_bounds__(256) k_decode_attn(const T* __restrict__ q, co
       float p = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) p += qv[j] * to_f32(frag_get<T>(kf[u], j));
-#pragma unroll
-      for (int mm = LPK / 2; mm >= 1; mm >>= 1) p = wave_sum_xor(p, mm);
+      p = dpp_group_sum<LPK>(p);
       sc[u] = (r0 + u * NGRP < hi) ? p : -INFINITY;
     }
     float mb = sc[0];
@@ -250,12 +248,9 @@ __global__ void __launch_bounds__(D) k_decode_combine(
   const float* wm = w_mix + (int64_t)h * wmix_hs;
   // block reductions of: q.k_new, q.W_mix[:,0], q.W_mix[:,1]
   float r0 = qv * to_f32(kn), r1 = qv * wm[2 * t], r2 = qv * wm[2 * t + 1];
-#pragma unroll
-  for (int mm = 32; mm >= 1; mm >>= 1) {
-    r0 = wave_sum_xor(r0, mm);
-    r1 = wave_sum_xor(r1, mm);
-    r2 = wave_sum_xor(r2, mm);
-  }
+  r0 = wave_sum64(r0);
+  r1 = wave_sum64(r1);
+  r2 = wave_sum64(r2);
   if (lane == 0) {
     red[0][w] = r0;
     red[1][w] = r1;
@@ -285,11 +280,8 @@ __global__ void __launch_bounds__(D) k_decode_combine(
   const float og = o_gdn[(int64_t)bh * D + t];
   // RMS of both branches
   float a2 = osm * osm, b2 = og * og;
-#pragma unroll
-  for (int mm = 32; mm >= 1; mm >>= 1) {
-    a2 = wave_sum_xor(a2, mm);
-    b2 = wave_sum_xor(b2, mm);
-  }
+  a2 = wave_sum64(a2);
+  b2 = wave_sum64(b2);
   __syncthreads();
   if (lane == 0) {
     red[0][w] = a2;

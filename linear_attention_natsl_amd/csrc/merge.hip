@@ -45,13 +45,10 @@ __global__ void __launch_bounds__(256) k_merge(const Tq* __restrict__ q, const T
     z0 += qv[j] * wm[2 * j];
     z1 += qv[j] * wm[2 * j + 1];
   }
-#pragma unroll
-  for (int m = LPT / 2; m >= 1; m >>= 1) {
-    ssa = wave_sum_xor(ssa, m);
-    ssb = wave_sum_xor(ssb, m);
-    z0 = wave_sum_xor(z0, m);
-    z1 = wave_sum_xor(z1, m);
-  }
+  ssa = dpp_group_sum<LPT>(ssa);
+  ssb = dpp_group_sum<LPT>(ssb);
+  z0 = dpp_group_sum<LPT>(z0);
+  z1 = dpp_group_sum<LPT>(z1);
   const float ra = 1.0f / sqrtf(ssa * (1.0f / D) + eps);
   const float rb = 1.0f / sqrtf(ssb * (1.0f / D) + eps);
   const float zm = fmaxf(z0, z1);
