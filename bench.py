@@ -269,6 +269,40 @@ def cpu_baseline(W, O, inp, route, workload):
                 seconds_measured=round(t_route + t_gdn + t_sm + t_merge, 2))
 
 
+def achievable_peaks():
+    """What this GPU reaches on plain library work, as context for the
+    datasheet peaks the roofline uses: a large bf16 GEMM (torch / hipBLASLt,
+    both operands contiguous) and a 1 GiB device-to-device copy.  Untimed
+    by the step clock; run after the timed regions."""
+    import torch
+    n = 8192
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    c = torch.empty(n, n, device="cuda", dtype=torch.bfloat16)
+    settle(lambda: torch.mm(a, b, out=c), 0.2)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        torch.mm(a, b, out=c)
+    e1.record()
+    torch.cuda.synchronize()
+    gemm_tf = 10 * 2 * n ** 3 / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    del a, b, c
+    x = torch.empty(2 ** 28, device="cuda", dtype=torch.float32)  # 1 GiB
+    y = torch.empty_like(x)
+    x.fill_(1.0)
+    settle(lambda: y.copy_(x), 0.1)
+    e0.record()
+    for _ in range(10):
+        y.copy_(x)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 10 * 2 * x.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del x, y
+    return dict(gemm_bf16_8192_tflops=round(gemm_tf, 1), gemm_frac_of_peak=round(gemm_tf / PEAK_BF16_TFLOPS, 4),
+                copy_1GiB_gbs=round(copy_gbs, 1), copy_frac_of_peak=round(copy_gbs / PEAK_HBM_GBS, 4))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -278,6 +312,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-calib", action="store_true", help="skip the achievable-peak GEMM and copy")
     ap.add_argument("--check-route", action="store_true")
     ap.add_argument("--profile-copy", action="store_true",
                     help="first run a plain 256 MiB read + 256 MiB write elementwise kernel three times, "
@@ -309,6 +344,8 @@ def main():
         res["decode"] = time_decode(args, N, W)
         print(f"decode: {res['decode']['ms_per_step']} ms/step, attn {res['decode']['roofline']['frac']*100:.1f}% "
               f"of HBM peak", file=sys.stderr, flush=True)
+    if not args.no_calib:
+        res["achievable"] = achievable_peaks()
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(W, O, inp, route, args.workload)
     print(json.dumps(res))

@@ -4,7 +4,7 @@
 //   n_x = o_x / sqrt(mean(o_x^2) + eps) * g_x,  (w_sm, w_lin) = softmax(q W_mix),
 //   out = w_sm n_sm + w_lin n_lin.
 // Bandwidth-bound: D/8 lanes per token, 8 elements per lane (16-byte bf16
-// loads), reductions across the token's lanes with xor shuffles.
+// loads), reductions across the token's lanes in registers (DPP row ops).
 #include "common.hpp"
 #include "kernels.hpp"
 
