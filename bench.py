@@ -101,6 +101,23 @@ def settle(fn, seconds=SETTLE_S):
         torch.cuda.synchronize()
 
 
+def kernel_table(N, fn, names, reps):
+    """Average duration of every kernel of a step, from `reps` untimed steps
+    with each kernel bracketed by events (the timed steps bracket only the
+    roofline kernel, so that the events do not lengthen the step)."""
+    import torch
+    N.profile_select(None)
+    N.profile_reset()
+    for _ in range(reps):
+        fn()
+    torch.cuda.synchronize()
+    out = {}
+    for name in names:
+        n, ms = N.profile_read(name)
+        out[name] = dict(launches=n, avg_us=round(1000.0 * ms / max(n, 1), 2))
+    return out
+
+
 def time_prefill(args, N, W, O):
     import torch
     wl = W.WORKLOADS[args.workload]
@@ -118,7 +135,9 @@ def time_prefill(args, N, W, O):
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
+    # timed steps: only the roofline kernel is bracketed by events
     N.profile_enable(True)
+    N.profile_select("softmax_masked")
     N.profile_reset()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -126,10 +145,10 @@ def time_prefill(args, N, W, O):
         call()
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
-    kernels = {}
-    for name in ("route", "compact", "gdn_prep", "gdn_scan", "softmax_masked", "merge"):
-        n, ms = N.profile_read(name)
-        kernels[name] = dict(launches=n, avg_us=round(1000.0 * ms / max(n, 1), 2))
+    n, ms = N.profile_read("softmax_masked")
+    sm_avg_us = 1000.0 * ms / max(n, 1)
+    kernels = kernel_table(N, call, ("route", "compact", "gdn_prep", "gdn_scan", "softmax_masked", "merge"),
+                           max(5, args.steps // 5))
     N.profile_enable(False)
     route = fwd.route.cpu().numpy()
     ref_route = O.route(inp["x"], inp["w_score"], inp["b_score"])[0] if args.check_route else None
@@ -139,7 +158,7 @@ def time_prefill(args, N, W, O):
     f_gdn = gdn_flops(wl.B, wl.H, wl.nc, n_lin, wl.D)
     ms_step = 1000.0 * dt / args.steps
     tok_s = wl.B * wl.L / (dt / args.steps)
-    sm_us = kernels["softmax_masked"]["avg_us"]
+    sm_us = round(sm_avg_us, 2)
     achieved = f_sm / (sm_us * 1e-6) / 1e12
     traffic = counters_traffic("softmax_masked", args.workload, source_hash("softmax_masked.hip", "common.hpp"))
     res = dict(
@@ -204,6 +223,7 @@ def time_decode(args, N, W):
     torch.cuda.synchronize()
     rows_start = (st.n_committed[:, 0] + st.n_open).cpu().numpy().astype(np.int64)
     N.profile_enable(True)
+    N.profile_select("decode_attn")
     N.profile_reset()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -211,17 +231,20 @@ def time_decode(args, N, W):
         dec(*a)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
-    kernels = {}
-    for name in ("decode_route", "decode_gdn", "decode_attn", "decode_combine", "decode_commit"):
-        n, ms = N.profile_read(name)
-        kernels[name] = dict(launches=n, avg_us=round(1000.0 * ms / max(n, 1), 2))
+    n, ms = N.profile_read("decode_attn")
+    attn_us = round(1000.0 * ms / max(n, 1), 2)
+    assert int(st.err.item()) == 0
+    # per-kernel table from an untimed burst, restored afterwards as above
+    kernels = kernel_table(N, lambda: dec(*a), ("decode_route", "decode_gdn", "decode_attn", "decode_combine",
+                                                "decode_commit"), 10)
     N.profile_enable(False)
     assert int(st.err.item()) == 0
+    for x, y in zip((st.n_committed, st.n_open, st.S_carry, st.S_work, st.x_sum, st.err), saved):
+        x.copy_(y)
     # rows read per step: step i reads rows_start + i cached rows per (b, h)
     mean_rows = float((rows_start[:, None] + np.arange(steps)[None, :]).mean())
     kv_bytes = B * H * mean_rows * 2 * D * 2
     step_bytes = kv_bytes + B * H * (2 * D * 2 + 2 * D * D * 4 + 4 * D * 2) + B * d * (2 + 8)
-    attn_us = kernels["decode_attn"]["avg_us"]
     achieved = kv_bytes / (attn_us * 1e-6) / 1e9
     traffic = counters_traffic("decode_attn", "decode", source_hash("decode.hip", "common.hpp"))
     return dict(

@@ -253,10 +253,15 @@ natsl_status natsl_decode_step(const natsl_dims* dims, const natsl_decode_cache*
  * in milliseconds since the last reset.  Names: "route", "compact",
  * "gdn_prep", "gdn_scan", "softmax_masked", "merge", "decode_route",
  * "decode_gdn", "decode_attn", "decode_combine", "decode_commit".
+ * natsl_profile_select restricts the recording to the kernel named `name`
+ * (NULL or "" records every kernel again), so that timing one kernel adds
+ * only its own two event records to a step; an unknown name is
+ * NATSL_ERR_INVALID_ARG and leaves the selection unchanged.
  */
 natsl_status natsl_profile_enable(int on);
 natsl_status natsl_profile_reset(void);
 natsl_status natsl_profile_read(const char* name, int* count, double* total_ms);
+natsl_status natsl_profile_select(const char* name);
 
 #ifdef __cplusplus
 }

@@ -24,7 +24,7 @@ STATUS = {0: "NATSL_OK", 1: "NATSL_ERR_INVALID_ARG", 2: "NATSL_ERR_UNSUPPORTED",
           3: "NATSL_ERR_WORKSPACE", 4: "NATSL_ERR_DEVICE", 5: "NATSL_ERR_CAPACITY"}
 EXPORTS = ["natsl_version", "natsl_last_error", "natsl_workspace_size", "natsl_route", "natsl_gdn_chunk",
            "natsl_softmax_masked", "natsl_merge", "natsl_forward", "natsl_decode_step",
-           "natsl_profile_enable", "natsl_profile_reset", "natsl_profile_read"]
+           "natsl_profile_enable", "natsl_profile_reset", "natsl_profile_read", "natsl_profile_select"]
 
 
 class NatslError(RuntimeError):
@@ -87,9 +87,10 @@ def lib():
                                         C.c_size_t, vp]
         L.natsl_profile_enable.argtypes = [C.c_int]
         L.natsl_profile_read.argtypes = [C.c_char_p, C.POINTER(C.c_int), C.POINTER(C.c_double)]
+        L.natsl_profile_select.argtypes = [C.c_char_p]
         for name in ("natsl_workspace_size", "natsl_route", "natsl_gdn_chunk", "natsl_softmax_masked",
                      "natsl_merge", "natsl_forward", "natsl_decode_step", "natsl_profile_enable",
-                     "natsl_profile_reset", "natsl_profile_read"):
+                     "natsl_profile_reset", "natsl_profile_read", "natsl_profile_select"):
             getattr(L, name).restype = st
         _lib = L
     return _lib
@@ -347,6 +348,11 @@ def profile_enable(on=True):
 
 def profile_reset():
     _check(lib().natsl_profile_reset())
+
+
+def profile_select(name=None):
+    """Record only kernel `name` (None: every kernel)."""
+    _check(lib().natsl_profile_select(name.encode() if name else None))
 
 
 def profile_read(name):

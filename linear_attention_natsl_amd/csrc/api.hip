@@ -54,8 +54,11 @@ std::vector<ProfRec> g_prof_pool;  // created on enable
 size_t g_prof_used = 0;
 int g_prof_open[KID_COUNT];         // index of the record whose start was recorded
 
+int g_prof_only = -1;                // record only this kernel id (-1: all)
+
 void prof_hook(int kid, hipStream_t st, int phase) {
   if (!g_prof_on) return;
+  if (g_prof_only >= 0 && kid != g_prof_only) return;
   if (phase == 0) {
     if (g_prof_used >= g_prof_pool.size()) {
       g_prof_open[kid] = -1;
@@ -518,6 +521,18 @@ natsl_status natsl_profile_enable(int on) {
 natsl_status natsl_profile_reset(void) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
   g_prof_used = 0;
+  return ok();
+}
+
+natsl_status natsl_profile_select(const char* name) {
+  int kid = -1;
+  if (name && name[0]) {
+    for (int i = 0; i < KID_COUNT; ++i)
+      if (strcmp(name, kKernelNames[i]) == 0) kid = i;
+    if (kid < 0) return fail(NATSL_ERR_INVALID_ARG, "unknown kernel name '%s'", name);
+  }
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_only = kid;
   return ok();
 }
 

@@ -212,7 +212,30 @@ __device__ __forceinline__ int opaque_sgpr(int x) {
   asm volatile("" : "+s"(x));
   return x;
 }
-__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
-__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+// Work-item and workgroup indices straight from the hardware.  HIP's
+// threadIdx / blockIdx / gridDim are device-library functions built with the
+// default target features; this library is compiled with packed fp32 ops
+// disabled, so they are not inlined into its kernels: every use becomes a call
+// whose result the compiler must take as divergent, which turns all control
+// flow derived from the block index into exec-mask branches.
+__device__ __forceinline__ int tid_x() { return (int)__builtin_amdgcn_workitem_id_x(); }
+__device__ __forceinline__ int bid_x() { return (int)__builtin_amdgcn_workgroup_id_x(); }
+__device__ __forceinline__ int bid_y() { return (int)__builtin_amdgcn_workgroup_id_y(); }
+// HSA kernel dispatch packet: workgroup_size_x (u16) at byte 4, grid_size_x
+// (u32, in work-items) at byte 12
+typedef const __attribute__((address_space(4))) char* dispatch_bytes;
+__device__ __forceinline__ int block_dim_x() {
+  const dispatch_bytes dp = (dispatch_bytes)__builtin_amdgcn_dispatch_ptr();
+  return *(const __attribute__((address_space(4))) uint16_t*)(dp + 4);
+}
+__device__ __forceinline__ int grid_dim_x() {
+  const dispatch_bytes dp = (dispatch_bytes)__builtin_amdgcn_dispatch_ptr();
+  return (int)(*(const __attribute__((address_space(4))) uint32_t*)(dp + 12) /
+               *(const __attribute__((address_space(4))) uint16_t*)(dp + 4));
+}
+__device__ __forceinline__ int lane_id() { return tid_x() & 63; }
+// wave-uniform by construction; readfirstlane lets the compiler know it, so
+// branches on the wave index are scalar branches
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(tid_x() >> 6); }
 
 }  // namespace natsl

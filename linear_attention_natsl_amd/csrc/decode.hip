@@ -31,9 +31,9 @@ __global__ void __launch_bounds__(256) k_decode_route(const T* __restrict__ x, c
                                                       int32_t* __restrict__ dec,
                                                       int32_t* __restrict__ route_out) {
   extern __shared__ float s_mean[];  // [d + 2G]
-  const int b = blockIdx.x;
+  const int b = bid_x();
   const bool complete = (n_open[b] + 1) == CHUNK;
-  for (int col0 = threadIdx.x * 8; col0 < d; col0 += 256 * 8) {
+  for (int col0 = tid_x() * 8; col0 < d; col0 += 256 * 8) {
     float xv[8];
     load8f<T>(x + (int64_t)b * d + col0, xv);
     float* xs = x_sum + (int64_t)b * d + col0;
@@ -49,7 +49,7 @@ __global__ void __launch_bounds__(256) k_decode_route(const T* __restrict__ x, c
     }
   }
   if (!complete) {
-    for (int gg = threadIdx.x; gg < G; gg += 256) {
+    for (int gg = tid_x(); gg < G; gg += 256) {
       dec[b * G + gg] = -1;
       if (route_out) route_out[b * G + gg] = -1;
     }
@@ -65,7 +65,7 @@ __global__ void __launch_bounds__(256) k_decode_route(const T* __restrict__ x, c
     if (lane == 0) s_mean[d + o] = p;
   }
   __syncthreads();
-  for (int gg = threadIdx.x; gg < G; gg += 256) {
+  for (int gg = tid_x(); gg < G; gg += 256) {
     const int r = (s_mean[d + 2 * gg] >= s_mean[d + 2 * gg + 1]) ? 0 : 1;
     dec[b * G + gg] = r;
     if (route_out) route_out[b * G + gg] = r;
@@ -83,9 +83,9 @@ __global__ void __launch_bounds__(256) k_decode_gdn(const T* __restrict__ q, con
   constexpr int RPT = D / TPC;  // rows per thread
   __shared__ float kq[3][D];
   __shared__ float red[TPC][D];
-  const int bh = blockIdx.x, b = bh / H, h = bh % H;
+  const int bh = bid_x(), b = bh / H, h = bh % H;
   const int grp = (G == 1) ? 0 : h;
-  const int t = threadIdx.x, col = t % D, part = t / D;
+  const int t = tid_x(), col = t % D, part = t / D;
   if (t < D) {
     kq[0][t] = to_f32(k[(int64_t)bh * D + t]);
     kq[1][t] = to_f32(q[(int64_t)bh * D + t]);
@@ -145,7 +145,7 @@ __global__ void __launch_bounds__(256) k_decode_attn(const T* __restrict__ q, co
   constexpr int NGRP = 4 * GPW;     // row groups per workgroup
   __shared__ float red_o[NGRP][D];
   __shared__ float red_m[NGRP], red_l[NGRP];
-  const int s = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H;
+  const int s = bid_x(), bh = bid_y(), b = bh / H, h = bh % H;
   const int grp = (G == 1) ? 0 : h;
   // rows actually present (after a capacity error the counters run past cap)
   const int n = min(n_committed[b * G + grp] + n_open[b], cap);
@@ -205,7 +205,7 @@ __global__ void __launch_bounds__(256) k_decode_attn(const T* __restrict__ q, co
 #pragma unroll
   for (int j = 0; j < 8; ++j) red_o[grpid][8 * sub + j] = acc[j];
   __syncthreads();
-  const int t = threadIdx.x;
+  const int t = tid_x();
   if (t < D) {
     float M = -INFINITY;
 #pragma unroll
@@ -237,9 +237,9 @@ __global__ void __launch_bounds__(D) k_decode_combine(
     const float* __restrict__ g_sm, const float* __restrict__ g_lin, float eps, T* __restrict__ out,
     float* __restrict__ o_sm_dbg, float* __restrict__ o_gdn_dbg, int32_t* __restrict__ err_flag) {
   __shared__ float red[4][D / 64 > 0 ? D / 64 : 1];
-  const int bh = blockIdx.x, b = bh / H, h = bh % H;
+  const int bh = bid_x(), b = bh / H, h = bh % H;
   const int grp = (G == 1) ? 0 : h;
-  const int t = threadIdx.x, lane = lane_id(), w = wave_id();
+  const int t = tid_x(), lane = lane_id(), w = wave_id();
   constexpr int NW = D / 64;
   const int n = n_committed[b * G + grp] + n_open[b];
   const float qv = to_f32(q[(int64_t)bh * D + t]);
@@ -314,7 +314,7 @@ __global__ void __launch_bounds__(D) k_decode_combine(
 
 __global__ void k_decode_commit(int B, int G, int32_t* __restrict__ n_committed,
                                 int32_t* __restrict__ n_open, const int32_t* __restrict__ dec) {
-  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  const int b = bid_x() * block_dim_x() + tid_x();
   if (b >= B) return;
   int no = n_open[b] + 1;
   if (no == CHUNK) {

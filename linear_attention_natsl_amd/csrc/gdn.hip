@@ -148,11 +148,11 @@ __global__ void __launch_bounds__(256, 2)
   float* ekl = gbl + CHUNK;               // exp(g_C - g)
 
   const int nc = L / CHUNK;
-  const int64_t ch = blockIdx.x;
+  const int64_t ch = bid_x();
   const int64_t bh = ch / nc;
   const int cc = (int)(ch % nc);
   const int64_t tok0 = bh * L + (int64_t)cc * CHUNK;  // row index into [B*H*L]
-  const int t = threadIdx.x, lane = lane_id(), w = wave_id();
+  const int t = tid_x(), lane = lane_id(), w = wave_id();
   const int g = lane >> 4, c = lane & 15;
 
   // Every global load of the chunk is issued first (one memory latency
@@ -456,10 +456,10 @@ __global__ void __launch_bounds__(256, 1)
 
   const int nc = L / CHUNK;
   const int nvt = D / DVT;
-  const int total = (int)gridDim.x;
+  const int total = (int)grid_dim_x();
   const int BH = total / nvt;
-  int logical = blockIdx.x;
-  if ((BH & 7) == 0) logical = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
+  int logical = bid_x();
+  if ((BH & 7) == 0) logical = (bid_x() & 7) * (total >> 3) + (bid_x() >> 3);
   const int64_t bh = logical / nvt;
   const int vt = logical % nvt;
   const int b = (int)(bh / H), h = (int)(bh % H);
@@ -573,7 +573,7 @@ __global__ void __launch_bounds__(256, 1)
   auto flush = [&](int c_first, int c_last) {
     const int rows = (c_last - c_first + 1) * CHUNK;
     constexpr int PER = 16 / (int)sizeof(To);  // elements per 16-byte store
-    for (int e = threadIdx.x; e < rows * (DVT / PER); e += 256) {
+    for (int e = tid_x(); e < rows * (DVT / PER); e += 256) {
       const int r = e / (DVT / PER), cl = (e % (DVT / PER)) * PER;
       const To* src = Ob + ((c_first % OUT_RING) * CHUNK + r) * DVT + cl;
       To* dst = oh + ((int64_t)c_first * CHUNK + r) * D + dv0 + cl;
@@ -691,13 +691,15 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW)
   // p % 8), so the second reads the shared operands from that XCD's L2
   int64_t bh;
   int part;
-  if (((gridDim.x / NSPLIT) & 7) == 0) {
-    const int x = blockIdx.x & 7, r = blockIdx.x >> 3;
-    part = r % NSPLIT;
+  // (unsigned: with signed division here the chunk loop below spills)
+  const unsigned bid = (unsigned)bid_x();
+  if ((((unsigned)grid_dim_x() / NSPLIT) & 7) == 0) {
+    const unsigned x = bid & 7, r = bid >> 3;
+    part = (int)(r % NSPLIT);
     bh = (int64_t)(r / NSPLIT) * 8 + x;
   } else {
-    bh = blockIdx.x / NSPLIT;
-    part = (int)(blockIdx.x % NSPLIT);
+    bh = bid / NSPLIT;
+    part = (int)(bid % NSPLIT);
   }
   const int b = (int)(bh / H), h = (int)(bh % H);
   const int grp = (G == 1) ? 0 : h;
@@ -709,7 +711,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW)
   const int dv0 = 16 * NV * (NW * part + w);
   const int nt0 = NV * (NW * part + w);  // first 16-column tile of this wave
 
-  for (int i = threadIdx.x; i < nc; i += 64 * NW) rl[i] = rt_g[i];
+  for (int i = tid_x(); i < nc; i += 64 * NW) rl[i] = rt_g[i];
 
   // fp32 state: rows d = 16 dt + 4g + i, columns dv0 + 16 nn + c
   f32x4 sm[8][NV];

@@ -18,7 +18,7 @@ __global__ void __launch_bounds__(256) k_merge(const Tq* __restrict__ q, const T
                                                const float* __restrict__ g_lin, To* __restrict__ out,
                                                int H, int L, float eps, int64_t ntok) {
   constexpr int LPT = D / 8;  // lanes per token
-  const int64_t gtid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t gtid = (int64_t)bid_x() * 256 + tid_x();
   const int64_t tok = gtid / LPT;
   const int sub = (int)(gtid % LPT);
   const bool valid = tok < ntok;

@@ -23,9 +23,9 @@ __global__ void __launch_bounds__(256) k_route(const T* __restrict__ x, const fl
                                                int nc, int32_t* __restrict__ route_out,
                                                float* __restrict__ scores) {
   extern __shared__ float s_mean[];  // [d]
-  const int c = blockIdx.x, b = blockIdx.y;
+  const int c = bid_x(), b = bid_y();
   const T* xc = x + ((int64_t)b * L + (int64_t)c * CHUNK) * d;
-  for (int col0 = threadIdx.x * 8; col0 < d; col0 += 256 * 8) {
+  for (int col0 = tid_x() * 8; col0 < d; col0 += 256 * 8) {
     float acc[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[j] = 0.f;
@@ -50,7 +50,7 @@ __global__ void __launch_bounds__(256) k_route(const T* __restrict__ x, const fl
     if (lane == 0) s_mean[d + o] = p;  // scores live after the mean
   }
   __syncthreads();
-  for (int gg = threadIdx.x; gg < G; gg += 256) {
+  for (int gg = tid_x(); gg < G; gg += 256) {
     const float s0 = s_mean[d + 2 * gg], s1 = s_mean[d + 2 * gg + 1];
     const int64_t idx = ((int64_t)b * G + gg) * nc + c;
     route_out[idx] = (s0 >= s1) ? 0 : 1;
@@ -66,8 +66,8 @@ __global__ void __launch_bounds__(64) k_compact(const int32_t* __restrict__ rout
                                                 int32_t* __restrict__ route_out, int nc,
                                                 int32_t* __restrict__ sel_idx,
                                                 int32_t* __restrict__ nsel_before) {
-  const int bg = blockIdx.x;
-  const int lane = threadIdx.x;
+  const int bg = bid_x();
+  const int lane = tid_x();
   const int32_t* r = route_in + (int64_t)bg * nc;
   int32_t* ro = route_out + (int64_t)bg * nc;
   int32_t* sel = sel_idx + (int64_t)bg * nc;

@@ -81,7 +81,7 @@ struct TileRegs {
 template <typename T, int D>
 __device__ __forceinline__ void tile_gload(TileRegs<T, D>& r, const T* kbase, const T* vbase) {
   using C = SmCfg<T, D>;
-  const int t = threadIdx.x;
+  const int t = tid_x();
 #pragma unroll
   for (int i = 0; i < C::KLOADS; ++i) {
     const int e = t + 256 * i;
@@ -102,7 +102,7 @@ __device__ __forceinline__ void tile_gload(TileRegs<T, D>& r, const T* kbase, co
 template <typename T, int D>
 __device__ __forceinline__ void tile_sstore(const TileRegs<T, D>& r, T* buf) {
   using C = SmCfg<T, D>;
-  const int t = threadIdx.x;
+  const int t = tid_x();
   T* ks = buf;
   T* vs = buf + C::KTILE;
 #pragma unroll
@@ -140,8 +140,8 @@ __global__ void __launch_bounds__(256, 2)
 
   const int nc = L / CHUNK;
   const int nb = (nc + 1) / 2;
-  const int BH = (int)(gridDim.x / nb);
-  const int p = blockIdx.x;
+  const int BH = (int)(grid_dim_x() / nb);
+  const int p = bid_x();
   int qblk, bh;
   if ((BH & 7) == 0) {
     const int xcd = p & 7, slot = p >> 3, hpx = BH >> 3;
@@ -351,8 +351,8 @@ __global__ void __launch_bounds__(512, 1)
 
   const int nc = L / CHUNK;
   const int nb = (nc + 3) / 4;
-  const int BH = (int)(gridDim.x / nb);
-  const int p = blockIdx.x;
+  const int BH = (int)(grid_dim_x() / nb);
+  const int p = bid_x();
   int qblk, bh;
   if ((BH & 7) == 0) {
     const int xcd = p & 7, slot = p >> 3, hpx = BH >> 3;
@@ -382,8 +382,8 @@ __global__ void __launch_bounds__(512, 1)
   const bf16* vh = v + head_off;
 
   // tile list in LDS (keeps its reads out of the vector-memory counter)
-  for (int i = threadIdx.x; i < nsb; i += 512) sel_l[i] = sel[i];
-  for (int i = threadIdx.x; i < nown; i += 512) sel_l[nsb + i] = c0 + i;
+  for (int i = tid_x(); i < nsb; i += 512) sel_l[i] = sel[i];
+  for (int i = tid_x(); i < nown; i += 512) sel_l[nsb + i] = c0 + i;
 
   Frag<bf16> qf[2][4];
   const int qtok0 = (c0 + (active ? mch : 0)) * CHUNK + 32 * (w & 1);

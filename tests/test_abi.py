@@ -170,3 +170,15 @@ def test_binding_rejects_without_gpu_tensor():
     import torch
     with pytest.raises(ValueError):
         N._p(torch.zeros(3), name="x")
+
+
+def test_profile_select(L):
+    # selecting a kernel only sets host state: no GPU involved
+    assert L.natsl_profile_select(b"no_such_kernel") == 1
+    assert b"no_such_kernel" in N.lib().natsl_last_error()
+    for name in (b"softmax_masked", b"decode_attn", b"", None):
+        assert L.natsl_profile_select(name) == 0
+    with pytest.raises(N.NatslError):
+        N.profile_select("gdn_everything")
+    N.profile_select("merge")
+    N.profile_select(None)
