@@ -167,7 +167,7 @@ def time_prefill(args, N, W, O):
         ms_per_step=round(ms_step, 4), higher_is_better=True, scaling="weak", vs_baseline=None,
         dtype="bf16" if inp["io"] == "bf16" else "f32", data="synthetic",
         config=dict(workload=f"{args.workload} prefill: B={wl.B} H={wl.H} L={wl.L} D={wl.D} d_model={wl.d}, "
-                    f"chunk 64, {inp['io']} io / fp32 accumulate",
+                    f"chunk 64, {inp['io']} io and branch outputs / fp32 accumulate",
                     B=wl.B, H=wl.H, L=wl.L, D=wl.D, d_model=wl.d, seed=wl.seed,
                     softmax_chunk_fraction=round(float((route == 0).mean()), 4),
                     route_matches_oracle=None if ref_route is None else bool(np.array_equal(route, ref_route)),

@@ -224,9 +224,9 @@ class Forward:
     def __init__(self, dm: Dims, device="cuda", branch_dtype=None, debug=False, want_state=False):
         self.dm = dm
         io_t = torch.bfloat16 if dm.io == BF16 else torch.float32
-        # fp32 branch intermediates by default: bf16 storage would add its own
-        # rounding to both RMS-normalised branches
-        self.branch_dtype = branch_dtype if branch_dtype is not None else torch.float32
+        # branch intermediates in the io dtype by default (the kernels
+        # accumulate in fp32 either way); fp32 storage on request
+        self.branch_dtype = branch_dtype if branch_dtype is not None else io_t
         self.ws_bytes = workspace_size(ENTRY_FORWARD, dm)
         self.ws = workspace(self.ws_bytes, device)
         shp = (dm.B, dm.H, dm.L, dm.Dv)

@@ -445,16 +445,45 @@ __global__ void __launch_bounds__(512, 1)
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
       for (int qs = 0; qs < 2; ++qs) s[kt][qs] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // all 16 K fragments of the tile are read before the 32 products, so the
+    // reads' latency overlaps instead of stalling each pair of products
+    {
+      Frag<bf16> ka[4][4];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+      for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        const int r = 16 * kt + c;
-        const Frag<bf16> a = load8<bf16>(ks_l + r * D + sm2_kslot(r, 4 * ks + g) * 8);
+        for (int kt = 0; kt < 4; ++kt) {
+          const int r = 16 * kt + c;
+          ka[ks][kt] = load8<bf16>(ks_l + r * D + sm2_kslot(r, 4 * ks + g) * 8);
+        }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int qs = 0; qs < 2; ++qs) mma(s[kt][qs], a, qf[qs][ks]);
-      }
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int qs = 0; qs < 2; ++qs) mma(s[kt][qs], ka[ks][kt], qf[qs][ks]);
+    }
 
+    // V^T fragments by transposed reads, issued before the softmax work so
+    // that it hides their latency: lane c of group g reads row
+    // 32 k2 + 4 g + c / 4 (+16 for the second half), columns 16 dt + 4 (c % 4) .. +3
+    Frag<bf16> va[D / 16][2];
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      const int colq = (16 * dt + 4 * (c & 3)) >> 3;  // 16-byte chunk of the 4 columns
+      const int half = ((c & 3) & 1) * 8;            // byte offset inside it
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        const int r0 = 32 * k2 + 4 * g + (c >> 2), r1 = r0 + 16;
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4i16*)(vs_l + r0 * 256 + sm2_vslot(r0, colq) * 16 + half));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4i16*)(vs_l + r1 * 256 + sm2_vslot(r1, colq) * 16 + half));
+        va[dt][k2].v = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
     if (mode == MODE_DIAG) {
 #pragma unroll
       for (int qs = 0; qs < 2; ++qs)
@@ -514,24 +543,14 @@ __global__ void __launch_bounds__(512, 1)
         }
       l_run[qs] = ls;
     }
-    // V^T fragments by transposed reads: lane c of group g reads row
-    // 32 k2 + 4 g + c / 4 (+16 for the second half), columns 16 dt + 4 (c % 4) .. +3
+    // O^T += V^T P^T
+    {
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) {
-      const int colq = (16 * dt + 4 * (c & 3)) >> 3;  // 16-byte chunk of the 4 columns
-      const int half = ((c & 3) & 1) * 8;            // byte offset inside it
+      for (int dt = 0; dt < D / 16; ++dt)
 #pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-        const int r0 = 32 * k2 + 4 * g + (c >> 2), r1 = r0 + 16;
-        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4i16*)(vs_l + r0 * 256 + sm2_vslot(r0, colq) * 16 + half));
-        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4i16*)(vs_l + r1 * 256 + sm2_vslot(r1, colq) * 16 + half));
-        Frag<bf16> a;
-        a.v = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
-        for (int qs = 0; qs < 2; ++qs) mma(o[dt][qs], a, pf[qs][k2]);
-      }
+          for (int qs = 0; qs < 2; ++qs) mma(o[dt][qs], va[dt][k2], pf[qs][k2]);
     }
   }
 

@@ -234,13 +234,13 @@ def test_forward_deterministic():
 
 
 # --------------------------------------------------------- full-size sampled ----
-def full_forward_check(name, heads, query_blocks=None, route_kind=None):
+def full_forward_check(name, heads, query_blocks=None, route_kind=None, branch=None):
     wl = W.WORKLOADS[name]
     inp = W.make_prefill(wl)
     r_ref = W.forced_routes(wl.B, wl.nc, route_kind) if route_kind else O.route(inp["x"], inp["w_score"],
                                                                                  inp["b_score"])[0]
-    say(f"[forward] full {name} {route_kind or ''} B={wl.B} H={wl.H} L={wl.L}")
-    f = run_forward(inp, wl.d, wl.B, wl.H, wl.L, wl.D, route_override=r_ref if route_kind else None)
+    say(f"[forward] full {name} {route_kind or ''} branch={branch} B={wl.B} H={wl.H} L={wl.L}")
+    f = run_forward(inp, wl.d, wl.B, wl.H, wl.L, wl.D, route_override=r_ref if route_kind else None, branch=branch)
     if not route_kind:
         assert np.array_equal(f.route.cpu().numpy(), r_ref)
     worst = 0.0
@@ -256,8 +256,9 @@ def full_forward_check(name, heads, query_blocks=None, route_kind=None):
     assert worst <= TOL_BF16
 
 
-def test_forward_prefill_full_sampled():
-    full_forward_check("prefill", heads=[(0, 0), (1, 7), (3, 15)])
+@pytest.mark.parametrize("branch", [None, torch.float32])
+def test_forward_prefill_full_sampled(branch):
+    full_forward_check("prefill", heads=[(0, 0), (1, 7), (3, 15)], branch=branch)
 
 
 def test_forward_long_full_sampled():
