@@ -33,7 +33,8 @@
  *   - tensors are dense row-major with the shapes given; io tensors (x, q, k,
  *     v, out) hold the io dtype of natsl_dims, alpha/beta/weights are fp32;
  *   - supported: Dk == Dv in {64, 128}, chunk == 64, L % 64 == 0, L >= 64,
- *     route_groups G in {1, H}, d_model % 8 == 0.  B == 0 is a no-op that
+ *     route_groups G in {1, H}, H <= 1024, d_model % 8 == 0 and
+ *     8 <= d_model <= 32768 (where d_model is used).  B == 0 is a no-op that
  *     succeeds after the dims check (tensor pointers may then be NULL).
  *   - route ids: 0 = softmax attention, 1 = Gated DeltaNet (linear).
  */

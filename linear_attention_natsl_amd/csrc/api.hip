@@ -111,6 +111,7 @@ natsl_status check_dims(const natsl_dims* d, bool need_L, bool need_dmodel) {
   if (d->chunk != 64) return fail(NATSL_ERR_UNSUPPORTED, "chunk must be 64 (got %d)", d->chunk);
   if (d->Dk != d->Dv) return fail(NATSL_ERR_UNSUPPORTED, "Dk (%d) != Dv (%d)", d->Dk, d->Dv);
   if (d->Dk != 64 && d->Dk != 128) return fail(NATSL_ERR_UNSUPPORTED, "head dim %d not in {64, 128}", d->Dk);
+  if (d->H > 1024) return fail(NATSL_ERR_UNSUPPORTED, "H=%d above 1024", d->H);
   if (d->route_groups != 1 && d->route_groups != d->H)
     return fail(NATSL_ERR_UNSUPPORTED, "route_groups %d not in {1, H=%d}", d->route_groups, d->H);
   if (need_L) {
@@ -119,8 +120,9 @@ natsl_status check_dims(const natsl_dims* d, bool need_L, bool need_dmodel) {
       return fail(NATSL_ERR_UNSUPPORTED, "B*H*L too large");
   }
   if (need_dmodel) {
-    if (d->d_model < 8 || d->d_model % 8 != 0 || d->d_model > 65536)
-      return fail(NATSL_ERR_UNSUPPORTED, "d_model=%d must be a multiple of 8 in [8, 65536]", d->d_model);
+    // the router keeps the chunk mean (d_model floats) and 2G scores in LDS
+    if (d->d_model < 8 || d->d_model % 8 != 0 || d->d_model > 32768)
+      return fail(NATSL_ERR_UNSUPPORTED, "d_model=%d must be a multiple of 8 in [8, 32768]", d->d_model);
   }
   return NATSL_OK;
 }

@@ -69,6 +69,15 @@ def test_dims_validation(L, mut, status):
     assert L.natsl_last_error()
 
 
+def test_dmodel_and_heads_limits(L):
+    # the router keeps d_model floats of chunk mean plus 2G scores in LDS: the
+    # dims check rejects larger shapes (2) before the NULL x is noticed (1)
+    for dm, H, status in ((32768, 4, 1), (32776, 4, 2), (256, 1024, 1), (256, 1025, 2)):
+        d = N.dims(1, H, 64, 128, dm, N.BF16)
+        got = L.natsl_route(C.byref(d), None, None, None, None, None, None, None, None, None)
+        assert got == status, (dm, H, got, L.natsl_last_error())
+
+
 def test_route_validation(L):
     d = good()
     # x, w_score, b_score, route_in(NULL), route_out, sel_idx, nsel_before, scores, stream
