@@ -422,6 +422,16 @@ __global__ void __launch_bounds__(512, 1)
     if (j < ntiles) issue(j);
 
   const int qrow_base = 32 * (w & 1);
+  Frag<bf16> va[D / 16][2];
+  Frag<bf16> pf[2][2];
+  auto pv = [&]() {
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+        for (int qs = 0; qs < 2; ++qs) mma(o[dt][qs], va[dt][k2], pf[qs][k2]);
+  };
   for (int it = 0; it < ntiles; ++it) {
     wait_vm(4 * (min(it + SM2_STAGES - 2, ntiles - 1) - it));  // this tile's loads have landed
     lds_barrier();                                              // ... for every wave
@@ -468,7 +478,6 @@ __global__ void __launch_bounds__(512, 1)
     // V^T fragments by transposed reads, issued before the softmax work so
     // that it hides their latency: lane c of group g reads row
     // 32 k2 + 4 g + c / 4 (+16 for the second half), columns 16 dt + 4 (c % 4) .. +3
-    Frag<bf16> va[D / 16][2];
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
       const int colq = (16 * dt + 4 * (c & 3)) >> 3;  // 16-byte chunk of the 4 columns
@@ -517,7 +526,6 @@ __global__ void __launch_bounds__(512, 1)
         for (int dt = 0; dt < D / 16; ++dt) o[dt][qs] *= alpha;
       }
     }
-    Frag<bf16> pf[2][2];
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs) {
       const float nm = -m_run[qs];
@@ -544,14 +552,7 @@ __global__ void __launch_bounds__(512, 1)
       l_run[qs] = ls;
     }
     // O^T += V^T P^T
-    {
-#pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt)
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-          for (int qs = 0; qs < 2; ++qs) mma(o[dt][qs], va[dt][k2], pf[qs][k2]);
-    }
+    pv();
   }
 
   if (!active) return;
