@@ -69,7 +69,8 @@ enum {
   NATSL_ENTRY_SOFTMAX_MASKED = 2,
   NATSL_ENTRY_MERGE = 3,
   NATSL_ENTRY_FORWARD = 4,
-  NATSL_ENTRY_DECODE_STEP = 5
+  NATSL_ENTRY_DECODE_STEP = 5,
+  NATSL_ENTRY_DECODE_HANDOFF = 6
 };
 
 typedef struct {
@@ -245,6 +246,35 @@ typedef struct {
 natsl_status natsl_decode_step(const natsl_dims* dims, const natsl_decode_cache* cache,
                                const natsl_decode_args* args, void* ws, size_t ws_bytes,
                                hipStream_t stream);
+
+/*
+ * Prefill -> decode handoff ("Technische Samenvatting: Neural Attention Search
+ * Linear (NAtS-L)", Kernmechanismen 3: the softmax operation keeps only the KV
+ * of the chunks routed to it, the linear operation its fixed-size state).
+ * Fills `cache` as a decode continuing after a prefill of dims->L tokens
+ * (L % 64 == 0) expects it:
+ *   k_cache/v_cache rows [0, 64 * n) of (b, h) = the K/V rows of the n
+ *     softmax-routed chunks of (b, g(h)), in chunk order (bit copies); rows
+ *     from 64 * n on are left as they were;
+ *   n_committed[b, g] = 64 * n;  n_open[b] = 0;
+ *   S_carry = S_final (the state natsl_forward returns) or zero when S_final
+ *     is NULL;  S_work = 0;  x_sum = 0;
+ *   *err_flag = 0, or 1 when some 64 * n exceeds cap (the rows at or beyond
+ *     cap are not written; n_committed still counts them).
+ *   dims      B, H, L, Dk (= Dv), route_groups G, d_model, io of the prefill
+ *   route     [B, G, L/64] int32, 0 = softmax, 1 = linear (route_out of
+ *             natsl_forward or natsl_route)
+ *   k, v      [B, H, L, Dk] io dtype: the prefill's keys and values
+ *   S_final   [B, H, Dk, Dv] fp32 or NULL
+ *   cache     its tensors as in natsl_decode_step, cap = its capacity
+ *   ws        workspace of natsl_workspace_size(NATSL_ENTRY_DECODE_HANDOFF)
+ * A prefix whose last chunk is incomplete continues with natsl_decode_step
+ * for its remaining tokens: the route of an incomplete chunk affects no
+ * prefill output, so that gives the same outputs and cache.
+ */
+natsl_status natsl_decode_handoff(const natsl_dims* dims, const int32_t* route, const void* k, const void* v,
+                                  const float* S_final, const natsl_decode_cache* cache, void* ws,
+                                  size_t ws_bytes, hipStream_t stream);
 
 /*
  * Kernel timing for measurement: when enabled, every kernel the library

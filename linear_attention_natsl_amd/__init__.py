@@ -19,12 +19,14 @@ LIB_PATH = os.path.join(HERE, "libnatsl.so")
 
 F32, BF16 = 0, 1
 ROUTE_SOFTMAX, ROUTE_LINEAR = 0, 1
-ENTRY_ROUTE, ENTRY_GDN_CHUNK, ENTRY_SOFTMAX_MASKED, ENTRY_MERGE, ENTRY_FORWARD, ENTRY_DECODE_STEP = range(6)
+ENTRY_ROUTE, ENTRY_GDN_CHUNK, ENTRY_SOFTMAX_MASKED, ENTRY_MERGE, ENTRY_FORWARD, ENTRY_DECODE_STEP, \
+    ENTRY_DECODE_HANDOFF = range(7)
 STATUS = {0: "NATSL_OK", 1: "NATSL_ERR_INVALID_ARG", 2: "NATSL_ERR_UNSUPPORTED",
           3: "NATSL_ERR_WORKSPACE", 4: "NATSL_ERR_DEVICE", 5: "NATSL_ERR_CAPACITY"}
 EXPORTS = ["natsl_version", "natsl_last_error", "natsl_workspace_size", "natsl_route", "natsl_gdn_chunk",
            "natsl_softmax_masked", "natsl_merge", "natsl_forward", "natsl_decode_step",
-           "natsl_profile_enable", "natsl_profile_reset", "natsl_profile_read", "natsl_profile_select"]
+           "natsl_decode_handoff", "natsl_profile_enable", "natsl_profile_reset", "natsl_profile_read",
+           "natsl_profile_select"]
 
 
 class NatslError(RuntimeError):
@@ -85,11 +87,14 @@ def lib():
         L.natsl_forward.argtypes = [C.POINTER(Dims), C.POINTER(ForwardArgs), vp, C.c_size_t, vp]
         L.natsl_decode_step.argtypes = [C.POINTER(Dims), C.POINTER(DecodeCache), C.POINTER(DecodeArgs), vp,
                                         C.c_size_t, vp]
+        L.natsl_decode_handoff.argtypes = [C.POINTER(Dims), vp, vp, vp, vp, C.POINTER(DecodeCache), vp, C.c_size_t,
+                                           vp]
         L.natsl_profile_enable.argtypes = [C.c_int]
         L.natsl_profile_read.argtypes = [C.c_char_p, C.POINTER(C.c_int), C.POINTER(C.c_double)]
         L.natsl_profile_select.argtypes = [C.c_char_p]
         for name in ("natsl_workspace_size", "natsl_route", "natsl_gdn_chunk", "natsl_softmax_masked",
-                     "natsl_merge", "natsl_forward", "natsl_decode_step", "natsl_profile_enable",
+                     "natsl_merge", "natsl_forward", "natsl_decode_step", "natsl_decode_handoff",
+                     "natsl_profile_enable",
                      "natsl_profile_reset", "natsl_profile_read", "natsl_profile_select"):
             getattr(L, name).restype = st
         _lib = L
@@ -340,6 +345,26 @@ def decode_step(dm: Dims, state: DecodeState, *args, debug=False, **kw):
     d = Decode(dm, state, device=args[1].device, debug=debug)
     d(*args, **kw)
     return d
+
+
+def decode_handoff(dm: Dims, route, k, v, S_final, state: DecodeState, stream=None):
+    """Fill `state` as the decode cache after a prefill of dm.L tokens: the
+    K/V rows of its softmax-routed chunks, S_carry = S_final (None: zero),
+    empty open chunk.  `route` is the forward's route [B, G, L/64]."""
+    B, H, G, nc, D = dm.B, dm.H, dm.route_groups, dm.L // 64, dm.Dk
+    io = _io_t(dm)
+    if state.k.dtype != io or tuple(state.k.shape[:2]) != (B, H) or state.k.shape[3] != D:
+        raise ValueError("decode state does not match the dims")
+    if tuple(state.n_committed.shape) != (B, G) or tuple(state.x_sum.shape) != (B, dm.d_model):
+        raise ValueError("decode state counters do not match the dims")
+    ws_bytes = workspace_size(ENTRY_DECODE_HANDOFF, dm)
+    ws = workspace(ws_bytes, k.device)
+    cs = state.struct()
+    _check(lib().natsl_decode_handoff(C.byref(dm), _p(route, torch.int32, "route", (B, G, nc)),
+                                      _p(k, io, "k", (B, H, dm.L, D)), _p(v, io, "v", (B, H, dm.L, D)),
+                                      _p(S_final, torch.float32, "S_final", (B, H, D, D)), C.byref(cs),
+                                      _p(ws), ws_bytes, _stream(stream)))
+    return state
 
 
 def profile_enable(on=True):

@@ -303,6 +303,10 @@ natsl_status natsl_workspace_size(int entry, const natsl_dims* dims, size_t* byt
       if (dims->L < 1) return fail(NATSL_ERR_INVALID_ARG, "decode: dims->L must hold the cache capacity");
       *bytes = decode_ws_bytes(dims->B, dims->H, dims->route_groups, dims->Dk, dims->L);
       return ok();
+    case NATSL_ENTRY_DECODE_HANDOFF:
+      CHECK(check_dims(dims, true, false));
+      *bytes = handoff_ws_bytes(dims->B, dims->route_groups, nchunks(dims));
+      return ok();
     default:
       return fail(NATSL_ERR_INVALID_ARG, "unknown entry id %d", entry);
   }
@@ -500,6 +504,50 @@ natsl_status natsl_decode_step(const natsl_dims* dims, const natsl_decode_cache*
   else
     e = dims->Dk == 64 ? launch_decode<float, 64>(L, ws, stream, prof) : launch_decode<float, 128>(L, ws, stream, prof);
   if (e != hipSuccess) return dev_fail(e, "natsl_decode_step");
+  return ok();
+}
+
+natsl_status natsl_decode_handoff(const natsl_dims* dims, const int32_t* route, const void* k, const void* v,
+                                  const float* S_final, const natsl_decode_cache* c, void* ws, size_t ws_bytes,
+                                  hipStream_t stream) {
+  CHECK(check_dims(dims, true, true));
+  if (dims->B == 0) return ok();  // empty batch: nothing to do, pointers may be NULL
+  NEED(route, "route");
+  NEED(k, "k");
+  NEED(v, "v");
+  NEED(c, "cache");
+  NEED(c->k_cache, "k_cache");
+  NEED(c->v_cache, "v_cache");
+  NEED(c->n_committed, "n_committed");
+  NEED(c->n_open, "n_open");
+  NEED(c->S_carry, "S_carry");
+  NEED(c->S_work, "S_work");
+  NEED(c->x_sum, "x_sum");
+  NEED(c->err_flag, "err_flag");
+  if (c->cap < 1) return fail(NATSL_ERR_INVALID_ARG, "cache capacity %d", c->cap);
+  CHECK(check_ws(ws, ws_bytes, handoff_ws_bytes(dims->B, dims->route_groups, nchunks(dims))));
+  HandoffLaunch L;
+  L.B = dims->B;
+  L.H = dims->H;
+  L.G = dims->route_groups;
+  L.L = dims->L;
+  L.D = dims->Dk;
+  L.d = dims->d_model;
+  L.cap = c->cap;
+  L.route = route;
+  L.k = k;
+  L.v = v;
+  L.S_final = S_final;
+  L.k_cache = c->k_cache;
+  L.v_cache = c->v_cache;
+  L.n_committed = c->n_committed;
+  L.n_open = c->n_open;
+  L.err_flag = c->err_flag;
+  L.S_carry = c->S_carry;
+  L.S_work = c->S_work;
+  L.x_sum = c->x_sum;
+  const hipError_t e = dims->io == NATSL_BF16 ? launch_handoff<bf16>(L, ws, stream) : launch_handoff<float>(L, ws, stream);
+  if (e != hipSuccess) return dev_fail(e, "natsl_decode_handoff");
   return ok();
 }
 

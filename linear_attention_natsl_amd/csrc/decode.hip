@@ -12,8 +12,8 @@
 // The step is HBM-bound (the cached rows dominate):
 //   k_decode_route    x_sum += x; on chunk completion score x_sum / 64
 //   k_decode_gdn      one 64 KiB fp32 state read + write per (b, h)
-//   k_decode_attn     split-KV flash decode: every workgroup streams 512 rows
-//                     of K and V (16 lanes per row, 16-byte loads, 8 rows per
+//   k_decode_attn     split-KV flash decode: every workgroup streams 1024 rows
+//                     of K and V (16 lanes per row, 16-byte loads, 16 rows per
 //                     lane group in flight) and leaves (max, sum, o) partials
 //   k_decode_combine  merge the partials and the new token, RMSNorm both
 //                     branches, Q-derived weights, append the new k/v row

@@ -61,6 +61,20 @@ struct DecodeLaunch {
   float *o_sm_dbg, *o_gdn_dbg;
 };
 size_t decode_ws_bytes(int B, int H, int G, int D, int cap);
+
+// prefill -> decode handoff
+struct HandoffLaunch {
+  int B, H, G, L, D, d, cap;
+  const int32_t* route;
+  const void *k, *v;
+  const float* S_final;
+  void *k_cache, *v_cache;
+  int32_t *n_committed, *n_open, *err_flag;
+  float *S_carry, *S_work, *x_sum;
+};
+size_t handoff_ws_bytes(int B, int G, int nc);
+template <typename T>
+hipError_t launch_handoff(const HandoffLaunch& a, void* ws, hipStream_t st);
 template <typename T, int D>
 hipError_t launch_decode(const DecodeLaunch& a, void* ws, hipStream_t st,
                          void (*prof)(int, hipStream_t, int));

@@ -153,6 +153,30 @@ def test_decode_validation(L):
     assert L.natsl_decode_step(C.byref(d), C.byref(c), C.byref(a), FAKE, need - 256, None) == 3
 
 
+def test_decode_handoff_validation(L):
+    d = good()
+    c = N.DecodeCache()
+    for f in ("k_cache", "v_cache", "n_committed", "n_open", "S_carry", "S_work", "x_sum", "err_flag"):
+        setattr(c, f, FAKE)
+    c.cap = 1024
+    need = N.workspace_size(N.ENTRY_DECODE_HANDOFF, d)
+    assert need == d.B * d.route_groups * (2 * (d.L // 64) + 1) * 4
+    call = lambda dd, route, cc, ws, nbytes: L.natsl_decode_handoff(C.byref(dd), route, FAKE, FAKE, None, C.byref(cc),
+                                                                    ws, nbytes, None)
+    assert call(d, None, c, FAKE, need) == 1             # route missing
+    assert call(d, FAKE, c, FAKE, need - 4) == 3         # workspace too small
+    bad = good()
+    bad.L = 100
+    assert call(bad, FAKE, c, FAKE, need) == 2           # L not a whole number of chunks
+    c0 = N.DecodeCache()
+    assert call(d, FAKE, c0, FAKE, need) == 1            # cache tensors missing
+    c.cap = 0
+    assert call(d, FAKE, c, FAKE, need) == 1             # no capacity
+    empty = good()
+    empty.B = 0
+    assert call(empty, None, N.DecodeCache(), None, 0) == 0  # empty batch is a no-op
+
+
 def test_workspace_sizes_monotone(L):
     prev = 0
     for Lq in (64, 128, 1024, 4096):

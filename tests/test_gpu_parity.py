@@ -334,6 +334,107 @@ def test_decode_steps_match_oracle(io, D):
     assert int(st.err.item()) == 0
 
 
+@pytest.mark.parametrize("io,D", [("f32", 64), ("bf16", 128)])
+def test_decode_handoff_then_decode(io, D):
+    """natsl_forward over a 192-token prefix, natsl_decode_handoff of its
+    route, K/V and final state, then 64 decode steps (one chunk completion):
+    the handed-off cache equals the oracle's cache for the prefix (rows and
+    counters bit-exact, S_carry = the forward's S_final), and every decoded
+    output matches the oracle's decode from that cache."""
+    B, H, L, n0 = 2, 2, 256, 192
+    wl, inp = small_case(io, B=B, H=H, L=L, D=D, seed=61, sm_frac=0.5)
+    d = wl.d
+    say(f"[handoff] io={io} D={D}")
+    pre = {k: (val[:, :n0] if k == "x" else val[:, :, :n0]) if k in ("x", "q", "k", "v", "alpha", "beta") else val
+           for k, val in inp.items()}
+    f = run_forward(pre, d, B, H, n0, D)
+    cap = L + 64
+    st = N.DecodeState(B, H, D, d, cap, io=torch.bfloat16 if io == "bf16" else torch.float32)
+    st.n_committed.fill_(5)
+    st.n_open.fill_(7)
+    st.err.fill_(3)
+    st.x_sum.fill_(1.0)
+    st.S_work.fill_(2.0)
+    dm_pre = N.dims(B, H, n0, D, d, io_code(inp))
+    tp = prefill_tensors(pre)
+    N.decode_handoff(dm_pre, f.route, tp["k"], tp["v"], f.S_final, st)
+    torch.cuda.synchronize()
+    ref = O.build_cache(pre["x"], pre["k"], pre["v"], pre["alpha"], pre["beta"], pre["w_score"], pre["b_score"],
+                        cap=cap)
+    nco = ref["n_committed"].astype(np.int32)
+    assert np.array_equal(st.n_committed.cpu().numpy(), nco)
+    assert np.array_equal(st.n_open.cpu().numpy(), np.zeros(B, np.int32))
+    assert int(st.err.item()) == 0
+    assert not st.x_sum.any() and not st.S_work.any()
+    assert torch.equal(st.S_carry, f.S_final)
+    kc, vc = host(st.k), host(st.v)
+    for b in range(B):
+        n = int(nco[b, 0])
+        assert 0 < n < n0
+        assert np.array_equal(kc[b, :, :n], ref["k"][b, :, :n]) and np.array_equal(vc[b, :, :n], ref["v"][b, :, :n])
+    e_state = maxerr(host(st.S_carry), ref["S_carry"])
+    say(f"  S_carry err {e_state:.3e}")
+    assert e_state <= (1e-4 if io == "f32" else 1e-2)
+    # continue with decode steps from the handed-off cache
+    dm = N.dims(B, H, L, D, d, io_code(inp))
+    dec = N.Decode(dm, st, debug=True)
+    t = prefill_tensors(inp)
+    tol = TOL_F32 if io == "f32" else TOL_BF16
+    cache = ref
+    worst = 0.0
+    for tok in range(n0, L):
+        dec(t["x"][:, tok].contiguous(), t["q"][:, :, tok].contiguous(), t["k"][:, :, tok].contiguous(),
+            t["v"][:, :, tok].contiguous(), t["alpha"][:, :, tok].contiguous(), t["beta"][:, :, tok].contiguous(),
+            t["w_score"], t["w_mix"], b_score=t["b_score"], g_sm=t["g_sm"], g_lin=t["g_lin"])
+        out_ref, br, cache = O.decode_step(cache, inp["x"][:, tok], inp["q"][:, :, tok], inp["k"][:, :, tok],
+                                           inp["v"][:, :, tok], inp["alpha"][:, :, tok], inp["beta"][:, :, tok],
+                                           inp["w_score"], inp["w_mix"], inp["b_score"], inp["g_sm"], inp["g_lin"])
+        torch.cuda.synchronize()
+        assert np.array_equal(dec.route.cpu().numpy(), br["routes"]), f"tok {tok}"
+        e = maxerr(host(dec.out), out_ref)
+        worst = max(worst, e)
+        assert e <= tol, f"tok {tok}: err {e}"
+    say(f"  decode worst err {worst:.3e}")
+    assert np.array_equal(st.n_committed.cpu().numpy(), cache["n_committed"].astype(np.int32))
+    assert int(st.err.item()) == 0
+
+
+def test_decode_handoff_groups_and_capacity():
+    """route_groups = H with forced per-head routes: each head's cache holds
+    its own softmax chunks and S_carry follows its own linear chunks; with a
+    capacity below the retained rows the flag is raised, the rows that fit
+    are written and the counters still count every row."""
+    B, H, L, D = 2, 4, 512, 128
+    G = H
+    wl, inp = small_case("bf16", B=B, H=H, L=L, D=D, seed=67, sm_frac=0.5)
+    rng = np.random.default_rng(67)
+    r = (rng.random((B, G, L // 64)) < 0.5).astype(np.int32)  # 1 = linear
+    r[:, :, 0] = 0
+    say("[handoff] groups = H, capacity")
+    f = run_forward(inp, wl.d, B, H, L, D, route_override=r, groups=G)
+    assert np.array_equal(f.route.cpu().numpy(), r)
+    dm = N.dims(B, H, L, D, wl.d, N.BF16, groups=G)
+    t = prefill_tensors(inp)
+    nsm = (r == 0).sum(axis=2) * 64
+    _, S_ref = O.gdn_branch(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], r)
+    for cap in (L, int(nsm.max()) - 32):
+        st = N.DecodeState(B, H, D, wl.d, cap, groups=G, io=torch.bfloat16)
+        N.decode_handoff(dm, f.route, t["k"], t["v"], f.S_final, st)
+        torch.cuda.synchronize()
+        assert np.array_equal(st.n_committed.cpu().numpy(), nsm.astype(np.int32))
+        assert int(st.err.item()) == (1 if cap < nsm.max() else 0)
+        kc = host(st.k)
+        for b in range(B):
+            for h in range(H):
+                rows = np.concatenate([inp["k"][b, h, c * 64:(c + 1) * 64] for c in range(L // 64) if r[b, h, c] == 0])
+                n = min(len(rows), cap)
+                assert np.array_equal(kc[b, h, :n], rows[:n]), (cap, b, h)
+        assert torch.equal(st.S_carry, f.S_final)
+    e = maxerr(host(f.S_final), S_ref)
+    say(f"  S_final err {e:.3e}")
+    assert e <= 1e-2
+
+
 def test_decode_full_sampled():
     """The decode workload at full size (B=64, ~8192 cached rows per head),
     one step; sampled sequences against the oracle."""
