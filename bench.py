@@ -118,6 +118,34 @@ def kernel_table(N, fn, names, reps):
     return out
 
 
+def time_handoff(N, dm, route, t, wl, reps=20):
+    """The prefill -> decode handoff of this prefill (its routes, K and V) into
+    a decode cache sized for its softmax rows: bytes moved = the softmax
+    chunks' K/V rows read and written + S_final read + S_carry, S_work
+    written; timed with events around the whole call."""
+    import torch
+    dev = t["k"].device
+    nsm = int((route == 0).sum(dim=2).max().item()) * 64
+    cap = nsm + 64
+    st = N.DecodeState(wl.B, wl.H, wl.D, wl.d, cap, groups=dm.route_groups, io=t["k"].dtype, device=dev)
+    S_final = torch.zeros(wl.B, wl.H, wl.D, wl.D, dtype=torch.float32, device=dev)
+    for _ in range(3):
+        N.decode_handoff(dm, route, t["k"], t["v"], S_final, st)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        N.decode_handoff(dm, route, t["k"], t["v"], S_final, st)
+    e1.record()
+    torch.cuda.synchronize()
+    us = 1000.0 * e0.elapsed_time(e1) / reps
+    rows = int((route == 0).sum().item()) * 64 * (wl.H // dm.route_groups)
+    nbytes = 2 * 2 * rows * wl.D * t["k"].element_size() + 3 * wl.B * wl.H * wl.D * wl.D * 4
+    return dict(workload=f"handoff of the {wl.name} prefill: {rows} softmax rows of K and V, cache capacity {cap}",
+                us=round(us, 2), bytes=nbytes, gbs=round(nbytes / (us * 1e-6) / 1e9, 1),
+                frac_hbm=round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4))
+
+
 def time_prefill(args, N, W, O):
     import torch
     wl = W.WORKLOADS[args.workload]
@@ -150,6 +178,7 @@ def time_prefill(args, N, W, O):
     kernels = kernel_table(N, call, ("route", "compact", "gdn_prep", "gdn_scan", "softmax_masked", "merge"),
                            max(5, args.steps // 5))
     N.profile_enable(False)
+    handoff = time_handoff(N, dm, fwd.route, t, wl)
     route = fwd.route.cpu().numpy()
     ref_route = O.route(inp["x"], inp["w_score"], inp["b_score"])[0] if args.check_route else None
     pairs = sm_pairs(route, wl.H)
@@ -179,6 +208,7 @@ def time_prefill(args, N, W, O):
                    layer_tflops=round((f_sm + f_gdn) / (dt / args.steps) / 1e12, 1),
                    layer_frac_of_mfma_peak=round((f_sm + f_gdn) / (dt / args.steps) / 1e12 / PEAK_BF16_TFLOPS, 4),
                    kernels=kernels),
+        handoff=handoff,
     )
     return res, inp, route
 
