@@ -435,6 +435,53 @@ def test_decode_handoff_groups_and_capacity():
     assert e <= 1e-2
 
 
+def test_decode_groups_per_head_mix():
+    """Per-head routing in decode (route_groups = H), a score bias, per-head
+    W_mix and branch gains.  Odd groups score with the two columns swapped,
+    so their routes are the opposite of the even groups' at the same planted
+    margin (|margin| ~ 1, the +-0.1 bias cannot flip it).  150 steps from a
+    100-token prefix against the oracle's decode."""
+    B, H, L, D = 2, 4, 256, 64
+    G = H
+    wl, inp = small_case("f32", B=B, H=H, L=L, D=D, seed=71, sm_frac=0.5)
+    d = wl.d
+    w1 = inp["w_score"]
+    wG = np.ascontiguousarray(np.concatenate([w1 if g % 2 == 0 else w1[:, ::-1] for g in range(G)], axis=1))
+    bG = np.tile(np.array([0.1, -0.1], np.float32), G)
+    wmix = np.random.default_rng(71).normal(0, 0.3, (H, D, 2)).astype(np.float32)
+    n0 = 100
+    say("[decode] groups = H, per-head W_mix, score bias")
+    cache = O.build_cache(inp["x"][:, :n0], inp["k"][:, :, :n0], inp["v"][:, :, :n0], inp["alpha"][:, :, :n0],
+                          inp["beta"][:, :, :n0], wG, bG, cap=L + 64, groups=G)
+    st = load_state(cache, B, H, D, d, "f32", groups=G)
+    dm = N.dims(B, H, L, D, d, N.F32, groups=G)
+    dec = N.Decode(dm, st, debug=True)
+    t = prefill_tensors(inp)
+    twG, tbG, twmix = dev(wG), dev(bG), dev(wmix)
+    worst = 0.0
+    seen = set()
+    for tok in range(n0, L):
+        dec(t["x"][:, tok].contiguous(), t["q"][:, :, tok].contiguous(), t["k"][:, :, tok].contiguous(),
+            t["v"][:, :, tok].contiguous(), t["alpha"][:, :, tok].contiguous(), t["beta"][:, :, tok].contiguous(),
+            twG, twmix, b_score=tbG, g_sm=t["g_sm"], g_lin=t["g_lin"], w_mix_head_stride=2 * D)
+        out_ref, br, cache = O.decode_step(cache, inp["x"][:, tok], inp["q"][:, :, tok], inp["k"][:, :, tok],
+                                           inp["v"][:, :, tok], inp["alpha"][:, :, tok], inp["beta"][:, :, tok],
+                                           wG, wmix, bG, inp["g_sm"], inp["g_lin"])
+        torch.cuda.synchronize()
+        routes = dec.route.cpu().numpy()
+        assert np.array_equal(routes, br["routes"]), f"tok {tok}"
+        if (routes >= 0).any():
+            assert np.array_equal(routes[:, 0::2], 1 - routes[:, 1::2]), "odd groups route opposite"
+        seen.update(int(x) for x in routes.ravel() if x >= 0)
+        e = maxerr(host(dec.out), out_ref)
+        worst = max(worst, e)
+        assert e <= TOL_F32, f"tok {tok}: err {e}"
+    say(f"  worst err {worst:.3e}, routes seen {seen}")
+    assert seen == {0, 1}
+    assert np.array_equal(st.n_committed.cpu().numpy(), cache["n_committed"].astype(np.int32))
+    assert maxerr(host(st.S_carry), cache["S_carry"]) <= 1e-4
+
+
 def test_decode_full_sampled():
     """The decode workload at full size (B=64, ~8192 cached rows per head),
     one step; sampled sequences against the oracle."""
