@@ -166,6 +166,18 @@ natsl_status natsl_merge(const natsl_dims* dims, const void* q, const void* o_sm
                          const float* g_sm, const float* g_lin, void* out, hipStream_t stream);
 
 typedef struct {
+  void* k_cache;               /* [B, H, cap, Dk] io: compacted KV             */
+  void* v_cache;               /* [B, H, cap, Dv] io                           */
+  int32_t cap;                 /* rows per (b, h)                              */
+  int32_t* n_committed;        /* [B, G] rows of committed softmax chunks      */
+  int32_t* n_open;             /* [B] tokens of the open (incomplete) chunk    */
+  float* S_carry;              /* [B, H, Dk, Dv] state after committed chunks  */
+  float* S_work;               /* [B, H, Dk, Dv] open chunk's pseudo-updated   */
+  float* x_sum;                /* [B, d_model] sum of x over the open chunk    */
+  int32_t* err_flag;           /* [1]: set to 1 when a row would exceed cap    */
+} natsl_decode_cache;
+
+typedef struct {
   const void* x;               /* [B, L, d_model] io (NULL if route_override) */
   const void* q;               /* [B, H, L, Dk] io                            */
   const void* k;               /* [B, H, L, Dk] io                            */
@@ -189,26 +201,26 @@ typedef struct {
                                   Gated DeltaNet branch output                */
   float* S_final;              /* [B, H, Dk, Dv] or NULL                      */
   void* out;                   /* [B, H, L, Dv] io                            */
+  const natsl_decode_cache* prefix; /* NULL, or the decode cache this segment
+                                  continues (chunked prefill, see below)      */
 } natsl_forward_args;
 
 /*
  * Whole layer forward: route + compaction, Gated DeltaNet branch and softmax
  * branch (run concurrently), merge.  ws from NATSL_ENTRY_FORWARD.
+ * Chunked prefill: with args->prefix set, the L tokens are a segment that
+ * continues that decode cache, which must sit at a chunk boundary
+ * (n_open == 0, e.g. right after natsl_decode_handoff): every query of the
+ * segment also attends to the cache's min(n_committed, cap) committed softmax
+ * rows (before the segment's own chunks), and the Gated DeltaNet branch starts
+ * from the cache's S_carry (S_init must then be NULL).  The outputs equal
+ * those of one prefill over the cached prefix and the segment; appending the
+ * segment with natsl_decode_handoff(..., append = 1) then gives the cache of
+ * that whole prefill.  The prefix is only read.
  */
 natsl_status natsl_forward(const natsl_dims* dims, const natsl_forward_args* args, void* ws,
                            size_t ws_bytes, hipStream_t stream);
 
-typedef struct {
-  void* k_cache;               /* [B, H, cap, Dk] io: compacted KV             */
-  void* v_cache;               /* [B, H, cap, Dv] io                           */
-  int32_t cap;                 /* rows per (b, h)                              */
-  int32_t* n_committed;        /* [B, G] rows of committed softmax chunks      */
-  int32_t* n_open;             /* [B] tokens of the open (incomplete) chunk    */
-  float* S_carry;              /* [B, H, Dk, Dv] state after committed chunks  */
-  float* S_work;               /* [B, H, Dk, Dv] open chunk's pseudo-updated   */
-  float* x_sum;                /* [B, d_model] sum of x over the open chunk    */
-  int32_t* err_flag;           /* [1]: set to 1 when a row would exceed cap    */
-} natsl_decode_cache;
 
 typedef struct {
   const void* x;               /* [B, d_model] io                              */
@@ -267,13 +279,20 @@ natsl_status natsl_decode_step(const natsl_dims* dims, const natsl_decode_cache*
  *   k, v      [B, H, L, Dk] io dtype: the prefill's keys and values
  *   S_final   [B, H, Dk, Dv] fp32 or NULL
  *   cache     its tensors as in natsl_decode_step, cap = its capacity
+ *   append    0: as above.  1: the cache already holds a prefix at a chunk
+ *             boundary and the L tokens were a segment prefilled on top of it
+ *             (natsl_forward with args->prefix = cache): the segment's softmax
+ *             rows go to rows [n_committed, n_committed + 64 n) and
+ *             n_committed += 64 n; S_carry = S_final (required); S_work,
+ *             x_sum, n_open as above; *err_flag is not cleared, and is set
+ *             when a row would reach cap or the cache has an open chunk.
  *   ws        workspace of natsl_workspace_size(NATSL_ENTRY_DECODE_HANDOFF)
  * A prefix whose last chunk is incomplete continues with natsl_decode_step
  * for its remaining tokens: the route of an incomplete chunk affects no
  * prefill output, so that gives the same outputs and cache.
  */
 natsl_status natsl_decode_handoff(const natsl_dims* dims, const int32_t* route, const void* k, const void* v,
-                                  const float* S_final, const natsl_decode_cache* cache, void* ws,
+                                  const float* S_final, int append, const natsl_decode_cache* cache, void* ws,
                                   size_t ws_bytes, hipStream_t stream);
 
 /*

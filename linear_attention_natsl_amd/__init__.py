@@ -48,7 +48,7 @@ class ForwardArgs(C.Structure):
                 ("g_lin", C.c_void_p), ("route_override", C.c_void_p), ("S_init", C.c_void_p),
                 ("branch_dtype", C.c_int), ("route_out", C.c_void_p), ("scores_out", C.c_void_p),
                 ("o_sm_dbg", C.c_void_p), ("o_gdn_dbg", C.c_void_p), ("S_final", C.c_void_p),
-                ("out", C.c_void_p)]
+                ("out", C.c_void_p), ("prefix", C.c_void_p)]
 
 
 class DecodeCache(C.Structure):
@@ -87,8 +87,8 @@ def lib():
         L.natsl_forward.argtypes = [C.POINTER(Dims), C.POINTER(ForwardArgs), vp, C.c_size_t, vp]
         L.natsl_decode_step.argtypes = [C.POINTER(Dims), C.POINTER(DecodeCache), C.POINTER(DecodeArgs), vp,
                                         C.c_size_t, vp]
-        L.natsl_decode_handoff.argtypes = [C.POINTER(Dims), vp, vp, vp, vp, C.POINTER(DecodeCache), vp, C.c_size_t,
-                                           vp]
+        L.natsl_decode_handoff.argtypes = [C.POINTER(Dims), vp, vp, vp, vp, C.c_int, C.POINTER(DecodeCache), vp,
+                                           C.c_size_t, vp]
         L.natsl_profile_enable.argtypes = [C.c_int]
         L.natsl_profile_read.argtypes = [C.c_char_p, C.POINTER(C.c_int), C.POINTER(C.c_double)]
         L.natsl_profile_select.argtypes = [C.c_char_p]
@@ -244,7 +244,10 @@ class Forward:
             if want_state else None
 
     def __call__(self, x, q, k, v, alpha, beta, w_score, w_mix, b_score=None, g_sm=None, g_lin=None,
-                 route_override=None, S_init=None, w_mix_head_stride=0, stream=None):
+                 route_override=None, S_init=None, w_mix_head_stride=0, stream=None, prefix=None):
+        """prefix: a DecodeState at a chunk boundary that these L tokens
+        continue (chunked prefill): the softmax branch also attends to its
+        committed rows and the Gated DeltaNet branch starts from its S_carry."""
         dm = self.dm
         io, qs, ts, nc, G2 = _io_t(dm), (dm.B, dm.H, dm.L, dm.Dk), (dm.B, dm.H, dm.L), dm.L // 64, 2 * dm.route_groups
         if w_mix_head_stride not in (0, 2 * dm.Dk):
@@ -264,7 +267,16 @@ class Forward:
         a.route_out, a.scores_out = _p(self.route), (_p(self.scores) if route_override is None else None)
         a.o_sm_dbg, a.o_gdn_dbg = _p(self.o_sm), _p(self.o_gdn)
         a.S_final, a.out = _p(self.S_final), _p(self.out)
+        pre = None
+        if prefix is not None:
+            if prefix.k.dtype != io or tuple(prefix.k.shape[:2]) != (dm.B, dm.H) or prefix.k.shape[3] != dm.Dk:
+                raise ValueError("prefix cache does not match the dims")
+            if tuple(prefix.n_committed.shape) != (dm.B, dm.route_groups):
+                raise ValueError("prefix cache counters do not match the dims")
+            pre = prefix.struct()
+            a.prefix = C.cast(C.pointer(pre), C.c_void_p)
         _check(lib().natsl_forward(C.byref(self.dm), C.byref(a), _p(self.ws), self.ws_bytes, _stream(stream)))
+        del pre
         return self.out
 
 
@@ -347,10 +359,12 @@ def decode_step(dm: Dims, state: DecodeState, *args, debug=False, **kw):
     return d
 
 
-def decode_handoff(dm: Dims, route, k, v, S_final, state: DecodeState, stream=None):
+def decode_handoff(dm: Dims, route, k, v, S_final, state: DecodeState, append=False, stream=None):
     """Fill `state` as the decode cache after a prefill of dm.L tokens: the
     K/V rows of its softmax-routed chunks, S_carry = S_final (None: zero),
-    empty open chunk.  `route` is the forward's route [B, G, L/64]."""
+    empty open chunk.  `route` is the forward's route [B, G, L/64].  With
+    append=True the tokens were a segment prefilled on top of `state`
+    (Forward(..., prefix=state)) and its rows are added after the cached ones."""
     B, H, G, nc, D = dm.B, dm.H, dm.route_groups, dm.L // 64, dm.Dk
     io = _io_t(dm)
     if state.k.dtype != io or tuple(state.k.shape[:2]) != (B, H) or state.k.shape[3] != D:
@@ -362,7 +376,8 @@ def decode_handoff(dm: Dims, route, k, v, S_final, state: DecodeState, stream=No
     cs = state.struct()
     _check(lib().natsl_decode_handoff(C.byref(dm), _p(route, torch.int32, "route", (B, G, nc)),
                                       _p(k, io, "k", (B, H, dm.L, D)), _p(v, io, "v", (B, H, dm.L, D)),
-                                      _p(S_final, torch.float32, "S_final", (B, H, D, D)), C.byref(cs),
+                                      _p(S_final, torch.float32, "S_final", (B, H, D, D)), 1 if append else 0,
+                                      C.byref(cs),
                                       _p(ws), ws_bytes, _stream(stream)))
     return state
 

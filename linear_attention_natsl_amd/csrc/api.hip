@@ -201,24 +201,26 @@ hipError_t do_route(const natsl_dims* d, const void* x, const float* w, const fl
 
 template <typename T, typename To>
 hipError_t do_softmax_t(const natsl_dims* d, const void* q, const void* k, const void* v,
-                        const int32_t* sel, const int32_t* nsb, void* o, float* lse, hipStream_t st) {
+                        const int32_t* sel, const int32_t* nsb, void* o, float* lse, hipStream_t st,
+                        const SmPrefix& pre) {
   if (d->Dk == 64)
     return launch_softmax_masked<T, To, 64>((const T*)q, (const T*)k, (const T*)v, sel, nsb, (To*)o, lse,
-                                            d->B, d->H, d->L, d->route_groups, eff_scale(d), st);
+                                            d->B, d->H, d->L, d->route_groups, eff_scale(d), st, pre);
   return launch_softmax_masked<T, To, 128>((const T*)q, (const T*)k, (const T*)v, sel, nsb, (To*)o, lse,
-                                           d->B, d->H, d->L, d->route_groups, eff_scale(d), st);
+                                           d->B, d->H, d->L, d->route_groups, eff_scale(d), st, pre);
 }
 hipError_t do_softmax(const natsl_dims* d, const void* q, const void* k, const void* v, const int32_t* sel,
-                      const int32_t* nsb, void* o, natsl_dtype od, float* lse, hipStream_t st) {
+                      const int32_t* nsb, void* o, natsl_dtype od, float* lse, hipStream_t st,
+                      const SmPrefix& pre = SmPrefix()) {
   auto prof = prof_fn();
   if (prof) prof(KID_SOFTMAX, st, 0);
   hipError_t e;
   if (d->io == NATSL_BF16)
-    e = od == NATSL_BF16 ? do_softmax_t<bf16, bf16>(d, q, k, v, sel, nsb, o, lse, st)
-                         : do_softmax_t<bf16, float>(d, q, k, v, sel, nsb, o, lse, st);
+    e = od == NATSL_BF16 ? do_softmax_t<bf16, bf16>(d, q, k, v, sel, nsb, o, lse, st, pre)
+                         : do_softmax_t<bf16, float>(d, q, k, v, sel, nsb, o, lse, st, pre);
   else
-    e = od == NATSL_BF16 ? do_softmax_t<float, bf16>(d, q, k, v, sel, nsb, o, lse, st)
-                         : do_softmax_t<float, float>(d, q, k, v, sel, nsb, o, lse, st);
+    e = od == NATSL_BF16 ? do_softmax_t<float, bf16>(d, q, k, v, sel, nsb, o, lse, st, pre)
+                         : do_softmax_t<float, float>(d, q, k, v, sel, nsb, o, lse, st, pre);
   if (e == hipSuccess && prof) prof(KID_SOFTMAX, st, 1);
   return e;
 }
@@ -406,6 +408,23 @@ natsl_status natsl_forward(const natsl_dims* dims, const natsl_forward_args* a, 
   if (a->branch_dtype != NATSL_F32 && a->branch_dtype != NATSL_BF16)
     return fail(NATSL_ERR_INVALID_ARG, "bad branch dtype");
   if (a->w_mix_head_stride < 0) return fail(NATSL_ERR_INVALID_ARG, "negative w_mix head stride");
+  // chunked prefill: the segment continues a decode cache at a chunk boundary
+  SmPrefix pre;
+  const float* S_init = a->S_init;
+  if (a->prefix) {
+    const natsl_decode_cache* c = a->prefix;
+    NEED(c->k_cache, "prefix k_cache");
+    NEED(c->v_cache, "prefix v_cache");
+    NEED(c->n_committed, "prefix n_committed");
+    NEED(c->S_carry, "prefix S_carry");
+    if (a->S_init) return fail(NATSL_ERR_INVALID_ARG, "S_init and prefix are exclusive (the prefix's S_carry is used)");
+    if (c->cap < 0) return fail(NATSL_ERR_INVALID_ARG, "prefix capacity %d", c->cap);
+    pre.k = c->k_cache;
+    pre.v = c->v_cache;
+    pre.n_committed = c->n_committed;
+    pre.cap = c->cap;
+    S_init = c->S_carry;
+  }
   FwdWs w;
   const size_t need = fwd_ws(dims, a->branch_dtype, nullptr, nullptr);
   CHECK(check_ws(ws, ws_bytes, need));
@@ -425,10 +444,10 @@ natsl_status natsl_forward(const natsl_dims* dims, const natsl_forward_args* a, 
   e = do_route(dims, a->x, a->w_score, a->b_score, a->route_override, route, w.sel, w.nsb, a->scores_out, stream);
   if (e != hipSuccess) return dev_fail(e, "natsl_forward/route");
   if ((e = hipEventRecord(ctx->routed, stream)) != hipSuccess) return dev_fail(e, "hipEventRecord");
-  e = do_gdn(dims, a->q, a->k, a->v, a->alpha, a->beta, route, a->S_init, o_gd, a->branch_dtype, a->S_final,
+  e = do_gdn(dims, a->q, a->k, a->v, a->alpha, a->beta, route, S_init, o_gd, a->branch_dtype, a->S_final,
              w.gdn, ctx->aux, ctx->aux, nullptr, ctx->routed);
   if (e != hipSuccess) return dev_fail(e, "natsl_forward/gdn");
-  e = do_softmax(dims, a->q, a->k, a->v, w.sel, w.nsb, o_sm, a->branch_dtype, nullptr, stream);
+  e = do_softmax(dims, a->q, a->k, a->v, w.sel, w.nsb, o_sm, a->branch_dtype, nullptr, stream, pre);
   if (e != hipSuccess) return dev_fail(e, "natsl_forward/softmax");
   if ((e = hipEventRecord(ctx->join, ctx->aux)) != hipSuccess) return dev_fail(e, "hipEventRecord");
   if ((e = hipStreamWaitEvent(stream, ctx->join, 0)) != hipSuccess) return dev_fail(e, "hipStreamWaitEvent");
@@ -508,8 +527,8 @@ natsl_status natsl_decode_step(const natsl_dims* dims, const natsl_decode_cache*
 }
 
 natsl_status natsl_decode_handoff(const natsl_dims* dims, const int32_t* route, const void* k, const void* v,
-                                  const float* S_final, const natsl_decode_cache* c, void* ws, size_t ws_bytes,
-                                  hipStream_t stream) {
+                                  const float* S_final, int append, const natsl_decode_cache* c, void* ws,
+                                  size_t ws_bytes, hipStream_t stream) {
   CHECK(check_dims(dims, true, true));
   if (dims->B == 0) return ok();  // empty batch: nothing to do, pointers may be NULL
   NEED(route, "route");
@@ -525,8 +544,11 @@ natsl_status natsl_decode_handoff(const natsl_dims* dims, const int32_t* route, 
   NEED(c->x_sum, "x_sum");
   NEED(c->err_flag, "err_flag");
   if (c->cap < 1) return fail(NATSL_ERR_INVALID_ARG, "cache capacity %d", c->cap);
+  if (append != 0 && append != 1) return fail(NATSL_ERR_INVALID_ARG, "append must be 0 or 1 (got %d)", append);
+  if (append && !S_final) return fail(NATSL_ERR_INVALID_ARG, "appending needs the segment's S_final");
   CHECK(check_ws(ws, ws_bytes, handoff_ws_bytes(dims->B, dims->route_groups, nchunks(dims))));
   HandoffLaunch L;
+  L.append = append;
   L.B = dims->B;
   L.H = dims->H;
   L.G = dims->route_groups;

@@ -35,10 +35,18 @@ hipError_t launch_merge(const Tq* q, const Tb* o_sm, const Tb* o_gdn, const floa
                         const float* g_sm, const float* g_lin, Tq* out, int B, int H, int L,
                         float eps, hipStream_t st);
 
+// cached softmax rows a prefill segment also attends to (chunked prefill):
+// n_committed[b, g] rows (a multiple of 64) of k, v [B, H, cap, D]
+struct SmPrefix {
+  const void* k = nullptr;
+  const void* v = nullptr;
+  const int32_t* n_committed = nullptr;
+  int cap = 0;
+};
 template <typename T, typename To, int D>
 hipError_t launch_softmax_masked(const T* q, const T* k, const T* v, const int32_t* sel_idx,
                                  const int32_t* nsel_before, To* o_sm, float* lse, int B, int H,
-                                 int L, int G, float scale, hipStream_t st);
+                                 int L, int G, float scale, hipStream_t st, const SmPrefix& pre = SmPrefix());
 
 size_t gdn_ws_bytes(int io_is_bf16, int D, int64_t nch);
 template <typename T, typename To, int D>
@@ -64,7 +72,7 @@ size_t decode_ws_bytes(int B, int H, int G, int D, int cap);
 
 // prefill -> decode handoff
 struct HandoffLaunch {
-  int B, H, G, L, D, d, cap;
+  int B, H, G, L, D, d, cap, append;
   const int32_t* route;
   const void *k, *v;
   const float* S_final;

@@ -133,7 +133,8 @@ __global__ void __launch_bounds__(256, 2)
     k_softmax_masked(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                      const int32_t* __restrict__ sel_idx, const int32_t* __restrict__ nsel_before,
                      To* __restrict__ o_sm, float* __restrict__ lse, int H, int L, int G,
-                     float scale_log2) {
+                     float scale_log2, const T* __restrict__ pre_k, const T* __restrict__ pre_v,
+                     const int32_t* __restrict__ pnc, int pcap) {
   using C = SmCfg<T, D>;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   T* smem = reinterpret_cast<T*>(smem_raw);
@@ -157,8 +158,13 @@ __global__ void __launch_bounds__(256, 2)
   const int32_t* nsbp = nsel_before + ((int64_t)b * G + grp) * (nc + 1);
   const int c0 = 2 * qblk, c1 = c0 + 1;
   const bool has_c1 = c1 < nc;
-  const int nsb = nsbp[c0];
-  const bool c0_sm = nsbp[c0 + 1] > nsb;
+  // key tiles: the prefix cache's rows (npre tiles), the softmax chunks
+  // before c0, c0, c1
+  // (rows of a cache that overflowed were never written: at most cap rows)
+  const int npre = pnc ? min(pnc[(int64_t)b * G + grp], pcap) / CHUNK : 0;
+  const int nsel = nsbp[c0];
+  const int nsb = npre + nsel;
+  const bool c0_sm = nsbp[c0 + 1] > nsel;
   const int ntiles = nsb + 1 + (has_c1 ? 1 : 0);
 
   const int lane = lane_id(), w = wave_id();
@@ -189,23 +195,26 @@ __global__ void __launch_bounds__(256, 2)
   float m_run[2] = {-INFINITY, -INFINITY};
   float l_run[2] = {0.f, 0.f};
 
-  auto tile_chunk = [&](int it) -> int { return it < nsb ? sel[it] : (it == nsb ? c0 : c1); };
+  const int64_t pre_off = (int64_t)bh * pcap * D;
+  auto tile_load = [&](TileRegs<T, D>& r, int it) {
+    if (it < npre) {
+      tile_gload<T, D>(r, pre_k + pre_off + (int64_t)it * CHUNK * D, pre_v + pre_off + (int64_t)it * CHUNK * D);
+    } else {
+      const int j = it - npre;
+      const int kc = j < nsel ? sel[j] : (j == nsel ? c0 : c1);
+      tile_gload<T, D>(r, kh + (int64_t)kc * CHUNK * D, vh + (int64_t)kc * CHUNK * D);
+    }
+  };
 
   TileRegs<T, D> pre;
-  {
-    const int kc = tile_chunk(0);
-    tile_gload<T, D>(pre, kh + (int64_t)kc * CHUNK * D, vh + (int64_t)kc * CHUNK * D);
-    tile_sstore<T, D>(pre, smem);
-  }
+  tile_load(pre, 0);
+  tile_sstore<T, D>(pre, smem);
   __syncthreads();
 
   const int qrow_base = 32 * (w & 1);  // query row inside its own chunk, minus 16qs + c
   for (int it = 0; it < ntiles; ++it) {
     const bool more = it + 1 < ntiles;
-    if (more) {
-      const int kc = tile_chunk(it + 1);
-      tile_gload<T, D>(pre, kh + (int64_t)kc * CHUNK * D, vh + (int64_t)kc * CHUNK * D);
-    }
+    if (more) tile_load(pre, it + 1);
     int mode;
     if (it < nsb) mode = MODE_FULL;
     else if (it == nsb) mode = my_c1 ? (c0_sm ? MODE_FULL : MODE_SKIP) : MODE_DIAG;
@@ -344,7 +353,9 @@ template <typename To>
 __global__ void __launch_bounds__(512, 1)
     k_softmax_v2(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
                  const int32_t* __restrict__ sel_idx, const int32_t* __restrict__ nsel_before,
-                 To* __restrict__ o_sm, float* __restrict__ lse, int H, int L, int G, float scale_log2) {
+                 To* __restrict__ o_sm, float* __restrict__ lse, int H, int L, int G, float scale_log2,
+                 const bf16* __restrict__ pre_k, const bf16* __restrict__ pre_v, const int32_t* __restrict__ pnc,
+                 int pcap) {
   constexpr int D = 128;
   extern __shared__ __align__(16) unsigned char lds[];
   int32_t* sel_l = reinterpret_cast<int32_t*>(lds + SM2_STAGES * SM2_TILE_BYTES);
@@ -368,7 +379,12 @@ __global__ void __launch_bounds__(512, 1)
   const int32_t* nsbp = nsel_before + ((int64_t)b * G + grp) * (nc + 1);
   const int c0 = 4 * qblk;
   const int nown = min(4, nc - c0);
-  const int nsb = nsbp[c0];
+  // key tiles: the prefix cache's rows (npre tiles), the softmax chunks
+  // before c0, then the block's own chunks
+  // (rows of a cache that overflowed were never written: at most cap rows)
+  const int npre = pnc ? min(pnc[(int64_t)b * G + grp], pcap) / CHUNK : 0;
+  const int nsel = nsbp[c0];
+  const int nsb = npre + nsel;
   const int ntiles = nsb + nown;
   int sm_bits = 0;
   for (int j = 0; j < nown; ++j) sm_bits |= (nsbp[c0 + j + 1] > nsbp[c0 + j]) ? (1 << j) : 0;
@@ -381,9 +397,12 @@ __global__ void __launch_bounds__(512, 1)
   const bf16* kh = k + head_off;
   const bf16* vh = v + head_off;
 
-  // tile list in LDS (keeps its reads out of the vector-memory counter)
-  for (int i = tid_x(); i < nsb; i += 512) sel_l[i] = sel[i];
+  // tile list in LDS (keeps its reads out of the vector-memory counter):
+  // prefix tile j is stored as -1 - j
+  for (int i = tid_x(); i < npre; i += 512) sel_l[i] = -1 - i;
+  for (int i = tid_x(); i < nsel; i += 512) sel_l[npre + i] = sel[i];
   for (int i = tid_x(); i < nown; i += 512) sel_l[nsb + i] = c0 + i;
+  const int64_t pre_off = (int64_t)bh * pcap * D;
 
   Frag<bf16> qf[2][4];
   const int qtok0 = (c0 + (active ? mch : 0)) * CHUNK + 32 * (w & 1);
@@ -398,8 +417,8 @@ __global__ void __launch_bounds__(512, 1)
   auto issue = [&](int it) {
     const int kc = sel_l[it];
     unsigned char* st = lds + (it % SM2_STAGES) * SM2_TILE_BYTES;
-    const bf16* kg = kh + (int64_t)kc * CHUNK * D;
-    const bf16* vg = vh + (int64_t)kc * CHUNK * D;
+    const bf16* kg = kc >= 0 ? kh + (int64_t)kc * CHUNK * D : pre_k + pre_off + (int64_t)(-1 - kc) * CHUNK * D;
+    const bf16* vg = kc >= 0 ? vh + (int64_t)kc * CHUNK * D : pre_v + pre_off + (int64_t)(-1 - kc) * CHUNK * D;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int e0 = w * 128 + i * 64;  // first 16-byte chunk of this wave instruction
@@ -574,7 +593,7 @@ __global__ void __launch_bounds__(512, 1)
 template <typename T, typename To, int D>
 hipError_t launch_softmax_masked(const T* q, const T* k, const T* v, const int32_t* sel_idx,
                                  const int32_t* nsel_before, To* o_sm, float* lse, int B, int H,
-                                 int L, int G, float scale, hipStream_t st) {
+                                 int L, int G, float scale, hipStream_t st, const SmPrefix& pre) {
   using C = SmCfg<T, D>;
   if constexpr (sizeof(T) == 2 && D == 128) {
     static bool attr2 = false;
@@ -585,10 +604,12 @@ hipError_t launch_softmax_masked(const T* q, const T* k, const T* v, const int32
       attr2 = true;
     }
     const int nc = L / CHUNK;
-    if (nc <= 1024) {
+    // the tile list (prefix tiles + chunks) lives in a 1024-entry LDS array
+    if (nc + (pre.n_committed ? pre.cap / CHUNK : 0) <= 1024) {
       const int64_t grid = (int64_t)B * H * ((nc + 3) / 4);
       hipLaunchKernelGGL(k_softmax_v2<To>, dim3((unsigned)grid), dim3(512), SM2_LDS, st, (const bf16*)q,
-                         (const bf16*)k, (const bf16*)v, sel_idx, nsel_before, o_sm, lse, H, L, G, scale * LOG2E);
+                         (const bf16*)k, (const bf16*)v, sel_idx, nsel_before, o_sm, lse, H, L, G, scale * LOG2E,
+                         (const bf16*)pre.k, (const bf16*)pre.v, pre.n_committed, pre.cap);
       return hipGetLastError();
     }
   }
@@ -603,7 +624,8 @@ hipError_t launch_softmax_masked(const T* q, const T* k, const T* v, const int32
   const int nb = (nc + 1) / 2;
   const int64_t grid = (int64_t)B * H * nb;
   hipLaunchKernelGGL((k_softmax_masked<T, To, D>), dim3((unsigned)grid), dim3(256), C::LDS_BYTES,
-                     st, q, k, v, sel_idx, nsel_before, o_sm, lse, H, L, G, scale * LOG2E);
+                     st, q, k, v, sel_idx, nsel_before, o_sm, lse, H, L, G, scale * LOG2E, (const T*)pre.k,
+                     (const T*)pre.v, pre.n_committed, pre.cap);
   return hipGetLastError();
 }
 
@@ -611,7 +633,7 @@ hipError_t launch_softmax_masked(const T* q, const T* k, const T* v, const int32
   template hipError_t launch_softmax_masked<T, To, D>(const T*, const T*, const T*,            \
                                                       const int32_t*, const int32_t*, To*,     \
                                                       float*, int, int, int, int, float,       \
-                                                      hipStream_t);
+                                                      hipStream_t, const SmPrefix&);
 INST(float, float, 64)
 INST(float, float, 128)
 INST(float, bf16, 64)

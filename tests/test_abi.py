@@ -161,8 +161,8 @@ def test_decode_handoff_validation(L):
     c.cap = 1024
     need = N.workspace_size(N.ENTRY_DECODE_HANDOFF, d)
     assert need == d.B * d.route_groups * (2 * (d.L // 64) + 1) * 4
-    call = lambda dd, route, cc, ws, nbytes: L.natsl_decode_handoff(C.byref(dd), route, FAKE, FAKE, None, C.byref(cc),
-                                                                    ws, nbytes, None)
+    call = lambda dd, route, cc, ws, nbytes, append=0, S=None: L.natsl_decode_handoff(
+        C.byref(dd), route, FAKE, FAKE, S, append, C.byref(cc), ws, nbytes, None)
     assert call(d, None, c, FAKE, need) == 1             # route missing
     assert call(d, FAKE, c, FAKE, need - 4) == 3         # workspace too small
     bad = good()
@@ -175,6 +175,28 @@ def test_decode_handoff_validation(L):
     empty = good()
     empty.B = 0
     assert call(empty, None, N.DecodeCache(), None, 0) == 0  # empty batch is a no-op
+    c.cap = 1024
+    assert call(d, FAKE, c, FAKE, need, append=1) == 1   # appending needs S_final
+    assert call(d, FAKE, c, FAKE, need, append=2, S=FAKE) == 1  # append is 0 or 1
+
+
+def test_forward_prefix_validation(L):
+    d = good()
+    a = N.ForwardArgs()
+    for f in ("x", "q", "k", "v", "alpha", "beta", "w_score", "w_mix", "out"):
+        setattr(a, f, FAKE)
+    c = N.DecodeCache()
+    a.prefix = C.cast(C.pointer(c), C.c_void_p)
+    need = N.workspace_size(N.ENTRY_FORWARD, d)
+    assert L.natsl_forward(C.byref(d), C.byref(a), FAKE, need, None) == 1      # prefix tensors missing
+    for f in ("k_cache", "v_cache", "n_committed", "n_open", "S_carry", "S_work", "x_sum", "err_flag"):
+        setattr(c, f, FAKE)
+    c.cap = -1
+    assert L.natsl_forward(C.byref(d), C.byref(a), FAKE, need, None) == 1      # bad capacity
+    c.cap = 1024
+    a.S_init = FAKE
+    assert L.natsl_forward(C.byref(d), C.byref(a), FAKE, need, None) == 1      # S_init with a prefix
+    assert b"exclusive" in L.natsl_last_error()
 
 
 def test_workspace_sizes_monotone(L):

@@ -482,6 +482,65 @@ def test_decode_groups_per_head_mix():
     assert maxerr(host(st.S_carry), cache["S_carry"]) <= 1e-4
 
 
+@pytest.mark.parametrize("io,D,per_head", [("f32", 64, False), ("bf16", 128, False), ("bf16", 128, True)])
+def test_chunked_prefill_equals_one_shot(io, D, per_head):
+    """Chunked prefill: forward over the first 320 tokens, handoff, forward
+    over the remaining 256 tokens on top of that cache (prefix), handoff with
+    append.  The queries see the same keys in the same chunk order and the
+    state is carried exactly, so the second segment's outputs, routes and
+    final state, and the final cache, are bit-identical to one prefill over
+    all 576 tokens and its handoff (and the outputs match the oracle)."""
+    B, H, L, L1 = 2, 4, 576, 320
+    G = H if per_head else 1
+    wl, inp = small_case(io, B=B, H=H, L=L, D=D, seed=73, sm_frac=0.5)
+    d = wl.d
+    say(f"[chunked prefill] io={io} D={D} G={G}")
+    r = None
+    if per_head:
+        rng = np.random.default_rng(73)
+        r = (rng.random((B, G, L // 64)) < 0.5).astype(np.int32)
+    seg = lambda a, lo, hi: {k: ((val[:, lo:hi] if k == "x" else val[:, :, lo:hi])
+                                 if k in ("x", "q", "k", "v", "alpha", "beta") else val) for k, val in a.items()}
+    s1, s2 = seg(inp, 0, L1), seg(inp, L1, L)
+    cap = L + 64
+    io_t = torch.bfloat16 if io == "bf16" else torch.float32
+    full = run_forward(inp, d, B, H, L, D, route_override=r, groups=G)
+    st_full = N.DecodeState(B, H, D, d, cap, groups=G, io=io_t)
+    t_full = prefill_tensors(inp)
+    N.decode_handoff(N.dims(B, H, L, D, d, io_code(inp), groups=G), full.route, t_full["k"], t_full["v"],
+                     full.S_final, st_full)
+    f1 = run_forward(s1, d, B, H, L1, D, route_override=None if r is None else r[:, :, :L1 // 64], groups=G)
+    st = N.DecodeState(B, H, D, d, cap, groups=G, io=io_t)
+    t1 = prefill_tensors(s1)
+    N.decode_handoff(N.dims(B, H, L1, D, d, io_code(inp), groups=G), f1.route, t1["k"], t1["v"], f1.S_final, st)
+    dm2 = N.dims(B, H, L - L1, D, d, io_code(inp), groups=G)
+    f2 = N.Forward(dm2, debug=True, want_state=True)
+    t2 = prefill_tensors(s2)
+    ro2 = None if r is None else dev(np.ascontiguousarray(r[:, :, L1 // 64:]))
+    f2(t2["x"] if r is None else None, t2["q"], t2["k"], t2["v"], t2["alpha"], t2["beta"],
+       t2["w_score"] if r is None else None, t2["w_mix"], b_score=t2["b_score"] if r is None else None,
+       g_sm=t2["g_sm"], g_lin=t2["g_lin"], route_override=ro2, prefix=st)
+    N.decode_handoff(dm2, f2.route, t2["k"], t2["v"], f2.S_final, st, append=True)
+    torch.cuda.synchronize()
+    assert torch.equal(f2.route, full.route[:, :, L1 // 64:])
+    assert torch.equal(f2.out, full.out[:, :, L1:]), "segment outputs differ from the one-shot prefill"
+    assert torch.equal(f2.S_final, full.S_final)
+    assert torch.equal(st.n_committed, st_full.n_committed)
+    assert int(st.err.item()) == 0 and int(st_full.err.item()) == 0
+    assert not st.n_open.any() and torch.equal(st.S_carry, st_full.S_carry)
+    nco = st.n_committed.cpu().numpy()
+    for b in range(B):
+        for h in range(H):
+            n = int(nco[b, h if G > 1 else 0])
+            assert torch.equal(st.k[b, h, :n], st_full.k[b, h, :n]) and torch.equal(st.v[b, h, :n], st_full.v[b, h, :n])
+    if not per_head:
+        ref = O.forward(inp["x"], inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["w_score"],
+                        inp["w_mix"], inp["b_score"], inp["g_sm"], inp["g_lin"])
+        e = maxerr(host(f2.out), ref["out"][:, :, L1:])
+        say(f"  segment out err vs oracle {e:.3e}")
+        assert e <= (TOL_F32 if io == "f32" else TOL_BF16)
+
+
 def test_decode_full_sampled():
     """The decode workload at full size (B=64, ~8192 cached rows per head),
     one step; sampled sequences against the oracle."""
