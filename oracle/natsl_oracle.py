@@ -1,4 +1,5 @@
-"""fp64 CPU oracle for the NAtS-L hybrid attention layer (forward and decode step).
+"""fp64 CPU oracle for the NAtS-L hybrid attention layer (forward, decode step,
+and the gradient of the softmax branch).
 
 TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import this module:
 only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg use it.
@@ -199,6 +200,43 @@ def softmax_branch_bruteforce(q, k, v, route_bgc, scale=None, chunk=CHUNK):
                 p /= p.sum()
                 o[b, h, t] = sum(pi * v[b, h, s] for pi, s in zip(p, keys))
     return o
+
+
+def softmax_branch_backward(q, k, v, route_bgc, d_o, scale=None, chunk=CHUNK):
+    """Gradient of the softmax branch (softmax_branch above) for an upstream
+    gradient d_o [B,H,L,Dv]: returns dq, dk, dv.  The pages define only the
+    forward; this is its exact derivative, taken one 64-row query block at a
+    time with the block's visible keys (block_mask):
+        p  = softmax over the visible keys of scale * q k^T
+        o  = p v
+        dp = d_o v^T,  delta = rowsum(d_o * o),  ds = p * (dp - delta)
+        dq = scale * ds k,   dk += scale * ds^T q,   dv += p^T d_o
+    (masked keys have p = 0 and receive nothing)."""
+    q, k, v, d_o = _f64(q), _f64(k), _f64(v), _f64(d_o)
+    B, H, L, Dk = q.shape
+    G = route_bgc.shape[1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(Dk)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for b in range(B):
+        for g in range(G):
+            heads = [h for h in range(H) if group_of_head(h, H, G) == g]
+            for t0 in range(0, L, chunk):
+                t1 = min(L, t0 + chunk)
+                m = block_mask(route_bgc[b, g], t0, t1, chunk)
+                z = scale * np.einsum("hqd,hkd->hqk", q[b, heads, t0:t1], k[b, heads, :t1])
+                z = np.where(m[None], z, -np.inf)
+                p = np.exp(z - z.max(axis=-1, keepdims=True))
+                p /= p.sum(axis=-1, keepdims=True)
+                o = np.einsum("hqk,hkd->hqd", p, v[b, heads, :t1])
+                g_o = d_o[b, heads, t0:t1]
+                dp = np.einsum("hqd,hkd->hqk", g_o, v[b, heads, :t1])
+                delta = np.sum(g_o * o, axis=-1, keepdims=True)
+                ds = p * (dp - delta)
+                dq[b, heads, t0:t1] = scale * np.einsum("hqk,hkd->hqd", ds, k[b, heads, :t1])
+                dk[b, heads, :t1] += scale * np.einsum("hqk,hqd->hkd", ds, q[b, heads, t0:t1])
+                dv[b, heads, :t1] += np.einsum("hqk,hqd->hkd", p, g_o)
+    return dq, dk, dv
 
 
 # ---------------------------------------------------------------------------

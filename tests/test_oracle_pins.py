@@ -384,3 +384,73 @@ def test_decode_capacity_flag():
     _, _, c2 = O.decode_step(cache, *args, np.full((B, H), 0.9), np.full((B, H), 0.5),
                              RNG.standard_normal((d, 2)), np.zeros((D, 2)))
     assert c2["err"] == 1
+
+
+# ------------------------------------------------- softmax branch gradient ----
+def _sm_loss(q, k, v, r, d_o):
+    return float(np.sum(d_o * O.softmax_branch(q, k, v, r)))
+
+
+def test_softmax_backward_finite_differences():
+    """Central differences of <d_o, softmax_branch(q, k, v)> on a 3-chunk case
+    whose middle chunk is linear (the last chunk's queries skip it): catches a
+    dropped delta term, a transposed product, or a gradient leaking into
+    masked keys."""
+    _, q, k, v, _, _ = rand_inputs(B=1, H=2, L=192, D=4, seed=21)
+    r = np.array([[[O.SM, O.LIN, O.SM]]])
+    d_o = np.random.default_rng(22).standard_normal(v.shape)
+    dq, dk, dv = O.softmax_branch_backward(q, k, v, r, d_o)
+    rng = np.random.default_rng(23)
+    eps = 1e-6
+    for name, arr, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        for _ in range(12):
+            idx = tuple(rng.integers(0, s) for s in arr.shape)
+            args = {"q": q, "k": k, "v": v}
+            plus, minus = {n: a.copy() for n, a in args.items()}, {n: a.copy() for n, a in args.items()}
+            plus[name][idx] += eps
+            minus[name][idx] -= eps
+            fd = (_sm_loss(plus["q"], plus["k"], plus["v"], r, d_o) -
+                  _sm_loss(minus["q"], minus["k"], minus["v"], r, d_o)) / (2 * eps)
+            assert abs(fd - grad[idx]) <= 1e-7 * max(1.0, abs(fd)), (name, idx, fd, grad[idx])
+    # the keys of the linear chunk get a gradient only from their own chunk's
+    # queries: zeroing the later queries' upstream gradient leaves it unchanged
+    d_o2 = d_o.copy()
+    d_o2[:, :, 128:] = 0.0
+    _, dk2, dv2 = O.softmax_branch_backward(q, k, v, r, d_o2)
+    np.testing.assert_allclose(dk2[:, :, 64:128], dk[:, :, 64:128], atol=1e-14)
+    np.testing.assert_allclose(dv2[:, :, 64:128], dv[:, :, 64:128], atol=1e-14)
+
+
+def _sdpa_grads(q, k, v, d_o):
+    """dq, dk, dv of torch's fp64 causal scaled_dot_product_attention
+    (library routine and autograd)."""
+    t = [torch.from_numpy(np.ascontiguousarray(a)).requires_grad_(True) for a in (q, k, v)]
+    out = torch.nn.functional.scaled_dot_product_attention(*t, is_causal=True)
+    return [g.numpy() for g in torch.autograd.grad(out, t, torch.from_numpy(d_o))]
+
+
+def test_softmax_backward_all_softmax_is_causal_attention():
+    """Every chunk softmax-routed: the branch is plain causal attention, so its
+    gradient is torch's autograd of causal attention.  Catches a wrong scale
+    placement or a causal-mask off-by-one in the gradient."""
+    _, q, k, v, _, _ = rand_inputs(B=2, H=2, L=192, D=8, seed=31)
+    d_o = np.random.default_rng(32).standard_normal(v.shape)
+    r = np.zeros((2, 1, 3), np.int32)
+    got = O.softmax_branch_backward(q, k, v, r, d_o)
+    for g, ref in zip(got, _sdpa_grads(q, k, v, d_o)):
+        np.testing.assert_allclose(g, ref, atol=1e-10)
+
+
+def test_softmax_backward_all_linear_is_per_chunk_attention():
+    """Every chunk linear-routed: each chunk attends causally to itself only,
+    so the gradient is chunk-by-chunk causal attention's.  Catches gradient
+    flowing across chunk boundaries."""
+    _, q, k, v, _, _ = rand_inputs(B=1, H=2, L=192, D=8, seed=41)
+    d_o = np.random.default_rng(42).standard_normal(v.shape)
+    r = np.ones((1, 1, 3), np.int32)
+    got = O.softmax_branch_backward(q, k, v, r, d_o)
+    for c in range(3):
+        sl = slice(64 * c, 64 * (c + 1))
+        ref = _sdpa_grads(q[:, :, sl], k[:, :, sl], v[:, :, sl], d_o[:, :, sl])
+        for g, rf in zip(got, ref):
+            np.testing.assert_allclose(g[:, :, sl], rf, atol=1e-10)
