@@ -146,6 +146,31 @@ def time_handoff(N, dm, route, t, wl, reps=20):
                 frac_hbm=round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4))
 
 
+def time_softmax_backward(N, dm, t, wl, pairs, reps=3):
+    """Gradient of the softmax branch on this workload (dq, dk, dv from the
+    forward's o and lse and a random upstream gradient), timed with events;
+    algorithmic work 10 D FLOP per visible pair (recomputed scores, dP, dQ,
+    dK, dV; the kernels recompute scores and dP twice, 14 D)."""
+    import torch
+    _, sel, nsb, _ = N.route(dm, t["x"], t["w_score"], t["b_score"])
+    o, lse = N.softmax_masked(dm, t["q"], t["k"], t["v"], sel, nsb, o_dtype=t["q"].dtype, want_lse=True)
+    d_o = torch.randn_like(t["q"])
+    for _ in range(2):
+        N.softmax_masked_backward(dm, t["q"], t["k"], t["v"], sel, nsb, o, lse, d_o)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        N.softmax_masked_backward(dm, t["q"], t["k"], t["v"], sel, nsb, o, lse, d_o)
+    e1.record()
+    torch.cuda.synchronize()
+    us = 1000.0 * e0.elapsed_time(e1) / reps
+    flops = 10 * wl.D * pairs
+    tf = flops / (us * 1e-6) / 1e12
+    return dict(workload=f"gradient of the softmax branch on the {wl.name} prefill", us=round(us, 1),
+                flops=flops, tflops=round(tf, 1), frac_mfma=round(tf / PEAK_BF16_TFLOPS, 4))
+
+
 def time_prefill(args, N, W, O):
     import torch
     wl = W.WORKLOADS[args.workload]
@@ -179,6 +204,7 @@ def time_prefill(args, N, W, O):
                            max(5, args.steps // 5))
     N.profile_enable(False)
     handoff = time_handoff(N, dm, fwd.route, t, wl)
+    backward = time_softmax_backward(N, dm, t, wl, sm_pairs(fwd.route.cpu().numpy(), wl.H))
     route = fwd.route.cpu().numpy()
     ref_route = O.route(inp["x"], inp["w_score"], inp["b_score"])[0] if args.check_route else None
     pairs = sm_pairs(route, wl.H)
@@ -209,6 +235,7 @@ def time_prefill(args, N, W, O):
                    layer_frac_of_mfma_peak=round((f_sm + f_gdn) / (dt / args.steps) / 1e12 / PEAK_BF16_TFLOPS, 4),
                    kernels=kernels),
         handoff=handoff,
+        softmax_backward=backward,
     )
     return res, inp, route
 

@@ -70,7 +70,8 @@ enum {
   NATSL_ENTRY_MERGE = 3,
   NATSL_ENTRY_FORWARD = 4,
   NATSL_ENTRY_DECODE_STEP = 5,
-  NATSL_ENTRY_DECODE_HANDOFF = 6
+  NATSL_ENTRY_DECODE_HANDOFF = 6,
+  NATSL_ENTRY_SOFTMAX_BACKWARD = 7
 };
 
 typedef struct {
@@ -150,6 +151,27 @@ natsl_status natsl_softmax_masked(const natsl_dims* dims, const void* q, const v
                                   const void* v, const int32_t* sel_idx,
                                   const int32_t* nsel_before, void* o_sm, natsl_dtype o_dtype,
                                   float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Gradient of the softmax branch (the pages define the forward,
+ * Kernmechanismen 3; this is its exact derivative).  For the keys each query
+ * sees in natsl_softmax_masked, with p = exp(scale q.k - lse) and
+ * delta = rowsum(d_o * o_sm):
+ *   dq = scale sum_k p (d_o.v_k - delta) k,   dk = scale sum_q p (d_o.v - delta) q,
+ *   dv = sum_q p d_o.
+ *   q, k, v        [B, H, L, Dk] io dtype (the forward's inputs)
+ *   sel_idx, nsel_before  the forward's compaction (natsl_route)
+ *   o_sm           [B, H, L, Dv] io dtype: the forward's softmax branch output
+ *   lse            [B, H, L] fp32: the forward's natural-log logsumexp of the
+ *                  scaled scores (natsl_softmax_masked with lse)
+ *   d_o            [B, H, L, Dv] io dtype: gradient of the loss w.r.t. o_sm
+ *   dq, dk, dv     [B, H, L, D] fp32 outputs (written, not accumulated)
+ *   ws             workspace of natsl_workspace_size(NATSL_ENTRY_SOFTMAX_BACKWARD)
+ */
+natsl_status natsl_softmax_masked_backward(const natsl_dims* dims, const void* q, const void* k, const void* v,
+                                           const int32_t* sel_idx, const int32_t* nsel_before, const void* o_sm,
+                                           const float* lse, const void* d_o, float* dq, float* dk, float* dv,
+                                           void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Output merging (Kernmechanismen 4): per (b, h, t)
@@ -302,7 +324,8 @@ natsl_status natsl_decode_handoff(const natsl_dims* dims, const int32_t* route, 
  * named `name`, the number of recorded launches and their summed duration
  * in milliseconds since the last reset.  Names: "route", "compact",
  * "gdn_prep", "gdn_scan", "softmax_masked", "merge", "decode_route",
- * "decode_gdn", "decode_attn", "decode_combine", "decode_commit".
+ * "decode_gdn", "decode_attn", "decode_combine", "decode_commit",
+ * "softmax_backward", "decode_handoff" (each a whole call of that entry).
  * natsl_profile_select restricts the recording to the kernel named `name`
  * (NULL or "" records every kernel again), so that timing one kernel adds
  * only its own two event records to a step; an unknown name is

@@ -20,12 +20,12 @@ LIB_PATH = os.path.join(HERE, "libnatsl.so")
 F32, BF16 = 0, 1
 ROUTE_SOFTMAX, ROUTE_LINEAR = 0, 1
 ENTRY_ROUTE, ENTRY_GDN_CHUNK, ENTRY_SOFTMAX_MASKED, ENTRY_MERGE, ENTRY_FORWARD, ENTRY_DECODE_STEP, \
-    ENTRY_DECODE_HANDOFF = range(7)
+    ENTRY_DECODE_HANDOFF, ENTRY_SOFTMAX_BACKWARD = range(8)
 STATUS = {0: "NATSL_OK", 1: "NATSL_ERR_INVALID_ARG", 2: "NATSL_ERR_UNSUPPORTED",
           3: "NATSL_ERR_WORKSPACE", 4: "NATSL_ERR_DEVICE", 5: "NATSL_ERR_CAPACITY"}
 EXPORTS = ["natsl_version", "natsl_last_error", "natsl_workspace_size", "natsl_route", "natsl_gdn_chunk",
            "natsl_softmax_masked", "natsl_merge", "natsl_forward", "natsl_decode_step",
-           "natsl_decode_handoff", "natsl_profile_enable", "natsl_profile_reset", "natsl_profile_read",
+           "natsl_decode_handoff", "natsl_softmax_masked_backward", "natsl_profile_enable", "natsl_profile_reset", "natsl_profile_read",
            "natsl_profile_select"]
 
 
@@ -89,11 +89,13 @@ def lib():
                                         C.c_size_t, vp]
         L.natsl_decode_handoff.argtypes = [C.POINTER(Dims), vp, vp, vp, vp, C.c_int, C.POINTER(DecodeCache), vp,
                                            C.c_size_t, vp]
+        L.natsl_softmax_masked_backward.argtypes = [C.POINTER(Dims)] + [vp] * 12 + [C.c_size_t, vp]
         L.natsl_profile_enable.argtypes = [C.c_int]
         L.natsl_profile_read.argtypes = [C.c_char_p, C.POINTER(C.c_int), C.POINTER(C.c_double)]
         L.natsl_profile_select.argtypes = [C.c_char_p]
         for name in ("natsl_workspace_size", "natsl_route", "natsl_gdn_chunk", "natsl_softmax_masked",
                      "natsl_merge", "natsl_forward", "natsl_decode_step", "natsl_decode_handoff",
+                     "natsl_softmax_masked_backward",
                      "natsl_profile_enable",
                      "natsl_profile_reset", "natsl_profile_read", "natsl_profile_select"):
             getattr(L, name).restype = st
@@ -357,6 +359,24 @@ def decode_step(dm: Dims, state: DecodeState, *args, debug=False, **kw):
     d = Decode(dm, state, device=args[1].device, debug=debug)
     d(*args, **kw)
     return d
+
+
+def softmax_masked_backward(dm: Dims, q, k, v, sel_idx, nsel_before, o_sm, lse, d_o, stream=None):
+    """Gradient of the softmax branch: returns fp32 (dq, dk, dv).  o_sm and lse
+    are the forward's outputs (softmax_masked(..., o_dtype=io, want_lse=True)),
+    d_o the upstream gradient, both in the io dtype."""
+    io, qs, nc = _io_t(dm), (dm.B, dm.H, dm.L, dm.Dk), dm.L // 64
+    dq = torch.empty(qs, dtype=torch.float32, device=q.device)
+    dk, dv = torch.empty_like(dq), torch.empty_like(dq)
+    ws_bytes = workspace_size(ENTRY_SOFTMAX_BACKWARD, dm)
+    ws = workspace(ws_bytes, q.device)
+    _check(lib().natsl_softmax_masked_backward(
+        C.byref(dm), _p(q, io, "q", qs), _p(k, io, "k", qs), _p(v, io, "v", qs),
+        _p(sel_idx, torch.int32, "sel_idx", (dm.B, dm.route_groups, nc)),
+        _p(nsel_before, torch.int32, "nsel_before", (dm.B, dm.route_groups, nc + 1)),
+        _p(o_sm, io, "o_sm", qs), _p(lse, torch.float32, "lse", qs[:3]), _p(d_o, io, "d_o", qs),
+        _p(dq), _p(dk), _p(dv), _p(ws), ws_bytes, _stream(stream)))
+    return dq, dk, dv
 
 
 def decode_handoff(dm: Dims, route, k, v, S_final, state: DecodeState, append=False, stream=None):

@@ -43,7 +43,7 @@ size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 // ---------------------------------------------------------------- timing ----
 const char* kKernelNames[KID_COUNT] = {"route",        "compact",       "gdn_prep",   "gdn_scan",
                                        "softmax_masked", "merge",       "decode_route", "decode_gdn",
-                                       "decode_attn",  "decode_combine", "decode_commit"};
+                                       "decode_attn",  "decode_combine", "decode_commit", "softmax_backward", "decode_handoff"};
 struct ProfRec {
   int kid;
   hipEvent_t a, b;
@@ -305,6 +305,10 @@ natsl_status natsl_workspace_size(int entry, const natsl_dims* dims, size_t* byt
       if (dims->L < 1) return fail(NATSL_ERR_INVALID_ARG, "decode: dims->L must hold the cache capacity");
       *bytes = decode_ws_bytes(dims->B, dims->H, dims->route_groups, dims->Dk, dims->L);
       return ok();
+    case NATSL_ENTRY_SOFTMAX_BACKWARD:
+      CHECK(check_dims(dims, true, false));
+      *bytes = sm_bwd_ws_bytes(dims->B, dims->H, dims->L);
+      return ok();
     case NATSL_ENTRY_DECODE_HANDOFF:
       CHECK(check_dims(dims, true, false));
       *bytes = handoff_ws_bytes(dims->B, dims->route_groups, nchunks(dims));
@@ -526,6 +530,50 @@ natsl_status natsl_decode_step(const natsl_dims* dims, const natsl_decode_cache*
   return ok();
 }
 
+natsl_status natsl_softmax_masked_backward(const natsl_dims* dims, const void* q, const void* k, const void* v,
+                                           const int32_t* sel_idx, const int32_t* nsel_before, const void* o_sm,
+                                           const float* lse, const void* d_o, float* dq, float* dk, float* dv,
+                                           void* ws, size_t ws_bytes, hipStream_t stream) {
+  CHECK(check_dims(dims, true, false));
+  if (dims->B == 0) return ok();  // empty batch: nothing to do, pointers may be NULL
+  NEED(q, "q");
+  NEED(k, "k");
+  NEED(v, "v");
+  NEED(sel_idx, "sel_idx");
+  NEED(nsel_before, "nsel_before");
+  NEED(o_sm, "o_sm");
+  NEED(lse, "lse");
+  NEED(d_o, "d_o");
+  NEED(dq, "dq");
+  NEED(dk, "dk");
+  NEED(dv, "dv");
+  CHECK(check_ws(ws, ws_bytes, sm_bwd_ws_bytes(dims->B, dims->H, dims->L)));
+  const float sc = eff_scale(dims);
+  const int B = dims->B, H = dims->H, L = dims->L, G = dims->route_groups;
+  hipError_t e;
+  auto prof = prof_fn();
+  if (prof) prof(KID_SOFTMAX_BWD, stream, 0);
+  if (dims->io == NATSL_BF16)
+    e = dims->Dk == 64
+            ? launch_softmax_backward<bf16, bf16, 64>((const bf16*)q, (const bf16*)k, (const bf16*)v, sel_idx,
+                                                      nsel_before, (const bf16*)o_sm, lse, (const bf16*)d_o, dq, dk,
+                                                      dv, ws, B, H, L, G, sc, stream)
+            : launch_softmax_backward<bf16, bf16, 128>((const bf16*)q, (const bf16*)k, (const bf16*)v, sel_idx,
+                                                       nsel_before, (const bf16*)o_sm, lse, (const bf16*)d_o, dq, dk,
+                                                       dv, ws, B, H, L, G, sc, stream);
+  else
+    e = dims->Dk == 64
+            ? launch_softmax_backward<float, float, 64>((const float*)q, (const float*)k, (const float*)v, sel_idx,
+                                                        nsel_before, (const float*)o_sm, lse, (const float*)d_o, dq,
+                                                        dk, dv, ws, B, H, L, G, sc, stream)
+            : launch_softmax_backward<float, float, 128>((const float*)q, (const float*)k, (const float*)v, sel_idx,
+                                                         nsel_before, (const float*)o_sm, lse, (const float*)d_o, dq,
+                                                         dk, dv, ws, B, H, L, G, sc, stream);
+  if (prof) prof(KID_SOFTMAX_BWD, stream, 1);
+  if (e != hipSuccess) return dev_fail(e, "natsl_softmax_masked_backward");
+  return ok();
+}
+
 natsl_status natsl_decode_handoff(const natsl_dims* dims, const int32_t* route, const void* k, const void* v,
                                   const float* S_final, int append, const natsl_decode_cache* c, void* ws,
                                   size_t ws_bytes, hipStream_t stream) {
@@ -568,7 +616,10 @@ natsl_status natsl_decode_handoff(const natsl_dims* dims, const int32_t* route, 
   L.S_carry = c->S_carry;
   L.S_work = c->S_work;
   L.x_sum = c->x_sum;
+  auto prof = prof_fn();
+  if (prof) prof(KID_HANDOFF, stream, 0);
   const hipError_t e = dims->io == NATSL_BF16 ? launch_handoff<bf16>(L, ws, stream) : launch_handoff<float>(L, ws, stream);
+  if (prof) prof(KID_HANDOFF, stream, 1);
   if (e != hipSuccess) return dev_fail(e, "natsl_decode_handoff");
   return ok();
 }

@@ -21,6 +21,8 @@ enum {
   KID_DECODE_ATTN,
   KID_DECODE_COMBINE,
   KID_DECODE_COMMIT,
+  KID_SOFTMAX_BWD,
+  KID_HANDOFF,
   KID_COUNT
 };
 
@@ -43,6 +45,13 @@ struct SmPrefix {
   const int32_t* n_committed = nullptr;
   int cap = 0;
 };
+// softmax branch gradient: o and d_o in the io dtype (To == T); ws holds delta
+size_t sm_bwd_ws_bytes(int B, int H, int L);
+template <typename T, typename To, int D>
+hipError_t launch_softmax_backward(const T* q, const T* k, const T* v, const int32_t* sel_idx,
+                                   const int32_t* nsel_before, const To* o, const float* lse, const T* d_o,
+                                   float* dq, float* dk, float* dv, void* ws, int B, int H, int L, int G,
+                                   float scale, hipStream_t st);
 template <typename T, typename To, int D>
 hipError_t launch_softmax_masked(const T* q, const T* k, const T* v, const int32_t* sel_idx,
                                  const int32_t* nsel_before, To* o_sm, float* lse, int B, int H,

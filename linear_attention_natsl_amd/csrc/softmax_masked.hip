@@ -644,4 +644,278 @@ INST(bf16, bf16, 64)
 INST(bf16, bf16, 128)
 #undef INST
 
+
+// ---------------------------------------------------------------------------
+// Gradient of the softmax branch.  The pages define the forward only; this is
+// its exact derivative.  With p = exp(scale s - lse) over the visible keys
+// (lse from the forward pass), upstream gradient dO and delta = rowsum(dO * O):
+//   dP = dO V^T,   dS = P * (dP - delta),
+//   dQ = scale dS K,   dK = scale dS^T Q,   dV = P^T dO.
+// Three launches: delta per query; dQ with one workgroup per query chunk (4
+// waves x 16 queries) walking that chunk's visible key tiles (the forward's
+// tile list); dK and dV with one workgroup per key chunk (4 waves x 16 keys)
+// walking the query chunks that see it (every later chunk if the chunk is
+// softmax-routed, else only its own).  Products contracting over d take K, V,
+// Q, dO with 8 contiguous d per lane (row layout); products contracting over
+// tokens take the accumulator-shaped B operand (P^T or dS^T straight from the
+// accumulators) and the other operand in the key-group layout, as in the
+// forward's O^T = V^T P^T.  Gradients are written in fp32.
+
+template <typename To, int D>
+__global__ void __launch_bounds__(256) k_sm_bwd_delta(const To* __restrict__ o, const To* __restrict__ d_o,
+                                                      float* __restrict__ delta, int64_t ntok) {
+  const int64_t t = (int64_t)bid_x() * 256 + tid_x();
+  if (t >= ntok) return;
+  float acc = 0.f;
+#pragma unroll
+  for (int c = 0; c < D; c += 8) {
+    float a[8], b[8];
+    load8f<To>(o + t * D + c, a);
+    load8f<To>(d_o + t * D + c, b);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc = fmaf(a[j], b[j], acc);
+  }
+  delta[t] = acc;
+}
+
+template <typename T, int D>
+__global__ void __launch_bounds__(256) k_sm_bwd_dq(const T* __restrict__ q, const T* __restrict__ k,
+                                                   const T* __restrict__ v, const T* __restrict__ d_o,
+                                                   const int32_t* __restrict__ sel_idx,
+                                                   const int32_t* __restrict__ nsel_before,
+                                                   const float* __restrict__ lse, const float* __restrict__ delta,
+                                                   float* __restrict__ dq, int H, int L, int G, float scale) {
+  using C = SmCfg<T, D>;
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  T* kbuf = reinterpret_cast<T*>(smem_raw);  // K rows, K key groups
+  T* vbuf = kbuf + C::BUF;                   // V rows (its key-group part unused)
+  const int nc = L / CHUNK;
+  const int BH = (int)(grid_dim_x() / nc);
+  const int p = bid_x();
+  const int qc = nc - 1 - p / BH;  // later query chunks see more keys: first
+  const int bh = p % BH;
+  const int b = bh / H, h = bh % H;
+  const int grp = (G == 1) ? 0 : h;
+  const int32_t* sel = sel_idx + ((int64_t)b * G + grp) * nc;
+  const int nsb = nsel_before[((int64_t)b * G + grp) * (nc + 1) + qc];
+  const int lane = lane_id(), w = wave_id();
+  const int g = lane >> 4, c = lane & 15;
+  const int64_t head_off = (int64_t)bh * L * D;
+  const int64_t tok = (int64_t)qc * CHUNK + 16 * w + c;
+  Frag<T> qf[C::KF], df[C::KF];
+#pragma unroll
+  for (int ks = 0; ks < C::KF; ++ks) {
+    qf[ks] = load8<T>(q + head_off + tok * D + 32 * ks + 8 * g);
+    df[ks] = load8<T>(d_o + head_off + tok * D + 32 * ks + 8 * g);
+  }
+  const float lse2 = lse[(int64_t)bh * L + tok] * LOG2E;
+  const float dlt = delta[(int64_t)bh * L + tok];
+  const float scale_log2 = scale * LOG2E;
+  const int qrow = 16 * w + c;
+  f32x4 acc[D / 16];
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  TileRegs<T, D> rk, rv;
+  for (int it = 0; it <= nsb; ++it) {
+    const int kc = it < nsb ? sel[it] : qc;
+    const bool diag = it == nsb;
+    tile_gload<T, D>(rk, k + head_off + (int64_t)kc * CHUNK * D, k + head_off + (int64_t)kc * CHUNK * D);
+    tile_gload<T, D>(rv, v + head_off + (int64_t)kc * CHUNK * D, v + head_off + (int64_t)kc * CHUNK * D);
+    __syncthreads();  // the previous tile's reads are done
+    tile_sstore<T, D>(rk, kbuf);
+    tile_sstore<T, D>(rv, vbuf);
+    __syncthreads();
+    // S^T and dP^T for 64 keys x this wave's 16 queries
+    f32x4 s[4], dp[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) s[kt] = dp[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < C::KF; ++ks)
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        mma(s[kt], load8<T>(kbuf + (16 * kt + c) * C::KP + 32 * ks + 8 * g), qf[ks]);
+        mma(dp[kt], load8<T>(vbuf + (16 * kt + c) * C::KP + 32 * ks + 8 * g), df[ks]);
+      }
+    // dS^T = P^T (dP^T - delta), packed as the B operand (keys in accumulator order)
+    Frag<T> dsf[2];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool vis = !diag || (16 * kt + 4 * g + i) <= qrow;
+        const float pp = vis ? __builtin_amdgcn_exp2f(fmaf(s[kt][i], scale_log2, -lse2)) : 0.f;
+        frag_set(dsf[kt >> 1], 4 * (kt & 1) + i, pp * (dp[kt][i] - dlt));
+      }
+    // dQ^T += K^T dS^T
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        const T* kg = kbuf + C::KTILE;
+        const Frag<T> a = load4x2<T>(kg + kg_index<C::VRL>(8 * k2 + g, 16 * dt + c),
+                                     kg + kg_index<C::VRL>(8 * k2 + 4 + g, 16 * dt + c));
+        mma(acc[dt], a, dsf[k2]);
+      }
+  }
+  float* out = dq + head_off + tok * D;
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) {
+    f32x4 r = acc[dt] * scale;
+    *reinterpret_cast<f32x4*>(out + 16 * dt + 4 * g) = r;
+  }
+}
+
+template <typename T, int D>
+__global__ void __launch_bounds__(256) k_sm_bwd_dkdv(const T* __restrict__ q, const T* __restrict__ k,
+                                                     const T* __restrict__ v, const T* __restrict__ d_o,
+                                                     const int32_t* __restrict__ nsel_before,
+                                                     const float* __restrict__ lse, const float* __restrict__ delta,
+                                                     float* __restrict__ dk, float* __restrict__ dv, int H, int L,
+                                                     int G, float scale) {
+  using C = SmCfg<T, D>;
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  T* qbuf = reinterpret_cast<T*>(smem_raw);  // Q rows, dO key groups
+  T* dbuf = qbuf + C::BUF;                   // dO rows, Q key groups
+  float* lse_s = reinterpret_cast<float*>(dbuf + C::BUF);
+  float* dlt_s = lse_s + CHUNK;
+  const int nc = L / CHUNK;
+  const int BH = (int)(grid_dim_x() / nc);
+  const int p = bid_x();
+  const int kc = p / BH;  // earlier key chunks are seen by more queries: first
+  const int bh = p % BH;
+  const int b = bh / H, h = bh % H;
+  const int grp = (G == 1) ? 0 : h;
+  const int32_t* nsbp = nsel_before + ((int64_t)b * G + grp) * (nc + 1);
+  const bool kc_sm = nsbp[kc + 1] > nsbp[kc];
+  const int qlast = kc_sm ? nc - 1 : kc;
+  const int lane = lane_id(), w = wave_id();
+  const int g = lane >> 4, c = lane & 15;
+  const int64_t head_off = (int64_t)bh * L * D;
+  const int64_t key = (int64_t)kc * CHUNK + 16 * w + c;
+  Frag<T> kf[C::KF], vf[C::KF];
+#pragma unroll
+  for (int ks = 0; ks < C::KF; ++ks) {
+    kf[ks] = load8<T>(k + head_off + key * D + 32 * ks + 8 * g);
+    vf[ks] = load8<T>(v + head_off + key * D + 32 * ks + 8 * g);
+  }
+  const float scale_log2 = scale * LOG2E;
+  const int kcol = 16 * w + c;
+  f32x4 adk[D / 16], adv[D / 16];
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) adk[dt] = adv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  TileRegs<T, D> ra, rb;
+  for (int qcx = kc; qcx <= qlast; ++qcx) {
+    const bool diag = qcx == kc;
+    const T* qg = q + head_off + (int64_t)qcx * CHUNK * D;
+    const T* dg = d_o + head_off + (int64_t)qcx * CHUNK * D;
+    tile_gload<T, D>(ra, qg, dg);
+    tile_gload<T, D>(rb, dg, qg);
+    __syncthreads();
+    tile_sstore<T, D>(ra, qbuf);
+    tile_sstore<T, D>(rb, dbuf);
+    if (tid_x() < CHUNK) {
+      lse_s[tid_x()] = lse[(int64_t)bh * L + (int64_t)qcx * CHUNK + tid_x()] * LOG2E;
+      dlt_s[tid_x()] = delta[(int64_t)bh * L + (int64_t)qcx * CHUNK + tid_x()];
+    }
+    __syncthreads();
+    // S and dP for 64 queries x this wave's 16 keys: rows = queries
+    f32x4 pm[4], dsm[4];
+#pragma unroll
+    for (int qt = 0; qt < 4; ++qt) {
+      f32x4 s = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < C::KF; ++ks) {
+        mma(s, load8<T>(qbuf + (16 * qt + c) * C::KP + 32 * ks + 8 * g), kf[ks]);
+        mma(dp, load8<T>(dbuf + (16 * qt + c) * C::KP + 32 * ks + 8 * g), vf[ks]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int qrow = 16 * qt + 4 * g + i;
+        const bool vis = !diag || kcol <= qrow;
+        const float pp = vis ? __builtin_amdgcn_exp2f(fmaf(s[i], scale_log2, -lse_s[qrow])) : 0.f;
+        pm[qt][i] = pp;
+        dsm[qt][i] = pp * (dp[i] - dlt_s[qrow]);
+      }
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS, contraction over the 64 queries
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      Frag<T> pf, dsf;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        frag_set(pf, j, pm[2 * k2][j]);
+        frag_set(pf, 4 + j, pm[2 * k2 + 1][j]);
+        frag_set(dsf, j, dsm[2 * k2][j]);
+        frag_set(dsf, 4 + j, dsm[2 * k2 + 1][j]);
+      }
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) {
+        const T* dgk = qbuf + C::KTILE;  // dO key groups
+        const T* qgk = dbuf + C::KTILE;  // Q key groups
+        mma(adv[dt], load4x2<T>(dgk + kg_index<C::VRL>(8 * k2 + g, 16 * dt + c),
+                                dgk + kg_index<C::VRL>(8 * k2 + 4 + g, 16 * dt + c)), pf);
+        mma(adk[dt], load4x2<T>(qgk + kg_index<C::VRL>(8 * k2 + g, 16 * dt + c),
+                                qgk + kg_index<C::VRL>(8 * k2 + 4 + g, 16 * dt + c)), dsf);
+      }
+    }
+  }
+  float* okr = dk + head_off + key * D;
+  float* ovr = dv + head_off + key * D;
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) {
+    f32x4 r = adk[dt] * scale;
+    *reinterpret_cast<f32x4*>(okr + 16 * dt + 4 * g) = r;
+    *reinterpret_cast<f32x4*>(ovr + 16 * dt + 4 * g) = adv[dt];
+  }
+}
+
+size_t sm_bwd_ws_bytes(int B, int H, int L) { return (size_t)B * H * L * sizeof(float); }
+
+template <typename T, typename To, int D>
+hipError_t launch_softmax_backward(const T* q, const T* k, const T* v, const int32_t* sel_idx,
+                                   const int32_t* nsel_before, const To* o, const float* lse, const T* d_o,
+                                   float* dq, float* dk, float* dv, void* ws, int B, int H, int L, int G,
+                                   float scale, hipStream_t st) {
+  using C = SmCfg<T, D>;
+  // the delta pass reads dO in the output dtype: only io == output dtype here
+  static_assert(sizeof(To) > 0, "");
+  float* delta = static_cast<float*>(ws);
+  const int64_t ntok = (int64_t)B * H * L;
+  const int nc = L / CHUNK;
+  constexpr int LDS_DQ = 2 * C::BUF * (int)sizeof(T);
+  constexpr int LDS_DKDV = 2 * C::BUF * (int)sizeof(T) + 2 * CHUNK * 4;
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute((const void*)k_sm_bwd_dq<T, D>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       LDS_DQ);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute((const void*)k_sm_bwd_dkdv<T, D>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              LDS_DKDV);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  hipLaunchKernelGGL((k_sm_bwd_delta<To, D>), dim3((unsigned)((ntok + 255) / 256)), dim3(256), 0, st, o,
+                     (const To*)d_o, delta, ntok);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t grid = (int64_t)B * H * nc;
+  hipLaunchKernelGGL((k_sm_bwd_dq<T, D>), dim3((unsigned)grid), dim3(256), LDS_DQ, st, q, k, v, d_o, sel_idx,
+                     nsel_before, lse, delta, dq, H, L, G, scale);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((k_sm_bwd_dkdv<T, D>), dim3((unsigned)grid), dim3(256), LDS_DKDV, st, q, k, v, d_o,
+                     nsel_before, lse, delta, dk, dv, H, L, G, scale);
+  return hipGetLastError();
+}
+
+#define INSTB(T, D)                                                                                    \
+  template hipError_t launch_softmax_backward<T, T, D>(const T*, const T*, const T*, const int32_t*,  \
+                                                       const int32_t*, const T*, const float*, const T*, \
+                                                       float*, float*, float*, void*, int, int, int, int, \
+                                                       float, hipStream_t);
+INSTB(float, 64)
+INSTB(float, 128)
+INSTB(bf16, 64)
+INSTB(bf16, 128)
+#undef INSTB
+
 }  // namespace natsl

@@ -237,3 +237,16 @@ def test_profile_select(L):
         N.profile_select("gdn_everything")
     N.profile_select("merge")
     N.profile_select(None)
+
+
+def test_binding_argtypes_match_prototypes(L):
+    """The ctypes argument list of every declared function has the length of
+    its C prototype (a short list passes the trailing stream handle as a
+    32-bit int)."""
+    src = open(HDR).read()
+    protos = {m.group(1): m.group(2) for m in re.finditer(r"natsl_status\s+(natsl_\w+)\s*\(([^;]*?)\);", src, re.S)}
+    assert len(protos) >= 12
+    for name, args in protos.items():
+        n = 0 if args.strip() == "void" else len([a for a in args.split(",") if a.strip()])
+        at = getattr(L, name).argtypes
+        assert (at is None and n == 0) or (at is not None and len(at) == n), (name, n, at)

@@ -334,6 +334,41 @@ def test_decode_steps_match_oracle(io, D):
     assert int(st.err.item()) == 0
 
 
+@pytest.mark.parametrize("io,D,L,q_scale,per_head", [("f32", 64, 256, 1.0, False), ("f32", 128, 320, 1.0, False),
+                                                      ("bf16", 128, 640, 1.0, False), ("bf16", 128, 576, 8.0, False),
+                                                      ("bf16", 64, 448, 1.0, True)])
+def test_softmax_backward_parity(io, D, L, q_scale, per_head):
+    """Gradient of the softmax branch against the oracle's derivative, from
+    the GPU forward's o and lse; the error is taken relative to each
+    gradient's largest magnitude (bf16: P and dS are rounded to bf16 for the
+    matrix cores, and o is the bf16 forward output)."""
+    B, H = 2, 2
+    wl, inp = small_case(io, B=B, H=H, L=L, D=D, q_scale=q_scale, seed=81)
+    G = H if per_head else 1
+    nc = L // 64
+    if per_head:
+        r = (np.random.default_rng(81).random((B, G, nc)) < 0.5).astype(np.int32)
+    else:
+        r = np.broadcast_to(inp["plan"], (B, 1, nc)).copy()
+    sel, nsb = O.compact(r)
+    dm = N.dims(B, H, L, D, wl.d, io_code(inp), groups=G)
+    say(f"[softmax backward] io={io} D={D} L={L} qs={q_scale} G={G}")
+    tq, tk, tv = dev(inp["q"], io), dev(inp["k"], io), dev(inp["v"], io)
+    io_t = torch.bfloat16 if io == "bf16" else torch.float32
+    o, lse = N.softmax_masked(dm, tq, tk, tv, dev(sel), dev(nsb), o_dtype=io_t, want_lse=True)
+    d_o = np.random.default_rng(82).standard_normal(inp["q"].shape).astype(np.float32)
+    if io == "bf16":
+        d_o = torch.from_numpy(d_o).to(torch.bfloat16).float().numpy()
+    dq, dk, dv = N.softmax_masked_backward(dm, tq, tk, tv, dev(sel), dev(nsb), o, lse, dev(d_o, io))
+    torch.cuda.synchronize()
+    ref = O.softmax_branch_backward(inp["q"], inp["k"], inp["v"], r, d_o)
+    tol = 1e-4 if io == "f32" else 3e-2
+    for name, got, rf in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+        e = maxerr(host(got), rf) / max(1e-30, float(np.abs(rf).max()))
+        say(f"  {name} rel err {e:.3e}")
+        assert e <= tol, (name, e)
+
+
 @pytest.mark.parametrize("io,D", [("f32", 64), ("bf16", 128)])
 def test_decode_handoff_then_decode(io, D):
     """natsl_forward over a 192-token prefix, natsl_decode_handoff of its
