@@ -116,11 +116,33 @@ __device__ __forceinline__ void tile_sstore(const TileRegs<T, D>& r, T* buf) {
     const int task = t + 256 * i;
     if (task < C::VTASKS) {
       const int kg = task / (D / 8), col = (task % (D / 8)) * 8;
+      if constexpr (sizeof(T) == 2) {
+        // 4 tokens x 8 columns of bf16 transposed in registers: word m of
+        // token tk holds columns 2m (low half) and 2m + 1 (high half); v_perm
+        // pairs the halves of two tokens (element extraction from the bf16
+        // vectors went through scratch memory)
+        uint32_t w[4][4];
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        store_col4<T>(vs + kg_index<C::VRL>(kg, col + j), frag_get<T>(r.v[i][0], j),
-                      frag_get<T>(r.v[i][1], j), frag_get<T>(r.v[i][2], j),
-                      frag_get<T>(r.v[i][3], j));
+        for (int tk = 0; tk < 4; ++tk) {
+          const uint4 u = __builtin_bit_cast(uint4, r.v[i][tk].v);
+          w[tk][0] = u.x; w[tk][1] = u.y; w[tk][2] = u.z; w[tk][3] = u.w;
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const uint2 lo = {__builtin_amdgcn_perm(w[1][m], w[0][m], 0x05040100u),
+                            __builtin_amdgcn_perm(w[3][m], w[2][m], 0x05040100u)};
+          const uint2 hi = {__builtin_amdgcn_perm(w[1][m], w[0][m], 0x07060302u),
+                            __builtin_amdgcn_perm(w[3][m], w[2][m], 0x07060302u)};
+          *reinterpret_cast<uint2*>(vs + kg_index<C::VRL>(kg, col + 2 * m)) = lo;
+          *reinterpret_cast<uint2*>(vs + kg_index<C::VRL>(kg, col + 2 * m + 1)) = hi;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          store_col4<T>(vs + kg_index<C::VRL>(kg, col + j), frag_get<T>(r.v[i][0], j),
+                        frag_get<T>(r.v[i][1], j), frag_get<T>(r.v[i][2], j),
+                        frag_get<T>(r.v[i][3], j));
+      }
     }
   }
 }
@@ -678,8 +700,56 @@ __global__ void __launch_bounds__(256) k_sm_bwd_delta(const To* __restrict__ o, 
   delta[t] = acc;
 }
 
+// One 64-token tile loaded once and written to LDS in both layouts: thread t
+// takes 4 consecutive tokens 4 (t / (D/8)) .. +3 of the 8 columns
+// 8 (t % (D/8)) .. +7 (threads past the 64 tokens idle), writes them as rows
+// (pitch KP) and, if kg is given, as one key group (4 tokens of each column
+// contiguous).
 template <typename T, int D>
-__global__ void __launch_bounds__(256) k_sm_bwd_dq(const T* __restrict__ q, const T* __restrict__ k,
+struct Stage4 {
+  Frag<T> f[4];
+};
+template <typename T, int D>
+__device__ __forceinline__ void stage_load(Stage4<T, D>& st, const T* src) {
+  const int t = tid_x(), rg = t / (D / 8), cc = t % (D / 8);
+  if (4 * rg < CHUNK)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) st.f[i] = load8<T>(src + (int64_t)(4 * rg + i) * D + 8 * cc);
+}
+template <typename T, int D>
+__device__ __forceinline__ void stage_store(const Stage4<T, D>& st, T* rows, T* kg) {
+  using C = SmCfg<T, D>;
+  const int t = tid_x(), rg = t / (D / 8), cc = t % (D / 8);
+  if (4 * rg >= CHUNK) return;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) store8<T>(rows + (4 * rg + i) * C::KP + 8 * cc, st.f[i]);
+  if (!kg) return;
+  if constexpr (sizeof(T) == 2) {
+    uint32_t w[4][4];
+#pragma unroll
+    for (int tk = 0; tk < 4; ++tk) {
+      const uint4 u = __builtin_bit_cast(uint4, st.f[tk].v);
+      w[tk][0] = u.x; w[tk][1] = u.y; w[tk][2] = u.z; w[tk][3] = u.w;
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const uint2 lo = {__builtin_amdgcn_perm(w[1][m], w[0][m], 0x05040100u),
+                        __builtin_amdgcn_perm(w[3][m], w[2][m], 0x05040100u)};
+      const uint2 hi = {__builtin_amdgcn_perm(w[1][m], w[0][m], 0x07060302u),
+                        __builtin_amdgcn_perm(w[3][m], w[2][m], 0x07060302u)};
+      *reinterpret_cast<uint2*>(kg + kg_index<C::VRL>(rg, 8 * cc + 2 * m)) = lo;
+      *reinterpret_cast<uint2*>(kg + kg_index<C::VRL>(rg, 8 * cc + 2 * m + 1)) = hi;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      store_col4<T>(kg + kg_index<C::VRL>(rg, 8 * cc + j), frag_get<T>(st.f[0], j), frag_get<T>(st.f[1], j),
+                    frag_get<T>(st.f[2], j), frag_get<T>(st.f[3], j));
+  }
+}
+
+template <typename T, int D>
+__global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) k_sm_bwd_dq(const T* __restrict__ q, const T* __restrict__ k,
                                                    const T* __restrict__ v, const T* __restrict__ d_o,
                                                    const int32_t* __restrict__ sel_idx,
                                                    const int32_t* __restrict__ nsel_before,
@@ -715,16 +785,21 @@ __global__ void __launch_bounds__(256) k_sm_bwd_dq(const T* __restrict__ q, cons
   f32x4 acc[D / 16];
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  TileRegs<T, D> rk, rv;
-  for (int it = 0; it <= nsb; ++it) {
+  // the next tile's global loads are issued before this tile's products
+  Stage4<T, D> rk, rv;
+  auto gload = [&](int it) {
     const int kc = it < nsb ? sel[it] : qc;
+    stage_load<T, D>(rk, k + head_off + (int64_t)kc * CHUNK * D);
+    stage_load<T, D>(rv, v + head_off + (int64_t)kc * CHUNK * D);
+  };
+  gload(0);
+  for (int it = 0; it <= nsb; ++it) {
     const bool diag = it == nsb;
-    tile_gload<T, D>(rk, k + head_off + (int64_t)kc * CHUNK * D, k + head_off + (int64_t)kc * CHUNK * D);
-    tile_gload<T, D>(rv, v + head_off + (int64_t)kc * CHUNK * D, v + head_off + (int64_t)kc * CHUNK * D);
     __syncthreads();  // the previous tile's reads are done
-    tile_sstore<T, D>(rk, kbuf);
-    tile_sstore<T, D>(rv, vbuf);
+    stage_store<T, D>(rk, kbuf, kbuf + C::KTILE);
+    stage_store<T, D>(rv, vbuf, nullptr);
     __syncthreads();
+    if (it < nsb) gload(it + 1);
     // S^T and dP^T for 64 keys x this wave's 16 queries
     f32x4 s[4], dp[4];
 #pragma unroll
@@ -766,7 +841,7 @@ __global__ void __launch_bounds__(256) k_sm_bwd_dq(const T* __restrict__ q, cons
 }
 
 template <typename T, int D>
-__global__ void __launch_bounds__(256) k_sm_bwd_dkdv(const T* __restrict__ q, const T* __restrict__ k,
+__global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) k_sm_bwd_dkdv(const T* __restrict__ q, const T* __restrict__ k,
                                                      const T* __restrict__ v, const T* __restrict__ d_o,
                                                      const int32_t* __restrict__ nsel_before,
                                                      const float* __restrict__ lse, const float* __restrict__ delta,
@@ -803,21 +878,29 @@ __global__ void __launch_bounds__(256) k_sm_bwd_dkdv(const T* __restrict__ q, co
   f32x4 adk[D / 16], adv[D / 16];
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) adk[dt] = adv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  TileRegs<T, D> ra, rb;
+  // the next query chunk's global loads are issued before this one's products
+  Stage4<T, D> ra, rb;
+  float lse_r = 0.f, dlt_r = 0.f;
+  auto gload = [&](int qcx) {
+    stage_load<T, D>(ra, q + head_off + (int64_t)qcx * CHUNK * D);
+    stage_load<T, D>(rb, d_o + head_off + (int64_t)qcx * CHUNK * D);
+    if (tid_x() < CHUNK) {
+      lse_r = lse[(int64_t)bh * L + (int64_t)qcx * CHUNK + tid_x()] * LOG2E;
+      dlt_r = delta[(int64_t)bh * L + (int64_t)qcx * CHUNK + tid_x()];
+    }
+  };
+  gload(kc);
   for (int qcx = kc; qcx <= qlast; ++qcx) {
     const bool diag = qcx == kc;
-    const T* qg = q + head_off + (int64_t)qcx * CHUNK * D;
-    const T* dg = d_o + head_off + (int64_t)qcx * CHUNK * D;
-    tile_gload<T, D>(ra, qg, dg);
-    tile_gload<T, D>(rb, dg, qg);
-    __syncthreads();
-    tile_sstore<T, D>(ra, qbuf);
-    tile_sstore<T, D>(rb, dbuf);
+    __syncthreads();  // the previous chunk's reads are done
+    stage_store<T, D>(ra, qbuf, dbuf + C::KTILE);  // Q rows; Q key groups next to dO rows
+    stage_store<T, D>(rb, dbuf, qbuf + C::KTILE);  // dO rows; dO key groups next to Q rows
     if (tid_x() < CHUNK) {
-      lse_s[tid_x()] = lse[(int64_t)bh * L + (int64_t)qcx * CHUNK + tid_x()] * LOG2E;
-      dlt_s[tid_x()] = delta[(int64_t)bh * L + (int64_t)qcx * CHUNK + tid_x()];
+      lse_s[tid_x()] = lse_r;
+      dlt_s[tid_x()] = dlt_r;
     }
     __syncthreads();
+    if (qcx < qlast) gload(qcx + 1);
     // S and dP for 64 queries x this wave's 16 keys: rows = queries
     f32x4 pm[4], dsm[4];
 #pragma unroll
