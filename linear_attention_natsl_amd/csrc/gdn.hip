@@ -142,7 +142,7 @@ __global__ void __launch_bounds__(256, 2)
   T* Vg = (T*)(lds + C::OFF_VG);
   float* LT = (float*)(lds + C::OFF_LT);
   float* Rs = (float*)(lds + C::OFF_RS);
-  float* gl = (float*)(lds + C::OFF_GL);  // cumulative log decay
+  float* gl = (float*)(lds + C::OFF_GL);  // cumulative log2 decay
   float* bl = gl + CHUNK;                 // beta
   float* gbl = bl + CHUNK;                // beta * gamma
   float* ekl = gbl + CHUNK;               // exp(g_C - g)
@@ -175,11 +175,12 @@ __global__ void __launch_bounds__(256, 2)
   Frag<T> qa[C::KF];
 #pragma unroll
   for (int ks = 0; ks < C::KF; ++ks) qa[ks] = load8<T>(q + (tok0 + 16 * w + c) * D + 32 * ks + 8 * g);
-  // cumulative log decay (wave 0), beta
+  // cumulative log decay in log2 units (wave 0), beta: every decay below is
+  // one v_exp_f32 of a difference (the library expf is a dozen VALU ops)
   if (w == 0) {
     const float a = alpha[tok0 + lane];
     const float bt = beta[tok0 + lane];
-    float s = logf(a);
+    float s = __builtin_amdgcn_logf(a);
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const float o = __shfl_up(s, off, 64);
@@ -188,11 +189,11 @@ __global__ void __launch_bounds__(256, 2)
     const float gC = __shfl(s, 63, 64);
     gl[lane] = s;
     bl[lane] = bt;
-    gbl[lane] = bt * expf(s);
-    ekl[lane] = expf(gC - s);
-    ws.gm[ch * C::GM + lane] = expf(s);
-    ws.gm[ch * C::GM + 80 + lane] = expf(gC - s);
-    if (lane == 0) ws.gm[ch * C::GM + 64] = expf(gC);
+    gbl[lane] = bt * __builtin_amdgcn_exp2f(s);
+    ekl[lane] = __builtin_amdgcn_exp2f(gC - s);
+    ws.gm[ch * C::GM + lane] = __builtin_amdgcn_exp2f(s);
+    ws.gm[ch * C::GM + 80 + lane] = __builtin_amdgcn_exp2f(gC - s);
+    if (lane == 0) ws.gm[ch * C::GM + 64] = __builtin_amdgcn_exp2f(gC);
   }
   // K -> row layout and key-group layout, V -> key-group layout
   if (t < TASKS) {
@@ -234,7 +235,7 @@ __global__ void __launch_bounds__(256, 2)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * w + 4 * g + i, col = 16 * ct + c;
-      LT[r * C::LTP + col] = (col < r) ? bl[r] * expf(gl[r] - gl[col]) * akk[ct][i] : 0.f;
+      LT[r * C::LTP + col] = (col < r) ? bl[r] * __builtin_amdgcn_exp2f(gl[r] - gl[col]) * akk[ct][i] : 0.f;
     }
   // P = tril(Gamma . QK^T): apt[ct][i] is (query 16w + c, key 16ct + 4g + i); the
   // fragment of key half k2 holds keys 32k2 + 4g + j and 32k2 + 16 + 4g + j,
@@ -247,7 +248,7 @@ __global__ void __launch_bounds__(256, 2)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int col = 16 * ct + 4 * g + i;
-        const float pv = (col <= r) ? expf(gl[r] - gl[col]) * apt[ct][i] : 0.f;
+        const float pv = (col <= r) ? __builtin_amdgcn_exp2f(gl[r] - gl[col]) * apt[ct][i] : 0.f;
         const int k2 = ct >> 1, j = (ct & 1) * 4 + i;
         frag_set(ph[k2], j, pv);
         frag_set(pl[k2], j, pv - to_f32(frag_get<T>(ph[k2], j)));
