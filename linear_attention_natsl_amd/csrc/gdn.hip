@@ -26,9 +26,10 @@
 //               per-lane fragment order the scan consumes (every scan load is
 //               16 B per lane, 1 KiB contiguous per wave).  T diag(b) and
 //               T diag(b gamma) are split into bf16 hi + lo parts for their
-//               products, and P is stored as hi + lo, so neither is rounded to
-//               bf16 precision; K^T stays exact (its exp(g_C - g) scale is
-//               applied to U in fp32 by the scan).
+//               products, so neither is rounded to bf16 precision; P is
+//               stored as hi + lo except for the bf16 head-form scan, which
+//               takes P in bf16 like -W and U; K^T stays exact (its
+//               exp(g_C - g) scale is applied to U in fp32 by the scan).
 //   k_gdn_scan  one workgroup per (b, h, 32-column slice of Dv), sequential
 //               over chunks.  Columns of S evolve independently under the
 //               delta rule, so slicing Dv needs no communication.  The fp32
@@ -238,8 +239,9 @@ __global__ void __launch_bounds__(256, 2)
       LT[r * C::LTP + col] = (col < r) ? bl[r] * __builtin_amdgcn_exp2f(gl[r] - gl[col]) * akk[ct][i] : 0.f;
     }
   // P = tril(Gamma . QK^T): apt[ct][i] is (query 16w + c, key 16ct + 4g + i); the
-  // fragment of key half k2 holds keys 32k2 + 4g + j and 32k2 + 16 + 4g + j,
-  // split into a bf16 part and the remainder bf16 could not hold (zero for fp32)
+  // fragment of key half k2 holds keys 32k2 + 4g + j and 32k2 + 16 + 4g + j.
+  // The head-form scan takes P in bf16 (as it takes -W); otherwise P is split
+  // into a bf16 part and the remainder bf16 could not hold (zero for fp32)
   {
     Frag<T> ph[2], pl[2];
     const int r = 16 * w + c;
@@ -251,12 +253,16 @@ __global__ void __launch_bounds__(256, 2)
         const float pv = (col <= r) ? __builtin_amdgcn_exp2f(gl[r] - gl[col]) * apt[ct][i] : 0.f;
         const int k2 = ct >> 1, j = (ct & 1) * 4 + i;
         frag_set(ph[k2], j, pv);
-        frag_set(pl[k2], j, pv - to_f32(frag_get<T>(ph[k2], j)));
+        if constexpr (!scan_head_form<T, D>()) frag_set(pl[k2], j, pv - to_f32(frag_get<T>(ph[k2], j)));
       }
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
-      store8<T>(ws.pm + (((ch * 4 + w) * 2 + k2) * 2 + 0) * 512 + lane * 8, ph[k2]);
-      store8<T>(ws.pm + (((ch * 4 + w) * 2 + k2) * 2 + 1) * 512 + lane * 8, pl[k2]);
+      if constexpr (scan_head_form<T, D>()) {
+        store8<T>(ws.pm + ch * C::PM + (w * 2 + k2) * 512 + lane * 8, ph[k2]);  // first half of the chunk's slot
+      } else {
+        store8<T>(ws.pm + (((ch * 4 + w) * 2 + k2) * 2 + 0) * 512 + lane * 8, ph[k2]);
+        store8<T>(ws.pm + (((ch * 4 + w) * 2 + k2) * 2 + 1) * 512 + lane * 8, pl[k2]);
+      }
     }
   }
   __syncthreads();
@@ -640,7 +646,7 @@ __global__ void __launch_bounds__(256, 1)
 // B operand (contraction over d) is packed from the fp32 accumulators directly
 // (accumulator-shaped map, which is how the chunk prep writes -W for this
 // form); U's B operand (contraction over tokens) likewise.
-// The operands every wave needs (-W, Q, P hi + lo, K^T: 64 KiB, plus the
+// The operands every wave needs (-W, Q, P, K^T: 56 KiB in bf16, plus the
 // decays) go through a 2-stage LDS ring by direct global -> LDS loads issued
 // one chunk ahead; each wave loads its own U~ columns into registers one chunk
 // ahead.  All loads of a chunk, and the output stores of the previous one, are
@@ -648,9 +654,9 @@ __global__ void __launch_bounds__(256, 1)
 // chunk.
 constexpr int SCH_WN = 0;              // -W fragments [rt 4][ks 4][lane][8]
 constexpr int SCH_Q = 16384;           // Q rows, 16-byte chunk q of row r at slot q ^ (r & 15)
-constexpr int SCH_PM = 2 * 16384;      // P fragments [rt 4][k2 2][hi, lo][lane][8]
-constexpr int SCH_KT = 3 * 16384;      // K^T fragments [dt 8][k2 2][lane][8]
-constexpr int SCH_GM = 4 * 16384;      // gamma[64], gamma_C at 64, exp(g_C - g)[64] at 80 (fp32)
+constexpr int SCH_PM = 2 * 16384;      // P fragments (bf16) [rt 4][k2 2][lane][8]
+constexpr int SCH_KT = SCH_PM + 8192;  // K^T fragments [dt 8][k2 2][lane][8]
+constexpr int SCH_GM = SCH_KT + 16384; // gamma[64], gamma_C at 64, exp(g_C - g)[64] at 80 (fp32)
 constexpr int SCH_STAGE = SCH_GM + 576;
 constexpr int SCH_ROUTE = 2 * SCH_STAGE;
 constexpr int SCH_NW = 4;              // waves per workgroup
@@ -736,7 +742,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW)
   const uint32_t off_lin = (uint32_t)(w * 1024 + lane * 16);
   const int qr = 4 * w + (lane >> 4);
   const uint32_t off_q = (uint32_t)(w * 1024 + (lane >> 4) * 256 + (((lane & 15) ^ (qr & 15)) * 16));
-  // part 0: -W, 1: Q, 2: P, 3: K^T and the decays
+  // part 0: -W, 1: Q, 2: P (8 KiB), 3: K^T and the decays
   auto load_stage = [&](int cc, int st, int part) {
     const int64_t ch = bh * nc + cc;
     unsigned char* sb = lds + opaque_sgpr(st * SCH_STAGE);
@@ -757,8 +763,10 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW)
       src = reinterpret_cast<const unsigned char*>(ws.kt + ch * C::KT);
       dst = SCH_KT;
     }
+    const int nb = part == 2 ? NB / 2 : NB;  // P: 8 KiB
 #pragma unroll
-    for (int i = 0; i < NB; ++i) gload_lds16_s(src + i * NW * 1024, off, sb + dst + (NW * i + w) * 1024);
+    for (int i = 0; i < NB; ++i)
+      if (i < nb) gload_lds16_s(src + i * NW * 1024, off, sb + dst + (NW * i + w) * 1024);
     if (part == 3 && w == 0 && lane < 36)  // 576 bytes of decays
       gload_lds16_s(ws.gm + ch * C::GM, (uint32_t)(lane * 16), sb + SCH_GM);
   };
@@ -801,16 +809,13 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW)
                             reinterpret_cast<const bf16*>(qrow + ((q2 ^ c) * 16) + half));
     }
   };
-  struct FragP { Frag<bf16> p[2][2][2]; };  // P for two row tiles: [tile][k2][hi, lo]
+  struct FragP { Frag<bf16> p[2][2]; };  // P for two row tiles: [tile][k2]
   auto read_p = [&](const unsigned char* sb, int rt0, FragP& f) {
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-        for (int hl = 0; hl < 2; ++hl)
-          f.p[t][k2][hl] = load8<bf16>(
-              reinterpret_cast<const bf16*>(sb + SCH_PM + ((((rt0 + t) * 2 + k2) * 2 + hl) * 64 + lane) * 16));
+        f.p[t][k2] = load8<bf16>(reinterpret_cast<const bf16*>(sb + SCH_PM + (((rt0 + t) * 2 + k2) * 64 + lane) * 16));
   };
   struct FragK { Frag<bf16> k[4][2]; };  // K^T for four d tiles: [tile][k2]
   auto read_k = [&](const unsigned char* sb, int dt0, FragK& f) {
@@ -903,7 +908,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW)
 #pragma unroll
       for (int nn = 0; nn < NV; ++nn) o[rt][nn] *= gam;
     }
-    // O += P U  (P as hi + lo), two row tiles per group
+    // O += P U, two row tiles per group
     FragK fk[2];
 #pragma unroll
     for (int gp = 0; gp < 2; ++gp) {
@@ -919,9 +924,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW)
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
-          for (int hl = 0; hl < 2; ++hl)
-#pragma unroll
-            for (int nn = 0; nn < NV; ++nn) mma(o[2 * gp + t][nn], fp[gp].p[t][k2][hl], bu[k2][nn]);
+          for (int nn = 0; nn < NV; ++nn) mma(o[2 * gp + t][nn], fp[gp].p[t][k2], bu[k2][nn]);
       fence();
     }
     // S <- gamma_C S + K^T diag(exp(g_C - g)) U, four d tiles per group
