@@ -198,6 +198,13 @@ __device__ __forceinline__ void gload_lds16_s(const void* gbase, uint32_t voff, 
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(base), "v"(voff), "s"(gs)
                : "memory", "m0");
 }
+// s_waitcnt until at most N vector memory operations of this wave are
+// outstanding (they complete in issue order); expcnt / lgkmcnt not waited
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
 // s_waitcnt with vmcnt = n (expcnt / lgkmcnt not waited); n in {0, 4, 8}
 __device__ __forceinline__ void wait_vm(int n) {
   if (n >= 8) __builtin_amdgcn_s_waitcnt(0x0F78);

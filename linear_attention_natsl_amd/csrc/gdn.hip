@@ -656,7 +656,8 @@ constexpr int SCH_WN = 0;              // -W fragments [rt 4][ks 4][lane][8]
 constexpr int SCH_Q = 16384;           // Q rows, 16-byte chunk q of row r at slot q ^ (r & 15)
 constexpr int SCH_PM = 2 * 16384;      // P fragments (bf16) [rt 4][k2 2][lane][8]
 constexpr int SCH_KT = SCH_PM + 8192;  // K^T fragments [dt 8][k2 2][lane][8]
-constexpr int SCH_GM = SCH_KT + 16384; // gamma[64], gamma_C at 64, exp(g_C - g)[64] at 80 (fp32)
+constexpr int SCH_UT = SCH_KT + 16384; // the workgroup's U~ columns (fp32 accumulator order) [rt 4][tile 4][lane][4]
+constexpr int SCH_GM = SCH_UT + 16384; // gamma[64], gamma_C at 64, exp(g_C - g)[64] at 80 (fp32)
 constexpr int SCH_STAGE = SCH_GM + 576;
 constexpr int SCH_ROUTE = 2 * SCH_STAGE;
 constexpr int SCH_NW = 4;              // waves per workgroup
@@ -716,7 +717,6 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW)
   const int lane = lane_id(), w = wave_id();
   const int g = lane >> 4, c = lane & 15;
   const int dv0 = 16 * NV * (NW * part + w);
-  const int nt0 = NV * (NW * part + w);  // first 16-column tile of this wave
 
   for (int i = tid_x(); i < nc; i += 64 * NW) rl[i] = rt_g[i];
 
@@ -735,53 +735,60 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW)
         for (int i = 0; i < 4; ++i) sm[dt][nn][i] = S_init[(bh * D + 16 * dt + 4 * g + i) * D + dv0 + 16 * nn + c];
   }
 
-  // chunk cc's shared operands -> stage st.  Wave w loads the 1 KiB blocks
+  // chunk cc's operands -> stage st, all by direct global -> LDS loads (so
+  // that the waits below can count them).  Wave w loads the 1 KiB blocks
   // NW i + w of each 16 KiB operand; for Q, LDS position e = 64 blk + lane
   // holds 16-byte chunk (e & 15) ^ (r & 15) of row r = e / 16, and r & 15 does
-  // not depend on i
+  // not depend on i.  Per wave: NB blocks each of -W, Q and K^T, 4 NV of U~,
+  // NB / 2 of P and one partial block of the decays.
   const uint32_t off_lin = (uint32_t)(w * 1024 + lane * 16);
   const int qr = 4 * w + (lane >> 4);
   const uint32_t off_q = (uint32_t)(w * 1024 + (lane >> 4) * 256 + (((lane & 15) ^ (qr & 15)) * 16));
-  // part 0: -W, 1: Q, 2: P (8 KiB), 3: K^T and the decays
-  auto load_stage = [&](int cc, int st, int part) {
+  constexpr int GMW = 36 / NW;  // 16-byte pieces of the 576 decay bytes per wave
+  static_assert(36 % NW == 0, "decays split evenly over the waves");
+  // op 0: -W, 1: Q, 2: P (8 KiB) and the decays, 3: K^T, 4: this
+  // workgroup's U~ columns ([rt][16-column tile] blocks)
+  auto load_part = [&](int cc, int st, int op) {
     const int64_t ch = bh * nc + cc;
     unsigned char* sb = lds + opaque_sgpr(st * SCH_STAGE);
+    if (op == 4) {
+      const unsigned char* ub = reinterpret_cast<const unsigned char*>(ws.ut + ch * 4 * C::NT * 256);
+#pragma unroll
+      for (int i = 0; i < 4 * NV; ++i) {
+        const int j = NW * i + w;  // block: row tile j / (NV NW), local column tile j % (NV NW)
+        const int rt = j / (NV * NW), k = j % (NV * NW);
+        gload_lds16_s(ub + (rt * C::NT + NV * NW * part + k) * 1024, (uint32_t)(lane * 16), sb + SCH_UT + j * 1024);
+      }
+      return;
+    }
     const unsigned char* src;
     uint32_t off = off_lin;
     int dst;
-    if (part == 0) {
+    if (op == 0) {
       src = reinterpret_cast<const unsigned char*>(ws.wn + ch * C::WN);
       dst = SCH_WN;
-    } else if (part == 1) {
+    } else if (op == 1) {
       src = reinterpret_cast<const unsigned char*>(qh + (int64_t)cc * CHUNK * D);
       off = off_q;
       dst = SCH_Q;
-    } else if (part == 2) {
+    } else if (op == 2) {
       src = reinterpret_cast<const unsigned char*>(ws.pm + ch * C::PM);
       dst = SCH_PM;
     } else {
       src = reinterpret_cast<const unsigned char*>(ws.kt + ch * C::KT);
       dst = SCH_KT;
     }
-    const int nb = part == 2 ? NB / 2 : NB;  // P: 8 KiB
+    const int nb = op == 2 ? NB / 2 : NB;  // P: 8 KiB
 #pragma unroll
     for (int i = 0; i < NB; ++i)
       if (i < nb) gload_lds16_s(src + i * NW * 1024, off, sb + dst + (NW * i + w) * 1024);
-    if (part == 3 && w == 0 && lane < 36)  // 576 bytes of decays
-      gload_lds16_s(ws.gm + ch * C::GM, (uint32_t)(lane * 16), sb + SCH_GM);
+    if (op == 2 && lane < GMW)  // 576 bytes of decays, a share per wave
+      gload_lds16_s(reinterpret_cast<const unsigned char*>(ws.gm + ch * C::GM) + w * GMW * 16, (uint32_t)(lane * 16),
+                    sb + SCH_GM + w * GMW * 16);
   };
-  // this wave's U~ columns of chunk cc, accumulator order [rt][nn]
-  // (uniform base + 32-bit lane offset: the compiler can use the SGPR-base
-  // forms and needs no 64-bit address per load or store)
-  const uint32_t ut_off = (uint32_t)(nt0 * 256 + lane * 4);
-  auto load_ut = [&](int cc, f32x4 (&u)[4][NV]) {
-    const float* ub = ws.ut + (bh * nc + cc) * 4 * C::NT * 256;
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-      for (int nn = 0; nn < NV; ++nn)
-        u[rt][nn] = *reinterpret_cast<const f32x4*>(ub + (ut_off + (uint32_t)((rt * C::NT + nn) * 256)));
-  };
+  // DMA operations a wave issues per part
+  constexpr int N_W = NB, N_Q = NB, N_U = 4 * NV, N_P = NB / 2 + 1, N_KT = NB;
+  static_assert(N_W + N_Q + N_U + N_P + N_KT + 16 * NV < 64, "vmcnt range");
   const uint32_t o_off = (uint32_t)(4 * g * D + dv0 + c);
   auto store_o = [&](int cc, const f32x4 (&o)[4][NV]) {
     To* ob = oh + (int64_t)cc * CHUNK * D;
@@ -792,7 +799,6 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW)
 #pragma unroll
         for (int i = 0; i < 4; ++i) ob[o_off + (uint32_t)((16 * rt + i) * D + 16 * nn)] = from_f32<To>(o[rt][nn][i]);
   };
-
   // Operand fragments from LDS are read one group ahead of the products that
   // use them (sched_barrier fences pin that order: left free, the scheduler
   // hoists every read of the chunk and runs out of registers; fenced without a
@@ -827,26 +833,25 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW)
   };
   auto fence = []() { __builtin_amdgcn_sched_barrier(0); };
 
-  // chunk cc from stage st: u holds its U~ on entry (U afterwards), u_nxt
-  // receives the next chunk's U~; o_prev holds the previous chunk's outputs on
-  // entry (stored here, a whole chunk before the wait that covers the stores)
-  // and o receives this chunk's
-  auto step = [&](int cc, int st, f32x4 (&u)[4][NV], f32x4 (&u_nxt)[4][NV], f32x4 (&o)[4][NV],
-                  f32x4 (&o_prev)[4][NV]) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this chunk's loads (and older stores) are done
-    lds_barrier();                       // ... for every wave; every wave is done with chunk cc - 1
-    // pin this chunk's U~ ahead of the next chunk's loads
+  // chunk cc from stage st.  Order of the loads for chunk cc + 1 (issued
+  // during chunk cc): -W, Q, U~, P and the decays, spread over the first half;
+  // K^T last, after this chunk's K^T is in.  So the wait at the top of a chunk
+  // leaves that chunk's K^T in flight (N_KT), and the state update waits for
+  // it behind everything issued after it.  o_prev holds the previous chunk's
+  // outputs on entry (stored here); o receives this chunk's.
+  auto step = [&](int cc, int st, f32x4 (&o)[4][NV], f32x4 (&o_prev)[4][NV]) {
+    wait_vmcnt<N_KT>();  // all of chunk cc's operands but K^T (and older stores) are in
+    lds_barrier();       // ... for every wave; every wave is done with chunk cc - 1
+    const unsigned char* sb = lds + opaque_sgpr(st * SCH_STAGE);
+    f32x4 u[4][NV];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-      for (int nn = 0; nn < NV; ++nn) asm volatile("" : "+v"(u[rt][nn]));
+      for (int nn = 0; nn < NV; ++nn)
+        u[rt][nn] = *reinterpret_cast<const f32x4*>(sb + SCH_UT + ((rt * NV * NW + NV * w + nn) * 64 + lane) * 16);
     if (cc > 0) store_o(cc - 1, o_prev);  // outputs of chunk cc - 1
-    // The next chunk's loads are spread over this one: a CU moves only a few
-    // tens of bytes per clock from L2, and issuing all ~96 KiB at once stalls
-    // the wave for the whole transfer instead of overlapping it with compute.
     const bool more = cc + 1 < nc;
-    if (more) load_stage(cc + 1, st ^ 1, 0);
-    const unsigned char* sb = lds + opaque_sgpr(st * SCH_STAGE);
+    if (more) load_part(cc + 1, st ^ 1, 0);
     const float* gm = reinterpret_cast<const float*>(sb + SCH_GM);
     const bool lin = rl[cc] == 1;
 
@@ -870,8 +875,9 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW)
     for (int rt = 0; rt < 4; ++rt) {
       if (rt < 3) read_a(sb, rt + 1, fa[(rt + 1) & 1]);
       else read_p(sb, 0, fp[0]);
-      if (more && rt == 1) load_stage(cc + 1, st ^ 1, 1);
-      if (more && rt == 3) load_stage(cc + 1, st ^ 1, 2);
+      if (more && rt == 0) load_part(cc + 1, st ^ 1, 1);
+      if (more && rt == 1) load_part(cc + 1, st ^ 1, 4);
+      if (more && rt == 2) load_part(cc + 1, st ^ 1, 2);
       fence();
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
@@ -912,11 +918,15 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW)
     FragK fk[2];
 #pragma unroll
     for (int gp = 0; gp < 2; ++gp) {
-      if (gp == 0) read_p(sb, 2, fp[1]);
-      else read_k(sb, 0, fk[0]);
-      if (more && gp == 1) {
-        load_stage(cc + 1, st ^ 1, 3);
-        load_ut(cc + 1, u_nxt);
+      if (gp == 0) {
+        read_p(sb, 2, fp[1]);
+      } else {
+        // this chunk's K^T: everything issued after it may stay in flight
+        if (more) wait_vmcnt<N_W + N_Q + N_U + N_P>();
+        else wait_vmcnt<0>();
+        lds_barrier();
+        if (more) load_part(cc + 1, st ^ 1, 3);
+        read_k(sb, 0, fk[0]);
       }
       fence();
 #pragma unroll
@@ -946,17 +956,20 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW)
     }
   };
 
-  f32x4 utA[4][NV], utB[4][NV], oA[4][NV], oB[4][NV];
-#pragma unroll
-  for (int part = 0; part < 4; ++part) load_stage(0, 0, part);
-  load_ut(0, utA);
+  f32x4 oA[4][NV], oB[4][NV];
+  // prologue in the order the chunk loop issues: K^T last
+  load_part(0, 0, 0);
+  load_part(0, 0, 1);
+  load_part(0, 0, 4);
+  load_part(0, 0, 2);
+  load_part(0, 0, 3);
   int cc = 0;
   for (; cc + 2 <= nc; cc += 2) {
-    step(cc, 0, utA, utB, oA, oB);
-    step(cc + 1, 1, utB, utA, oB, oA);
+    step(cc, 0, oA, oB);
+    step(cc + 1, 1, oB, oA);
   }
   const bool odd = cc < nc;
-  if (odd) step(cc, 0, utA, utB, oA, oB);
+  if (odd) step(cc, 0, oA, oB);
   // outputs of the last chunk
   if (odd)
     store_o(nc - 1, oA);
