@@ -374,7 +374,9 @@ __global__ void __launch_bounds__(256, 2)
       for (int i = 0; i < 4; ++i) Ks[(16 * w + 4 * g + i) * C::KP + 16 * n + c] = from_f32<T>(-wa[n][i]);
   }
   // K^T fragments: rows = d, contraction over tokens (KMAP_ACC); exact copies
-  // of K (the exp(g_C - g) row scale is applied to U by the scan)
+  // of K (the exp(g_C - g) row scale is applied to U by the scan).  The
+  // head-form scan reads K itself (transposed LDS reads) and needs none.
+  if constexpr (!scan_head_form<T, D>())
   for (int f = w; f < C::NT * 2; f += 4) {
     const int n = f >> 1, k2 = f & 1;
     store8<T>(ws.kt + ((ch * C::NT + n) * 2 + k2) * 512 + lane * 8,
@@ -655,7 +657,7 @@ __global__ void __launch_bounds__(256, 1)
 constexpr int SCH_WN = 0;              // -W fragments [rt 4][ks 4][lane][8]
 constexpr int SCH_Q = 16384;           // Q rows, 16-byte chunk q of row r at slot q ^ (r & 15)
 constexpr int SCH_PM = 2 * 16384;      // P fragments (bf16) [rt 4][k2 2][lane][8]
-constexpr int SCH_KT = SCH_PM + 8192;  // K^T fragments [dt 8][k2 2][lane][8]
+constexpr int SCH_KT = SCH_PM + 8192;  // K rows, 16-byte chunk q of row r at slot q ^ ((r & 7) << 1)
 constexpr int SCH_UT = SCH_KT + 16384; // the workgroup's U~ columns (fp32 accumulator order) [rt 4][tile 4][lane][4]
 constexpr int SCH_GM = SCH_UT + 16384; // gamma[64], gamma_C at 64, exp(g_C - g)[64] at 80 (fp32)
 constexpr int SCH_STAGE = SCH_GM + 576;
@@ -683,7 +685,8 @@ __device__ __forceinline__ Frag<bf16> pack_acc2(const f32x4& a, const f32x4& b) 
 // VALU touch of the state)
 template <typename To, int NW, int NSPLIT>
 __global__ void __launch_bounds__(64 * NW, 8 / NW)
-    k_gdn_scan_head(const bf16* __restrict__ q, const int32_t* __restrict__ route, GdnWs<bf16, 128> ws,
+    k_gdn_scan_head(const bf16* __restrict__ q, const bf16* __restrict__ k, const int32_t* __restrict__ route,
+                    GdnWs<bf16, 128> ws,
                     const float* __restrict__ S_init, To* __restrict__ o_gdn, float* __restrict__ S_final,
                     int H, int L, int G) {
   constexpr int D = 128;
@@ -713,6 +716,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW)
   const int grp = (G == 1) ? 0 : h;
   const int32_t* rt_g = route + ((int64_t)b * G + grp) * nc;
   const bf16* qh = q + bh * L * D;
+  const bf16* kh = k + bh * L * D;
   To* oh = o_gdn + bh * L * D;
   const int lane = lane_id(), w = wave_id();
   const int g = lane >> 4, c = lane & 15;
@@ -739,14 +743,16 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW)
   // that the waits below can count them).  Wave w loads the 1 KiB blocks
   // NW i + w of each 16 KiB operand; for Q, LDS position e = 64 blk + lane
   // holds 16-byte chunk (e & 15) ^ (r & 15) of row r = e / 16, and r & 15 does
-  // not depend on i.  Per wave: NB blocks each of -W, Q and K^T, 4 NV of U~,
-  // NB / 2 of P and one partial block of the decays.
+  // not depend on i; K likewise with slot (e & 15) ^ ((r & 7) << 1).  Per
+  // wave: NB blocks each of -W, Q and K, 4 NV of U~, NB / 2 of P and one
+  // partial block of the decays.
   const uint32_t off_lin = (uint32_t)(w * 1024 + lane * 16);
   const int qr = 4 * w + (lane >> 4);
   const uint32_t off_q = (uint32_t)(w * 1024 + (lane >> 4) * 256 + (((lane & 15) ^ (qr & 15)) * 16));
+  const uint32_t off_k = (uint32_t)(w * 1024 + (lane >> 4) * 256 + (((lane & 15) ^ ((qr & 7) << 1)) * 16));
   constexpr int GMW = 36 / NW;  // 16-byte pieces of the 576 decay bytes per wave
   static_assert(36 % NW == 0, "decays split evenly over the waves");
-  // op 0: -W, 1: Q, 2: P (8 KiB) and the decays, 3: K^T, 4: this
+  // op 0: -W, 1: Q, 2: P (8 KiB) and the decays, 3: K, 4: this
   // workgroup's U~ columns ([rt][16-column tile] blocks)
   auto load_part = [&](int cc, int st, int op) {
     const int64_t ch = bh * nc + cc;
@@ -756,8 +762,8 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW)
 #pragma unroll
       for (int i = 0; i < 4 * NV; ++i) {
         const int j = NW * i + w;  // block: row tile j / (NV NW), local column tile j % (NV NW)
-        const int rt = j / (NV * NW), k = j % (NV * NW);
-        gload_lds16_s(ub + (rt * C::NT + NV * NW * part + k) * 1024, (uint32_t)(lane * 16), sb + SCH_UT + j * 1024);
+        const int rt = j / (NV * NW), tl = j % (NV * NW);
+        gload_lds16_s(ub + (rt * C::NT + NV * NW * part + tl) * 1024, (uint32_t)(lane * 16), sb + SCH_UT + j * 1024);
       }
       return;
     }
@@ -775,7 +781,8 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW)
       src = reinterpret_cast<const unsigned char*>(ws.pm + ch * C::PM);
       dst = SCH_PM;
     } else {
-      src = reinterpret_cast<const unsigned char*>(ws.kt + ch * C::KT);
+      src = reinterpret_cast<const unsigned char*>(kh + (int64_t)cc * CHUNK * D);
+      off = off_k;
       dst = SCH_KT;
     }
     const int nb = op == 2 ? NB / 2 : NB;  // P: 8 KiB
@@ -789,32 +796,26 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW)
   // DMA operations a wave issues per part
   constexpr int N_W = NB, N_Q = NB, N_U = 4 * NV, N_P = NB / 2 + 1, N_KT = NB;
   static_assert(N_W + N_Q + N_U + N_P + N_KT + 16 * NV < 64, "vmcnt range");
-  const uint32_t o_off = (uint32_t)(4 * g * D + dv0 + c);
+  // outputs: a uniform base per store plus one 32-bit byte offset per lane
+  // (the SGPR-base store form; 64-bit lane addresses per store cost registers)
+  const uint32_t o_boff = (uint32_t)((4 * g * D + dv0 + c) * sizeof(To));
   auto store_o = [&](int cc, const f32x4 (&o)[4][NV]) {
-    To* ob = oh + (int64_t)cc * CHUNK * D;
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
       for (int nn = 0; nn < NV; ++nn)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ob[o_off + (uint32_t)((16 * rt + i) * D + 16 * nn)] = from_f32<To>(o[rt][nn][i]);
+        for (int i = 0; i < 4; ++i) {
+          unsigned char* base =
+              reinterpret_cast<unsigned char*>(oh + (int64_t)cc * CHUNK * D + (16 * rt + i) * D + 16 * nn);
+          *reinterpret_cast<To*>(base + o_boff) = from_f32<To>(o[rt][nn][i]);
+        }
   };
-  // Operand fragments from LDS are read one group ahead of the products that
-  // use them (sched_barrier fences pin that order: left free, the scheduler
-  // hoists every read of the chunk and runs out of registers; fenced without a
-  // lead, every group waits out the LDS latency).
-  struct FragA { Frag<bf16> w[4], q[4]; };  // -W and Q for one 16-token row tile, all 4 d steps
-  auto read_a = [&](const unsigned char* sb, int rt, FragA& f) {
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      f.w[ks] = load8<bf16>(reinterpret_cast<const bf16*>(sb + SCH_WN + ((rt * 4 + ks) * 64 + lane) * 16));
-      // Q row 16 rt + c, columns 32 ks + 4g .. +3 and 32 ks + 16 + 4g .. +3
-      const unsigned char* qrow = sb + SCH_Q + (16 * rt + c) * 256;
-      const int q1 = 4 * ks + (g >> 1), q2 = q1 + 2, half = (g & 1) * 8;
-      f.q[ks] = ld4x2<bf16>(reinterpret_cast<const bf16*>(qrow + ((q1 ^ c) * 16) + half),
-                            reinterpret_cast<const bf16*>(qrow + ((q2 ^ c) * 16) + half));
-    }
-  };
+  // Operand fragments from LDS are read ahead of the products that use them
+  // (two (row tile, d step) steps ahead for -W and Q, two d tiles ahead for
+  // K^T, a row-tile pair ahead for P); sched_barrier fences pin that order:
+  // left free, the scheduler hoists every read of the chunk and runs out of
+  // registers; fenced without a lead, every step waits out the LDS latency.
   struct FragP { Frag<bf16> p[2][2]; };  // P for two row tiles: [tile][k2]
   auto read_p = [&](const unsigned char* sb, int rt0, FragP& f) {
 #pragma unroll
@@ -823,13 +824,31 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW)
       for (int k2 = 0; k2 < 2; ++k2)
         f.p[t][k2] = load8<bf16>(reinterpret_cast<const bf16*>(sb + SCH_PM + (((rt0 + t) * 2 + k2) * 64 + lane) * 16));
   };
-  struct FragK { Frag<bf16> k[4][2]; };  // K^T for four d tiles: [tile][k2]
-  auto read_k = [&](const unsigned char* sb, int dt0, FragK& f) {
+  auto read_wq = [&](const unsigned char* sb, int s_, Frag<bf16>& fw, Frag<bf16>& fq) {
+    const int rt = s_ >> 2, ks = s_ & 3;
+    fw = load8<bf16>(reinterpret_cast<const bf16*>(sb + SCH_WN + ((rt * 4 + ks) * 64 + lane) * 16));
+    const unsigned char* qrow = sb + SCH_Q + (16 * rt + c) * 256;
+    const int q1 = 4 * ks + (g >> 1), q2 = q1 + 2, half = (g & 1) * 8;
+    fq = ld4x2<bf16>(reinterpret_cast<const bf16*>(qrow + ((q1 ^ c) * 16) + half),
+                     reinterpret_cast<const bf16*>(qrow + ((q2 ^ c) * 16) + half));
+  };
+  // K^T fragments of d tile dt (rows d = 16 dt + c, tokens 32 k2 + 4g + j and
+  // 32 k2 + 16 + 4g + j) from the row-major K by transposed reads, which swap
+  // 4 x 4 blocks of 16-bit values across each 16-lane group: lane c of group g
+  // reads token row 32 k2 + 4g + c / 4 (+16), columns 16 dt + 4 (c % 4) .. +3
+  auto read_k1 = [&](const unsigned char* sb, int dt, Frag<bf16> (&f)[2]) {
+    const unsigned char* kl = sb + SCH_KT;
+    const int colq = (16 * dt + 4 * (c & 3)) >> 3;  // 16-byte chunk of the 4 columns
+    const int half = (c & 1) * 8;                    // byte offset inside it
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2)
-        f.k[t][k2] = load8<bf16>(reinterpret_cast<const bf16*>(sb + SCH_KT + (((dt0 + t) * 2 + k2) * 64 + lane) * 16));
+    for (int k2 = 0; k2 < 2; ++k2) {
+      const int r0 = 32 * k2 + 4 * g + (c >> 2), r1 = r0 + 16;
+      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4i16*)(kl + r0 * 256 + ((colq ^ ((r0 & 7) << 1)) * 16) + half));
+      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4i16*)(kl + r1 * 256 + ((colq ^ ((r1 & 7) << 1)) * 16) + half));
+      f[k2].v = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
   };
   auto fence = []() { __builtin_amdgcn_sched_barrier(0); };
 
@@ -866,26 +885,27 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW)
 #pragma unroll
       for (int nn = 0; nn < NV; ++nn) o[rt][nn] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // U = U~ - W S  and  Q S, one row tile per group
-    FragA fa[2];
+    // U = U~ - W S  and  Q S: 16 (row tile, d step) steps, operands read two
+    // steps ahead
+    Frag<bf16> fw[3], fq[3];
     FragP fp[2];
-    read_a(sb, 0, fa[0]);
+    read_wq(sb, 0, fw[0], fq[0]);
+    read_wq(sb, 1, fw[1], fq[1]);
     fence();
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      if (rt < 3) read_a(sb, rt + 1, fa[(rt + 1) & 1]);
-      else read_p(sb, 0, fp[0]);
-      if (more && rt == 0) load_part(cc + 1, st ^ 1, 1);
-      if (more && rt == 1) load_part(cc + 1, st ^ 1, 4);
-      if (more && rt == 2) load_part(cc + 1, st ^ 1, 2);
+    for (int s_ = 0; s_ < 16; ++s_) {
+      const int rt = s_ >> 2, ks = s_ & 3;
+      if (s_ + 2 < 16) read_wq(sb, s_ + 2, fw[(s_ + 2) % 3], fq[(s_ + 2) % 3]);
+      if (s_ == 13) read_p(sb, 0, fp[0]);
+      if (more && s_ == 3) load_part(cc + 1, st ^ 1, 1);
+      if (more && s_ == 7) load_part(cc + 1, st ^ 1, 4);
+      if (more && s_ == 11) load_part(cc + 1, st ^ 1, 2);
       fence();
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int nn = 0; nn < NV; ++nn) {
-          mma(u[rt][nn], fa[rt & 1].w[ks], bs[ks][nn]);
-          mma(o[rt][nn], fa[rt & 1].q[ks], bs[ks][nn]);
-        }
+      for (int nn = 0; nn < NV; ++nn) {
+        mma(u[rt][nn], fw[s_ % 3], bs[ks][nn]);
+        mma(o[rt][nn], fq[s_ % 3], bs[ks][nn]);
+      }
       fence();
     }
     // branch-free rollback: a softmax-routed chunk updates with decay 1 and a
@@ -915,7 +935,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW)
       for (int nn = 0; nn < NV; ++nn) o[rt][nn] *= gam;
     }
     // O += P U, two row tiles per group
-    FragK fk[2];
+    Frag<bf16> fk[3][2];
 #pragma unroll
     for (int gp = 0; gp < 2; ++gp) {
       if (gp == 0) {
@@ -926,7 +946,8 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW)
         else wait_vmcnt<0>();
         lds_barrier();
         if (more) load_part(cc + 1, st ^ 1, 3);
-        read_k(sb, 0, fk[0]);
+        read_k1(sb, 0, fk[0]);
+        read_k1(sb, 1, fk[1]);
       }
       fence();
 #pragma unroll
@@ -943,15 +964,13 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW)
 #pragma unroll
       for (int nn = 0; nn < NV; ++nn) sm[dt][nn] *= gce;
 #pragma unroll
-    for (int gk = 0; gk < 2; ++gk) {
-      if (gk == 0) read_k(sb, 4, fk[1]);
+    for (int dt = 0; dt < 8; ++dt) {
+      if (dt + 2 < 8) read_k1(sb, dt + 2, fk[(dt + 2) % 3]);
       fence();
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
+      for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-          for (int nn = 0; nn < NV; ++nn) mma(sm[4 * gk + t][nn], fk[gk].k[t][k2], be[k2][nn]);
+        for (int nn = 0; nn < NV; ++nn) mma(sm[dt][nn], fk[dt % 3][k2], be[k2][nn]);
       fence();
     }
   };
@@ -1034,7 +1053,7 @@ hipError_t launch_gdn(const T* q, const T* k, const T* v, const float* alpha, co
     const size_t lds = SCH_ROUTE + ((size_t)nc * 4 + 255) / 256 * 256;
     hipLaunchKernelGGL((k_gdn_scan_head<To, SCH_NW, SCH_NSPLIT>), dim3((unsigned)(B * H * SCH_NSPLIT)), dim3(64 * SCH_NW),
                        lds, st_scan,
-                       (const bf16*)q,
+                       (const bf16*)q, (const bf16*)k,
                        route, ws, S_init, o_gdn, S_final, H, L, G);
   } else {
     hipLaunchKernelGGL((k_gdn_scan<T, To, D, DVT, SCAN_NS>), dim3((unsigned)(B * H * (D / DVT))), dim3(256), 0,

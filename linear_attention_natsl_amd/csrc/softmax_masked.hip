@@ -366,8 +366,6 @@ constexpr int SM2_STAGES = 4;
 constexpr int SM2_TILE_BYTES = 2 * CHUNK * 128 * 2;  // K + V, bf16, D = 128
 constexpr int SM2_LDS = SM2_STAGES * SM2_TILE_BYTES + 4 * 1024;  // + sel list (up to 1024 chunks)
 
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-
 __device__ __forceinline__ int sm2_kslot(int r, int q) { return q ^ (r & 15); }
 __device__ __forceinline__ int sm2_vslot(int r, int q) { return q ^ ((r & 7) << 1); }
 
