@@ -49,19 +49,25 @@ struct GdnCfg {
   static constexpr int LTP = CHUNK + 1;                 // fp32 pitch of L / T
   static constexpr int KF = D / 32;
   static constexpr int NT = D / 16;                     // 16-wide column tiles of D
-  // LDS layout of the prep kernel (bytes)
-  static constexpr int OFF_KS = 0;
+  // LDS layout of the prep kernel (bytes).  The bf16, D = 128 form (the one
+  // the head-form scan reads) keeps the K rows, the inverse's block scratch
+  // and the K / V key-group copies in one region, live one after the other
+  // (K and V wait in registers until the inverse is done), so that three
+  // workgroups fit in a CU's 160 KiB instead of two.
+  static constexpr bool ALIAS = sizeof(T) == 2 && D == 128;
   static constexpr int RL = kg_row<T, D>();             // padded key-group row (columns)
-  static constexpr int OFF_KG = OFF_KS + CHUNK * KP * (int)sizeof(T);
-  static constexpr int OFF_VG = OFF_KG + 16 * RL * 4 * (int)sizeof(T);
-  static constexpr int OFF_LT = OFF_VG + 16 * RL * 4 * (int)sizeof(T);
-  // P staging (before the inverse) and the inverse's block scratch (during it)
-  // share one region
-  static constexpr int OFF_PS = OFF_LT + CHUNK * LTP * 4;
-  static constexpr int OFF_RS = OFF_PS;
-  static constexpr int PS_BYTES = ((CHUNK * PP * (int)sizeof(T) + 15) / 16) * 16;
-  static constexpr int OFF_GL = OFF_PS + (PS_BYTES > 3 * 16 * 17 * 4 ? PS_BYTES : 3 * 16 * 17 * 4);
-  static constexpr int PREP_LDS = OFF_GL + 4 * CHUNK * 4;
+  static constexpr int KS_BYTES = CHUNK * KP * (int)sizeof(T);
+  static constexpr int KG_BYTES = 16 * RL * 4 * (int)sizeof(T);
+  static constexpr int RS_BYTES = 3 * 16 * 17 * 4;
+  static constexpr int OFF_KS = 0;
+  static constexpr int OFF_KG = ALIAS ? 0 : OFF_KS + KS_BYTES;
+  static constexpr int OFF_VG = OFF_KG + KG_BYTES;
+  static constexpr int R0_END = ALIAS ? (KS_BYTES > 2 * KG_BYTES ? KS_BYTES : 2 * KG_BYTES) : OFF_VG + KG_BYTES;
+  static constexpr int OFF_LT = R0_END;
+  static constexpr int OFF_RS = ALIAS ? 0 : OFF_LT + CHUNK * LTP * 4;
+  static constexpr int OFF_GL = ALIAS ? OFF_LT + CHUNK * LTP * 4 : OFF_RS + RS_BYTES;
+  static constexpr int PREP_LDS = OFF_GL + 3 * CHUNK * 4;
+  static_assert(!ALIAS || 3 * PREP_LDS <= 160 * 1024, "three prep workgroups per CU");
   // per chunk-head workspace (elements)
   static constexpr int64_t WN = (int64_t)CHUNK * D;   // T
   static constexpr int64_t UT = (int64_t)CHUNK * D;   // float
@@ -132,7 +138,7 @@ template <typename T, int D> constexpr bool scan_head_form() { return sizeof(T) 
 
 // ---------------------------------------------------------------- prep ----
 template <typename T, int D>
-__global__ void __launch_bounds__(256, 2)
+__global__ void __launch_bounds__(256, (GdnCfg<T, D>::ALIAS ? 3 : 2))
     k_gdn_prep(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                const float* __restrict__ alpha, const float* __restrict__ beta, GdnWs<T, D> ws,
                int L) {
@@ -146,7 +152,6 @@ __global__ void __launch_bounds__(256, 2)
   float* gl = (float*)(lds + C::OFF_GL);  // cumulative log2 decay
   float* bl = gl + CHUNK;                 // beta
   float* gbl = bl + CHUNK;                // beta * gamma
-  float* ekl = gbl + CHUNK;               // exp(g_C - g)
 
   const int nc = L / CHUNK;
   const int64_t ch = bid_x();
@@ -191,23 +196,28 @@ __global__ void __launch_bounds__(256, 2)
     gl[lane] = s;
     bl[lane] = bt;
     gbl[lane] = bt * __builtin_amdgcn_exp2f(s);
-    ekl[lane] = __builtin_amdgcn_exp2f(gC - s);
     ws.gm[ch * C::GM + lane] = __builtin_amdgcn_exp2f(s);
     ws.gm[ch * C::GM + 80 + lane] = __builtin_amdgcn_exp2f(gC - s);
     if (lane == 0) ws.gm[ch * C::GM + 64] = __builtin_amdgcn_exp2f(gC);
   }
-  // K -> row layout and key-group layout, V -> key-group layout
+  // K -> row layout and key-group layout, V -> key-group layout (the
+  // key-group copies only after the inverse when they share the K rows' LDS)
+  auto store_kv_groups = [&]() {
+    if (t < TASKS) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        st4<T>(Kg + kg_index<C::RL>(kg, col + j), to_f32(frag_get<T>(kr[0], j)), to_f32(frag_get<T>(kr[1], j)),
+               to_f32(frag_get<T>(kr[2], j)), to_f32(frag_get<T>(kr[3], j)));
+        st4<T>(Vg + kg_index<C::RL>(kg, col + j), to_f32(frag_get<T>(vr[0], j)), to_f32(frag_get<T>(vr[1], j)),
+               to_f32(frag_get<T>(vr[2], j)), to_f32(frag_get<T>(vr[3], j)));
+      }
+    }
+  };
   if (t < TASKS) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) store8<T>(Ks + (4 * kg + i) * C::KP + col, kr[i]);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      st4<T>(Kg + kg_index<C::RL>(kg, col + j), to_f32(frag_get<T>(kr[0], j)), to_f32(frag_get<T>(kr[1], j)),
-             to_f32(frag_get<T>(kr[2], j)), to_f32(frag_get<T>(kr[3], j)));
-      st4<T>(Vg + kg_index<C::RL>(kg, col + j), to_f32(frag_get<T>(vr[0], j)), to_f32(frag_get<T>(vr[1], j)),
-             to_f32(frag_get<T>(vr[2], j)), to_f32(frag_get<T>(vr[3], j)));
-    }
   }
+  if constexpr (!C::ALIAS) store_kv_groups();
   __syncthreads();
 
   // K K^T rows 16w .. 16w+15, and P^T = K Q^T for the queries 16w .. 16w+15:
@@ -283,31 +293,58 @@ __global__ void __launch_bounds__(256, 2)
     for (int r = 0; r < 16; ++r) LT[(o + r) * C::LTP + o + j] = x[r];
   }
   __syncthreads();
-  // (b) block rows a = 1..3:  T_ab = -T_aa * sum_{b<=m<a} L_am T_mb
+  // (b) block rows a = 1..3:  T_ab = -T_aa * sum_{b<=m<a} L_am T_mb, on fp32
+  // MFMA (16x16x4: in step j lane (g, c) gives A[c][4j + g] and B[4j + g][c],
+  // and holds C[4g + i][c]).  Wave w owns the target block (a, w) of every
+  // round a > w.  All L_am and T_aa fragments a wave needs are read before the
+  // first round writes, so a round's writes (which replace L_ab by T_ab) never
+  // race with reads of the blocks they replace: one barrier per round.
   {
-    const int rr = t >> 4, col = t & 15;
+    float la[3][3][4], ta[3][4];
+#pragma unroll
     for (int a = 1; a < 4; ++a) {
-      for (int bb = 0; bb < a; ++bb) {
-        float acc = 0.f;
-        for (int m = bb; m < a; ++m) {
+      if (w < a) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i)
-            acc += LT[(16 * a + rr) * C::LTP + 16 * m + i] * LT[(16 * m + i) * C::LTP + 16 * bb + col];
-        }
-        Rs[(bb * 16 + rr) * 17 + col] = acc;
+        for (int m = 0; m < 3; ++m)
+          if (m >= w && m < a) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) la[a - 1][m][j] = LT[(16 * a + c) * C::LTP + 16 * m + 4 * j + g];
+          }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ta[a - 1][j] = LT[(16 * a + c) * C::LTP + 16 * a + 4 * j + g];
       }
-      __syncthreads();
-      for (int bb = 0; bb < a; ++bb) {
-        float acc = 0.f;
+    }
+    float* Rw = Rs + w * 16 * 17;  // wave-private 16 x 16 scratch (waves 0..2)
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          acc += LT[(16 * a + rr) * C::LTP + 16 * a + i] * Rs[(bb * 16 + i) * 17 + col];
-        LT[(16 * a + rr) * C::LTP + 16 * bb + col] = -acc;
+    for (int a = 1; a < 4; ++a) {
+      if (w < a) {
+        f32x4 r = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < 3; ++m)
+          if (m >= w && m < a) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              r = __builtin_amdgcn_mfma_f32_16x16x4f32(la[a - 1][m][j], LT[(16 * m + 4 * j + g) * C::LTP + 16 * w + c],
+                                                       r, 0, 0, 0);
+          }
+        // R (accumulator layout) -> B operand layout through the wave's scratch
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Rw[(4 * g + i) * 17 + c] = r[i];
+        f32x4 tt = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          tt = __builtin_amdgcn_mfma_f32_16x16x4f32(ta[a - 1][j], Rw[(4 * j + g) * 17 + c], tt, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) LT[(16 * a + 4 * g + i) * C::LTP + 16 * w + c] = -tt[i];
       }
       __syncthreads();
     }
   }
 
+  if constexpr (C::ALIAS) {  // the inverse's scratch is dead (barrier above)
+    store_kv_groups();
+    __syncthreads();
+  }
   // U~ = T diag(b) V and W = T diag(b gamma) K, rows 16w .. 16w+15
   f32x4 ut[C::NT], wa[C::NT];
 #pragma unroll
