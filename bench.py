@@ -20,7 +20,7 @@ on) during the timed region:
   decode   decode_attn, HBM-bound: the cached K/V bytes it must read / average
            launch time, against 8 TB/s.
 cpu_baseline: the fp64 oracle on a bounded sample (one head: router on all
-chunks, Gated DeltaNet on all tokens, softmax on every 8th query block), the
+chunks, Gated DeltaNet on all tokens, softmax on every 2nd query block), the
 per-head time scaled to all heads.
 """
 import argparse
@@ -317,8 +317,8 @@ def time_decode(args, N, W):
 
 def cpu_baseline(W, O, inp, route, workload):
     """The oracle as it stands, on head 0 of the prefill workload: router on
-    all chunks, Gated DeltaNet over every token, softmax on every 8th 64-row
-    query block; scaled to the whole job."""
+    all chunks, Gated DeltaNet over every token, softmax on every 2nd 64-row
+    query block (about 10-15 s of CPU work); scaled to the whole job."""
     try:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
@@ -332,7 +332,7 @@ def cpu_baseline(W, O, inp, route, workload):
     t0 = time.perf_counter()
     o_gdn, _ = O.gdn_branch(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(inp["alpha"]), sl(inp["beta"]), r)
     t_gdn = time.perf_counter() - t0
-    blocks = list(range(0, wl.nc, 8))
+    blocks = list(range(0, wl.nc, 2))
     t0 = time.perf_counter()
     o_sm = O.softmax_branch(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), r, query_blocks=blocks)
     t_sm = time.perf_counter() - t0
@@ -383,6 +383,129 @@ def achievable_peaks():
                 copy_1GiB_gbs=round(copy_gbs, 1), copy_frac_of_peak=round(copy_gbs / PEAK_HBM_GBS, 4))
 
 
+PROFILE_CMD = "python3 bench.py --steps 10 --warmup 2 --no-cpu --no-calib --decode-steps 20 --profile-copy"
+KERNEL_NAMES = [  # substring of the kernel symbol -> short name
+    ("k_softmax_v2", "softmax_masked"), ("k_route", "route"), ("k_compact", "compact"), ("k_gdn_prep", "gdn_prep"),
+    ("k_gdn_scan", "gdn_scan"), ("k_merge", "merge"), ("k_decode_route", "decode_route"),
+    ("k_decode_gdn", "decode_gdn"), ("k_decode_attn", "decode_attn"), ("k_decode_combine", "decode_combine"),
+    ("k_decode_commit", "decode_commit"), ("k_handoff_state", "handoff_state"), ("k_handoff_kv", "handoff_kv"),
+    ("k_sm_bwd_delta", "sm_bwd_delta"), ("k_sm_bwd_dq", "sm_bwd_dq"), ("k_sm_bwd_dkdv", "sm_bwd_dkdv"),
+    ("AUnaryFunctor<float, float", "calib_mul_256MiB"),
+]
+
+
+def summarize_profiles(d):
+    """Writes the profiles/ summaries from the rocprofv3 runs of PROFILE_CMD
+    under directory d: prof_trace/ (--kernel-trace --stats, whose stdout went
+    to prof_trace.log), prof_fetch/ (--pmc FETCH_SIZE), prof_write/ (--pmc
+    WRITE_SIZE).  Counters are KiB per dispatch, scaled by what they read for
+    the 256 MiB read + 256 MiB write calibration kernel of --profile-copy."""
+    import csv
+    import glob
+
+    def short(name):
+        for sub, n in KERNEL_NAMES:
+            if sub in name:
+                return n
+        return None
+
+    def find(sub, fname):
+        hits = glob.glob(os.path.join(d, sub, "**", fname), recursive=True)
+        if not hits:
+            raise SystemExit(f"no {fname} under {os.path.join(d, sub)}")
+        return hits[0]
+
+    stats = {}
+    for r in csv.DictReader(open(find("prof_trace", "*kernel_stats.csv"))):
+        n = short(r["Name"])
+        if n:
+            stats[n] = dict(calls=int(r["Calls"]), avg_us=float(r["AverageNs"]) / 1e3, min_us=float(r["MinNs"]) / 1e3,
+                            max_us=float(r["MaxNs"]) / 1e3, symbol=r["Name"])
+    ctr = {}
+    for key, sub in (("fetch", "prof_fetch"), ("write", "prof_write")):
+        vals = {}
+        for r in csv.DictReader(open(find(sub, "*counter_collection.csv"))):
+            n = short(r["Kernel_Name"])
+            if n:
+                vals.setdefault(n, []).append(float(r["Counter_Value"]) * 1024.0)
+        ctr[key] = {n: sum(v) / len(v) for n, v in vals.items()}
+    calib = 256 * 2 ** 20
+    fscale = calib / ctr["fetch"]["calib_mul_256MiB"]
+    wscale = calib / ctr["write"]["calib_mul_256MiB"]
+    bench_line = None
+    for line in open(os.path.join(d, "prof_trace.log")):
+        if line.startswith('{"metric"'):
+            bench_line = json.loads(line)
+    if bench_line is None:
+        raise SystemExit("no bench line in prof_trace.log")
+    cmds = "\n".join(f"    rocprofv3 {a} --output-format csv -d <dir>/{b} -o b -- {PROFILE_CMD}" for a, b in
+                     (("--kernel-trace --stats", "prof_trace"), ("--pmc FETCH_SIZE", "prof_fetch"),
+                      ("--pmc WRITE_SIZE", "prof_write")))
+    scaling = (f"Counter scaling: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by what they read for a plain "
+               f"elementwise kernel that reads 256 MiB and writes 256 MiB (torch.mul over 64 Mi fp32, run by "
+               f"`--profile-copy` in the same process): FETCH_SIZE x {fscale:.3f}, WRITE_SIZE x {wscale:.3f}.")
+    rd = lambda n: ctr["fetch"].get(n, 0.0) * fscale
+    wr = lambda n: ctr["write"].get(n, 0.0) * wscale
+    out = os.path.join(ROOT, "profiles")
+    # all kernels
+    lines = ["# All kernels of one bench run (long prefill forward + decode step + handoff + softmax-branch gradient)", "",
+             "Commands (from the repository root on one MI355X; rocprofv3 writes CSV; the three runs are separate):", "",
+             cmds, "",
+             f"bench.py reported {bench_line['ms_per_step']} ms per forward step ({bench_line['value']:.0f} tokens/s) "
+             f"and {bench_line['decode']['ms_per_step']} ms per decode step in the traced run. bench.py first runs each "
+             f"step untimed for 0.3 s (clock settle), so the dispatch counts include those steps.", "",
+             "| kernel | calls | avg us | min us | max us | HBM read MB/launch | HBM write MB/launch |",
+             "|---|---|---|---|---|---|---|"]
+    for _, n in KERNEL_NAMES:
+        if n in stats:
+            st = stats[n]
+            lines.append(f"| {n} | {st['calls']} | {st['avg_us']:.1f} | {st['min_us']:.1f} | {st['max_us']:.1f} | "
+                         f"{rd(n) / 1e6:.1f} | {wr(n) / 1e6:.1f} |")
+    lines += ["", scaling,
+              "The forward's kernels overlap (the Gated DeltaNet prep and scan run on a helper stream beside routing and "
+              "softmax_masked), so their durations do not add up to the step time."]
+    with open(os.path.join(out, "kernels_long_and_decode.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    # roofline kernels
+    for n, wl, srcs, title, bench_part in (
+            ("softmax_masked", "long", ("softmax_masked.hip", "common.hpp"),
+             "softmax_masked on the long prefill (B=1 H=16 L=32768 D=128, bf16, 25% softmax chunks)", bench_line),
+            ("decode_attn", "decode", ("decode.hip", "common.hpp"),
+             "decode_attn on the decode step (B=64 H=16 D=128, about 8192 cached rows per head, bf16)",
+             bench_line["decode"])):
+        h = source_hash(*srcs)
+        rf = bench_part["roofline"]
+        st = stats[n]
+        c = dict(kernel=n, workload=wl, source_hash=h, hbm_bytes_per_launch=int(rd(n) + wr(n)),
+                 hbm_read_bytes=int(rd(n)), hbm_write_bytes=int(wr(n)), fetch_scale=fscale, write_scale=wscale,
+                 command=PROFILE_CMD)
+        with open(os.path.join(out, f"{n}_{wl}_counters.txt"), "w") as f:
+            json.dump(c, f, indent=1)
+        if rf["unit"] == "TFLOP/s":
+            work = f"| algorithmic FLOPs per launch | {rf['flops_per_launch']:.3e} |"
+            ach = rf["flops_per_launch"] / (st["avg_us"] * 1e-6) / 1e12
+            achieved = f"| achieved (trace average) | {ach:.1f} TFLOP/s = {100 * ach / rf['peak']:.1f}% of {rf['peak']:.0f} TFLOP/s |"
+        else:
+            work = f"| algorithmic bytes per launch | {rf['bytes_per_launch'] / 1e6:.1f} MB |"
+            ach = rf["bytes_per_launch"] / (st["avg_us"] * 1e-6) / 1e9
+            achieved = f"| achieved (trace average) | {ach:.0f} GB/s = {100 * ach / rf['peak']:.1f}% of {rf['peak']:.0f} GB/s |"
+        lines = [f"# {title}", "", "Commands:", "", cmds, "",
+                 f"Kernel `{st['symbol']}`, source hash {h}.", "",
+                 "| figure | value |", "|---|---|",
+                 f"| dispatches | {st['calls']} |",
+                 f"| average duration (rocprofv3 kernel trace) | {st['avg_us']:.1f} us |",
+                 f"| average duration (bench.py HIP events over its timed steps, same run) | {rf['avg_launch_us']:.1f} us |",
+                 work, achieved,
+                 f"| HBM read per launch (FETCH_SIZE scaled) | {rd(n) / 1e6:.1f} MB |",
+                 f"| HBM write per launch (WRITE_SIZE scaled) | {wr(n) / 1e6:.1f} MB |", "", scaling]
+        if n == "softmax_masked":
+            lines.append("In the forward pass this kernel shares the GPU with the Gated DeltaNet chunk prep and scan "
+                         "(second stream).")
+        with open(os.path.join(out, f"{n}_{wl}.md"), "w") as f:
+            f.write("\n".join(lines) + "\n")
+    print("wrote", out)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -397,7 +520,12 @@ def main():
     ap.add_argument("--profile-copy", action="store_true",
                     help="first run a plain 256 MiB read + 256 MiB write elementwise kernel three times, "
                          "the known-size reference for scaling FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--summarize-profiles", metavar="DIR", default=None,
+                    help="CPU only: write the profiles/ summaries from the rocprofv3 runs of PROFILE_CMD under DIR")
     args = ap.parse_args()
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
               "(shard over (batch, head) with one process per GPU; see the design notes)", file=sys.stderr)
