@@ -118,6 +118,23 @@ def kernel_table(N, fn, names, reps):
     return out
 
 
+def time_softmax_alone(N, dm, route, t, io_t, reps):
+    """Average duration of the softmax branch's launch on the forward's
+    compaction of `route`, with nothing else on the GPU: events around `reps`
+    back-to-back launches after a settle."""
+    import torch
+    _, sel, nsb, _ = N.route(dm, None, None, route_in=route)
+    call = lambda: N.softmax_masked(dm, t["q"], t["k"], t["v"], sel, nsb, o_dtype=io_t)
+    settle(call)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    return 1000.0 * e0.elapsed_time(e1) / reps
+
+
 def time_handoff(N, dm, route, t, wl, reps=20):
     """The prefill -> decode handoff of this prefill (its routes, K and V) into
     a decode cache sized for its softmax rows: bytes moved = the softmax
@@ -203,6 +220,7 @@ def time_prefill(args, N, W, O):
     kernels = kernel_table(N, call, ("route", "compact", "gdn_prep", "gdn_scan", "softmax_masked", "merge"),
                            max(5, args.steps // 5))
     N.profile_enable(False)
+    sm_alone_us = None if args.no_alone else time_softmax_alone(N, dm, fwd.route, t, io_t, max(10, args.steps // 2))
     handoff = time_handoff(N, dm, fwd.route, t, wl)
     backward = time_softmax_backward(N, dm, t, wl, sm_pairs(fwd.route.cpu().numpy(), wl.H))
     route = fwd.route.cpu().numpy()
@@ -229,7 +247,12 @@ def time_prefill(args, N, W, O):
                     parallelism="single GPU"),
         roofline=dict(bound="mfma", kernel="softmax_masked", achieved=round(achieved, 1), peak=PEAK_BF16_TFLOPS,
                       unit="TFLOP/s", frac=round(achieved / PEAK_BF16_TFLOPS, 4), traffic=traffic,
-                      flops_per_launch=f_sm, avg_launch_us=sm_us),
+                      flops_per_launch=f_sm, avg_launch_us=sm_us,
+                      alone=None if sm_alone_us is None else dict(
+                          avg_launch_us=round(sm_alone_us, 2), achieved=round(f_sm / (sm_alone_us * 1e-6) / 1e12, 1),
+                          frac=round(f_sm / (sm_alone_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                          note="the same launch with the GPU to itself (in the forward it shares the GPU with the "
+                               "Gated DeltaNet prep and scan)")),
         layer=dict(flops_softmax=f_sm, flops_gdn=f_gdn,
                    layer_tflops=round((f_sm + f_gdn) / (dt / args.steps) / 1e12, 1),
                    layer_frac_of_mfma_peak=round((f_sm + f_gdn) / (dt / args.steps) / 1e12 / PEAK_BF16_TFLOPS, 4),
@@ -383,7 +406,7 @@ def achievable_peaks():
                 copy_1GiB_gbs=round(copy_gbs, 1), copy_frac_of_peak=round(copy_gbs / PEAK_HBM_GBS, 4))
 
 
-PROFILE_CMD = "python3 bench.py --steps 10 --warmup 2 --no-cpu --no-calib --decode-steps 20 --profile-copy"
+PROFILE_CMD = "python3 bench.py --steps 10 --warmup 2 --no-cpu --no-calib --no-alone --decode-steps 20 --profile-copy"
 KERNEL_NAMES = [  # substring of the kernel symbol -> short name
     ("k_softmax_v2", "softmax_masked"), ("k_route", "route"), ("k_compact", "compact"), ("k_gdn_prep", "gdn_prep"),
     ("k_gdn_scan", "gdn_scan"), ("k_merge", "merge"), ("k_decode_route", "decode_route"),
@@ -516,6 +539,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-calib", action="store_true", help="skip the achievable-peak GEMM and copy")
+    ap.add_argument("--no-alone", action="store_true",
+                    help="skip timing the softmax branch alone (profiled runs: its launches would mix with the "
+                         "forward's in the kernel trace)")
     ap.add_argument("--check-route", action="store_true")
     ap.add_argument("--profile-copy", action="store_true",
                     help="first run a plain 256 MiB read + 256 MiB write elementwise kernel three times, "

@@ -141,6 +141,7 @@ int nchunks(const natsl_dims* d) { return d->L / 64; }
 struct FwdWs {
   int32_t *route, *sel, *nsb;
   void *o_sm, *o_gdn, *gdn;
+  float* mixd;  // per token z0 - z1 of the mixing scores (softmax branch -> merge)
 };
 size_t fwd_ws(const natsl_dims* d, natsl_dtype branch, FwdWs* w, void* base) {
   const int64_t nc = nchunks(d), BG = (int64_t)d->B * d->route_groups;
@@ -154,6 +155,7 @@ size_t fwd_ws(const natsl_dims* d, natsl_dtype branch, FwdWs* w, void* base) {
   const size_t o_r = take(BG * nc * 4), o_s = take(BG * nc * 4), o_n = take(BG * (nc + 1) * 4);
   const size_t o_sm = take(bsz), o_gd = take(bsz);
   const size_t o_gdn = take(gdn_ws_bytes(d->io == NATSL_BF16, d->Dk, (int64_t)d->B * d->H * nc));
+  const size_t o_mix = take((size_t)d->B * d->H * d->L * 4);
   if (w) {
     char* p = (char*)base;
     w->route = (int32_t*)(p + o_r);
@@ -162,6 +164,7 @@ size_t fwd_ws(const natsl_dims* d, natsl_dtype branch, FwdWs* w, void* base) {
     w->o_sm = p + o_sm;
     w->o_gdn = p + o_gd;
     w->gdn = p + o_gdn;
+    w->mixd = (float*)(p + o_mix);
   }
   return off;
 }
@@ -202,25 +205,25 @@ hipError_t do_route(const natsl_dims* d, const void* x, const float* w, const fl
 template <typename T, typename To>
 hipError_t do_softmax_t(const natsl_dims* d, const void* q, const void* k, const void* v,
                         const int32_t* sel, const int32_t* nsb, void* o, float* lse, hipStream_t st,
-                        const SmPrefix& pre) {
+                        const SmPrefix& pre, const SmMix& mix) {
   if (d->Dk == 64)
     return launch_softmax_masked<T, To, 64>((const T*)q, (const T*)k, (const T*)v, sel, nsb, (To*)o, lse,
-                                            d->B, d->H, d->L, d->route_groups, eff_scale(d), st, pre);
+                                            d->B, d->H, d->L, d->route_groups, eff_scale(d), st, pre, mix);
   return launch_softmax_masked<T, To, 128>((const T*)q, (const T*)k, (const T*)v, sel, nsb, (To*)o, lse,
-                                           d->B, d->H, d->L, d->route_groups, eff_scale(d), st, pre);
+                                           d->B, d->H, d->L, d->route_groups, eff_scale(d), st, pre, mix);
 }
 hipError_t do_softmax(const natsl_dims* d, const void* q, const void* k, const void* v, const int32_t* sel,
                       const int32_t* nsb, void* o, natsl_dtype od, float* lse, hipStream_t st,
-                      const SmPrefix& pre = SmPrefix()) {
+                      const SmPrefix& pre = SmPrefix(), const SmMix& mix = SmMix()) {
   auto prof = prof_fn();
   if (prof) prof(KID_SOFTMAX, st, 0);
   hipError_t e;
   if (d->io == NATSL_BF16)
-    e = od == NATSL_BF16 ? do_softmax_t<bf16, bf16>(d, q, k, v, sel, nsb, o, lse, st, pre)
-                         : do_softmax_t<bf16, float>(d, q, k, v, sel, nsb, o, lse, st, pre);
+    e = od == NATSL_BF16 ? do_softmax_t<bf16, bf16>(d, q, k, v, sel, nsb, o, lse, st, pre, mix)
+                         : do_softmax_t<bf16, float>(d, q, k, v, sel, nsb, o, lse, st, pre, mix);
   else
-    e = od == NATSL_BF16 ? do_softmax_t<float, bf16>(d, q, k, v, sel, nsb, o, lse, st, pre)
-                         : do_softmax_t<float, float>(d, q, k, v, sel, nsb, o, lse, st, pre);
+    e = od == NATSL_BF16 ? do_softmax_t<float, bf16>(d, q, k, v, sel, nsb, o, lse, st, pre, mix)
+                         : do_softmax_t<float, float>(d, q, k, v, sel, nsb, o, lse, st, pre, mix);
   if (e == hipSuccess && prof) prof(KID_SOFTMAX, st, 1);
   return e;
 }
@@ -253,24 +256,26 @@ hipError_t do_gdn(const natsl_dims* d, const void* q, const void* k, const void*
 
 template <typename Tq, typename Tb>
 hipError_t do_merge_t(const natsl_dims* d, const void* q, const void* osm, const void* ogd, const float* wm,
-                      int64_t hs, const float* gs, const float* gl, void* out, hipStream_t st) {
+                      int64_t hs, const float* gs, const float* gl, void* out, hipStream_t st, const float* mixd) {
   if (d->Dk == 64)
     return launch_merge<Tq, Tb, 64>((const Tq*)q, (const Tb*)osm, (const Tb*)ogd, wm, hs, gs, gl, (Tq*)out,
-                                    d->B, d->H, d->L, eff_eps(d), st);
+                                    d->B, d->H, d->L, eff_eps(d), st, mixd);
   return launch_merge<Tq, Tb, 128>((const Tq*)q, (const Tb*)osm, (const Tb*)ogd, wm, hs, gs, gl, (Tq*)out,
-                                   d->B, d->H, d->L, eff_eps(d), st);
+                                   d->B, d->H, d->L, eff_eps(d), st, mixd);
 }
+// mixd (nullable): the mixing scores' difference per token, from the softmax branch
 hipError_t do_merge(const natsl_dims* d, const void* q, const void* osm, const void* ogd, natsl_dtype bd,
-                    const float* wm, int64_t hs, const float* gs, const float* gl, void* out, hipStream_t st) {
+                    const float* wm, int64_t hs, const float* gs, const float* gl, void* out, hipStream_t st,
+                    const float* mixd = nullptr) {
   auto prof = prof_fn();
   if (prof) prof(KID_MERGE, st, 0);
   hipError_t e;
   if (d->io == NATSL_BF16)
-    e = bd == NATSL_BF16 ? do_merge_t<bf16, bf16>(d, q, osm, ogd, wm, hs, gs, gl, out, st)
-                         : do_merge_t<bf16, float>(d, q, osm, ogd, wm, hs, gs, gl, out, st);
+    e = bd == NATSL_BF16 ? do_merge_t<bf16, bf16>(d, q, osm, ogd, wm, hs, gs, gl, out, st, mixd)
+                         : do_merge_t<bf16, float>(d, q, osm, ogd, wm, hs, gs, gl, out, st, mixd);
   else
-    e = bd == NATSL_BF16 ? do_merge_t<float, bf16>(d, q, osm, ogd, wm, hs, gs, gl, out, st)
-                         : do_merge_t<float, float>(d, q, osm, ogd, wm, hs, gs, gl, out, st);
+    e = bd == NATSL_BF16 ? do_merge_t<float, bf16>(d, q, osm, ogd, wm, hs, gs, gl, out, st, mixd)
+                         : do_merge_t<float, float>(d, q, osm, ogd, wm, hs, gs, gl, out, st, mixd);
   if (e == hipSuccess && prof) prof(KID_MERGE, st, 1);
   return e;
 }
@@ -451,12 +456,19 @@ natsl_status natsl_forward(const natsl_dims* dims, const natsl_forward_args* a, 
   e = do_gdn(dims, a->q, a->k, a->v, a->alpha, a->beta, route, S_init, o_gd, a->branch_dtype, a->S_final,
              w.gdn, ctx->aux, ctx->aux, nullptr, ctx->routed);
   if (e != hipSuccess) return dev_fail(e, "natsl_forward/gdn");
-  e = do_softmax(dims, a->q, a->k, a->v, w.sel, w.nsb, o_sm, a->branch_dtype, nullptr, stream, pre);
+  // the softmax branch also leaves the merge's mixing scores (bf16 D = 128 kernel)
+  bool mix_done = false;
+  SmMix mix;
+  mix.w_mix = a->w_mix;
+  mix.hs = a->w_mix_head_stride;
+  mix.d = w.mixd;
+  mix.done = &mix_done;
+  e = do_softmax(dims, a->q, a->k, a->v, w.sel, w.nsb, o_sm, a->branch_dtype, nullptr, stream, pre, mix);
   if (e != hipSuccess) return dev_fail(e, "natsl_forward/softmax");
   if ((e = hipEventRecord(ctx->join, ctx->aux)) != hipSuccess) return dev_fail(e, "hipEventRecord");
   if ((e = hipStreamWaitEvent(stream, ctx->join, 0)) != hipSuccess) return dev_fail(e, "hipStreamWaitEvent");
   e = do_merge(dims, a->q, o_sm, o_gd, a->branch_dtype, a->w_mix, a->w_mix_head_stride, a->g_sm, a->g_lin, a->out,
-               stream);
+               stream, mix_done ? w.mixd : nullptr);
   if (e != hipSuccess) return dev_fail(e, "natsl_forward/merge");
   return ok();
 }

@@ -32,10 +32,12 @@ hipError_t launch_route(const T* x, const float* w, const float* bsc, int B, int
 hipError_t launch_compact(const int32_t* route_in, int32_t* route_out, int B, int G, int nc,
                           int32_t* sel_idx, int32_t* nsel_before, hipStream_t st);
 
+// mixd (nullable): per-token z0 - z1 of the mixing scores q W_mix, already
+// computed (by the softmax branch); then q and w_mix are not read
 template <typename Tq, typename Tb, int D>
 hipError_t launch_merge(const Tq* q, const Tb* o_sm, const Tb* o_gdn, const float* w_mix, int64_t hs,
                         const float* g_sm, const float* g_lin, Tq* out, int B, int H, int L,
-                        float eps, hipStream_t st);
+                        float eps, hipStream_t st, const float* mixd = nullptr);
 
 // cached softmax rows a prefill segment also attends to (chunked prefill):
 // n_committed[b, g] rows (a multiple of 64) of k, v [B, H, cap, D]
@@ -52,10 +54,20 @@ hipError_t launch_softmax_backward(const T* q, const T* k, const T* v, const int
                                    const int32_t* nsel_before, const To* o, const float* lse, const T* d_o,
                                    float* dq, float* dk, float* dv, void* ws, int B, int H, int L, int G,
                                    float scale, hipStream_t st);
+// the merge's mixing scores from the softmax branch's own q fragments: when
+// d is set and the launch uses the bf16 D = 128 kernel, d[b, h, t] =
+// q W_mix[:, 0] - q W_mix[:, 1] is written and *done set (false otherwise)
+struct SmMix {
+  const float* w_mix = nullptr;
+  int64_t hs = 0;  // head stride of w_mix in floats (0 = shared)
+  float* d = nullptr;
+  bool* done = nullptr;
+};
 template <typename T, typename To, int D>
 hipError_t launch_softmax_masked(const T* q, const T* k, const T* v, const int32_t* sel_idx,
                                  const int32_t* nsel_before, To* o_sm, float* lse, int B, int H,
-                                 int L, int G, float scale, hipStream_t st, const SmPrefix& pre = SmPrefix());
+                                 int L, int G, float scale, hipStream_t st, const SmPrefix& pre = SmPrefix(),
+                                 const SmMix& mix = SmMix());
 
 size_t gdn_ws_bytes(int io_is_bf16, int D, int64_t nch);
 template <typename T, typename To, int D>

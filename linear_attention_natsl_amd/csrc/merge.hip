@@ -16,7 +16,8 @@ __global__ void __launch_bounds__(256) k_merge(const Tq* __restrict__ q, const T
                                                const float* __restrict__ w_mix, int64_t wmix_hs,
                                                const float* __restrict__ g_sm,
                                                const float* __restrict__ g_lin, To* __restrict__ out,
-                                               int H, int L, float eps, int64_t ntok) {
+                                               int H, int L, float eps, int64_t ntok,
+                                               const float* __restrict__ mixd) {
   constexpr int LPT = D / 8;  // lanes per token
   const int64_t gtid = (int64_t)bid_x() * 256 + tid_x();
   const int64_t tok = gtid / LPT;
@@ -25,36 +26,52 @@ __global__ void __launch_bounds__(256) k_merge(const Tq* __restrict__ q, const T
   const int64_t t = valid ? tok : 0;
   const int h = (int)((t / L) % H);
   const int col = sub * 8;
-  float qv[8], a[8], b[8];
-  load8f<Tq>(q + t * D + col, qv);
+  float a[8], b[8];
   load8f<Tb>(o_sm + t * D + col, a);
   load8f<Tb>(o_gdn + t * D + col, b);
-  // the lane's 8 rows of W_mix [D, 2] are 16 consecutive floats
-  const f32x4* wm4 = reinterpret_cast<const f32x4*>(w_mix + (int64_t)h * wmix_hs + col * 2);
-  float wm[16];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const f32x4 t4 = wm4[j];
-    wm[4 * j] = t4[0]; wm[4 * j + 1] = t4[1]; wm[4 * j + 2] = t4[2]; wm[4 * j + 3] = t4[3];
-  }
-  float ssa = 0.f, ssb = 0.f, z0 = 0.f, z1 = 0.f;
+  float ssa = 0.f, ssb = 0.f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     ssa += a[j] * a[j];
     ssb += b[j] * b[j];
-    z0 += qv[j] * wm[2 * j];
-    z1 += qv[j] * wm[2 * j + 1];
   }
   ssa = dpp_group_sum<LPT>(ssa);
   ssb = dpp_group_sum<LPT>(ssb);
-  z0 = dpp_group_sum<LPT>(z0);
-  z1 = dpp_group_sum<LPT>(z1);
   const float ra = 1.0f / sqrtf(ssa * (1.0f / D) + eps);
   const float rb = 1.0f / sqrtf(ssb * (1.0f / D) + eps);
-  const float zm = fmaxf(z0, z1);
-  const float e0 = expf(z0 - zm), e1 = expf(z1 - zm);
-  const float inv = 1.0f / (e0 + e1);
-  const float w0 = e0 * inv * ra, w1 = e1 * inv * rb;
+  // mixing weights softmax(z0, z1), z = q W_mix
+  float m0, m1;
+  if (mixd) {  // z0 - z1 given
+    const float dz = mixd[t];
+    const float e = expf(-fabsf(dz)), inv = 1.0f / (1.0f + e);
+    m0 = dz >= 0.f ? inv : e * inv;
+    m1 = dz >= 0.f ? e * inv : inv;
+  } else {
+    float qv[8];
+    load8f<Tq>(q + t * D + col, qv);
+    // the lane's 8 rows of W_mix [D, 2] are 16 consecutive floats
+    const f32x4* wm4 = reinterpret_cast<const f32x4*>(w_mix + (int64_t)h * wmix_hs + col * 2);
+    float wm[16];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 t4 = wm4[j];
+      wm[4 * j] = t4[0]; wm[4 * j + 1] = t4[1]; wm[4 * j + 2] = t4[2]; wm[4 * j + 3] = t4[3];
+    }
+    float z0 = 0.f, z1 = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      z0 += qv[j] * wm[2 * j];
+      z1 += qv[j] * wm[2 * j + 1];
+    }
+    z0 = dpp_group_sum<LPT>(z0);
+    z1 = dpp_group_sum<LPT>(z1);
+    const float zm = fmaxf(z0, z1);
+    const float e0 = expf(z0 - zm), e1 = expf(z1 - zm);
+    const float inv = 1.0f / (e0 + e1);
+    m0 = e0 * inv;
+    m1 = e1 * inv;
+  }
+  const float w0 = m0 * ra, w1 = m1 * rb;
   float gs[8], gl[8];
   if (g_sm) load8f<float>(g_sm + col, gs);
   else
@@ -78,19 +95,19 @@ __global__ void __launch_bounds__(256) k_merge(const Tq* __restrict__ q, const T
 template <typename Tq, typename Tb, int D>
 hipError_t launch_merge(const Tq* q, const Tb* o_sm, const Tb* o_gdn, const float* w_mix, int64_t hs,
                         const float* g_sm, const float* g_lin, Tq* out, int B, int H, int L,
-                        float eps, hipStream_t st) {
+                        float eps, hipStream_t st, const float* mixd) {
   const int64_t ntok = (int64_t)B * H * L;
   const int64_t threads = ntok * (D / 8);
   const int64_t blocks = (threads + 255) / 256;
   hipLaunchKernelGGL((k_merge<Tq, Tb, Tq, D>), dim3((unsigned)blocks), dim3(256), 0, st, q, o_sm,
-                     o_gdn, w_mix, hs, g_sm, g_lin, out, H, L, eps, ntok);
+                     o_gdn, w_mix, hs, g_sm, g_lin, out, H, L, eps, ntok, mixd);
   return hipGetLastError();
 }
 
 #define INST(Tq, Tb, D)                                                                          \
   template hipError_t launch_merge<Tq, Tb, D>(const Tq*, const Tb*, const Tb*, const float*,     \
                                               int64_t, const float*, const float*, Tq*, int, int, \
-                                              int, float, hipStream_t);
+                                              int, float, hipStream_t, const float*);
 INST(float, float, 64)
 INST(float, float, 128)
 INST(float, bf16, 64)

@@ -375,7 +375,7 @@ __global__ void __launch_bounds__(512, 1)
                  const int32_t* __restrict__ sel_idx, const int32_t* __restrict__ nsel_before,
                  To* __restrict__ o_sm, float* __restrict__ lse, int H, int L, int G, float scale_log2,
                  const bf16* __restrict__ pre_k, const bf16* __restrict__ pre_v, const int32_t* __restrict__ pnc,
-                 int pcap) {
+                 int pcap, const float* __restrict__ w_mix, int64_t wmix_hs, float* __restrict__ mixd) {
   constexpr int D = 128;
   extern __shared__ __align__(16) unsigned char lds[];
   int32_t* sel_l = reinterpret_cast<int32_t*>(lds + SM2_STAGES * SM2_TILE_BYTES);
@@ -608,13 +608,39 @@ __global__ void __launch_bounds__(512, 1)
     }
     if (lse && g == 0) lse[(int64_t)bh * L + tok] = (m_run[qs] + log2f(lt)) * LN2;
   }
+  // the merge's mixing scores, from the q fragments already in registers:
+  // lane group g holds q[t][32 ks + 8 g + j], whose W_mix rows are 16
+  // consecutive floats per ks
+  if (mixd) {
+    const float* wm = w_mix + (int64_t)h * wmix_hs;
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
+      float z0 = 0.f, z1 = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const f32x4* w4 = reinterpret_cast<const f32x4*>(wm + (32 * ks + 8 * g) * 2);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const f32x4 ww = w4[jj];  // W_mix rows 32 ks + 8 g + 2 jj and + 1, both columns
+          const float qa = (float)qf[qs][ks].v[2 * jj], qb = (float)qf[qs][ks].v[2 * jj + 1];
+          z0 += qa * ww[0] + qb * ww[2];
+          z1 += qa * ww[1] + qb * ww[3];
+        }
+      }
+      z0 = group4_sum(z0);
+      z1 = group4_sum(z1);
+      if (g == 0) mixd[(int64_t)bh * L + qtok0 + 16 * qs + c] = z0 - z1;
+    }
+  }
 }
 
 template <typename T, typename To, int D>
 hipError_t launch_softmax_masked(const T* q, const T* k, const T* v, const int32_t* sel_idx,
                                  const int32_t* nsel_before, To* o_sm, float* lse, int B, int H,
-                                 int L, int G, float scale, hipStream_t st, const SmPrefix& pre) {
+                                 int L, int G, float scale, hipStream_t st, const SmPrefix& pre,
+                                 const SmMix& mix) {
   using C = SmCfg<T, D>;
+  if (mix.done) *mix.done = false;
   if constexpr (sizeof(T) == 2 && D == 128) {
     static bool attr2 = false;
     if (!attr2) {
@@ -629,8 +655,11 @@ hipError_t launch_softmax_masked(const T* q, const T* k, const T* v, const int32
       const int64_t grid = (int64_t)B * H * ((nc + 3) / 4);
       hipLaunchKernelGGL(k_softmax_v2<To>, dim3((unsigned)grid), dim3(512), SM2_LDS, st, (const bf16*)q,
                          (const bf16*)k, (const bf16*)v, sel_idx, nsel_before, o_sm, lse, H, L, G, scale * LOG2E,
-                         (const bf16*)pre.k, (const bf16*)pre.v, pre.n_committed, pre.cap);
-      return hipGetLastError();
+                         (const bf16*)pre.k, (const bf16*)pre.v, pre.n_committed, pre.cap, mix.w_mix, mix.hs,
+                         mix.w_mix ? mix.d : nullptr);
+      const hipError_t e = hipGetLastError();
+      if (e == hipSuccess && mix.done) *mix.done = mix.w_mix && mix.d;
+      return e;
     }
   }
   static bool attr_set = false;
@@ -653,7 +682,7 @@ hipError_t launch_softmax_masked(const T* q, const T* k, const T* v, const int32
   template hipError_t launch_softmax_masked<T, To, D>(const T*, const T*, const T*,            \
                                                       const int32_t*, const int32_t*, To*,     \
                                                       float*, int, int, int, int, float,       \
-                                                      hipStream_t, const SmPrefix&);
+                                                      hipStream_t, const SmPrefix&, const SmMix&);
 INST(float, float, 64)
 INST(float, float, 128)
 INST(float, bf16, 64)

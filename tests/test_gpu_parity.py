@@ -256,6 +256,38 @@ def full_forward_check(name, heads, query_blocks=None, route_kind=None, branch=N
     assert worst <= TOL_BF16
 
 
+def test_forward_per_head_mix_bf16():
+    """bf16 D = 128 forward with per-head W_mix and branch gains.  This form
+    takes the merge's mixing scores from the softmax branch (computed from the
+    q fragments it holds) instead of re-reading q: checked against the oracle
+    and against the public merge of the same branch outputs, which computes
+    them from q."""
+    B, H, L, D = 2, 4, 576, 128
+    wl, inp = small_case("bf16", B=B, H=H, L=L, D=D, seed=77)
+    say("[forward] bf16 D=128, per-head W_mix and gains")
+    rng = np.random.default_rng(77)
+    wmix = rng.normal(0, 0.3, (H, D, 2)).astype(np.float32)
+    # gains <= 1, so the RMS-normalised outputs' tolerance bounds out as well
+    g_sm = rng.uniform(0.5, 1.0, D).astype(np.float32)
+    g_lin = rng.uniform(0.5, 1.0, D).astype(np.float32)
+    t = prefill_tensors(inp)
+    dm = N.dims(B, H, L, D, wl.d, N.BF16)
+    f = N.Forward(dm, debug=True)
+    f(t["x"], t["q"], t["k"], t["v"], t["alpha"], t["beta"], t["w_score"], dev(wmix), b_score=t["b_score"],
+      g_sm=dev(g_sm), g_lin=dev(g_lin), w_mix_head_stride=2 * D)
+    m = N.merge(dm, t["q"], f.o_sm, f.o_gdn, dev(wmix), w_mix_head_stride=2 * D, g_sm=dev(g_sm), g_lin=dev(g_lin))
+    torch.cuda.synchronize()
+    ref = O.forward(inp["x"], inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["w_score"], wmix,
+                    inp["b_score"], g_sm, g_lin)
+    assert np.array_equal(f.route.cpu().numpy(), ref["route"])
+    e = maxerr(host(f.out), ref["out"])
+    e2 = maxerr(host(f.out), host(m))
+    say(f"  out err vs oracle {e:.3e}, vs merge from q {e2:.3e}")
+    assert e <= TOL_BF16
+    # the same bf16 branch outputs mixed two ways: at most a few bf16 roundings apart
+    assert e2 <= 1e-2
+
+
 @pytest.mark.parametrize("branch", [None, torch.float32])
 def test_forward_prefill_full_sampled(branch):
     full_forward_check("prefill", heads=[(0, 0), (1, 7), (3, 15)], branch=branch)
