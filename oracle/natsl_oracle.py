@@ -1,5 +1,5 @@
 """fp64 CPU oracle for the NAtS-L hybrid attention layer (forward, decode step,
-and the gradient of the softmax branch).
+and the gradients of the softmax and Gated DeltaNet branches).
 
 TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import this module:
 only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg use it.
@@ -308,6 +308,72 @@ def gdn_branch_bruteforce(q, k, v, alpha, beta, route_bgc, S_init=None, chunk=CH
                     S = gdn_token_update(S, k[b, h, s], v[b, h, s], alpha[b, h, s], beta[b, h, s])
                 o[b, h, t] = gdn_readout(S, q[b, h, t])
     return o
+
+
+def gdn_branch_backward(q, k, v, alpha, beta, route_bgc, d_o, S_init=None, dS_final=None, chunk=CHUNK):
+    """Gradient of gdn_branch for an upstream gradient d_o [B,H,L,Dv] of its
+    outputs (and dS_final [B,H,Dk,Dv] of its final carried state, if any):
+    returns dq, dk, dv, dalpha, dbeta, dS_init.  The pages define only the
+    forward; this is its exact derivative, taken token by token in reverse.
+
+    With G = d loss / d S_t (key-major) and S = S_{t-1}, a = S^T k_t:
+        G     += q_t d_o_t^T             (o_t = S_t^T q_t)
+        dq_t   = S_t d_o_t
+        w      = G^T k_t
+        dv_t   = beta_t w
+        dbeta  = w . (v_t - alpha_t a)
+        dalpha = sum(G * (S - beta_t k_t a^T))
+        dk_t   = beta_t G v_t - alpha_t beta_t (G a + S w)
+        G      <- alpha_t (G - beta_t k_t w^T)   (the gradient of S_{t-1})
+    Rollback: a chunk that keeps its end state (linear route) passes the
+    carried state's gradient into its last token; one that restores its
+    chunk-start state passes it straight to the chunk start, and its tokens
+    see only their own outputs' gradients (G starts at zero)."""
+    q, k, v, alpha, beta, d_o = map(_f64, (q, k, v, alpha, beta, d_o))
+    B, H, L, Dk = q.shape
+    Dv = v.shape[3]
+    G_ = route_bgc.shape[1]
+    gidx = np.array([group_of_head(h, H, G_) for h in range(H)])
+    # chunk-start carried states of the forward
+    carry = np.zeros((B, H, Dk, Dv)) if S_init is None else _f64(S_init).copy()
+    starts = []
+    for c0 in range(0, L, chunk):
+        starts.append(carry.copy())
+        S = carry.copy()
+        for t in range(c0, min(L, c0 + chunk)):
+            S = gdn_token_update(S, k[:, :, t], v[:, :, t], alpha[:, :, t], beta[:, :, t])
+        if c0 + chunk <= L:
+            keep = route_bgc[:, gidx, c0 // chunk] == LIN
+            carry = np.where(keep[:, :, None, None], S, carry)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    dalpha, dbeta = np.zeros_like(alpha), np.zeros_like(beta)
+    Gc = np.zeros((B, H, Dk, Dv)) if dS_final is None else _f64(dS_final).copy()  # d loss / d carried state
+    for c0 in reversed(range(0, L, chunk)):
+        c1 = min(L, c0 + chunk)
+        keep = (route_bgc[:, gidx, c0 // chunk] == LIN) if c0 + chunk <= L else np.zeros((B, H), bool)
+        kp = keep[:, :, None, None]
+        # states before each token of the chunk
+        prev = [starts[c0 // chunk]]
+        for t in range(c0, c1 - 1):
+            prev.append(gdn_token_update(prev[-1], k[:, :, t], v[:, :, t], alpha[:, :, t], beta[:, :, t]))
+        G = np.where(kp, Gc, 0.0)
+        for t in reversed(range(c0, c1)):
+            S = prev[t - c0]
+            kt, vt, qt, gt = k[:, :, t], v[:, :, t], q[:, :, t], d_o[:, :, t]
+            at, bt = alpha[:, :, t][..., None], beta[:, :, t][..., None]
+            St = gdn_token_update(S, kt, vt, alpha[:, :, t], beta[:, :, t])
+            G = G + qt[..., :, None] * gt[..., None, :]
+            dq[:, :, t] = np.einsum("...kv,...v->...k", St, gt)
+            a = np.einsum("...kv,...k->...v", S, kt)
+            w = np.einsum("...kv,...k->...v", G, kt)
+            dv[:, :, t] = bt * w
+            dbeta[:, :, t] = np.sum(w * (vt - at * a), axis=-1)
+            dalpha[:, :, t] = np.sum(G * (S - bt[..., None] * kt[..., :, None] * a[..., None, :]), axis=(-2, -1))
+            dk[:, :, t] = (bt * np.einsum("...kv,...v->...k", G, vt)
+                           - at * bt * (np.einsum("...kv,...v->...k", G, a) + np.einsum("...kv,...v->...k", S, w)))
+            G = at[..., None] * (G - bt[..., None] * kt[..., :, None] * w[..., None, :])
+        Gc = G + np.where(kp, 0.0, Gc)
+    return dq, dk, dv, dalpha, dbeta, Gc
 
 
 # ---------------------------------------------------------------------------
