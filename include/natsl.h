@@ -71,7 +71,8 @@ enum {
   NATSL_ENTRY_FORWARD = 4,
   NATSL_ENTRY_DECODE_STEP = 5,
   NATSL_ENTRY_DECODE_HANDOFF = 6,
-  NATSL_ENTRY_SOFTMAX_BACKWARD = 7
+  NATSL_ENTRY_SOFTMAX_BACKWARD = 7,
+  NATSL_ENTRY_GDN_BACKWARD = 8
 };
 
 typedef struct {
@@ -172,6 +173,35 @@ natsl_status natsl_softmax_masked_backward(const natsl_dims* dims, const void* q
                                            const int32_t* sel_idx, const int32_t* nsel_before, const void* o_sm,
                                            const float* lse, const void* d_o, float* dq, float* dk, float* dv,
                                            void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Gradient of the Gated DeltaNet branch through the per-chunk rollback (the
+ * pages define the forward, Kernmechanismen 3; this is its exact derivative).
+ * The forward is natsl_gdn_chunk's: S_t = alpha_t (S_{t-1} - beta_t k_t k_t^T
+ * S_{t-1}) + beta_t k_t v_t^T, o_t = S_t^T q_t, and a chunk keeps its end state
+ * only when linear-routed.  Taken token by token in reverse: G += q_t d_o_t^T,
+ * dq_t = S_t d_o_t, w = G^T k_t, dv_t = beta_t w, dbeta_t = w.(v_t - alpha_t
+ * S_{t-1}^T k_t), dalpha_t = <G, S_{t-1} - beta_t k_t k_t^T S_{t-1}>, dk_t =
+ * beta_t G v_t - alpha_t beta_t (G S_{t-1}^T k_t + S_{t-1} w), G <- alpha_t
+ * (G - beta_t k_t w^T); the carried state's gradient enters a linear chunk's
+ * last token and skips a softmax chunk to its start.
+ *   q, k, v        [B, H, L, D] io dtype, alpha, beta [B, H, L] fp32, route
+ *                  [B, G, Nc] int32 (0 softmax, 1 linear): the forward's inputs
+ *   S_init         [B, H, Dk, Dv] fp32 initial state, or NULL (zeros)
+ *   d_o            [B, H, L, Dv] fp32: gradient of the loss w.r.t. o_gdn
+ *   dS_final       [B, H, Dk, Dv] fp32 gradient w.r.t. the final carried state,
+ *                  or NULL (zeros)
+ *   dq, dk, dv     [B, H, L, D] fp32 outputs; dalpha, dbeta [B, H, L] fp32
+ *   dS_init        [B, H, Dk, Dv] fp32 gradient w.r.t. S_init, or NULL
+ *   ws             workspace of natsl_workspace_size(NATSL_ENTRY_GDN_BACKWARD)
+ * Every output is written, not accumulated.  This is the per-token form (one
+ * workgroup per head, three barriers per token): a correct path, not a fast one.
+ */
+natsl_status natsl_gdn_backward(const natsl_dims* dims, const void* q, const void* k, const void* v,
+                                const float* alpha, const float* beta, const int32_t* route, const float* S_init,
+                                const float* d_o, const float* dS_final, float* dq, float* dk, float* dv,
+                                float* dalpha, float* dbeta, float* dS_init, void* ws, size_t ws_bytes,
+                                hipStream_t stream);
 
 /*
  * Output merging (Kernmechanismen 4): per (b, h, t)

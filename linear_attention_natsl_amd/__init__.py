@@ -20,12 +20,12 @@ LIB_PATH = os.path.join(HERE, "libnatsl.so")
 F32, BF16 = 0, 1
 ROUTE_SOFTMAX, ROUTE_LINEAR = 0, 1
 ENTRY_ROUTE, ENTRY_GDN_CHUNK, ENTRY_SOFTMAX_MASKED, ENTRY_MERGE, ENTRY_FORWARD, ENTRY_DECODE_STEP, \
-    ENTRY_DECODE_HANDOFF, ENTRY_SOFTMAX_BACKWARD = range(8)
+    ENTRY_DECODE_HANDOFF, ENTRY_SOFTMAX_BACKWARD, ENTRY_GDN_BACKWARD = range(9)
 STATUS = {0: "NATSL_OK", 1: "NATSL_ERR_INVALID_ARG", 2: "NATSL_ERR_UNSUPPORTED",
           3: "NATSL_ERR_WORKSPACE", 4: "NATSL_ERR_DEVICE", 5: "NATSL_ERR_CAPACITY"}
 EXPORTS = ["natsl_version", "natsl_last_error", "natsl_workspace_size", "natsl_route", "natsl_gdn_chunk",
            "natsl_softmax_masked", "natsl_merge", "natsl_forward", "natsl_decode_step",
-           "natsl_decode_handoff", "natsl_softmax_masked_backward", "natsl_profile_enable", "natsl_profile_reset", "natsl_profile_read",
+           "natsl_decode_handoff", "natsl_softmax_masked_backward", "natsl_gdn_backward", "natsl_profile_enable", "natsl_profile_reset", "natsl_profile_read",
            "natsl_profile_select"]
 
 
@@ -90,12 +90,13 @@ def lib():
         L.natsl_decode_handoff.argtypes = [C.POINTER(Dims), vp, vp, vp, vp, C.c_int, C.POINTER(DecodeCache), vp,
                                            C.c_size_t, vp]
         L.natsl_softmax_masked_backward.argtypes = [C.POINTER(Dims)] + [vp] * 12 + [C.c_size_t, vp]
+        L.natsl_gdn_backward.argtypes = [C.POINTER(Dims)] + [vp] * 16 + [C.c_size_t, vp]
         L.natsl_profile_enable.argtypes = [C.c_int]
         L.natsl_profile_read.argtypes = [C.c_char_p, C.POINTER(C.c_int), C.POINTER(C.c_double)]
         L.natsl_profile_select.argtypes = [C.c_char_p]
         for name in ("natsl_workspace_size", "natsl_route", "natsl_gdn_chunk", "natsl_softmax_masked",
                      "natsl_merge", "natsl_forward", "natsl_decode_step", "natsl_decode_handoff",
-                     "natsl_softmax_masked_backward",
+                     "natsl_softmax_masked_backward", "natsl_gdn_backward",
                      "natsl_profile_enable",
                      "natsl_profile_reset", "natsl_profile_read", "natsl_profile_select"):
             getattr(L, name).restype = st
@@ -377,6 +378,31 @@ def softmax_masked_backward(dm: Dims, q, k, v, sel_idx, nsel_before, o_sm, lse, 
         _p(o_sm, io, "o_sm", qs), _p(lse, torch.float32, "lse", qs[:3]), _p(d_o, io, "d_o", qs),
         _p(dq), _p(dk), _p(dv), _p(ws), ws_bytes, _stream(stream)))
     return dq, dk, dv
+
+
+def gdn_backward(dm: Dims, q, k, v, alpha, beta, route_bgc, d_o, S_init=None, dS_final=None, want_dS_init=True,
+                 stream=None):
+    """Gradient of the Gated DeltaNet branch through the rollback: returns fp32
+    (dq, dk, dv, dalpha, dbeta, dS_init).  q, k, v, alpha, beta, route_bgc and
+    S_init are the forward's inputs (gdn_chunk), d_o the fp32 upstream gradient
+    of o_gdn, dS_final that of the final carried state (None: zero)."""
+    io, qs, ts = _io_t(dm), (dm.B, dm.H, dm.L, dm.Dk), (dm.B, dm.H, dm.L)
+    ss = (dm.B, dm.H, dm.Dk, dm.Dv)
+    dq = torch.empty(qs, dtype=torch.float32, device=q.device)
+    dk, dv = torch.empty_like(dq), torch.empty_like(dq)
+    da = torch.empty(ts, dtype=torch.float32, device=q.device)
+    db = torch.empty_like(da)
+    dS0 = torch.empty(ss, dtype=torch.float32, device=q.device) if want_dS_init else None
+    ws_bytes = workspace_size(ENTRY_GDN_BACKWARD, dm)
+    ws = workspace(ws_bytes, q.device)
+    _check(lib().natsl_gdn_backward(
+        C.byref(dm), _p(q, io, "q", qs), _p(k, io, "k", qs), _p(v, io, "v", qs),
+        _p(alpha, torch.float32, "alpha", ts), _p(beta, torch.float32, "beta", ts),
+        _p(route_bgc, torch.int32, "route", (dm.B, dm.route_groups, dm.L // 64)),
+        _p(S_init, torch.float32, "S_init", ss), _p(d_o, torch.float32, "d_o", qs),
+        _p(dS_final, torch.float32, "dS_final", ss), _p(dq), _p(dk), _p(dv), _p(da), _p(db), _p(dS0),
+        _p(ws), ws_bytes, _stream(stream)))
+    return dq, dk, dv, da, db, dS0
 
 
 def decode_handoff(dm: Dims, route, k, v, S_final, state: DecodeState, append=False, stream=None):

@@ -43,7 +43,8 @@ size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 // ---------------------------------------------------------------- timing ----
 const char* kKernelNames[KID_COUNT] = {"route",        "compact",       "gdn_prep",   "gdn_scan",
                                        "softmax_masked", "merge",       "decode_route", "decode_gdn",
-                                       "decode_attn",  "decode_combine", "decode_commit", "softmax_backward", "decode_handoff"};
+                                       "decode_attn",  "decode_combine", "decode_commit", "softmax_backward", "decode_handoff",
+                                       "gdn_backward"};
 struct ProfRec {
   int kid;
   hipEvent_t a, b;
@@ -318,6 +319,10 @@ natsl_status natsl_workspace_size(int entry, const natsl_dims* dims, size_t* byt
       CHECK(check_dims(dims, true, false));
       *bytes = handoff_ws_bytes(dims->B, dims->route_groups, nchunks(dims));
       return ok();
+    case NATSL_ENTRY_GDN_BACKWARD:
+      CHECK(check_dims(dims, true, false));
+      *bytes = gdn_bwd_ws_bytes(dims->B, dims->H, dims->L, dims->Dk);
+      return ok();
     default:
       return fail(NATSL_ERR_INVALID_ARG, "unknown entry id %d", entry);
   }
@@ -583,6 +588,49 @@ natsl_status natsl_softmax_masked_backward(const natsl_dims* dims, const void* q
                                                          dk, dv, ws, B, H, L, G, sc, stream);
   if (prof) prof(KID_SOFTMAX_BWD, stream, 1);
   if (e != hipSuccess) return dev_fail(e, "natsl_softmax_masked_backward");
+  return ok();
+}
+
+natsl_status natsl_gdn_backward(const natsl_dims* dims, const void* q, const void* k, const void* v,
+                                const float* alpha, const float* beta, const int32_t* route, const float* S_init,
+                                const float* d_o, const float* dS_final, float* dq, float* dk, float* dv,
+                                float* dalpha, float* dbeta, float* dS_init, void* ws, size_t ws_bytes,
+                                hipStream_t stream) {
+  CHECK(check_dims(dims, true, false));
+  if (dims->B == 0) return ok();  // empty batch: nothing to do, pointers may be NULL
+  NEED(q, "q");
+  NEED(k, "k");
+  NEED(v, "v");
+  NEED(alpha, "alpha");
+  NEED(beta, "beta");
+  NEED(route, "route");
+  NEED(d_o, "d_o");
+  NEED(dq, "dq");
+  NEED(dk, "dk");
+  NEED(dv, "dv");
+  NEED(dalpha, "dalpha");
+  NEED(dbeta, "dbeta");
+  CHECK(check_ws(ws, ws_bytes, gdn_bwd_ws_bytes(dims->B, dims->H, dims->L, dims->Dk)));
+  const int B = dims->B, H = dims->H, L = dims->L, G = dims->route_groups;
+  hipError_t e;
+  auto prof = prof_fn();
+  if (prof) prof(KID_GDN_BWD, stream, 0);
+  if (dims->io == NATSL_BF16)
+    e = dims->Dk == 64 ? launch_gdn_backward<bf16, 64>((const bf16*)q, (const bf16*)k, (const bf16*)v, alpha, beta,
+                                                       route, S_init, d_o, dS_final, dq, dk, dv, dalpha, dbeta,
+                                                       dS_init, ws, B, H, L, G, stream)
+                       : launch_gdn_backward<bf16, 128>((const bf16*)q, (const bf16*)k, (const bf16*)v, alpha, beta,
+                                                        route, S_init, d_o, dS_final, dq, dk, dv, dalpha, dbeta,
+                                                        dS_init, ws, B, H, L, G, stream);
+  else
+    e = dims->Dk == 64 ? launch_gdn_backward<float, 64>((const float*)q, (const float*)k, (const float*)v, alpha,
+                                                        beta, route, S_init, d_o, dS_final, dq, dk, dv, dalpha,
+                                                        dbeta, dS_init, ws, B, H, L, G, stream)
+                       : launch_gdn_backward<float, 128>((const float*)q, (const float*)k, (const float*)v, alpha,
+                                                         beta, route, S_init, d_o, dS_final, dq, dk, dv, dalpha,
+                                                         dbeta, dS_init, ws, B, H, L, G, stream);
+  if (prof) prof(KID_GDN_BWD, stream, 1);
+  if (e != hipSuccess) return dev_fail(e, "natsl_gdn_backward");
   return ok();
 }
 

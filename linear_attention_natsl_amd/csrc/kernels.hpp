@@ -23,6 +23,7 @@ enum {
   KID_DECODE_COMMIT,
   KID_SOFTMAX_BWD,
   KID_HANDOFF,
+  KID_GDN_BWD,
   KID_COUNT
 };
 
@@ -70,6 +71,14 @@ hipError_t launch_softmax_masked(const T* q, const T* k, const T* v, const int32
                                  const SmMix& mix = SmMix());
 
 size_t gdn_ws_bytes(int io_is_bf16, int D, int64_t nch);
+// Gated DeltaNet branch gradient (per-token reverse sweep): ws holds the
+// chunk-start states [B, H, Nc, D, D] and a per-(b, h) chunk of token states
+size_t gdn_bwd_ws_bytes(int B, int H, int L, int D);
+template <typename T, int D>
+hipError_t launch_gdn_backward(const T* q, const T* k, const T* v, const float* alpha, const float* beta,
+                               const int32_t* route, const float* S_init, const float* d_o, const float* dS_final,
+                               float* dq, float* dk, float* dv, float* dalpha, float* dbeta, float* dS_init,
+                               void* ws, int B, int H, int L, int G, hipStream_t st);
 template <typename T, typename To, int D>
 hipError_t launch_gdn(const T* q, const T* k, const T* v, const float* alpha, const float* beta,
                       const int32_t* route, const float* S_init, To* o_gdn, float* S_final, void* ws,
