@@ -37,6 +37,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_FP32_VALU_TFLOPS = 157.3  # MI355X fp32 vector
 
 
 def sm_pairs(route_bgc, H, chunk=64):
@@ -188,6 +189,31 @@ def time_softmax_backward(N, dm, t, wl, pairs, reps=3):
                 flops=flops, tflops=round(tf, 1), frac_mfma=round(tf / PEAK_BF16_TFLOPS, 4))
 
 
+def time_gdn_backward(N, dm, t, wl, route, reps=2):
+    """Gradient of the Gated DeltaNet branch on this workload (a random fp32
+    upstream gradient on o_gdn), timed with events.  Plain fp32 VALU work, so
+    it is set against the fp32 vector peak; algorithmic work 16 D^2 FLOP per
+    token for the reverse step (outer product, two column and two row
+    contractions, the decay gradient, the erase of G), not counting the two
+    forward recomputations the per-token form also runs."""
+    import torch
+    d_o = torch.randn(t["q"].shape, dtype=torch.float32, device=t["q"].device)
+    N.gdn_backward(dm, t["q"], t["k"], t["v"], t["alpha"], t["beta"], route, d_o)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        N.gdn_backward(dm, t["q"], t["k"], t["v"], t["alpha"], t["beta"], route, d_o)
+    e1.record()
+    torch.cuda.synchronize()
+    us = 1000.0 * e0.elapsed_time(e1) / reps
+    flops = 16 * wl.D * wl.D * wl.B * wl.H * wl.L
+    tf = flops / (us * 1e-6) / 1e12
+    return dict(workload=f"gradient of the Gated DeltaNet branch on the {wl.name} prefill (per-token form)",
+                us=round(us, 1), flops=flops, tflops=round(tf, 2), bound="alu",
+                frac_fp32_valu=round(tf / PEAK_FP32_VALU_TFLOPS, 4))
+
+
 def time_prefill(args, N, W, O):
     import torch
     wl = W.WORKLOADS[args.workload]
@@ -223,6 +249,7 @@ def time_prefill(args, N, W, O):
     sm_alone_us = None if args.no_alone else time_softmax_alone(N, dm, fwd.route, t, io_t, max(10, args.steps // 2))
     handoff = time_handoff(N, dm, fwd.route, t, wl)
     backward = time_softmax_backward(N, dm, t, wl, sm_pairs(fwd.route.cpu().numpy(), wl.H))
+    gdn_backward = time_gdn_backward(N, dm, t, wl, fwd.route)
     route = fwd.route.cpu().numpy()
     ref_route = O.route(inp["x"], inp["w_score"], inp["b_score"])[0] if args.check_route else None
     pairs = sm_pairs(route, wl.H)
@@ -259,6 +286,7 @@ def time_prefill(args, N, W, O):
                    kernels=kernels),
         handoff=handoff,
         softmax_backward=backward,
+        gdn_backward=gdn_backward,
     )
     return res, inp, route
 
@@ -413,6 +441,7 @@ KERNEL_NAMES = [  # substring of the kernel symbol -> short name
     ("k_decode_gdn", "decode_gdn"), ("k_decode_attn", "decode_attn"), ("k_decode_combine", "decode_combine"),
     ("k_decode_commit", "decode_commit"), ("k_handoff_state", "handoff_state"), ("k_handoff_kv", "handoff_kv"),
     ("k_sm_bwd_delta", "sm_bwd_delta"), ("k_sm_bwd_dq", "sm_bwd_dq"), ("k_sm_bwd_dkdv", "sm_bwd_dkdv"),
+    ("k_gdn_bwd_ckpt", "gdn_bwd_ckpt"), ("k_gdn_bwd", "gdn_bwd"),
     ("AUnaryFunctor<float, float", "calib_mul_256MiB"),
 ]
 
@@ -471,7 +500,7 @@ def summarize_profiles(d):
     wr = lambda n: ctr["write"].get(n, 0.0) * wscale
     out = os.path.join(ROOT, "profiles")
     # all kernels
-    lines = ["# All kernels of one bench run (long prefill forward + decode step + handoff + softmax-branch gradient)", "",
+    lines = ["# All kernels of one bench run (long prefill forward + decode step + handoff + both branch gradients)", "",
              "Commands (from the repository root on one MI355X; rocprofv3 writes CSV; the three runs are separate):", "",
              cmds, "",
              f"bench.py reported {bench_line['ms_per_step']} ms per forward step ({bench_line['value']:.0f} tokens/s) "

@@ -60,10 +60,10 @@ __device__ __forceinline__ void gdn_fwd_token(float (&S)[D / 2], const float* ve
   constexpr int RPT = D / 2;
   const int r0 = hf * RPT;
   __syncthreads();  // vec staged
-  float pa = 0.f;
+  float p4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) pa += S[i] * vec[r0 + i];
-  part[hf * D + j] = pa;
+  for (int i = 0; i < RPT; ++i) p4[i & 3] += S[i] * vec[r0 + i];
+  part[hf * D + j] = (p4[0] + p4[1]) + (p4[2] + p4[3]);
   __syncthreads();  // column-sum halves exchanged
   const float a = part[j] + part[D + j], vj = vec[D + j];
 #pragma unroll
@@ -98,15 +98,23 @@ __global__ void __launch_bounds__(2 * D) k_gdn_bwd_ckpt(const T* __restrict__ k,
     S[i] = S_init ? S_init[((int64_t)bh * D + r0 + i) * D + j] : 0.f;
     carry[i] = S[i];
   }
+  // this thread's staged value (k or v) and the decays, loaded a token ahead
+  auto ld = [&](int tt) { return t < D ? to_f32(kh[(int64_t)tt * D + t]) : to_f32(vh[(int64_t)tt * D + (t - D)]); };
+  float nx = ld(0), na = ah[0], nb = bth[0];
   for (int c = 0; c < nc; ++c) {
 #pragma unroll
     for (int i = 0; i < C::RPT; ++i) ck[((int64_t)c * D + r0 + i) * D + j] = carry[i];
     for (int tt = c * CHUNK; tt < (c + 1) * CHUNK; ++tt) {
       float* vec = lds_f + C::OFF_VEC + (tt & 1) * 4 * D;
       float* part = lds_f + C::OFF_PART + (tt & 1) * 4 * D;
-      if (t < D) vec[t] = to_f32(kh[(int64_t)tt * D + t]);
-      else vec[t] = to_f32(vh[(int64_t)tt * D + (t - D)]);
-      gdn_fwd_token<D>(S, vec, part, j, hf, ah[tt], bth[tt]);
+      const float cur = nx, al = na, be = nb;
+      if (tt + 1 < L) {
+        nx = ld(tt + 1);
+        na = ah[tt + 1];
+        nb = bth[tt + 1];
+      }
+      vec[t] = cur;
+      gdn_fwd_token<D>(S, vec, part, j, hf, al, be);
     }
     const bool lin = rt[c] == kRouteLinear;
 #pragma unroll
@@ -158,6 +166,8 @@ __global__ void __launch_bounds__(2 * D) k_gdn_bwd(const T* __restrict__ q, cons
     float S[C::RPT];
 #pragma unroll
     for (int i = 0; i < C::RPT; ++i) S[i] = ck[((int64_t)c * D + r0 + i) * D + j];
+    auto ldf = [&](int tt) { return t < D ? to_f32(kh[(int64_t)tt * D + t]) : to_f32(vh[(int64_t)tt * D + (t - D)]); };
+    float nx = ldf(c0), na = ah[c0], nb = bth[c0];
     for (int s = 0; s < CHUNK; ++s) {
       const int tt = c0 + s;
 #pragma unroll
@@ -165,44 +175,61 @@ __global__ void __launch_bounds__(2 * D) k_gdn_bwd(const T* __restrict__ q, cons
       if (s == CHUNK - 1) break;  // the chunk's end state is not needed
       float* vec = lds_f + C::OFF_VEC + (tt & 1) * 4 * D;
       float* part = lds_f + C::OFF_PART + (tt & 1) * 4 * D;
-      if (t < D) vec[t] = to_f32(kh[(int64_t)tt * D + t]);
-      else vec[t] = to_f32(vh[(int64_t)tt * D + (t - D)]);
-      gdn_fwd_token<D>(S, vec, part, j, hf, ah[tt], bth[tt]);
+      const float cur = nx, al = na, be = nb;
+      nx = ldf(tt + 1);  // tt + 1 <= c0 + 63: inside the chunk
+      na = ah[tt + 1];
+      nb = bth[tt + 1];
+      vec[t] = cur;
+      gdn_fwd_token<D>(S, vec, part, j, hf, al, be);
     }
     __syncthreads();  // every read of the recompute's buffers is done
     const bool lin = rt[c] == kRouteLinear;
     float Gm[C::RPT];
 #pragma unroll
     for (int i = 0; i < C::RPT; ++i) Gm[i] = lin ? Gc[i] : 0.f;
+    // this thread's two staged values (k and q, or v and d_o) and the decays,
+    // loaded a token ahead (the sweep runs backward)
+    auto ld2 = [&](int tt, float& x0, float& x1) {
+      if (t < D) {
+        x0 = to_f32(kh[(int64_t)tt * D + t]);
+        x1 = to_f32(qh[(int64_t)tt * D + t]);
+      } else {
+        x0 = to_f32(vh[(int64_t)tt * D + (t - D)]);
+        x1 = doh[(int64_t)tt * D + (t - D)];
+      }
+    };
+    float n0, n1;
+    ld2(c0 + CHUNK - 1, n0, n1);
+    float nal = ah[c0 + CHUNK - 1], nbe = bth[c0 + CHUNK - 1];
     for (int tt = c0 + CHUNK - 1; tt >= c0; --tt) {
       float* vec = lds_f + C::OFF_VEC + (tt & 1) * 4 * D;  // [k | v | q | do]
       float* part = lds_f + C::OFF_PART + (tt & 1) * 4 * D;  // [a halves | w halves]
-      if (t < D) {
-        vec[t] = to_f32(kh[(int64_t)tt * D + t]);
-        vec[2 * D + t] = to_f32(qh[(int64_t)tt * D + t]);
-      } else {
-        vec[t] = to_f32(vh[(int64_t)tt * D + (t - D)]);
-        vec[3 * D + (t - D)] = doh[(int64_t)tt * D + (t - D)];
+      const float x0 = n0, x1 = n1, al = nal, be = nbe;
+      if (tt > c0) {
+        ld2(tt - 1, n0, n1);
+        nal = ah[tt - 1];
+        nbe = bth[tt - 1];
       }
+      vec[t] = x0;
+      vec[2 * D + t] = x1;  // q at 2D + t (t < D); d_o at 3D + (t - D) = 2D + t (t >= D)
       __syncthreads();  // vectors staged
       float Sp[C::RPT];
 #pragma unroll
       for (int i = 0; i < C::RPT; ++i) Sp[i] = sc[((int64_t)(tt - c0) * D + r0 + i) * D + j];
       const float doj = vec[3 * D + j], vj = vec[D + j];
-      float pa = 0.f, pw = 0.f;
+      float pa[4] = {0.f, 0.f, 0.f, 0.f}, pw[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < C::RPT; ++i) {
         const float ki = vec[r0 + i];
         Gm[i] += vec[2 * D + r0 + i] * doj;  // o_t = S_t^T q_t
-        pa += Sp[i] * ki;
-        pw += Gm[i] * ki;
+        pa[i & 3] += Sp[i] * ki;
+        pw[i & 3] += Gm[i] * ki;
       }
-      part[hf * D + j] = pa;
-      part[2 * D + hf * D + j] = pw;
+      part[hf * D + j] = (pa[0] + pa[1]) + (pa[2] + pa[3]);
+      part[2 * D + hf * D + j] = (pw[0] + pw[1]) + (pw[2] + pw[3]);
       __syncthreads();  // column-sum halves exchanged
       const float a = part[j] + part[D + j];
       const float w = part[2 * D + j] + part[3 * D + j];
-      const float al = ah[tt], be = bth[tt];
       const float cv = be * vj - al * be * a, cw = al * be * w;
       float pal = 0.f;
 #pragma unroll
@@ -226,9 +253,10 @@ __global__ void __launch_bounds__(2 * D) k_gdn_bwd(const T* __restrict__ q, cons
       {
         const float* X = (t < D) ? xq : xk;
         const int r = t % D;
-        float s = 0.f;
-        for (int jj = 0; jj < D; ++jj) s += X[r * C::XP + jj];
-        ((t < D) ? dq : dk)[(tok0 + tt) * D + r] = s;
+        float s4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+        for (int jj = 0; jj < D; ++jj) s4[jj & 3] += X[r * C::XP + jj];
+        ((t < D) ? dq : dk)[(tok0 + tt) * D + r] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
       }
       if (t == 0) {
         float sa = 0.f, sb = 0.f;
