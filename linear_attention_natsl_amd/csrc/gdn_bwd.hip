@@ -13,15 +13,19 @@
 // linear-routed; otherwise it passes straight to the chunk start and the
 // chunk's tokens see only their own outputs' gradients.
 //
-// One workgroup per (b, h) with 2 D threads: thread (j, half) holds rows
-// half D/2 .. half D/2 + D/2 - 1 of state column j, so the column sums
-// (S^T k, G^T k) are a register sum plus one LDS exchange, and the row sums
-// (dq, dk) go through an LDS transpose.  Two launches:
-//   k_gdn_bwd_ckpt  the forward, storing every chunk's starting (carried) state
-//   k_gdn_bwd       chunks in reverse: recompute the chunk's per-token states
-//                   into a scratch slot, then sweep its tokens backward
-// Three barriers per token: this is the plain per-token form, a first
-// correct GPU path for the gradient (the chunkwise form is not built).
+// The columns of S (and of G) evolve independently, so each head's 16-column
+// groups run in workgroups of their own (D / 16 per head).  Thread (jl, rg)
+// holds rows rg D/16 .. of column 16 cg + jl: the column sums (S^T k, G^T k)
+// are a row-swap sum over the wave's 4 lane groups plus one LDS exchange
+// across the 4 waves; the row sums (dq, dk) and the scalar gradients (dalpha,
+// dbeta) are per-group partials, added over the groups in a fixed order by a
+// last kernel (so the result does not depend on scheduling).  Launches:
+//   k_gdn_bwd_ckpt    the forward, storing every chunk's starting (carried) state
+//   k_gdn_bwd         chunks in reverse: recompute the chunk's per-token states
+//                     into a scratch slot, then sweep its tokens backward
+//   k_gdn_bwd_reduce  dq, dk, dalpha, dbeta from the groups' partials
+// Three barriers per token: this is the plain per-token form (the chunkwise
+// form on MFMA is not built).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -31,41 +35,55 @@ constexpr int kRouteLinear = 1;  // route id of the linear (Gated DeltaNet) oper
 
 template <int D>
 struct GdnBwdCfg {
-  static constexpr int NT = 2 * D;   // threads
-  static constexpr int RPT = D / 2;  // state rows per thread
-  static constexpr int XP = D + 1;   // pitch of the row-sum arrays
-  // LDS (floats): vec[2][4][D] (k, v, q, do by token parity), part[2][4][D]
-  // (column-sum halves of a and w), xq[D][XP], xk[D][XP], red[NT / 64][2]
+  static constexpr int CW = 16;       // state columns per workgroup
+  static constexpr int NCG = D / CW;  // column groups (workgroups) per head
+  static constexpr int NT = 256;      // 16 columns x 16 row groups
+  static constexpr int RPT = D / 16;  // state rows per thread
+  // LDS (floats): vec[2][2 D + 2 CW] (k, q, the group's v and d_o, by token
+  // parity), part[2][2][4][CW] (per-wave column sums of a and w, by parity),
+  // red[4][2] (per-wave dalpha, dbeta)
+  static constexpr int VEC = 2 * D + 2 * CW;
   static constexpr int OFF_VEC = 0;
-  static constexpr int OFF_PART = OFF_VEC + 2 * 4 * D;
-  static constexpr int OFF_XQ = OFF_PART + 2 * 4 * D;
-  static constexpr int OFF_XK = OFF_XQ + D * XP;
-  static constexpr int OFF_RED = OFF_XK + D * XP;
-  static constexpr int LDS_FLOATS = OFF_RED + 2 * (NT / 64);
-  static constexpr int CKPT_LDS_FLOATS = OFF_XQ;  // the forward needs vec and part only
+  static constexpr int OFF_PART = OFF_VEC + 2 * VEC;
+  static constexpr int OFF_RED = OFF_PART + 2 * 2 * 4 * CW;
+  static constexpr int LDS_FLOATS = OFF_RED + 8;
 };
 
 size_t gdn_bwd_ws_bytes(int B, int H, int L, int D) {
-  const size_t nc = (size_t)L / CHUNK;
-  return ((size_t)B * H * (nc + CHUNK) * D * D * 4 + 255) / 256 * 256;
+  const size_t nc = (size_t)L / CHUNK, ntok = (size_t)B * H * L, ncg = (size_t)D / 16;
+  const size_t floats = (size_t)B * H * (nc + CHUNK) * D * D  // chunk-start states, chunk token states
+                        + 2 * ntok * ncg * D                  // dq, dk partials
+                        + 2 * ntok * ncg;                     // dalpha, dbeta partials
+  return (floats * 4 + 255) / 256 * 256;
 }
 
-// One forward token on the thread's rows of column j:
+// sum over the workgroup's 16 row groups of a per-thread partial for the
+// thread's column: the wave's 4 lane groups by row swaps, the 4 waves through
+// LDS (part[4][16]); the caller's barrier separates the write and the reads
+__device__ __forceinline__ void col_part(float x, float* part, int jl, int wv, int lane) {
+  x = group4_sum(x);
+  if (lane < 16) part[wv * 16 + jl] = x;
+}
+__device__ __forceinline__ float col_total(const float* part, int jl) {
+  return (part[jl] + part[16 + jl]) + (part[32 + jl] + part[48 + jl]);
+}
+
+// One forward token on the thread's rows of its column:
 //   S <- a (S - b k (k^T S)) + b k v^T
-// vec: this token's [k | v] (staged by the caller before the first barrier),
-// part: this token's exchange buffer.
+// vec: this token's [k (D) | . (D) | v of the group (16)], staged by the caller
+// before the first barrier; part: this token's exchange buffer [4][16].
 template <int D>
-__device__ __forceinline__ void gdn_fwd_token(float (&S)[D / 2], const float* vec, float* part, int j, int hf,
-                                              float al, float be) {
-  constexpr int RPT = D / 2;
-  const int r0 = hf * RPT;
+__device__ __forceinline__ void gdn_fwd_token(float (&S)[D / 16], const float* vec, float* part, int jl, int rg,
+                                              int wv, int lane, float al, float be) {
+  constexpr int RPT = D / 16;
+  const int r0 = rg * RPT;
   __syncthreads();  // vec staged
   float p4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < RPT; ++i) p4[i & 3] += S[i] * vec[r0 + i];
-  part[hf * D + j] = (p4[0] + p4[1]) + (p4[2] + p4[3]);
-  __syncthreads();  // column-sum halves exchanged
-  const float a = part[j] + part[D + j], vj = vec[D + j];
+  col_part((p4[0] + p4[1]) + (p4[2] + p4[3]), part, jl, wv, lane);
+  __syncthreads();  // column sums exchanged
+  const float a = col_total(part, jl), vj = vec[2 * D + jl];
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
     const float ki = vec[r0 + i];
@@ -74,19 +92,19 @@ __device__ __forceinline__ void gdn_fwd_token(float (&S)[D / 2], const float* ve
 }
 
 template <typename T, int D>
-__global__ void __launch_bounds__(2 * D) k_gdn_bwd_ckpt(const T* __restrict__ k, const T* __restrict__ v,
-                                                        const float* __restrict__ alpha,
-                                                        const float* __restrict__ beta,
-                                                        const int32_t* __restrict__ route,
-                                                        const float* __restrict__ S_init, float* __restrict__ ckpt,
-                                                        int H, int L, int G) {
+__global__ void __launch_bounds__(256) k_gdn_bwd_ckpt(const T* __restrict__ k, const T* __restrict__ v,
+                                                      const float* __restrict__ alpha, const float* __restrict__ beta,
+                                                      const int32_t* __restrict__ route,
+                                                      const float* __restrict__ S_init, float* __restrict__ ckpt,
+                                                      int H, int L, int G) {
   using C = GdnBwdCfg<D>;
   extern __shared__ float lds_f[];
   const int nc = L / CHUNK;
-  const int bh = bid_x(), b = bh / H, h = bh % H;
+  const int bh = bid_x() / C::NCG, cg = bid_x() % C::NCG, b = bh / H, h = bh % H;
   const int grp = (G == 1) ? 0 : h;
   const int32_t* rt = route + ((int64_t)b * G + grp) * nc;
-  const int t = tid_x(), j = t % D, hf = t / D, r0 = hf * C::RPT;
+  const int t = tid_x(), jl = t & 15, rg = t >> 4, wv = wave_id(), lane = lane_id();
+  const int j = C::CW * cg + jl, r0 = rg * C::RPT;
   const T* kh = k + (int64_t)bh * L * D;
   const T* vh = v + (int64_t)bh * L * D;
   const float* ah = alpha + (int64_t)bh * L;
@@ -98,23 +116,27 @@ __global__ void __launch_bounds__(2 * D) k_gdn_bwd_ckpt(const T* __restrict__ k,
     S[i] = S_init ? S_init[((int64_t)bh * D + r0 + i) * D + j] : 0.f;
     carry[i] = S[i];
   }
-  // this thread's staged value (k or v) and the decays, loaded a token ahead
-  auto ld = [&](int tt) { return t < D ? to_f32(kh[(int64_t)tt * D + t]) : to_f32(vh[(int64_t)tt * D + (t - D)]); };
+  // this thread's staged value (k, or v of the group) and the decays, loaded
+  // a token ahead; dst: its place in vec (-1: none)
+  const int dst = t < D ? t : (t < D + 16 ? 2 * D + (t - D) : -1);
+  auto ld = [&](int tt) {
+    return t < D ? to_f32(kh[(int64_t)tt * D + t]) : (t < D + 16 ? to_f32(vh[(int64_t)tt * D + C::CW * cg + (t - D)]) : 0.f);
+  };
   float nx = ld(0), na = ah[0], nb = bth[0];
   for (int c = 0; c < nc; ++c) {
 #pragma unroll
     for (int i = 0; i < C::RPT; ++i) ck[((int64_t)c * D + r0 + i) * D + j] = carry[i];
     for (int tt = c * CHUNK; tt < (c + 1) * CHUNK; ++tt) {
-      float* vec = lds_f + C::OFF_VEC + (tt & 1) * 4 * D;
-      float* part = lds_f + C::OFF_PART + (tt & 1) * 4 * D;
+      float* vec = lds_f + C::OFF_VEC + (tt & 1) * C::VEC;
+      float* part = lds_f + C::OFF_PART + (tt & 1) * 2 * 4 * C::CW;
       const float cur = nx, al = na, be = nb;
       if (tt + 1 < L) {
         nx = ld(tt + 1);
         na = ah[tt + 1];
         nb = bth[tt + 1];
       }
-      vec[t] = cur;
-      gdn_fwd_token<D>(S, vec, part, j, hf, al, be);
+      if (dst >= 0) vec[dst] = cur;
+      gdn_fwd_token<D>(S, vec, part, jl, rg, wv, lane, al, be);
     }
     const bool lin = rt[c] == kRouteLinear;
 #pragma unroll
@@ -126,26 +148,24 @@ __global__ void __launch_bounds__(2 * D) k_gdn_bwd_ckpt(const T* __restrict__ k,
 }
 
 template <typename T, int D>
-__global__ void __launch_bounds__(2 * D) k_gdn_bwd(const T* __restrict__ q, const T* __restrict__ k,
-                                                   const T* __restrict__ v, const float* __restrict__ alpha,
-                                                   const float* __restrict__ beta, const int32_t* __restrict__ route,
-                                                   const float* __restrict__ d_o, const float* __restrict__ dS_final,
-                                                   const float* __restrict__ ckpt, float* __restrict__ scratch,
-                                                   float* __restrict__ dq, float* __restrict__ dk,
-                                                   float* __restrict__ dv, float* __restrict__ dalpha,
-                                                   float* __restrict__ dbeta, float* __restrict__ dS_init, int H,
-                                                   int L, int G) {
+__global__ void __launch_bounds__(256) k_gdn_bwd(const T* __restrict__ q, const T* __restrict__ k,
+                                                 const T* __restrict__ v, const float* __restrict__ alpha,
+                                                 const float* __restrict__ beta, const int32_t* __restrict__ route,
+                                                 const float* __restrict__ d_o, const float* __restrict__ dS_final,
+                                                 const float* __restrict__ ckpt, float* __restrict__ scratch,
+                                                 float* __restrict__ dq_p, float* __restrict__ dk_p,
+                                                 float* __restrict__ da_p, float* __restrict__ db_p,
+                                                 float* __restrict__ dv, float* __restrict__ dS_init, int H, int L,
+                                                 int G) {
   using C = GdnBwdCfg<D>;
   extern __shared__ float lds_f[];
-  float* xq = lds_f + C::OFF_XQ;
-  float* xk = lds_f + C::OFF_XK;
   float* red = lds_f + C::OFF_RED;
   const int nc = L / CHUNK;
-  const int bh = bid_x(), b = bh / H, h = bh % H;
+  const int bh = bid_x() / C::NCG, cg = bid_x() % C::NCG, b = bh / H, h = bh % H;
   const int grp = (G == 1) ? 0 : h;
   const int32_t* rt = route + ((int64_t)b * G + grp) * nc;
-  const int t = tid_x(), j = t % D, hf = t / D, r0 = hf * C::RPT;
-  const int lane = lane_id(), wv = wave_id();
+  const int t = tid_x(), jl = t & 15, rg = t >> 4, wv = wave_id(), lane = lane_id();
+  const int j = C::CW * cg + jl, r0 = rg * C::RPT;
   const int64_t tok0 = (int64_t)bh * L;
   const T* qh = q + tok0 * D;
   const T* kh = k + tok0 * D;
@@ -160,113 +180,108 @@ __global__ void __launch_bounds__(2 * D) k_gdn_bwd(const T* __restrict__ q, cons
 #pragma unroll
   for (int i = 0; i < C::RPT; ++i) Gc[i] = dS_final ? dS_final[((int64_t)bh * D + r0 + i) * D + j] : 0.f;
 
+  // staged values: slot A (t < 2 D) k or q, slot B (t < 32) v or d_o of the group
+  const int dstA = t < 2 * D ? t : -1;
+  const int dstB = t < 2 * C::CW ? 2 * D + t : -1;
+  auto ldA = [&](int tt) {
+    return t < D ? to_f32(kh[(int64_t)tt * D + t]) : (t < 2 * D ? to_f32(qh[(int64_t)tt * D + (t - D)]) : 0.f);
+  };
+  auto ldB = [&](int tt) {
+    return t < C::CW ? to_f32(vh[(int64_t)tt * D + C::CW * cg + t])
+                     : (t < 2 * C::CW ? doh[(int64_t)tt * D + C::CW * cg + (t - C::CW)] : 0.f);
+  };
+  auto ldF = [&](int tt) {  // the forward's staged value: k, or v of the group
+    return t < D ? to_f32(kh[(int64_t)tt * D + t]) : (t < D + 16 ? to_f32(vh[(int64_t)tt * D + C::CW * cg + (t - D)]) : 0.f);
+  };
+  const int dstF = t < D ? t : (t < D + 16 ? 2 * D + (t - D) : -1);
+
   for (int c = nc - 1; c >= 0; --c) {
     const int c0 = c * CHUNK;
     // recompute the chunk's states: slot s holds the state before token c0 + s
     float S[C::RPT];
 #pragma unroll
     for (int i = 0; i < C::RPT; ++i) S[i] = ck[((int64_t)c * D + r0 + i) * D + j];
-    auto ldf = [&](int tt) { return t < D ? to_f32(kh[(int64_t)tt * D + t]) : to_f32(vh[(int64_t)tt * D + (t - D)]); };
-    float nx = ldf(c0), na = ah[c0], nb = bth[c0];
+    float nx = ldF(c0), na = ah[c0], nb = bth[c0];
     for (int s = 0; s < CHUNK; ++s) {
       const int tt = c0 + s;
 #pragma unroll
       for (int i = 0; i < C::RPT; ++i) sc[((int64_t)s * D + r0 + i) * D + j] = S[i];
       if (s == CHUNK - 1) break;  // the chunk's end state is not needed
-      float* vec = lds_f + C::OFF_VEC + (tt & 1) * 4 * D;
-      float* part = lds_f + C::OFF_PART + (tt & 1) * 4 * D;
+      float* vec = lds_f + C::OFF_VEC + (tt & 1) * C::VEC;
+      float* part = lds_f + C::OFF_PART + (tt & 1) * 2 * 4 * C::CW;
       const float cur = nx, al = na, be = nb;
-      nx = ldf(tt + 1);  // tt + 1 <= c0 + 63: inside the chunk
+      nx = ldF(tt + 1);  // tt + 1 <= c0 + 63: inside the chunk
       na = ah[tt + 1];
       nb = bth[tt + 1];
-      vec[t] = cur;
-      gdn_fwd_token<D>(S, vec, part, j, hf, al, be);
+      if (dstF >= 0) vec[dstF] = cur;
+      gdn_fwd_token<D>(S, vec, part, jl, rg, wv, lane, al, be);
     }
     __syncthreads();  // every read of the recompute's buffers is done
     const bool lin = rt[c] == kRouteLinear;
     float Gm[C::RPT];
 #pragma unroll
     for (int i = 0; i < C::RPT; ++i) Gm[i] = lin ? Gc[i] : 0.f;
-    // this thread's two staged values (k and q, or v and d_o) and the decays,
-    // loaded a token ahead (the sweep runs backward)
-    auto ld2 = [&](int tt, float& x0, float& x1) {
-      if (t < D) {
-        x0 = to_f32(kh[(int64_t)tt * D + t]);
-        x1 = to_f32(qh[(int64_t)tt * D + t]);
-      } else {
-        x0 = to_f32(vh[(int64_t)tt * D + (t - D)]);
-        x1 = doh[(int64_t)tt * D + (t - D)];
-      }
-    };
-    float n0, n1;
-    ld2(c0 + CHUNK - 1, n0, n1);
+    // staged values and decays loaded a token ahead (the sweep runs backward)
+    float nA = ldA(c0 + CHUNK - 1), nB = ldB(c0 + CHUNK - 1);
     float nal = ah[c0 + CHUNK - 1], nbe = bth[c0 + CHUNK - 1];
     for (int tt = c0 + CHUNK - 1; tt >= c0; --tt) {
-      float* vec = lds_f + C::OFF_VEC + (tt & 1) * 4 * D;  // [k | v | q | do]
-      float* part = lds_f + C::OFF_PART + (tt & 1) * 4 * D;  // [a halves | w halves]
-      const float x0 = n0, x1 = n1, al = nal, be = nbe;
+      float* vec = lds_f + C::OFF_VEC + (tt & 1) * C::VEC;  // [k | q | v (16) | d_o (16)]
+      float* part = lds_f + C::OFF_PART + (tt & 1) * 2 * 4 * C::CW;  // [a: 4 x 16 | w: 4 x 16]
+      const float xA = nA, xB = nB, al = nal, be = nbe;
       if (tt > c0) {
-        ld2(tt - 1, n0, n1);
+        nA = ldA(tt - 1);
+        nB = ldB(tt - 1);
         nal = ah[tt - 1];
         nbe = bth[tt - 1];
       }
-      vec[t] = x0;
-      vec[2 * D + t] = x1;  // q at 2D + t (t < D); d_o at 3D + (t - D) = 2D + t (t >= D)
+      if (dstA >= 0) vec[dstA] = xA;
+      if (dstB >= 0) vec[dstB] = xB;
       __syncthreads();  // vectors staged
       float Sp[C::RPT];
 #pragma unroll
       for (int i = 0; i < C::RPT; ++i) Sp[i] = sc[((int64_t)(tt - c0) * D + r0 + i) * D + j];
-      const float doj = vec[3 * D + j], vj = vec[D + j];
+      const float vj = vec[2 * D + jl], doj = vec[2 * D + C::CW + jl];
       float pa[4] = {0.f, 0.f, 0.f, 0.f}, pw[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < C::RPT; ++i) {
         const float ki = vec[r0 + i];
-        Gm[i] += vec[2 * D + r0 + i] * doj;  // o_t = S_t^T q_t
+        Gm[i] += vec[D + r0 + i] * doj;  // o_t = S_t^T q_t
         pa[i & 3] += Sp[i] * ki;
         pw[i & 3] += Gm[i] * ki;
       }
-      part[hf * D + j] = (pa[0] + pa[1]) + (pa[2] + pa[3]);
-      part[2 * D + hf * D + j] = (pw[0] + pw[1]) + (pw[2] + pw[3]);
-      __syncthreads();  // column-sum halves exchanged
-      const float a = part[j] + part[D + j];
-      const float w = part[2 * D + j] + part[3 * D + j];
+      col_part((pa[0] + pa[1]) + (pa[2] + pa[3]), part, jl, wv, lane);
+      col_part((pw[0] + pw[1]) + (pw[2] + pw[3]), part + 4 * C::CW, jl, wv, lane);
+      __syncthreads();  // column sums exchanged
+      const float a = col_total(part, jl), w = col_total(part + 4 * C::CW, jl);
       const float cv = be * vj - al * be * a, cw = al * be * w;
       float pal = 0.f;
+      const int64_t tok = tok0 + tt;
 #pragma unroll
       for (int i = 0; i < C::RPT; ++i) {
         const float ki = vec[r0 + i];
         const float erased = Sp[i] - be * ki * a;
-        xq[(r0 + i) * C::XP + j] = (al * erased + be * ki * vj) * doj;  // S_t do
-        xk[(r0 + i) * C::XP + j] = Gm[i] * cv - cw * Sp[i];
+        // this group's share of the row sums dq = S_t d_o and dk
+        const float rq = dpp_group_sum<16>((al * erased + be * ki * vj) * doj);
+        const float rk = dpp_group_sum<16>(Gm[i] * cv - cw * Sp[i]);
+        if (jl == 0) {
+          dq_p[(tok * C::NCG + cg) * D + r0 + i] = rq;
+          dk_p[(tok * C::NCG + cg) * D + r0 + i] = rk;
+        }
         pal += Gm[i] * erased;
         Gm[i] = al * (Gm[i] - be * ki * w);  // the gradient of S_{t-1}
       }
-      float pbe = (hf == 0) ? w * (vj - al * a) : 0.f;
+      float pbe = (rg == 0) ? w * (vj - al * a) : 0.f;
       pal = wave_sum64(pal);
       pbe = wave_sum64(pbe);
       if (lane == 0) {
         red[2 * wv] = pal;
         red[2 * wv + 1] = pbe;
       }
-      if (hf == 0) dv[((int64_t)tt) * D + tok0 * D + j] = be * w;
-      __syncthreads();  // row-sum arrays and scalar partials written
-      {
-        const float* X = (t < D) ? xq : xk;
-        const int r = t % D;
-        float s4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-        for (int jj = 0; jj < D; ++jj) s4[jj & 3] += X[r * C::XP + jj];
-        ((t < D) ? dq : dk)[(tok0 + tt) * D + r] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
-      }
+      if (rg == 0) dv[tok * D + j] = be * w;
+      __syncthreads();  // scalar partials written
       if (t == 0) {
-        float sa = 0.f, sb = 0.f;
-#pragma unroll
-        for (int x = 0; x < C::NT / 64; ++x) {
-          sa += red[2 * x];
-          sb += red[2 * x + 1];
-        }
-        dalpha[tok0 + tt] = sa;
-        dbeta[tok0 + tt] = sb;
+        da_p[tok * C::NCG + cg] = (red[0] + red[2]) + (red[4] + red[6]);
+        db_p[tok * C::NCG + cg] = (red[1] + red[3]) + (red[5] + red[7]);
       }
     }
 #pragma unroll
@@ -278,31 +293,64 @@ __global__ void __launch_bounds__(2 * D) k_gdn_bwd(const T* __restrict__ q, cons
   }
 }
 
+// dq, dk, dalpha, dbeta: the column groups' partials added in group order
+template <int D>
+__global__ void __launch_bounds__(256) k_gdn_bwd_reduce(const float* __restrict__ dq_p, const float* __restrict__ dk_p,
+                                                        const float* __restrict__ da_p, const float* __restrict__ db_p,
+                                                        float* __restrict__ dq, float* __restrict__ dk,
+                                                        float* __restrict__ dalpha, float* __restrict__ dbeta,
+                                                        int64_t ntok) {
+  constexpr int NCG = GdnBwdCfg<D>::NCG;
+  const int64_t gid = (int64_t)bid_x() * 256 + tid_x();
+  const int64_t tok = gid / D;
+  const int i = (int)(gid % D);
+  if (tok >= ntok) return;
+  float sq = 0.f, sk = 0.f;
+#pragma unroll
+  for (int cg = 0; cg < NCG; ++cg) {
+    sq += dq_p[(tok * NCG + cg) * D + i];
+    sk += dk_p[(tok * NCG + cg) * D + i];
+  }
+  dq[tok * D + i] = sq;
+  dk[tok * D + i] = sk;
+  if (i == 0) {
+    float sa = 0.f, sb = 0.f;
+#pragma unroll
+    for (int cg = 0; cg < NCG; ++cg) {
+      sa += da_p[tok * NCG + cg];
+      sb += db_p[tok * NCG + cg];
+    }
+    dalpha[tok] = sa;
+    dbeta[tok] = sb;
+  }
+}
+
 template <typename T, int D>
 hipError_t launch_gdn_backward(const T* q, const T* k, const T* v, const float* alpha, const float* beta,
                                const int32_t* route, const float* S_init, const float* d_o, const float* dS_final,
                                float* dq, float* dk, float* dv, float* dalpha, float* dbeta, float* dS_init,
                                void* ws, int B, int H, int L, int G, hipStream_t st) {
   using C = GdnBwdCfg<D>;
-  static bool attr = false;
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_gdn_bwd<T, D>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       C::LDS_FLOATS * 4);
-    if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute((const void*)k_gdn_bwd_ckpt<T, D>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            C::CKPT_LDS_FLOATS * 4);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
   const int nc = L / CHUNK;
+  const int64_t ntok = (int64_t)B * H * L;
   float* ckpt = (float*)ws;
   float* scratch = ckpt + (size_t)B * H * nc * D * D;
-  hipLaunchKernelGGL((k_gdn_bwd_ckpt<T, D>), dim3(B * H), dim3(2 * D), C::CKPT_LDS_FLOATS * 4, st, k, v, alpha,
-                     beta, route, S_init, ckpt, H, L, G);
+  float* dq_p = scratch + (size_t)B * H * CHUNK * D * D;
+  float* dk_p = dq_p + (size_t)ntok * C::NCG * D;
+  float* da_p = dk_p + (size_t)ntok * C::NCG * D;
+  float* db_p = da_p + (size_t)ntok * C::NCG;
+  const size_t lds = C::LDS_FLOATS * 4;
+  const unsigned grid = (unsigned)(B * H * C::NCG);
+  hipLaunchKernelGGL((k_gdn_bwd_ckpt<T, D>), dim3(grid), dim3(C::NT), lds, st, k, v, alpha, beta, route, S_init,
+                     ckpt, H, L, G);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_gdn_bwd<T, D>), dim3(B * H), dim3(2 * D), C::LDS_FLOATS * 4, st, q, k, v, alpha, beta,
-                     route, d_o, dS_final, ckpt, scratch, dq, dk, dv, dalpha, dbeta, dS_init, H, L, G);
+  hipLaunchKernelGGL((k_gdn_bwd<T, D>), dim3(grid), dim3(C::NT), lds, st, q, k, v, alpha, beta, route, d_o,
+                     dS_final, ckpt, scratch, dq_p, dk_p, da_p, db_p, dv, dS_init, H, L, G);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int64_t threads = ntok * D;
+  hipLaunchKernelGGL((k_gdn_bwd_reduce<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, dq_p, dk_p,
+                     da_p, db_p, dq, dk, dalpha, dbeta, ntok);
   return hipGetLastError();
 }
 
