@@ -441,7 +441,7 @@ KERNEL_NAMES = [  # substring of the kernel symbol -> short name
     ("k_decode_gdn", "decode_gdn"), ("k_decode_attn", "decode_attn"), ("k_decode_combine", "decode_combine"),
     ("k_decode_commit", "decode_commit"), ("k_handoff_state", "handoff_state"), ("k_handoff_kv", "handoff_kv"),
     ("k_sm_bwd_delta", "sm_bwd_delta"), ("k_sm_bwd_dq", "sm_bwd_dq"), ("k_sm_bwd_dkdv", "sm_bwd_dkdv"),
-    ("k_gdn_bwd_ckpt", "gdn_bwd_ckpt"), ("k_gdn_bwd", "gdn_bwd"),
+    ("k_gdn_bwd_ckpt", "gdn_bwd_ckpt"), ("k_gdn_bwdI", "gdn_bwd"), ("k_gdn_bwd_reduce", "gdn_bwd_reduce"),
     ("AUnaryFunctor<float, float", "calib_mul_256MiB"),
 ]
 
