@@ -224,22 +224,27 @@ __global__ void __launch_bounds__(256) k_gdn_bwd(const T* __restrict__ q, const 
     // staged values and decays loaded a token ahead (the sweep runs backward)
     float nA = ldA(c0 + CHUNK - 1), nB = ldB(c0 + CHUNK - 1);
     float nal = ah[c0 + CHUNK - 1], nbe = bth[c0 + CHUNK - 1];
+    float nS[C::RPT];  // the thread's elements of S_{t-1}, also a token ahead
+#pragma unroll
+    for (int i = 0; i < C::RPT; ++i) nS[i] = sc[((int64_t)(CHUNK - 1) * D + r0 + i) * D + j];
     for (int tt = c0 + CHUNK - 1; tt >= c0; --tt) {
       float* vec = lds_f + C::OFF_VEC + (tt & 1) * C::VEC;  // [k | q | v (16) | d_o (16)]
       float* part = lds_f + C::OFF_PART + (tt & 1) * 2 * 4 * C::CW;  // [a: 4 x 16 | w: 4 x 16]
       const float xA = nA, xB = nB, al = nal, be = nbe;
+      float Sp[C::RPT];
+#pragma unroll
+      for (int i = 0; i < C::RPT; ++i) Sp[i] = nS[i];
       if (tt > c0) {
         nA = ldA(tt - 1);
         nB = ldB(tt - 1);
         nal = ah[tt - 1];
         nbe = bth[tt - 1];
+#pragma unroll
+        for (int i = 0; i < C::RPT; ++i) nS[i] = sc[((int64_t)(tt - 1 - c0) * D + r0 + i) * D + j];
       }
       if (dstA >= 0) vec[dstA] = xA;
       if (dstB >= 0) vec[dstB] = xB;
       __syncthreads();  // vectors staged
-      float Sp[C::RPT];
-#pragma unroll
-      for (int i = 0; i < C::RPT; ++i) Sp[i] = sc[((int64_t)(tt - c0) * D + r0 + i) * D + j];
       const float vj = vec[2 * D + jl], doj = vec[2 * D + C::CW + jl];
       float pa[4] = {0.f, 0.f, 0.f, 0.f}, pw[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
