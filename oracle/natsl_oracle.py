@@ -1,5 +1,5 @@
 """fp64 CPU oracle for the NAtS-L hybrid attention layer (forward, decode step,
-and the gradients of the softmax and Gated DeltaNet branches).
+and the gradients of the softmax and Gated DeltaNet branches and of the merge).
 
 TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import this module:
 only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg use it.
@@ -407,6 +407,43 @@ def merge(q, o_sm, o_gdn, w_mix, g_sm=None, g_lin=None, eps=1e-6):
     w = mix_weights(q, w_mix)
     out = w[..., 0:1] * n_sm + w[..., 1:2] * n_lin
     return out, n_sm, n_lin, w
+
+
+def merge_backward(q, o_sm, o_gdn, w_mix, d_out, g_sm=None, g_lin=None, eps=1e-6):
+    """Gradient of merge for an upstream gradient d_out [B,H,L,Dv]: returns
+    d_o_sm, d_o_gdn, dq (the mixing weights' share of q's gradient), dw_mix
+    (the shape of w_mix), dg_sm, dg_lin ([Dv]; ones when the gain is None).
+    The pages define only the forward; this is its exact derivative:
+        dn_x = w_x d_out,  dw_x = d_out . n_x
+        dz_0 = w_0 w_1 (dw_0 - dw_1) = -dz_1          (softmax of two logits)
+        dq = dz_0 (W_mix[:, 0] - W_mix[:, 1]),  dW_mix[:, c] += q dz_c
+        with r_x = (mean(o_x^2) + eps)^(-1/2) and u = dn_x * g_x:
+        d o_x = r_x u - (r_x^3 / Dv) o_x (u . o_x),   dg_x += dn_x * o_x r_x"""
+    q, o_sm, o_gdn, d_out = map(_f64, (q, o_sm, o_gdn, d_out))
+    Dv = o_sm.shape[-1]
+    gs = np.ones(Dv) if g_sm is None else _f64(g_sm)
+    gl = np.ones(Dv) if g_lin is None else _f64(g_lin)
+    w = mix_weights(q, w_mix)
+    wm = _f64(w_mix)
+    outs = []
+    for o, g, wx in ((o_sm, gs, w[..., 0:1]), (o_gdn, gl, w[..., 1:2])):
+        r = 1.0 / np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + eps)
+        dn = wx * d_out
+        u = dn * g
+        do = r * u - (r ** 3 / Dv) * o * np.sum(u * o, axis=-1, keepdims=True)
+        dg = np.sum(dn * o * r, axis=(0, 1, 2))
+        dw = np.sum(d_out * (o * r * g), axis=-1)
+        outs.append((do, dg, dw))
+    (d_sm, dg_sm, dw0), (d_gdn, dg_lin, dw1) = outs
+    dz0 = w[..., 0] * w[..., 1] * (dw0 - dw1)
+    dz = np.stack([dz0, -dz0], axis=-1)
+    if wm.ndim == 2:
+        dq = np.einsum("bhtj,kj->bhtk", dz, wm)
+        dwm = np.einsum("bhtk,bhtj->kj", q, dz)
+    else:
+        dq = np.einsum("bhtj,hkj->bhtk", dz, wm)
+        dwm = np.einsum("bhtk,bhtj->hkj", q, dz)
+    return d_sm, d_gdn, dq, dwm, dg_sm, dg_lin
 
 
 # ---------------------------------------------------------------------------

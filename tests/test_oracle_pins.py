@@ -539,3 +539,40 @@ def test_gdn_backward_matches_autograd():
     ref = _gdn_torch_grads(q, k, v, a, b, r, d_o, S0, chunk)
     for name, g, rf in zip(("q", "k", "v", "alpha", "beta", "S_init"), got, ref):
         np.testing.assert_allclose(g, rf, atol=1e-10, err_msg=name)
+
+
+# --------------------------------------------------------- merge gradient ----
+def test_merge_backward_matches_autograd_and_fd():
+    """The merge's gradient (both branch outputs, q through the mixing weights,
+    W_mix shared and per head, and both gains) against torch autograd of the
+    merge written out in torch, and a few entries against central differences
+    of merge itself.  Catches a dropped RMS-norm term, a wrong softmax-of-two
+    derivative or swapped mixing columns."""
+    rng = np.random.default_rng(91)
+    B, H, L, D = 2, 3, 5, 6
+    q, a, b, d_out = (rng.standard_normal((B, H, L, D)) for _ in range(4))
+    gs, gl = rng.uniform(0.5, 1.5, D), rng.uniform(0.5, 1.5, D)
+    for wm in (rng.standard_normal((D, 2)), rng.standard_normal((H, D, 2))):
+        got = O.merge_backward(q, a, b, wm, d_out, gs, gl)
+        T = lambda x: torch.from_numpy(np.ascontiguousarray(x)).requires_grad_(True)
+        tq, ta, tb, tw, tgs, tgl = map(T, (q, a, b, wm, gs, gl))
+        eps = 1e-6
+        ns = ta / torch.sqrt((ta * ta).mean(-1, keepdim=True) + eps) * tgs
+        nl = tb / torch.sqrt((tb * tb).mean(-1, keepdim=True) + eps) * tgl
+        z = tq @ tw if wm.ndim == 2 else torch.einsum("bhtk,hkj->bhtj", tq, tw)
+        w = torch.softmax(z, dim=-1)
+        out = w[..., 0:1] * ns + w[..., 1:2] * nl
+        ref = torch.autograd.grad(out, (ta, tb, tq, tw, tgs, tgl), torch.from_numpy(d_out))
+        for name, g, r in zip(("d_o_sm", "d_o_gdn", "dq", "dw_mix", "dg_sm", "dg_lin"), got, ref):
+            np.testing.assert_allclose(g, r.numpy(), atol=1e-12, err_msg=name)
+        loss = lambda q_, a_, b_: float(np.sum(O.merge(q_, a_, b_, wm, gs, gl)[0] * d_out))
+        h = 1e-6
+        for arr_i, grad in ((0, got[2]), (1, got[0]), (2, got[1])):
+            for _ in range(4):
+                idx = tuple(int(rng.integers(0, s)) for s in q.shape)
+                args_p = [q.copy(), a.copy(), b.copy()]
+                args_m = [q.copy(), a.copy(), b.copy()]
+                args_p[arr_i][idx] += h
+                args_m[arr_i][idx] -= h
+                fd = (loss(*args_p) - loss(*args_m)) / (2 * h)
+                assert abs(fd - grad[idx]) <= 1e-7 * max(1.0, abs(fd))
