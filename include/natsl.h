@@ -72,7 +72,8 @@ enum {
   NATSL_ENTRY_DECODE_STEP = 5,
   NATSL_ENTRY_DECODE_HANDOFF = 6,
   NATSL_ENTRY_SOFTMAX_BACKWARD = 7,
-  NATSL_ENTRY_GDN_BACKWARD = 8
+  NATSL_ENTRY_GDN_BACKWARD = 8,
+  NATSL_ENTRY_MERGE_BACKWARD = 9
 };
 
 typedef struct {
@@ -202,6 +203,31 @@ natsl_status natsl_gdn_backward(const natsl_dims* dims, const void* q, const voi
                                 const float* d_o, const float* dS_final, float* dq, float* dk, float* dv,
                                 float* dalpha, float* dbeta, float* dS_init, void* ws, size_t ws_bytes,
                                 hipStream_t stream);
+
+/*
+ * Gradient of the output merging (Kernmechanismen 4 defines the forward; this
+ * is its exact derivative).  With r_x = (mean(o_x^2) + eps)^(-1/2),
+ * n_x = o_x r_x g_x and (w_sm, w_lin) = softmax(q W_mix):
+ *   dn_x = w_x d_out,  dw_x = d_out . n_x,  dz_sm = w_sm w_lin (dw_sm - dw_lin) = -dz_lin
+ *   d_o_x = r_x u - (r_x^3 / Dv) o_x (u . o_x) with u = dn_x g_x
+ *   dq = dz_sm (W_mix[:, 0] - W_mix[:, 1])   (the mixing weights' share of q's gradient)
+ *   dW_mix[:, 0] = sum_t q dz_sm = -dW_mix[:, 1],   dg_x = sum_t dn_x o_x r_x
+ *   q [B, H, L, Dk] io dtype, o_sm, o_gdn [B, H, L, Dv] of branch_dtype, w_mix,
+ *   w_mix_head_stride, g_sm, g_lin (NULL = ones) as in natsl_merge
+ *   d_out          [B, H, L, Dv] fp32: gradient of the loss w.r.t. out
+ *   d_o_sm, d_o_gdn, dq  [B, H, L, D] fp32 outputs
+ *   dw_mix         the shape of w_mix, fp32, or NULL; sums over all heads when
+ *                  W_mix is shared (head stride 0)
+ *   dg_sm, dg_lin  [Dv] fp32 (gradients of the gains, also when they are NULL
+ *                  = ones), or NULL
+ *   ws             workspace of natsl_workspace_size(NATSL_ENTRY_MERGE_BACKWARD)
+ * Sums over tokens are added in a fixed order: results are deterministic.
+ */
+natsl_status natsl_merge_backward(const natsl_dims* dims, const void* q, const void* o_sm, const void* o_gdn,
+                                  natsl_dtype branch_dtype, const float* w_mix, int64_t w_mix_head_stride,
+                                  const float* g_sm, const float* g_lin, const float* d_out, float* d_o_sm,
+                                  float* d_o_gdn, float* dq, float* dw_mix, float* dg_sm, float* dg_lin, void* ws,
+                                  size_t ws_bytes, hipStream_t stream);
 
 /*
  * Output merging (Kernmechanismen 4): per (b, h, t)

@@ -20,12 +20,12 @@ LIB_PATH = os.path.join(HERE, "libnatsl.so")
 F32, BF16 = 0, 1
 ROUTE_SOFTMAX, ROUTE_LINEAR = 0, 1
 ENTRY_ROUTE, ENTRY_GDN_CHUNK, ENTRY_SOFTMAX_MASKED, ENTRY_MERGE, ENTRY_FORWARD, ENTRY_DECODE_STEP, \
-    ENTRY_DECODE_HANDOFF, ENTRY_SOFTMAX_BACKWARD, ENTRY_GDN_BACKWARD = range(9)
+    ENTRY_DECODE_HANDOFF, ENTRY_SOFTMAX_BACKWARD, ENTRY_GDN_BACKWARD, ENTRY_MERGE_BACKWARD = range(10)
 STATUS = {0: "NATSL_OK", 1: "NATSL_ERR_INVALID_ARG", 2: "NATSL_ERR_UNSUPPORTED",
           3: "NATSL_ERR_WORKSPACE", 4: "NATSL_ERR_DEVICE", 5: "NATSL_ERR_CAPACITY"}
 EXPORTS = ["natsl_version", "natsl_last_error", "natsl_workspace_size", "natsl_route", "natsl_gdn_chunk",
            "natsl_softmax_masked", "natsl_merge", "natsl_forward", "natsl_decode_step",
-           "natsl_decode_handoff", "natsl_softmax_masked_backward", "natsl_gdn_backward", "natsl_profile_enable", "natsl_profile_reset", "natsl_profile_read",
+           "natsl_decode_handoff", "natsl_softmax_masked_backward", "natsl_gdn_backward", "natsl_merge_backward", "natsl_profile_enable", "natsl_profile_reset", "natsl_profile_read",
            "natsl_profile_select"]
 
 
@@ -91,12 +91,14 @@ def lib():
                                            C.c_size_t, vp]
         L.natsl_softmax_masked_backward.argtypes = [C.POINTER(Dims)] + [vp] * 12 + [C.c_size_t, vp]
         L.natsl_gdn_backward.argtypes = [C.POINTER(Dims)] + [vp] * 16 + [C.c_size_t, vp]
+        L.natsl_merge_backward.argtypes = [C.POINTER(Dims), vp, vp, vp, C.c_int, vp, C.c_int64] + [vp] * 10 + \
+            [C.c_size_t, vp]
         L.natsl_profile_enable.argtypes = [C.c_int]
         L.natsl_profile_read.argtypes = [C.c_char_p, C.POINTER(C.c_int), C.POINTER(C.c_double)]
         L.natsl_profile_select.argtypes = [C.c_char_p]
         for name in ("natsl_workspace_size", "natsl_route", "natsl_gdn_chunk", "natsl_softmax_masked",
                      "natsl_merge", "natsl_forward", "natsl_decode_step", "natsl_decode_handoff",
-                     "natsl_softmax_masked_backward", "natsl_gdn_backward",
+                     "natsl_softmax_masked_backward", "natsl_gdn_backward", "natsl_merge_backward",
                      "natsl_profile_enable",
                      "natsl_profile_reset", "natsl_profile_read", "natsl_profile_select"):
             getattr(L, name).restype = st
@@ -403,6 +405,33 @@ def gdn_backward(dm: Dims, q, k, v, alpha, beta, route_bgc, d_o, S_init=None, dS
         _p(dS_final, torch.float32, "dS_final", ss), _p(dq), _p(dk), _p(dv), _p(da), _p(db), _p(dS0),
         _p(ws), ws_bytes, _stream(stream)))
     return dq, dk, dv, da, db, dS0
+
+
+def merge_backward(dm: Dims, q, o_sm, o_gdn, w_mix, d_out, w_mix_head_stride=0, g_sm=None, g_lin=None,
+                   stream=None):
+    """Gradient of the merge: returns fp32 (d_o_sm, d_o_gdn, dq, dw_mix, dg_sm,
+    dg_lin); dq is the mixing weights' share of q's gradient.  d_out is the
+    fp32 upstream gradient of out."""
+    if o_sm.dtype != o_gdn.dtype:
+        raise TypeError("o_sm and o_gdn must share a dtype")
+    if w_mix_head_stride not in (0, 2 * dm.Dk):
+        raise ValueError("w_mix_head_stride must be 0 or 2*Dk")
+    qs = (dm.B, dm.H, dm.L, dm.Dk)
+    wm_shape = (dm.Dk, 2) if w_mix_head_stride == 0 else (dm.H, dm.Dk, 2)
+    d_sm = torch.empty(qs, dtype=torch.float32, device=q.device)
+    d_gdn, dq = torch.empty_like(d_sm), torch.empty_like(d_sm)
+    dwm = torch.empty(wm_shape, dtype=torch.float32, device=q.device)
+    dgs = torch.empty(dm.Dv, dtype=torch.float32, device=q.device)
+    dgl = torch.empty_like(dgs)
+    ws_bytes = workspace_size(ENTRY_MERGE_BACKWARD, dm)
+    ws = workspace(ws_bytes, q.device)
+    _check(lib().natsl_merge_backward(
+        C.byref(dm), _p(q, _io_t(dm), "q", qs), _p(o_sm, None, "o_sm", qs), _p(o_gdn, None, "o_gdn", qs), _dt(o_sm),
+        _p(w_mix, torch.float32, "w_mix", wm_shape), w_mix_head_stride,
+        _p(g_sm, torch.float32, "g_sm", (dm.Dv,)), _p(g_lin, torch.float32, "g_lin", (dm.Dv,)),
+        _p(d_out, torch.float32, "d_out", qs), _p(d_sm), _p(d_gdn), _p(dq), _p(dwm), _p(dgs), _p(dgl),
+        _p(ws), ws_bytes, _stream(stream)))
+    return d_sm, d_gdn, dq, dwm, dgs, dgl
 
 
 def decode_handoff(dm: Dims, route, k, v, S_final, state: DecodeState, append=False, stream=None):

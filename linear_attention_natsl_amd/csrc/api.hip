@@ -44,7 +44,7 @@ size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 const char* kKernelNames[KID_COUNT] = {"route",        "compact",       "gdn_prep",   "gdn_scan",
                                        "softmax_masked", "merge",       "decode_route", "decode_gdn",
                                        "decode_attn",  "decode_combine", "decode_commit", "softmax_backward", "decode_handoff",
-                                       "gdn_backward"};
+                                       "gdn_backward", "merge_backward"};
 struct ProfRec {
   int kid;
   hipEvent_t a, b;
@@ -264,6 +264,17 @@ hipError_t do_merge_t(const natsl_dims* d, const void* q, const void* osm, const
   return launch_merge<Tq, Tb, 128>((const Tq*)q, (const Tb*)osm, (const Tb*)ogd, wm, hs, gs, gl, (Tq*)out,
                                    d->B, d->H, d->L, eff_eps(d), st, mixd);
 }
+template <typename Tq, typename Tb>
+hipError_t do_merge_bwd_t(const natsl_dims* d, const void* q, const void* osm, const void* ogd, const float* wm,
+                          int64_t hs, const float* gs, const float* gl, const float* d_out, float* d_sm, float* d_gdn,
+                          float* dq, float* dwm, float* dgs, float* dgl, void* ws, hipStream_t st) {
+  if (d->Dk == 64)
+    return launch_merge_backward<Tq, Tb, 64>((const Tq*)q, (const Tb*)osm, (const Tb*)ogd, wm, hs, gs, gl, d_out, d_sm,
+                                             d_gdn, dq, dwm, dgs, dgl, ws, d->B, d->H, d->L, eff_eps(d), st);
+  return launch_merge_backward<Tq, Tb, 128>((const Tq*)q, (const Tb*)osm, (const Tb*)ogd, wm, hs, gs, gl, d_out, d_sm,
+                                            d_gdn, dq, dwm, dgs, dgl, ws, d->B, d->H, d->L, eff_eps(d), st);
+}
+
 // mixd (nullable): the mixing scores' difference per token, from the softmax branch
 hipError_t do_merge(const natsl_dims* d, const void* q, const void* osm, const void* ogd, natsl_dtype bd,
                     const float* wm, int64_t hs, const float* gs, const float* gl, void* out, hipStream_t st,
@@ -322,6 +333,10 @@ natsl_status natsl_workspace_size(int entry, const natsl_dims* dims, size_t* byt
     case NATSL_ENTRY_GDN_BACKWARD:
       CHECK(check_dims(dims, true, false));
       *bytes = gdn_bwd_ws_bytes(dims->B, dims->H, dims->L, dims->Dk);
+      return ok();
+    case NATSL_ENTRY_MERGE_BACKWARD:
+      CHECK(check_dims(dims, true, false));
+      *bytes = merge_bwd_ws_bytes(dims->B, dims->H, dims->L, dims->Dk);
       return ok();
     default:
       return fail(NATSL_ERR_INVALID_ARG, "unknown entry id %d", entry);
@@ -631,6 +646,46 @@ natsl_status natsl_gdn_backward(const natsl_dims* dims, const void* q, const voi
                                                          dbeta, dS_init, ws, B, H, L, G, stream);
   if (prof) prof(KID_GDN_BWD, stream, 1);
   if (e != hipSuccess) return dev_fail(e, "natsl_gdn_backward");
+  return ok();
+}
+
+natsl_status natsl_merge_backward(const natsl_dims* dims, const void* q, const void* o_sm, const void* o_gdn,
+                                  natsl_dtype branch_dtype, const float* w_mix, int64_t w_mix_head_stride,
+                                  const float* g_sm, const float* g_lin, const float* d_out, float* d_o_sm,
+                                  float* d_o_gdn, float* dq, float* dw_mix, float* dg_sm, float* dg_lin, void* ws,
+                                  size_t ws_bytes, hipStream_t stream) {
+  CHECK(check_dims(dims, true, false));
+  if (dims->B == 0) return ok();  // empty batch: nothing to do, pointers may be NULL
+  NEED(q, "q");
+  NEED(o_sm, "o_sm");
+  NEED(o_gdn, "o_gdn");
+  NEED(w_mix, "w_mix");
+  NEED(d_out, "d_out");
+  NEED(d_o_sm, "d_o_sm");
+  NEED(d_o_gdn, "d_o_gdn");
+  NEED(dq, "dq");
+  if (branch_dtype != NATSL_F32 && branch_dtype != NATSL_BF16) return fail(NATSL_ERR_INVALID_ARG, "bad branch dtype");
+  if (w_mix_head_stride != 0 && w_mix_head_stride != 2 * dims->Dk)
+    return fail(NATSL_ERR_INVALID_ARG, "w_mix head stride must be 0 or 2 Dk (got %lld)", (long long)w_mix_head_stride);
+  CHECK(check_ws(ws, ws_bytes, merge_bwd_ws_bytes(dims->B, dims->H, dims->L, dims->Dk)));
+  auto prof = prof_fn();
+  if (prof) prof(KID_MERGE_BWD, stream, 0);
+  hipError_t e;
+  const int64_t hs = w_mix_head_stride;
+  if (dims->io == NATSL_BF16)
+    e = branch_dtype == NATSL_BF16
+            ? do_merge_bwd_t<bf16, bf16>(dims, q, o_sm, o_gdn, w_mix, hs, g_sm, g_lin, d_out, d_o_sm, d_o_gdn, dq,
+                                         dw_mix, dg_sm, dg_lin, ws, stream)
+            : do_merge_bwd_t<bf16, float>(dims, q, o_sm, o_gdn, w_mix, hs, g_sm, g_lin, d_out, d_o_sm, d_o_gdn, dq,
+                                          dw_mix, dg_sm, dg_lin, ws, stream);
+  else
+    e = branch_dtype == NATSL_BF16
+            ? do_merge_bwd_t<float, bf16>(dims, q, o_sm, o_gdn, w_mix, hs, g_sm, g_lin, d_out, d_o_sm, d_o_gdn, dq,
+                                          dw_mix, dg_sm, dg_lin, ws, stream)
+            : do_merge_bwd_t<float, float>(dims, q, o_sm, o_gdn, w_mix, hs, g_sm, g_lin, d_out, d_o_sm, d_o_gdn, dq,
+                                           dw_mix, dg_sm, dg_lin, ws, stream);
+  if (prof) prof(KID_MERGE_BWD, stream, 1);
+  if (e != hipSuccess) return dev_fail(e, "natsl_merge_backward");
   return ok();
 }
 

@@ -24,6 +24,7 @@ enum {
   KID_SOFTMAX_BWD,
   KID_HANDOFF,
   KID_GDN_BWD,
+  KID_MERGE_BWD,
   KID_COUNT
 };
 
@@ -39,6 +40,14 @@ template <typename Tq, typename Tb, int D>
 hipError_t launch_merge(const Tq* q, const Tb* o_sm, const Tb* o_gdn, const float* w_mix, int64_t hs,
                         const float* g_sm, const float* g_lin, Tq* out, int B, int H, int L,
                         float eps, hipStream_t st, const float* mixd = nullptr);
+
+// merge gradient: d_out fp32; ws holds per-block partial sums
+size_t merge_bwd_ws_bytes(int B, int H, int L, int D);
+template <typename Tq, typename Tb, int D>
+hipError_t launch_merge_backward(const Tq* q, const Tb* o_sm, const Tb* o_gdn, const float* w_mix, int64_t hs,
+                                 const float* g_sm, const float* g_lin, const float* d_out, float* d_sm,
+                                 float* d_gdn, float* dq, float* dw_mix, float* dg_sm, float* dg_lin, void* ws,
+                                 int B, int H, int L, float eps, hipStream_t st);
 
 // cached softmax rows a prefill segment also attends to (chunked prefill):
 // n_committed[b, g] rows (a multiple of 64) of k, v [B, H, cap, D]

@@ -437,6 +437,38 @@ def test_gdn_backward_parity(io, D, L, per_head, alpha):
         assert e <= 1e-4, name
 
 
+@pytest.mark.parametrize("io,branch,D,per_head,gains", [("f32", "f32", 64, False, False),
+                                                        ("bf16", "bf16", 128, True, True),
+                                                        ("bf16", "f32", 128, False, True)])
+def test_merge_backward_parity(io, branch, D, per_head, gains):
+    """Gradient of the merge (both branch outputs, q through the mixing
+    weights, W_mix shared or per head, the gains) against the oracle's exact
+    derivative; each within 1e-4 of its largest magnitude (the kernel works in
+    fp32 on the same inputs; W_mix and gain gradients are sums over every
+    token, added in a fixed order)."""
+    B, H, L = 2, 3, 128
+    say(f"[merge backward] io={io} branch={branch} D={D} per_head={per_head} gains={gains}")
+    rng = np.random.default_rng(95)
+    io_t = torch.bfloat16 if io == "bf16" else torch.float32
+    br_t = torch.bfloat16 if branch == "bf16" else torch.float32
+    mk = lambda scale, dt: torch.from_numpy((scale * rng.standard_normal((B, H, L, D))).astype(np.float32)).cuda().to(dt)
+    q, a, b = mk(1.0, io_t), mk(2.0, br_t), mk(0.5, br_t)
+    wm = rng.normal(0, 0.3, (H, D, 2) if per_head else (D, 2)).astype(np.float32)
+    gs = rng.uniform(0.5, 1.5, D).astype(np.float32) if gains else None
+    gl = rng.uniform(0.5, 1.5, D).astype(np.float32) if gains else None
+    d_out = rng.standard_normal((B, H, L, D)).astype(np.float32)
+    dm = N.dims(B, H, L, D, 64, N.BF16 if io == "bf16" else N.F32)
+    got = N.merge_backward(dm, q, a, b, dev(wm), dev(d_out), w_mix_head_stride=2 * D if per_head else 0,
+                           g_sm=None if gs is None else dev(gs), g_lin=None if gl is None else dev(gl))
+    torch.cuda.synchronize()
+    h64 = lambda x: x.float().cpu().numpy().astype(np.float64)
+    ref = O.merge_backward(h64(q), h64(a), h64(b), wm, d_out, gs, gl)
+    for name, g, rf in zip(("d_o_sm", "d_o_gdn", "dq", "dw_mix", "dg_sm", "dg_lin"), got, ref):
+        e = maxerr(h64(g), rf) / max(1.0, np.abs(rf).max())
+        say(f"  {name}: rel err {e:.2e}")
+        assert e <= 1e-4, name
+
+
 @pytest.mark.parametrize("io,D", [("f32", 64), ("bf16", 128)])
 def test_decode_handoff_then_decode(io, D):
     """natsl_forward over a 192-token prefix, natsl_decode_handoff of its
