@@ -214,6 +214,31 @@ def time_gdn_backward(N, dm, t, wl, route, reps=2):
                 frac_fp32_valu=round(tf / PEAK_FP32_VALU_TFLOPS, 4))
 
 
+def time_merge_backward(N, dm, t, wl, reps=5):
+    """Gradient of the merge on this workload (random bf16 branch outputs, a
+    random fp32 upstream gradient), timed with events; HBM-bound: it reads q,
+    both branch outputs and d_out and writes three fp32 gradients."""
+    import torch
+    shp = t["q"].shape
+    o_sm = torch.randn(shp, dtype=torch.bfloat16, device=t["q"].device)
+    o_gdn = torch.randn_like(o_sm)
+    d_out = torch.randn(shp, dtype=torch.float32, device=t["q"].device)
+    call = lambda: N.merge_backward(dm, t["q"], o_sm, o_gdn, t["w_mix"], d_out)
+    call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    us = 1000.0 * e0.elapsed_time(e1) / reps
+    n = int(np.prod(shp))
+    nbytes = n * (2 + 2 + 2 + 4) + 3 * n * 4
+    return dict(workload=f"gradient of the merge on the {wl.name} prefill", us=round(us, 1), bytes=nbytes,
+                gbs=round(nbytes / (us * 1e-6) / 1e9, 1), frac_hbm=round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4))
+
+
 def time_prefill(args, N, W, O):
     import torch
     wl = W.WORKLOADS[args.workload]
@@ -250,6 +275,7 @@ def time_prefill(args, N, W, O):
     handoff = time_handoff(N, dm, fwd.route, t, wl)
     backward = time_softmax_backward(N, dm, t, wl, sm_pairs(fwd.route.cpu().numpy(), wl.H))
     gdn_backward = time_gdn_backward(N, dm, t, wl, fwd.route)
+    merge_backward = time_merge_backward(N, dm, t, wl)
     route = fwd.route.cpu().numpy()
     ref_route = O.route(inp["x"], inp["w_score"], inp["b_score"])[0] if args.check_route else None
     pairs = sm_pairs(route, wl.H)
@@ -287,6 +313,7 @@ def time_prefill(args, N, W, O):
         handoff=handoff,
         softmax_backward=backward,
         gdn_backward=gdn_backward,
+        merge_backward=merge_backward,
     )
     return res, inp, route
 
@@ -437,11 +464,12 @@ def achievable_peaks():
 PROFILE_CMD = "python3 bench.py --steps 10 --warmup 2 --no-cpu --no-calib --no-alone --decode-steps 20 --profile-copy"
 KERNEL_NAMES = [  # substring of the kernel symbol -> short name
     ("k_softmax_v2", "softmax_masked"), ("k_route", "route"), ("k_compact", "compact"), ("k_gdn_prep", "gdn_prep"),
-    ("k_gdn_scan", "gdn_scan"), ("k_merge", "merge"), ("k_decode_route", "decode_route"),
+    ("k_gdn_scan", "gdn_scan"), ("k_mergeI", "merge"), ("k_decode_route", "decode_route"),
     ("k_decode_gdn", "decode_gdn"), ("k_decode_attn", "decode_attn"), ("k_decode_combine", "decode_combine"),
     ("k_decode_commit", "decode_commit"), ("k_handoff_state", "handoff_state"), ("k_handoff_kv", "handoff_kv"),
     ("k_sm_bwd_delta", "sm_bwd_delta"), ("k_sm_bwd_dq", "sm_bwd_dq"), ("k_sm_bwd_dkdv", "sm_bwd_dkdv"),
     ("k_gdn_bwd_ckpt", "gdn_bwd_ckpt"), ("k_gdn_bwdI", "gdn_bwd"), ("k_gdn_bwd_reduce", "gdn_bwd_reduce"),
+    ("k_merge_bwd_reduce", "merge_bwd_reduce"), ("k_merge_bwdI", "merge_bwd"),
     ("AUnaryFunctor<float, float", "calib_mul_256MiB"),
 ]
 

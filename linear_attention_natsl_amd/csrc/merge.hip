@@ -208,35 +208,48 @@ __global__ void __launch_bounds__(256) k_merge_bwd(const Tq* __restrict__ q, con
 }
 
 // dW_mix (per head when wmix_hs != 0, else over every head) and the gains'
-// gradients from the blocks' partials, added in block order
+// gradients from the blocks' partials: one workgroup per output element, each
+// thread adding a fixed strided subset of the blocks, then a fixed-order tree
+// (deterministic)
 template <int D>
 __global__ void __launch_bounds__(256) k_merge_bwd_reduce(const float* __restrict__ part, int64_t nblk,
                                                           int64_t blk_per_head, int H, int per_head,
                                                           float* __restrict__ dw_mix, float* __restrict__ dg_sm,
                                                           float* __restrict__ dg_lin) {
-  const int e = bid_x() * 256 + tid_x();
+  __shared__ float red[256];
   // outputs: [0, D) dg_sm, [D, 2D) dg_lin, then dW_mix column sums: D (shared) or H D (per head)
-  const int nout = 2 * D + (per_head ? H * D : D);
-  if (e >= nout) return;
-  float s = 0.f;
+  const int e = bid_x(), t = tid_x();
+  int off, hh = 0;
+  bool head_only = false;
   if (e < 2 * D) {
-    const int off = D + e;  // partial slots D .. 3D - 1
-    for (int64_t x = 0; x < nblk; ++x) s += part[x * 3 * D + off];
-    if (e < D) {
-      if (dg_sm) dg_sm[e] = s;
-    } else if (dg_lin) {
-      dg_lin[e - D] = s;
-    }
-    return;
+    off = D + e;  // partial slots D .. 3D - 1
+  } else {
+    const int r = e - 2 * D;
+    hh = per_head ? r / D : 0;
+    off = r % D;
+    head_only = per_head != 0;
   }
-  const int r = e - 2 * D, hh = per_head ? r / D : 0, d = r % D;
-  for (int64_t x = 0; x < nblk; ++x) {
-    const int64_t head = (x / blk_per_head) % H;
-    if (!per_head || head == hh) s += part[x * 3 * D + d];
+  const int64_t count = head_only ? nblk / H : nblk;  // a head's blocks: B runs of blk_per_head
+  float s = 0.f;
+  for (int64_t n = t; n < count; n += 256) {
+    const int64_t x = head_only ? ((n / blk_per_head) * H + hh) * blk_per_head + n % blk_per_head : n;
+    s += part[x * 3 * D + off];
   }
-  if (dw_mix) {
-    dw_mix[((int64_t)hh * D + d) * 2] = s;
-    dw_mix[((int64_t)hh * D + d) * 2 + 1] = -s;
+  red[t] = s;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (t < w) red[t] += red[t + w];
+    __syncthreads();
+  }
+  if (t != 0) return;
+  s = red[0];
+  if (e < D) {
+    if (dg_sm) dg_sm[e] = s;
+  } else if (e < 2 * D) {
+    if (dg_lin) dg_lin[e - D] = s;
+  } else if (dw_mix) {
+    dw_mix[((int64_t)hh * D + off) * 2] = s;
+    dw_mix[((int64_t)hh * D + off) * 2 + 1] = -s;
   }
 }
 
@@ -261,8 +274,8 @@ hipError_t launch_merge_backward(const Tq* q, const Tb* o_sm, const Tb* o_gdn, c
   if (e != hipSuccess) return e;
   const int per_head = hs != 0;
   const int nout = 2 * D + (per_head ? H * D : D);
-  hipLaunchKernelGGL((k_merge_bwd_reduce<D>), dim3((unsigned)((nout + 255) / 256)), dim3(256), 0, st, part, nblk,
-                     (int64_t)(L / TPB), H, per_head, dw_mix, dg_sm, dg_lin);
+  hipLaunchKernelGGL((k_merge_bwd_reduce<D>), dim3((unsigned)nout), dim3(256), 0, st, part, nblk, (int64_t)(L / TPB), H,
+                     per_head, dw_mix, dg_sm, dg_lin);
   return hipGetLastError();
 }
 
