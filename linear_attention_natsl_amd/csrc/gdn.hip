@@ -385,17 +385,12 @@ __global__ void __launch_bounds__(256, (GdnCfg<T, D>::ALIAS ? 3 : 2))
       }
     }
   }
-  // U~ in accumulator order (the scan uses it as the C operand): [rt][n][lane][4];
-  // bf16 for the head-form scan (its U is rounded to bf16 for both products
-  // anyway), fp32 otherwise
+  // U~ in accumulator order (the scan uses it as the C operand): [rt][n][lane][4]
+  // (fp32: in bf16 it added a third to the bf16 workloads' largest
+  // RMS-normalised error for under 1% of the forward's time)
 #pragma unroll
-  for (int n = 0; n < C::NT; ++n) {
-    if constexpr (scan_head_form<T, D>())
-      st4<bf16>(reinterpret_cast<bf16*>(ws.ut) + ((ch * 4 + w) * C::NT + n) * 256 + lane * 4, ut[n][0], ut[n][1],
-                ut[n][2], ut[n][3]);
-    else
-      *reinterpret_cast<f32x4*>(ws.ut + ((ch * 4 + w) * C::NT + n) * 256 + lane * 4) = ut[n];
-  }
+  for (int n = 0; n < C::NT; ++n)
+    *reinterpret_cast<f32x4*>(ws.ut + ((ch * 4 + w) * C::NT + n) * 256 + lane * 4) = ut[n];
   // -W -> A fragments with contraction over d.  Head form: straight from the
   // transposed accumulators (d 32 ks + 4g + j from tile 2 ks, d 32 ks + 16 +
   // 4g + j from tile 2 ks + 1); otherwise through Ks (row layout, 8
@@ -694,15 +689,16 @@ __global__ void __launch_bounds__(256, 1)
 // form); U's B operand (contraction over tokens) likewise.
 // The operands every wave needs (-W, Q, P, K^T: 56 KiB in bf16, plus the
 // decays) go through a 2-stage LDS ring by direct global -> LDS loads issued
-// one chunk ahead, and so do the workgroup's U~ columns (bf16: 8 KiB).  All loads of a chunk, and the output stores of the previous one, are
+// one chunk ahead, and so do the workgroup's U~ columns (16 KiB).  All loads
+// of a chunk, and the output stores of the previous one, are
 // issued a whole chunk before the single vmcnt(0) wait at the top of the next
 // chunk.
 constexpr int SCH_WN = 0;              // -W fragments [rt 4][ks 4][lane][8]
 constexpr int SCH_Q = 16384;           // Q rows, 16-byte chunk q of row r at slot q ^ (r & 15)
 constexpr int SCH_PM = 2 * 16384;      // P fragments (bf16) [rt 4][k2 2][lane][8]
 constexpr int SCH_KT = SCH_PM + 8192;  // K rows, 16-byte chunk q of row r at slot q ^ ((r & 7) << 1)
-constexpr int SCH_UT = SCH_KT + 16384; // the workgroup's U~ columns (bf16 accumulator order) [rt 4][tile 4][lane][4]
-constexpr int SCH_GM = SCH_UT + 8192;  // gamma[64], gamma_C at 64, exp(g_C - g)[64] at 80 (fp32)
+constexpr int SCH_UT = SCH_KT + 16384; // the workgroup's U~ columns (fp32 accumulator order) [rt 4][tile 4][lane][4]
+constexpr int SCH_GM = SCH_UT + 16384; // gamma[64], gamma_C at 64, exp(g_C - g)[64] at 80 (fp32)
 constexpr int SCH_STAGE = SCH_GM + 576;
 constexpr int SCH_ROUTE = 2 * SCH_STAGE;
 constexpr int SCH_NW = 4;              // waves per workgroup
@@ -787,7 +783,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW)
   // NW i + w of each 16 KiB operand; for Q, LDS position e = 64 blk + lane
   // holds 16-byte chunk (e & 15) ^ (r & 15) of row r = e / 16, and r & 15 does
   // not depend on i; K likewise with slot (e & 15) ^ ((r & 7) << 1).  Per
-  // wave: NB blocks each of -W, Q and K, 2 NV of U~, NB / 2 of P and one
+  // wave: NB blocks each of -W, Q and K, 4 NV of U~, NB / 2 of P and one
   // partial block of the decays.
   const uint32_t off_lin = (uint32_t)(w * 1024 + lane * 16);
   const int qr = 4 * w + (lane >> 4);
@@ -796,20 +792,17 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW)
   constexpr int GMW = 36 / NW;  // 16-byte pieces of the 576 decay bytes per wave
   static_assert(36 % NW == 0, "decays split evenly over the waves");
   // op 0: -W, 1: Q, 2: P (8 KiB) and the decays, 3: K, 4: this
-  // workgroup's U~ columns (bf16, 1 KiB blocks of two 16-column tiles of one
-  // row tile)
+  // workgroup's U~ columns ([rt][16-column tile] blocks)
   auto load_part = [&](int cc, int st, int op) {
     const int64_t ch = bh * nc + cc;
     unsigned char* sb = lds + opaque_sgpr(st * SCH_STAGE);
     if (op == 4) {
-      const unsigned char* ub = reinterpret_cast<const unsigned char*>(ws.ut) + ch * 4 * C::NT * 512;
-      constexpr int HP = NV * NW / 2;  // tile pairs per row tile
+      const unsigned char* ub = reinterpret_cast<const unsigned char*>(ws.ut + ch * 4 * C::NT * 256);
 #pragma unroll
-      for (int i = 0; i < 2 * NV; ++i) {
-        const int j = NW * i + w;  // block: row tile j / HP, local tiles 2 (j % HP) and 2 (j % HP) + 1
-        const int rt = j / HP, hp = j % HP;
-        gload_lds16_s(ub + (rt * C::NT + NV * NW * part + 2 * hp) * 512, (uint32_t)(lane * 16),
-                      sb + SCH_UT + j * 1024);
+      for (int i = 0; i < 4 * NV; ++i) {
+        const int j = NW * i + w;  // block: row tile j / (NV NW), local column tile j % (NV NW)
+        const int rt = j / (NV * NW), tl = j % (NV * NW);
+        gload_lds16_s(ub + (rt * C::NT + NV * NW * part + tl) * 1024, (uint32_t)(lane * 16), sb + SCH_UT + j * 1024);
       }
       return;
     }
@@ -840,7 +833,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW)
                     sb + SCH_GM + w * GMW * 16);
   };
   // DMA operations a wave issues per part
-  constexpr int N_W = NB, N_Q = NB, N_U = 2 * NV, N_P = NB / 2 + 1, N_KT = NB;
+  constexpr int N_W = NB, N_Q = NB, N_U = 4 * NV, N_P = NB / 2 + 1, N_KT = NB;
   static_assert(N_W + N_Q + N_U + N_P + N_KT + 16 * NV < 64, "vmcnt range");
   // outputs: a uniform base per store plus one 32-bit byte offset per lane
   // (the SGPR-base store form; 64-bit lane addresses per store cost registers)
@@ -913,10 +906,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW)
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
       for (int nn = 0; nn < NV; ++nn)
-      {
-        const bf16x4 ub4 = *reinterpret_cast<const bf16x4*>(sb + SCH_UT + ((rt * NV * NW + NV * w + nn) * 64 + lane) * 8);
-        u[rt][nn] = f32x4{(float)ub4[0], (float)ub4[1], (float)ub4[2], (float)ub4[3]};
-      }
+        u[rt][nn] = *reinterpret_cast<const f32x4*>(sb + SCH_UT + ((rt * NV * NW + NV * w + nn) * 64 + lane) * 16);
     if (cc > 0) store_o(cc - 1, o_prev);  // outputs of chunk cc - 1
     const bool more = cc + 1 < nc;
     if (more) load_part(cc + 1, st ^ 1, 0);
