@@ -576,3 +576,45 @@ def test_merge_backward_matches_autograd_and_fd():
                 args_m[arr_i][idx] -= h
                 fd = (loss(*args_p) - loss(*args_m)) / (2 * h)
                 assert abs(fd - grad[idx]) <= 1e-7 * max(1.0, abs(fd))
+
+
+def test_layer_gradient_chain_matches_finite_differences():
+    """The layer's gradient for fixed routes is the merge's gradient followed
+    by both branches' (q collects three shares: the mixing weights', the
+    softmax branch's and the Gated DeltaNet branch's).  That chain of oracle
+    gradients against central differences of the whole oracle forward (all
+    inputs but the routes; softmax / linear / softmax chunks of 4 tokens)."""
+    rng = np.random.default_rng(97)
+    B, H, L, D, chunk = 1, 2, 12, 4, 4
+    q, k, v = (rng.standard_normal((B, H, L, D)) for _ in range(3))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    a = rng.uniform(0.8, 0.99, (B, H, L))
+    b = 1.0 / (1.0 + np.exp(-rng.standard_normal((B, H, L))))
+    wm = rng.normal(0, 0.5, (D, 2))
+    gs, gl = rng.uniform(0.5, 1.5, D), rng.uniform(0.5, 1.5, D)
+    r = np.array([[[O.SM, O.LIN, O.SM]]])
+    d_out = rng.standard_normal((B, H, L, D))
+    x = np.zeros((B, L, 3))
+    fwd = O.forward(x, q, k, v, a, b, None, wm, g_sm=gs, g_lin=gl, route_override=r, chunk=chunk)
+    d_sm, d_gdn, dq_mix, dwm, dgs, dgl = O.merge_backward(q, fwd["o_sm"], fwd["o_gdn"], wm, d_out, gs, gl)
+    dq1, dk1, dv1 = O.softmax_branch_backward(q, k, v, r, d_sm, chunk=chunk)
+    dq2, dk2, dv2, da, db, _ = O.gdn_branch_backward(q, k, v, a, b, r, d_gdn, chunk=chunk)
+    grads = {"q": dq_mix + dq1 + dq2, "k": dk1 + dk2, "v": dv1 + dv2, "a": da, "b": db, "wm": dwm,
+             "gs": dgs, "gl": dgl}
+    args = {"q": q, "k": k, "v": v, "a": a, "b": b, "wm": wm, "gs": gs, "gl": gl}
+
+    def loss(p):
+        o = O.forward(x, p["q"], p["k"], p["v"], p["a"], p["b"], None, p["wm"], g_sm=p["gs"], g_lin=p["gl"],
+                      route_override=r, chunk=chunk)["out"]
+        return float(np.sum(o * d_out))
+
+    h = 1e-6
+    for name, g in grads.items():
+        for _ in range(6):
+            idx = tuple(int(rng.integers(0, s)) for s in args[name].shape)
+            pp = {n: x_.copy() for n, x_ in args.items()}
+            pm = {n: x_.copy() for n, x_ in args.items()}
+            pp[name][idx] += h
+            pm[name][idx] -= h
+            fd = (loss(pp) - loss(pm)) / (2 * h)
+            assert abs(fd - g[idx]) <= 1e-6 * max(1.0, abs(fd)), (name, idx, fd, g[idx])
