@@ -470,6 +470,53 @@ def test_merge_backward_parity(io, branch, D, per_head, gains):
 
 
 @pytest.mark.parametrize("io,D", [("f32", 64), ("bf16", 128)])
+def test_layer_gradient_chain(io, D):
+    """The layer's gradient for fixed routes on the GPU: the forward's branch
+    outputs (natsl_softmax_masked with lse, natsl_gdn_chunk), then
+    natsl_merge_backward, natsl_softmax_masked_backward (upstream gradient in
+    the io dtype, as that entry takes it) and natsl_gdn_backward, the three
+    shares of dq summed.  Against the oracle's chain (pinned on the CPU by
+    central differences of the whole layer).  fp32: within 1e-4 of each
+    gradient's largest magnitude; bf16: 1e-2 (the softmax branch's upstream
+    gradient is rounded to bf16)."""
+    B, H, L = 2, 2, 320
+    wl, inp = small_case(io, B=B, H=H, L=L, D=D, seed=99)
+    say(f"[layer gradient] io={io} D={D}")
+    rng = np.random.default_rng(98)
+    r = np.broadcast_to(inp["plan"], (B, 1, L // 64)).copy().astype(np.int32)
+    gs = rng.uniform(0.5, 1.5, D).astype(np.float32)
+    gl = rng.uniform(0.5, 1.5, D).astype(np.float32)
+    d_out = rng.standard_normal((B, H, L, D)).astype(np.float32)
+    io_t = torch.bfloat16 if io == "bf16" else torch.float32
+    dm = N.dims(B, H, L, D, wl.d, io_code(inp))
+    tq, tk, tv = dev(inp["q"], io), dev(inp["k"], io), dev(inp["v"], io)
+    ta, tb, tr = dev(inp["alpha"]), dev(inp["beta"]), dev(r)
+    _, sel, nsb, _ = N.route(dm, None, None, route_in=tr)
+    o_sm, lse = N.softmax_masked(dm, tq, tk, tv, sel, nsb, o_dtype=io_t, want_lse=True)
+    o_gdn, _ = N.gdn_chunk(dm, tq, tk, tv, ta, tb, tr, o_dtype=io_t)
+    d_sm, d_gdn, dq_mix, dwm, dgs, dgl = N.merge_backward(dm, tq, o_sm, o_gdn, dev(inp["w_mix"]), dev(d_out),
+                                                          g_sm=dev(gs), g_lin=dev(gl))
+    dq1, dk1, dv1 = N.softmax_masked_backward(dm, tq, tk, tv, sel, nsb, o_sm, lse, d_sm.to(io_t))
+    dq2, dk2, dv2, da, db, _ = N.gdn_backward(dm, tq, tk, tv, ta, tb, tr, d_gdn)
+    got = {"dq": dq_mix + dq1 + dq2, "dk": dk1 + dk2, "dv": dv1 + dv2, "dalpha": da, "dbeta": db,
+           "dw_mix": dwm, "dg_sm": dgs, "dg_lin": dgl}
+    torch.cuda.synchronize()
+    fwd = O.forward(inp["x"], inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], None, inp["w_mix"],
+                    g_sm=gs, g_lin=gl, route_override=r)
+    e_sm, e_gdn, eq_mix, ewm, egs, egl = O.merge_backward(inp["q"], fwd["o_sm"], fwd["o_gdn"], inp["w_mix"], d_out,
+                                                          gs, gl)
+    eq1, ek1, ev1 = O.softmax_branch_backward(inp["q"], inp["k"], inp["v"], r, e_sm)
+    eq2, ek2, ev2, ea, eb, _ = O.gdn_branch_backward(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], r, e_gdn)
+    ref = {"dq": eq_mix + eq1 + eq2, "dk": ek1 + ek2, "dv": ev1 + ev2, "dalpha": ea, "dbeta": eb, "dw_mix": ewm,
+           "dg_sm": egs, "dg_lin": egl}
+    tol = 1e-4 if io == "f32" else 1e-2
+    for name in ref:
+        e = maxerr(host(got[name]), ref[name]) / max(1.0, np.abs(ref[name]).max())
+        say(f"  {name}: rel err {e:.2e}")
+        assert e <= tol, name
+
+
+@pytest.mark.parametrize("io,D", [("f32", 64), ("bf16", 128)])
 def test_decode_handoff_then_decode(io, D):
     """natsl_forward over a 192-token prefix, natsl_decode_handoff of its
     route, K/V and final state, then 64 decode steps (one chunk completion):
