@@ -24,8 +24,10 @@
 //   k_gdn_bwd         chunks in reverse: recompute the chunk's per-token states
 //                     into a scratch slot, then sweep its tokens backward
 //   k_gdn_bwd_reduce  dq, dk, dalpha, dbeta from the groups' partials
-// Three barriers per token: this is the plain per-token form (the chunkwise
-// form on MFMA is not built).
+// Each thread reads its own rows of k and q and its column of v and d_o from
+// global memory (a token ahead), so a token needs one barrier, for the
+// column-sum exchange.  This is the plain per-token form (the chunkwise form
+// on MFMA is not built).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -39,21 +41,17 @@ struct GdnBwdCfg {
   static constexpr int NCG = D / CW;  // column groups (workgroups) per head
   static constexpr int NT = 256;      // 16 columns x 16 row groups
   static constexpr int RPT = D / 16;  // state rows per thread
-  // LDS (floats): vec[2][2 D + 2 CW] (k, q, the group's v and d_o, by token
-  // parity), part[2][2][4][CW] (per-wave column sums of a and w, by parity),
-  // red[4][2] (per-wave dalpha, dbeta)
-  static constexpr int VEC = 2 * D + 2 * CW;
-  static constexpr int OFF_VEC = 0;
-  static constexpr int OFF_PART = OFF_VEC + 2 * VEC;
-  static constexpr int OFF_RED = OFF_PART + 2 * 2 * 4 * CW;
-  static constexpr int LDS_FLOATS = OFF_RED + 8;
+  // LDS: part[2][2][4][CW] floats (per-wave column sums of a and w, by token
+  // parity); every other per-token value reaches the threads from global
+  // memory directly, so a token needs one barrier (the column-sum exchange)
+  static constexpr int LDS_FLOATS = 2 * 2 * 4 * CW;
 };
 
 size_t gdn_bwd_ws_bytes(int B, int H, int L, int D) {
   const size_t nc = (size_t)L / CHUNK, ntok = (size_t)B * H * L, ncg = (size_t)D / 16;
   const size_t floats = (size_t)B * H * (nc + CHUNK) * D * D  // chunk-start states, chunk token states
                         + 2 * ntok * ncg * D                  // dq, dk partials
-                        + 2 * ntok * ncg;                     // dalpha, dbeta partials
+                        + 2 * ntok * ncg * 4;                 // dalpha, dbeta partials (per wave)
   return (floats * 4 + 255) / 256 * 256;
 }
 
@@ -68,27 +66,58 @@ __device__ __forceinline__ float col_total(const float* part, int jl) {
   return (part[jl] + part[16 + jl]) + (part[32 + jl] + part[48 + jl]);
 }
 
+// A token's inputs as one thread needs them: k (and q) at its RPT rows, v
+// (and d_o) at its column, the decays
+template <int RPT>
+struct TokIn {
+  float k[RPT], q[RPT];
+  float v, d_o, al, be;
+};
+template <typename T, int D, bool BWD>
+__device__ __forceinline__ void load_tok(TokIn<D / 16>& x, const T* kh, const T* qh, const T* vh, const float* doh,
+                                         const float* ah, const float* bth, int tt, int r0, int j) {
+  constexpr int RPT = D / 16;
+  if constexpr (RPT % 8 == 0) {  // whole 8-element vectors of the thread's rows
+    float kk[8], qq[8];
+#pragma unroll
+    for (int h8 = 0; h8 < RPT; h8 += 8) {
+      load8f<T>(kh + (int64_t)tt * D + r0 + h8, kk);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x.k[h8 + i] = kk[i];
+      if (BWD) {
+        load8f<T>(qh + (int64_t)tt * D + r0 + h8, qq);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x.q[h8 + i] = qq[i];
+      }
+    }
+  } else {  // fewer rows than a vector: exactly the thread's rows
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      x.k[i] = to_f32(kh[(int64_t)tt * D + r0 + i]);
+      if (BWD) x.q[i] = to_f32(qh[(int64_t)tt * D + r0 + i]);
+    }
+  }
+  x.v = to_f32(vh[(int64_t)tt * D + j]);
+  x.d_o = BWD ? doh[(int64_t)tt * D + j] : 0.f;
+  x.al = ah[tt];
+  x.be = bth[tt];
+}
+
 // One forward token on the thread's rows of its column:
 //   S <- a (S - b k (k^T S)) + b k v^T
-// vec: this token's [k (D) | . (D) | v of the group (16)], staged by the caller
-// before the first barrier; part: this token's exchange buffer [4][16].
+// part: this token's exchange buffer [4][16] (alternating by token parity)
 template <int D>
-__device__ __forceinline__ void gdn_fwd_token(float (&S)[D / 16], const float* vec, float* part, int jl, int rg,
-                                              int wv, int lane, float al, float be) {
+__device__ __forceinline__ void gdn_fwd_token(float (&S)[D / 16], const TokIn<D / 16>& x, float* part, int jl, int wv,
+                                              int lane) {
   constexpr int RPT = D / 16;
-  const int r0 = rg * RPT;
-  __syncthreads();  // vec staged
   float p4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) p4[i & 3] += S[i] * vec[r0 + i];
+  for (int i = 0; i < RPT; ++i) p4[i & 3] += S[i] * x.k[i];
   col_part((p4[0] + p4[1]) + (p4[2] + p4[3]), part, jl, wv, lane);
   __syncthreads();  // column sums exchanged
-  const float a = col_total(part, jl), vj = vec[2 * D + jl];
+  const float a = col_total(part, jl);
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) {
-    const float ki = vec[r0 + i];
-    S[i] = al * (S[i] - be * ki * a) + be * ki * vj;
-  }
+  for (int i = 0; i < RPT; ++i) S[i] = x.al * (S[i] - x.be * x.k[i] * a) + x.be * x.k[i] * x.v;
 }
 
 template <typename T, int D>
@@ -116,27 +145,15 @@ __global__ void __launch_bounds__(256) k_gdn_bwd_ckpt(const T* __restrict__ k, c
     S[i] = S_init ? S_init[((int64_t)bh * D + r0 + i) * D + j] : 0.f;
     carry[i] = S[i];
   }
-  // this thread's staged value (k, or v of the group) and the decays, loaded
-  // a token ahead; dst: its place in vec (-1: none)
-  const int dst = t < D ? t : (t < D + 16 ? 2 * D + (t - D) : -1);
-  auto ld = [&](int tt) {
-    return t < D ? to_f32(kh[(int64_t)tt * D + t]) : (t < D + 16 ? to_f32(vh[(int64_t)tt * D + C::CW * cg + (t - D)]) : 0.f);
-  };
-  float nx = ld(0), na = ah[0], nb = bth[0];
+  TokIn<C::RPT> nx;  // the next token's inputs, loaded a token ahead
+  load_tok<T, D, false>(nx, kh, kh, vh, nullptr, ah, bth, 0, r0, j);
   for (int c = 0; c < nc; ++c) {
 #pragma unroll
     for (int i = 0; i < C::RPT; ++i) ck[((int64_t)c * D + r0 + i) * D + j] = carry[i];
     for (int tt = c * CHUNK; tt < (c + 1) * CHUNK; ++tt) {
-      float* vec = lds_f + C::OFF_VEC + (tt & 1) * C::VEC;
-      float* part = lds_f + C::OFF_PART + (tt & 1) * 2 * 4 * C::CW;
-      const float cur = nx, al = na, be = nb;
-      if (tt + 1 < L) {
-        nx = ld(tt + 1);
-        na = ah[tt + 1];
-        nb = bth[tt + 1];
-      }
-      if (dst >= 0) vec[dst] = cur;
-      gdn_fwd_token<D>(S, vec, part, jl, rg, wv, lane, al, be);
+      const TokIn<C::RPT> cur = nx;
+      if (tt + 1 < L) load_tok<T, D, false>(nx, kh, kh, vh, nullptr, ah, bth, tt + 1, r0, j);
+      gdn_fwd_token<D>(S, cur, lds_f + (tt & 1) * 4 * C::CW, jl, wv, lane);
     }
     const bool lin = rt[c] == kRouteLinear;
 #pragma unroll
@@ -159,7 +176,6 @@ __global__ void __launch_bounds__(256) k_gdn_bwd(const T* __restrict__ q, const 
                                                  int G) {
   using C = GdnBwdCfg<D>;
   extern __shared__ float lds_f[];
-  float* red = lds_f + C::OFF_RED;
   const int nc = L / CHUNK;
   const int bh = bid_x() / C::NCG, cg = bid_x() % C::NCG, b = bh / H, h = bh % H;
   const int grp = (G == 1) ? 0 : h;
@@ -180,90 +196,68 @@ __global__ void __launch_bounds__(256) k_gdn_bwd(const T* __restrict__ q, const 
 #pragma unroll
   for (int i = 0; i < C::RPT; ++i) Gc[i] = dS_final ? dS_final[((int64_t)bh * D + r0 + i) * D + j] : 0.f;
 
-  // staged values: slot A (t < 2 D) k or q, slot B (t < 32) v or d_o of the group
-  const int dstA = t < 2 * D ? t : -1;
-  const int dstB = t < 2 * C::CW ? 2 * D + t : -1;
-  auto ldA = [&](int tt) {
-    return t < D ? to_f32(kh[(int64_t)tt * D + t]) : (t < 2 * D ? to_f32(qh[(int64_t)tt * D + (t - D)]) : 0.f);
-  };
-  auto ldB = [&](int tt) {
-    return t < C::CW ? to_f32(vh[(int64_t)tt * D + C::CW * cg + t])
-                     : (t < 2 * C::CW ? doh[(int64_t)tt * D + C::CW * cg + (t - C::CW)] : 0.f);
-  };
-  auto ldF = [&](int tt) {  // the forward's staged value: k, or v of the group
-    return t < D ? to_f32(kh[(int64_t)tt * D + t]) : (t < D + 16 ? to_f32(vh[(int64_t)tt * D + C::CW * cg + (t - D)]) : 0.f);
-  };
-  const int dstF = t < D ? t : (t < D + 16 ? 2 * D + (t - D) : -1);
-
   for (int c = nc - 1; c >= 0; --c) {
     const int c0 = c * CHUNK;
+    // the previous chunk's last sweep token read the parity-0 exchange buffer
+    // that this chunk's first recompute token writes
+    __syncthreads();
     // recompute the chunk's states: slot s holds the state before token c0 + s
     float S[C::RPT];
 #pragma unroll
     for (int i = 0; i < C::RPT; ++i) S[i] = ck[((int64_t)c * D + r0 + i) * D + j];
-    float nx = ldF(c0), na = ah[c0], nb = bth[c0];
+    TokIn<C::RPT> nx;
+    load_tok<T, D, false>(nx, kh, kh, vh, nullptr, ah, bth, c0, r0, j);
     for (int s = 0; s < CHUNK; ++s) {
       const int tt = c0 + s;
 #pragma unroll
       for (int i = 0; i < C::RPT; ++i) sc[((int64_t)s * D + r0 + i) * D + j] = S[i];
       if (s == CHUNK - 1) break;  // the chunk's end state is not needed
-      float* vec = lds_f + C::OFF_VEC + (tt & 1) * C::VEC;
-      float* part = lds_f + C::OFF_PART + (tt & 1) * 2 * 4 * C::CW;
-      const float cur = nx, al = na, be = nb;
-      nx = ldF(tt + 1);  // tt + 1 <= c0 + 63: inside the chunk
-      na = ah[tt + 1];
-      nb = bth[tt + 1];
-      if (dstF >= 0) vec[dstF] = cur;
-      gdn_fwd_token<D>(S, vec, part, jl, rg, wv, lane, al, be);
+      const TokIn<C::RPT> cur = nx;
+      load_tok<T, D, false>(nx, kh, kh, vh, nullptr, ah, bth, tt + 1, r0, j);  // tt + 1 <= c0 + 63
+      gdn_fwd_token<D>(S, cur, lds_f + (tt & 1) * 4 * C::CW, jl, wv, lane);
     }
-    __syncthreads();  // every read of the recompute's buffers is done
     const bool lin = rt[c] == kRouteLinear;
     float Gm[C::RPT];
 #pragma unroll
     for (int i = 0; i < C::RPT; ++i) Gm[i] = lin ? Gc[i] : 0.f;
-    // staged values and decays loaded a token ahead (the sweep runs backward)
-    float nA = ldA(c0 + CHUNK - 1), nB = ldB(c0 + CHUNK - 1);
-    float nal = ah[c0 + CHUNK - 1], nbe = bth[c0 + CHUNK - 1];
-    float nS[C::RPT];  // the thread's elements of S_{t-1}, also a token ahead
+    // inputs and the thread's elements of S_{t-1}, loaded a token ahead (the
+    // sweep runs backward)
+    TokIn<C::RPT> nt;
+    load_tok<T, D, true>(nt, kh, qh, vh, doh, ah, bth, c0 + CHUNK - 1, r0, j);
+    float nS[C::RPT];
 #pragma unroll
     for (int i = 0; i < C::RPT; ++i) nS[i] = sc[((int64_t)(CHUNK - 1) * D + r0 + i) * D + j];
     for (int tt = c0 + CHUNK - 1; tt >= c0; --tt) {
-      float* vec = lds_f + C::OFF_VEC + (tt & 1) * C::VEC;  // [k | q | v (16) | d_o (16)]
-      float* part = lds_f + C::OFF_PART + (tt & 1) * 2 * 4 * C::CW;  // [a: 4 x 16 | w: 4 x 16]
-      const float xA = nA, xB = nB, al = nal, be = nbe;
+      // (the recompute's last exchange buffer was token c0 + 62, parity 0; the
+      // sweep's first is token c0 + 63, parity 1, and the parities alternate)
+      float* part = lds_f + (tt & 1) * 2 * 4 * C::CW;  // [a: 4 x 16 | w: 4 x 16]
+      const TokIn<C::RPT> x = nt;
       float Sp[C::RPT];
 #pragma unroll
       for (int i = 0; i < C::RPT; ++i) Sp[i] = nS[i];
       if (tt > c0) {
-        nA = ldA(tt - 1);
-        nB = ldB(tt - 1);
-        nal = ah[tt - 1];
-        nbe = bth[tt - 1];
+        load_tok<T, D, true>(nt, kh, qh, vh, doh, ah, bth, tt - 1, r0, j);
 #pragma unroll
         for (int i = 0; i < C::RPT; ++i) nS[i] = sc[((int64_t)(tt - 1 - c0) * D + r0 + i) * D + j];
       }
-      if (dstA >= 0) vec[dstA] = xA;
-      if (dstB >= 0) vec[dstB] = xB;
-      __syncthreads();  // vectors staged
-      const float vj = vec[2 * D + jl], doj = vec[2 * D + C::CW + jl];
       float pa[4] = {0.f, 0.f, 0.f, 0.f}, pw[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < C::RPT; ++i) {
-        const float ki = vec[r0 + i];
-        Gm[i] += vec[D + r0 + i] * doj;  // o_t = S_t^T q_t
-        pa[i & 3] += Sp[i] * ki;
-        pw[i & 3] += Gm[i] * ki;
+        Gm[i] += x.q[i] * x.d_o;  // o_t = S_t^T q_t
+        pa[i & 3] += Sp[i] * x.k[i];
+        pw[i & 3] += Gm[i] * x.k[i];
       }
       col_part((pa[0] + pa[1]) + (pa[2] + pa[3]), part, jl, wv, lane);
       col_part((pw[0] + pw[1]) + (pw[2] + pw[3]), part + 4 * C::CW, jl, wv, lane);
       __syncthreads();  // column sums exchanged
       const float a = col_total(part, jl), w = col_total(part + 4 * C::CW, jl);
+      const float al = x.al, be = x.be, vj = x.v, doj = x.d_o;
       const float cv = be * vj - al * be * a, cw = al * be * w;
       float pal = 0.f;
       const int64_t tok = tok0 + tt;
 #pragma unroll
       for (int i = 0; i < C::RPT; ++i) {
-        const float ki = vec[r0 + i];
+        const float ki = x.k[i];
         const float erased = Sp[i] - be * ki * a;
         // this group's share of the row sums dq = S_t d_o and dk
         const float rq = dpp_group_sum<16>((al * erased + be * ki * vj) * doj);
@@ -278,16 +272,11 @@ __global__ void __launch_bounds__(256) k_gdn_bwd(const T* __restrict__ q, const 
       float pbe = (rg == 0) ? w * (vj - al * a) : 0.f;
       pal = wave_sum64(pal);
       pbe = wave_sum64(pbe);
-      if (lane == 0) {
-        red[2 * wv] = pal;
-        red[2 * wv + 1] = pbe;
+      if (lane == 0) {  // per-wave partials, added by k_gdn_bwd_reduce
+        da_p[(tok * C::NCG + cg) * 4 + wv] = pal;
+        db_p[(tok * C::NCG + cg) * 4 + wv] = pbe;
       }
       if (rg == 0) dv[tok * D + j] = be * w;
-      __syncthreads();  // scalar partials written
-      if (t == 0) {
-        da_p[tok * C::NCG + cg] = (red[0] + red[2]) + (red[4] + red[6]);
-        db_p[tok * C::NCG + cg] = (red[1] + red[3]) + (red[5] + red[7]);
-      }
     }
 #pragma unroll
     for (int i = 0; i < C::RPT; ++i) Gc[i] = Gm[i] + (lin ? 0.f : Gc[i]);
@@ -298,7 +287,8 @@ __global__ void __launch_bounds__(256) k_gdn_bwd(const T* __restrict__ q, const 
   }
 }
 
-// dq, dk, dalpha, dbeta: the column groups' partials added in group order
+// dq, dk, dalpha, dbeta: the column groups' (and waves') partials added in a
+// fixed order
 template <int D>
 __global__ void __launch_bounds__(256) k_gdn_bwd_reduce(const float* __restrict__ dq_p, const float* __restrict__ dk_p,
                                                         const float* __restrict__ da_p, const float* __restrict__ db_p,
@@ -321,9 +311,9 @@ __global__ void __launch_bounds__(256) k_gdn_bwd_reduce(const float* __restrict_
   if (i == 0) {
     float sa = 0.f, sb = 0.f;
 #pragma unroll
-    for (int cg = 0; cg < NCG; ++cg) {
-      sa += da_p[tok * NCG + cg];
-      sb += db_p[tok * NCG + cg];
+    for (int x = 0; x < NCG * 4; ++x) {
+      sa += da_p[tok * NCG * 4 + x];
+      sb += db_p[tok * NCG * 4 + x];
     }
     dalpha[tok] = sa;
     dbeta[tok] = sb;
@@ -343,7 +333,7 @@ hipError_t launch_gdn_backward(const T* q, const T* k, const T* v, const float* 
   float* dq_p = scratch + (size_t)B * H * CHUNK * D * D;
   float* dk_p = dq_p + (size_t)ntok * C::NCG * D;
   float* da_p = dk_p + (size_t)ntok * C::NCG * D;
-  float* db_p = da_p + (size_t)ntok * C::NCG;
+  float* db_p = da_p + (size_t)ntok * C::NCG * 4;
   const size_t lds = C::LDS_FLOATS * 4;
   const unsigned grid = (unsigned)(B * H * C::NCG);
   hipLaunchKernelGGL((k_gdn_bwd_ckpt<T, D>), dim3(grid), dim3(C::NT), lds, st, k, v, alpha, beta, route, S_init,
