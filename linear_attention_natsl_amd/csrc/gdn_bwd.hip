@@ -13,10 +13,11 @@
 // linear-routed; otherwise it passes straight to the chunk start and the
 // chunk's tokens see only their own outputs' gradients.
 //
-// The columns of S (and of G) evolve independently, so each head's 16-column
-// groups run in workgroups of their own (D / 16 per head).  Thread (jl, rg)
-// holds rows rg D/16 .. of column 16 cg + jl: the column sums (S^T k, G^T k)
-// are a row-swap sum over the wave's 4 lane groups plus one LDS exchange
+// The columns of S (and of G) evolve independently, so each head's 8-column
+// groups run in workgroups of their own (D / 8 per head: 256 workgroups for 16
+// heads, a wave on every SIMD).  Thread (jl, rg) holds the D / 32 rows
+// rg D/32 .. of column 8 cg + jl: the column sums (S^T k, G^T k) are a lane
+// swap and a row-swap sum over the wave's 8 row groups plus one LDS exchange
 // across the 4 waves; the row sums (dq, dk) and the scalar gradients (dalpha,
 // dbeta) are per-group partials, added over the groups in a fixed order by a
 // last kernel (so the result does not depend on scheduling).  Launches:
@@ -37,10 +38,12 @@ constexpr int kRouteLinear = 1;  // route id of the linear (Gated DeltaNet) oper
 
 template <int D>
 struct GdnBwdCfg {
-  static constexpr int CW = 16;       // state columns per workgroup
+  static constexpr int CW = 8;        // state columns per workgroup
   static constexpr int NCG = D / CW;  // column groups (workgroups) per head
-  static constexpr int NT = 256;      // 16 columns x 16 row groups
-  static constexpr int RPT = D / 16;  // state rows per thread
+  static constexpr int NT = 256;      // CW columns x NT / CW row groups
+  static constexpr int RPT = D * CW / NT;  // state rows per thread
+  static constexpr int PF = 4;        // tokens of inputs in flight (ring depth); divides the chunk
+  static_assert(CW == 8 && CHUNK % PF == 0, "column and row sums assume 8 columns");
   // LDS: part[2][2][4][CW] floats (per-wave column sums of a and w, by token
   // parity); every other per-token value reaches the threads from global
   // memory directly, so a token needs one barrier (the column-sum exchange)
@@ -48,49 +51,75 @@ struct GdnBwdCfg {
 };
 
 size_t gdn_bwd_ws_bytes(int B, int H, int L, int D) {
-  const size_t nc = (size_t)L / CHUNK, ntok = (size_t)B * H * L, ncg = (size_t)D / 16;
+  const size_t nc = (size_t)L / CHUNK, ntok = (size_t)B * H * L, ncg = (size_t)D / GdnBwdCfg<128>::CW;
   const size_t floats = (size_t)B * H * (nc + CHUNK) * D * D  // chunk-start states, chunk token states
                         + 2 * ntok * ncg * D                  // dq, dk partials
                         + 2 * ntok * ncg * 4;                 // dalpha, dbeta partials (per wave)
   return (floats * 4 + 255) / 256 * 256;
 }
 
-// sum over the workgroup's 16 row groups of a per-thread partial for the
-// thread's column: the wave's 4 lane groups by row swaps, the 4 waves through
-// LDS (part[4][16]); the caller's barrier separates the write and the reads
+// sum over the workgroup's 32 row groups of a per-thread partial for the
+// thread's column: lanes l and l + 8 of each 16-lane row by a DPP rotate, the
+// wave's 4 rows by row swaps, the 4 waves through LDS (part[4][CW]); the
+// caller's barrier separates the write and the reads
 __device__ __forceinline__ void col_part(float x, float* part, int jl, int wv, int lane) {
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, true));  // row_ror 8
   x = group4_sum(x);
-  if (lane < 16) part[wv * 16 + jl] = x;
+  if (lane < 8) part[wv * 8 + jl] = x;
 }
 __device__ __forceinline__ float col_total(const float* part, int jl) {
-  return (part[jl] + part[16 + jl]) + (part[32 + jl] + part[48 + jl]);
+  return (part[jl] + part[8 + jl]) + (part[16 + jl] + part[24 + jl]);
+}
+
+// One reduce-scatter step over lane pairs given by a DPP pattern: of the N
+// values, the lane keeps the lower half (keep_lo) or the upper half, adds the
+// partner's copy of that half, and leaves the result in v[0 .. N/2).
+template <int N, int CTRL>
+__device__ __forceinline__ void rs_step(float* v, bool keep_lo) {
+#pragma unroll
+  for (int k = 0; k < N / 2; ++k) {
+    const float send = keep_lo ? v[k + N / 2] : v[k];
+    const float keep = keep_lo ? v[k] : v[k + N / 2];
+    v[k] = keep + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send), CTRL, 0xF, 0xF, true));
+  }
+}
+// Sum of each of the N values over the 8 lanes of a row group (lanes jl =
+// 0..7, 8-aligned); lane jl returns the sum of value jl % N.  The pairings are
+// l <-> 7 - l, l <-> l ^ 2, l <-> l ^ 1, which together span the 8 lanes.
+template <int N>
+__device__ __forceinline__ float group8_reduce_scatter(float* v, int jl) {
+  static_assert(N == 8 || N == 4, "8 or 4 values");
+  if constexpr (N == 8) {
+    rs_step<8, 0x141>(v, (jl & 4) == 0);  // row_half_mirror
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v[k]), 0x141, 0xF, 0xF, true));
+  }
+  rs_step<4, 0x4E>(v, (jl & 2) == 0);  // quad_perm 2,3,0,1
+  rs_step<2, 0xB1>(v, (jl & 1) == 0);  // quad_perm 1,0,3,2
+  return v[0];
+}
+
+// alpha or beta of token c0 + s, from the chunk's values held one per lane
+__device__ __forceinline__ float lane_bcast(float x, int s) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), s));
 }
 
 // A token's inputs as one thread needs them: k (and q) at its RPT rows, v
-// (and d_o) at its column, the decays
+// (and d_o) at its column
 template <int RPT>
 struct TokIn {
   float k[RPT], q[RPT];
-  float v, d_o, al, be;
+  float v, d_o;
 };
 template <typename T, int D, bool BWD>
-__device__ __forceinline__ void load_tok(TokIn<D / 16>& x, const T* kh, const T* qh, const T* vh, const float* doh,
-                                         const float* ah, const float* bth, int tt, int r0, int j) {
-  constexpr int RPT = D / 16;
-  if constexpr (RPT % 8 == 0) {  // whole 8-element vectors of the thread's rows
-    float kk[8], qq[8];
-#pragma unroll
-    for (int h8 = 0; h8 < RPT; h8 += 8) {
-      load8f<T>(kh + (int64_t)tt * D + r0 + h8, kk);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) x.k[h8 + i] = kk[i];
-      if (BWD) {
-        load8f<T>(qh + (int64_t)tt * D + r0 + h8, qq);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) x.q[h8 + i] = qq[i];
-      }
-    }
-  } else {  // fewer rows than a vector: exactly the thread's rows
+__device__ __forceinline__ void load_tok(TokIn<GdnBwdCfg<D>::RPT>& x, const T* kh, const T* qh, const T* vh,
+                                         const float* doh, int tt, int r0, int j) {
+  constexpr int RPT = GdnBwdCfg<D>::RPT;
+  if constexpr (RPT == 4) {  // one 4-element vector of the thread's rows
+    load4f<T>(kh + (int64_t)tt * D + r0, x.k);
+    if (BWD) load4f<T>(qh + (int64_t)tt * D + r0, x.q);
+  } else {  // exactly the thread's rows
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       x.k[i] = to_f32(kh[(int64_t)tt * D + r0 + i]);
@@ -99,25 +128,38 @@ __device__ __forceinline__ void load_tok(TokIn<D / 16>& x, const T* kh, const T*
   }
   x.v = to_f32(vh[(int64_t)tt * D + j]);
   x.d_o = BWD ? doh[(int64_t)tt * D + j] : 0.f;
-  x.al = ah[tt];
-  x.be = bth[tt];
 }
 
-// One forward token on the thread's rows of its column:
-//   S <- a (S - b k (k^T S)) + b k v^T
-// part: this token's exchange buffer [4][16] (alternating by token parity)
+// the thread's RPT state elements, contiguous in the scratch (8-byte aligned)
+template <int RPT>
+__device__ __forceinline__ void store_state(float* p, const float (&S)[RPT]) {
+#pragma unroll
+  for (int h = 0; h < RPT; h += 2) *(float2*)(p + h) = make_float2(S[h], S[h + 1]);
+}
+template <int RPT>
+__device__ __forceinline__ void load_state(float (&S)[RPT], const float* p) {
+#pragma unroll
+  for (int h = 0; h < RPT; h += 2) {
+    const float2 x = *(const float2*)(p + h);
+    S[h] = x.x;
+    S[h + 1] = x.y;
+  }
+}
+
+// one forward token on the thread's elements: a = S^T k (column sums), then
+// S <- al (S - be k a^T) + be k v^T
 template <int D>
-__device__ __forceinline__ void gdn_fwd_token(float (&S)[D / 16], const TokIn<D / 16>& x, float* part, int jl, int wv,
-                                              int lane) {
-  constexpr int RPT = D / 16;
+__device__ __forceinline__ void gdn_fwd_token(float (&S)[GdnBwdCfg<D>::RPT], const TokIn<GdnBwdCfg<D>::RPT>& x,
+                                              float al, float be, float* part, int jl, int wv, int lane) {
+  constexpr int RPT = GdnBwdCfg<D>::RPT;
   float p4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < RPT; ++i) p4[i & 3] += S[i] * x.k[i];
   col_part((p4[0] + p4[1]) + (p4[2] + p4[3]), part, jl, wv, lane);
-  __syncthreads();  // column sums exchanged
+  lds_barrier();  // column sums exchanged (global loads stay in flight)
   const float a = col_total(part, jl);
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) S[i] = x.al * (S[i] - x.be * x.k[i] * a) + x.be * x.k[i] * x.v;
+  for (int i = 0; i < RPT; ++i) S[i] = al * (S[i] - be * x.k[i] * a) + be * x.k[i] * x.v;
 }
 
 template <typename T, int D>
@@ -132,7 +174,7 @@ __global__ void __launch_bounds__(256) k_gdn_bwd_ckpt(const T* __restrict__ k, c
   const int bh = bid_x() / C::NCG, cg = bid_x() % C::NCG, b = bh / H, h = bh % H;
   const int grp = (G == 1) ? 0 : h;
   const int32_t* rt = route + ((int64_t)b * G + grp) * nc;
-  const int t = tid_x(), jl = t & 15, rg = t >> 4, wv = wave_id(), lane = lane_id();
+  const int t = tid_x(), jl = t % C::CW, rg = t / C::CW, wv = wave_id(), lane = lane_id();
   const int j = C::CW * cg + jl, r0 = rg * C::RPT;
   const T* kh = k + (int64_t)bh * L * D;
   const T* vh = v + (int64_t)bh * L * D;
@@ -145,15 +187,22 @@ __global__ void __launch_bounds__(256) k_gdn_bwd_ckpt(const T* __restrict__ k, c
     S[i] = S_init ? S_init[((int64_t)bh * D + r0 + i) * D + j] : 0.f;
     carry[i] = S[i];
   }
-  TokIn<C::RPT> nx;  // the next token's inputs, loaded a token ahead
-  load_tok<T, D, false>(nx, kh, kh, vh, nullptr, ah, bth, 0, r0, j);
+  TokIn<C::RPT> ring[C::PF];  // slot u: the token tt with tt % PF == u, PF tokens ahead
+#pragma unroll
+  for (int u = 0; u < C::PF; ++u) load_tok<T, D, false>(ring[u], kh, kh, vh, nullptr, u, r0, j);  // L >= 64
   for (int c = 0; c < nc; ++c) {
+    const float al_c = ah[c * CHUNK + lane], be_c = bth[c * CHUNK + lane];  // lane s: token c0 + s
 #pragma unroll
     for (int i = 0; i < C::RPT; ++i) ck[((int64_t)c * D + r0 + i) * D + j] = carry[i];
-    for (int tt = c * CHUNK; tt < (c + 1) * CHUNK; ++tt) {
-      const TokIn<C::RPT> cur = nx;
-      if (tt + 1 < L) load_tok<T, D, false>(nx, kh, kh, vh, nullptr, ah, bth, tt + 1, r0, j);
-      gdn_fwd_token<D>(S, cur, lds_f + (tt & 1) * 4 * C::CW, jl, wv, lane);
+    for (int s0 = 0; s0 < CHUNK; s0 += C::PF) {
+#pragma unroll
+      for (int u = 0; u < C::PF; ++u) {
+        const int s = s0 + u, tt = c * CHUNK + s;
+        const TokIn<C::RPT> cur = ring[u];
+        if (tt + C::PF < L) load_tok<T, D, false>(ring[u], kh, kh, vh, nullptr, tt + C::PF, r0, j);
+        gdn_fwd_token<D>(S, cur, lane_bcast(al_c, s), lane_bcast(be_c, s), lds_f + (tt & 1) * 4 * C::CW, jl, wv,
+                         lane);
+      }
     }
     const bool lin = rt[c] == kRouteLinear;
 #pragma unroll
@@ -171,17 +220,20 @@ __global__ void __launch_bounds__(256) k_gdn_bwd(const T* __restrict__ q, const 
                                                  const float* __restrict__ d_o, const float* __restrict__ dS_final,
                                                  const float* __restrict__ ckpt, float* __restrict__ scratch,
                                                  float* __restrict__ dq_p, float* __restrict__ dk_p,
-                                                 float* __restrict__ da_p, float* __restrict__ db_p,
-                                                 float* __restrict__ dv, float* __restrict__ dS_init, int H, int L,
-                                                 int G) {
+                                                 float* __restrict__ dab_p, float* __restrict__ dv,
+                                                 float* __restrict__ dS_init, int H, int L, int G) {
   using C = GdnBwdCfg<D>;
+  constexpr int NV = 2 * C::RPT;  // row-sum values per thread and token: dq, dk at its rows
   extern __shared__ float lds_f[];
   const int nc = L / CHUNK;
   const int bh = bid_x() / C::NCG, cg = bid_x() % C::NCG, b = bh / H, h = bh % H;
   const int grp = (G == 1) ? 0 : h;
   const int32_t* rt = route + ((int64_t)b * G + grp) * nc;
-  const int t = tid_x(), jl = t & 15, rg = t >> 4, wv = wave_id(), lane = lane_id();
+  const int t = tid_x(), jl = t % C::CW, rg = t / C::CW, wv = wave_id(), lane = lane_id();
   const int j = C::CW * cg + jl, r0 = rg * C::RPT;
+  // after the row-group reduction lane jl holds value jl % NV: dq (below RPT) or dk at row r0 + jl % RPT
+  const int vi = jl % NV;
+  float* const dqk_p = (vi < C::RPT) ? dq_p : dk_p;
   const int64_t tok0 = (int64_t)bh * L;
   const T* qh = q + tok0 * D;
   const T* kh = k + tok0 * D;
@@ -190,7 +242,8 @@ __global__ void __launch_bounds__(256) k_gdn_bwd(const T* __restrict__ q, const 
   const float* ah = alpha + tok0;
   const float* bth = beta + tok0;
   const float* ck = ckpt + (int64_t)bh * nc * D * D;
-  float* sc = scratch + (int64_t)bh * CHUNK * D * D;  // S_{t-1} of the chunk's tokens (own elements only)
+  // S_{t-1} of the chunk's tokens: slot s of thread t at (s * 256 + t) * RPT
+  float* sc = scratch + (int64_t)bid_x() * CHUNK * D * C::CW + (int64_t)t * C::RPT;
 
   float Gc[C::RPT];  // gradient of the carried state after the current chunk
 #pragma unroll
@@ -201,82 +254,93 @@ __global__ void __launch_bounds__(256) k_gdn_bwd(const T* __restrict__ q, const 
     // the previous chunk's last sweep token read the parity-0 exchange buffer
     // that this chunk's first recompute token writes
     __syncthreads();
+    const float al_c = ah[c0 + lane], be_c = bth[c0 + lane];  // lane s: token c0 + s
     // recompute the chunk's states: slot s holds the state before token c0 + s
     float S[C::RPT];
 #pragma unroll
     for (int i = 0; i < C::RPT; ++i) S[i] = ck[((int64_t)c * D + r0 + i) * D + j];
-    TokIn<C::RPT> nx;
-    load_tok<T, D, false>(nx, kh, kh, vh, nullptr, ah, bth, c0, r0, j);
-    for (int s = 0; s < CHUNK; ++s) {
-      const int tt = c0 + s;
+    {
+      TokIn<C::RPT> ring[C::PF];  // slot u: the token c0 + s with s % PF == u
 #pragma unroll
-      for (int i = 0; i < C::RPT; ++i) sc[((int64_t)s * D + r0 + i) * D + j] = S[i];
-      if (s == CHUNK - 1) break;  // the chunk's end state is not needed
-      const TokIn<C::RPT> cur = nx;
-      load_tok<T, D, false>(nx, kh, kh, vh, nullptr, ah, bth, tt + 1, r0, j);  // tt + 1 <= c0 + 63
-      gdn_fwd_token<D>(S, cur, lds_f + (tt & 1) * 4 * C::CW, jl, wv, lane);
+      for (int u = 0; u < C::PF; ++u) load_tok<T, D, false>(ring[u], kh, kh, vh, nullptr, c0 + u, r0, j);
+      for (int s0 = 0; s0 < CHUNK; s0 += C::PF) {
+#pragma unroll
+        for (int u = 0; u < C::PF; ++u) {
+          const int s = s0 + u, tt = c0 + s;
+          store_state<C::RPT>(sc + (int64_t)s * C::NT * C::RPT, S);
+          if (s < CHUNK - 1) {  // the chunk's end state is not needed
+            const TokIn<C::RPT> cur = ring[u];
+            if (s + C::PF < CHUNK - 1)  // tokens up to c0 + 62
+              load_tok<T, D, false>(ring[u], kh, kh, vh, nullptr, tt + C::PF, r0, j);
+            gdn_fwd_token<D>(S, cur, lane_bcast(al_c, s), lane_bcast(be_c, s), lds_f + (tt & 1) * 4 * C::CW, jl, wv,
+                             lane);
+          }
+        }
+      }
     }
+    // (a full barrier: this thread's scratch stores complete before the sweep
+    // reads them back; the per-token barriers order LDS only)
+    __syncthreads();
     const bool lin = rt[c] == kRouteLinear;
     float Gm[C::RPT];
 #pragma unroll
     for (int i = 0; i < C::RPT; ++i) Gm[i] = lin ? Gc[i] : 0.f;
-    // inputs and the thread's elements of S_{t-1}, loaded a token ahead (the
-    // sweep runs backward)
-    TokIn<C::RPT> nt;
-    load_tok<T, D, true>(nt, kh, qh, vh, doh, ah, bth, c0 + CHUNK - 1, r0, j);
-    float nS[C::RPT];
+    // inputs and S_{t-1}, PF tokens ahead; the sweep runs backward: step r is
+    // token c0 + 63 - r, in slot r % PF
+    TokIn<C::RPT> ring[C::PF];
+    float ringS[C::PF][C::RPT];
 #pragma unroll
-    for (int i = 0; i < C::RPT; ++i) nS[i] = sc[((int64_t)(CHUNK - 1) * D + r0 + i) * D + j];
-    for (int tt = c0 + CHUNK - 1; tt >= c0; --tt) {
-      // (the recompute's last exchange buffer was token c0 + 62, parity 0; the
-      // sweep's first is token c0 + 63, parity 1, and the parities alternate)
-      float* part = lds_f + (tt & 1) * 2 * 4 * C::CW;  // [a: 4 x 16 | w: 4 x 16]
-      const TokIn<C::RPT> x = nt;
-      float Sp[C::RPT];
+    for (int u = 0; u < C::PF; ++u) {
+      load_tok<T, D, true>(ring[u], kh, qh, vh, doh, c0 + CHUNK - 1 - u, r0, j);
+      load_state<C::RPT>(ringS[u], sc + (int64_t)(CHUNK - 1 - u) * C::NT * C::RPT);
+    }
+    for (int r00 = 0; r00 < CHUNK; r00 += C::PF) {
 #pragma unroll
-      for (int i = 0; i < C::RPT; ++i) Sp[i] = nS[i];
-      if (tt > c0) {
-        load_tok<T, D, true>(nt, kh, qh, vh, doh, ah, bth, tt - 1, r0, j);
+      for (int u = 0; u < C::PF; ++u) {
+        const int rs = r00 + u, s = CHUNK - 1 - rs, tt = c0 + s;
+        // (the recompute's last exchange buffer was token c0 + 62, parity 0;
+        // the sweep's first is token c0 + 63, parity 1, and they alternate)
+        float* part = lds_f + (tt & 1) * 2 * 4 * C::CW;  // [a: 4 x CW | w: 4 x CW]
+        const TokIn<C::RPT> x = ring[u];
+        float Sp[C::RPT];
 #pragma unroll
-        for (int i = 0; i < C::RPT; ++i) nS[i] = sc[((int64_t)(tt - 1 - c0) * D + r0 + i) * D + j];
-      }
-      float pa[4] = {0.f, 0.f, 0.f, 0.f}, pw[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int i = 0; i < C::RPT; ++i) {
-        Gm[i] += x.q[i] * x.d_o;  // o_t = S_t^T q_t
-        pa[i & 3] += Sp[i] * x.k[i];
-        pw[i & 3] += Gm[i] * x.k[i];
-      }
-      col_part((pa[0] + pa[1]) + (pa[2] + pa[3]), part, jl, wv, lane);
-      col_part((pw[0] + pw[1]) + (pw[2] + pw[3]), part + 4 * C::CW, jl, wv, lane);
-      __syncthreads();  // column sums exchanged
-      const float a = col_total(part, jl), w = col_total(part + 4 * C::CW, jl);
-      const float al = x.al, be = x.be, vj = x.v, doj = x.d_o;
-      const float cv = be * vj - al * be * a, cw = al * be * w;
-      float pal = 0.f;
-      const int64_t tok = tok0 + tt;
-#pragma unroll
-      for (int i = 0; i < C::RPT; ++i) {
-        const float ki = x.k[i];
-        const float erased = Sp[i] - be * ki * a;
-        // this group's share of the row sums dq = S_t d_o and dk
-        const float rq = dpp_group_sum<16>((al * erased + be * ki * vj) * doj);
-        const float rk = dpp_group_sum<16>(Gm[i] * cv - cw * Sp[i]);
-        if (jl == 0) {
-          dq_p[(tok * C::NCG + cg) * D + r0 + i] = rq;
-          dk_p[(tok * C::NCG + cg) * D + r0 + i] = rk;
+        for (int i = 0; i < C::RPT; ++i) Sp[i] = ringS[u][i];
+        if (rs + C::PF < CHUNK) {  // token tt - PF >= c0
+          load_tok<T, D, true>(ring[u], kh, qh, vh, doh, tt - C::PF, r0, j);
+          load_state<C::RPT>(ringS[u], sc + (int64_t)(s - C::PF) * C::NT * C::RPT);
         }
-        pal += Gm[i] * erased;
-        Gm[i] = al * (Gm[i] - be * ki * w);  // the gradient of S_{t-1}
+        float pa[4] = {0.f, 0.f, 0.f, 0.f}, pw[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < C::RPT; ++i) {
+          Gm[i] += x.q[i] * x.d_o;  // o_t = S_t^T q_t
+          pa[i & 3] += Sp[i] * x.k[i];
+          pw[i & 3] += Gm[i] * x.k[i];
+        }
+        col_part((pa[0] + pa[1]) + (pa[2] + pa[3]), part, jl, wv, lane);
+        col_part((pw[0] + pw[1]) + (pw[2] + pw[3]), part + 4 * C::CW, jl, wv, lane);
+        lds_barrier();  // column sums exchanged (global loads stay in flight)
+        const float a = col_total(part, jl), w = col_total(part + 4 * C::CW, jl);
+        const float al = lane_bcast(al_c, s), be = lane_bcast(be_c, s), vj = x.v, doj = x.d_o;
+        const float cv = be * vj - al * be * a, cw = al * be * w;
+        float pal = 0.f, rv[NV];
+#pragma unroll
+        for (int i = 0; i < C::RPT; ++i) {
+          const float ki = x.k[i];
+          const float erased = Sp[i] - be * ki * a;
+          rv[i] = (al * erased + be * ki * vj) * doj;  // this column's share of dq = S_t d_o
+          rv[C::RPT + i] = Gm[i] * cv - cw * Sp[i];    // and of dk
+          pal += Gm[i] * erased;
+          Gm[i] = al * (Gm[i] - be * ki * w);  // the gradient of S_{t-1}
+        }
+        const float r = group8_reduce_scatter<NV>(rv, jl);
+        const int64_t tok = tok0 + tt;
+        if (jl < NV) dqk_p[(tok * C::NCG + cg) * D + r0 + vi % C::RPT] = r;
+        float pbe = (rg == 0) ? w * (vj - al * a) : 0.f;
+        pal = wave_sum64(pal);
+        pbe = wave_sum64(pbe);
+        if (lane < 2) dab_p[((tok * C::NCG + cg) * 4 + wv) * 2 + lane] = lane ? pbe : pal;  // per-wave partials
+        if (rg == 0) dv[tok * D + j] = be * w;
       }
-      float pbe = (rg == 0) ? w * (vj - al * a) : 0.f;
-      pal = wave_sum64(pal);
-      pbe = wave_sum64(pbe);
-      if (lane == 0) {  // per-wave partials, added by k_gdn_bwd_reduce
-        da_p[(tok * C::NCG + cg) * 4 + wv] = pal;
-        db_p[(tok * C::NCG + cg) * 4 + wv] = pbe;
-      }
-      if (rg == 0) dv[tok * D + j] = be * w;
     }
 #pragma unroll
     for (int i = 0; i < C::RPT; ++i) Gc[i] = Gm[i] + (lin ? 0.f : Gc[i]);
@@ -287,14 +351,13 @@ __global__ void __launch_bounds__(256) k_gdn_bwd(const T* __restrict__ q, const 
   }
 }
 
-// dq, dk, dalpha, dbeta: the column groups' (and waves') partials added in a
-// fixed order
+// dq, dk: the NCG groups' partials added in group order; dalpha, dbeta: the
+// NCG x 4 per-wave partials (interleaved alpha, beta) in order
 template <int D>
 __global__ void __launch_bounds__(256) k_gdn_bwd_reduce(const float* __restrict__ dq_p, const float* __restrict__ dk_p,
-                                                        const float* __restrict__ da_p, const float* __restrict__ db_p,
-                                                        float* __restrict__ dq, float* __restrict__ dk,
-                                                        float* __restrict__ dalpha, float* __restrict__ dbeta,
-                                                        int64_t ntok) {
+                                                        const float* __restrict__ dab_p, float* __restrict__ dq,
+                                                        float* __restrict__ dk, float* __restrict__ dalpha,
+                                                        float* __restrict__ dbeta, int64_t ntok) {
   constexpr int NCG = GdnBwdCfg<D>::NCG;
   const int64_t gid = (int64_t)bid_x() * 256 + tid_x();
   const int64_t tok = gid / D;
@@ -312,8 +375,8 @@ __global__ void __launch_bounds__(256) k_gdn_bwd_reduce(const float* __restrict_
     float sa = 0.f, sb = 0.f;
 #pragma unroll
     for (int x = 0; x < NCG * 4; ++x) {
-      sa += da_p[tok * NCG * 4 + x];
-      sb += db_p[tok * NCG * 4 + x];
+      sa += dab_p[(tok * NCG * 4 + x) * 2];
+      sb += dab_p[(tok * NCG * 4 + x) * 2 + 1];
     }
     dalpha[tok] = sa;
     dbeta[tok] = sb;
@@ -332,8 +395,7 @@ hipError_t launch_gdn_backward(const T* q, const T* k, const T* v, const float* 
   float* scratch = ckpt + (size_t)B * H * nc * D * D;
   float* dq_p = scratch + (size_t)B * H * CHUNK * D * D;
   float* dk_p = dq_p + (size_t)ntok * C::NCG * D;
-  float* da_p = dk_p + (size_t)ntok * C::NCG * D;
-  float* db_p = da_p + (size_t)ntok * C::NCG * 4;
+  float* dab_p = dk_p + (size_t)ntok * C::NCG * D;  // ntok x NCG x 4 waves x (dalpha, dbeta)
   const size_t lds = C::LDS_FLOATS * 4;
   const unsigned grid = (unsigned)(B * H * C::NCG);
   hipLaunchKernelGGL((k_gdn_bwd_ckpt<T, D>), dim3(grid), dim3(C::NT), lds, st, k, v, alpha, beta, route, S_init,
@@ -341,11 +403,11 @@ hipError_t launch_gdn_backward(const T* q, const T* k, const T* v, const float* 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((k_gdn_bwd<T, D>), dim3(grid), dim3(C::NT), lds, st, q, k, v, alpha, beta, route, d_o,
-                     dS_final, ckpt, scratch, dq_p, dk_p, da_p, db_p, dv, dS_init, H, L, G);
+                     dS_final, ckpt, scratch, dq_p, dk_p, dab_p, dv, dS_init, H, L, G);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t threads = ntok * D;
   hipLaunchKernelGGL((k_gdn_bwd_reduce<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, dq_p, dk_p,
-                     da_p, db_p, dq, dk, dalpha, dbeta, ntok);
+                     dab_p, dq, dk, dalpha, dbeta, ntok);
   return hipGetLastError();
 }
 
