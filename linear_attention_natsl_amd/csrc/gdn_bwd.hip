@@ -14,21 +14,24 @@
 // chunk's tokens see only their own outputs' gradients.
 //
 // The columns of S (and of G) evolve independently, so each head's 8-column
-// groups run in workgroups of their own (D / 8 per head: 256 workgroups for 16
-// heads, a wave on every SIMD).  Thread (jl, rg) holds the D / 32 rows
-// rg D/32 .. of column 8 cg + jl: the column sums (S^T k, G^T k) are a lane
-// swap and a row-swap sum over the wave's 8 row groups plus one LDS exchange
-// across the 4 waves; the row sums (dq, dk) and the scalar gradients (dalpha,
+// groups run in workgroups of their own: one wave each (D / 8 per head).  Lane
+// (jl, rg) holds the D / 8 rows rg D/8 .. of column 8 cg + jl, so the column
+// sums (S^T k, G^T k) stay in registers (a DPP rotate and two row swaps) and a
+// token needs no barrier.  The row sums (dq, dk) are reduced over the 8 lanes
+// of a row group by a reduce-scatter that leaves each lane a contiguous run of
+// rows (one vector store per token); they and the scalar gradients (dalpha,
 // dbeta) are per-group partials, added over the groups in a fixed order by a
 // last kernel (so the result does not depend on scheduling).  Launches:
 //   k_gdn_bwd_ckpt    the forward, storing every chunk's starting (carried) state
 //   k_gdn_bwd         chunks in reverse: recompute the chunk's per-token states
 //                     into a scratch slot, then sweep its tokens backward
 //   k_gdn_bwd_reduce  dq, dk, dalpha, dbeta from the groups' partials
-// Each thread reads its own rows of k and q and its column of v and d_o from
-// global memory (a token ahead), so a token needs one barrier, for the
-// column-sum exchange.  This is the plain per-token form (the chunkwise form
-// on MFMA is not built).
+// Each lane reads its own rows of k and q and its column of v and d_o from
+// global memory a few tokens ahead through a ring of registers (the sweep
+// reads its scratch states the same way); alpha and beta come from one load
+// per chunk (lane s holds token s) and a lane broadcast.  The scratch holds
+// each lane's rows contiguously, moved as 16-byte vectors.  This is the plain
+// per-token form (the chunkwise form on MFMA is not built).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -38,37 +41,29 @@ constexpr int kRouteLinear = 1;  // route id of the linear (Gated DeltaNet) oper
 
 template <int D>
 struct GdnBwdCfg {
-  static constexpr int CW = 8;        // state columns per workgroup
-  static constexpr int NCG = D / CW;  // column groups (workgroups) per head
-  static constexpr int NT = 256;      // CW columns x NT / CW row groups
-  static constexpr int RPT = D * CW / NT;  // state rows per thread
-  static constexpr int PF = 4;        // tokens of inputs in flight (ring depth); divides the chunk
-  static_assert(CW == 8 && CHUNK % PF == 0, "column and row sums assume 8 columns");
-  // LDS: part[2][2][4][CW] floats (per-wave column sums of a and w, by token
-  // parity); every other per-token value reaches the threads from global
-  // memory directly, so a token needs one barrier (the column-sum exchange)
-  static constexpr int LDS_FLOATS = 2 * 2 * 4 * CW;
+  static constexpr int CW = 8;             // state columns per workgroup
+  static constexpr int NCG = D / CW;       // column groups (workgroups) per head
+  static constexpr int NT = 64;            // one wave: CW columns x 8 row groups
+  static constexpr int RPT = D * CW / NT;  // state rows per thread (D / 8)
+  static constexpr int PF = 4;             // forward tokens of inputs in flight (ring depth)
+  static constexpr int PFB = 2;            // the same for the backward sweep (inputs and S_{t-1})
+  static_assert(CW == 8 && RPT % 4 == 0 && CHUNK % PF == 0 && CHUNK % PFB == 0, "8 columns, whole row vectors");
 };
 
 size_t gdn_bwd_ws_bytes(int B, int H, int L, int D) {
   const size_t nc = (size_t)L / CHUNK, ntok = (size_t)B * H * L, ncg = (size_t)D / GdnBwdCfg<128>::CW;
   const size_t floats = (size_t)B * H * (nc + CHUNK) * D * D  // chunk-start states, chunk token states
                         + 2 * ntok * ncg * D                  // dq, dk partials
-                        + 2 * ntok * ncg * 4;                 // dalpha, dbeta partials (per wave)
+                        + 2 * ntok * ncg;                     // dalpha, dbeta partials
   return (floats * 4 + 255) / 256 * 256;
 }
 
-// sum over the workgroup's 32 row groups of a per-thread partial for the
-// thread's column: lanes l and l + 8 of each 16-lane row by a DPP rotate, the
-// wave's 4 rows by row swaps, the 4 waves through LDS (part[4][CW]); the
-// caller's barrier separates the write and the reads
-__device__ __forceinline__ void col_part(float x, float* part, int jl, int wv, int lane) {
+// sum over the wave's 8 row groups of a per-thread partial for the thread's
+// column (lanes l and l + 8 of each 16-lane row by a DPP rotate, the 4 rows by
+// row swaps); every lane receives its column's total
+__device__ __forceinline__ float col_sum(float x) {
   x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, true));  // row_ror 8
-  x = group4_sum(x);
-  if (lane < 8) part[wv * 8 + jl] = x;
-}
-__device__ __forceinline__ float col_total(const float* part, int jl) {
-  return (part[jl] + part[8 + jl]) + (part[16 + jl] + part[24 + jl]);
+  return group4_sum(x);
 }
 
 // One reduce-scatter step over lane pairs given by a DPP pattern: of the N
@@ -84,20 +79,15 @@ __device__ __forceinline__ void rs_step(float* v, bool keep_lo) {
   }
 }
 // Sum of each of the N values over the 8 lanes of a row group (lanes jl =
-// 0..7, 8-aligned); lane jl returns the sum of value jl % N.  The pairings are
-// l <-> 7 - l, l <-> l ^ 2, l <-> l ^ 1, which together span the 8 lanes.
+// 0..7, 8-aligned); lane jl is left with the sums of values jl N/8 ..
+// (jl + 1) N/8 - 1 in v[0 .. N/8).  The pairings are l <-> 7 - l, l <-> l ^ 2,
+// l <-> l ^ 1, which together span the 8 lanes.
 template <int N>
-__device__ __forceinline__ float group8_reduce_scatter(float* v, int jl) {
-  static_assert(N == 8 || N == 4, "8 or 4 values");
-  if constexpr (N == 8) {
-    rs_step<8, 0x141>(v, (jl & 4) == 0);  // row_half_mirror
-  } else {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) v[k] += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v[k]), 0x141, 0xF, 0xF, true));
-  }
-  rs_step<4, 0x4E>(v, (jl & 2) == 0);  // quad_perm 2,3,0,1
-  rs_step<2, 0xB1>(v, (jl & 1) == 0);  // quad_perm 1,0,3,2
-  return v[0];
+__device__ __forceinline__ void group8_reduce_scatter(float* v, int jl) {
+  static_assert(N % 8 == 0, "whole values per lane");
+  rs_step<N, 0x141>(v, (jl & 4) == 0);      // row_half_mirror
+  rs_step<N / 2, 0x4E>(v, (jl & 2) == 0);   // quad_perm 2,3,0,1
+  rs_step<N / 4, 0xB1>(v, (jl & 1) == 0);   // quad_perm 1,0,3,2
 }
 
 // alpha or beta of token c0 + s, from the chunk's values held one per lane
@@ -105,44 +95,71 @@ __device__ __forceinline__ float lane_bcast(float x, int s) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), s));
 }
 
-// A token's inputs as one thread needs them: k (and q) at its RPT rows, v
-// (and d_o) at its column
+// A token's inputs as one lane needs them: k (and q) at its RPT rows, v (and
+// d_o) at its column, kept as loaded (raw 16-byte words) so that a load in
+// the ring is not waited for until the token is reached; widened by tok_f32.
+template <typename T, int RPT>
+struct TokRaw {
+  static constexpr int NW = RPT * (int)sizeof(T) / 16;  // 16-byte words of the lane's rows
+  uint4 k[NW], q[NW];
+  T v;
+  float d_o;
+};
 template <int RPT>
 struct TokIn {
   float k[RPT], q[RPT];
   float v, d_o;
 };
 template <typename T, int D, bool BWD>
-__device__ __forceinline__ void load_tok(TokIn<GdnBwdCfg<D>::RPT>& x, const T* kh, const T* qh, const T* vh,
+__device__ __forceinline__ void load_tok(TokRaw<T, GdnBwdCfg<D>::RPT>& x, const T* kh, const T* qh, const T* vh,
                                          const float* doh, int tt, int r0, int j) {
-  constexpr int RPT = GdnBwdCfg<D>::RPT;
-  if constexpr (RPT == 4) {  // one 4-element vector of the thread's rows
-    load4f<T>(kh + (int64_t)tt * D + r0, x.k);
-    if (BWD) load4f<T>(qh + (int64_t)tt * D + r0, x.q);
-  } else {  // exactly the thread's rows
+  constexpr int NW = TokRaw<T, GdnBwdCfg<D>::RPT>::NW;
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      x.k[i] = to_f32(kh[(int64_t)tt * D + r0 + i]);
-      if (BWD) x.q[i] = to_f32(qh[(int64_t)tt * D + r0 + i]);
-    }
+  for (int w = 0; w < NW; ++w) {
+    x.k[w] = *(const uint4*)(kh + (int64_t)tt * D + r0 + w * (16 / (int)sizeof(T)));
+    if (BWD) x.q[w] = *(const uint4*)(qh + (int64_t)tt * D + r0 + w * (16 / (int)sizeof(T)));
   }
-  x.v = to_f32(vh[(int64_t)tt * D + j]);
+  x.v = vh[(int64_t)tt * D + j];
   x.d_o = BWD ? doh[(int64_t)tt * D + j] : 0.f;
 }
+// element i of a run of raw 16-byte words holding T values
+template <typename T>
+__device__ __forceinline__ float raw_f32(const uint4* w, int i) {
+  constexpr int E = 16 / (int)sizeof(T);  // elements per word
+  const uint4 x = w[i / E];
+  const int c = (i % E) * (int)sizeof(T) / 4;  // 32-bit component
+  const uint32_t u = c == 0 ? x.x : c == 1 ? x.y : c == 2 ? x.z : x.w;
+  if constexpr (sizeof(T) == 2) return __uint_as_float((i & 1) ? (u & 0xffff0000u) : (u << 16));  // bf16 -> fp32
+  else return __uint_as_float(u);
+}
+template <typename T, int RPT, bool BWD>
+__device__ __forceinline__ TokIn<RPT> tok_f32(const TokRaw<T, RPT>& r) {
+  TokIn<RPT> x;
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    x.k[i] = raw_f32<T>(r.k, i);
+    x.q[i] = BWD ? raw_f32<T>(r.q, i) : 0.f;
+  }
+  x.v = to_f32(r.v);
+  x.d_o = r.d_o;
+  return x;
+}
 
-// the thread's RPT state elements, contiguous in the scratch (8-byte aligned)
+// the thread's RPT state elements, contiguous in the scratch (16-byte aligned)
 template <int RPT>
 __device__ __forceinline__ void store_state(float* p, const float (&S)[RPT]) {
 #pragma unroll
-  for (int h = 0; h < RPT; h += 2) *(float2*)(p + h) = make_float2(S[h], S[h + 1]);
+  for (int h = 0; h < RPT; h += 4) *(float4*)(p + h) = make_float4(S[h], S[h + 1], S[h + 2], S[h + 3]);
 }
 template <int RPT>
 __device__ __forceinline__ void load_state(float (&S)[RPT], const float* p) {
 #pragma unroll
-  for (int h = 0; h < RPT; h += 2) {
-    const float2 x = *(const float2*)(p + h);
+  for (int h = 0; h < RPT; h += 4) {
+    const float4 x = *(const float4*)(p + h);
     S[h] = x.x;
     S[h + 1] = x.y;
+    S[h + 2] = x.z;
+    S[h + 3] = x.w;
   }
 }
 
@@ -150,31 +167,28 @@ __device__ __forceinline__ void load_state(float (&S)[RPT], const float* p) {
 // S <- al (S - be k a^T) + be k v^T
 template <int D>
 __device__ __forceinline__ void gdn_fwd_token(float (&S)[GdnBwdCfg<D>::RPT], const TokIn<GdnBwdCfg<D>::RPT>& x,
-                                              float al, float be, float* part, int jl, int wv, int lane) {
+                                              float al, float be) {
   constexpr int RPT = GdnBwdCfg<D>::RPT;
   float p4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < RPT; ++i) p4[i & 3] += S[i] * x.k[i];
-  col_part((p4[0] + p4[1]) + (p4[2] + p4[3]), part, jl, wv, lane);
-  lds_barrier();  // column sums exchanged (global loads stay in flight)
-  const float a = col_total(part, jl);
+  const float a = col_sum((p4[0] + p4[1]) + (p4[2] + p4[3]));
 #pragma unroll
   for (int i = 0; i < RPT; ++i) S[i] = al * (S[i] - be * x.k[i] * a) + be * x.k[i] * x.v;
 }
 
 template <typename T, int D>
-__global__ void __launch_bounds__(256) k_gdn_bwd_ckpt(const T* __restrict__ k, const T* __restrict__ v,
+__global__ void __launch_bounds__(64) k_gdn_bwd_ckpt(const T* __restrict__ k, const T* __restrict__ v,
                                                       const float* __restrict__ alpha, const float* __restrict__ beta,
                                                       const int32_t* __restrict__ route,
                                                       const float* __restrict__ S_init, float* __restrict__ ckpt,
                                                       int H, int L, int G) {
   using C = GdnBwdCfg<D>;
-  extern __shared__ float lds_f[];
   const int nc = L / CHUNK;
   const int bh = bid_x() / C::NCG, cg = bid_x() % C::NCG, b = bh / H, h = bh % H;
   const int grp = (G == 1) ? 0 : h;
   const int32_t* rt = route + ((int64_t)b * G + grp) * nc;
-  const int t = tid_x(), jl = t % C::CW, rg = t / C::CW, wv = wave_id(), lane = lane_id();
+  const int t = tid_x(), jl = t % C::CW, rg = t / C::CW, lane = t;
   const int j = C::CW * cg + jl, r0 = rg * C::RPT;
   const T* kh = k + (int64_t)bh * L * D;
   const T* vh = v + (int64_t)bh * L * D;
@@ -187,7 +201,7 @@ __global__ void __launch_bounds__(256) k_gdn_bwd_ckpt(const T* __restrict__ k, c
     S[i] = S_init ? S_init[((int64_t)bh * D + r0 + i) * D + j] : 0.f;
     carry[i] = S[i];
   }
-  TokIn<C::RPT> ring[C::PF];  // slot u: the token tt with tt % PF == u, PF tokens ahead
+  TokRaw<T, C::RPT> ring[C::PF];  // slot u: the token tt with tt % PF == u, PF tokens ahead
 #pragma unroll
   for (int u = 0; u < C::PF; ++u) load_tok<T, D, false>(ring[u], kh, kh, vh, nullptr, u, r0, j);  // L >= 64
   for (int c = 0; c < nc; ++c) {
@@ -198,10 +212,11 @@ __global__ void __launch_bounds__(256) k_gdn_bwd_ckpt(const T* __restrict__ k, c
 #pragma unroll
       for (int u = 0; u < C::PF; ++u) {
         const int s = s0 + u, tt = c * CHUNK + s;
-        const TokIn<C::RPT> cur = ring[u];
-        if (tt + C::PF < L) load_tok<T, D, false>(ring[u], kh, kh, vh, nullptr, tt + C::PF, r0, j);
-        gdn_fwd_token<D>(S, cur, lane_bcast(al_c, s), lane_bcast(be_c, s), lds_f + (tt & 1) * 4 * C::CW, jl, wv,
-                         lane);
+        const TokIn<C::RPT> cur = tok_f32<T, C::RPT, false>(ring[u]);
+        // (unconditional, clamped to the last token: a branch around the load
+        // would make the compiler wait for it at the join)
+        load_tok<T, D, false>(ring[u], kh, kh, vh, nullptr, min(tt + C::PF, L - 1), r0, j);
+        gdn_fwd_token<D>(S, cur, lane_bcast(al_c, s), lane_bcast(be_c, s));
       }
     }
     const bool lin = rt[c] == kRouteLinear;
@@ -214,7 +229,7 @@ __global__ void __launch_bounds__(256) k_gdn_bwd_ckpt(const T* __restrict__ k, c
 }
 
 template <typename T, int D>
-__global__ void __launch_bounds__(256) k_gdn_bwd(const T* __restrict__ q, const T* __restrict__ k,
+__global__ void __launch_bounds__(64) k_gdn_bwd(const T* __restrict__ q, const T* __restrict__ k,
                                                  const T* __restrict__ v, const float* __restrict__ alpha,
                                                  const float* __restrict__ beta, const int32_t* __restrict__ route,
                                                  const float* __restrict__ d_o, const float* __restrict__ dS_final,
@@ -224,16 +239,17 @@ __global__ void __launch_bounds__(256) k_gdn_bwd(const T* __restrict__ q, const 
                                                  float* __restrict__ dS_init, int H, int L, int G) {
   using C = GdnBwdCfg<D>;
   constexpr int NV = 2 * C::RPT;  // row-sum values per thread and token: dq, dk at its rows
-  extern __shared__ float lds_f[];
+  constexpr int VPL = NV / 8;     // of which each lane stores VPL after the row-group reduction
   const int nc = L / CHUNK;
   const int bh = bid_x() / C::NCG, cg = bid_x() % C::NCG, b = bh / H, h = bh % H;
   const int grp = (G == 1) ? 0 : h;
   const int32_t* rt = route + ((int64_t)b * G + grp) * nc;
-  const int t = tid_x(), jl = t % C::CW, rg = t / C::CW, wv = wave_id(), lane = lane_id();
+  const int t = tid_x(), jl = t % C::CW, rg = t / C::CW, lane = t;
   const int j = C::CW * cg + jl, r0 = rg * C::RPT;
-  // after the row-group reduction lane jl holds value jl % NV: dq (below RPT) or dk at row r0 + jl % RPT
-  const int vi = jl % NV;
-  float* const dqk_p = (vi < C::RPT) ? dq_p : dk_p;
+  // after the row-group reduction lane jl holds values jl VPL ..: dq (lanes 0-3) or dk (lanes 4-7) at rows
+  // r0 + (jl % 4) VPL ..
+  float* const dqk_p = (jl < 4) ? dq_p : dk_p;
+  const int rq0 = r0 + (jl % 4) * VPL;
   const int64_t tok0 = (int64_t)bh * L;
   const T* qh = q + tok0 * D;
   const T* kh = k + tok0 * D;
@@ -251,16 +267,13 @@ __global__ void __launch_bounds__(256) k_gdn_bwd(const T* __restrict__ q, const 
 
   for (int c = nc - 1; c >= 0; --c) {
     const int c0 = c * CHUNK;
-    // the previous chunk's last sweep token read the parity-0 exchange buffer
-    // that this chunk's first recompute token writes
-    __syncthreads();
     const float al_c = ah[c0 + lane], be_c = bth[c0 + lane];  // lane s: token c0 + s
     // recompute the chunk's states: slot s holds the state before token c0 + s
     float S[C::RPT];
 #pragma unroll
     for (int i = 0; i < C::RPT; ++i) S[i] = ck[((int64_t)c * D + r0 + i) * D + j];
     {
-      TokIn<C::RPT> ring[C::PF];  // slot u: the token c0 + s with s % PF == u
+      TokRaw<T, C::RPT> ring[C::PF];  // slot u: the token c0 + s with s % PF == u
 #pragma unroll
       for (int u = 0; u < C::PF; ++u) load_tok<T, D, false>(ring[u], kh, kh, vh, nullptr, c0 + u, r0, j);
       for (int s0 = 0; s0 < CHUNK; s0 += C::PF) {
@@ -268,47 +281,39 @@ __global__ void __launch_bounds__(256) k_gdn_bwd(const T* __restrict__ q, const 
         for (int u = 0; u < C::PF; ++u) {
           const int s = s0 + u, tt = c0 + s;
           store_state<C::RPT>(sc + (int64_t)s * C::NT * C::RPT, S);
-          if (s < CHUNK - 1) {  // the chunk's end state is not needed
-            const TokIn<C::RPT> cur = ring[u];
-            if (s + C::PF < CHUNK - 1)  // tokens up to c0 + 62
-              load_tok<T, D, false>(ring[u], kh, kh, vh, nullptr, tt + C::PF, r0, j);
-            gdn_fwd_token<D>(S, cur, lane_bcast(al_c, s), lane_bcast(be_c, s), lds_f + (tt & 1) * 4 * C::CW, jl, wv,
-                             lane);
-          }
+          // (token c0 + 63 runs too, without a branch; its end state is not used)
+          const TokIn<C::RPT> cur = tok_f32<T, C::RPT, false>(ring[u]);
+          load_tok<T, D, false>(ring[u], kh, kh, vh, nullptr, c0 + min(s + C::PF, CHUNK - 1), r0, j);
+          gdn_fwd_token<D>(S, cur, lane_bcast(al_c, s), lane_bcast(be_c, s));
         }
       }
     }
-    // (a full barrier: this thread's scratch stores complete before the sweep
-    // reads them back; the per-token barriers order LDS only)
+    // (this thread's scratch stores complete before the sweep reads them back)
     __syncthreads();
     const bool lin = rt[c] == kRouteLinear;
     float Gm[C::RPT];
 #pragma unroll
     for (int i = 0; i < C::RPT; ++i) Gm[i] = lin ? Gc[i] : 0.f;
-    // inputs and S_{t-1}, PF tokens ahead; the sweep runs backward: step r is
-    // token c0 + 63 - r, in slot r % PF
-    TokIn<C::RPT> ring[C::PF];
-    float ringS[C::PF][C::RPT];
+    // inputs and S_{t-1}, PFB tokens ahead; the sweep runs backward: step r is
+    // token c0 + 63 - r, in slot r % PFB
+    TokRaw<T, C::RPT> ring[C::PFB];
+    float ringS[C::PFB][C::RPT];
 #pragma unroll
-    for (int u = 0; u < C::PF; ++u) {
+    for (int u = 0; u < C::PFB; ++u) {
       load_tok<T, D, true>(ring[u], kh, qh, vh, doh, c0 + CHUNK - 1 - u, r0, j);
       load_state<C::RPT>(ringS[u], sc + (int64_t)(CHUNK - 1 - u) * C::NT * C::RPT);
     }
-    for (int r00 = 0; r00 < CHUNK; r00 += C::PF) {
+    for (int r00 = 0; r00 < CHUNK; r00 += C::PFB) {
 #pragma unroll
-      for (int u = 0; u < C::PF; ++u) {
+      for (int u = 0; u < C::PFB; ++u) {
         const int rs = r00 + u, s = CHUNK - 1 - rs, tt = c0 + s;
-        // (the recompute's last exchange buffer was token c0 + 62, parity 0;
-        // the sweep's first is token c0 + 63, parity 1, and they alternate)
-        float* part = lds_f + (tt & 1) * 2 * 4 * C::CW;  // [a: 4 x CW | w: 4 x CW]
-        const TokIn<C::RPT> x = ring[u];
+        const TokIn<C::RPT> x = tok_f32<T, C::RPT, true>(ring[u]);
         float Sp[C::RPT];
 #pragma unroll
         for (int i = 0; i < C::RPT; ++i) Sp[i] = ringS[u][i];
-        if (rs + C::PF < CHUNK) {  // token tt - PF >= c0
-          load_tok<T, D, true>(ring[u], kh, qh, vh, doh, tt - C::PF, r0, j);
-          load_state<C::RPT>(ringS[u], sc + (int64_t)(s - C::PF) * C::NT * C::RPT);
-        }
+        // the token PFB steps on, clamped to the chunk's first (unconditional)
+        load_tok<T, D, true>(ring[u], kh, qh, vh, doh, c0 + max(s - C::PFB, 0), r0, j);
+        load_state<C::RPT>(ringS[u], sc + (int64_t)max(s - C::PFB, 0) * C::NT * C::RPT);
         float pa[4] = {0.f, 0.f, 0.f, 0.f}, pw[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < C::RPT; ++i) {
@@ -316,10 +321,8 @@ __global__ void __launch_bounds__(256) k_gdn_bwd(const T* __restrict__ q, const 
           pa[i & 3] += Sp[i] * x.k[i];
           pw[i & 3] += Gm[i] * x.k[i];
         }
-        col_part((pa[0] + pa[1]) + (pa[2] + pa[3]), part, jl, wv, lane);
-        col_part((pw[0] + pw[1]) + (pw[2] + pw[3]), part + 4 * C::CW, jl, wv, lane);
-        lds_barrier();  // column sums exchanged (global loads stay in flight)
-        const float a = col_total(part, jl), w = col_total(part + 4 * C::CW, jl);
+        const float a = col_sum((pa[0] + pa[1]) + (pa[2] + pa[3]));
+        const float w = col_sum((pw[0] + pw[1]) + (pw[2] + pw[3]));
         const float al = lane_bcast(al_c, s), be = lane_bcast(be_c, s), vj = x.v, doj = x.d_o;
         const float cv = be * vj - al * be * a, cw = al * be * w;
         float pal = 0.f, rv[NV];
@@ -332,13 +335,20 @@ __global__ void __launch_bounds__(256) k_gdn_bwd(const T* __restrict__ q, const 
           pal += Gm[i] * erased;
           Gm[i] = al * (Gm[i] - be * ki * w);  // the gradient of S_{t-1}
         }
-        const float r = group8_reduce_scatter<NV>(rv, jl);
+        group8_reduce_scatter<NV>(rv, jl);
         const int64_t tok = tok0 + tt;
-        if (jl < NV) dqk_p[(tok * C::NCG + cg) * D + r0 + vi % C::RPT] = r;
+        float* dst = dqk_p + (tok * C::NCG + cg) * D + rq0;
+        if constexpr (VPL % 4 == 0) {
+#pragma unroll
+          for (int h = 0; h < VPL; h += 4) *(float4*)(dst + h) = make_float4(rv[h], rv[h + 1], rv[h + 2], rv[h + 3]);
+        } else {
+#pragma unroll
+          for (int h = 0; h < VPL; h += 2) *(float2*)(dst + h) = make_float2(rv[h], rv[h + 1]);
+        }
         float pbe = (rg == 0) ? w * (vj - al * a) : 0.f;
         pal = wave_sum64(pal);
         pbe = wave_sum64(pbe);
-        if (lane < 2) dab_p[((tok * C::NCG + cg) * 4 + wv) * 2 + lane] = lane ? pbe : pal;  // per-wave partials
+        if (lane < 2) dab_p[(tok * C::NCG + cg) * 2 + lane] = lane ? pbe : pal;  // this group's partials
         if (rg == 0) dv[tok * D + j] = be * w;
       }
     }
@@ -351,8 +361,8 @@ __global__ void __launch_bounds__(256) k_gdn_bwd(const T* __restrict__ q, const 
   }
 }
 
-// dq, dk: the NCG groups' partials added in group order; dalpha, dbeta: the
-// NCG x 4 per-wave partials (interleaved alpha, beta) in order
+// dq, dk, dalpha, dbeta: the NCG groups' partials added in group order
+// (dalpha and dbeta interleaved)
 template <int D>
 __global__ void __launch_bounds__(256) k_gdn_bwd_reduce(const float* __restrict__ dq_p, const float* __restrict__ dk_p,
                                                         const float* __restrict__ dab_p, float* __restrict__ dq,
@@ -374,9 +384,9 @@ __global__ void __launch_bounds__(256) k_gdn_bwd_reduce(const float* __restrict_
   if (i == 0) {
     float sa = 0.f, sb = 0.f;
 #pragma unroll
-    for (int x = 0; x < NCG * 4; ++x) {
-      sa += dab_p[(tok * NCG * 4 + x) * 2];
-      sb += dab_p[(tok * NCG * 4 + x) * 2 + 1];
+    for (int x = 0; x < NCG; ++x) {
+      sa += dab_p[(tok * NCG + x) * 2];
+      sb += dab_p[(tok * NCG + x) * 2 + 1];
     }
     dalpha[tok] = sa;
     dbeta[tok] = sb;
@@ -395,8 +405,8 @@ hipError_t launch_gdn_backward(const T* q, const T* k, const T* v, const float* 
   float* scratch = ckpt + (size_t)B * H * nc * D * D;
   float* dq_p = scratch + (size_t)B * H * CHUNK * D * D;
   float* dk_p = dq_p + (size_t)ntok * C::NCG * D;
-  float* dab_p = dk_p + (size_t)ntok * C::NCG * D;  // ntok x NCG x 4 waves x (dalpha, dbeta)
-  const size_t lds = C::LDS_FLOATS * 4;
+  float* dab_p = dk_p + (size_t)ntok * C::NCG * D;  // ntok x NCG x (dalpha, dbeta)
+  const size_t lds = 0;
   const unsigned grid = (unsigned)(B * H * C::NCG);
   hipLaunchKernelGGL((k_gdn_bwd_ckpt<T, D>), dim3(grid), dim3(C::NT), lds, st, k, v, alpha, beta, route, S_init,
                      ckpt, H, L, G);
