@@ -13,12 +13,12 @@
 // linear-routed; otherwise it passes straight to the chunk start and the
 // chunk's tokens see only their own outputs' gradients.
 //
-// The columns of S (and of G) evolve independently, so each head's 8-column
-// groups run in workgroups of their own: one wave each (D / 8 per head).  Lane
-// (jl, rg) holds the D / 8 rows rg D/8 .. of column 8 cg + jl, so the column
-// sums (S^T k, G^T k) stay in registers (a DPP rotate and two row swaps) and a
-// token needs no barrier.  The row sums (dq, dk) are reduced over the 8 lanes
-// of a row group by a reduce-scatter that leaves each lane a contiguous run of
+// The columns of S (and of G) evolve independently, so each head's CW-column
+// groups (4 at D = 128, 8 at D = 64) run in workgroups of their own: one wave
+// each.  Lane (jl, rg) holds the RPT = D CW / 64 rows rg RPT .. of column
+// CW cg + jl, so the column sums (S^T k, G^T k) stay in registers (DPP rotates
+// and two row swaps) and a token needs no barrier.  The row sums (dq, dk) are
+// reduced over the CW lanes of a row group by a reduce-scatter that leaves each lane a contiguous run of
 // rows (one vector store per token); they and the scalar gradients (dalpha,
 // dbeta) are per-group partials, added over the groups in a fixed order by a
 // last kernel (so the result does not depend on scheduling).  Launches:
@@ -41,27 +41,30 @@ constexpr int kRouteLinear = 1;  // route id of the linear (Gated DeltaNet) oper
 
 template <int D>
 struct GdnBwdCfg {
-  static constexpr int CW = 8;             // state columns per workgroup
+  static constexpr int CW = D == 128 ? 4 : 8;  // state columns per workgroup (a lane's rows fill 16-byte words)
   static constexpr int NCG = D / CW;       // column groups (workgroups) per head
-  static constexpr int NT = 64;            // one wave: CW columns x 8 row groups
-  static constexpr int RPT = D * CW / NT;  // state rows per thread (D / 8)
+  static constexpr int NT = 64;            // one wave: CW columns x 64 / CW row groups
+  static constexpr int RPT = D * CW / NT;  // state rows per thread
   static constexpr int PF = 4;             // forward tokens of inputs in flight (ring depth)
   static constexpr int PFB = 2;            // the same for the backward sweep (inputs and S_{t-1})
-  static_assert(CW == 8 && RPT % 4 == 0 && CHUNK % PF == 0 && CHUNK % PFB == 0, "8 columns, whole row vectors");
+  static_assert((CW == 4 || CW == 8) && RPT % 8 == 0 && CHUNK % PF == 0 && CHUNK % PFB == 0,
+                "4 or 8 columns, whole row vectors");
 };
 
 size_t gdn_bwd_ws_bytes(int B, int H, int L, int D) {
-  const size_t nc = (size_t)L / CHUNK, ntok = (size_t)B * H * L, ncg = (size_t)D / GdnBwdCfg<128>::CW;
+  const size_t nc = (size_t)L / CHUNK, ntok = (size_t)B * H * L, ncg = (size_t)(D == 128 ? GdnBwdCfg<128>::NCG : GdnBwdCfg<64>::NCG);
   const size_t floats = (size_t)B * H * (nc + CHUNK) * D * D  // chunk-start states, chunk token states
                         + 2 * ntok * ncg * D                  // dq, dk partials
                         + 2 * ntok * ncg;                     // dalpha, dbeta partials
   return (floats * 4 + 255) / 256 * 256;
 }
 
-// sum over the wave's 8 row groups of a per-thread partial for the thread's
-// column (lanes l and l + 8 of each 16-lane row by a DPP rotate, the 4 rows by
+// sum over the wave's row groups of a per-thread partial for the thread's
+// column (the lanes l + CW i of each 16-lane row by DPP rotates, the 4 rows by
 // row swaps); every lane receives its column's total
+template <int CW>
 __device__ __forceinline__ float col_sum(float x) {
+  if (CW == 4) x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x124, 0xF, 0xF, true));  // row_ror 4
   x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, true));  // row_ror 8
   return group4_sum(x);
 }
@@ -78,16 +81,21 @@ __device__ __forceinline__ void rs_step(float* v, bool keep_lo) {
     v[k] = keep + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send), CTRL, 0xF, 0xF, true));
   }
 }
-// Sum of each of the N values over the 8 lanes of a row group (lanes jl =
-// 0..7, 8-aligned); lane jl is left with the sums of values jl N/8 ..
-// (jl + 1) N/8 - 1 in v[0 .. N/8).  The pairings are l <-> 7 - l, l <-> l ^ 2,
-// l <-> l ^ 1, which together span the 8 lanes.
-template <int N>
-__device__ __forceinline__ void group8_reduce_scatter(float* v, int jl) {
-  static_assert(N % 8 == 0, "whole values per lane");
-  rs_step<N, 0x141>(v, (jl & 4) == 0);      // row_half_mirror
-  rs_step<N / 2, 0x4E>(v, (jl & 2) == 0);   // quad_perm 2,3,0,1
-  rs_step<N / 4, 0xB1>(v, (jl & 1) == 0);   // quad_perm 1,0,3,2
+// Sum of each of the N values over the CW lanes of a row group (lanes jl =
+// 0..CW-1, CW-aligned); lane jl is left with the sums of values jl N/CW ..
+// (jl + 1) N/CW - 1 in v[0 .. N/CW).  The pairings are l <-> 7 - l (CW = 8),
+// l <-> l ^ 2, l <-> l ^ 1, which together span the CW lanes.
+template <int CW, int N>
+__device__ __forceinline__ void group_reduce_scatter(float* v, int jl) {
+  static_assert(N % CW == 0, "whole values per lane");
+  if constexpr (CW == 8) {
+    rs_step<N, 0x141>(v, (jl & 4) == 0);     // row_half_mirror
+    rs_step<N / 2, 0x4E>(v, (jl & 2) == 0);  // quad_perm 2,3,0,1
+    rs_step<N / 4, 0xB1>(v, (jl & 1) == 0);  // quad_perm 1,0,3,2
+  } else {
+    rs_step<N, 0x4E>(v, (jl & 2) == 0);
+    rs_step<N / 2, 0xB1>(v, (jl & 1) == 0);
+  }
 }
 
 // alpha or beta of token c0 + s, from the chunk's values held one per lane
@@ -172,7 +180,7 @@ __device__ __forceinline__ void gdn_fwd_token(float (&S)[GdnBwdCfg<D>::RPT], con
   float p4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < RPT; ++i) p4[i & 3] += S[i] * x.k[i];
-  const float a = col_sum((p4[0] + p4[1]) + (p4[2] + p4[3]));
+  const float a = col_sum<GdnBwdCfg<D>::CW>((p4[0] + p4[1]) + (p4[2] + p4[3]));
 #pragma unroll
   for (int i = 0; i < RPT; ++i) S[i] = al * (S[i] - be * x.k[i] * a) + be * x.k[i] * x.v;
 }
@@ -239,17 +247,17 @@ __global__ void __launch_bounds__(64) k_gdn_bwd(const T* __restrict__ q, const T
                                                  float* __restrict__ dS_init, int H, int L, int G) {
   using C = GdnBwdCfg<D>;
   constexpr int NV = 2 * C::RPT;  // row-sum values per thread and token: dq, dk at its rows
-  constexpr int VPL = NV / 8;     // of which each lane stores VPL after the row-group reduction
+  constexpr int VPL = NV / C::CW;  // of which each lane stores VPL after the row-group reduction
   const int nc = L / CHUNK;
   const int bh = bid_x() / C::NCG, cg = bid_x() % C::NCG, b = bh / H, h = bh % H;
   const int grp = (G == 1) ? 0 : h;
   const int32_t* rt = route + ((int64_t)b * G + grp) * nc;
   const int t = tid_x(), jl = t % C::CW, rg = t / C::CW, lane = t;
   const int j = C::CW * cg + jl, r0 = rg * C::RPT;
-  // after the row-group reduction lane jl holds values jl VPL ..: dq (lanes 0-3) or dk (lanes 4-7) at rows
-  // r0 + (jl % 4) VPL ..
-  float* const dqk_p = (jl < 4) ? dq_p : dk_p;
-  const int rq0 = r0 + (jl % 4) * VPL;
+  // after the row-group reduction lane jl holds values jl VPL ..: dq (the lower half of the lanes) or dk
+  // at rows r0 + (jl % (CW / 2)) VPL ..
+  float* const dqk_p = (jl < C::CW / 2) ? dq_p : dk_p;
+  const int rq0 = r0 + (jl % (C::CW / 2)) * VPL;
   const int64_t tok0 = (int64_t)bh * L;
   const T* qh = q + tok0 * D;
   const T* kh = k + tok0 * D;
@@ -321,8 +329,8 @@ __global__ void __launch_bounds__(64) k_gdn_bwd(const T* __restrict__ q, const T
           pa[i & 3] += Sp[i] * x.k[i];
           pw[i & 3] += Gm[i] * x.k[i];
         }
-        const float a = col_sum((pa[0] + pa[1]) + (pa[2] + pa[3]));
-        const float w = col_sum((pw[0] + pw[1]) + (pw[2] + pw[3]));
+        const float a = col_sum<C::CW>((pa[0] + pa[1]) + (pa[2] + pa[3]));
+        const float w = col_sum<C::CW>((pw[0] + pw[1]) + (pw[2] + pw[3]));
         const float al = lane_bcast(al_c, s), be = lane_bcast(be_c, s), vj = x.v, doj = x.d_o;
         const float cv = be * vj - al * be * a, cw = al * be * w;
         float pal = 0.f, rv[NV];
@@ -335,7 +343,7 @@ __global__ void __launch_bounds__(64) k_gdn_bwd(const T* __restrict__ q, const T
           pal += Gm[i] * erased;
           Gm[i] = al * (Gm[i] - be * ki * w);  // the gradient of S_{t-1}
         }
-        group8_reduce_scatter<NV>(rv, jl);
+        group_reduce_scatter<C::CW, NV>(rv, jl);
         const int64_t tok = tok0 + tt;
         float* dst = dqk_p + (tok * C::NCG + cg) * D + rq0;
         if constexpr (VPL % 4 == 0) {
