@@ -469,7 +469,7 @@ KERNEL_NAMES = [  # substring of the kernel symbol -> short name
     ("k_decode_commit", "decode_commit"), ("k_handoff_state", "handoff_state"), ("k_handoff_kv", "handoff_kv"),
     ("k_sm_bwd_delta", "sm_bwd_delta"), ("k_sm_bwd_dq", "sm_bwd_dq"), ("k_sm_bwd_dkdv", "sm_bwd_dkdv"),
     ("k_gdn_bwd_ckpt", "gdn_bwd_ckpt"), ("k_gdn_bwdI", "gdn_bwd"), ("k_gdn_bwd_reduce", "gdn_bwd_reduce"),
-    ("k_merge_bwd_reduce", "merge_bwd_reduce"), ("k_merge_bwdI", "merge_bwd"),
+    ("k_merge_bwd_reduce", "merge_bwd_reduce"), ("k_merge_bwd_final", "merge_bwd_final"), ("k_merge_bwdI", "merge_bwd"),
     ("AUnaryFunctor<float, float", "calib_mul_256MiB"),
 ]
 

@@ -208,55 +208,84 @@ __global__ void __launch_bounds__(256) k_merge_bwd(const Tq* __restrict__ q, con
 }
 
 // dW_mix (per head when wmix_hs != 0, else over every head) and the gains'
-// gradients from the blocks' partials: one workgroup per output element, each
-// thread adding a fixed strided subset of the blocks, then a fixed-order tree
-// (deterministic)
+// gradients from the blocks' partials, in two deterministic stages.  Output
+// groups of 64 consecutive partial slots: the gains' 2D slots (over every
+// block), then D / 64 groups of dW_mix slots per head (or once, shared).
+// Stage 1: workgroup (group, range) adds the group's 64 slots over one of
+// kMergeSplit contiguous block ranges (wave w takes every 4th block, so each
+// wave reads 256 contiguous bytes per block), the 4 waves added in order.
+// Stage 2: each slot's kMergeSplit range sums added in range order.
+constexpr int kMergeSplit = 64;
+
+__device__ __forceinline__ void merge_group(int g, int D, int per_head, int64_t nblk, int H, int& base, int& hh,
+                                            bool& head_only, int64_t& count) {
+  const int gains = 2 * D / 64;
+  if (g < gains) {
+    base = D + 64 * g;  // partial slots D .. 3D - 1: dg_sm, dg_lin
+    hh = 0;
+    head_only = false;
+    count = nblk;
+  } else {
+    const int r = g - gains;
+    hh = per_head ? r / (D / 64) : 0;
+    base = 64 * (r % (D / 64));  // partial slots 0 .. D - 1: dW_mix column 0
+    head_only = per_head != 0;
+    count = head_only ? nblk / H : nblk;  // a head's blocks: B runs of blk_per_head
+  }
+}
+
 template <int D>
 __global__ void __launch_bounds__(256) k_merge_bwd_reduce(const float* __restrict__ part, int64_t nblk,
                                                           int64_t blk_per_head, int H, int per_head,
-                                                          float* __restrict__ dw_mix, float* __restrict__ dg_sm,
-                                                          float* __restrict__ dg_lin) {
-  __shared__ float red[256];
-  // outputs: [0, D) dg_sm, [D, 2D) dg_lin, then dW_mix column sums: D (shared) or H D (per head)
-  const int e = bid_x(), t = tid_x();
-  int off, hh = 0;
-  bool head_only = false;
-  if (e < 2 * D) {
-    off = D + e;  // partial slots D .. 3D - 1
-  } else {
-    const int r = e - 2 * D;
-    hh = per_head ? r / D : 0;
-    off = r % D;
-    head_only = per_head != 0;
-  }
-  const int64_t count = head_only ? nblk / H : nblk;  // a head's blocks: B runs of blk_per_head
+                                                          float* __restrict__ part2) {
+  __shared__ float red[4][64];
+  const int g = bid_x() / kMergeSplit, sp = bid_x() % kMergeSplit, t = tid_x(), el = t & 63, sb = t >> 6;
+  int base, hh;
+  bool head_only;
+  int64_t count;
+  merge_group(g, D, per_head, nblk, H, base, hh, head_only, count);
+  const int64_t chunk = (count + kMergeSplit - 1) / kMergeSplit;
+  const int64_t n0 = sp * chunk, n1 = min(count, n0 + chunk);
   float s = 0.f;
-  for (int64_t n = t; n < count; n += 256) {
+  for (int64_t n = n0 + sb; n < n1; n += 4) {
     const int64_t x = head_only ? ((n / blk_per_head) * H + hh) * blk_per_head + n % blk_per_head : n;
-    s += part[x * 3 * D + off];
+    s += part[x * 3 * D + base + el];
   }
-  red[t] = s;
+  red[sb][el] = s;
   __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (t < w) red[t] += red[t + w];
-    __syncthreads();
-  }
-  if (t != 0) return;
-  s = red[0];
-  if (e < D) {
-    if (dg_sm) dg_sm[e] = s;
-  } else if (e < 2 * D) {
-    if (dg_lin) dg_lin[e - D] = s;
+  if (t < 64) part2[(int64_t)bid_x() * 64 + t] = (red[0][t] + red[1][t]) + (red[2][t] + red[3][t]);
+}
+
+template <int D>
+__global__ void __launch_bounds__(64) k_merge_bwd_final(const float* __restrict__ part2, int64_t nblk, int H,
+                                                        int per_head, float* __restrict__ dw_mix,
+                                                        float* __restrict__ dg_sm, float* __restrict__ dg_lin) {
+  const int g = bid_x(), t = tid_x();
+  int base, hh;
+  bool head_only;
+  int64_t count;
+  merge_group(g, D, per_head, nblk, H, base, hh, head_only, count);
+  float s = 0.f;
+  for (int sp = 0; sp < kMergeSplit; ++sp) s += part2[((int64_t)g * kMergeSplit + sp) * 64 + t];
+  const int slot = base + t;
+  if (g < 2 * D / 64) {
+    if (slot < 2 * D) {
+      if (dg_sm) dg_sm[slot - D] = s;
+    } else if (dg_lin) {
+      dg_lin[slot - 2 * D] = s;
+    }
   } else if (dw_mix) {
-    dw_mix[((int64_t)hh * D + off) * 2] = s;
-    dw_mix[((int64_t)hh * D + off) * 2 + 1] = -s;
+    dw_mix[((int64_t)hh * D + slot) * 2] = s;
+    dw_mix[((int64_t)hh * D + slot) * 2 + 1] = -s;
   }
 }
 
 size_t merge_bwd_ws_bytes(int B, int H, int L, int D) {
   const int64_t tpb = 256 / (D / 8);
   const int64_t nblk = ((int64_t)B * H * L) / tpb;
-  return ((size_t)nblk * 3 * D * 4 + 255) / 256 * 256;
+  const int64_t ngroups = 2 * D / 64 + (int64_t)H * D / 64;  // the per-head case (the larger)
+  const size_t part = ((size_t)nblk * 3 * D * 4 + 255) / 256 * 256;
+  return part + (size_t)ngroups * kMergeSplit * 64 * 4;
 }
 
 template <typename Tq, typename Tb, int D>
@@ -268,14 +297,18 @@ hipError_t launch_merge_backward(const Tq* q, const Tb* o_sm, const Tb* o_gdn, c
   const int64_t ntok = (int64_t)B * H * L;
   const int64_t nblk = ntok / TPB;  // L % 64 == 0: whole blocks, each within one head
   float* part = (float*)ws;
+  float* part2 = (float*)((char*)ws + ((size_t)nblk * 3 * D * 4 + 255) / 256 * 256);
   hipLaunchKernelGGL((k_merge_bwd<Tq, Tb, D>), dim3((unsigned)nblk), dim3(256), 0, st, q, o_sm, o_gdn, w_mix, hs,
                      g_sm, g_lin, d_out, d_sm, d_gdn, dq, part, H, L, eps);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int per_head = hs != 0;
-  const int nout = 2 * D + (per_head ? H * D : D);
-  hipLaunchKernelGGL((k_merge_bwd_reduce<D>), dim3((unsigned)nout), dim3(256), 0, st, part, nblk, (int64_t)(L / TPB), H,
-                     per_head, dw_mix, dg_sm, dg_lin);
+  const int ngroups = 2 * D / 64 + (per_head ? H : 1) * D / 64;
+  hipLaunchKernelGGL((k_merge_bwd_reduce<D>), dim3((unsigned)(ngroups * kMergeSplit)), dim3(256), 0, st, part, nblk,
+                     (int64_t)(L / TPB), H, per_head, part2);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((k_merge_bwd_final<D>), dim3((unsigned)ngroups), dim3(64), 0, st, part2, nblk, H, per_head,
+                     dw_mix, dg_sm, dg_lin);
   return hipGetLastError();
 }
 
