@@ -45,8 +45,8 @@ struct GdnBwdCfg {
   static constexpr int NCG = D / CW;       // column groups (workgroups) per head
   static constexpr int NT = 64;            // one wave: CW columns x 64 / CW row groups
   static constexpr int RPT = D * CW / NT;  // state rows per thread
-  static constexpr int PF = 4;             // forward tokens of inputs in flight (ring depth)
-  static constexpr int PFB = 2;            // the same for the backward sweep (inputs and S_{t-1})
+  static constexpr int PF = 16;            // forward tokens of inputs in flight (ring depth)
+  static constexpr int PFB = 8;            // the same for the backward sweep (inputs and S_{t-1})
   static_assert((CW == 4 || CW == 8) && RPT % 8 == 0 && CHUNK % PF == 0 && CHUNK % PFB == 0,
                 "4 or 8 columns, whole row vectors");
 };
