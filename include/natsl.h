@@ -196,7 +196,10 @@ natsl_status natsl_softmax_masked_backward(const natsl_dims* dims, const void* q
  *   dS_init        [B, H, Dk, Dv] fp32 gradient w.r.t. S_init, or NULL
  *   ws             workspace of natsl_workspace_size(NATSL_ENTRY_GDN_BACKWARD)
  * Every output is written, not accumulated.  This is the per-token form (one
- * workgroup per head, three barriers per token): a correct path, not a fast one.
+ * wave per group of 4 state columns at D = 128, 8 at D = 64; a checkpoint
+ * pass, a per-chunk recompute and reverse sweep, then a fixed-order reduction
+ * of the groups' partials, so results are deterministic): latency-bound, not
+ * the chunkwise matrix form.
  */
 natsl_status natsl_gdn_backward(const natsl_dims* dims, const void* q, const void* k, const void* v,
                                 const float* alpha, const float* beta, const int32_t* route, const float* S_init,
