@@ -370,31 +370,45 @@ __global__ void __launch_bounds__(64) k_gdn_bwd(const T* __restrict__ q, const T
 }
 
 // dq, dk, dalpha, dbeta: the NCG groups' partials added in group order
-// (dalpha and dbeta interleaved)
+// (dalpha and dbeta interleaved).  Threads [0, ntok D/4) take 4 consecutive
+// rows of one token's dq and dk (16-byte loads from the workspace; scalar
+// stores, the outputs carrying no alignment promise); threads
+// [ntok D/4, ntok D/4 + ntok) take one token's dalpha and dbeta.
 template <int D>
 __global__ void __launch_bounds__(256) k_gdn_bwd_reduce(const float* __restrict__ dq_p, const float* __restrict__ dk_p,
                                                         const float* __restrict__ dab_p, float* __restrict__ dq,
                                                         float* __restrict__ dk, float* __restrict__ dalpha,
                                                         float* __restrict__ dbeta, int64_t ntok) {
   constexpr int NCG = GdnBwdCfg<D>::NCG;
+  static_assert(NCG % 2 == 0 && D % 4 == 0, "whole 16-byte partial vectors");
   const int64_t gid = (int64_t)bid_x() * 256 + tid_x();
-  const int64_t tok = gid / D;
-  const int i = (int)(gid % D);
-  if (tok >= ntok) return;
-  float sq = 0.f, sk = 0.f;
+  const int64_t nvec = ntok * (D / 4);
+  if (gid < nvec) {
+    const int64_t tok = gid / (D / 4);
+    const int i = (int)(gid % (D / 4)) * 4;
+    float sq[4] = {0.f, 0.f, 0.f, 0.f}, sk[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int cg = 0; cg < NCG; ++cg) {
-    sq += dq_p[(tok * NCG + cg) * D + i];
-    sk += dk_p[(tok * NCG + cg) * D + i];
-  }
-  dq[tok * D + i] = sq;
-  dk[tok * D + i] = sk;
-  if (i == 0) {
+    for (int cg = 0; cg < NCG; ++cg) {
+      const float4 a = *(const float4*)(dq_p + (tok * NCG + cg) * D + i);
+      const float4 c = *(const float4*)(dk_p + (tok * NCG + cg) * D + i);
+      sq[0] += a.x; sq[1] += a.y; sq[2] += a.z; sq[3] += a.w;
+      sk[0] += c.x; sk[1] += c.y; sk[2] += c.z; sk[3] += c.w;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      dq[tok * D + i + r] = sq[r];
+      dk[tok * D + i + r] = sk[r];
+    }
+  } else if (gid < nvec + ntok) {
+    const int64_t tok = gid - nvec;
     float sa = 0.f, sb = 0.f;
 #pragma unroll
-    for (int x = 0; x < NCG; ++x) {
-      sa += dab_p[(tok * NCG + x) * 2];
-      sb += dab_p[(tok * NCG + x) * 2 + 1];
+    for (int x = 0; x < NCG; x += 2) {  // groups x and x + 1
+      const float4 a = *(const float4*)(dab_p + (tok * NCG + x) * 2);
+      sa += a.x;
+      sb += a.y;
+      sa += a.z;
+      sb += a.w;
     }
     dalpha[tok] = sa;
     dbeta[tok] = sb;
@@ -423,7 +437,7 @@ hipError_t launch_gdn_backward(const T* q, const T* k, const T* v, const float* 
   hipLaunchKernelGGL((k_gdn_bwd<T, D>), dim3(grid), dim3(C::NT), lds, st, q, k, v, alpha, beta, route, d_o,
                      dS_final, ckpt, scratch, dq_p, dk_p, dab_p, dv, dS_init, H, L, G);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int64_t threads = ntok * D;
+  const int64_t threads = ntok * (D / 4) + ntok;
   hipLaunchKernelGGL((k_gdn_bwd_reduce<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, dq_p, dk_p,
                      dab_p, dq, dk, dalpha, dbeta, ntok);
   return hipGetLastError();
