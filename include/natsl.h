@@ -21,10 +21,19 @@
  *     library never allocates, frees or synchronises device memory;
  *   - scratch memory is a caller-provided workspace whose size comes from
  *     natsl_workspace_size(); it must be 256-byte aligned;
- *   - every call is asynchronous on the caller's stream (natsl_forward may
- *     fork work onto one library-owned helper stream of default priority and
- *     joins it back before returning; the join is an event wait, not a host
- *     synchronisation);
+ *   - every call is asynchronous on the caller's stream (natsl_forward forks
+ *     work onto a library-owned helper stream of default priority and joins
+ *     it back before returning, also when it fails after the fork; the join
+ *     is an event wait, not a host synchronisation);
+ *   - threads: every entry point may be called from several host threads at
+ *     once, on the same or different streams.  The library keeps no mutable
+ *     state between calls except (a) helper streams and their events, which
+ *     natsl_forward takes from a per-device pool for the duration of its
+ *     enqueue, so concurrent forwards never share them, (b) a record of the
+ *     kernels whose LDS limit has been raised, guarded by a mutex, and (c)
+ *     the natsl_profile_* timing records, guarded by a mutex (timing several
+ *     threads at once mixes their records).  Calls whose device buffers
+ *     overlap must be ordered by the caller (same stream, or events);
  *   - every call validates its arguments on the host BEFORE enqueueing any
  *     work; on failure nothing is enqueued, a status != NATSL_OK is
  *     returned and natsl_last_error() (thread-local) describes the problem;
@@ -33,9 +42,12 @@
  *   - tensors are dense row-major with the shapes given; io tensors (x, q, k,
  *     v, out) hold the io dtype of natsl_dims, alpha/beta/weights are fp32;
  *   - supported: Dk == Dv in {64, 128}, chunk == 64, L % 64 == 0, L >= 64,
- *     route_groups G in {1, H}, H <= 1024, d_model % 8 == 0 and
- *     8 <= d_model <= 32768 (where d_model is used).  B == 0 is a no-op that
- *     succeeds after the dims check (tensor pointers may then be NULL).
+ *     B * H * L < 2^31, route_groups G in {1, H}, H <= 1024, d_model % 8 == 0
+ *     and 8 <= d_model <= 32768 (where d_model is used).  The Gated DeltaNet
+ *     branch (natsl_gdn_chunk, natsl_forward) with bf16 io and D = 128 takes
+ *     at most 15232 chunks per sequence (L <= 974848); a longer L is
+ *     NATSL_ERR_UNSUPPORTED before anything is enqueued.  B == 0 is a no-op
+ *     that succeeds after the dims check (tensor pointers may then be NULL).
  *   - route ids: 0 = softmax attention, 1 = Gated DeltaNet (linear).
  */
 #ifndef NATSL_H
@@ -287,8 +299,20 @@ typedef struct {
 } natsl_forward_args;
 
 /*
- * Whole layer forward: route + compaction, Gated DeltaNet branch and softmax
- * branch (run concurrently), merge.  ws from NATSL_ENTRY_FORWARD.
+ * Whole layer forward ("Technische Samenvatting: Neural Attention Search
+ * Linear (NAtS-L)", Kernmechanismen 1-4): route + compaction (item 1), the
+ * Gated DeltaNet branch with per-chunk rollback and the softmax branch over
+ * the retained softmax chunks plus the own chunk (item 3; run concurrently),
+ * then RMSNorm of both outputs and the Q-derived weighted sum (item 4).
+ * Every pointer of args is a device pointer as documented in the struct; x
+ * and w_score may be NULL only with route_override.  Outputs: out always;
+ * route_out, scores_out (router only), o_sm_dbg, o_gdn_dbg, S_final when
+ * non-NULL.  ws from NATSL_ENTRY_FORWARD (caller-owned, >= that size, 256-byte
+ * aligned); the call reads and writes it until the work it enqueues on
+ * `stream` has finished.  Errors: NATSL_ERR_INVALID_ARG (NULL input, bad
+ * dtype or stride, S_init together with a prefix), NATSL_ERR_UNSUPPORTED
+ * (dims), NATSL_ERR_WORKSPACE, all before anything is enqueued;
+ * NATSL_ERR_DEVICE for a failed HIP call (the helper stream is still joined).
  * Chunked prefill: with args->prefix set, the L tokens are a segment that
  * continues that decode cache, which must sit at a chunk boundary
  * (n_open == 0, e.g. right after natsl_decode_handoff): every query of the
@@ -324,13 +348,21 @@ typedef struct {
 } natsl_decode_args;
 
 /*
- * One decode step: every sequence appends one token to its open chunk.
- * Softmax over the committed softmax chunks' rows, the open chunk's earlier
- * rows and the new token; the Gated DeltaNet state is pseudo-updated from
- * S_carry (first token of a chunk) or S_work.  When the open chunk reaches
- * 64 tokens it is routed from x_sum / 64: softmax commits its 64 rows
- * (n_committed += 64), linear commits its state (S_carry <- S_work) and its
- * rows are dropped.  The new row is written at index n_committed + n_open;
+ * One decode step ("Technische Samenvatting: Neural Attention Search Linear
+ * (NAtS-L)", Kernmechanismen 1, 3 and 4 applied one token at a time: the two
+ * hidden states are the retained softmax KV and the Gated DeltaNet state;
+ * the chunk's operation is chosen when the chunk is complete, and only the
+ * chosen operation keeps it).  Every sequence appends one token to its open
+ * chunk.  Softmax over the committed softmax chunks' rows, the open chunk's
+ * earlier rows and the new token; the Gated DeltaNet state is pseudo-updated
+ * from S_carry (first token of a chunk) or S_work.  When the open chunk
+ * reaches 64 tokens it is routed from x_sum / 64: softmax commits its 64
+ * rows (n_committed += 64), linear commits its state (S_carry <- S_work) and
+ * its rows are dropped.  The cache (natsl_decode_cache) is read and updated
+ * in place on the device; args' tensors are read, out / route_out / the dbg
+ * outputs written.  Errors: NATSL_ERR_INVALID_ARG (NULL tensor, cap < 1),
+ * NATSL_ERR_UNSUPPORTED (dims), NATSL_ERR_WORKSPACE, all before anything is
+ * enqueued; NATSL_ERR_DEVICE for a failed launch.  The new row is written at index n_committed + n_open;
  * if that index is >= cap the row is not written and *err_flag is set to 1
  * (checked by the caller after the step; counters still advance).
  * ws from NATSL_ENTRY_DECODE_STEP (depends on cap via dims->L: pass

@@ -8,11 +8,33 @@
 #include <string.h>
 
 #include <mutex>
+#include <set>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "../../include/natsl.h"
+#include "helper_pool.hpp"
 #include "kernels.hpp"
+
+namespace natsl {
+
+// (device, kernel) pairs whose dynamic LDS limit has been raised
+static std::mutex g_attr_mu;
+static std::set<std::pair<int, const void*>> g_attr_done;
+
+hipError_t set_lds_limit(const void* fn, int bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(g_attr_mu);
+  if (g_attr_done.count({dev, fn})) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) g_attr_done.insert({dev, fn});
+  return e;
+}
+
+}  // namespace natsl
 
 using namespace natsl;
 
@@ -58,6 +80,7 @@ int g_prof_open[KID_COUNT];         // index of the record whose start was recor
 int g_prof_only = -1;                // record only this kernel id (-1: all)
 
 void prof_hook(int kid, hipStream_t st, int phase) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
   if (!g_prof_on) return;
   if (g_prof_only >= 0 && kid != g_prof_only) return;
   if (phase == 0) {
@@ -75,32 +98,46 @@ void prof_hook(int kid, hipStream_t st, int phase) {
 }
 void (*prof_fn())(int, hipStream_t, int) { return g_prof_on ? prof_hook : nullptr; }
 
-// ------------------------------------------------------------ helper stream ----
-struct DevCtx {
-  bool init = false;
+// ------------------------------------------------------------ helper streams ----
+// natsl_forward runs the Gated DeltaNet branch on a helper stream (default
+// priority) ordered against the caller's stream by three events.  A helper
+// (stream + events) belongs to one call for the whole of that call's enqueue
+// (HelperPool: taken from a per-device free list, given back when the call
+// returns), so concurrent calls from several host threads never share events
+// and never serialise on one helper stream.  A helper is reused only after
+// its previous call has enqueued all its waits, and a HIP event wait captures
+// the record that precedes it, so reuse cannot alias two calls' records.
+struct Helper {
   hipStream_t aux = nullptr;
   hipEvent_t fork = nullptr, join = nullptr, routed = nullptr;
 };
-std::mutex g_ctx_mu;
-DevCtx g_ctx[64];
+HelperPool<Helper> g_helpers;
 
-natsl_status get_ctx(DevCtx** out) {
+Helper* make_helper(int /*dev: current*/) {
+  Helper* h = new Helper();
+  if (hipStreamCreateWithFlags(&h->aux, hipStreamNonBlocking) != hipSuccess) {
+    delete h;
+    return nullptr;
+  }
+  if (hipEventCreateWithFlags(&h->fork, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&h->join, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&h->routed, hipEventDisableTiming) != hipSuccess)
+    return nullptr;  // the stream is kept: nothing may destroy a stream another call could use
+  return h;
+}
+
+natsl_status acquire_helper(HelperPool<Helper>::Lease* lease) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return dev_fail(e, "hipGetDevice");
-  if (dev < 0 || dev >= 64) return fail(NATSL_ERR_UNSUPPORTED, "device ordinal %d", dev);
-  std::lock_guard<std::mutex> lk(g_ctx_mu);
-  DevCtx& c = g_ctx[dev];
-  if (!c.init) {
-    if ((e = hipStreamCreateWithFlags(&c.aux, hipStreamNonBlocking)) != hipSuccess)
-      return dev_fail(e, "hipStreamCreateWithFlags");
-    if ((e = hipEventCreateWithFlags(&c.fork, hipEventDisableTiming)) != hipSuccess ||
-        (e = hipEventCreateWithFlags(&c.join, hipEventDisableTiming)) != hipSuccess ||
-        (e = hipEventCreateWithFlags(&c.routed, hipEventDisableTiming)) != hipSuccess)
-      return dev_fail(e, "hipEventCreateWithFlags");
-    c.init = true;
+  Helper* h = g_helpers.acquire(dev, make_helper);
+  if (!h) {
+    e = hipGetLastError();
+    return e != hipSuccess ? dev_fail(e, "helper stream / events") : fail(NATSL_ERR_UNSUPPORTED, "device ordinal %d", dev);
   }
-  *out = &c;
+  lease->pool = &g_helpers;
+  lease->dev = dev;
+  lease->ctx = h;
   return NATSL_OK;
 }
 
@@ -168,6 +205,15 @@ size_t fwd_ws(const natsl_dims* d, natsl_dtype branch, FwdWs* w, void* base) {
     w->mixd = (float*)(p + o_mix);
   }
   return off;
+}
+
+// the Gated DeltaNet branch's sequence-length limit (checked before any launch)
+natsl_status check_gdn_len(const natsl_dims* d) {
+  const int maxc = gdn_max_chunks(d->io == NATSL_BF16, d->Dk);
+  if (nchunks(d) > maxc)
+    return fail(NATSL_ERR_UNSUPPORTED, "L=%d: the Gated DeltaNet branch supports at most %d chunks (L <= %lld) "
+                "for this io dtype and head dim", d->L, maxc, (long long)maxc * 64);
+  return NATSL_OK;
 }
 
 natsl_status check_ws(void* ws, size_t have, size_t need) {
@@ -311,10 +357,12 @@ natsl_status natsl_workspace_size(int entry, const natsl_dims* dims, size_t* byt
       return ok();
     case NATSL_ENTRY_GDN_CHUNK:
       CHECK(check_dims(dims, true, false));
+      CHECK(check_gdn_len(dims));
       *bytes = gdn_ws_bytes(dims->io == NATSL_BF16, dims->Dk, (int64_t)dims->B * dims->H * nchunks(dims));
       return ok();
     case NATSL_ENTRY_FORWARD:
       CHECK(check_dims(dims, true, false));
+      CHECK(check_gdn_len(dims));
       *bytes = fwd_ws(dims, NATSL_F32, nullptr, nullptr);  // fp32 branches: the larger of the two
       return ok();
     case NATSL_ENTRY_DECODE_STEP:
@@ -374,8 +422,8 @@ natsl_status natsl_gdn_chunk(const natsl_dims* dims, const void* q, const void* 
   NEED(route, "route");
   NEED(o_gdn, "o_gdn");
   if (o_dtype != NATSL_F32 && o_dtype != NATSL_BF16) return fail(NATSL_ERR_INVALID_ARG, "bad o_dtype");
-  size_t need = 0;
-  natsl_workspace_size(NATSL_ENTRY_GDN_CHUNK, dims, &need);
+  CHECK(check_gdn_len(dims));
+  const size_t need = gdn_ws_bytes(dims->io == NATSL_BF16, dims->Dk, (int64_t)dims->B * dims->H * nchunks(dims));
   CHECK(check_ws(ws, ws_bytes, need));
   hipError_t e = do_gdn(dims, q, k, v, alpha, beta, route, S_init, o_gdn, o_dtype, S_final, ws, stream);
   if (e != hipSuccess) return dev_fail(e, "natsl_gdn_chunk");
@@ -437,6 +485,7 @@ natsl_status natsl_forward(const natsl_dims* dims, const natsl_forward_args* a, 
   if (a->branch_dtype != NATSL_F32 && a->branch_dtype != NATSL_BF16)
     return fail(NATSL_ERR_INVALID_ARG, "bad branch dtype");
   if (a->w_mix_head_stride < 0) return fail(NATSL_ERR_INVALID_ARG, "negative w_mix head stride");
+  CHECK(check_gdn_len(dims));
   // chunked prefill: the segment continues a decode cache at a chunk boundary
   SmPrefix pre;
   const float* S_init = a->S_init;
@@ -458,8 +507,9 @@ natsl_status natsl_forward(const natsl_dims* dims, const natsl_forward_args* a, 
   const size_t need = fwd_ws(dims, a->branch_dtype, nullptr, nullptr);
   CHECK(check_ws(ws, ws_bytes, need));
   fwd_ws(dims, a->branch_dtype, &w, ws);
-  DevCtx* ctx = nullptr;
-  CHECK(get_ctx(&ctx));
+  HelperPool<Helper>::Lease lease;
+  CHECK(acquire_helper(&lease));
+  Helper* ctx = lease.ctx;
   int32_t* route = a->route_out ? a->route_out : w.route;
   void* o_sm = a->o_sm_dbg ? a->o_sm_dbg : w.o_sm;
   void* o_gd = a->o_gdn_dbg ? a->o_gdn_dbg : w.o_gdn;
@@ -470,12 +520,19 @@ natsl_status natsl_forward(const natsl_dims* dims, const natsl_forward_args* a, 
   hipError_t e;
   if ((e = hipEventRecord(ctx->fork, stream)) != hipSuccess) return dev_fail(e, "hipEventRecord");
   if ((e = hipStreamWaitEvent(ctx->aux, ctx->fork, 0)) != hipSuccess) return dev_fail(e, "hipStreamWaitEvent");
+  // from here on, a failure still joins the helper stream back into the
+  // caller's stream (best effort), so that nothing the call queued can outlive
+  // what the caller orders after it
+  auto fail_joined = [&](hipError_t err, const char* where) {
+    if (hipEventRecord(ctx->join, ctx->aux) == hipSuccess) (void)hipStreamWaitEvent(stream, ctx->join, 0);
+    return dev_fail(err, where);
+  };
   e = do_route(dims, a->x, a->w_score, a->b_score, a->route_override, route, w.sel, w.nsb, a->scores_out, stream);
-  if (e != hipSuccess) return dev_fail(e, "natsl_forward/route");
-  if ((e = hipEventRecord(ctx->routed, stream)) != hipSuccess) return dev_fail(e, "hipEventRecord");
+  if (e != hipSuccess) return fail_joined(e, "natsl_forward/route");
+  if ((e = hipEventRecord(ctx->routed, stream)) != hipSuccess) return fail_joined(e, "hipEventRecord");
   e = do_gdn(dims, a->q, a->k, a->v, a->alpha, a->beta, route, S_init, o_gd, a->branch_dtype, a->S_final,
              w.gdn, ctx->aux, ctx->aux, nullptr, ctx->routed);
-  if (e != hipSuccess) return dev_fail(e, "natsl_forward/gdn");
+  if (e != hipSuccess) return fail_joined(e, "natsl_forward/gdn");
   // the softmax branch also leaves the merge's mixing scores (bf16 D = 128 kernel)
   bool mix_done = false;
   SmMix mix;
@@ -484,7 +541,7 @@ natsl_status natsl_forward(const natsl_dims* dims, const natsl_forward_args* a, 
   mix.d = w.mixd;
   mix.done = &mix_done;
   e = do_softmax(dims, a->q, a->k, a->v, w.sel, w.nsb, o_sm, a->branch_dtype, nullptr, stream, pre, mix);
-  if (e != hipSuccess) return dev_fail(e, "natsl_forward/softmax");
+  if (e != hipSuccess) return fail_joined(e, "natsl_forward/softmax");
   if ((e = hipEventRecord(ctx->join, ctx->aux)) != hipSuccess) return dev_fail(e, "hipEventRecord");
   if ((e = hipStreamWaitEvent(stream, ctx->join, 0)) != hipSuccess) return dev_fail(e, "hipStreamWaitEvent");
   e = do_merge(dims, a->q, o_sm, o_gd, a->branch_dtype, a->w_mix, a->w_mix_head_stride, a->g_sm, a->g_lin, a->out,

@@ -701,6 +701,8 @@ constexpr int SCH_UT = SCH_KT + 16384; // the workgroup's U~ columns (fp32 accum
 constexpr int SCH_GM = SCH_UT + 16384; // gamma[64], gamma_C at 64, exp(g_C - g)[64] at 80 (fp32)
 constexpr int SCH_STAGE = SCH_GM + 576;
 constexpr int SCH_ROUTE = 2 * SCH_STAGE;
+// route bytes of the head's chunks fill the rest of the LDS after the ring
+constexpr int SCH_MAX_NC = (LDS_MAX_BYTES - SCH_ROUTE) & ~15;
 constexpr int SCH_NW = 4;              // waves per workgroup
 constexpr int SCH_NSPLIT = 2;          // workgroups per head
 // (every wave reads all 64 KiB of shared operands from LDS per chunk, so LDS
@@ -734,7 +736,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW)
   constexpr int NB = 16 / NW;        // 1 KiB blocks of each 16 KiB operand per wave
   using C = GdnCfg<bf16, D>;
   extern __shared__ __align__(16) unsigned char lds[];
-  int32_t* rl = reinterpret_cast<int32_t*>(lds + SCH_ROUTE);
+  unsigned char* rl = lds + SCH_ROUTE;  // one route byte per chunk
 
   const int nc = L / CHUNK;
   // the NSPLIT workgroups of a head go to one XCD (workgroup p runs on XCD
@@ -761,7 +763,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW)
   const int g = lane >> 4, c = lane & 15;
   const int dv0 = 16 * NV * (NW * part + w);
 
-  for (int i = tid_x(); i < nc; i += 64 * NW) rl[i] = rt_g[i];
+  for (int i = tid_x(); i < nc; i += 64 * NW) rl[i] = (unsigned char)(rt_g[i] == 1);
 
   // fp32 state: rows d = 16 dt + 4g + i, columns dv0 + 16 nn + c
   f32x4 sm[8][NV];
@@ -1053,20 +1055,22 @@ hipError_t launch_gdn(const T* q, const T* k, const T* v, const float* alpha, co
   using C = GdnCfg<T, D>;
   constexpr int DVT = 32;
   constexpr int SCAN_NS = sizeof(T) == 2 ? 4 : 2;  // operand sets in flight in the scan
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_gdn_prep<T, D>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::PREP_LDS);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
   const int nc = L / CHUNK;
+  // (the C ABI has already rejected longer sequences; nothing is launched
+  // when this fails)
+  if (nc > gdn_max_chunks(sizeof(T) == 2, D)) return hipErrorInvalidValue;
+  hipError_t e = set_lds_limit((const void*)k_gdn_prep<T, D>, C::PREP_LDS);
+  if (e != hipSuccess) return e;
+  if constexpr (scan_head_form<T, D>()) {
+    e = set_lds_limit((const void*)k_gdn_scan_head<To, SCH_NW, SCH_NSPLIT>, SCH_ROUTE + SCH_MAX_NC);
+    if (e != hipSuccess) return e;
+  }
   const int64_t nch = (int64_t)B * H * nc;
   GdnWs<T, D> ws = carve<T, D>(wsp, nch);
   if (prof) prof(KID_GDN_PREP, st_prep, 0);
   hipLaunchKernelGGL((k_gdn_prep<T, D>), dim3((unsigned)nch), dim3(256), C::PREP_LDS, st_prep, q, k, v,
                      alpha, beta, ws, L);
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (prof) prof(KID_GDN_PREP, st_prep, 1);
   if (st_scan != st_prep) {
@@ -1081,15 +1085,7 @@ hipError_t launch_gdn(const T* q, const T* k, const T* v, const float* alpha, co
   }
   if (prof) prof(KID_GDN_SCAN, st_scan, 0);
   if constexpr (scan_head_form<T, D>()) {
-    static bool attr_head = false;
-    if (!attr_head) {
-      e = hipFuncSetAttribute((const void*)k_gdn_scan_head<To, SCH_NW, SCH_NSPLIT>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, SCH_ROUTE + 4096);
-      if (e != hipSuccess) return e;
-      attr_head = true;
-    }
-    if (nc > 1024) return hipErrorInvalidValue;
-    const size_t lds = SCH_ROUTE + ((size_t)nc * 4 + 255) / 256 * 256;
+    const size_t lds = SCH_ROUTE + ((size_t)nc + 15) / 16 * 16;
     hipLaunchKernelGGL((k_gdn_scan_head<To, SCH_NW, SCH_NSPLIT>), dim3((unsigned)(B * H * SCH_NSPLIT)), dim3(64 * SCH_NW),
                        lds, st_scan,
                        (const bf16*)q, (const bf16*)k,
@@ -1102,6 +1098,10 @@ hipError_t launch_gdn(const T* q, const T* k, const T* v, const float* alpha, co
   if (e != hipSuccess) return e;
   if (prof) prof(KID_GDN_SCAN, st_scan, 1);
   return hipSuccess;
+}
+
+int gdn_max_chunks(int io_is_bf16, int D) {
+  return (io_is_bf16 && D == 128) ? SCH_MAX_NC : (1 << 30);
 }
 
 #define INST(T, To, D)                                                                            \

@@ -28,6 +28,18 @@ enum {
   KID_COUNT
 };
 
+// Largest dynamic LDS a workgroup may request on gfx950 (160 KiB per CU).
+constexpr int LDS_MAX_BYTES = 160 * 1024;
+
+// Raises kernel fn's dynamic LDS limit to `bytes` on the current device,
+// once per (device, kernel); safe to call from several host threads.
+hipError_t set_lds_limit(const void* fn, int bytes);
+
+// Most chunks per sequence the Gated DeltaNet branch supports for this io
+// dtype and head dim (the bf16 D = 128 scan keeps one route byte per chunk in
+// LDS); the C ABI rejects longer sequences before launching anything.
+int gdn_max_chunks(int io_is_bf16, int D);
+
 template <typename T>
 hipError_t launch_route(const T* x, const float* w, const float* bsc, int B, int L, int d, int G,
                         int32_t* route_out, float* scores, hipStream_t st);

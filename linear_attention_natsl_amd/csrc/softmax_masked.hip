@@ -364,7 +364,9 @@ __global__ void __launch_bounds__(256, 2)
 // chunk c0 + m (32 each), so register use matches the kernel above.
 constexpr int SM2_STAGES = 4;
 constexpr int SM2_TILE_BYTES = 2 * CHUNK * 128 * 2;  // K + V, bf16, D = 128
-constexpr int SM2_LDS = SM2_STAGES * SM2_TILE_BYTES + 4 * 1024;  // + sel list (up to 1024 chunks)
+constexpr int SM2_LIST = 4096;  // key-tile list entries (prefix tiles + softmax chunks + own chunks)
+constexpr int SM2_LDS = SM2_STAGES * SM2_TILE_BYTES + 4 * SM2_LIST;
+static_assert(SM2_LDS <= LDS_MAX_BYTES, "ring + tile list exceed the LDS");
 
 __device__ __forceinline__ int sm2_kslot(int r, int q) { return q ^ (r & 15); }
 __device__ __forceinline__ int sm2_vslot(int r, int q) { return q ^ ((r & 7) << 1); }
@@ -642,33 +644,25 @@ hipError_t launch_softmax_masked(const T* q, const T* k, const T* v, const int32
   using C = SmCfg<T, D>;
   if (mix.done) *mix.done = false;
   if constexpr (sizeof(T) == 2 && D == 128) {
-    static bool attr2 = false;
-    if (!attr2) {
-      hipError_t e = hipFuncSetAttribute((const void*)k_softmax_v2<To>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                         SM2_LDS);
-      if (e != hipSuccess) return e;
-      attr2 = true;
-    }
     const int nc = L / CHUNK;
-    // the tile list (prefix tiles + chunks) lives in a 1024-entry LDS array
-    if (nc + (pre.n_committed ? pre.cap / CHUNK : 0) <= 1024) {
+    // the tile list (prefix tiles + chunks) lives in an SM2_LIST-entry LDS
+    // array; a longer list (a prefix cache of more than 4096 - nc chunks)
+    // takes the kernel below, which reads the chunk list from global memory
+    if ((int64_t)nc + (pre.n_committed ? pre.cap / CHUNK : 0) <= SM2_LIST) {
+      hipError_t e = set_lds_limit((const void*)k_softmax_v2<To>, SM2_LDS);
+      if (e != hipSuccess) return e;
       const int64_t grid = (int64_t)B * H * ((nc + 3) / 4);
       hipLaunchKernelGGL(k_softmax_v2<To>, dim3((unsigned)grid), dim3(512), SM2_LDS, st, (const bf16*)q,
                          (const bf16*)k, (const bf16*)v, sel_idx, nsel_before, o_sm, lse, H, L, G, scale * LOG2E,
                          (const bf16*)pre.k, (const bf16*)pre.v, pre.n_committed, pre.cap, mix.w_mix, mix.hs,
                          mix.w_mix ? mix.d : nullptr);
-      const hipError_t e = hipGetLastError();
+      e = hipGetLastError();
       if (e == hipSuccess && mix.done) *mix.done = mix.w_mix && mix.d;
       return e;
     }
   }
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_softmax_masked<T, To, D>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  const hipError_t ea = set_lds_limit((const void*)k_softmax_masked<T, To, D>, C::LDS_BYTES);
+  if (ea != hipSuccess) return ea;
   const int nc = L / CHUNK;
   const int nb = (nc + 1) / 2;
   const int64_t grid = (int64_t)B * H * nb;
@@ -994,19 +988,12 @@ hipError_t launch_softmax_backward(const T* q, const T* k, const T* v, const int
   const int nc = L / CHUNK;
   constexpr int LDS_DQ = 2 * C::BUF * (int)sizeof(T);
   constexpr int LDS_DKDV = 2 * C::BUF * (int)sizeof(T) + 2 * CHUNK * 4;
-  static bool attr = false;
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_sm_bwd_dq<T, D>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       LDS_DQ);
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute((const void*)k_sm_bwd_dkdv<T, D>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              LDS_DKDV);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
+  hipError_t e = set_lds_limit((const void*)k_sm_bwd_dq<T, D>, LDS_DQ);
+  if (e == hipSuccess) e = set_lds_limit((const void*)k_sm_bwd_dkdv<T, D>, LDS_DKDV);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((k_sm_bwd_delta<To, D>), dim3((unsigned)((ntok + 255) / 256)), dim3(256), 0, st, o,
                      (const To*)d_o, delta, ntok);
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t grid = (int64_t)B * H * nc;
   hipLaunchKernelGGL((k_sm_bwd_dq<T, D>), dim3((unsigned)grid), dim3(256), LDS_DQ, st, q, k, v, d_o, sel_idx,

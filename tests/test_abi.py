@@ -250,3 +250,24 @@ def test_binding_argtypes_match_prototypes(L):
         n = 0 if args.strip() == "void" else len([a for a in args.split(",") if a.strip()])
         at = getattr(L, name).argtypes
         assert (at is None and n == 0) or (at is not None and len(at) == n), (name, n, at)
+
+
+def test_gdn_length_limit_rejected_before_enqueue(L):
+    """bf16 D = 128 keeps one route byte per chunk in the scan's LDS: up to
+    15232 chunks (L = 974848) are accepted, one chunk more is UNSUPPORTED in
+    natsl_workspace_size, natsl_gdn_chunk and natsl_forward, before anything
+    is enqueued (the fake pointers are never touched); a 128k-token prefill
+    is accepted; fp32 io has no such limit."""
+    lim = 15232
+    for nch, io, ok in ((lim, N.BF16, True), (lim + 1, N.BF16, False), (2048, N.BF16, True), (lim + 1, N.F32, True)):
+        d = N.dims(1, 1, 64 * nch, 128, 256, io)
+        n = C.c_size_t(0)
+        for entry in (N.ENTRY_FORWARD, N.ENTRY_GDN_CHUNK):
+            got = L.natsl_workspace_size(entry, C.byref(d), C.byref(n))
+            assert got == (0 if ok else 2), (nch, io, entry, got)
+        if not ok:
+            assert b"15232" in L.natsl_last_error()
+            assert L.natsl_gdn_chunk(C.byref(d), *([FAKE] * 6), None, FAKE, 0, None, FAKE, 1 << 40, None) == 2
+            a = N.ForwardArgs()
+            a.q = a.k = a.v = a.alpha = a.beta = a.w_mix = a.out = a.route_override = FAKE
+            assert L.natsl_forward(C.byref(d), C.byref(a), FAKE, 1 << 40, None) == 2
