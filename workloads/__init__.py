@@ -179,6 +179,8 @@ def make_prefill(wl: Workload, seed=None, L=None, B=None, H=None, alpha_range=(0
     if routing == "iid":
         plan = np.where(rs[3].random(L // CHUNK) < sm_frac, 0, 1).astype(np.int32)
         x = plant(x, w_score, plan)
+    elif routing == "forced":
+        pass  # routes come from forced_routes() through route_override; x stays unplanted
     elif routing == "planted":
         e = wl.extra
         nc = L // CHUNK
@@ -186,6 +188,8 @@ def make_prefill(wl: Workload, seed=None, L=None, B=None, H=None, alpha_range=(0
         plan = plan_bursts(nc, int(e["n_sm"] * scale), e["n_burst"], int(e["burst_total"] * scale),
                            max(1, int(e["min_burst"] * scale)), rs[3])
         x = plant(np.ascontiguousarray(x), w_score, plan)
+    elif routing != "natural":
+        raise ValueError(f"unknown routing {routing!r}")
     q = q_scale * rs[4].standard_normal(size=(B, H, L, D), dtype=np.float32)
     k = _unit_rows(rs[5].standard_normal(size=(B, H, L, D), dtype=np.float32))
     v = rs[6].standard_normal(size=(B, H, L, D), dtype=np.float32)
