@@ -32,7 +32,8 @@
  *     enqueue, so concurrent forwards never share them, (b) a record of the
  *     kernels whose LDS limit has been raised, guarded by a mutex, and (c)
  *     the natsl_profile_* timing records, guarded by a mutex (timing several
- *     threads at once mixes their records).  Calls whose device buffers
+ *     threads at once mixes their records), and (d) the scratch array of
+ *     natsl_decode_step_noalloc (see there).  Calls whose device buffers
  *     overlap must be ordered by the caller (same stream, or events);
  *   - every call validates its arguments on the host BEFORE enqueueing any
  *     work; on failure nothing is enqueued, a status != NATSL_OK is
@@ -371,6 +372,29 @@ typedef struct {
 natsl_status natsl_decode_step(const natsl_dims* dims, const natsl_decode_cache* cache,
                                const natsl_decode_args* args, void* ws, size_t ws_bytes,
                                hipStream_t stream);
+
+/* Scratch the allocation-free decode step holds per device (bytes). */
+#define NATSL_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+/*
+ * Allocation-free decode step, for callers that cannot allocate device
+ * memory or hand over a workspace: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  The same step, arguments
+ * and errors as natsl_decode_step without ws / ws_bytes: the step's scratch
+ * (per-sequence chunk decisions, the Gated DeltaNet outputs, the split-KV
+ * partials) lives in a NATSL_DECODE_NOALLOC_SCRATCH_BYTES array that the
+ * library keeps in each device's memory until the process ends; the call
+ * itself allocates nothing.  Dims whose natsl_workspace_size(
+ * NATSL_ENTRY_DECODE_STEP) exceeds that size are NATSL_ERR_WORKSPACE, before
+ * anything is enqueued (e.g. B = 64, H = 16, D = 128 takes caches of up to
+ * about 28,000 rows).  Every call on one device uses that device's array and
+ * leaves its contents behind (each step writes every scratch value it later
+ * reads, so nothing needs clearing): two calls whose work can overlap on one
+ * device (different streams with no ordering between them) race on it and
+ * must be ordered by the caller.
+ */
+natsl_status natsl_decode_step_noalloc(const natsl_dims* dims, const natsl_decode_cache* cache,
+                                       const natsl_decode_args* args, hipStream_t stream);
 
 /*
  * Prefill -> decode handoff ("Technische Samenvatting: Neural Attention Search

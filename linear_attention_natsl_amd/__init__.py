@@ -25,8 +25,10 @@ STATUS = {0: "NATSL_OK", 1: "NATSL_ERR_INVALID_ARG", 2: "NATSL_ERR_UNSUPPORTED",
           3: "NATSL_ERR_WORKSPACE", 4: "NATSL_ERR_DEVICE", 5: "NATSL_ERR_CAPACITY"}
 EXPORTS = ["natsl_version", "natsl_last_error", "natsl_workspace_size", "natsl_route", "natsl_gdn_chunk",
            "natsl_softmax_masked", "natsl_merge", "natsl_forward", "natsl_decode_step",
-           "natsl_decode_handoff", "natsl_softmax_masked_backward", "natsl_gdn_backward", "natsl_merge_backward", "natsl_profile_enable", "natsl_profile_reset", "natsl_profile_read",
+           "natsl_decode_handoff", "natsl_softmax_masked_backward", "natsl_gdn_backward", "natsl_merge_backward",
+           "natsl_decode_step_noalloc", "natsl_profile_enable", "natsl_profile_reset", "natsl_profile_read",
            "natsl_profile_select"]
+DECODE_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 class NatslError(RuntimeError):
@@ -87,6 +89,7 @@ def lib():
         L.natsl_forward.argtypes = [C.POINTER(Dims), C.POINTER(ForwardArgs), vp, C.c_size_t, vp]
         L.natsl_decode_step.argtypes = [C.POINTER(Dims), C.POINTER(DecodeCache), C.POINTER(DecodeArgs), vp,
                                         C.c_size_t, vp]
+        L.natsl_decode_step_noalloc.argtypes = [C.POINTER(Dims), C.POINTER(DecodeCache), C.POINTER(DecodeArgs), vp]
         L.natsl_decode_handoff.argtypes = [C.POINTER(Dims), vp, vp, vp, vp, C.c_int, C.POINTER(DecodeCache), vp,
                                            C.c_size_t, vp]
         L.natsl_softmax_masked_backward.argtypes = [C.POINTER(Dims)] + [vp] * 12 + [C.c_size_t, vp]
@@ -97,7 +100,8 @@ def lib():
         L.natsl_profile_read.argtypes = [C.c_char_p, C.POINTER(C.c_int), C.POINTER(C.c_double)]
         L.natsl_profile_select.argtypes = [C.c_char_p]
         for name in ("natsl_workspace_size", "natsl_route", "natsl_gdn_chunk", "natsl_softmax_masked",
-                     "natsl_merge", "natsl_forward", "natsl_decode_step", "natsl_decode_handoff",
+                     "natsl_merge", "natsl_forward", "natsl_decode_step", "natsl_decode_step_noalloc",
+                     "natsl_decode_handoff",
                      "natsl_softmax_masked_backward", "natsl_gdn_backward", "natsl_merge_backward",
                      "natsl_profile_enable",
                      "natsl_profile_reset", "natsl_profile_read", "natsl_profile_select"):
@@ -311,9 +315,11 @@ class DecodeState:
 
 
 class Decode:
-    """Reusable decode step bound to a DecodeState (allocates only at init)."""
+    """Reusable decode step bound to a DecodeState (allocates only at init).
+    noalloc=True calls natsl_decode_step_noalloc: no workspace, the library's
+    per-device scratch array instead."""
 
-    def __init__(self, dm: Dims, state: DecodeState, device="cuda", debug=False):
+    def __init__(self, dm: Dims, state: DecodeState, device="cuda", debug=False, noalloc=False):
         self.dm = Dims.from_buffer_copy(dm)
         self.dm.L = state.cap
         exp = (dm.B, dm.H, state.cap, dm.Dk)
@@ -327,8 +333,9 @@ class Decode:
             raise TypeError("cache dtype must be the io dtype")
         self.state = state
         self.cstruct = state.struct()
-        self.ws_bytes = workspace_size(ENTRY_DECODE_STEP, self.dm)
-        self.ws = workspace(self.ws_bytes, device)
+        self.noalloc = noalloc
+        self.ws_bytes = 0 if noalloc else workspace_size(ENTRY_DECODE_STEP, self.dm)
+        self.ws = None if noalloc else workspace(self.ws_bytes, device)
         io_t = torch.bfloat16 if dm.io == BF16 else torch.float32
         self.out = torch.empty(dm.B, dm.H, dm.Dv, dtype=io_t, device=device)
         self.route = torch.empty(dm.B, dm.route_groups, dtype=torch.int32, device=device)
@@ -353,8 +360,12 @@ class Decode:
         a.g_sm, a.g_lin = _p(g_sm, torch.float32, "g_sm", (dm.Dv,)), _p(g_lin, torch.float32, "g_lin", (dm.Dv,))
         a.out, a.route_out = _p(self.out), _p(self.route)
         a.o_sm_dbg, a.o_gdn_dbg = _p(self.o_sm), _p(self.o_gdn)
-        _check(lib().natsl_decode_step(C.byref(self.dm), C.byref(self.cstruct), C.byref(a), _p(self.ws),
-                                       self.ws_bytes, _stream(stream)))
+        if self.noalloc:
+            _check(lib().natsl_decode_step_noalloc(C.byref(self.dm), C.byref(self.cstruct), C.byref(a),
+                                                   _stream(stream)))
+        else:
+            _check(lib().natsl_decode_step(C.byref(self.dm), C.byref(self.cstruct), C.byref(a), _p(self.ws),
+                                           self.ws_bytes, _stream(stream)))
         return self.out
 
 

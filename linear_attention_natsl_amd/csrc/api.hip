@@ -550,8 +550,12 @@ natsl_status natsl_forward(const natsl_dims* dims, const natsl_forward_args* a, 
   return ok();
 }
 
-natsl_status natsl_decode_step(const natsl_dims* dims, const natsl_decode_cache* c, const natsl_decode_args* a,
-                               void* ws, size_t ws_bytes, hipStream_t stream) {
+namespace {
+// Validation and launch of a decode step whose scratch is `ws` (ws_bytes
+// available; checked before anything is enqueued).  noalloc: ws is null and
+// the device's static scratch array is used instead.
+natsl_status decode_step_impl(const natsl_dims* dims, const natsl_decode_cache* c, const natsl_decode_args* a,
+                              void* ws, size_t ws_bytes, bool noalloc, hipStream_t stream) {
   CHECK(check_dims(dims, false, true));
   if (dims->B == 0) return ok();  // empty batch: nothing to do, pointers may be NULL
   NEED(c, "cache");
@@ -576,7 +580,16 @@ natsl_status natsl_decode_step(const natsl_dims* dims, const natsl_decode_cache*
   NEED(a->out, "out");
   if (a->w_mix_head_stride < 0) return fail(NATSL_ERR_INVALID_ARG, "negative w_mix head stride");
   const size_t need = decode_ws_bytes(dims->B, dims->H, dims->route_groups, dims->Dk, c->cap);
-  CHECK(check_ws(ws, ws_bytes, need));
+  if (noalloc) {
+    if (need > DECODE_SCRATCH_BYTES)
+      return fail(NATSL_ERR_WORKSPACE, "natsl_decode_step_noalloc: these dims need %zu bytes of scratch, above the "
+                  "%zu the allocation-free entry point holds per device (use natsl_decode_step with a workspace)",
+                  need, (size_t)DECODE_SCRATCH_BYTES);
+    const hipError_t e = decode_scratch_address(&ws);
+    if (e != hipSuccess) return dev_fail(e, "natsl_decode_step_noalloc: scratch address");
+  } else {
+    CHECK(check_ws(ws, ws_bytes, need));
+  }
   DecodeLaunch L;
   L.B = dims->B;
   L.H = dims->H;
@@ -615,8 +628,19 @@ natsl_status natsl_decode_step(const natsl_dims* dims, const natsl_decode_cache*
     e = dims->Dk == 64 ? launch_decode<bf16, 64>(L, ws, stream, prof) : launch_decode<bf16, 128>(L, ws, stream, prof);
   else
     e = dims->Dk == 64 ? launch_decode<float, 64>(L, ws, stream, prof) : launch_decode<float, 128>(L, ws, stream, prof);
-  if (e != hipSuccess) return dev_fail(e, "natsl_decode_step");
+  if (e != hipSuccess) return dev_fail(e, noalloc ? "natsl_decode_step_noalloc" : "natsl_decode_step");
   return ok();
+}
+}  // namespace
+
+natsl_status natsl_decode_step(const natsl_dims* dims, const natsl_decode_cache* c, const natsl_decode_args* a,
+                               void* ws, size_t ws_bytes, hipStream_t stream) {
+  return decode_step_impl(dims, c, a, ws, ws_bytes, false, stream);
+}
+
+natsl_status natsl_decode_step_noalloc(const natsl_dims* dims, const natsl_decode_cache* c,
+                                       const natsl_decode_args* a, hipStream_t stream) {
+  return decode_step_impl(dims, c, a, nullptr, 0, true, stream);
 }
 
 natsl_status natsl_softmax_masked_backward(const natsl_dims* dims, const void* q, const void* k, const void* v,

@@ -18,10 +18,18 @@
 //   k_decode_combine  merge the partials and the new token, RMSNorm both
 //                     branches, Q-derived weights, append the new k/v row
 //   k_decode_commit   advance the counters
+#include <mutex>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace natsl {
+
+// Scratch of the allocation-free decode step: one array per device, in the
+// code object's device memory, which every such call on that device uses.
+// (Its name is a host-side stand-in in host code; kernels get the device
+// address that hipGetSymbolAddress returns, kept per device below.)
+static __device__ __align__(256) unsigned char scratch[DECODE_SCRATCH_BYTES];
 
 template <typename T>
 __global__ void __launch_bounds__(256) k_decode_route(const T* __restrict__ x, const float* __restrict__ w,
@@ -323,6 +331,26 @@ __global__ void k_decode_commit(int B, int G, int32_t* __restrict__ n_committed,
     no = 0;
   }
   n_open[b] = no;
+}
+
+hipError_t decode_scratch_address(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* ptrs[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // with device `dev` current
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    ptrs[dev] = p;
+  }
+  *out = ptrs[dev];
+  return hipSuccess;
 }
 
 size_t decode_ws_bytes(int B, int H, int G, int D, int cap) {

@@ -271,3 +271,19 @@ def test_gdn_length_limit_rejected_before_enqueue(L):
             a = N.ForwardArgs()
             a.q = a.k = a.v = a.alpha = a.beta = a.w_mix = a.out = a.route_override = FAKE
             assert L.natsl_forward(C.byref(d), C.byref(a), FAKE, 1 << 40, None) == 2
+
+
+def test_decode_noalloc_rejects_oversized_before_enqueue(L):
+    """The allocation-free decode step holds 16 MiB of scratch per device: dims
+    that need more are NATSL_ERR_WORKSPACE before anything is enqueued (the
+    fake pointers are never touched)."""
+    assert N.DECODE_NOALLOC_SCRATCH_BYTES == 16 << 20
+    d = N.dims(64, 16, 40000, 128, 256, N.BF16)
+    assert N.workspace_size(N.ENTRY_DECODE_STEP, d) > N.DECODE_NOALLOC_SCRATCH_BYTES
+    c = N.DecodeCache(FAKE, FAKE, 40000, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    a = N.DecodeArgs()
+    a.x = a.q = a.k = a.v = a.alpha = a.beta = a.w_score = a.w_mix = a.out = FAKE
+    d.L = 1
+    assert L.natsl_decode_step_noalloc(C.byref(d), C.byref(c), C.byref(a), None) == 3
+    assert b"16777216" in L.natsl_last_error()
+    assert L.natsl_decode_step_noalloc(C.byref(d), None, C.byref(a), None) == 1
