@@ -136,6 +136,28 @@ def time_softmax_alone(N, dm, route, t, io_t, reps):
     return 1000.0 * e0.elapsed_time(e1) / reps
 
 
+def time_route_alone(N, dm, t, wl, reps=50):
+    """The router + compaction on the prefill's x with the GPU to itself: one
+    pass over x (B L d_model values) per launch, set against the HBM peak."""
+    import torch
+    call = lambda: N.route(dm, t["x"], t["w_score"], t["b_score"])
+    settle(call, 0.1)
+    N.profile_enable(True)
+    N.profile_select(None)
+    N.profile_reset()
+    for _ in range(reps):
+        call()
+    torch.cuda.synchronize()
+    n, ms = N.profile_read("route")
+    nc, mc = N.profile_read("compact")
+    N.profile_enable(False)
+    us = 1000.0 * ms / max(n, 1)
+    nbytes = wl.B * wl.L * wl.d * t["x"].element_size()
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return dict(avg_us=round(us, 2), compact_avg_us=round(1000.0 * mc / max(nc, 1), 2), bytes=nbytes,
+                gbs=round(gbs, 1), frac_hbm=round(gbs / PEAK_HBM_GBS, 4))
+
+
 def time_handoff(N, dm, route, t, wl, reps=20):
     """The prefill -> decode handoff of this prefill (its routes, K and V) into
     a decode cache sized for its softmax rows: bytes moved = the softmax
@@ -353,6 +375,7 @@ def time_prefill(args, N, W, O):
     r = run_prefill_case(args, N, W, wl, inp, t, dm, flusher=flusher)
     fwd = r["fwd"]
     sm_alone_us = None if args.no_alone else time_softmax_alone(N, dm, fwd.route, t, io_t, max(10, args.steps // 2))
+    route_alone = None if args.no_alone else time_route_alone(N, dm, t, wl)
     extras = {}
     if not args.no_extras:
         extras = dict(handoff=time_handoff(N, dm, fwd.route, t, wl),
@@ -388,7 +411,7 @@ def time_prefill(args, N, W, O):
                    layer_tflops=round((f_sm + f_gdn) / step_s / 1e12, 1),
                    layer_frac_of_mfma_peak=round((f_sm + f_gdn) / step_s / 1e12 / PEAK_BF16_TFLOPS, 4),
                    step_stats=dict(flushed=r["per_step"], back_to_back=r["warm_steps"]),
-                   kernels=r["kernels"]),
+                   kernels=r["kernels"], route_alone=route_alone),
         **extras,
     )
     return res, inp, route

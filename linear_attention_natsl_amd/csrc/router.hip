@@ -61,6 +61,72 @@ __global__ void __launch_bounds__(256) k_route(const T* __restrict__ x, const fl
   }
 }
 
+// Fast path for d_model = 8 * 2^k <= 8192: 1024 threads per chunk.  The d/8
+// column groups of 8 contiguous values (16-byte loads) times RS = 8192 / d
+// row slices cover the chunk's 64 x d values once; each thread issues all of
+// its 64 / RS loads before adding any, so the whole chunk is in flight at
+// once.  The RS partial sums of a column are then added in slice order
+// through LDS (fixed order: deterministic).
+template <typename T>
+__global__ void __launch_bounds__(1024, 2) k_route_wide(const T* __restrict__ x, const float* __restrict__ w,
+                                                     const float* __restrict__ bsc, int L, int d, int G, int nc,
+                                                     int32_t* __restrict__ route_out, float* __restrict__ scores) {
+  extern __shared__ float s_part[];  // [RS][d] partial sums, then the mean [d] and 2G scores
+  const int c = bid_x(), b = bid_y();
+  const int tid = tid_x();
+  const int ncg = d >> 3;          // column groups
+  const int rs = 1024 / ncg;       // row slices (1 .. 64 ... capped below)
+  const int rows = CHUNK / rs;     // rows per thread
+  const int cg = tid % ncg, sl = tid / ncg;
+  const T* xc = x + ((int64_t)b * L + (int64_t)c * CHUNK + (int64_t)sl * rows) * d + cg * 8;
+  float acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+  {
+    // batches of 8 independent 16-byte loads (two workgroups per CU keep
+    // 16 per column group in flight)
+    for (int r = 0; r < rows; r += 8) {
+      Frag<T> v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = load8<T>(xc + (int64_t)min(r + u, rows - 1) * d);
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (r + u < rows)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc[j] += to_f32(frag_get<T>(v[u], j));
+    }
+  }
+  float* mine = s_part + sl * d + cg * 8;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) mine[j] = acc[j];
+  __syncthreads();
+  float* s_mean = s_part + rs * d;
+  for (int col = tid; col < d; col += 1024) {
+    float t = 0.f;
+    for (int k = 0; k < rs; ++k) t += s_part[k * d + col];
+    s_mean[col] = t * (1.0f / CHUNK);
+  }
+  __syncthreads();
+  const int lane = lane_id(), wv = wave_id();
+  for (int o = wv; o < 2 * G; o += 16) {
+    float p = 0.f;
+    for (int j = lane; j < d; j += 64) p += s_mean[j] * w[(int64_t)j * 2 * G + o];
+    p = wave_sum64(p);
+    if (bsc) p += bsc[o];
+    if (lane == 0) s_mean[d + o] = p;
+  }
+  __syncthreads();
+  for (int gg = tid; gg < G; gg += 1024) {
+    const float s0 = s_mean[d + 2 * gg], s1 = s_mean[d + 2 * gg + 1];
+    const int64_t idx = ((int64_t)b * G + gg) * nc + c;
+    route_out[idx] = (s0 >= s1) ? 0 : 1;
+    if (scores) {
+      scores[idx * 2] = s0;
+      scores[idx * 2 + 1] = s1;
+    }
+  }
+}
+
 // One wave per (b, g): ordered list of softmax chunks and exclusive prefix counts.
 __global__ void __launch_bounds__(64) k_compact(const int32_t* __restrict__ route_in,
                                                 int32_t* __restrict__ route_out, int nc,
@@ -94,6 +160,19 @@ template <typename T>
 hipError_t launch_route(const T* x, const float* w, const float* bsc, int B, int L, int d, int G,
                         int32_t* route_out, float* scores, hipStream_t st) {
   const int nc = L / CHUNK;
+  // wide path: d = 8 * 2^k with 64 <= d <= 8192 (1 to 16 row slices of 64 / rs rows)
+  const bool pow2 = (d & (d - 1)) == 0;
+  if (pow2 && d >= 512 && d <= 8192) {
+    const int rs = 8192 / d;
+    const size_t lds = (size_t)(rs * d + d + 2 * G) * sizeof(float);
+    if (lds <= (size_t)LDS_MAX_BYTES) {
+      const hipError_t e = set_lds_limit((const void*)k_route_wide<T>, (int)lds);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(k_route_wide<T>, dim3(nc, B), dim3(1024), lds, st, x, w, bsc, L, d, G, nc, route_out,
+                         scores);
+      return hipGetLastError();
+    }
+  }
   const size_t lds = (size_t)(d + 2 * G) * sizeof(float);
   hipLaunchKernelGGL(k_route<T>, dim3(nc, B), dim3(256), lds, st, x, w, bsc, L, d, G, nc, route_out,
                      scores);
