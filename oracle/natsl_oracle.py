@@ -586,3 +586,100 @@ def decode_step(cache, x, q, k, v, alpha, beta, w_score, w_mix, b_score=None, g_
                 c["x_sum"][b, g] = 0.0
     return out[:, :, 0], dict(o_sm=o_sm, o_gdn=o_gdn, n_sm=n_sm[:, :, 0], n_lin=n_lin[:, :, 0],
                               weights=w[:, :, 0], routes=routes), c
+
+
+# ---------------------------------------------------------------------------
+# Native Hybrid Attention: one softmax over compressed slots + a sliding
+# window ("Native Hybrid Attention for Efficient Sequence Modeling", section 2
+# Methodologie, "Unificatie van Intra-layer Hybridisatie")
+# ---------------------------------------------------------------------------
+def nha_attention(q, k, v, slot_gate, window, scale=None):
+    """Plain per-token definition.
+
+    The page describes it this way: long-term information is compressed into
+    a fixed number of key-value slots by a linear RNN update (after Gated Slot
+    Attention); the slots are joined with the short-term tokens of a sliding
+    window into ONE key-value set, and one softmax attention runs over that
+    set.  A window of 0 leaves a pure linear RNN, a window of the whole
+    sequence a full Transformer.
+
+    Readings (the page gives no equations):
+      * window w (tokens): query t sees the keys of tokens t-w+1 .. t itself;
+      * token s enters the slots when it leaves the window, i.e. before query
+        s + w is answered (w = 0: every token enters before its own query);
+      * slot update, per slot i with the gate a_s[i] in (0, 1) of the
+        entering token (the Gated Slot Attention form: forget, then write the
+        complement):  K~[i] <- a_s[i] K~[i] + (1 - a_s[i]) k_s, the same for V~;
+        slots start at zero;
+      * the slots join the key set only once a token has entered them, so
+        w >= L is exactly causal softmax attention.
+    q, k, v [B,H,L,D]; slot_gate [B,H,L,m]; returns o [B,H,L,D]."""
+    q, k, v, a = map(_f64, (q, k, v, slot_gate))
+    B, H, L, D = q.shape
+    m = a.shape[3]
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    o = np.zeros_like(v)
+    for b in range(B):
+        for h in range(H):
+            Ks = np.zeros((m, D))
+            Vs = np.zeros((m, D))
+            entered = 0
+            for t in range(L):
+                s = t - window  # the token that leaves the window before query t
+                if s >= 0:
+                    g = a[b, h, s][:, None]
+                    Ks = g * Ks + (1.0 - g) * k[b, h, s][None, :]
+                    Vs = g * Vs + (1.0 - g) * v[b, h, s][None, :]
+                    entered += 1
+                lo = max(0, t - window + 1)
+                keys = [k[b, h, lo:t + 1]]
+                vals = [v[b, h, lo:t + 1]]
+                if entered:
+                    keys.insert(0, Ks)
+                    vals.insert(0, Vs)
+                kk = np.concatenate(keys, axis=0)
+                vv = np.concatenate(vals, axis=0)
+                if kk.shape[0] == 0:
+                    continue
+                z = scale * (kk @ q[b, h, t])
+                p = np.exp(z - z.max())
+                o[b, h, t] = (p @ vv) / p.sum()
+    return o
+
+
+def nha_attention_bruteforce(q, k, v, slot_gate, window, scale=None):
+    """Brute-force twin: every query builds its slots from scratch as the
+    closed-form sum over the tokens that have entered them,
+        K~_t[i] = sum_{s <= t-w} (prod_{s < r <= t-w} a_r[i]) (1 - a_s[i]) k_s,
+    then takes one softmax over [slots; window keys].  Tiny inputs only."""
+    q, k, v, a = map(_f64, (q, k, v, slot_gate))
+    B, H, L, D = q.shape
+    m = a.shape[3]
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    o = np.zeros_like(v)
+    for b in range(B):
+        for h in range(H):
+            for t in range(L):
+                last = t - window
+                keys, vals = [], []
+                if last >= 0:
+                    Ks = np.zeros((m, D))
+                    Vs = np.zeros((m, D))
+                    for s in range(last + 1):
+                        wgt = (1.0 - a[b, h, s]) * np.prod(a[b, h, s + 1:last + 1], axis=0)
+                        Ks += wgt[:, None] * k[b, h, s][None, :]
+                        Vs += wgt[:, None] * v[b, h, s][None, :]
+                    keys += list(Ks)
+                    vals += list(Vs)
+                for s in range(max(0, t - window + 1), t + 1):
+                    keys.append(k[b, h, s])
+                    vals.append(v[b, h, s])
+                if not keys:
+                    continue
+                z = np.array([scale * float(q[b, h, t] @ kk) for kk in keys])
+                p = np.exp(z - z.max())
+                p /= p.sum()
+                o[b, h, t] = sum(pi * vv for pi, vv in zip(p, vals))
+    return o
