@@ -433,6 +433,38 @@ natsl_status natsl_decode_handoff(const natsl_dims* dims, const int32_t* route, 
                                   size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Native Hybrid Attention ("Native Hybrid Attention for Efficient Sequence
+ * Modeling", section 2 Methodologie, "Unificatie van Intra-layer
+ * Hybridisatie"): long-term information is compressed into `slots` key-value
+ * slots by a linear RNN update, the slots are joined with the tokens of a
+ * sliding window into one key-value set, and one softmax attention runs over
+ * that set (window 0: the slots alone, a linear RNN; a window covering the
+ * sequence: causal softmax attention).  The page gives no equations; this
+ * library's reading:
+ *   - query t sees the keys and values of tokens t-window+1 .. t;
+ *   - token s enters the slots when it leaves the window (before query
+ *     s + window), per slot i with its gate a_s[i] in [0, 1]:
+ *       K~[i] <- a_s[i] K~[i] + (1 - a_s[i]) k_s,  V~[i] likewise;
+ *     slots start at zero and join the key set once a token has entered;
+ *   - scores scale * q_t . key (scale: dims->sm_scale, <= 0 = 1/sqrt(Dk)).
+ *   dims        B, H, L, Dk = Dv in {64, 128}, io (L % 64 == 0; route_groups,
+ *               d_model unused)
+ *   q, k, v     [B, H, L, D] io dtype
+ *   slot_gate   [B, H, L, slots] fp32, the gate of each token for each slot
+ *   slots       16, 32 or 64
+ *   window      tokens, a multiple of 64 (>= L: plain causal attention)
+ *   out         [B, H, L, D] io dtype
+ *   ws          natsl_nha_workspace_size bytes (the slots' states at every
+ *               chunk start and the window's partial result, fp32)
+ * Errors: NATSL_ERR_UNSUPPORTED (slots, window or dims), NATSL_ERR_INVALID_ARG,
+ * NATSL_ERR_WORKSPACE, before anything is enqueued; NATSL_ERR_DEVICE.
+ */
+natsl_status natsl_nha_workspace_size(const natsl_dims* dims, int slots, int window, size_t* bytes);
+natsl_status natsl_nha_attention(const natsl_dims* dims, const void* q, const void* k, const void* v,
+                                 const float* slot_gate, int slots, int window, void* out, void* ws,
+                                 size_t ws_bytes, hipStream_t stream);
+
+/*
  * Kernel timing for measurement: when enabled, every kernel the library
  * launches is bracketed by HIP events on the stream it runs on.
  * natsl_profile_read synchronises those events and returns, for the kernel
@@ -440,7 +472,8 @@ natsl_status natsl_decode_handoff(const natsl_dims* dims, const int32_t* route, 
  * in milliseconds since the last reset.  Names: "route", "compact",
  * "gdn_prep", "gdn_scan", "softmax_masked", "merge", "decode_route",
  * "decode_gdn", "decode_attn", "decode_combine", "decode_commit",
- * "softmax_backward", "decode_handoff" (each a whole call of that entry).
+ * "softmax_backward", "decode_handoff", "gdn_backward", "merge_backward",
+ * "nha" (each a whole call of that entry).
  * natsl_profile_select restricts the recording to the kernel named `name`
  * (NULL or "" records every kernel again), so that timing one kernel adds
  * only its own two event records to a step; an unknown name is

@@ -26,7 +26,7 @@ STATUS = {0: "NATSL_OK", 1: "NATSL_ERR_INVALID_ARG", 2: "NATSL_ERR_UNSUPPORTED",
 EXPORTS = ["natsl_version", "natsl_last_error", "natsl_workspace_size", "natsl_route", "natsl_gdn_chunk",
            "natsl_softmax_masked", "natsl_merge", "natsl_forward", "natsl_decode_step",
            "natsl_decode_handoff", "natsl_softmax_masked_backward", "natsl_gdn_backward", "natsl_merge_backward",
-           "natsl_decode_step_noalloc", "natsl_profile_enable", "natsl_profile_reset", "natsl_profile_read",
+           "natsl_decode_step_noalloc", "natsl_nha_workspace_size", "natsl_nha_attention", "natsl_profile_enable", "natsl_profile_reset", "natsl_profile_read",
            "natsl_profile_select"]
 DECODE_NOALLOC_SCRATCH_BYTES = 16 << 20
 
@@ -90,6 +90,8 @@ def lib():
         L.natsl_decode_step.argtypes = [C.POINTER(Dims), C.POINTER(DecodeCache), C.POINTER(DecodeArgs), vp,
                                         C.c_size_t, vp]
         L.natsl_decode_step_noalloc.argtypes = [C.POINTER(Dims), C.POINTER(DecodeCache), C.POINTER(DecodeArgs), vp]
+        L.natsl_nha_workspace_size.argtypes = [C.POINTER(Dims), C.c_int, C.c_int, C.POINTER(C.c_size_t)]
+        L.natsl_nha_attention.argtypes = [C.POINTER(Dims), vp, vp, vp, vp, C.c_int, C.c_int, vp, vp, C.c_size_t, vp]
         L.natsl_decode_handoff.argtypes = [C.POINTER(Dims), vp, vp, vp, vp, C.c_int, C.POINTER(DecodeCache), vp,
                                            C.c_size_t, vp]
         L.natsl_softmax_masked_backward.argtypes = [C.POINTER(Dims)] + [vp] * 12 + [C.c_size_t, vp]
@@ -101,6 +103,7 @@ def lib():
         L.natsl_profile_select.argtypes = [C.c_char_p]
         for name in ("natsl_workspace_size", "natsl_route", "natsl_gdn_chunk", "natsl_softmax_masked",
                      "natsl_merge", "natsl_forward", "natsl_decode_step", "natsl_decode_step_noalloc",
+                     "natsl_nha_workspace_size", "natsl_nha_attention",
                      "natsl_decode_handoff",
                      "natsl_softmax_masked_backward", "natsl_gdn_backward", "natsl_merge_backward",
                      "natsl_profile_enable",
@@ -228,6 +231,31 @@ def merge(dm: Dims, q, o_sm, o_gdn, w_mix, w_mix_head_stride=0, g_sm=None, g_lin
                              _p(g_sm, torch.float32, "g_sm", (dm.Dv,)), _p(g_lin, torch.float32, "g_lin", (dm.Dv,)),
                              _p(out),
                              _stream(stream)))
+    return out
+
+
+def nha_workspace_size(dm: Dims, slots, window):
+    n = C.c_size_t(0)
+    _check(lib().natsl_nha_workspace_size(C.byref(dm), slots, window, C.byref(n)))
+    return n.value
+
+
+def nha_attention(dm: Dims, q, k, v, slot_gate, window, ws=None, stream=None):
+    """Native Hybrid Attention: one softmax over gated key-value slots and a
+    sliding window of `window` tokens (a multiple of 64).  slot_gate is
+    [B, H, L, slots] fp32 with slots in {16, 32, 64}.  Returns out in the io
+    dtype."""
+    io, qs = _io_t(dm), (dm.B, dm.H, dm.L, dm.Dk)
+    slots = slot_gate.shape[-1] if slot_gate.dim() == 4 else -1
+    nbytes = nha_workspace_size(dm, slots, window)
+    if ws is None:
+        ws = workspace(nbytes, q.device)
+    elif ws.numel() * ws.element_size() < nbytes:
+        raise ValueError("workspace too small")
+    out = torch.empty(qs, dtype=io, device=q.device)
+    _check(lib().natsl_nha_attention(C.byref(dm), _p(q, io, "q", qs), _p(k, io, "k", qs), _p(v, io, "v", qs),
+                                     _p(slot_gate, torch.float32, "slot_gate", (dm.B, dm.H, dm.L, slots)), slots,
+                                     window, _p(out), _p(ws), nbytes, _stream(stream)))
     return out
 
 

@@ -66,7 +66,7 @@ size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 const char* kKernelNames[KID_COUNT] = {"route",        "compact",       "gdn_prep",   "gdn_scan",
                                        "softmax_masked", "merge",       "decode_route", "decode_gdn",
                                        "decode_attn",  "decode_combine", "decode_commit", "softmax_backward", "decode_handoff",
-                                       "gdn_backward", "merge_backward"};
+                                       "gdn_backward", "merge_backward", "nha"};
 struct ProfRec {
   int kid;
   hipEvent_t a, b;
@@ -817,6 +817,49 @@ natsl_status natsl_decode_handoff(const natsl_dims* dims, const int32_t* route, 
   const hipError_t e = dims->io == NATSL_BF16 ? launch_handoff<bf16>(L, ws, stream) : launch_handoff<float>(L, ws, stream);
   if (prof) prof(KID_HANDOFF, stream, 1);
   if (e != hipSuccess) return dev_fail(e, "natsl_decode_handoff");
+  return ok();
+}
+
+natsl_status natsl_nha_workspace_size(const natsl_dims* dims, int slots, int window, size_t* bytes) {
+  if (!bytes) return fail(NATSL_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = 0;
+  CHECK(check_dims(dims, true, false));
+  if (slots != 16 && slots != 32 && slots != 64) return fail(NATSL_ERR_UNSUPPORTED, "slots %d not in {16, 32, 64}", slots);
+  if (window < 0 || window % 64 != 0)
+    return fail(NATSL_ERR_UNSUPPORTED, "window %d must be a non-negative multiple of 64", window);
+  *bytes = nha_ws_bytes(dims->B, dims->H, dims->L, dims->Dk, slots, window);
+  return ok();
+}
+
+natsl_status natsl_nha_attention(const natsl_dims* dims, const void* q, const void* k, const void* v,
+                                 const float* slot_gate, int slots, int window, void* out, void* ws, size_t ws_bytes,
+                                 hipStream_t stream) {
+  size_t need = 0;
+  CHECK(natsl_nha_workspace_size(dims, slots, window, &need));
+  if (dims->B == 0) return ok();  // empty batch: nothing to do, pointers may be NULL
+  NEED(q, "q");
+  NEED(k, "k");
+  NEED(v, "v");
+  NEED(slot_gate, "slot_gate");
+  NEED(out, "out");
+  CHECK(check_ws(ws, ws_bytes, need));
+  const float sc = eff_scale(dims);
+  const int B = dims->B, H = dims->H, L = dims->L;
+  hipError_t e;
+  auto prof = prof_fn();
+  if (prof) prof(KID_NHA, stream, 0);
+  if (dims->io == NATSL_BF16)
+    e = dims->Dk == 64 ? launch_nha<bf16, bf16, 64>((const bf16*)q, (const bf16*)k, (const bf16*)v, slot_gate, slots,
+                                                    (bf16*)out, ws, B, H, L, window, sc, stream)
+                       : launch_nha<bf16, bf16, 128>((const bf16*)q, (const bf16*)k, (const bf16*)v, slot_gate,
+                                                     slots, (bf16*)out, ws, B, H, L, window, sc, stream);
+  else
+    e = dims->Dk == 64 ? launch_nha<float, float, 64>((const float*)q, (const float*)k, (const float*)v, slot_gate,
+                                                      slots, (float*)out, ws, B, H, L, window, sc, stream)
+                       : launch_nha<float, float, 128>((const float*)q, (const float*)k, (const float*)v, slot_gate,
+                                                       slots, (float*)out, ws, B, H, L, window, sc, stream);
+  if (prof) prof(KID_NHA, stream, 1);
+  if (e != hipSuccess) return dev_fail(e, "natsl_nha_attention");
   return ok();
 }
 

@@ -25,6 +25,7 @@ enum {
   KID_HANDOFF,
   KID_GDN_BWD,
   KID_MERGE_BWD,
+  KID_NHA,
   KID_COUNT
 };
 
@@ -90,6 +91,23 @@ hipError_t launch_softmax_masked(const T* q, const T* k, const T* v, const int32
                                  const int32_t* nsel_before, To* o_sm, float* lse, int B, int H,
                                  int L, int G, float scale, hipStream_t st, const SmPrefix& pre = SmPrefix(),
                                  const SmMix& mix = SmMix());
+
+// sliding-window causal softmax (the generic kernel's window mode): a query
+// sees the win_chunks * 64 most recent tokens including itself; lse nullable
+template <typename T, typename To, int D>
+hipError_t launch_softmax_window(const T* q, const T* k, const T* v, To* o, float* lse, int B, int H, int L,
+                                 int win_chunks, float scale, hipStream_t st);
+
+// Native Hybrid Attention (slots + sliding window, one softmax)
+struct NhaWs {
+  float* Sk;  // [B, H, ne, M, D] per chunk e: its slot-key change, then the slot keys before it
+  float* Sv;  // [B, H, ne, M, D] the same for the slot values
+  float* G;   // [B, H, ne, M]    the chunk's decay of every slot
+};
+size_t nha_ws_bytes(int B, int H, int L, int D, int M, int window);
+template <typename T, typename To, int D>
+hipError_t launch_nha(const T* q, const T* k, const T* v, const float* gate, int M, To* out, void* ws, int B, int H,
+                      int L, int window, float scale, hipStream_t st);
 
 size_t gdn_ws_bytes(int io_is_bf16, int D, int64_t nch);
 // Gated DeltaNet branch gradient (per-token reverse sweep): ws holds the

@@ -147,7 +147,7 @@ __device__ __forceinline__ void tile_sstore(const TileRegs<T, D>& r, T* buf) {
   }
 }
 
-enum { MODE_SKIP = 0, MODE_FULL = 1, MODE_DIAG = 2 };
+enum { MODE_SKIP = 0, MODE_FULL = 1, MODE_DIAG = 2, MODE_WSTART = 3 };
 constexpr float RESCALE_TH = 8.0f;  // log2 units
 
 template <typename T, typename To, int D>
@@ -156,7 +156,11 @@ __global__ void __launch_bounds__(256, 2)
                      const int32_t* __restrict__ sel_idx, const int32_t* __restrict__ nsel_before,
                      To* __restrict__ o_sm, float* __restrict__ lse, int H, int L, int G,
                      float scale_log2, const T* __restrict__ pre_k, const T* __restrict__ pre_v,
-                     const int32_t* __restrict__ pnc, int pcap) {
+                     const int32_t* __restrict__ pnc, int pcap, int win) {
+  // win > 0: sliding-window mode instead of the routed key set: a query of
+  // chunk c at offset j sees chunk c - win from offset j + 1 on, the chunks
+  // in between in full and chunk c up to offset j (the win * 64 most recent
+  // tokens including itself); sel_idx, nsel_before and the prefix are unused
   using C = SmCfg<T, D>;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   T* smem = reinterpret_cast<T*>(smem_raw);
@@ -176,18 +180,23 @@ __global__ void __launch_bounds__(256, 2)
   }
   const int b = bh / H, h = bh % H;
   const int grp = (G == 1) ? 0 : h;
-  const int32_t* sel = sel_idx + ((int64_t)b * G + grp) * nc;
-  const int32_t* nsbp = nsel_before + ((int64_t)b * G + grp) * (nc + 1);
   const int c0 = 2 * qblk, c1 = c0 + 1;
   const bool has_c1 = c1 < nc;
+  const int32_t* sel = win > 0 ? nullptr : sel_idx + ((int64_t)b * G + grp) * nc;
+  const int32_t* nsbp = win > 0 ? nullptr : nsel_before + ((int64_t)b * G + grp) * (nc + 1);
   // key tiles: the prefix cache's rows (npre tiles), the softmax chunks
   // before c0, c0, c1
-  // (rows of a cache that overflowed were never written: at most cap rows)
-  const int npre = pnc ? min(pnc[(int64_t)b * G + grp], pcap) / CHUNK : 0;
-  const int nsel = nsbp[c0];
+  // (rows of a cache that overflowed were never written: at most cap rows);
+  // window mode: chunks c1 (or c0) down to wlo, newest first, so that every
+  // query meets its own (diagonal) chunk before the chunk where its window
+  // starts, which may hide all of its keys from it
+  const int wlo = max(0, c0 - win);
+  const int whi = has_c1 ? c1 : c0;
+  const int npre = (win == 0 && pnc) ? min(pnc[(int64_t)b * G + grp], pcap) / CHUNK : 0;
+  const int nsel = win > 0 ? 0 : nsbp[c0];
   const int nsb = npre + nsel;
-  const bool c0_sm = nsbp[c0 + 1] > nsel;
-  const int ntiles = nsb + 1 + (has_c1 ? 1 : 0);
+  const bool c0_sm = win > 0 ? false : nsbp[c0 + 1] > nsel;
+  const int ntiles = win > 0 ? whi - wlo + 1 : nsb + 1 + (has_c1 ? 1 : 0);
 
   const int lane = lane_id(), w = wave_id();
   const int g = lane >> 4, c = lane & 15;
@@ -219,7 +228,10 @@ __global__ void __launch_bounds__(256, 2)
 
   const int64_t pre_off = (int64_t)bh * pcap * D;
   auto tile_load = [&](TileRegs<T, D>& r, int it) {
-    if (it < npre) {
+    if (win > 0) {
+      const int kc = whi - it;
+      tile_gload<T, D>(r, kh + (int64_t)kc * CHUNK * D, vh + (int64_t)kc * CHUNK * D);
+    } else if (it < npre) {
       tile_gload<T, D>(r, pre_k + pre_off + (int64_t)it * CHUNK * D, pre_v + pre_off + (int64_t)it * CHUNK * D);
     } else {
       const int j = it - npre;
@@ -238,7 +250,11 @@ __global__ void __launch_bounds__(256, 2)
     const bool more = it + 1 < ntiles;
     if (more) tile_load(pre, it + 1);
     int mode;
-    if (it < nsb) mode = MODE_FULL;
+    if (win > 0) {
+      const int kc = whi - it, cw = my_c1 ? c1 : c0;
+      mode = (kc > cw || kc < cw - win) ? MODE_SKIP : (kc == cw) ? MODE_DIAG : (kc == cw - win) ? MODE_WSTART
+                                                                                                   : MODE_FULL;
+    } else if (it < nsb) mode = MODE_FULL;
     else if (it == nsb) mode = my_c1 ? (c0_sm ? MODE_FULL : MODE_SKIP) : MODE_DIAG;
     else mode = my_c1 ? MODE_DIAG : MODE_SKIP;
     if (!active) mode = MODE_SKIP;
@@ -275,6 +291,12 @@ __global__ void __launch_bounds__(256, 2)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
               if ((16 * kt + 4 * g + i) > qrow) s[kt][qs][i] = -INFINITY;
+        } else if (mode == MODE_WSTART) {  // keys already past the window's start
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if ((16 * kt + 4 * g + i) <= qrow) s[kt][qs][i] = -INFINITY;
         }
         float mt = fmaxf(fmaxf(s[0][qs][0], s[0][qs][1]), fmaxf(s[0][qs][2], s[0][qs][3]));
 #pragma unroll
@@ -285,13 +307,17 @@ __global__ void __launch_bounds__(256, 2)
         mt *= scale_log2;  // scale > 0: max commutes with scaling
         if (__ballot(mt > m_run[qs] + RESCALE_TH) != 0) {
           const float m_new = fmaxf(m_run[qs], mt);
-          const float alpha = __builtin_amdgcn_exp2f(m_run[qs] - m_new);  // 0 on the first tile
+          // 0 on a row's first visible tile; a row that has still seen no
+          // visible key (m stays -inf) keeps its zeros
+          const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[qs] - m_new);
           m_run[qs] = m_new;
           l_run[qs] *= alpha;
 #pragma unroll
           for (int dt = 0; dt < D / 16; ++dt) o[dt][qs] *= alpha;
         }
-        const float nm = -m_run[qs];
+        // (a row that has seen no visible key yet keeps m = -inf: its
+        // weights are 0, not 2^(-inf + inf))
+        const float nm = m_run[qs] == -INFINITY ? 0.f : -m_run[qs];
         float ls = 0.f;
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
@@ -668,9 +694,36 @@ hipError_t launch_softmax_masked(const T* q, const T* k, const T* v, const int32
   const int64_t grid = (int64_t)B * H * nb;
   hipLaunchKernelGGL((k_softmax_masked<T, To, D>), dim3((unsigned)grid), dim3(256), C::LDS_BYTES,
                      st, q, k, v, sel_idx, nsel_before, o_sm, lse, H, L, G, scale * LOG2E, (const T*)pre.k,
-                     (const T*)pre.v, pre.n_committed, pre.cap);
+                     (const T*)pre.v, pre.n_committed, pre.cap, 0);
   return hipGetLastError();
 }
+
+template <typename T, typename To, int D>
+hipError_t launch_softmax_window(const T* q, const T* k, const T* v, To* o, float* lse, int B, int H, int L,
+                                 int win_chunks, float scale, hipStream_t st) {
+  using C = SmCfg<T, D>;
+  if (win_chunks < 1) return hipErrorInvalidValue;
+  const hipError_t ea = set_lds_limit((const void*)k_softmax_masked<T, To, D>, C::LDS_BYTES);
+  if (ea != hipSuccess) return ea;
+  const int nc = L / CHUNK;
+  const int64_t grid = (int64_t)B * H * ((nc + 1) / 2);
+  hipLaunchKernelGGL((k_softmax_masked<T, To, D>), dim3((unsigned)grid), dim3(256), C::LDS_BYTES, st, q, k, v,
+                     (const int32_t*)nullptr, (const int32_t*)nullptr, o, lse, H, L, 1, scale * LOG2E,
+                     (const T*)nullptr, (const T*)nullptr, (const int32_t*)nullptr, 0, win_chunks);
+  return hipGetLastError();
+}
+#define INSTW(T, To, D)                                                                                \
+  template hipError_t launch_softmax_window<T, To, D>(const T*, const T*, const T*, To*, float*, int, int, \
+                                                      int, int, float, hipStream_t);
+INSTW(float, float, 64)
+INSTW(float, float, 128)
+INSTW(bf16, float, 64)
+INSTW(bf16, float, 128)
+INSTW(float, bf16, 64)
+INSTW(float, bf16, 128)
+INSTW(bf16, bf16, 64)
+INSTW(bf16, bf16, 128)
+#undef INSTW
 
 #define INST(T, To, D)                                                                         \
   template hipError_t launch_softmax_masked<T, To, D>(const T*, const T*, const T*,            \

@@ -593,7 +593,7 @@ def decode_step(cache, x, q, k, v, alpha, beta, w_score, w_mix, b_score=None, g_
 # window ("Native Hybrid Attention for Efficient Sequence Modeling", section 2
 # Methodologie, "Unificatie van Intra-layer Hybridisatie")
 # ---------------------------------------------------------------------------
-def nha_attention(q, k, v, slot_gate, window, scale=None):
+def nha_attention(q, k, v, slot_gate, window, scale=None, query_blocks=None, chunk=CHUNK):
     """Plain per-token definition.
 
     The page describes it this way: long-term information is compressed into
@@ -613,13 +613,16 @@ def nha_attention(q, k, v, slot_gate, window, scale=None):
         slots start at zero;
       * the slots join the key set only once a token has entered them, so
         w >= L is exactly causal softmax attention.
-    q, k, v [B,H,L,D]; slot_gate [B,H,L,m]; returns o [B,H,L,D]."""
+    q, k, v [B,H,L,D]; slot_gate [B,H,L,m]; returns o [B,H,L,D].
+    query_blocks, if given, lists the 64-row query blocks whose outputs are
+    computed (the slots still take every token); other rows stay zero."""
     q, k, v, a = map(_f64, (q, k, v, slot_gate))
     B, H, L, D = q.shape
     m = a.shape[3]
     if scale is None:
         scale = 1.0 / np.sqrt(D)
     o = np.zeros_like(v)
+    wanted = None if query_blocks is None else set(query_blocks)
     for b in range(B):
         for h in range(H):
             Ks = np.zeros((m, D))
@@ -632,6 +635,8 @@ def nha_attention(q, k, v, slot_gate, window, scale=None):
                     Ks = g * Ks + (1.0 - g) * k[b, h, s][None, :]
                     Vs = g * Vs + (1.0 - g) * v[b, h, s][None, :]
                     entered += 1
+                if wanted is not None and t // chunk not in wanted:
+                    continue
                 lo = max(0, t - window + 1)
                 keys = [k[b, h, lo:t + 1]]
                 vals = [v[b, h, lo:t + 1]]

@@ -201,6 +201,24 @@ def make_prefill(wl: Workload, seed=None, L=None, B=None, H=None, alpha_range=(0
                 g_sm=np.ones(D, np.float32), g_lin=np.ones(D, np.float32), plan=plan, io=io)
 
 
+# Native Hybrid Attention inputs (slots + sliding window): the long prefill's
+# shape with 64 slots and a 2048-token window
+NHA = dict(B=1, H=16, L=32768, D=128, slots=64, window=2048, seed=6)
+
+
+def make_nha(B, H, L, D, slots, io="bf16", seed=6, q_scale=1.0, gate_mean=2.0):
+    """q, v ~ N(0, 1), k ~ N(0, 1) L2-normalised per token (q scaled by
+    q_scale for sharp attention), slot gates sigmoid(N(gate_mean, 1)) per
+    token and slot (mean ~0.85: slots forget over a few tokens to a few tens
+    of tokens); bf16 io rounds q, k, v.  Returns numpy float32 arrays."""
+    rs = _streams(seed)
+    q = q_scale * rs[4].standard_normal(size=(B, H, L, D), dtype=np.float32)
+    k = _unit_rows(rs[5].standard_normal(size=(B, H, L, D), dtype=np.float32))
+    v = rs[6].standard_normal(size=(B, H, L, D), dtype=np.float32)
+    gate = (1.0 / (1.0 + np.exp(-(gate_mean + rs[7].standard_normal(size=(B, H, L, slots)))))).astype(np.float32)
+    return dict(q=_io(q, io), k=_io(k, io), v=_io(v, io), gate=gate, io=io)
+
+
 def forced_routes(B, nc, kind, G=1):
     """route [B, G, Nc] int32 for forced runs: 'sm' (all softmax) or 'lin'."""
     return np.full((B, G, nc), 0 if kind == "sm" else 1, dtype=np.int32)
