@@ -468,6 +468,56 @@ def time_prefill_config(args, N, W, name, route_kind=None):
     return out, inp, r["route"]
 
 
+def time_nha(args, N, W, reps=10):
+    """Native Hybrid Attention on its workload (the long prefill's shape, 64
+    slots, a 2048-token window, bf16): the whole call timed with events, the
+    four kernels from the library's events.  Algorithmic work: 4 D FLOPs per
+    (query, window key) pair and per (query, slot) pair (scores and read-out,
+    as for softmax attention), plus 4 D FLOPs per (token, slot) for the slot
+    update (K~ and V~, two multiply-adds each)."""
+    import torch
+    c = W.NHA
+    B, H, L, D, m, w = c["B"], c["H"], c["L"], c["D"], c["slots"], c["window"]
+    inp = W.make_nha(B, H, L, D, m, io="bf16", seed=c["seed"])
+    dev = torch.device("cuda:0")
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(torch.bfloat16)
+    q, k, v = bf(inp["q"]), bf(inp["k"]), bf(inp["v"])
+    gate = torch.from_numpy(inp["gate"]).to(dev)
+    del inp
+    dm = N.dims(B, H, L, D, 64, N.BF16)
+    ws = N.workspace(N.nha_workspace_size(dm, m, w), dev)
+    call = lambda: N.nha_attention(dm, q, k, v, gate, w, ws=ws)
+    settle(call)
+    stats = evented_steps(call, reps, flush=Flusher(dev))
+    warm = evented_steps(call, reps)
+    N.profile_enable(True)
+    kernels = kernel_table(N, call, ("nha_window", "nha_chunk", "nha_scan", "nha_slots"), 5)
+    N.profile_enable(False)
+    pairs_win = B * H * sum(min(t + 1, w) for t in range(L))
+    f_win = 4 * D * pairs_win
+    nct = L - w if L > w else 0  # queries whose slots are in use
+    f_slots = 4 * D * m * B * H * nct          # scores and read-out over the slots
+    f_update = 4 * D * m * B * H * L           # slot updates
+    med = warm["median_ms"]
+    work = {"nha_window": ("mfma", f_win, PEAK_BF16_TFLOPS, "TFLOP/s"),
+            "nha_slots": ("alu", f_slots + f_update, PEAK_FP32_VALU_TFLOPS, "TFLOP/s"),
+            "nha_chunk": ("alu", 4 * D * m * B * H * L, PEAK_FP32_VALU_TFLOPS, "TFLOP/s"),
+            "nha_scan": ("hbm", 2 * 2 * B * H * max(L // 64 - w // 64, 0) * m * D * 4, PEAK_HBM_GBS, "GB/s")}
+    dom = max(work, key=lambda n: kernels[n]["avg_us"])
+    bound, amount, peak, unit = work[dom]
+    us = kernels[dom]["avg_us"]
+    ach = amount / (us * 1e-6) / (1e12 if unit == "TFLOP/s" else 1e9)
+    rl = dict(bound=bound, kernel=dom, achieved=round(ach, 1), peak=peak, unit=unit, frac=round(ach / peak, 4),
+              traffic=None, avg_launch_us=us)
+    rl["flops_per_launch" if unit == "TFLOP/s" else "bytes_per_launch"] = amount
+    return dict(workload=f"Native Hybrid Attention: B={B} H={H} L={L} D={D}, {m} slots, window {w} tokens, bf16",
+                value=round(B * L / (med * 1e-3), 1), unit="tokens/s", ms_per_call_median=med,
+                step_stats=dict(flushed=stats, back_to_back=warm),
+                flops=dict(window=f_win, slots=f_slots, slot_updates=f_update),
+                layer_frac_of_mfma_peak=round((f_win + f_slots + f_update) / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                roofline=rl, kernels=kernels)
+
+
 def decode_state(N, W, dev, n_open=0):
     """The decode workload's cache on the device (n_open = 0 as generated:
     position 32768 starts a chunk); inputs of the new token."""
@@ -770,6 +820,7 @@ PROFILE_PARTS = {  # part -> bench.py command profiled (one rocprofv3 run per pa
     "prefill": PROFILE_BASE + " --only prefill",
     "degen_sm": PROFILE_BASE + " --only degen_sm",
     "degen_lin": PROFILE_BASE + " --only degen_lin",
+    "nha": PROFILE_BASE + " --only nha",
 }
 PROFILE_PASSES = {  # pass -> rocprofv3 options
     "trace": "--kernel-trace --stats",
@@ -785,6 +836,8 @@ KERNEL_NAMES = [  # substring of the kernel symbol -> short name
     ("k_sm_bwd_delta", "sm_bwd_delta"), ("k_sm_bwd_dq", "sm_bwd_dq"), ("k_sm_bwd_dkdv", "sm_bwd_dkdv"),
     ("k_gdn_bwd_ckpt", "gdn_bwd_ckpt"), ("k_gdn_bwdI", "gdn_bwd"), ("k_gdn_bwd_reduce", "gdn_bwd_reduce"),
     ("k_merge_bwd_reduce", "merge_bwd_reduce"), ("k_merge_bwd_final", "merge_bwd_final"), ("k_merge_bwdI", "merge_bwd"),
+    ("k_softmax_maskedIDF16bfLi128", "nha_window"), ("k_nha_chunk", "nha_chunk"), ("k_nha_scan", "nha_scan"),
+    ("k_nha_slots", "nha_slots"),
     ("AUnaryFunctor<float, float", "calib_mul_256MiB"), ("Cijk_", "calib_gemm_bf16_4096"),
 ]
 MFMA_KERNELS = ("softmax_masked", "gdn_prep", "gdn_scan", "sm_bwd_dq", "sm_bwd_dkdv", "calib_gemm_bf16_4096")
@@ -979,7 +1032,7 @@ def summarize_profiles(d):
     print("wrote", out)
 
 
-CONFIG_NAMES = ("prefill", "degen_sm", "degen_lin", "decode_open32", "decode_open63")
+CONFIG_NAMES = ("prefill", "degen_sm", "degen_lin", "decode_open32", "decode_open63", "nha")
 
 
 def main():
@@ -1070,6 +1123,10 @@ def main():
                     configs[name] = (time_decode_open(args, N, W, dstate, n_open), None, None)
                     print(f"{name}: {configs[name][0]['ms_per_step_median_flushed']} ms/step (median, flushed)",
                           file=sys.stderr, flush=True)
+        if only in (None, "nha"):
+            configs["nha"] = (time_nha(args, N, W), None, None)
+            print(f"nha: {configs['nha'][0]['ms_per_call_median']} ms/call, dominant {configs['nha'][0]['roofline']['kernel']} "
+                  f"{configs['nha'][0]['roofline']['frac']*100:.1f}%", file=sys.stderr, flush=True)
     del dstate
     if configs:
         res["configs"] = {k: v[0] for k, v in configs.items()}

@@ -66,7 +66,8 @@ size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 const char* kKernelNames[KID_COUNT] = {"route",        "compact",       "gdn_prep",   "gdn_scan",
                                        "softmax_masked", "merge",       "decode_route", "decode_gdn",
                                        "decode_attn",  "decode_combine", "decode_commit", "softmax_backward", "decode_handoff",
-                                       "gdn_backward", "merge_backward", "nha"};
+                                       "gdn_backward", "merge_backward", "nha", "nha_window", "nha_chunk", "nha_scan",
+                                       "nha_slots"};
 struct ProfRec {
   int kid;
   hipEvent_t a, b;
@@ -850,14 +851,14 @@ natsl_status natsl_nha_attention(const natsl_dims* dims, const void* q, const vo
   if (prof) prof(KID_NHA, stream, 0);
   if (dims->io == NATSL_BF16)
     e = dims->Dk == 64 ? launch_nha<bf16, bf16, 64>((const bf16*)q, (const bf16*)k, (const bf16*)v, slot_gate, slots,
-                                                    (bf16*)out, ws, B, H, L, window, sc, stream)
+                                                    (bf16*)out, ws, B, H, L, window, sc, stream, prof)
                        : launch_nha<bf16, bf16, 128>((const bf16*)q, (const bf16*)k, (const bf16*)v, slot_gate,
-                                                     slots, (bf16*)out, ws, B, H, L, window, sc, stream);
+                                                     slots, (bf16*)out, ws, B, H, L, window, sc, stream, prof);
   else
     e = dims->Dk == 64 ? launch_nha<float, float, 64>((const float*)q, (const float*)k, (const float*)v, slot_gate,
-                                                      slots, (float*)out, ws, B, H, L, window, sc, stream)
+                                                      slots, (float*)out, ws, B, H, L, window, sc, stream, prof)
                        : launch_nha<float, float, 128>((const float*)q, (const float*)k, (const float*)v, slot_gate,
-                                                       slots, (float*)out, ws, B, H, L, window, sc, stream);
+                                                       slots, (float*)out, ws, B, H, L, window, sc, stream, prof);
   if (prof) prof(KID_NHA, stream, 1);
   if (e != hipSuccess) return dev_fail(e, "natsl_nha_attention");
   return ok();

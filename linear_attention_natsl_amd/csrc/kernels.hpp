@@ -26,6 +26,10 @@ enum {
   KID_GDN_BWD,
   KID_MERGE_BWD,
   KID_NHA,
+  KID_NHA_WINDOW,
+  KID_NHA_CHUNK,
+  KID_NHA_SCAN,
+  KID_NHA_SLOTS,
   KID_COUNT
 };
 
@@ -107,7 +111,7 @@ struct NhaWs {
 size_t nha_ws_bytes(int B, int H, int L, int D, int M, int window);
 template <typename T, typename To, int D>
 hipError_t launch_nha(const T* q, const T* k, const T* v, const float* gate, int M, To* out, void* ws, int B, int H,
-                      int L, int window, float scale, hipStream_t st);
+                      int L, int window, float scale, hipStream_t st, void (*prof)(int, hipStream_t, int));
 
 size_t gdn_ws_bytes(int io_is_bf16, int D, int64_t nch);
 // Gated DeltaNet branch gradient (per-token reverse sweep): ws holds the

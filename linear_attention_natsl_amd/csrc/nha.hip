@@ -266,14 +266,17 @@ size_t nha_ws_bytes(int B, int H, int L, int D, int M, int window) {
 
 template <typename T, typename To, int D>
 hipError_t launch_nha_m(const T* q, const T* k, const T* v, const float* gate, int M, To* out, void* wsp, int B,
-                        int H, int L, int window, float scale, hipStream_t st) {
+                        int H, int L, int window, float scale, hipStream_t st, void (*prof)(int, hipStream_t, int)) {
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   const int nc = L / CHUNK, nw = window / CHUNK;
   const int ne = nc > nw ? nc - nw : 0;
   const int64_t BH = (int64_t)B * H;
   hipError_t e;
   if (ne == 0) {  // the window covers the sequence: causal softmax attention
-    return launch_softmax_window<T, To, D>(q, k, v, out, nullptr, B, H, L, nc, scale, st);
+    if (prof) prof(KID_NHA_WINDOW, st, 0);
+    e = launch_softmax_window<T, To, D>(q, k, v, out, nullptr, B, H, L, nc, scale, st);
+    if (e == hipSuccess && prof) prof(KID_NHA_WINDOW, st, 1);
+    return e;
   }
   char* p = (char*)wsp;
   NhaWs ws;
@@ -283,25 +286,34 @@ hipError_t launch_nha_m(const T* q, const T* k, const T* v, const float* gate, i
   float* o_w = (float*)p; p += al((size_t)BH * L * D * 4);
   float* lse_w = (float*)p;
   if (nw > 0) {
+    if (prof) prof(KID_NHA_WINDOW, st, 0);
     e = launch_softmax_window<T, float, D>(q, k, v, o_w, lse_w, B, H, L, nw, scale, st);
     if (e != hipSuccess) return e;
+    if (prof) prof(KID_NHA_WINDOW, st, 1);
   }
   const float* ow = nw > 0 ? o_w : nullptr;
   const float* lw = nw > 0 ? lse_w : nullptr;
   const size_t lds = (size_t)(CHUNK * (D + 4) + (M + CHUNK) * (D + 4) + CHUNK * M + CHUNK * (M + CHUNK) + CHUNK) * 4;
 #define NHA_M(MM)                                                                                                  \
   do {                                                                                                             \
+    if ((e = set_lds_limit((const void*)k_nha_slots<T, To, D, MM>, (int)lds)) != hipSuccess) return e;            \
+    if (prof) prof(KID_NHA_CHUNK, st, 0);                                                                          \
     hipLaunchKernelGGL((k_nha_chunk<T, D, MM>), dim3((unsigned)(BH * ne)), dim3(256), 0, st, k, v, gate, ws, L,     \
                        ne);                                                                                        \
     if ((e = hipGetLastError()) != hipSuccess) return e;                                                          \
+    if (prof) prof(KID_NHA_CHUNK, st, 1);                                                                          \
     const int64_t nthr = BH * 2 * MM * D;                                                                          \
+    if (prof) prof(KID_NHA_SCAN, st, 0);                                                                           \
     hipLaunchKernelGGL((k_nha_scan<D, MM>), dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0, st, ws, (int)BH,   \
                        ne);                                                                                        \
     if ((e = hipGetLastError()) != hipSuccess) return e;                                                          \
-    if ((e = set_lds_limit((const void*)k_nha_slots<T, To, D, MM>, (int)lds)) != hipSuccess) return e;            \
+    if (prof) prof(KID_NHA_SCAN, st, 1);                                                                           \
+    if (prof) prof(KID_NHA_SLOTS, st, 0);                                                                          \
     hipLaunchKernelGGL((k_nha_slots<T, To, D, MM>), dim3((unsigned)(BH * nc)), dim3(256), lds, st, q, k, v, gate,  \
                        ws, ow, lw, out, L, nw, ne, scale);                                                         \
-    return hipGetLastError();                                                                                      \
+    if ((e = hipGetLastError()) != hipSuccess) return e;                                                          \
+    if (prof) prof(KID_NHA_SLOTS, st, 1);                                                                          \
+    return hipSuccess;                                                                                             \
   } while (0)
   if (M == 16) NHA_M(16);
   if (M == 32) NHA_M(32);
@@ -312,13 +324,13 @@ hipError_t launch_nha_m(const T* q, const T* k, const T* v, const float* gate, i
 
 template <typename T, typename To, int D>
 hipError_t launch_nha(const T* q, const T* k, const T* v, const float* gate, int M, To* out, void* ws, int B, int H,
-                      int L, int window, float scale, hipStream_t st) {
-  return launch_nha_m<T, To, D>(q, k, v, gate, M, out, ws, B, H, L, window, scale, st);
+                      int L, int window, float scale, hipStream_t st, void (*prof)(int, hipStream_t, int)) {
+  return launch_nha_m<T, To, D>(q, k, v, gate, M, out, ws, B, H, L, window, scale, st, prof);
 }
 
 #define INST(T, To, D)                                                                                          \
   template hipError_t launch_nha<T, To, D>(const T*, const T*, const T*, const float*, int, To*, void*, int, int, \
-                                           int, int, float, hipStream_t);
+                                           int, int, float, hipStream_t, void (*)(int, hipStream_t, int));
 INST(float, float, 64)
 INST(float, float, 128)
 INST(bf16, bf16, 64)
