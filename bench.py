@@ -836,7 +836,7 @@ KERNEL_NAMES = [  # substring of the kernel symbol -> short name
     ("k_sm_bwd_delta", "sm_bwd_delta"), ("k_sm_bwd_dq", "sm_bwd_dq"), ("k_sm_bwd_dkdv", "sm_bwd_dkdv"),
     ("k_gdn_bwd_ckpt", "gdn_bwd_ckpt"), ("k_gdn_bwdI", "gdn_bwd"), ("k_gdn_bwd_reduce", "gdn_bwd_reduce"),
     ("k_merge_bwd_reduce", "merge_bwd_reduce"), ("k_merge_bwd_final", "merge_bwd_final"), ("k_merge_bwdI", "merge_bwd"),
-    ("k_softmax_maskedIDF16bfLi128", "nha_window"), ("k_nha_chunk", "nha_chunk"), ("k_nha_scan", "nha_scan"),
+    ("k_softmax_masked", "nha_window"), ("k_nha_chunk", "nha_chunk"), ("k_nha_scan", "nha_scan"),
     ("k_nha_slots", "nha_slots"),
     ("AUnaryFunctor<float, float", "calib_mul_256MiB"), ("Cijk_", "calib_gemm_bf16_4096"),
 ]
