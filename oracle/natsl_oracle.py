@@ -202,7 +202,7 @@ def softmax_branch_bruteforce(q, k, v, route_bgc, scale=None, chunk=CHUNK):
     return o
 
 
-def softmax_branch_backward(q, k, v, route_bgc, d_o, scale=None, chunk=CHUNK):
+def softmax_branch_backward(q, k, v, route_bgc, d_o, scale=None, chunk=CHUNK, with_gate=False):
     """Gradient of the softmax branch (softmax_branch above) for an upstream
     gradient d_o [B,H,L,Dv]: returns dq, dk, dv.  The pages define only the
     forward; this is its exact derivative, taken one 64-row query block at a
@@ -211,13 +211,21 @@ def softmax_branch_backward(q, k, v, route_bgc, d_o, scale=None, chunk=CHUNK):
         o  = p v
         dp = d_o v^T,  delta = rowsum(d_o * o),  ds = p * (dp - delta)
         dq = scale * ds k,   dk += scale * ds^T q,   dv += p^T d_o
-    (masked keys have p = 0 and receive nothing)."""
+    (masked keys have p = 0 and receive nothing).
+
+    with_gate: also returns dgate [B,H,Nc], the derivative with respect to
+    each chunk's softmax gate h_c (see route_backward): the layer with chunk
+    c's keys weighted by h_c for the queries of later chunks, at h_c = 0 or 1;
+    with p~ = exp(scale q.k - lse) over ALL keys of chunk c (visible or not),
+        dgate[c] = sum_{t in later chunks} sum_{s in c} p~_ts (d_o_t . v_s - delta_t)."""
     q, k, v, d_o = _f64(q), _f64(k), _f64(v), _f64(d_o)
     B, H, L, Dk = q.shape
     G = route_bgc.shape[1]
     if scale is None:
         scale = 1.0 / np.sqrt(Dk)
     dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    nc = L // chunk
+    dgate = np.zeros((B, H, nc))
     for b in range(B):
         for g in range(G):
             heads = [h for h in range(H) if group_of_head(h, H, G) == g]
@@ -236,7 +244,16 @@ def softmax_branch_backward(q, k, v, route_bgc, d_o, scale=None, chunk=CHUNK):
                 dq[b, heads, t0:t1] = scale * np.einsum("hqk,hkd->hqd", ds, k[b, heads, :t1])
                 dk[b, heads, :t1] += scale * np.einsum("hqk,hqd->hkd", ds, q[b, heads, t0:t1])
                 dv[b, heads, :t1] += np.einsum("hqk,hqd->hkd", p, g_o)
-    return dq, dk, dv
+                if with_gate and t0 >= chunk:
+                    # every key of the chunks before this block, visible or not
+                    zall = scale * np.einsum("hqd,hkd->hqk", q[b, heads, t0:t1], k[b, heads, :t0])
+                    lse = (zmax_all := z.max(axis=-1, keepdims=True)) + np.log(
+                        np.exp(z - zmax_all).sum(axis=-1, keepdims=True))
+                    pt = np.exp(zall - lse)
+                    dpa = np.einsum("hqd,hkd->hqk", g_o, v[b, heads, :t0])
+                    contrib = (pt * (dpa - delta)).sum(axis=1)  # [heads, t0]
+                    dgate[b, heads, :t0 // chunk] += contrib.reshape(len(heads), t0 // chunk, chunk).sum(axis=2)
+    return (dq, dk, dv, dgate) if with_gate else (dq, dk, dv)
 
 
 # ---------------------------------------------------------------------------
@@ -310,7 +327,8 @@ def gdn_branch_bruteforce(q, k, v, alpha, beta, route_bgc, S_init=None, chunk=CH
     return o
 
 
-def gdn_branch_backward(q, k, v, alpha, beta, route_bgc, d_o, S_init=None, dS_final=None, chunk=CHUNK):
+def gdn_branch_backward(q, k, v, alpha, beta, route_bgc, d_o, S_init=None, dS_final=None, chunk=CHUNK,
+                        with_gate=False):
     """Gradient of gdn_branch for an upstream gradient d_o [B,H,L,Dv] of its
     outputs (and dS_final [B,H,Dk,Dv] of its final carried state, if any):
     returns dq, dk, dv, dalpha, dbeta, dS_init.  The pages define only the
@@ -328,7 +346,12 @@ def gdn_branch_backward(q, k, v, alpha, beta, route_bgc, d_o, S_init=None, dS_fi
     Rollback: a chunk that keeps its end state (linear route) passes the
     carried state's gradient into its last token; one that restores its
     chunk-start state passes it straight to the chunk start, and its tokens
-    see only their own outputs' gradients (G starts at zero)."""
+    see only their own outputs' gradients (G starts at zero).
+
+    with_gate: also returns dgate [B,H,Nc], the derivative with respect to
+    each chunk's linear gate h_c (see route_backward): the carried state after
+    chunk c written as S_start + h_c (S_end - S_start), at h_c = 0 or 1, so
+        dgate[c] = <d loss / d carried state after c, S_end - S_start>."""
     q, k, v, alpha, beta, d_o = map(_f64, (q, k, v, alpha, beta, d_o))
     B, H, L, Dk = q.shape
     Dv = v.shape[3]
@@ -348,6 +371,7 @@ def gdn_branch_backward(q, k, v, alpha, beta, route_bgc, d_o, S_init=None, dS_fi
     dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
     dalpha, dbeta = np.zeros_like(alpha), np.zeros_like(beta)
     Gc = np.zeros((B, H, Dk, Dv)) if dS_final is None else _f64(dS_final).copy()  # d loss / d carried state
+    dgate = np.zeros((B, H, L // chunk))
     for c0 in reversed(range(0, L, chunk)):
         c1 = min(L, c0 + chunk)
         keep = (route_bgc[:, gidx, c0 // chunk] == LIN) if c0 + chunk <= L else np.zeros((B, H), bool)
@@ -356,6 +380,10 @@ def gdn_branch_backward(q, k, v, alpha, beta, route_bgc, d_o, S_init=None, dS_fi
         prev = [starts[c0 // chunk]]
         for t in range(c0, c1 - 1):
             prev.append(gdn_token_update(prev[-1], k[:, :, t], v[:, :, t], alpha[:, :, t], beta[:, :, t]))
+        if with_gate and c1 - c0 == chunk:
+            S_end = gdn_token_update(prev[-1], k[:, :, c1 - 1], v[:, :, c1 - 1], alpha[:, :, c1 - 1],
+                                     beta[:, :, c1 - 1])
+            dgate[:, :, c0 // chunk] = np.sum(Gc * (S_end - prev[0]), axis=(-2, -1))
         G = np.where(kp, Gc, 0.0)
         for t in reversed(range(c0, c1)):
             S = prev[t - c0]
@@ -373,7 +401,50 @@ def gdn_branch_backward(q, k, v, alpha, beta, route_bgc, d_o, S_init=None, dS_fi
                            - at * bt * (np.einsum("...kv,...v->...k", G, a) + np.einsum("...kv,...v->...k", S, w)))
             G = at[..., None] * (G - bt[..., None] * kt[..., :, None] * w[..., None, :])
         Gc = G + np.where(kp, 0.0, Gc)
-    return dq, dk, dv, dalpha, dbeta, Gc
+    out = (dq, dk, dv, dalpha, dbeta, Gc)
+    return out + (dgate,) if with_gate else out
+
+
+def route_backward(x, w_score, dgate_sm, dgate_lin, b_score=None, chunk=CHUNK, groups=1):
+    """Gradient of the router under the straight-through reading of
+    [NL] Kernmechanismen 5 (the operation selection is learned end to end,
+    with gradients computed for the attention score layer; the pages do not
+    say how the argmax is differentiated).
+
+    The route of chunk c enters the layer as a one-hot gate h_c =
+    onehot(argmax s_c): the softmax branch weights chunk c's keys by
+    h_c[softmax] for the queries of later chunks, the Gated DeltaNet branch
+    commits chunk c's end state with weight h_c[linear]; at h in {0, 1} that
+    is exactly the routed forward.  Straight-through: the backward takes
+    d h_c / d s_c to be the Jacobian of softmax(s_c).  Then with
+    dh = (dgate_sm, dgate_lin) summed over the heads of each route group and
+    pi = softmax(s_c):
+        ds_c = pi * (dh - pi . dh)
+        dW_score[:, 2g + o] = sum_{b, c} mean_c(x) ds[b, g, c, o],  db = sum ds,
+        dx_t = W_score ds_{c(t)} / chunk
+    x [B,L,d]; dgate_* [B,H,Nc] (per head); returns dx, dW_score, db, ds."""
+    x = _f64(x)
+    w = _f64(w_score)
+    B, L, d = x.shape
+    nc = L // chunk
+    G = groups
+    H = np.asarray(dgate_sm).shape[1]
+    s = route_scores(x, w, b_score, chunk, G)  # [B, G, Nc, 2]
+    z = s - s.max(axis=-1, keepdims=True)
+    pi = np.exp(z) / np.exp(z).sum(axis=-1, keepdims=True)
+    dh = np.zeros((B, G, nc, 2))
+    for h in range(H):
+        g = group_of_head(h, H, G)
+        dh[:, g, :, SM] += _f64(dgate_sm)[:, h]
+        dh[:, g, :, LIN] += _f64(dgate_lin)[:, h]
+    ds = pi * (dh - (pi * dh).sum(axis=-1, keepdims=True))
+    pooled = x[:, : nc * chunk].reshape(B, nc, chunk, d).mean(axis=2)  # [B, Nc, d]
+    ds_flat = ds.transpose(0, 2, 1, 3).reshape(B, nc, 2 * G)           # columns (2g, 2g+1)
+    dW = np.einsum("bcd,bco->do", pooled, ds_flat)
+    db = ds_flat.sum(axis=(0, 1))
+    dx = np.zeros_like(x)
+    dx[:, : nc * chunk] = np.repeat(np.einsum("do,bco->bcd", w, ds_flat) / chunk, chunk, axis=1)
+    return dx, dW, db, ds
 
 
 # ---------------------------------------------------------------------------
