@@ -86,7 +86,8 @@ enum {
   NATSL_ENTRY_DECODE_HANDOFF = 6,
   NATSL_ENTRY_SOFTMAX_BACKWARD = 7,
   NATSL_ENTRY_GDN_BACKWARD = 8,
-  NATSL_ENTRY_MERGE_BACKWARD = 9
+  NATSL_ENTRY_MERGE_BACKWARD = 9,
+  NATSL_ENTRY_ROUTE_BACKWARD = 10
 };
 
 typedef struct {
@@ -181,12 +182,18 @@ natsl_status natsl_softmax_masked(const natsl_dims* dims, const void* q, const v
  *                  scaled scores (natsl_softmax_masked with lse)
  *   d_o            [B, H, L, Dv] io dtype: gradient of the loss w.r.t. o_sm
  *   dq, dk, dv     [B, H, L, D] fp32 outputs (written, not accumulated)
+ *   dgate          [B, H, Nc] fp32 or NULL: the derivative with respect to each
+ *                  chunk's softmax gate (see natsl_route_backward): with
+ *                  p~ = exp(scale q.k - lse) over every key of chunk c, visible
+ *                  or not, dgate[c] = sum over the queries of later chunks and
+ *                  the keys of c of p~ (d_o.v - delta).  Requesting it makes a
+ *                  linear-routed chunk visit the later query chunks too.
  *   ws             workspace of natsl_workspace_size(NATSL_ENTRY_SOFTMAX_BACKWARD)
  */
 natsl_status natsl_softmax_masked_backward(const natsl_dims* dims, const void* q, const void* k, const void* v,
                                            const int32_t* sel_idx, const int32_t* nsel_before, const void* o_sm,
                                            const float* lse, const void* d_o, float* dq, float* dk, float* dv,
-                                           void* ws, size_t ws_bytes, hipStream_t stream);
+                                           float* dgate, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Gradient of the Gated DeltaNet branch through the per-chunk rollback (the
@@ -207,6 +214,10 @@ natsl_status natsl_softmax_masked_backward(const natsl_dims* dims, const void* q
  *                  or NULL (zeros)
  *   dq, dk, dv     [B, H, L, D] fp32 outputs; dalpha, dbeta [B, H, L] fp32
  *   dS_init        [B, H, Dk, Dv] fp32 gradient w.r.t. S_init, or NULL
+ *   dgate          [B, H, Nc] fp32 or NULL: the derivative with respect to each
+ *                  chunk's linear gate (see natsl_route_backward; the carried
+ *                  state after chunk c written S_start + h (S_end - S_start)):
+ *                  <d loss / d carried state after c, S_end - S_start>
  *   ws             workspace of natsl_workspace_size(NATSL_ENTRY_GDN_BACKWARD)
  * Every output is written, not accumulated.  This is the per-token form (one
  * wave per group of 4 state columns at D = 128, 8 at D = 64; a checkpoint
@@ -217,8 +228,37 @@ natsl_status natsl_softmax_masked_backward(const natsl_dims* dims, const void* q
 natsl_status natsl_gdn_backward(const natsl_dims* dims, const void* q, const void* k, const void* v,
                                 const float* alpha, const float* beta, const int32_t* route, const float* S_init,
                                 const float* d_o, const float* dS_final, float* dq, float* dk, float* dv,
-                                float* dalpha, float* dbeta, float* dS_init, void* ws, size_t ws_bytes,
+                                float* dalpha, float* dbeta, float* dS_init, float* dgate, void* ws, size_t ws_bytes,
                                 hipStream_t stream);
+
+/*
+ * Gradient of the router ("Technische Samenvatting: Neural Attention Search
+ * Linear (NAtS-L)", Kernmechanismen 5: the operation selection is learned end
+ * to end, with gradients computed for the attention score layer; the pages do
+ * not say how the argmax is differentiated).  This library's reading is the
+ * straight-through estimator: the route of chunk c enters the layer as a
+ * one-hot gate h_c = onehot(argmax s_c) -- the softmax branch weights chunk
+ * c's keys by h_c[softmax] for the queries of later chunks, the Gated DeltaNet
+ * branch commits chunk c's end state with weight h_c[linear], which at one-hot
+ * h is exactly the routed forward -- and d h_c / d s_c is taken to be the
+ * Jacobian of softmax(s_c).  With dh = (dgate_sm, dgate_lin) summed over the
+ * heads of each route group and pi = softmax(s_c):
+ *   ds = pi (dh - pi . dh);  dW[:, 2g + o] = sum_{b, c} mean_c(x) ds[b, g, c, o];
+ *   db = sum ds;  dx_t = W ds_{c(t)} / 64.
+ *   dims          B, H, L, d_model, route_groups, io (x's dtype)
+ *   x             [B, L, d_model] io dtype;  w_score [d_model, 2G] fp32
+ *   scores        [B, G, Nc, 2] fp32: the forward's scores (natsl_route /
+ *                 natsl_forward scores_out)
+ *   dgate_sm, dgate_lin  [B, H, Nc] fp32 (natsl_softmax_masked_backward and
+ *                 natsl_gdn_backward with dgate)
+ *   dx            [B, L, d_model] fp32 or NULL;  dw_score [d_model, 2G] fp32;
+ *   db_score      [2G] fp32 or NULL (all written, not accumulated)
+ *   ws            workspace of natsl_workspace_size(NATSL_ENTRY_ROUTE_BACKWARD)
+ * Sums run in a fixed order (deterministic).  Errors as for natsl_route.
+ */
+natsl_status natsl_route_backward(const natsl_dims* dims, const void* x, const float* w_score, const float* scores,
+                                  const float* dgate_sm, const float* dgate_lin, float* dx, float* dw_score,
+                                  float* db_score, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Gradient of the output merging (Kernmechanismen 4 defines the forward; this
@@ -473,7 +513,8 @@ natsl_status natsl_nha_attention(const natsl_dims* dims, const void* q, const vo
  * "gdn_prep", "gdn_scan", "softmax_masked", "merge", "decode_route",
  * "decode_gdn", "decode_attn", "decode_combine", "decode_commit",
  * "softmax_backward", "decode_handoff", "gdn_backward", "merge_backward",
- * "nha" (each a whole call of that entry).
+ * "route_backward", "nha" (each a whole call of that entry) and "nha_window",
+ * "nha_chunk", "nha_scan", "nha_slots" (the kernels of natsl_nha_attention).
  * natsl_profile_select restricts the recording to the kernel named `name`
  * (NULL or "" records every kernel again), so that timing one kernel adds
  * only its own two event records to a step; an unknown name is

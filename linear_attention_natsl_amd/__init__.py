@@ -20,13 +20,14 @@ LIB_PATH = os.path.join(HERE, "libnatsl.so")
 F32, BF16 = 0, 1
 ROUTE_SOFTMAX, ROUTE_LINEAR = 0, 1
 ENTRY_ROUTE, ENTRY_GDN_CHUNK, ENTRY_SOFTMAX_MASKED, ENTRY_MERGE, ENTRY_FORWARD, ENTRY_DECODE_STEP, \
-    ENTRY_DECODE_HANDOFF, ENTRY_SOFTMAX_BACKWARD, ENTRY_GDN_BACKWARD, ENTRY_MERGE_BACKWARD = range(10)
+    ENTRY_DECODE_HANDOFF, ENTRY_SOFTMAX_BACKWARD, ENTRY_GDN_BACKWARD, ENTRY_MERGE_BACKWARD, \
+    ENTRY_ROUTE_BACKWARD = range(11)
 STATUS = {0: "NATSL_OK", 1: "NATSL_ERR_INVALID_ARG", 2: "NATSL_ERR_UNSUPPORTED",
           3: "NATSL_ERR_WORKSPACE", 4: "NATSL_ERR_DEVICE", 5: "NATSL_ERR_CAPACITY"}
 EXPORTS = ["natsl_version", "natsl_last_error", "natsl_workspace_size", "natsl_route", "natsl_gdn_chunk",
            "natsl_softmax_masked", "natsl_merge", "natsl_forward", "natsl_decode_step",
            "natsl_decode_handoff", "natsl_softmax_masked_backward", "natsl_gdn_backward", "natsl_merge_backward",
-           "natsl_decode_step_noalloc", "natsl_nha_workspace_size", "natsl_nha_attention", "natsl_profile_enable", "natsl_profile_reset", "natsl_profile_read",
+           "natsl_decode_step_noalloc", "natsl_route_backward", "natsl_nha_workspace_size", "natsl_nha_attention", "natsl_profile_enable", "natsl_profile_reset", "natsl_profile_read",
            "natsl_profile_select"]
 DECODE_NOALLOC_SCRATCH_BYTES = 16 << 20
 
@@ -94,8 +95,9 @@ def lib():
         L.natsl_nha_attention.argtypes = [C.POINTER(Dims), vp, vp, vp, vp, C.c_int, C.c_int, vp, vp, C.c_size_t, vp]
         L.natsl_decode_handoff.argtypes = [C.POINTER(Dims), vp, vp, vp, vp, C.c_int, C.POINTER(DecodeCache), vp,
                                            C.c_size_t, vp]
-        L.natsl_softmax_masked_backward.argtypes = [C.POINTER(Dims)] + [vp] * 12 + [C.c_size_t, vp]
-        L.natsl_gdn_backward.argtypes = [C.POINTER(Dims)] + [vp] * 16 + [C.c_size_t, vp]
+        L.natsl_softmax_masked_backward.argtypes = [C.POINTER(Dims)] + [vp] * 13 + [C.c_size_t, vp]
+        L.natsl_gdn_backward.argtypes = [C.POINTER(Dims)] + [vp] * 17 + [C.c_size_t, vp]
+        L.natsl_route_backward.argtypes = [C.POINTER(Dims)] + [vp] * 9 + [C.c_size_t, vp]
         L.natsl_merge_backward.argtypes = [C.POINTER(Dims), vp, vp, vp, C.c_int, vp, C.c_int64] + [vp] * 10 + \
             [C.c_size_t, vp]
         L.natsl_profile_enable.argtypes = [C.c_int]
@@ -103,7 +105,7 @@ def lib():
         L.natsl_profile_select.argtypes = [C.c_char_p]
         for name in ("natsl_workspace_size", "natsl_route", "natsl_gdn_chunk", "natsl_softmax_masked",
                      "natsl_merge", "natsl_forward", "natsl_decode_step", "natsl_decode_step_noalloc",
-                     "natsl_nha_workspace_size", "natsl_nha_attention",
+                     "natsl_nha_workspace_size", "natsl_nha_attention", "natsl_route_backward",
                      "natsl_decode_handoff",
                      "natsl_softmax_masked_backward", "natsl_gdn_backward", "natsl_merge_backward",
                      "natsl_profile_enable",
@@ -403,13 +405,16 @@ def decode_step(dm: Dims, state: DecodeState, *args, debug=False, **kw):
     return d
 
 
-def softmax_masked_backward(dm: Dims, q, k, v, sel_idx, nsel_before, o_sm, lse, d_o, stream=None):
-    """Gradient of the softmax branch: returns fp32 (dq, dk, dv).  o_sm and lse
-    are the forward's outputs (softmax_masked(..., o_dtype=io, want_lse=True)),
-    d_o the upstream gradient, both in the io dtype."""
+def softmax_masked_backward(dm: Dims, q, k, v, sel_idx, nsel_before, o_sm, lse, d_o, stream=None, want_gate=False):
+    """Gradient of the softmax branch: returns fp32 (dq, dk, dv), and the
+    per-chunk softmax-gate derivative [B, H, Nc] as a fourth value when
+    want_gate.  o_sm and lse are the forward's outputs (softmax_masked(...,
+    o_dtype=io, want_lse=True)), d_o the upstream gradient, both in the io
+    dtype."""
     io, qs, nc = _io_t(dm), (dm.B, dm.H, dm.L, dm.Dk), dm.L // 64
     dq = torch.empty(qs, dtype=torch.float32, device=q.device)
     dk, dv = torch.empty_like(dq), torch.empty_like(dq)
+    dg = torch.empty(dm.B, dm.H, nc, dtype=torch.float32, device=q.device) if want_gate else None
     ws_bytes = workspace_size(ENTRY_SOFTMAX_BACKWARD, dm)
     ws = workspace(ws_bytes, q.device)
     _check(lib().natsl_softmax_masked_backward(
@@ -417,12 +422,12 @@ def softmax_masked_backward(dm: Dims, q, k, v, sel_idx, nsel_before, o_sm, lse, 
         _p(sel_idx, torch.int32, "sel_idx", (dm.B, dm.route_groups, nc)),
         _p(nsel_before, torch.int32, "nsel_before", (dm.B, dm.route_groups, nc + 1)),
         _p(o_sm, io, "o_sm", qs), _p(lse, torch.float32, "lse", qs[:3]), _p(d_o, io, "d_o", qs),
-        _p(dq), _p(dk), _p(dv), _p(ws), ws_bytes, _stream(stream)))
-    return dq, dk, dv
+        _p(dq), _p(dk), _p(dv), _p(dg), _p(ws), ws_bytes, _stream(stream)))
+    return (dq, dk, dv, dg) if want_gate else (dq, dk, dv)
 
 
 def gdn_backward(dm: Dims, q, k, v, alpha, beta, route_bgc, d_o, S_init=None, dS_final=None, want_dS_init=True,
-                 stream=None):
+                 stream=None, want_gate=False):
     """Gradient of the Gated DeltaNet branch through the rollback: returns fp32
     (dq, dk, dv, dalpha, dbeta, dS_init).  q, k, v, alpha, beta, route_bgc and
     S_init are the forward's inputs (gdn_chunk), d_o the fp32 upstream gradient
@@ -434,6 +439,7 @@ def gdn_backward(dm: Dims, q, k, v, alpha, beta, route_bgc, d_o, S_init=None, dS
     da = torch.empty(ts, dtype=torch.float32, device=q.device)
     db = torch.empty_like(da)
     dS0 = torch.empty(ss, dtype=torch.float32, device=q.device) if want_dS_init else None
+    dg = torch.empty(dm.B, dm.H, dm.L // 64, dtype=torch.float32, device=q.device) if want_gate else None
     ws_bytes = workspace_size(ENTRY_GDN_BACKWARD, dm)
     ws = workspace(ws_bytes, q.device)
     _check(lib().natsl_gdn_backward(
@@ -441,9 +447,26 @@ def gdn_backward(dm: Dims, q, k, v, alpha, beta, route_bgc, d_o, S_init=None, dS
         _p(alpha, torch.float32, "alpha", ts), _p(beta, torch.float32, "beta", ts),
         _p(route_bgc, torch.int32, "route", (dm.B, dm.route_groups, dm.L // 64)),
         _p(S_init, torch.float32, "S_init", ss), _p(d_o, torch.float32, "d_o", qs),
-        _p(dS_final, torch.float32, "dS_final", ss), _p(dq), _p(dk), _p(dv), _p(da), _p(db), _p(dS0),
+        _p(dS_final, torch.float32, "dS_final", ss), _p(dq), _p(dk), _p(dv), _p(da), _p(db), _p(dS0), _p(dg),
         _p(ws), ws_bytes, _stream(stream)))
-    return dq, dk, dv, da, db, dS0
+    return (dq, dk, dv, da, db, dS0, dg) if want_gate else (dq, dk, dv, da, db, dS0)
+
+
+def route_backward(dm: Dims, x, w_score, scores, dgate_sm, dgate_lin, want_dx=True, want_db=True, stream=None):
+    """Router gradient under the straight-through reading (natsl_route_backward):
+    returns fp32 (dx or None, dw_score, db_score or None)."""
+    io, nc, G = _io_t(dm), dm.L // 64, dm.route_groups
+    dx = torch.empty(dm.B, dm.L, dm.d_model, dtype=torch.float32, device=x.device) if want_dx else None
+    dw = torch.empty(dm.d_model, 2 * G, dtype=torch.float32, device=x.device)
+    db = torch.empty(2 * G, dtype=torch.float32, device=x.device) if want_db else None
+    ws_bytes = workspace_size(ENTRY_ROUTE_BACKWARD, dm)
+    ws = workspace(ws_bytes, x.device)
+    _check(lib().natsl_route_backward(
+        C.byref(dm), _p(x, io, "x", (dm.B, dm.L, dm.d_model)), _p(w_score, torch.float32, "w_score", (dm.d_model, 2 * G)),
+        _p(scores, torch.float32, "scores", (dm.B, G, nc, 2)),
+        _p(dgate_sm, torch.float32, "dgate_sm", (dm.B, dm.H, nc)), _p(dgate_lin, torch.float32, "dgate_lin", (dm.B, dm.H, nc)),
+        _p(dx), _p(dw), _p(db), _p(ws), ws_bytes, _stream(stream)))
+    return dx, dw, db
 
 
 def merge_backward(dm: Dims, q, o_sm, o_gdn, w_mix, d_out, w_mix_head_stride=0, g_sm=None, g_lin=None,

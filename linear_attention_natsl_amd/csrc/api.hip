@@ -67,7 +67,7 @@ const char* kKernelNames[KID_COUNT] = {"route",        "compact",       "gdn_pre
                                        "softmax_masked", "merge",       "decode_route", "decode_gdn",
                                        "decode_attn",  "decode_combine", "decode_commit", "softmax_backward", "decode_handoff",
                                        "gdn_backward", "merge_backward", "nha", "nha_window", "nha_chunk", "nha_scan",
-                                       "nha_slots"};
+                                       "nha_slots", "route_backward"};
 struct ProfRec {
   int kid;
   hipEvent_t a, b;
@@ -387,6 +387,10 @@ natsl_status natsl_workspace_size(int entry, const natsl_dims* dims, size_t* byt
       CHECK(check_dims(dims, true, false));
       *bytes = merge_bwd_ws_bytes(dims->B, dims->H, dims->L, dims->Dk);
       return ok();
+    case NATSL_ENTRY_ROUTE_BACKWARD:
+      CHECK(check_dims(dims, true, true));
+      *bytes = route_bwd_ws_bytes(dims->B, dims->route_groups, dims->L, dims->d_model);
+      return ok();
     default:
       return fail(NATSL_ERR_INVALID_ARG, "unknown entry id %d", entry);
   }
@@ -647,7 +651,7 @@ natsl_status natsl_decode_step_noalloc(const natsl_dims* dims, const natsl_decod
 natsl_status natsl_softmax_masked_backward(const natsl_dims* dims, const void* q, const void* k, const void* v,
                                            const int32_t* sel_idx, const int32_t* nsel_before, const void* o_sm,
                                            const float* lse, const void* d_o, float* dq, float* dk, float* dv,
-                                           void* ws, size_t ws_bytes, hipStream_t stream) {
+                                           float* dgate, void* ws, size_t ws_bytes, hipStream_t stream) {
   CHECK(check_dims(dims, true, false));
   if (dims->B == 0) return ok();  // empty batch: nothing to do, pointers may be NULL
   NEED(q, "q");
@@ -671,18 +675,18 @@ natsl_status natsl_softmax_masked_backward(const natsl_dims* dims, const void* q
     e = dims->Dk == 64
             ? launch_softmax_backward<bf16, bf16, 64>((const bf16*)q, (const bf16*)k, (const bf16*)v, sel_idx,
                                                       nsel_before, (const bf16*)o_sm, lse, (const bf16*)d_o, dq, dk,
-                                                      dv, ws, B, H, L, G, sc, stream)
+                                                      dv, dgate, ws, B, H, L, G, sc, stream)
             : launch_softmax_backward<bf16, bf16, 128>((const bf16*)q, (const bf16*)k, (const bf16*)v, sel_idx,
                                                        nsel_before, (const bf16*)o_sm, lse, (const bf16*)d_o, dq, dk,
-                                                       dv, ws, B, H, L, G, sc, stream);
+                                                       dv, dgate, ws, B, H, L, G, sc, stream);
   else
     e = dims->Dk == 64
             ? launch_softmax_backward<float, float, 64>((const float*)q, (const float*)k, (const float*)v, sel_idx,
                                                         nsel_before, (const float*)o_sm, lse, (const float*)d_o, dq,
-                                                        dk, dv, ws, B, H, L, G, sc, stream)
+                                                        dk, dv, dgate, ws, B, H, L, G, sc, stream)
             : launch_softmax_backward<float, float, 128>((const float*)q, (const float*)k, (const float*)v, sel_idx,
                                                          nsel_before, (const float*)o_sm, lse, (const float*)d_o, dq,
-                                                         dk, dv, ws, B, H, L, G, sc, stream);
+                                                         dk, dv, dgate, ws, B, H, L, G, sc, stream);
   if (prof) prof(KID_SOFTMAX_BWD, stream, 1);
   if (e != hipSuccess) return dev_fail(e, "natsl_softmax_masked_backward");
   return ok();
@@ -691,7 +695,7 @@ natsl_status natsl_softmax_masked_backward(const natsl_dims* dims, const void* q
 natsl_status natsl_gdn_backward(const natsl_dims* dims, const void* q, const void* k, const void* v,
                                 const float* alpha, const float* beta, const int32_t* route, const float* S_init,
                                 const float* d_o, const float* dS_final, float* dq, float* dk, float* dv,
-                                float* dalpha, float* dbeta, float* dS_init, void* ws, size_t ws_bytes,
+                                float* dalpha, float* dbeta, float* dS_init, float* dgate, void* ws, size_t ws_bytes,
                                 hipStream_t stream) {
   CHECK(check_dims(dims, true, false));
   if (dims->B == 0) return ok();  // empty batch: nothing to do, pointers may be NULL
@@ -715,17 +719,17 @@ natsl_status natsl_gdn_backward(const natsl_dims* dims, const void* q, const voi
   if (dims->io == NATSL_BF16)
     e = dims->Dk == 64 ? launch_gdn_backward<bf16, 64>((const bf16*)q, (const bf16*)k, (const bf16*)v, alpha, beta,
                                                        route, S_init, d_o, dS_final, dq, dk, dv, dalpha, dbeta,
-                                                       dS_init, ws, B, H, L, G, stream)
+                                                       dS_init, dgate, ws, B, H, L, G, stream)
                        : launch_gdn_backward<bf16, 128>((const bf16*)q, (const bf16*)k, (const bf16*)v, alpha, beta,
                                                         route, S_init, d_o, dS_final, dq, dk, dv, dalpha, dbeta,
-                                                        dS_init, ws, B, H, L, G, stream);
+                                                        dS_init, dgate, ws, B, H, L, G, stream);
   else
     e = dims->Dk == 64 ? launch_gdn_backward<float, 64>((const float*)q, (const float*)k, (const float*)v, alpha,
                                                         beta, route, S_init, d_o, dS_final, dq, dk, dv, dalpha,
-                                                        dbeta, dS_init, ws, B, H, L, G, stream)
+                                                        dbeta, dS_init, dgate, ws, B, H, L, G, stream)
                        : launch_gdn_backward<float, 128>((const float*)q, (const float*)k, (const float*)v, alpha,
                                                          beta, route, S_init, d_o, dS_final, dq, dk, dv, dalpha,
-                                                         dbeta, dS_init, ws, B, H, L, G, stream);
+                                                         dbeta, dS_init, dgate, ws, B, H, L, G, stream);
   if (prof) prof(KID_GDN_BWD, stream, 1);
   if (e != hipSuccess) return dev_fail(e, "natsl_gdn_backward");
   return ok();
@@ -818,6 +822,32 @@ natsl_status natsl_decode_handoff(const natsl_dims* dims, const int32_t* route, 
   const hipError_t e = dims->io == NATSL_BF16 ? launch_handoff<bf16>(L, ws, stream) : launch_handoff<float>(L, ws, stream);
   if (prof) prof(KID_HANDOFF, stream, 1);
   if (e != hipSuccess) return dev_fail(e, "natsl_decode_handoff");
+  return ok();
+}
+
+natsl_status natsl_route_backward(const natsl_dims* dims, const void* x, const float* w_score, const float* scores,
+                                  const float* dgate_sm, const float* dgate_lin, float* dx, float* dw_score,
+                                  float* db_score, void* ws, size_t ws_bytes, hipStream_t stream) {
+  CHECK(check_dims(dims, true, true));
+  if (dims->B == 0) return ok();  // empty batch: nothing to do, pointers may be NULL
+  NEED(x, "x");
+  NEED(w_score, "w_score");
+  NEED(scores, "scores");
+  NEED(dgate_sm, "dgate_sm");
+  NEED(dgate_lin, "dgate_lin");
+  NEED(dw_score, "dw_score");
+  CHECK(check_ws(ws, ws_bytes, route_bwd_ws_bytes(dims->B, dims->route_groups, dims->L, dims->d_model)));
+  auto prof = prof_fn();
+  if (prof) prof(KID_ROUTE_BWD, stream, 0);
+  const hipError_t e =
+      dims->io == NATSL_BF16
+          ? launch_route_backward<bf16>((const bf16*)x, w_score, scores, dgate_sm, dgate_lin, dx, dw_score, db_score,
+                                        ws, dims->B, dims->H, dims->L, dims->d_model, dims->route_groups, stream)
+          : launch_route_backward<float>((const float*)x, w_score, scores, dgate_sm, dgate_lin, dx, dw_score,
+                                         db_score, ws, dims->B, dims->H, dims->L, dims->d_model, dims->route_groups,
+                                         stream);
+  if (prof) prof(KID_ROUTE_BWD, stream, 1);
+  if (e != hipSuccess) return dev_fail(e, "natsl_route_backward");
   return ok();
 }
 

@@ -55,7 +55,8 @@ size_t gdn_bwd_ws_bytes(int B, int H, int L, int D) {
   const size_t nc = (size_t)L / CHUNK, ntok = (size_t)B * H * L, ncg = (size_t)(D == 128 ? GdnBwdCfg<128>::NCG : GdnBwdCfg<64>::NCG);
   const size_t floats = (size_t)B * H * (nc + CHUNK) * D * D  // chunk-start states, chunk token states
                         + 2 * ntok * ncg * D                  // dq, dk partials
-                        + 2 * ntok * ncg;                     // dalpha, dbeta partials
+                        + 2 * ntok * ncg                      // dalpha, dbeta partials
+                        + (size_t)B * H * ncg * nc;           // linear-gate partials
   return (floats * 4 + 255) / 256 * 256;
 }
 
@@ -244,7 +245,8 @@ __global__ void __launch_bounds__(64) k_gdn_bwd(const T* __restrict__ q, const T
                                                  const float* __restrict__ ckpt, float* __restrict__ scratch,
                                                  float* __restrict__ dq_p, float* __restrict__ dk_p,
                                                  float* __restrict__ dab_p, float* __restrict__ dv,
-                                                 float* __restrict__ dS_init, int H, int L, int G) {
+                                                 float* __restrict__ dS_init, float* __restrict__ gate_p, int H,
+                                                 int L, int G) {
   using C = GdnBwdCfg<D>;
   constexpr int NV = 2 * C::RPT;  // row-sum values per thread and token: dq, dk at its rows
   constexpr int VPL = NV / C::CW;  // of which each lane stores VPL after the row-group reduction
@@ -295,6 +297,16 @@ __global__ void __launch_bounds__(64) k_gdn_bwd(const T* __restrict__ q, const T
           gdn_fwd_token<D>(S, cur, lane_bcast(al_c, s), lane_bcast(be_c, s));
         }
       }
+    }
+    // the linear gate's derivative (the chunk's end state committed as
+    // S_start + h (S_end - S_start)): <d loss / d carried state after the
+    // chunk, S_end - S_start>, this group's columns; S holds S_end here
+    if (gate_p) {
+      float pg = 0.f;
+#pragma unroll
+      for (int i = 0; i < C::RPT; ++i) pg += Gc[i] * (S[i] - ck[((int64_t)c * D + r0 + i) * D + j]);
+      pg = wave_sum64(pg);
+      if (lane == 0) gate_p[(int64_t)bid_x() * nc + c] = pg;
     }
     // (this thread's scratch stores complete before the sweep reads them back)
     __syncthreads();
@@ -415,11 +427,22 @@ __global__ void __launch_bounds__(256) k_gdn_bwd_reduce(const float* __restrict_
   }
 }
 
+// the linear gates' derivative: the column groups' partials added in order
+__global__ void __launch_bounds__(256) k_gdn_bwd_gate_reduce(const float* __restrict__ gate_p,
+                                                             float* __restrict__ dgate, int ncg, int nc, int64_t n) {
+  const int64_t i = (int64_t)bid_x() * 256 + tid_x();  // (bh, c)
+  if (i >= n) return;
+  const int64_t bh = i / nc, c = i % nc;
+  float s = 0.f;
+  for (int cg = 0; cg < ncg; ++cg) s += gate_p[(bh * ncg + cg) * nc + c];
+  dgate[i] = s;
+}
+
 template <typename T, int D>
 hipError_t launch_gdn_backward(const T* q, const T* k, const T* v, const float* alpha, const float* beta,
                                const int32_t* route, const float* S_init, const float* d_o, const float* dS_final,
                                float* dq, float* dk, float* dv, float* dalpha, float* dbeta, float* dS_init,
-                               void* ws, int B, int H, int L, int G, hipStream_t st) {
+                               float* dgate, void* ws, int B, int H, int L, int G, hipStream_t st) {
   using C = GdnBwdCfg<D>;
   const int nc = L / CHUNK;
   const int64_t ntok = (int64_t)B * H * L;
@@ -428,6 +451,7 @@ hipError_t launch_gdn_backward(const T* q, const T* k, const T* v, const float* 
   float* dq_p = scratch + (size_t)B * H * CHUNK * D * D;
   float* dk_p = dq_p + (size_t)ntok * C::NCG * D;
   float* dab_p = dk_p + (size_t)ntok * C::NCG * D;  // ntok x NCG x (dalpha, dbeta)
+  float* gate_p = dab_p + (size_t)ntok * C::NCG * 2;  // [B H][NCG][Nc]
   const size_t lds = 0;
   const unsigned grid = (unsigned)(B * H * C::NCG);
   hipLaunchKernelGGL((k_gdn_bwd_ckpt<T, D>), dim3(grid), dim3(C::NT), lds, st, k, v, alpha, beta, route, S_init,
@@ -435,8 +459,14 @@ hipError_t launch_gdn_backward(const T* q, const T* k, const T* v, const float* 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((k_gdn_bwd<T, D>), dim3(grid), dim3(C::NT), lds, st, q, k, v, alpha, beta, route, d_o,
-                     dS_final, ckpt, scratch, dq_p, dk_p, dab_p, dv, dS_init, H, L, G);
+                     dS_final, ckpt, scratch, dq_p, dk_p, dab_p, dv, dS_init, dgate ? gate_p : nullptr, H, L, G);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (dgate) {
+    const int64_t n = (int64_t)B * H * nc;
+    hipLaunchKernelGGL(k_gdn_bwd_gate_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, gate_p, dgate,
+                       C::NCG, nc, n);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   const int64_t threads = ntok * (D / 4) + ntok;
   hipLaunchKernelGGL((k_gdn_bwd_reduce<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, dq_p, dk_p,
                      dab_p, dq, dk, dalpha, dbeta, ntok);
@@ -446,7 +476,7 @@ hipError_t launch_gdn_backward(const T* q, const T* k, const T* v, const float* 
 #define INST(T, D)                                                                                                \
   template hipError_t launch_gdn_backward<T, D>(const T*, const T*, const T*, const float*, const float*,         \
                                                 const int32_t*, const float*, const float*, const float*, float*, \
-                                                float*, float*, float*, float*, float*, void*, int, int, int, int, \
+                                                float*, float*, float*, float*, float*, float*, void*, int, int, int, int, \
                                                 hipStream_t);
 INST(float, 64)
 INST(float, 128)

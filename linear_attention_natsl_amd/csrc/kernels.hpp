@@ -30,6 +30,7 @@ enum {
   KID_NHA_CHUNK,
   KID_NHA_SCAN,
   KID_NHA_SLOTS,
+  KID_ROUTE_BWD,
   KID_COUNT
 };
 
@@ -50,6 +51,12 @@ hipError_t launch_route(const T* x, const float* w, const float* bsc, int B, int
                         int32_t* route_out, float* scores, hipStream_t st);
 hipError_t launch_compact(const int32_t* route_in, int32_t* route_out, int B, int G, int nc,
                           int32_t* sel_idx, int32_t* nsel_before, hipStream_t st);
+// router gradient (straight-through): ws holds ds [B, G, Nc, 2] and the chunk means [B, Nc, d]
+size_t route_bwd_ws_bytes(int B, int G, int L, int d);
+template <typename T>
+hipError_t launch_route_backward(const T* x, const float* w, const float* scores, const float* dg_sm,
+                                 const float* dg_lin, float* dx, float* dw, float* db, void* ws, int B, int H, int L,
+                                 int d, int G, hipStream_t st);
 
 // mixd (nullable): per-token z0 - z1 of the mixing scores q W_mix, already
 // computed (by the softmax branch); then q and w_mix are not read
@@ -79,8 +86,8 @@ size_t sm_bwd_ws_bytes(int B, int H, int L);
 template <typename T, typename To, int D>
 hipError_t launch_softmax_backward(const T* q, const T* k, const T* v, const int32_t* sel_idx,
                                    const int32_t* nsel_before, const To* o, const float* lse, const T* d_o,
-                                   float* dq, float* dk, float* dv, void* ws, int B, int H, int L, int G,
-                                   float scale, hipStream_t st);
+                                   float* dq, float* dk, float* dv, float* dgate, void* ws, int B, int H, int L,
+                                   int G, float scale, hipStream_t st);
 // the merge's mixing scores from the softmax branch's own q fragments: when
 // d is set and the launch uses the bf16 D = 128 kernel, d[b, h, t] =
 // q W_mix[:, 0] - q W_mix[:, 1] is written and *done set (false otherwise)
@@ -121,7 +128,7 @@ template <typename T, int D>
 hipError_t launch_gdn_backward(const T* q, const T* k, const T* v, const float* alpha, const float* beta,
                                const int32_t* route, const float* S_init, const float* d_o, const float* dS_final,
                                float* dq, float* dk, float* dv, float* dalpha, float* dbeta, float* dS_init,
-                               void* ws, int B, int H, int L, int G, hipStream_t st);
+                               float* dgate, void* ws, int B, int H, int L, int G, hipStream_t st);
 template <typename T, typename To, int D>
 hipError_t launch_gdn(const T* q, const T* k, const T* v, const float* alpha, const float* beta,
                       const int32_t* route, const float* S_init, To* o_gdn, float* S_final, void* ws,

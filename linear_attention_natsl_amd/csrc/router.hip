@@ -156,6 +156,120 @@ __global__ void __launch_bounds__(64) k_compact(const int32_t* __restrict__ rout
   if (lane == 0) nsb[nc] = base;
 }
 
+// ---------------------------------------------------------------------------
+// Router gradient ("Technische Samenvatting: Neural Attention Search Linear
+// (NAtS-L)", Kernmechanismen 5: the selection is learned end to end, with
+// gradients for the attention score layer).  Straight-through reading: the
+// route of chunk c is a one-hot gate h_c whose derivative with respect to the
+// scores is taken to be the Jacobian of softmax(s_c).  From the branches' gate
+// derivatives dh (per head, summed over the heads of the route group):
+//   ds = pi (dh - pi . dh),  pi = softmax(s_c)
+//   dW[:, 2g + o] = sum_{b, c} mean_c(x) ds[b, g, c, o],   db = sum ds,
+//   dx_t = W ds_{c(t)} / 64
+// Every sum runs in a fixed order: deterministic.
+
+// ds [B, G, Nc, 2], one thread per (b, g, c)
+__global__ void __launch_bounds__(256) k_route_bwd_ds(const float* __restrict__ scores,
+                                                      const float* __restrict__ dg_sm,
+                                                      const float* __restrict__ dg_lin, int B, int H, int G, int nc,
+                                                      float* __restrict__ ds) {
+  const int64_t i = (int64_t)bid_x() * 256 + tid_x();
+  if (i >= (int64_t)B * G * nc) return;
+  const int c = (int)(i % nc), g = (int)((i / nc) % G), b = (int)(i / ((int64_t)nc * G));
+  const int hpg = H / G;
+  float dh0 = 0.f, dh1 = 0.f;
+  for (int h = g * hpg; h < (g + 1) * hpg; ++h) {
+    const int64_t j = ((int64_t)b * H + h) * nc + c;
+    dh0 += dg_sm[j];
+    dh1 += dg_lin[j];
+  }
+  const float s0 = scores[i * 2], s1 = scores[i * 2 + 1];
+  const float m = fmaxf(s0, s1);
+  const float e0 = __expf(s0 - m), e1 = __expf(s1 - m);
+  const float p0 = e0 / (e0 + e1), p1 = e1 / (e0 + e1);
+  const float pd = p0 * dh0 + p1 * dh1;
+  ds[i * 2] = p0 * (dh0 - pd);
+  ds[i * 2 + 1] = p1 * (dh1 - pd);
+}
+
+// per (b, c): the chunk mean of x (kept for dW) and dx of the chunk's rows
+template <typename T>
+__global__ void __launch_bounds__(256) k_route_bwd_x(const T* __restrict__ x, const float* __restrict__ w,
+                                                     const float* __restrict__ ds, int L, int d, int G, int nc,
+                                                     float* __restrict__ pooled, float* __restrict__ dx) {
+  const int c = bid_x(), b = bid_y();
+  const T* xc = x + ((int64_t)b * L + (int64_t)c * CHUNK) * d;
+  const float* dsc = ds + ((int64_t)b * G * nc + c) * 2;  // + (g nc) * 2 + o
+  for (int col = tid_x(); col < d; col += 256) {
+    float sx = 0.f;
+    for (int r = 0; r < CHUNK; ++r) sx += to_f32(xc[(int64_t)r * d + col]);
+    pooled[((int64_t)b * nc + c) * d + col] = sx * (1.0f / CHUNK);
+    if (dx) {
+      float gx = 0.f;
+      for (int g = 0; g < G; ++g)
+        gx += w[(int64_t)col * 2 * G + 2 * g] * dsc[(int64_t)g * nc * 2] +
+              w[(int64_t)col * 2 * G + 2 * g + 1] * dsc[(int64_t)g * nc * 2 + 1];
+      gx *= 1.0f / CHUNK;
+      float* dxc = dx + ((int64_t)b * L + (int64_t)c * CHUNK) * d + col;
+      for (int r = 0; r < CHUNK; ++r) dxc[(int64_t)r * d] = gx;
+    }
+  }
+}
+
+// dW [d, 2G] and db [2G]: one thread per output, the (b, c) sum in order
+__global__ void __launch_bounds__(256) k_route_bwd_w(const float* __restrict__ pooled, const float* __restrict__ ds,
+                                                     int B, int G, int nc, int d, float* __restrict__ dw,
+                                                     float* __restrict__ db) {
+  const int64_t i = (int64_t)bid_x() * 256 + tid_x();
+  const int64_t nw = (int64_t)d * 2 * G;
+  if (i < nw) {
+    const int col = (int)(i / (2 * G)), o = (int)(i % (2 * G)), g = o / 2, oo = o % 2;
+    float acc = 0.f;
+    for (int b = 0; b < B; ++b)
+      for (int c = 0; c < nc; ++c)
+        acc += pooled[((int64_t)b * nc + c) * d + col] * ds[(((int64_t)b * G + g) * nc + c) * 2 + oo];
+    dw[i] = acc;
+  } else if (db && i < nw + 2 * G) {
+    const int o = (int)(i - nw), g = o / 2, oo = o % 2;
+    float acc = 0.f;
+    for (int b = 0; b < B; ++b)
+      for (int c = 0; c < nc; ++c) acc += ds[(((int64_t)b * G + g) * nc + c) * 2 + oo];
+    db[o] = acc;
+  }
+}
+
+size_t route_bwd_ws_bytes(int B, int G, int L, int d) {
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t nc = (size_t)L / CHUNK;
+  return al((size_t)B * G * nc * 2 * 4) + al((size_t)B * nc * d * 4);
+}
+
+template <typename T>
+hipError_t launch_route_backward(const T* x, const float* w, const float* scores, const float* dg_sm,
+                                 const float* dg_lin, float* dx, float* dw, float* db, void* wsp, int B, int H, int L,
+                                 int d, int G, hipStream_t st) {
+  auto al = [](size_t v) { return (v + 255) & ~(size_t)255; };
+  const int nc = L / CHUNK;
+  float* ds = (float*)wsp;
+  float* pooled = (float*)((char*)wsp + al((size_t)B * G * nc * 2 * 4));
+  const int64_t n = (int64_t)B * G * nc;
+  hipLaunchKernelGGL(k_route_bwd_ds, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, scores, dg_sm, dg_lin, B,
+                     H, G, nc, ds);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_route_bwd_x<T>, dim3(nc, B), dim3(256), 0, st, x, w, ds, L, d, G, nc, pooled, dx);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int64_t nt = (int64_t)d * 2 * G + 2 * G;
+  hipLaunchKernelGGL(k_route_bwd_w, dim3((unsigned)((nt + 255) / 256)), dim3(256), 0, st, pooled, ds, B, G, nc, d,
+                     dw, db);
+  return hipGetLastError();
+}
+template hipError_t launch_route_backward<float>(const float*, const float*, const float*, const float*,
+                                                 const float*, float*, float*, float*, void*, int, int, int, int,
+                                                 int, hipStream_t);
+template hipError_t launch_route_backward<bf16>(const bf16*, const float*, const float*, const float*, const float*,
+                                                float*, float*, float*, void*, int, int, int, int, int, hipStream_t);
+
 template <typename T>
 hipError_t launch_route(const T* x, const float* w, const float* bsc, int B, int L, int d, int G,
                         int32_t* route_out, float* scores, hipStream_t st) {

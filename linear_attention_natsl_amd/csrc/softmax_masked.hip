@@ -757,21 +757,26 @@ INST(bf16, bf16, 128)
 // accumulators) and the other operand in the key-group layout, as in the
 // forward's O^T = V^T P^T.  Gradients are written in fp32.
 
+// delta = rowsum(dO * O): D / 8 lanes per token, each with 8 contiguous
+// values of both rows (one 16-byte bf16 load each), summed across the lane
+// group in registers (DPP), so a wave reads whole rows contiguously
 template <typename To, int D>
 __global__ void __launch_bounds__(256) k_sm_bwd_delta(const To* __restrict__ o, const To* __restrict__ d_o,
                                                       float* __restrict__ delta, int64_t ntok) {
-  const int64_t t = (int64_t)bid_x() * 256 + tid_x();
-  if (t >= ntok) return;
+  constexpr int LPT = D / 8;  // lanes per token (8 or 16)
+  const int tid = tid_x();
+  const int64_t t = (int64_t)bid_x() * (256 / LPT) + tid / LPT;
+  const int c = (tid % LPT) * 8;
+  const bool in = t < ntok;
+  const int64_t tt = in ? t : ntok - 1;  // in-bounds row for the group's shuffle partners
+  float a[8], b[8];
+  load8f<To>(o + tt * D + c, a);
+  load8f<To>(d_o + tt * D + c, b);
   float acc = 0.f;
 #pragma unroll
-  for (int c = 0; c < D; c += 8) {
-    float a[8], b[8];
-    load8f<To>(o + t * D + c, a);
-    load8f<To>(d_o + t * D + c, b);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc = fmaf(a[j], b[j], acc);
-  }
-  delta[t] = acc;
+  for (int j = 0; j < 8; ++j) acc = fmaf(a[j], b[j], acc);
+  acc = dpp_group_sum<LPT>(acc);
+  if (in && (tid % LPT) == 0) delta[t] = acc;
 }
 
 // One 64-token tile loaded once and written to LDS in both layouts: thread t
@@ -920,7 +925,13 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) k_sm_bwd_dkdv(con
                                                      const int32_t* __restrict__ nsel_before,
                                                      const float* __restrict__ lse, const float* __restrict__ delta,
                                                      float* __restrict__ dk, float* __restrict__ dv, int H, int L,
-                                                     int G, float scale) {
+                                                     int G, float scale, float* __restrict__ dgate) {
+  // dgate (nullable) [B, H, Nc]: the derivative with respect to the chunk's
+  // softmax gate (its keys weighted by the gate for the queries of later
+  // chunks): the sum of dS = p (dP - delta) over every later query chunk, with
+  // p = exp(scale q.k - lse) whether or not the key chunk is softmax-routed;
+  // a linear-routed key chunk then visits the later query chunks for that sum
+  // only (its keys receive no dK / dV from them)
   using C = SmCfg<T, D>;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   T* qbuf = reinterpret_cast<T*>(smem_raw);  // Q rows, dO key groups
@@ -936,7 +947,8 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) k_sm_bwd_dkdv(con
   const int grp = (G == 1) ? 0 : h;
   const int32_t* nsbp = nsel_before + ((int64_t)b * G + grp) * (nc + 1);
   const bool kc_sm = nsbp[kc + 1] > nsbp[kc];
-  const int qlast = kc_sm ? nc - 1 : kc;
+  const int qlast = (kc_sm || dgate) ? nc - 1 : kc;
+  float gsum = 0.f;  // this lane's share of the gate derivative
   const int lane = lane_id(), w = wave_id();
   const int g = lane >> 4, c = lane & 15;
   const int64_t head_off = (int64_t)bh * L * D;
@@ -992,8 +1004,10 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) k_sm_bwd_dkdv(con
         const float pp = vis ? __builtin_amdgcn_exp2f(fmaf(s[i], scale_log2, -lse_s[qrow])) : 0.f;
         pm[qt][i] = pp;
         dsm[qt][i] = pp * (dp[i] - dlt_s[qrow]);
+        if (!diag) gsum += dsm[qt][i];
       }
     }
+    if (!diag && !kc_sm) continue;  // only the gate's sum: these keys are not visible in the forward
     // dV^T += dO^T P and dK^T += Q^T dS, contraction over the 64 queries
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
@@ -1024,6 +1038,13 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) k_sm_bwd_dkdv(con
     *reinterpret_cast<f32x4*>(okr + 16 * dt + 4 * g) = r;
     *reinterpret_cast<f32x4*>(ovr + 16 * dt + 4 * g) = adv[dt];
   }
+  if (dgate) {  // the wave sums, then the 4 waves in order (deterministic)
+    gsum = wave_sum64(gsum);
+    __syncthreads();  // lse_s is free again
+    if (lane == 0) lse_s[w] = gsum;
+    __syncthreads();
+    if (tid_x() == 0) dgate[(int64_t)bh * nc + kc] = (lse_s[0] + lse_s[1]) + (lse_s[2] + lse_s[3]);
+  }
 }
 
 size_t sm_bwd_ws_bytes(int B, int H, int L) { return (size_t)B * H * L * sizeof(float); }
@@ -1031,8 +1052,8 @@ size_t sm_bwd_ws_bytes(int B, int H, int L) { return (size_t)B * H * L * sizeof(
 template <typename T, typename To, int D>
 hipError_t launch_softmax_backward(const T* q, const T* k, const T* v, const int32_t* sel_idx,
                                    const int32_t* nsel_before, const To* o, const float* lse, const T* d_o,
-                                   float* dq, float* dk, float* dv, void* ws, int B, int H, int L, int G,
-                                   float scale, hipStream_t st) {
+                                   float* dq, float* dk, float* dv, float* dgate, void* ws, int B, int H, int L,
+                                   int G, float scale, hipStream_t st) {
   using C = SmCfg<T, D>;
   // the delta pass reads dO in the output dtype: only io == output dtype here
   static_assert(sizeof(To) > 0, "");
@@ -1044,7 +1065,8 @@ hipError_t launch_softmax_backward(const T* q, const T* k, const T* v, const int
   hipError_t e = set_lds_limit((const void*)k_sm_bwd_dq<T, D>, LDS_DQ);
   if (e == hipSuccess) e = set_lds_limit((const void*)k_sm_bwd_dkdv<T, D>, LDS_DKDV);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_sm_bwd_delta<To, D>), dim3((unsigned)((ntok + 255) / 256)), dim3(256), 0, st, o,
+  constexpr int TPB = 256 / (D / 8);  // tokens per block
+  hipLaunchKernelGGL((k_sm_bwd_delta<To, D>), dim3((unsigned)((ntok + TPB - 1) / TPB)), dim3(256), 0, st, o,
                      (const To*)d_o, delta, ntok);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -1053,14 +1075,14 @@ hipError_t launch_softmax_backward(const T* q, const T* k, const T* v, const int
                      nsel_before, lse, delta, dq, H, L, G, scale);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((k_sm_bwd_dkdv<T, D>), dim3((unsigned)grid), dim3(256), LDS_DKDV, st, q, k, v, d_o,
-                     nsel_before, lse, delta, dk, dv, H, L, G, scale);
+                     nsel_before, lse, delta, dk, dv, H, L, G, scale, dgate);
   return hipGetLastError();
 }
 
 #define INSTB(T, D)                                                                                    \
   template hipError_t launch_softmax_backward<T, T, D>(const T*, const T*, const T*, const int32_t*,  \
                                                        const int32_t*, const T*, const float*, const T*, \
-                                                       float*, float*, float*, void*, int, int, int, int, \
+                                                       float*, float*, float*, float*, void*, int, int, int, int, \
                                                        float, hipStream_t);
 INSTB(float, 64)
 INSTB(float, 128)
