@@ -211,6 +211,40 @@ def time_softmax_backward(N, dm, t, wl, pairs, reps=3):
                 flops=flops, tflops=round(tf, 1), frac_mfma=round(tf / PEAK_BF16_TFLOPS, 4))
 
 
+def time_route_gradient(N, dm, t, wl, reps=3):
+    """The router's gradient on this workload (straight-through reading): the
+    softmax branch's gradient with and without its gate derivatives (with
+    them every linear-routed key chunk also visits all later query chunks:
+    full causal attention work for the scores and dP), the Gated DeltaNet
+    gradient's gate partials, and natsl_route_backward (one pass over x plus
+    the score layer), each timed with events."""
+    import torch
+    r, sel, nsb, scores = N.route(dm, t["x"], t["w_score"], t["b_score"])
+    o, lse = N.softmax_masked(dm, t["q"], t["k"], t["v"], sel, nsb, o_dtype=t["q"].dtype, want_lse=True)
+    d_o = torch.randn_like(t["q"])
+    dg = torch.randn(wl.B, wl.H, wl.nc, dtype=torch.float32, device=t["q"].device)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return round(1000.0 * e0.elapsed_time(e1) / reps, 1)
+    sm = timed(lambda: N.softmax_masked_backward(dm, t["q"], t["k"], t["v"], sel, nsb, o, lse, d_o))
+    sm_g = timed(lambda: N.softmax_masked_backward(dm, t["q"], t["k"], t["v"], sel, nsb, o, lse, d_o, want_gate=True))
+    rb = timed(lambda: N.route_backward(dm, t["x"], t["w_score"], scores, dg, dg))
+    pairs_all = wl.B * wl.H * (wl.nc * (wl.nc - 1) // 2) * 64 * 64
+    return dict(workload=f"router gradient on the {wl.name} prefill (straight-through)",
+                softmax_backward_us=sm, softmax_backward_with_gate_us=sm_g, route_backward_us=rb,
+                gate_pairs=pairs_all,
+                note="the softmax gate needs p~ and dP for every (later query, key) pair: 4 D FLOPs per pair on the "
+                     "matrix cores for the pairs the forward skipped")
+
+
 def time_gdn_backward(N, dm, t, wl, route, reps=2):
     """Gradient of the Gated DeltaNet branch on this workload (a random fp32
     upstream gradient on o_gdn), timed with events.  Plain fp32 VALU work, so
@@ -381,7 +415,8 @@ def time_prefill(args, N, W, O):
         extras = dict(handoff=time_handoff(N, dm, fwd.route, t, wl),
                       softmax_backward=time_softmax_backward(N, dm, t, wl, r["pairs"]),
                       gdn_backward=time_gdn_backward(N, dm, t, wl, fwd.route),
-                      merge_backward=time_merge_backward(N, dm, t, wl))
+                      merge_backward=time_merge_backward(N, dm, t, wl),
+                      route_gradient=time_route_gradient(N, dm, t, wl))
     route = r["route"]
     ref_route = O.route(inp["x"], inp["w_score"], inp["b_score"])[0] if args.check_route else None
     f_sm, f_gdn, step_s = r["f_sm"], r["f_gdn"], r["step_s"]

@@ -64,13 +64,26 @@ __global__ void __launch_bounds__(256) k_nha_chunk(const T* __restrict__ k, cons
   float ak[SPT], av[SPT];
 #pragma unroll
   for (int u = 0; u < SPT; ++u) ak[u] = av[u] = 0.f;
-  for (int s = 0; s < CHUNK; ++s) {
-    const float ks = to_f32(kc[(int64_t)s * D]), vs = to_f32(vc[(int64_t)s * D]);
+  constexpr int PF = 8;  // tokens of k and v in flight (clamped, unconditional loads)
+  float kr[PF], vr[PF];
 #pragma unroll
-    for (int u = 0; u < SPT; ++u) {
-      const float w = wg[s][part * SPT + u];
-      ak[u] = fmaf(w, ks, ak[u]);
-      av[u] = fmaf(w, vs, av[u]);
+  for (int u = 0; u < PF; ++u) {
+    kr[u] = to_f32(kc[(int64_t)u * D]);
+    vr[u] = to_f32(vc[(int64_t)u * D]);
+  }
+  for (int s0 = 0; s0 < CHUNK; s0 += PF) {
+#pragma unroll
+    for (int x = 0; x < PF; ++x) {
+      const int s = s0 + x, sn = min(s + PF, CHUNK - 1);
+      const float ks = kr[x], vs = vr[x];
+      kr[x] = to_f32(kc[(int64_t)sn * D]);
+      vr[x] = to_f32(vc[(int64_t)sn * D]);
+#pragma unroll
+      for (int u = 0; u < SPT; ++u) {
+        const float w = wg[s][part * SPT + u];
+        ak[u] = fmaf(w, ks, ak[u]);
+        av[u] = fmaf(w, vs, av[u]);
+      }
     }
   }
   float* dk = ws.Sk + ((bh * ne + e) * M) * D + d;
@@ -136,8 +149,9 @@ __global__ void __launch_bounds__(256) k_nha_slots(const T* __restrict__ q, cons
   float* Qs = sh;                     // [64][DP]   queries
   float* KC = Qs + CHUNK * DP;        // [NCOL][DP] slot keys K~_e, then chunk e's keys
   float* A = KC + NCOL * DP;          // [64][M]    gates of chunk e's tokens
-  float* XQ = A + CHUNK * M;          // [64][NCOL] q.K~_e, q.k_s; then P[j][i] in the first M columns
-  float* WW = XQ + CHUNK * NCOL;      // [64] the window's weight per query
+  float* XS = A + CHUNK * M;          // [64 j][M]  q_j.K~_e[i], then P[j][i]
+  float* QKT = XS + CHUNK * M;        // [64 s][64 j] q_j.k_s (transposed: a step s reads its queries' row)
+  float* WW = QKT + CHUNK * CHUNK;    // [64] the window's weight per query
   const int nc = L / CHUNK;
   const int64_t bh = bid_x() / nc;
   const int c = bid_x() % nc;
@@ -145,25 +159,57 @@ __global__ void __launch_bounds__(256) k_nha_slots(const T* __restrict__ q, cons
   const int tid = tid_x();
   const int64_t row0 = bh * L + (int64_t)c * CHUNK;
   if (e < 0) {  // no token has left the window yet: the window's result stands
-    for (int x = tid; x < CHUNK * D; x += 256) out[row0 * D + x] = from_f32<To>(o_w[row0 * D + x]);
+    constexpr int NO = CHUNK * D / 4 / 256;
+    f32x4 ov[NO];
+#pragma unroll
+    for (int u = 0; u < NO; ++u) ov[u] = *reinterpret_cast<const f32x4*>(o_w + row0 * D + 4 * (tid + 256 * u));
+#pragma unroll
+    for (int u = 0; u < NO; ++u) {
+      const float f[4] = {ov[u][0], ov[u][1], ov[u][2], ov[u][3]};
+      store4f<To>(out + row0 * D + 4 * (tid + 256 * u), f);
+    }
     return;
   }
   const int64_t erow0 = bh * L + (int64_t)e * CHUNK;
-  // ---- stage q (chunk c), K~_e and chunk e's keys, chunk e's gates
-  for (int x = tid; x < CHUNK * D / 4; x += 256) {
-    const int r = x / (D / 4), col = (x % (D / 4)) * 4;
-    float f[4];
-    load4f<T>(q + (row0 + r) * D + col, f);
-    *reinterpret_cast<f32x4*>(Qs + r * DP + col) = f32x4{f[0], f[1], f[2], f[3]};
-    load4f<T>(k + (erow0 + r) * D + col, f);
-    *reinterpret_cast<f32x4*>(KC + (M + r) * DP + col) = f32x4{f[0], f[1], f[2], f[3]};
+  // ---- stage q (chunk c), K~_e and chunk e's keys, chunk e's gates: every
+  // load of the thread is issued before the first LDS store (a load, then its
+  // store, one after the other kept a single load in flight per wave)
+  {
+    constexpr int NQ = CHUNK * D / 8 / 256;  // 8-element pieces of q and of k per thread
+    constexpr int NS = M * D / 4 / 256;      // 4-float pieces of K~_e per thread
+    constexpr int NA = CHUNK * M / 4 / 256;  // 4-float pieces of the gates per thread
+    float qv[NQ][8], kv[NQ][8];
+    f32x4 sv[NS], av[NA];
+    const float* Ske = ws.Sk + (bh * ne + e) * M * D;
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) {
+      const int x = tid + 256 * u, r = x / (D / 8), col = (x % (D / 8)) * 8;
+      load8f<T>(q + (row0 + r) * D + col, qv[u]);
+      load8f<T>(k + (erow0 + r) * D + col, kv[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      const int x = tid + 256 * u, r = x / (D / 4), col = (x % (D / 4)) * 4;
+      sv[u] = *reinterpret_cast<const f32x4*>(Ske + r * D + col);
+    }
+#pragma unroll
+    for (int u = 0; u < NA; ++u) av[u] = *reinterpret_cast<const f32x4*>(gate + erow0 * M + 4 * (tid + 256 * u));
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) {
+      const int x = tid + 256 * u, r = x / (D / 8), col = (x % (D / 8)) * 8;
+      *reinterpret_cast<f32x4*>(Qs + r * DP + col) = f32x4{qv[u][0], qv[u][1], qv[u][2], qv[u][3]};
+      *reinterpret_cast<f32x4*>(Qs + r * DP + col + 4) = f32x4{qv[u][4], qv[u][5], qv[u][6], qv[u][7]};
+      *reinterpret_cast<f32x4*>(KC + (M + r) * DP + col) = f32x4{kv[u][0], kv[u][1], kv[u][2], kv[u][3]};
+      *reinterpret_cast<f32x4*>(KC + (M + r) * DP + col + 4) = f32x4{kv[u][4], kv[u][5], kv[u][6], kv[u][7]};
+    }
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      const int x = tid + 256 * u, r = x / (D / 4), col = (x % (D / 4)) * 4;
+      *reinterpret_cast<f32x4*>(KC + r * DP + col) = sv[u];
+    }
+#pragma unroll
+    for (int u = 0; u < NA; ++u) *reinterpret_cast<f32x4*>(A + 4 * (tid + 256 * u)) = av[u];
   }
-  const float* Ske = ws.Sk + (bh * ne + e) * M * D;
-  for (int x = tid; x < M * D / 4; x += 256) {
-    const int r = x / (D / 4), col = (x % (D / 4)) * 4;
-    *reinterpret_cast<f32x4*>(KC + r * DP + col) = *reinterpret_cast<const f32x4*>(Ske + r * D + col);
-  }
-  for (int x = tid; x < CHUNK * M; x += 256) A[x] = gate[erow0 * M + x];
   __syncthreads();
   // ---- X = Q [K~_e; K_e]^T (64 x NCOL): a 4 x (NCOL / 64) tile per thread
   {
@@ -189,39 +235,64 @@ __global__ void __launch_bounds__(256) k_nha_slots(const T* __restrict__ q, cons
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
-      for (int u = 0; u < CPT; ++u) XQ[(4 * rg + a) * NCOL + cg + 16 * u] = acc[a][u];
+      for (int u = 0; u < CPT; ++u) {
+        const int col = cg + 16 * u, j = 4 * rg + a;
+        if (u < M / 16) XS[j * M + col] = acc[a][u];
+        else QKT[(col - M) * CHUNK + j] = acc[a][u];
+      }
   }
   __syncthreads();
-  // ---- slot scores and one softmax over [slots, window] per query: groups
-  // of M lanes hold the M slots of one query
+  // ---- slot scores: lane group grp (M lanes, lane i = slot i) takes the
+  // JPG queries j = grp JPG .. and runs the slot key's recurrence over chunk
+  // e's tokens for all of them at once,
+  //   y_j(s) = a_s[i] y_j(s - 1) + (1 - a_s[i]) q_j.k_s,  y_j(-1) = q_j.K~_e[i],
+  // so z_j = q_j.K~ after token j = y_j(j); then one softmax per query over
+  // [slots, window] (the window through its lse)
   {
-    constexpr int NG = 256 / M;  // lane groups (queries in flight)
+    constexpr int NG = 256 / M, JPG = CHUNK / NG;  // JPG = M / 4 queries per group
     const int i = tid % M, grp = tid / M;
+    const int jb = grp * JPG;
     const int lane = lane_id();
-    for (int j = grp; j < CHUNK; j += NG) {
-      const float* xq = XQ + j * NCOL;
-      float term = 0.f, prod = 1.f;
-      for (int s = j; s >= 0; --s) {
-        const float a = A[s * M + i];
-        term = fmaf(prod * (1.f - a), xq[M + s], term);
-        prod *= a;
+    float y[JPG], z[JPG];
+#pragma unroll
+    for (int u = 0; u < JPG; ++u) y[u] = XS[(jb + u) * M + i];
+    for (int st = 0; st < jb; ++st) {  // tokens before the group's first query: every query takes them
+      const float a = A[st * M + i], b = 1.f - a;
+      const float* qk = QKT + st * CHUNK + jb;
+#pragma unroll
+      for (int u = 0; u < JPG; u += 4) {
+        const f32x4 v4 = *reinterpret_cast<const f32x4*>(qk + u);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) y[u + x] = fmaf(a, y[u + x], b * v4[x]);
       }
-      const float z = scale * fmaf(prod, xq[i], term);
+    }
+#pragma unroll
+    for (int u0 = 0; u0 < JPG; ++u0) {  // token jb + u0: queries jb + u0 .. take it, query jb + u0 is done
+      const int st = jb + u0;
+      const float a = A[st * M + i], b = 1.f - a;
+      const float* qk = QKT + st * CHUNK + jb;
+#pragma unroll
+      for (int u = u0; u < JPG; ++u) y[u] = fmaf(a, y[u], b * qk[u]);
+      z[u0] = y[u0];
+    }
+    // (each group writes only its own queries' rows of XS, after reading them)
+#pragma unroll
+    for (int u = 0; u < JPG; ++u) {
+      const int j = jb + u;
+      const float zz = scale * z[u];
       const float lw = lse_w ? lse_w[row0 + j] : -INFINITY;
-      float mx = z;
+      float mx = zz;
 #pragma unroll
       for (int msk = M / 2; msk >= 1; msk >>= 1) mx = fmaxf(mx, __shfl_xor(mx, msk, 64));
       mx = fmaxf(mx, lw);
-      const float p = __expf(z - mx);
+      const float p = __expf(zz - mx);
       float den = p;
 #pragma unroll
       for (int msk = M / 2; msk >= 1; msk >>= 1) den += __shfl_xor(den, msk, 64);
       const float pw = __expf(lw - mx);  // 0 for an empty window
       den += pw;
       const float inv = 1.f / den;
-      // written after every lane of the group has read X[j][i] above (the
-      // reads of row j happen in this iteration only, by this group only)
-      XQ[j * NCOL + i] = p * inv;
+      XS[j * M + i] = p * inv;
       if ((lane % M) == 0) WW[j] = pw * inv;
     }
   }
@@ -235,22 +306,36 @@ __global__ void __launch_bounds__(256) k_nha_slots(const T* __restrict__ q, cons
 #pragma unroll
     for (int u = 0; u < SPT; ++u) vt[u] = Sve[(int64_t)(part * SPT + u) * D];
     const T* vc = v + erow0 * D + d;
-    for (int j = 0; j < CHUNK; ++j) {
-      const float vj = to_f32(vc[(int64_t)j * D]);
-      const float* aj = A + j * M + part * SPT;
-      const float* pj = XQ + j * NCOL + part * SPT;
-      float acc = 0.f;
+    const float* owc = o_w ? o_w + row0 * D + d : nullptr;
+    // v and o_w of the next PF tokens in flight (unconditional loads at
+    // clamped rows, so that the compiler does not wait for each right away)
+    constexpr int PF = 8;
+    float vr[PF], owr[PF];
 #pragma unroll
-      for (int u = 0; u < SPT; ++u) {
-        const float a = aj[u];
-        vt[u] = fmaf(a, vt[u], (1.f - a) * vj);
-        acc = fmaf(pj[u], vt[u], acc);
-      }
+    for (int u = 0; u < PF; ++u) {
+      vr[u] = to_f32(vc[(int64_t)u * D]);
+      owr[u] = owc ? owc[(int64_t)u * D] : 0.f;
+    }
+    for (int j0 = 0; j0 < CHUNK; j0 += PF) {
 #pragma unroll
-      for (int msk = 1; msk < TPC; msk <<= 1) acc += __shfl_xor(acc, msk, 64);
-      if (part == 0) {
-        const float ow = o_w ? o_w[(row0 + j) * D + d] : 0.f;
-        out[(row0 + j) * D + d] = from_f32<To>(fmaf(WW[j], ow, acc));
+      for (int u = 0; u < PF; ++u) {
+        const int j = j0 + u;
+        const float vj = vr[u], ow = owr[u];
+        const int jn = min(j + PF, CHUNK - 1);
+        vr[u] = to_f32(vc[(int64_t)jn * D]);
+        if (owc) owr[u] = owc[(int64_t)jn * D];
+        const float* aj = A + j * M + part * SPT;
+        const float* pj = XS + j * M + part * SPT;
+        float acc = 0.f;
+#pragma unroll
+        for (int w = 0; w < SPT; ++w) {
+          const float a = aj[w];
+          vt[w] = fmaf(a, vt[w], (1.f - a) * vj);
+          acc = fmaf(pj[w], vt[w], acc);
+        }
+#pragma unroll
+        for (int msk = 1; msk < TPC; msk <<= 1) acc += __shfl_xor(acc, msk, 64);
+        if (part == 0) out[(row0 + j) * D + d] = from_f32<To>(fmaf(WW[j], ow, acc));
       }
     }
   }
@@ -293,7 +378,7 @@ hipError_t launch_nha_m(const T* q, const T* k, const T* v, const float* gate, i
   }
   const float* ow = nw > 0 ? o_w : nullptr;
   const float* lw = nw > 0 ? lse_w : nullptr;
-  const size_t lds = (size_t)(CHUNK * (D + 4) + (M + CHUNK) * (D + 4) + CHUNK * M + CHUNK * (M + CHUNK) + CHUNK) * 4;
+  const size_t lds = (size_t)(CHUNK * (D + 4) + (M + CHUNK) * (D + 4) + CHUNK * M + CHUNK * M + CHUNK * CHUNK + CHUNK) * 4;
 #define NHA_M(MM)                                                                                                  \
   do {                                                                                                             \
     if ((e = set_lds_limit((const void*)k_nha_slots<T, To, D, MM>, (int)lds)) != hipSuccess) return e;            \
