@@ -12,6 +12,11 @@
 // columns), sums in fp32 in a fixed order, stores the mean in LDS, and the
 // four waves form the 2G dot products with W_score (fixed-order wave
 // reductions), so the result is deterministic.
+//
+// Router gradient (straight-through; the pages leave the argmax's derivative
+// open): one pass over x that also writes dx (the chunk's score gradient
+// broadcast over its rows, fp32), then dW and db as fixed-order sums over
+// chunks.  Bandwidth-bound: 2 + 4 bytes per element of x (bf16 io).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -169,79 +174,167 @@ __global__ void __launch_bounds__(64) k_compact(const int32_t* __restrict__ rout
 // Every sum runs in a fixed order: deterministic.
 
 // ds [B, G, Nc, 2], one thread per (b, g, c)
-__global__ void __launch_bounds__(256) k_route_bwd_ds(const float* __restrict__ scores,
-                                                      const float* __restrict__ dg_sm,
-                                                      const float* __restrict__ dg_lin, int B, int H, int G, int nc,
-                                                      float* __restrict__ ds) {
-  const int64_t i = (int64_t)bid_x() * 256 + tid_x();
-  if (i >= (int64_t)B * G * nc) return;
-  const int c = (int)(i % nc), g = (int)((i / nc) % G), b = (int)(i / ((int64_t)nc * G));
-  const int hpg = H / G;
-  float dh0 = 0.f, dh1 = 0.f;
-  for (int h = g * hpg; h < (g + 1) * hpg; ++h) {
-    const int64_t j = ((int64_t)b * H + h) * nc + c;
-    dh0 += dg_sm[j];
-    dh1 += dg_lin[j];
-  }
-  const float s0 = scores[i * 2], s1 = scores[i * 2 + 1];
-  const float m = fmaxf(s0, s1);
-  const float e0 = __expf(s0 - m), e1 = __expf(s1 - m);
-  const float p0 = e0 / (e0 + e1), p1 = e1 / (e0 + e1);
-  const float pd = p0 * dh0 + p1 * dh1;
-  ds[i * 2] = p0 * (dh0 - pd);
-  ds[i * 2 + 1] = p1 * (dh1 - pd);
-}
-
-// per (b, c): the chunk mean of x (kept for dW) and dx of the chunk's rows
+// per (b, c, 2048-column slice): the straight-through step for the chunk's
+// score pairs, the chunk mean of x (kept for dW) and dx of the chunk's rows.
+// The gate derivatives of a group's heads are summed (dh), and ds = J^T dh
+// with J the Jacobian of the two-way softmax of the scores: ds_o = p_o (dh_o -
+// p . dh).  Each thread owns 8 columns (d_model is a multiple of 8): 16-byte
+// (bf16) or 2 x 16-byte (fp32) loads, eight rows in flight, each column
+// summed over the rows in order; dx of a chunk is one row (the mean's
+// gradient, d pooled / d x = 1/64) written to all 64 rows.
 template <typename T>
 __global__ void __launch_bounds__(256) k_route_bwd_x(const T* __restrict__ x, const float* __restrict__ w,
-                                                     const float* __restrict__ ds, int L, int d, int G, int nc,
-                                                     float* __restrict__ pooled, float* __restrict__ dx) {
-  const int c = bid_x(), b = bid_y();
-  const T* xc = x + ((int64_t)b * L + (int64_t)c * CHUNK) * d;
-  const float* dsc = ds + ((int64_t)b * G * nc + c) * 2;  // + (g nc) * 2 + o
-  for (int col = tid_x(); col < d; col += 256) {
-    float sx = 0.f;
-    for (int r = 0; r < CHUNK; ++r) sx += to_f32(xc[(int64_t)r * d + col]);
-    pooled[((int64_t)b * nc + c) * d + col] = sx * (1.0f / CHUNK);
-    if (dx) {
-      float gx = 0.f;
-      for (int g = 0; g < G; ++g)
-        gx += w[(int64_t)col * 2 * G + 2 * g] * dsc[(int64_t)g * nc * 2] +
-              w[(int64_t)col * 2 * G + 2 * g + 1] * dsc[(int64_t)g * nc * 2 + 1];
-      gx *= 1.0f / CHUNK;
-      float* dxc = dx + ((int64_t)b * L + (int64_t)c * CHUNK) * d + col;
-      for (int r = 0; r < CHUNK; ++r) dxc[(int64_t)r * d] = gx;
+                                                     const float* __restrict__ scores,
+                                                     const float* __restrict__ dg_sm,
+                                                     const float* __restrict__ dg_lin, int L, int d, int H, int G,
+                                                     int nc, float* __restrict__ ds, float* __restrict__ pooled,
+                                                     float* __restrict__ dx) {
+  extern __shared__ float s_ds[];  // [G][2]
+  const int c = bid_x(), b = bid_y(), z = (int)__builtin_amdgcn_workgroup_id_z();
+  const int col = (z * 256 + tid_x()) * 8;
+  // the gate sums' loads are issued first, the x rows' next; the barrier
+  // before dx waits for both
+  float dh[2] = {0.f, 0.f};
+  const int g_own = tid_x() < G ? tid_x() : -1;
+  if (g_own >= 0) {
+    const int hpg = H / G;
+    for (int h = g_own * hpg; h < (g_own + 1) * hpg; ++h) {
+      const int64_t j = ((int64_t)b * H + h) * nc + c;
+      dh[0] += dg_sm[j];
+      dh[1] += dg_lin[j];
     }
+  }
+  if (col < d) {
+    const T* xc = x + ((int64_t)b * L + (int64_t)c * CHUNK) * d + col;
+    float sx[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int r0 = 0; r0 < CHUNK; r0 += 8) {
+      Frag<T> raw[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) raw[u] = load8<T>(xc + (int64_t)(r0 + u) * d);
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sx[j] += to_f32(frag_get<T>(raw[u], j));
+    }
+    float4* pc4 = reinterpret_cast<float4*>(pooled + ((int64_t)b * nc + c) * d + col);
+    pc4[0] = make_float4(sx[0] * (1.0f / CHUNK), sx[1] * (1.0f / CHUNK), sx[2] * (1.0f / CHUNK),
+                         sx[3] * (1.0f / CHUNK));
+    pc4[1] = make_float4(sx[4] * (1.0f / CHUNK), sx[5] * (1.0f / CHUNK), sx[6] * (1.0f / CHUNK),
+                         sx[7] * (1.0f / CHUNK));
+  }
+  // G > 256 groups: the remaining ones in further passes (no x loads beside them)
+  for (int g = g_own >= 0 ? g_own : tid_x(); g < G; g += 256) {
+    if (g != g_own) {
+      dh[0] = dh[1] = 0.f;
+      const int hpg = H / G;
+      for (int h = g * hpg; h < (g + 1) * hpg; ++h) {
+        const int64_t j = ((int64_t)b * H + h) * nc + c;
+        dh[0] += dg_sm[j];
+        dh[1] += dg_lin[j];
+      }
+    }
+    const int64_t i = ((int64_t)b * G + g) * nc + c;
+    const float s0 = scores[i * 2], s1 = scores[i * 2 + 1];
+    const float m = fmaxf(s0, s1);
+    const float e0 = __expf(s0 - m), e1 = __expf(s1 - m);
+    const float p0 = e0 / (e0 + e1), p1 = e1 / (e0 + e1);
+    const float pd = p0 * dh[0] + p1 * dh[1];
+    const float d0 = p0 * (dh[0] - pd), d1 = p1 * (dh[1] - pd);
+    s_ds[2 * g] = d0;
+    s_ds[2 * g + 1] = d1;
+    if (z == 0) {
+      ds[i * 2] = d0;
+      ds[i * 2 + 1] = d1;
+    }
+  }
+  __syncthreads();
+  if (col >= d || !dx) return;
+  float gx[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float* wr = w + (int64_t)(col + j) * 2 * G;
+    float a = 0.f;
+    for (int g = 0; g < G; ++g) a += wr[2 * g] * s_ds[2 * g] + wr[2 * g + 1] * s_ds[2 * g + 1];
+    gx[j] = a * (1.0f / CHUNK);
+  }
+  const float4 g0 = make_float4(gx[0], gx[1], gx[2], gx[3]), g1 = make_float4(gx[4], gx[5], gx[6], gx[7]);
+  float* dxc = dx + ((int64_t)b * L + (int64_t)c * CHUNK) * d + col;
+#pragma unroll 8
+  for (int r = 0; r < CHUNK; ++r) {
+    float4* o = reinterpret_cast<float4*>(dxc + (int64_t)r * d);
+    o[0] = g0;
+    o[1] = g1;
   }
 }
 
-// dW [d, 2G] and db [2G]: one thread per output, the (b, c) sum in order
+// dW [d, 2G] = sum over (b, c) of pooled[b, c, :] x ds[b, g, c, :]: the
+// (b, c) range split into RB_SLICES interleaved slices (grid z), one thread
+// per (column, group), each slice's sum in order of (b, c); the slices are
+// then added in order by k_route_bwd_w_final, so the result is deterministic.
+constexpr int RB_SLICES = 16;
 __global__ void __launch_bounds__(256) k_route_bwd_w(const float* __restrict__ pooled, const float* __restrict__ ds,
-                                                     int B, int G, int nc, int d, float* __restrict__ dw,
-                                                     float* __restrict__ db) {
-  const int64_t i = (int64_t)bid_x() * 256 + tid_x();
-  const int64_t nw = (int64_t)d * 2 * G;
-  if (i < nw) {
-    const int col = (int)(i / (2 * G)), o = (int)(i % (2 * G)), g = o / 2, oo = o % 2;
-    float acc = 0.f;
-    for (int b = 0; b < B; ++b)
-      for (int c = 0; c < nc; ++c)
-        acc += pooled[((int64_t)b * nc + c) * d + col] * ds[(((int64_t)b * G + g) * nc + c) * 2 + oo];
-    dw[i] = acc;
-  } else if (db && i < nw + 2 * G) {
-    const int o = (int)(i - nw), g = o / 2, oo = o % 2;
-    float acc = 0.f;
-    for (int b = 0; b < B; ++b)
-      for (int c = 0; c < nc; ++c) acc += ds[(((int64_t)b * G + g) * nc + c) * 2 + oo];
-    db[o] = acc;
+                                                     int B, int G, int nc, int d, float* __restrict__ part) {
+  const int col = bid_x() * 256 + tid_x(), g = bid_y(), s = (int)__builtin_amdgcn_workgroup_id_z();
+  if (col >= d) return;
+  const int nbc = B * nc;
+  float a0 = 0.f, a1 = 0.f;
+  int bc = s;
+  for (; bc + 7 * RB_SLICES < nbc; bc += 8 * RB_SLICES) {
+    float p[8];
+    float2 q[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = bc + u * RB_SLICES, bb = i / nc, c = i - bb * nc;
+      p[u] = pooled[(int64_t)i * d + col];
+      q[u] = *reinterpret_cast<const float2*>(ds + (((int64_t)bb * G + g) * nc + c) * 2);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      a0 += p[u] * q[u].x;
+      a1 += p[u] * q[u].y;
+    }
   }
+  for (; bc < nbc; bc += RB_SLICES) {
+    const int bb = bc / nc, c = bc - bb * nc;
+    const float p = pooled[(int64_t)bc * d + col];
+    a0 += p * ds[(((int64_t)bb * G + g) * nc + c) * 2];
+    a1 += p * ds[(((int64_t)bb * G + g) * nc + c) * 2 + 1];
+  }
+  part[((int64_t)s * 2 * G + 2 * g) * d + col] = a0;
+  part[((int64_t)s * 2 * G + 2 * g + 1) * d + col] = a1;
+}
+
+// the slices' partial dW added in slice order (blocks below nbw); db [2G] as
+// the (b, c) sum of ds, one wave per output: lane-strided sums, then a
+// fixed-order wave reduction
+__global__ void __launch_bounds__(256) k_route_bwd_w_final(const float* __restrict__ part,
+                                                           const float* __restrict__ ds, int B, int G, int nc, int d,
+                                                           int nbw, float* __restrict__ dw, float* __restrict__ db) {
+  if (bid_x() < nbw) {
+    const int64_t i = (int64_t)bid_x() * 256 + tid_x();
+    if (i >= (int64_t)d * 2 * G) return;
+    const int col = (int)(i / (2 * G)), o = (int)(i % (2 * G));
+    float acc = 0.f;
+    for (int s = 0; s < RB_SLICES; ++s) acc += part[((int64_t)s * 2 * G + o) * d + col];
+    dw[i] = acc;
+    return;
+  }
+  const int o = (bid_x() - nbw) * 4 + wave_id();
+  if (o >= 2 * G) return;
+  const int g = o / 2, oo = o % 2;
+  float acc = 0.f;
+  for (int bc = lane_id(); bc < B * nc; bc += 64) {
+    const int bb = bc / nc, c = bc - bb * nc;
+    acc += ds[(((int64_t)bb * G + g) * nc + c) * 2 + oo];
+  }
+  acc = wave_sum64(acc);
+  if (lane_id() == 0) db[o] = acc;
 }
 
 size_t route_bwd_ws_bytes(int B, int G, int L, int d) {
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   const size_t nc = (size_t)L / CHUNK;
-  return al((size_t)B * G * nc * 2 * 4) + al((size_t)B * nc * d * 4);
+  return al((size_t)B * G * nc * 2 * 4) + al((size_t)B * nc * d * 4) + al((size_t)RB_SLICES * 2 * G * d * 4);
 }
 
 template <typename T>
@@ -252,15 +345,17 @@ hipError_t launch_route_backward(const T* x, const float* w, const float* scores
   const int nc = L / CHUNK;
   float* ds = (float*)wsp;
   float* pooled = (float*)((char*)wsp + al((size_t)B * G * nc * 2 * 4));
-  const int64_t n = (int64_t)B * G * nc;
-  hipLaunchKernelGGL(k_route_bwd_ds, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, scores, dg_sm, dg_lin, B,
-                     H, G, nc, ds);
+  float* part = (float*)((char*)pooled + al((size_t)B * nc * d * 4));
+  hipLaunchKernelGGL(k_route_bwd_x<T>, dim3(nc, B, (d + 2047) / 2048), dim3(256), (size_t)G * 2 * sizeof(float), st,
+                     x, w, scores, dg_sm, dg_lin, L, d, H, G, nc, ds, pooled, dx);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_route_bwd_x<T>, dim3(nc, B), dim3(256), 0, st, x, w, ds, L, d, G, nc, pooled, dx);
+  hipLaunchKernelGGL(k_route_bwd_w, dim3((d + 255) / 256, G, RB_SLICES), dim3(256), 0, st, pooled, ds, B, G, nc, d,
+                     part);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int64_t nt = (int64_t)d * 2 * G + 2 * G;
-  hipLaunchKernelGGL(k_route_bwd_w, dim3((unsigned)((nt + 255) / 256)), dim3(256), 0, st, pooled, ds, B, G, nc, d,
+  const int nbw = (int)(((int64_t)d * 2 * G + 255) / 256);
+  const int nbb = db ? (2 * G + 3) / 4 : 0;
+  hipLaunchKernelGGL(k_route_bwd_w_final, dim3((unsigned)(nbw + nbb)), dim3(256), 0, st, part, ds, B, G, nc, d, nbw,
                      dw, db);
   return hipGetLastError();
 }
