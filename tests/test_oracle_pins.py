@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import oracle as O
-from tests.chunkwise_model import gdn_chunkwise
+from tests.chunkwise_model import gdn_chunkwise, gdn_chunkwise_backward
 
 RNG = np.random.default_rng(1234)
 
@@ -266,6 +266,30 @@ def test_chunkwise_algebra_matches_oracle():
     oc, Sc = gdn_chunkwise(q, k, v, a, b, r, S_init=S0)
     np.testing.assert_allclose(oc, o, atol=1e-11)
     np.testing.assert_allclose(Sc, S, atol=1e-11)
+
+
+def test_chunkwise_gradient_algebra_matches_oracle():
+    """The chunkwise gradient the kernels use (the chunk form's derivative,
+    chunk by chunk in reverse: a backward state scan over chunks, then every
+    chunk's token gradients from its start state and the carried gradient)
+    reproduces the oracle's per-token reverse sweep, gate derivatives
+    included (mixed routes, nonzero initial state and final-state gradient)."""
+    r = np.random.default_rng(41)
+    B, H, L, D = 1, 2, 320, 8
+    q = r.standard_normal((B, H, L, D))
+    k = r.standard_normal((B, H, L, D))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = r.standard_normal((B, H, L, D))
+    a = r.uniform(0.8, 1.0, (B, H, L))
+    b = 1 / (1 + np.exp(-r.standard_normal((B, H, L))))
+    route = np.array([[[1, 0, 1, 1, 0]]], np.int32)
+    d_o = r.standard_normal((B, H, L, D))
+    S0 = r.standard_normal((B, H, D, D)) * 0.3
+    dSf = r.standard_normal((B, H, D, D))
+    ref = O.gdn_branch_backward(q, k, v, a, b, route, d_o, S_init=S0, dS_final=dSf, with_gate=True)
+    got = gdn_chunkwise_backward(q, k, v, a, b, route, d_o, S_init=S0, dS_final=dSf)
+    for name, x, y in zip(("dq", "dk", "dv", "dalpha", "dbeta", "dS_init", "dgate"), got, ref):
+        np.testing.assert_allclose(x, y, atol=1e-11 * max(1.0, np.abs(y).max()), err_msg=name)
 
 
 # ----------------------------------------------------------------- merge ----
