@@ -245,13 +245,16 @@ def time_route_gradient(N, dm, t, wl, reps=3):
                      "matrix cores for the pairs the forward skipped")
 
 
-def time_gdn_backward(N, dm, t, wl, route, reps=2):
+def time_gdn_backward(N, dm, t, wl, route, reps=3):
     """Gradient of the Gated DeltaNet branch on this workload (a random fp32
-    upstream gradient on o_gdn), timed with events.  Plain fp32 VALU work, so
-    it is set against the fp32 vector peak; algorithmic work 16 D^2 FLOP per
-    token for the reverse step (outer product, two column and two row
-    contractions, the decay gradient, the erase of G), not counting the two
-    forward recomputations the per-token form also runs."""
+    upstream gradient on o_gdn), timed with events.  Chunk form on the matrix
+    cores; its matrix products per chunk-head (C = 64 tokens) are 36 C^2 D +
+    16 C D^2 + 4 C^3 FLOP: the forward prep (K K^T, Q K^T, U~, W), the state
+    scan (W S, K~^T U), the backward prep (K K^T, Q K^T, W), the reverse scan
+    (K Gc, P^T dO, Q^T dO, W^T dU) and the chunk gradients (A, P, dP, dO S0^T,
+    U Gc^T, TdU S0^T, T^T dU, A U, dT, T^T dT T^T, E K, E^T K, F K, F^T Q).
+    Two of its five launches are sequential over the 512 chunks, so it is
+    latency-bound, not set against a roofline."""
     import torch
     d_o = torch.randn(t["q"].shape, dtype=torch.float32, device=t["q"].device)
     N.gdn_backward(dm, t["q"], t["k"], t["v"], t["alpha"], t["beta"], route, d_o)
@@ -263,11 +266,13 @@ def time_gdn_backward(N, dm, t, wl, route, reps=2):
     e1.record()
     torch.cuda.synchronize()
     us = 1000.0 * e0.elapsed_time(e1) / reps
-    flops = 16 * wl.D * wl.D * wl.B * wl.H * wl.L
+    C, D = 64, wl.D
+    flops = (36 * C * C * D + 16 * C * D * D + 4 * C ** 3) * wl.B * wl.H * (wl.L // C)
     tf = flops / (us * 1e-6) / 1e12
-    return dict(workload=f"gradient of the Gated DeltaNet branch on the {wl.name} prefill (per-token form)",
-                us=round(us, 1), flops=flops, tflops=round(tf, 2), bound="alu",
-                frac_fp32_valu=round(tf / PEAK_FP32_VALU_TFLOPS, 4))
+    ws = N.workspace_size(N.ENTRY_GDN_BACKWARD, dm)
+    return dict(workload=f"gradient of the Gated DeltaNet branch on the {wl.name} prefill (chunk form)",
+                us=round(us, 1), flops=flops, tflops=round(tf, 1), frac_bf16_mfma=round(tf / PEAK_BF16_TFLOPS, 4),
+                workspace_bytes=int(ws), note="latency-bound: two sequential sweeps over the chunks")
 
 
 def time_merge_backward(N, dm, t, wl, reps=5):

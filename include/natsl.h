@@ -200,14 +200,15 @@ natsl_status natsl_softmax_masked_backward(const natsl_dims* dims, const void* q
  * pages define the forward, Kernmechanismen 3; this is its exact derivative).
  * The forward is natsl_gdn_chunk's: S_t = alpha_t (S_{t-1} - beta_t k_t k_t^T
  * S_{t-1}) + beta_t k_t v_t^T, o_t = S_t^T q_t, and a chunk keeps its end state
- * only when linear-routed.  Taken token by token in reverse: G += q_t d_o_t^T,
- * dq_t = S_t d_o_t, w = G^T k_t, dv_t = beta_t w, dbeta_t = w.(v_t - alpha_t
- * S_{t-1}^T k_t), dalpha_t = <G, S_{t-1} - beta_t k_t k_t^T S_{t-1}>, dk_t =
- * beta_t G v_t - alpha_t beta_t (G S_{t-1}^T k_t + S_{t-1} w), G <- alpha_t
- * (G - beta_t k_t w^T); the carried state's gradient enters a linear chunk's
- * last token and skips a softmax chunk to its start.
+ * only when linear-routed.  Taken in chunk form: with the chunk form U = T
+ * (diag(beta) V - diag(beta gamma) K S0), O = diag(gamma) Q S0 + P U, S_end =
+ * gamma_C S0 + K~^T U, the carried state's gradient Gc runs backward over the
+ * chunks (Gc <- [linear ? gamma_C : 1] Gc + Q^T diag(gamma) dO - W^T dU, dU =
+ * P^T dO + [linear] K~ Gc), then each chunk's token gradients follow from its
+ * start state S0, U, Gc and dU through T, A, P and the decays.
  *   q, k, v        [B, H, L, D] io dtype, alpha, beta [B, H, L] fp32, route
- *                  [B, G, Nc] int32 (0 softmax, 1 linear): the forward's inputs
+ *                  [B, G, Nc] int32 (0 softmax, 1 linear): the forward's inputs;
+ *                  alpha in (0, 1] (d alpha is d log alpha / alpha)
  *   S_init         [B, H, Dk, Dv] fp32 initial state, or NULL (zeros)
  *   d_o            [B, H, L, Dv] fp32: gradient of the loss w.r.t. o_gdn
  *   dS_final       [B, H, Dk, Dv] fp32 gradient w.r.t. the final carried state,
@@ -218,12 +219,14 @@ natsl_status natsl_softmax_masked_backward(const natsl_dims* dims, const void* q
  *                  chunk's linear gate (see natsl_route_backward; the carried
  *                  state after chunk c written S_start + h (S_end - S_start)):
  *                  <d loss / d carried state after c, S_end - S_start>
- *   ws             workspace of natsl_workspace_size(NATSL_ENTRY_GDN_BACKWARD)
- * Every output is written, not accumulated.  This is the per-token form (one
- * wave per group of 4 state columns at D = 128, 8 at D = 64; a checkpoint
- * pass, a per-chunk recompute and reverse sweep, then a fixed-order reduction
- * of the groups' partials, so results are deterministic): latency-bound, not
- * the chunkwise matrix form.
+ *   ws             workspace of natsl_workspace_size(NATSL_ENTRY_GDN_BACKWARD):
+ *                  the chunk preps, and every chunk's S0, U and Gc in the io
+ *                  dtype (about 1.35 GB for B = 1, H = 16, L = 32768, D = 128
+ *                  bf16)
+ * Every output is written, not accumulated; results are deterministic.  The
+ * matrix products take io-dtype operands (bf16 for bf16 io) with fp32
+ * accumulation.  The bf16 D = 128 form has natsl_gdn_chunk's sequence-length
+ * limit (NATSL_ERR_UNSUPPORTED before anything is enqueued).
  */
 natsl_status natsl_gdn_backward(const natsl_dims* dims, const void* q, const void* k, const void* v,
                                 const float* alpha, const float* beta, const int32_t* route, const float* S_init,

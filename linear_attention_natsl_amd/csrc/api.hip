@@ -381,7 +381,8 @@ natsl_status natsl_workspace_size(int entry, const natsl_dims* dims, size_t* byt
       return ok();
     case NATSL_ENTRY_GDN_BACKWARD:
       CHECK(check_dims(dims, true, false));
-      *bytes = gdn_bwd_ws_bytes(dims->B, dims->H, dims->L, dims->Dk);
+      CHECK(check_gdn_len(dims));
+      *bytes = gdn_bwd_ws_bytes(dims->io == NATSL_BF16, dims->B, dims->H, dims->L, dims->Dk);
       return ok();
     case NATSL_ENTRY_MERGE_BACKWARD:
       CHECK(check_dims(dims, true, false));
@@ -711,7 +712,8 @@ natsl_status natsl_gdn_backward(const natsl_dims* dims, const void* q, const voi
   NEED(dv, "dv");
   NEED(dalpha, "dalpha");
   NEED(dbeta, "dbeta");
-  CHECK(check_ws(ws, ws_bytes, gdn_bwd_ws_bytes(dims->B, dims->H, dims->L, dims->Dk)));
+  CHECK(check_gdn_len(dims));
+  CHECK(check_ws(ws, ws_bytes, gdn_bwd_ws_bytes(dims->io == NATSL_BF16, dims->B, dims->H, dims->L, dims->Dk)));
   const int B = dims->B, H = dims->H, L = dims->L, G = dims->route_groups;
   hipError_t e;
   auto prof = prof_fn();

@@ -38,43 +38,10 @@
 //               chunk is computed (the barriers order LDS only, so those loads
 //               stay in flight across them).
 #include "common.hpp"
+#include "gdn_common.hpp"
 #include "kernels.hpp"
 
 namespace natsl {
-
-template <typename T, int D>
-struct GdnCfg {
-  static constexpr int KP = D + 16 / (int)sizeof(T);   // row-layout pitch (elements)
-  static constexpr int PP = CHUNK + 16 / (int)sizeof(T);
-  static constexpr int LTP = CHUNK + 1;                 // fp32 pitch of L / T
-  static constexpr int KF = D / 32;
-  static constexpr int NT = D / 16;                     // 16-wide column tiles of D
-  // LDS layout of the prep kernel (bytes).  The bf16, D = 128 form (the one
-  // the head-form scan reads) keeps the K rows, the inverse's block scratch
-  // and the K / V key-group copies in one region, live one after the other
-  // (K and V wait in registers until the inverse is done), so that three
-  // workgroups fit in a CU's 160 KiB instead of two.
-  static constexpr bool ALIAS = sizeof(T) == 2 && D == 128;
-  static constexpr int RL = kg_row<T, D>();             // padded key-group row (columns)
-  static constexpr int KS_BYTES = CHUNK * KP * (int)sizeof(T);
-  static constexpr int KG_BYTES = 16 * RL * 4 * (int)sizeof(T);
-  static constexpr int RS_BYTES = 3 * 16 * 17 * 4;
-  static constexpr int OFF_KS = 0;
-  static constexpr int OFF_KG = ALIAS ? 0 : OFF_KS + KS_BYTES;
-  static constexpr int OFF_VG = OFF_KG + KG_BYTES;
-  static constexpr int R0_END = ALIAS ? (KS_BYTES > 2 * KG_BYTES ? KS_BYTES : 2 * KG_BYTES) : OFF_VG + KG_BYTES;
-  static constexpr int OFF_LT = R0_END;
-  static constexpr int OFF_RS = ALIAS ? 0 : OFF_LT + CHUNK * LTP * 4;
-  static constexpr int OFF_GL = ALIAS ? OFF_LT + CHUNK * LTP * 4 : OFF_RS + RS_BYTES;
-  static constexpr int PREP_LDS = OFF_GL + 3 * CHUNK * 4;
-  static_assert(!ALIAS || 3 * PREP_LDS <= 160 * 1024, "three prep workgroups per CU");
-  // per chunk-head workspace (elements)
-  static constexpr int64_t WN = (int64_t)CHUNK * D;   // T
-  static constexpr int64_t UT = (int64_t)CHUNK * D;   // float
-  static constexpr int64_t KT = (int64_t)D * CHUNK;   // T
-  static constexpr int64_t PM = 2 * (int64_t)CHUNK * CHUNK;  // T: hi and lo parts
-  static constexpr int64_t GM = 144;  // float: gamma[64], gamma_C at 64, exp(g_C - g)[64] at 80
-};
 
 size_t gdn_ws_bytes(int io_is_bf16, int D, int64_t nch) {
   const size_t ts = io_is_bf16 ? 2 : 4;
@@ -82,59 +49,6 @@ size_t gdn_ws_bytes(int io_is_bf16, int D, int64_t nch) {
                      2 * (size_t)CHUNK * CHUNK * ts + 144 * 4;
   return per * (size_t)nch + 5 * 256;
 }
-
-template <typename T, int D>
-struct GdnWs {
-  T* wn;
-  float* ut;
-  T* kt;
-  T* pm;
-  float* gm;
-};
-
-template <typename T, int D>
-static GdnWs<T, D> carve(void* ws, int64_t nch) {
-  using C = GdnCfg<T, D>;
-  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  char* p = (char*)ws;
-  GdnWs<T, D> w;
-  w.wn = (T*)p; p += al(C::WN * nch * sizeof(T));
-  w.ut = (float*)p; p += al(C::UT * nch * sizeof(float));
-  w.kt = (T*)p; p += al(C::KT * nch * sizeof(T));
-  w.pm = (T*)p; p += al(C::PM * nch * sizeof(T));
-  w.gm = (float*)p;
-  return w;
-}
-
-template <typename T> __device__ __forceinline__ Frag<T> ld4x2(const T* p0, const T* p1);
-template <> __device__ __forceinline__ Frag<bf16> ld4x2<bf16>(const bf16* p0, const bf16* p1) {
-  bf16x4 a = *reinterpret_cast<const bf16x4*>(p0);
-  bf16x4 b = *reinterpret_cast<const bf16x4*>(p1);
-  Frag<bf16> f;
-  f.v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-  return f;
-}
-template <> __device__ __forceinline__ Frag<float> ld4x2<float>(const float* p0, const float* p1) {
-  f32x4 a = *reinterpret_cast<const f32x4*>(p0);
-  f32x4 b = *reinterpret_cast<const f32x4*>(p1);
-  Frag<float> f;
-  f.v[0] = a[0]; f.v[1] = a[1]; f.v[2] = a[2]; f.v[3] = a[3];
-  f.v[4] = b[0]; f.v[5] = b[1]; f.v[6] = b[2]; f.v[7] = b[3];
-  return f;
-}
-template <typename T> __device__ __forceinline__ void st4(T* p, float a, float b, float c, float d);
-template <> __device__ __forceinline__ void st4<bf16>(bf16* p, float a, float b, float c, float d) {
-  bf16x4 v = {(bf16)a, (bf16)b, (bf16)c, (bf16)d};
-  *reinterpret_cast<bf16x4*>(p) = v;
-}
-template <> __device__ __forceinline__ void st4<float>(float* p, float a, float b, float c, float d) {
-  f32x4 v = {a, b, c, d};
-  *reinterpret_cast<f32x4*>(p) = v;
-}
-
-// The scan runs one workgroup per head for bf16 with D = 128, and one per
-// (head, 32-column slice) otherwise; the two read -W in different orders.
-template <typename T, int D> constexpr bool scan_head_form() { return sizeof(T) == 2 && D == 128; }
 
 // ---------------------------------------------------------------- prep ----
 template <typename T, int D>
@@ -277,69 +191,7 @@ __global__ void __launch_bounds__(256, (GdnCfg<T, D>::ALIAS ? 3 : 2))
   }
   __syncthreads();
 
-  // T = (I + L)^-1, in place.  (a) 16x16 diagonal blocks: lane j of wave w
-  // solves column j of block w by forward substitution.
-  if (lane < 16) {
-    const int j = lane, o = 16 * w;
-    float x[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float acc = (r == j) ? 1.f : 0.f;
-#pragma unroll
-      for (int i = 0; i < r; ++i) acc -= LT[(o + r) * C::LTP + o + i] * x[i];
-      x[r] = acc;
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) LT[(o + r) * C::LTP + o + j] = x[r];
-  }
-  __syncthreads();
-  // (b) block rows a = 1..3:  T_ab = -T_aa * sum_{b<=m<a} L_am T_mb, on fp32
-  // MFMA (16x16x4: in step j lane (g, c) gives A[c][4j + g] and B[4j + g][c],
-  // and holds C[4g + i][c]).  Wave w owns the target block (a, w) of every
-  // round a > w.  All L_am and T_aa fragments a wave needs are read before the
-  // first round writes, so a round's writes (which replace L_ab by T_ab) never
-  // race with reads of the blocks they replace: one barrier per round.
-  {
-    float la[3][3][4], ta[3][4];
-#pragma unroll
-    for (int a = 1; a < 4; ++a) {
-      if (w < a) {
-#pragma unroll
-        for (int m = 0; m < 3; ++m)
-          if (m >= w && m < a) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) la[a - 1][m][j] = LT[(16 * a + c) * C::LTP + 16 * m + 4 * j + g];
-          }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) ta[a - 1][j] = LT[(16 * a + c) * C::LTP + 16 * a + 4 * j + g];
-      }
-    }
-    float* Rw = Rs + w * 16 * 17;  // wave-private 16 x 16 scratch (waves 0..2)
-#pragma unroll
-    for (int a = 1; a < 4; ++a) {
-      if (w < a) {
-        f32x4 r = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int m = 0; m < 3; ++m)
-          if (m >= w && m < a) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              r = __builtin_amdgcn_mfma_f32_16x16x4f32(la[a - 1][m][j], LT[(16 * m + 4 * j + g) * C::LTP + 16 * w + c],
-                                                       r, 0, 0, 0);
-          }
-        // R (accumulator layout) -> B operand layout through the wave's scratch
-#pragma unroll
-        for (int i = 0; i < 4; ++i) Rw[(4 * g + i) * 17 + c] = r[i];
-        f32x4 tt = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          tt = __builtin_amdgcn_mfma_f32_16x16x4f32(ta[a - 1][j], Rw[(4 * j + g) * 17 + c], tt, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) LT[(16 * a + 4 * g + i) * C::LTP + 16 * w + c] = -tt[i];
-      }
-      __syncthreads();
-    }
-  }
+  lt_inverse64<C::LTP>(LT, Rs);
 
   if constexpr (C::ALIAS) {  // the inverse's scratch is dead (barrier above)
     store_kv_groups();
@@ -488,11 +340,15 @@ __device__ __forceinline__ void scan_load(ScanOps<T, D, DVT>& op, const GdnWs<T,
 // prefetch of NS - 1 chunks ahead stays in flight across chunks.
 constexpr int OUT_RING = 8;
 
-template <typename T, typename To, int D, int DVT, int NS>
+// State mode (ST, for the gradient): the outputs are replaced by the chunks'
+// U = U~ - W S (through the same ring into o_gdn), and every chunk's start
+// state is written to s0_out ([B, H, Nc, D, D] in T, row-major); the output
+// products are skipped.
+template <typename T, typename To, int D, int DVT, int NS, bool ST>
 __global__ void __launch_bounds__(256, 1)
     k_gdn_scan(const T* __restrict__ q, const int32_t* __restrict__ route, GdnWs<T, D> ws,
                const float* __restrict__ S_init, To* __restrict__ o_gdn, float* __restrict__ S_final,
-               int H, int L, int G) {
+               T* __restrict__ s0_out, int H, int L, int G) {
   using O = ScanOps<T, D, DVT>;
   constexpr int SPP = D + 16 / (int)sizeof(T);  // pitch of the transposed bf16 state [dv][dk]
   __shared__ __align__(16) T Sp[2][DVT * SPP];
@@ -549,6 +405,17 @@ __global__ void __launch_bounds__(256, 1)
   // so every prefetched operand is consumed unconditionally (a use inside a
   // branch lets the compiler sink the load into it, defeating the prefetch).
   auto step = [&](const ScanOps<T, D, DVT>& op, int cc) {
+    if constexpr (ST) {
+#pragma unroll
+      for (int x = 0; x < O::DTW; ++x)
+#pragma unroll
+        for (int n = 0; n < O::NV; ++n)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int dk = 16 * (w * O::DTW + x) + 4 * g + i;
+            s0_out[((bh * nc + cc) * D + dk) * D + dv0 + 16 * n + c] = from_f32<T>(sm[x][n][i]);
+          }
+    }
     // S fragments (B operand, contraction over d): shared by U and Q S
     Frag<T> bs[O::KF][O::NV];
 #pragma unroll
@@ -566,7 +433,7 @@ __global__ void __launch_bounds__(256, 1)
 #pragma unroll
       for (int n = 0; n < O::NV; ++n) {
         mma(u[n], op.wn[ks], bs[ks][n]);   // U = U~ - W S
-        mma(oa[n], op.qa[ks], bs[ks][n]);  // Q S
+        if constexpr (!ST) mma(oa[n], op.qa[ks], bs[ks][n]);  // Q S
       }
     const bool lin = op.route == 1;
     const float gce = lin ? op.gC : 1.f;
@@ -594,14 +461,17 @@ __global__ void __launch_bounds__(256, 1)
     for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
       for (int n = 0; n < O::NV; ++n) {
-        mma(oa[n], op.pa[k2][0], bu[k2][n]);  // + P U
-        if (SPLIT) mma(oa[n], op.pa[k2][1], bu[k2][n]);
+        if constexpr (!ST) {
+          mma(oa[n], op.pa[k2][0], bu[k2][n]);  // + P U
+          if (SPLIT) mma(oa[n], op.pa[k2][1], bu[k2][n]);
+        }
       }
     To* ob = Ob + (cc % OUT_RING) * CHUNK * DVT;
 #pragma unroll
     for (int n = 0; n < O::NV; ++n)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ob[(16 * w + 4 * g + i) * DVT + 16 * n + c] = from_f32<To>(oa[n][i]);
+      for (int i = 0; i < 4; ++i)
+        ob[(16 * w + 4 * g + i) * DVT + 16 * n + c] = from_f32<To>(ST ? u[n][i] : oa[n][i]);
     // S <- gamma_C S + K^T diag(exp(g_C - g)) U   (linear-routed), else S unchanged
 #pragma unroll
     for (int x = 0; x < O::DTW; ++x)
@@ -724,12 +594,16 @@ __device__ __forceinline__ Frag<bf16> pack_acc2(const f32x4& a, const f32x4& b) 
 // compiler keeps the matrix products in their VGPR form: with 512 registers it
 // moves the accumulators to AGPRs and copies them back and forth for every
 // VALU touch of the state)
-template <typename To, int NW, int NSPLIT>
+// State mode (ST, for the gradient): the outputs are replaced by the chunks'
+// U = U~ - W S (written where o_gdn would go, [B, H, L, D] bf16), and every
+// chunk's start state is written to s0_out ([B, H, Nc, D, D] bf16, row-major);
+// the output products are skipped.
+template <typename To, int NW, int NSPLIT, bool ST>
 __global__ void __launch_bounds__(64 * NW, 8 / NW)
     k_gdn_scan_head(const bf16* __restrict__ q, const bf16* __restrict__ k, const int32_t* __restrict__ route,
                     GdnWs<bf16, 128> ws,
                     const float* __restrict__ S_init, To* __restrict__ o_gdn, float* __restrict__ S_final,
-                    int H, int L, int G) {
+                    bf16* __restrict__ s0_out, int H, int L, int G) {
   constexpr int D = 128;
   constexpr int NV = D / (16 * NW * NSPLIT);  // 16-column state tiles per wave
   static_assert(NV >= 1 && NW >= 4, "the Q swizzle assumes 4 KiB-aligned load groups");
@@ -836,7 +710,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW)
   };
   // DMA operations a wave issues per part
   constexpr int N_W = NB, N_Q = NB, N_U = 4 * NV, N_P = NB / 2 + 1, N_KT = NB;
-  static_assert(N_W + N_Q + N_U + N_P + N_KT + 16 * NV < 64, "vmcnt range");
+  static_assert(N_W + N_Q + N_U + N_P + N_KT + 16 * NV + (ST ? 16 * NV : 0) < 64, "vmcnt range");
   // outputs: a uniform base per store plus one 32-bit byte offset per lane
   // (the SGPR-base store form; 64-bit lane addresses per store cost registers)
   const uint32_t o_boff = (uint32_t)((4 * g * D + dv0 + c) * sizeof(To));
@@ -851,6 +725,29 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW)
               reinterpret_cast<unsigned char*>(oh + (int64_t)cc * CHUNK * D + (16 * rt + i) * D + 16 * nn);
           *reinterpret_cast<To*>(base + o_boff) = from_f32<To>(o[rt][nn][i]);
         }
+  };
+  // state mode: the chunk-start state, bf16 row-major, two columns per
+  // 4-byte store (lanes c and c ^ 1 trade values: the even lane writes rows
+  // 4g and 4g + 2, the odd one rows 4g + 1 and 4g + 3)
+  const bool codd = (c & 1) != 0;
+  const uint32_t s_boff = (uint32_t)((((4 * g + (codd ? 1 : 0)) * D) + (c & ~1)) * 2);
+  auto store_state = [&](int cc) {
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int nn = 0; nn < NV; ++nn) {
+        const f32x4 x = sm[dt][nn];
+        const float r0 = __int_as_float(
+            __builtin_amdgcn_mov_dpp(__float_as_int(codd ? x[0] : x[1]), 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
+        const float r1 = __int_as_float(
+            __builtin_amdgcn_mov_dpp(__float_as_int(codd ? x[2] : x[3]), 0xB1, 0xF, 0xF, false));
+        const bf16x2 a = codd ? bf16x2{(bf16)r0, (bf16)x[1]} : bf16x2{(bf16)x[0], (bf16)r0};
+        const bf16x2 b2 = codd ? bf16x2{(bf16)r1, (bf16)x[3]} : bf16x2{(bf16)x[2], (bf16)r1};
+        unsigned char* base = reinterpret_cast<unsigned char*>(
+            s0_out + (((int64_t)bh * nc + cc) * D + 16 * dt) * D + dv0 + 16 * nn);
+        *reinterpret_cast<bf16x2*>(base + s_boff) = a;
+        *reinterpret_cast<bf16x2*>(base + s_boff + 2 * D * 2) = b2;
+      }
   };
   // Operand fragments from LDS are read ahead of the products that use them
   // (two (row tile, d step) steps ahead for -W and Q, two d tiles ahead for
@@ -909,7 +806,8 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW)
 #pragma unroll
       for (int nn = 0; nn < NV; ++nn)
         u[rt][nn] = *reinterpret_cast<const f32x4*>(sb + SCH_UT + ((rt * NV * NW + NV * w + nn) * 64 + lane) * 16);
-    if (cc > 0) store_o(cc - 1, o_prev);  // outputs of chunk cc - 1
+    if (cc > 0) store_o(cc - 1, o_prev);  // outputs of chunk cc - 1 (state mode: its U)
+    if constexpr (ST) store_state(cc);
     const bool more = cc + 1 < nc;
     if (more) load_part(cc + 1, st ^ 1, 0);
     const float* gm = reinterpret_cast<const float*>(sb + SCH_GM);
@@ -945,7 +843,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW)
 #pragma unroll
       for (int nn = 0; nn < NV; ++nn) {
         mma(u[rt][nn], fw[s_ % 3], bs[ks][nn]);
-        mma(o[rt][nn], fq[s_ % 3], bs[ks][nn]);
+        if constexpr (!ST) mma(o[rt][nn], fq[s_ % 3], bs[ks][nn]);
       }
       fence();
     }
@@ -973,7 +871,12 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW)
     for (int rt = 0; rt < 4; ++rt) {
       const f32x4 gam = *reinterpret_cast<const f32x4*>(gm + 16 * rt + 4 * g);
 #pragma unroll
-      for (int nn = 0; nn < NV; ++nn) o[rt][nn] *= gam;
+      for (int nn = 0; nn < NV; ++nn) {
+        if constexpr (ST)
+          o[rt][nn] = u[rt][nn];
+        else
+          o[rt][nn] *= gam;
+      }
     }
     // O += P U, two row tiles per group
     Frag<bf16> fk[3][2];
@@ -996,7 +899,8 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW)
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
-          for (int nn = 0; nn < NV; ++nn) mma(o[2 * gp + t][nn], fp[gp].p[t][k2], bu[k2][nn]);
+          for (int nn = 0; nn < NV; ++nn)
+            if constexpr (!ST) mma(o[2 * gp + t][nn], fp[gp].p[t][k2], bu[k2][nn]);
       fence();
     }
     // S <- gamma_C S + K^T diag(exp(g_C - g)) U, four d tiles per group
@@ -1062,7 +966,7 @@ hipError_t launch_gdn(const T* q, const T* k, const T* v, const float* alpha, co
   hipError_t e = set_lds_limit((const void*)k_gdn_prep<T, D>, C::PREP_LDS);
   if (e != hipSuccess) return e;
   if constexpr (scan_head_form<T, D>()) {
-    e = set_lds_limit((const void*)k_gdn_scan_head<To, SCH_NW, SCH_NSPLIT>, SCH_ROUTE + SCH_MAX_NC);
+    e = set_lds_limit((const void*)k_gdn_scan_head<To, SCH_NW, SCH_NSPLIT, false>, SCH_ROUTE + SCH_MAX_NC);
     if (e != hipSuccess) return e;
   }
   const int64_t nch = (int64_t)B * H * nc;
@@ -1086,19 +990,63 @@ hipError_t launch_gdn(const T* q, const T* k, const T* v, const float* alpha, co
   if (prof) prof(KID_GDN_SCAN, st_scan, 0);
   if constexpr (scan_head_form<T, D>()) {
     const size_t lds = SCH_ROUTE + ((size_t)nc + 15) / 16 * 16;
-    hipLaunchKernelGGL((k_gdn_scan_head<To, SCH_NW, SCH_NSPLIT>), dim3((unsigned)(B * H * SCH_NSPLIT)), dim3(64 * SCH_NW),
-                       lds, st_scan,
-                       (const bf16*)q, (const bf16*)k,
-                       route, ws, S_init, o_gdn, S_final, H, L, G);
+    hipLaunchKernelGGL((k_gdn_scan_head<To, SCH_NW, SCH_NSPLIT, false>), dim3((unsigned)(B * H * SCH_NSPLIT)),
+                       dim3(64 * SCH_NW), lds, st_scan, (const bf16*)q, (const bf16*)k, route, ws, S_init, o_gdn,
+                       S_final, (bf16*)nullptr, H, L, G);
   } else {
-    hipLaunchKernelGGL((k_gdn_scan<T, To, D, DVT, SCAN_NS>), dim3((unsigned)(B * H * (D / DVT))), dim3(256), 0,
-                       st_scan, q, route, ws, S_init, o_gdn, S_final, H, L, G);
+    hipLaunchKernelGGL((k_gdn_scan<T, To, D, DVT, SCAN_NS, false>), dim3((unsigned)(B * H * (D / DVT))), dim3(256),
+                       0, st_scan, q, route, ws, S_init, o_gdn, S_final, (T*)nullptr, H, L, G);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (prof) prof(KID_GDN_SCAN, st_scan, 1);
   return hipSuccess;
 }
+
+// The forward in state mode, for the gradient: the chunk prep, then the scan
+// writing every chunk's start state (s0, [B, H, Nc, D, D] in T) and U (u,
+// [B, H, L, D] in T) instead of the outputs; one stream.
+template <typename T, int D>
+hipError_t launch_gdn_states(const T* q, const T* k, const T* v, const float* alpha, const float* beta,
+                             const int32_t* route, const float* S_init, T* s0, T* u, void* wsp, int B, int H, int L,
+                             int G, hipStream_t st) {
+  using C = GdnCfg<T, D>;
+  constexpr int DVT = 32;
+  constexpr int SCAN_NS = sizeof(T) == 2 ? 4 : 2;
+  const int nc = L / CHUNK;
+  if (nc > gdn_max_chunks(sizeof(T) == 2, D)) return hipErrorInvalidValue;
+  hipError_t e = set_lds_limit((const void*)k_gdn_prep<T, D>, C::PREP_LDS);
+  if (e != hipSuccess) return e;
+  const int64_t nch = (int64_t)B * H * nc;
+  GdnWs<T, D> ws = carve<T, D>(wsp, nch);
+  hipLaunchKernelGGL((k_gdn_prep<T, D>), dim3((unsigned)nch), dim3(256), C::PREP_LDS, st, q, k, v, alpha, beta, ws,
+                     L);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if constexpr (scan_head_form<T, D>()) {
+    e = set_lds_limit((const void*)k_gdn_scan_head<bf16, SCH_NW, SCH_NSPLIT, true>, SCH_ROUTE + SCH_MAX_NC);
+    if (e != hipSuccess) return e;
+    const size_t lds = SCH_ROUTE + ((size_t)nc + 15) / 16 * 16;
+    hipLaunchKernelGGL((k_gdn_scan_head<bf16, SCH_NW, SCH_NSPLIT, true>), dim3((unsigned)(B * H * SCH_NSPLIT)),
+                       dim3(64 * SCH_NW), lds, st, (const bf16*)q, (const bf16*)k, route, ws, S_init, (bf16*)u,
+                       (float*)nullptr, (bf16*)s0, H, L, G);
+  } else {
+    hipLaunchKernelGGL((k_gdn_scan<T, T, D, DVT, SCAN_NS, true>), dim3((unsigned)(B * H * (D / DVT))), dim3(256), 0,
+                       st, q, route, ws, S_init, u, (float*)nullptr, s0, H, L, G);
+  }
+  return hipGetLastError();
+}
+template hipError_t launch_gdn_states<float, 64>(const float*, const float*, const float*, const float*, const float*,
+                                                 const int32_t*, const float*, float*, float*, void*, int, int, int,
+                                                 int, hipStream_t);
+template hipError_t launch_gdn_states<float, 128>(const float*, const float*, const float*, const float*,
+                                                  const float*, const int32_t*, const float*, float*, float*, void*,
+                                                  int, int, int, int, hipStream_t);
+template hipError_t launch_gdn_states<bf16, 64>(const bf16*, const bf16*, const bf16*, const float*, const float*,
+                                                const int32_t*, const float*, bf16*, bf16*, void*, int, int, int, int,
+                                                hipStream_t);
+template hipError_t launch_gdn_states<bf16, 128>(const bf16*, const bf16*, const bf16*, const float*, const float*,
+                                                 const int32_t*, const float*, bf16*, bf16*, void*, int, int, int,
+                                                 int, hipStream_t);
 
 int gdn_max_chunks(int io_is_bf16, int D) {
   return (io_is_bf16 && D == 128) ? SCH_MAX_NC : (1 << 30);

@@ -1,441 +1,938 @@
-// Gradient of the Gated DeltaNet branch through the per-chunk rollback.
+// Gradient of the Gated DeltaNet branch through the per-chunk rollback, in
+// chunk form on the matrix cores.
 //
 // "Technische Samenvatting: Neural Attention Search Linear (NAtS-L)",
 // Kernmechanismen 3 defines the forward: every chunk pseudo-updates the state
-// token by token and keeps its end state only when it is routed to the linear
-// operation (otherwise the chunk-start state is restored).  This is the exact
-// derivative of that forward, taken token by token in reverse.  With
-// G = d loss / d S_t (key-major [Dk, Dv]) and S = S_{t-1}, a = S^T k_t:
-//   G += q_t do_t^T;  dq_t = S_t do_t;  w = G^T k_t;  dv_t = b_t w
-//   dbeta_t = w . (v_t - a_t a);  dalpha_t = <G, S - b_t k_t a^T>
-//   dk_t = b_t G v_t - a_t b_t (G a + S w);  G <- a_t (G - b_t k_t w^T)
-// The carried state's gradient enters a chunk's last token when the chunk is
-// linear-routed; otherwise it passes straight to the chunk start and the
-// chunk's tokens see only their own outputs' gradients.
+// and keeps its end state only when it is routed to the linear operation
+// (otherwise the chunk-start state is restored).  In chunk form (gdn.hip),
+// for a chunk with start state S0:
+//   U = T (diag(b) V - diag(b gamma) K S0),  O = diag(gamma) Q S0 + P U,
+//   S_end = gamma_C S0 + K~^T U,  K~ = diag(exp(g_C - g)) K.
+// This file takes the exact derivative of that form, chunk by chunk in
+// reverse.  With Gc = d loss / d carried state after chunk c and dSe = Gc for
+// a linear-routed chunk (its end state is committed), 0 otherwise:
+//   dU  = P^T dO + K~ dSe
+//   Gc' = gamma_C dSe + Q^T diag(gamma) dO - W^T dU  (+ Gc if not committed)
+// (W = T diag(b gamma) K) is a reverse recurrence over chunks whose columns
+// evolve independently, like the forward's state.  Given every chunk's S0, U,
+// Gc and dU, the token gradients of a chunk are local to it:
+//   dP = tril(dO U^T), F = dP * Gamma;  dQ = diag(gamma) dO S0^T + F K
+//   TdU = T^T dU;  dV = diag(b) TdU;  TdW = -TdU S0^T
+//   VmR = U + diag(b) A U  (= diag(b) V - diag(b gamma) K S0)
+//   dT = dU VmR^T;  dM = strict_tril(-T^T dT T^T);  E = diag(b) dM * Gamma
+//   dK = diag(b gamma) TdW + E K + E^T K + F^T Q + [committed] diag(e) U Gc^T
+// plus the per-token beta and log-decay gradients (row and column sums of the
+// same products), the decay gradient reverse-summed into d log alpha, and
+// the linear gate's derivative <Gc, S_end - S0> = (gamma_C - 1) <Gc, S0> +
+// sum_s e_s k_s . (U Gc^T)_s.  (A = strict_tril(Gamma . K K^T), Gamma[t][s]
+// = exp(g_t - g_s), g the in-chunk cumulative log decay.)
 //
-// The columns of S (and of G) evolve independently, so each head's CW-column
-// groups (4 at D = 128, 8 at D = 64) run in workgroups of their own: one wave
-// each.  Lane (jl, rg) holds the RPT = D CW / 64 rows rg RPT .. of column
-// CW cg + jl, so the column sums (S^T k, G^T k) stay in registers (DPP rotates
-// and two row swaps) and a token needs no barrier.  The row sums (dq, dk) are
-// reduced over the CW lanes of a row group by a reduce-scatter that leaves each lane a contiguous run of
-// rows (one vector store per token); they and the scalar gradients (dalpha,
-// dbeta) are per-group partials, added over the groups in a fixed order by a
-// last kernel (so the result does not depend on scheduling).  Launches:
-//   k_gdn_bwd_ckpt    the forward, storing every chunk's starting (carried) state
-//   k_gdn_bwd         chunks in reverse: recompute the chunk's per-token states
-//                     into a scratch slot, then sweep its tokens backward
-//   k_gdn_bwd_reduce  dq, dk, dalpha, dbeta from the groups' partials
-// Each lane reads its own rows of k and q and its column of v and d_o from
-// global memory a few tokens ahead through a ring of registers (the sweep
-// reads its scratch states the same way); alpha and beta come from one load
-// per chunk (lane s holds token s) and a lane broadcast.  The scratch holds
-// each lane's rows contiguously, moved as 16-byte vectors.  This is the plain
-// per-token form (the chunkwise form on MFMA is not built).
+// Launches (one stream):
+//   k_gdn_prep + scan    the forward in state mode (gdn.hip): every chunk's
+//                        S0 and U, bf16 or fp32 as the io dtype
+//   k_gdn_bwd_prep       one workgroup per chunk-head: T, and the fragment
+//                        copies of P^T, -W^T and Q^T the reverse scan reads
+//   k_gdn_bwd_scan       one workgroup per (head, 32-column slice), chunks in
+//                        reverse: Gc and dU of every chunk, and dS_init
+//   k_gdn_bwd_chunk      one workgroup per chunk-head: dq, dk, dv, dalpha,
+//                        dbeta and the gate derivative
+// The backward prep's outputs reuse the forward prep's workspace, which is
+// dead once the state scan is done.
 #include "common.hpp"
+#include "gdn_common.hpp"
 #include "kernels.hpp"
 
 namespace natsl {
 
-constexpr int kRouteLinear = 1;  // route id of the linear (Gated DeltaNet) operation
+constexpr int BWD_DVT = 32;  // state columns per reverse-scan workgroup
+constexpr int GM_FLOATS = 144;  // gamma[64], gamma_C at 64, exp(g_C - g)[64] at 80
 
-template <int D>
-struct GdnBwdCfg {
-  static constexpr int CW = D == 128 ? 4 : 8;  // state columns per workgroup (a lane's rows fill 16-byte words)
-  static constexpr int NCG = D / CW;       // column groups (workgroups) per head
-  static constexpr int NT = 64;            // one wave: CW columns x 64 / CW row groups
-  static constexpr int RPT = D * CW / NT;  // state rows per thread
-  static constexpr int PF = 16;            // forward tokens of inputs in flight (ring depth)
-  static constexpr int PFB = 8;            // the same for the backward sweep (inputs and S_{t-1})
-  static_assert((CW == 4 || CW == 8) && RPT % 8 == 0 && CHUNK % PF == 0 && CHUNK % PFB == 0,
-                "4 or 8 columns, whole row vectors");
+template <typename T, int D>
+struct GdnBwdWs {
+  T* pt;      // [nch][4 rs][2 k2][64][8]  P^T A fragments (rows s, contraction t, accumulator-shaped map)
+  T* wtn;     // [nch][D/16][2 k2][64][8]  -W^T A fragments (rows d, contraction s)
+  T* qt;      // [nch][D/16][2 k2][64][8]  Q^T A fragments (rows d, contraction t)
+  float* tm;  // [nch][64][64]             T = (I + diag(b) A)^-1
+  float* gm;  // [nch][GM_FLOATS]
+  T* du;      // [B, H, L, D]              dU of every chunk
 };
 
-size_t gdn_bwd_ws_bytes(int B, int H, int L, int D) {
-  const size_t nc = (size_t)L / CHUNK, ntok = (size_t)B * H * L, ncg = (size_t)(D == 128 ? GdnBwdCfg<128>::NCG : GdnBwdCfg<64>::NCG);
-  const size_t floats = (size_t)B * H * (nc + CHUNK) * D * D  // chunk-start states, chunk token states
-                        + 2 * ntok * ncg * D                  // dq, dk partials
-                        + 2 * ntok * ncg                      // dalpha, dbeta partials
-                        + (size_t)B * H * ncg * nc;           // linear-gate partials
-  return (floats * 4 + 255) / 256 * 256;
-}
+static inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// sum over the wave's row groups of a per-thread partial for the thread's
-// column (the lanes l + CW i of each 16-lane row by DPP rotates, the 4 rows by
-// row swaps); every lane receives its column's total
-template <int CW>
-__device__ __forceinline__ float col_sum(float x) {
-  if (CW == 4) x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x124, 0xF, 0xF, true));  // row_ror 4
-  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, true));  // row_ror 8
-  return group4_sum(x);
-}
-
-// One reduce-scatter step over lane pairs given by a DPP pattern: of the N
-// values, the lane keeps the lower half (keep_lo) or the upper half, adds the
-// partner's copy of that half, and leaves the result in v[0 .. N/2).
-template <int N, int CTRL>
-__device__ __forceinline__ void rs_step(float* v, bool keep_lo) {
-#pragma unroll
-  for (int k = 0; k < N / 2; ++k) {
-    const float send = keep_lo ? v[k + N / 2] : v[k];
-    const float keep = keep_lo ? v[k] : v[k + N / 2];
-    v[k] = keep + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send), CTRL, 0xF, 0xF, true));
-  }
-}
-// Sum of each of the N values over the CW lanes of a row group (lanes jl =
-// 0..CW-1, CW-aligned); lane jl is left with the sums of values jl N/CW ..
-// (jl + 1) N/CW - 1 in v[0 .. N/CW).  The pairings are l <-> 7 - l (CW = 8),
-// l <-> l ^ 2, l <-> l ^ 1, which together span the CW lanes.
-template <int CW, int N>
-__device__ __forceinline__ void group_reduce_scatter(float* v, int jl) {
-  static_assert(N % CW == 0, "whole values per lane");
-  if constexpr (CW == 8) {
-    rs_step<N, 0x141>(v, (jl & 4) == 0);     // row_half_mirror
-    rs_step<N / 2, 0x4E>(v, (jl & 2) == 0);  // quad_perm 2,3,0,1
-    rs_step<N / 4, 0xB1>(v, (jl & 1) == 0);  // quad_perm 1,0,3,2
-  } else {
-    rs_step<N, 0x4E>(v, (jl & 2) == 0);
-    rs_step<N / 2, 0xB1>(v, (jl & 1) == 0);
-  }
-}
-
-// alpha or beta of token c0 + s, from the chunk's values held one per lane
-__device__ __forceinline__ float lane_bcast(float x, int s) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), s));
-}
-
-// A token's inputs as one lane needs them: k (and q) at its RPT rows, v (and
-// d_o) at its column, kept as loaded (raw 16-byte words) so that a load in
-// the ring is not waited for until the token is reached; widened by tok_f32.
-template <typename T, int RPT>
-struct TokRaw {
-  static constexpr int NW = RPT * (int)sizeof(T) / 16;  // 16-byte words of the lane's rows
-  uint4 k[NW], q[NW];
-  T v;
-  float d_o;
-};
-template <int RPT>
-struct TokIn {
-  float k[RPT], q[RPT];
-  float v, d_o;
-};
-template <typename T, int D, bool BWD>
-__device__ __forceinline__ void load_tok(TokRaw<T, GdnBwdCfg<D>::RPT>& x, const T* kh, const T* qh, const T* vh,
-                                         const float* doh, int tt, int r0, int j) {
-  constexpr int NW = TokRaw<T, GdnBwdCfg<D>::RPT>::NW;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    x.k[w] = *(const uint4*)(kh + (int64_t)tt * D + r0 + w * (16 / (int)sizeof(T)));
-    if (BWD) x.q[w] = *(const uint4*)(qh + (int64_t)tt * D + r0 + w * (16 / (int)sizeof(T)));
-  }
-  x.v = vh[(int64_t)tt * D + j];
-  x.d_o = BWD ? doh[(int64_t)tt * D + j] : 0.f;
-}
-// element i of a run of raw 16-byte words holding T values
-template <typename T>
-__device__ __forceinline__ float raw_f32(const uint4* w, int i) {
-  constexpr int E = 16 / (int)sizeof(T);  // elements per word
-  const uint4 x = w[i / E];
-  const int c = (i % E) * (int)sizeof(T) / 4;  // 32-bit component
-  const uint32_t u = c == 0 ? x.x : c == 1 ? x.y : c == 2 ? x.z : x.w;
-  if constexpr (sizeof(T) == 2) return __uint_as_float((i & 1) ? (u & 0xffff0000u) : (u << 16));  // bf16 -> fp32
-  else return __uint_as_float(u);
-}
-template <typename T, int RPT, bool BWD>
-__device__ __forceinline__ TokIn<RPT> tok_f32(const TokRaw<T, RPT>& r) {
-  TokIn<RPT> x;
-#pragma unroll
-  for (int i = 0; i < RPT; ++i) {
-    x.k[i] = raw_f32<T>(r.k, i);
-    x.q[i] = BWD ? raw_f32<T>(r.q, i) : 0.f;
-  }
-  x.v = to_f32(r.v);
-  x.d_o = r.d_o;
-  return x;
-}
-
-// the thread's RPT state elements, contiguous in the scratch (16-byte aligned)
-template <int RPT>
-__device__ __forceinline__ void store_state(float* p, const float (&S)[RPT]) {
-#pragma unroll
-  for (int h = 0; h < RPT; h += 4) *(float4*)(p + h) = make_float4(S[h], S[h + 1], S[h + 2], S[h + 3]);
-}
-template <int RPT>
-__device__ __forceinline__ void load_state(float (&S)[RPT], const float* p) {
-#pragma unroll
-  for (int h = 0; h < RPT; h += 4) {
-    const float4 x = *(const float4*)(p + h);
-    S[h] = x.x;
-    S[h + 1] = x.y;
-    S[h + 2] = x.z;
-    S[h + 3] = x.w;
-  }
-}
-
-// one forward token on the thread's elements: a = S^T k (column sums), then
-// S <- al (S - be k a^T) + be k v^T
-template <int D>
-__device__ __forceinline__ void gdn_fwd_token(float (&S)[GdnBwdCfg<D>::RPT], const TokIn<GdnBwdCfg<D>::RPT>& x,
-                                              float al, float be) {
-  constexpr int RPT = GdnBwdCfg<D>::RPT;
-  float p4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int i = 0; i < RPT; ++i) p4[i & 3] += S[i] * x.k[i];
-  const float a = col_sum<GdnBwdCfg<D>::CW>((p4[0] + p4[1]) + (p4[2] + p4[3]));
-#pragma unroll
-  for (int i = 0; i < RPT; ++i) S[i] = al * (S[i] - be * x.k[i] * a) + be * x.k[i] * x.v;
+template <typename T, int D>
+static size_t bwd_region_bytes(int64_t nch) {
+  const size_t n = (size_t)nch;
+  return al256(n * CHUNK * CHUNK * sizeof(T)) + 2 * al256(n * CHUNK * D * sizeof(T)) +
+         al256(n * CHUNK * CHUNK * 4) + al256(n * GM_FLOATS * 4) + al256(n * CHUNK * D * sizeof(T));
 }
 
 template <typename T, int D>
-__global__ void __launch_bounds__(64) k_gdn_bwd_ckpt(const T* __restrict__ k, const T* __restrict__ v,
-                                                      const float* __restrict__ alpha, const float* __restrict__ beta,
-                                                      const int32_t* __restrict__ route,
-                                                      const float* __restrict__ S_init, float* __restrict__ ckpt,
-                                                      int H, int L, int G) {
-  using C = GdnBwdCfg<D>;
+static GdnBwdWs<T, D> carve_bwd(void* ws, int64_t nch) {
+  const size_t n = (size_t)nch;
+  char* p = (char*)ws;
+  GdnBwdWs<T, D> w;
+  w.pt = (T*)p;  p += al256(n * CHUNK * CHUNK * sizeof(T));
+  w.wtn = (T*)p; p += al256(n * CHUNK * D * sizeof(T));
+  w.qt = (T*)p;  p += al256(n * CHUNK * D * sizeof(T));
+  w.tm = (float*)p; p += al256(n * CHUNK * CHUNK * 4);
+  w.gm = (float*)p; p += al256(n * GM_FLOATS * 4);
+  w.du = (T*)p;
+  return w;
+}
+
+// workspace: [forward prep / backward prep region][S0 per chunk][U][Gc per chunk]
+template <typename T, int D>
+static size_t region_bytes(int64_t nch) {
+  const size_t f = al256(gdn_ws_bytes(sizeof(T) == 2, D, nch)), b = al256(bwd_region_bytes<T, D>(nch));
+  return f > b ? f : b;
+}
+
+size_t gdn_bwd_ws_bytes(int io_is_bf16, int B, int H, int L, int D) {
+  const int64_t nch = (int64_t)B * H * (L / CHUNK);
+  const size_t ts = io_is_bf16 ? 2 : 4;
+  size_t r;
+  if (io_is_bf16) r = D == 64 ? region_bytes<bf16, 64>(nch) : region_bytes<bf16, 128>(nch);
+  else r = D == 64 ? region_bytes<float, 64>(nch) : region_bytes<float, 128>(nch);
+  return r + 2 * al256((size_t)nch * D * D * ts) + al256((size_t)nch * CHUNK * D * ts);
+}
+
+// ------------------------------------------------------------ backward prep
+template <typename T, int D>
+struct BwdPrepCfg {
+  static constexpr int RL = kg_row<T, D>();
+  static constexpr int KG_BYTES = 16 * RL * 4 * (int)sizeof(T);
+  static constexpr int LTP = CHUNK + 1;
+  static constexpr int OFF_KG = 0, OFF_QG = KG_BYTES, OFF_LT = 2 * KG_BYTES;
+  static constexpr int OFF_RS = OFF_LT + CHUNK * LTP * 4;
+  static constexpr int OFF_GL = OFF_RS + 3 * 16 * 17 * 4;
+  static constexpr int LDS = OFF_GL + 3 * CHUNK * 4;
+  static constexpr int KF = D / 32, NT = D / 16;
+};
+
+// One workgroup per chunk-head: the per-token decays, L = diag(b) A and its
+// inverse T (as the forward prep), P, and W = T diag(b gamma) K.  P^T and
+// -W^T leave in the accumulator-shaped fragment order (row = s or d,
+// contraction over tokens): wave w holds rows 16w + 4g + i of P and W, which
+// are elements 4 (w & 1) + i of the fragments of token block w >> 1.
+template <typename T, int D>
+__global__ void __launch_bounds__(256) k_gdn_bwd_prep(const T* __restrict__ q, const T* __restrict__ k,
+                                                      const float* __restrict__ alpha,
+                                                      const float* __restrict__ beta, GdnBwdWs<T, D> bw, int L) {
+  using C = BwdPrepCfg<T, D>;
+  extern __shared__ __align__(16) unsigned char lds[];
+  T* Kg = (T*)(lds + C::OFF_KG);
+  T* Qg = (T*)(lds + C::OFF_QG);
+  float* LT = (float*)(lds + C::OFF_LT);
+  float* Rs = (float*)(lds + C::OFF_RS);
+  float* gl = (float*)(lds + C::OFF_GL);  // cumulative log2 decay
+  float* bl = gl + CHUNK;                 // beta
+  float* gbl = bl + CHUNK;                // beta * gamma
   const int nc = L / CHUNK;
-  const int bh = bid_x() / C::NCG, cg = bid_x() % C::NCG, b = bh / H, h = bh % H;
-  const int grp = (G == 1) ? 0 : h;
-  const int32_t* rt = route + ((int64_t)b * G + grp) * nc;
-  const int t = tid_x(), jl = t % C::CW, rg = t / C::CW, lane = t;
-  const int j = C::CW * cg + jl, r0 = rg * C::RPT;
-  const T* kh = k + (int64_t)bh * L * D;
-  const T* vh = v + (int64_t)bh * L * D;
-  const float* ah = alpha + (int64_t)bh * L;
-  const float* bth = beta + (int64_t)bh * L;
-  float* ck = ckpt + (int64_t)bh * nc * D * D;
-  float S[C::RPT], carry[C::RPT];
+  const int64_t ch = bid_x();
+  const int64_t bh = ch / nc;
+  const int cc = (int)(ch % nc);
+  const int64_t tok0 = bh * L + (int64_t)cc * CHUNK;
+  const int t = tid_x(), lane = lane_id(), w = wave_id();
+  const int g = lane >> 4, c = lane & 15;
+
+  constexpr int TASKS = (CHUNK / 4) * (D / 8);
+  static_assert(TASKS <= 256, "one task per thread");
+  const int kg = t / (D / 8), col = (t % (D / 8)) * 8;
+  Frag<T> kr[4], qr[4];
+  if (t < TASKS) {
 #pragma unroll
-  for (int i = 0; i < C::RPT; ++i) {
-    S[i] = S_init ? S_init[((int64_t)bh * D + r0 + i) * D + j] : 0.f;
-    carry[i] = S[i];
+    for (int i = 0; i < 4; ++i) {
+      kr[i] = load8<T>(k + (tok0 + 4 * kg + i) * D + col);
+      qr[i] = load8<T>(q + (tok0 + 4 * kg + i) * D + col);
+    }
   }
-  TokRaw<T, C::RPT> ring[C::PF];  // slot u: the token tt with tt % PF == u, PF tokens ahead
+  Frag<T> ka[C::KF], qa[C::KF];
 #pragma unroll
-  for (int u = 0; u < C::PF; ++u) load_tok<T, D, false>(ring[u], kh, kh, vh, nullptr, u, r0, j);  // L >= 64
-  for (int c = 0; c < nc; ++c) {
-    const float al_c = ah[c * CHUNK + lane], be_c = bth[c * CHUNK + lane];  // lane s: token c0 + s
+  for (int ks = 0; ks < C::KF; ++ks) {
+    ka[ks] = load8<T>(k + (tok0 + 16 * w + c) * D + 32 * ks + 8 * g);
+    qa[ks] = load8<T>(q + (tok0 + 16 * w + c) * D + 32 * ks + 8 * g);
+  }
+  if (w == 0) {
+    const float a = alpha[tok0 + lane];
+    const float bt = beta[tok0 + lane];
+    float s = __builtin_amdgcn_logf(a);
 #pragma unroll
-    for (int i = 0; i < C::RPT; ++i) ck[((int64_t)c * D + r0 + i) * D + j] = carry[i];
-    for (int s0 = 0; s0 < CHUNK; s0 += C::PF) {
-#pragma unroll
-      for (int u = 0; u < C::PF; ++u) {
-        const int s = s0 + u, tt = c * CHUNK + s;
-        const TokIn<C::RPT> cur = tok_f32<T, C::RPT, false>(ring[u]);
-        // (unconditional, clamped to the last token: a branch around the load
-        // would make the compiler wait for it at the join)
-        load_tok<T, D, false>(ring[u], kh, kh, vh, nullptr, min(tt + C::PF, L - 1), r0, j);
-        gdn_fwd_token<D>(S, cur, lane_bcast(al_c, s), lane_bcast(be_c, s));
-      }
+    for (int off = 1; off < 64; off <<= 1) {
+      const float o = __shfl_up(s, off, 64);
+      if (lane >= off) s += o;
     }
-    const bool lin = rt[c] == kRouteLinear;
+    const float gC = __shfl(s, 63, 64);
+    gl[lane] = s;
+    bl[lane] = bt;
+    gbl[lane] = bt * __builtin_amdgcn_exp2f(s);
+    bw.gm[ch * GM_FLOATS + lane] = __builtin_amdgcn_exp2f(s);
+    bw.gm[ch * GM_FLOATS + 80 + lane] = __builtin_amdgcn_exp2f(gC - s);
+    if (lane == 0) bw.gm[ch * GM_FLOATS + 64] = __builtin_amdgcn_exp2f(gC);
+  }
+  if (t < TASKS) {
 #pragma unroll
-    for (int i = 0; i < C::RPT; ++i) {
-      if (lin) carry[i] = S[i];
-      else S[i] = carry[i];
+    for (int j = 0; j < 8; ++j) {
+      st4<T>(Kg + kg_index<C::RL>(kg, col + j), to_f32(frag_get<T>(kr[0], j)), to_f32(frag_get<T>(kr[1], j)),
+             to_f32(frag_get<T>(kr[2], j)), to_f32(frag_get<T>(kr[3], j)));
+      st4<T>(Qg + kg_index<C::RL>(kg, col + j), to_f32(frag_get<T>(qr[0], j)), to_f32(frag_get<T>(qr[1], j)),
+             to_f32(frag_get<T>(qr[2], j)), to_f32(frag_get<T>(qr[3], j)));
     }
+  }
+  __syncthreads();
+
+  // K K^T and Q K^T, rows 16w .. 16w+15 (B: key rows 16ct + c)
+  f32x4 akk[4], apq[4];
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) {
+    akk[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    apq[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int ks = 0; ks < C::KF; ++ks)
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      const Frag<T> bk = load8<T>(k + (tok0 + 16 * ct + c) * D + 32 * ks + 8 * g);
+      mma(akk[ct], ka[ks], bk);
+      mma(apq[ct], qa[ks], bk);
+    }
+  const int hb = w & 1, kb = w >> 1;
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) {
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * w + 4 * g + i, s = 16 * ct + c;
+      const float gm_ = __builtin_amdgcn_exp2f(gl[r] - gl[s]);
+      LT[r * C::LTP + s] = (s < r) ? bl[r] * gm_ * akk[ct][i] : 0.f;
+      p[i] = (s <= r) ? gm_ * apq[ct][i] : 0.f;
+    }
+    st4<T>(bw.pt + ((ch * 4 + ct) * 2 + kb) * 512 + lane * 8 + hb * 4, p[0], p[1], p[2], p[3]);
+  }
+  __syncthreads();
+  lt_inverse64<C::LTP>(LT, Rs);
+  for (int e = t; e < CHUNK * CHUNK; e += 256) bw.tm[ch * CHUNK * CHUNK + e] = LT[(e >> 6) * C::LTP + (e & 63)];
+
+  // W = T diag(b gamma) K, rows 16w .. 16w+15 (T split into bf16 hi + lo)
+  constexpr bool SPLIT = sizeof(T) == 2;
+  f32x4 wa[C::NT];
+#pragma unroll
+  for (int n = 0; n < C::NT; ++n) wa[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k2 = 0; k2 < 2; ++k2) {
+    Frag<T> a2, a2l;
+    const float* trow = LT + (16 * w + c) * C::LTP;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int tk = 32 * k2 + kmap_acc(g, j);
+      const float x2 = trow[tk] * gbl[tk];
+      frag_set(a2, j, x2);
+      frag_set(a2l, j, x2 - to_f32(frag_get<T>(a2, j)));
+    }
+#pragma unroll
+    for (int n = 0; n < C::NT; ++n) {
+      const Frag<T> bk = ld4x2<T>(Kg + kg_index<C::RL>(8 * k2 + g, 16 * n + c),
+                                  Kg + kg_index<C::RL>(8 * k2 + 4 + g, 16 * n + c));
+      mma(wa[n], a2, bk);
+      if (SPLIT) mma(wa[n], a2l, bk);
+    }
+  }
+#pragma unroll
+  for (int n = 0; n < C::NT; ++n)
+    st4<T>(bw.wtn + ((ch * C::NT + n) * 2 + kb) * 512 + lane * 8 + hb * 4, -wa[n][0], -wa[n][1], -wa[n][2],
+           -wa[n][3]);
+  // Q^T fragments (rows d, tokens in the accumulator-shaped map)
+  for (int f = w; f < C::NT * 2; f += 4) {
+    const int n = f >> 1, k2 = f & 1;
+    store8<T>(bw.qt + ((ch * C::NT + n) * 2 + k2) * 512 + lane * 8,
+              ld4x2<T>(Qg + kg_index<C::RL>(8 * k2 + g, 16 * n + c), Qg + kg_index<C::RL>(8 * k2 + 4 + g, 16 * n + c)));
   }
 }
 
-template <typename T, int D>
-__global__ void __launch_bounds__(64) k_gdn_bwd(const T* __restrict__ q, const T* __restrict__ k,
-                                                 const T* __restrict__ v, const float* __restrict__ alpha,
-                                                 const float* __restrict__ beta, const int32_t* __restrict__ route,
-                                                 const float* __restrict__ d_o, const float* __restrict__ dS_final,
-                                                 const float* __restrict__ ckpt, float* __restrict__ scratch,
-                                                 float* __restrict__ dq_p, float* __restrict__ dk_p,
-                                                 float* __restrict__ dab_p, float* __restrict__ dv,
-                                                 float* __restrict__ dS_init, float* __restrict__ gate_p, int H,
-                                                 int L, int G) {
-  using C = GdnBwdCfg<D>;
-  constexpr int NV = 2 * C::RPT;  // row-sum values per thread and token: dq, dk at its rows
-  constexpr int VPL = NV / C::CW;  // of which each lane stores VPL after the row-group reduction
+// -------------------------------------------------------------- reverse scan
+template <typename T, int D, int DVT>
+struct BwdScanOps {
+  static constexpr int KF = D / 32, NV = DVT / 16, DTW = D / 64;
+  Frag<T> ka[KF];      // K rows 16w + c (contraction d, contiguous)
+  Frag<T> pt[2];       // P^T, row tile w
+  Frag<T> wt[DTW][2];  // -W^T, d tiles DTW w + x
+  Frag<T> qt[DTW][2];  // Q^T, d tiles DTW w + x
+  float dov[2][NV][8]; // d_o at tokens 32 k2 + kmap_acc(g, j), columns dv0 + 16 n + c
+  f32x4 gk[2][2];      // gamma at tokens 32 k2 + 4g + i and 32 k2 + 16 + 4g + i
+  f32x4 ek;            // exp(g_C - g) at rows 16w + 4g + i
+  float gC;
+  int route;
+};
+
+template <typename T, int D, int DVT>
+__device__ __forceinline__ void bwd_scan_load(BwdScanOps<T, D, DVT>& op, const GdnBwdWs<T, D>& bw, const T* kh,
+                                              const float* doh, const int32_t* rt, int64_t bh, int nc, int cc,
+                                              int dv0) {
+  using O = BwdScanOps<T, D, DVT>;
+  constexpr int NT = D / 16;
+  const int lane = lane_id(), w = wave_id();
+  const int g = lane >> 4, c = lane & 15;
+  const int64_t ch = bh * nc + cc;
+#pragma unroll
+  for (int ks = 0; ks < O::KF; ++ks) op.ka[ks] = load8<T>(kh + ((int64_t)cc * CHUNK + 16 * w + c) * D + 32 * ks + 8 * g);
+#pragma unroll
+  for (int k2 = 0; k2 < 2; ++k2) op.pt[k2] = load8<T>(bw.pt + ((ch * 4 + w) * 2 + k2) * 512 + lane * 8);
+#pragma unroll
+  for (int x = 0; x < O::DTW; ++x)
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      const int dt = O::DTW * w + x;
+      op.wt[x][k2] = load8<T>(bw.wtn + ((ch * NT + dt) * 2 + k2) * 512 + lane * 8);
+      op.qt[x][k2] = load8<T>(bw.qt + ((ch * NT + dt) * 2 + k2) * 512 + lane * 8);
+    }
+#pragma unroll
+  for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+    for (int n = 0; n < O::NV; ++n)
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        op.dov[k2][n][j] = doh[((int64_t)cc * CHUNK + 32 * k2 + kmap_acc(g, j)) * D + dv0 + 16 * n + c];
+  const float* gm = bw.gm + ch * GM_FLOATS;
+#pragma unroll
+  for (int k2 = 0; k2 < 2; ++k2) {
+    op.gk[k2][0] = *reinterpret_cast<const f32x4*>(gm + 32 * k2 + 4 * g);
+    op.gk[k2][1] = *reinterpret_cast<const f32x4*>(gm + 32 * k2 + 16 + 4 * g);
+  }
+  op.ek = *reinterpret_cast<const f32x4*>(gm + 80 + 16 * w + 4 * g);
+  op.gC = gm[64];
+  op.route = rt[cc];
+}
+
+// One workgroup per (b, h, DVT-column slice of Dv), chunks in reverse.  The
+// fp32 carried gradient lives in registers (rows d = 16 (DTW w + x) + 4g + i,
+// columns dv0 + 16 n + c), a T copy transposed in LDS feeds K Gc; dU goes
+// through LDS key groups into -W^T dU.  Per chunk: Gc -> workspace, then
+//   Z = K Gc;  dU = P^T dO + [committed] diag(e) Z -> workspace
+//   Gc <- [committed ? gamma_C : 1] Gc + Q^T (gamma dO) + (-W^T) dU.
+template <typename T, int D, int DVT>
+__global__ void __launch_bounds__(256, 1)
+    k_gdn_bwd_scan(const T* __restrict__ k, const float* __restrict__ d_o, const int32_t* __restrict__ route,
+                   GdnBwdWs<T, D> bw, const float* __restrict__ dS_final, T* __restrict__ g_out,
+                   float* __restrict__ dS_init, int H, int L, int G) {
+  using O = BwdScanOps<T, D, DVT>;
+  constexpr int SPP = D + 16 / (int)sizeof(T);
+  __shared__ __align__(16) T Gp[2][DVT * SPP];
+  constexpr int URL = kg_row<T, DVT>();
+  __shared__ __align__(16) T Ug[(CHUNK / 4) * URL * 4];
+
   const int nc = L / CHUNK;
-  const int bh = bid_x() / C::NCG, cg = bid_x() % C::NCG, b = bh / H, h = bh % H;
+  const int nvt = D / DVT;
+  const int total = (int)grid_dim_x();
+  const int BH = total / nvt;
+  int logical = bid_x();
+  if ((BH & 7) == 0) logical = (bid_x() & 7) * (total >> 3) + (bid_x() >> 3);
+  const int64_t bh = logical / nvt;
+  const int vt = logical % nvt;
+  const int b = (int)(bh / H), h = (int)(bh % H);
   const int grp = (G == 1) ? 0 : h;
   const int32_t* rt = route + ((int64_t)b * G + grp) * nc;
-  const int t = tid_x(), jl = t % C::CW, rg = t / C::CW, lane = t;
-  const int j = C::CW * cg + jl, r0 = rg * C::RPT;
-  // after the row-group reduction lane jl holds values jl VPL ..: dq (the lower half of the lanes) or dk
-  // at rows r0 + (jl % (CW / 2)) VPL ..
-  float* const dqk_p = (jl < C::CW / 2) ? dq_p : dk_p;
-  const int rq0 = r0 + (jl % (C::CW / 2)) * VPL;
-  const int64_t tok0 = (int64_t)bh * L;
-  const T* qh = q + tok0 * D;
-  const T* kh = k + tok0 * D;
-  const T* vh = v + tok0 * D;
-  const float* doh = d_o + tok0 * D;
-  const float* ah = alpha + tok0;
-  const float* bth = beta + tok0;
-  const float* ck = ckpt + (int64_t)bh * nc * D * D;
-  // S_{t-1} of the chunk's tokens: slot s of thread t at (s * 256 + t) * RPT
-  float* sc = scratch + (int64_t)bid_x() * CHUNK * D * C::CW + (int64_t)t * C::RPT;
+  const int dv0 = vt * DVT;
+  const T* kh = k + bh * L * D;
+  const float* doh = d_o + bh * L * D;
+  const int lane = lane_id(), w = wave_id();
+  const int g = lane >> 4, c = lane & 15;
 
-  float Gc[C::RPT];  // gradient of the carried state after the current chunk
+  f32x4 sm[O::DTW][O::NV];
 #pragma unroll
-  for (int i = 0; i < C::RPT; ++i) Gc[i] = dS_final ? dS_final[((int64_t)bh * D + r0 + i) * D + j] : 0.f;
+  for (int x = 0; x < O::DTW; ++x)
+#pragma unroll
+    for (int n = 0; n < O::NV; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int dk = 16 * (w * O::DTW + x) + 4 * g + i;
+        sm[x][n][i] = dS_final ? dS_final[(bh * D + dk) * D + dv0 + 16 * n + c] : 0.f;
+      }
+  int sb = 0;
+  auto write_g = [&](int buf) {
+#pragma unroll
+    for (int x = 0; x < O::DTW; ++x)
+#pragma unroll
+      for (int n = 0; n < O::NV; ++n)
+        st4<T>(&Gp[buf][(16 * n + c) * SPP + 16 * (w * O::DTW + x) + 4 * g], sm[x][n][0], sm[x][n][1], sm[x][n][2],
+               sm[x][n][3]);
+  };
+  write_g(0);
+  lds_barrier();
 
-  for (int c = nc - 1; c >= 0; --c) {
-    const int c0 = c * CHUNK;
-    const float al_c = ah[c0 + lane], be_c = bth[c0 + lane];  // lane s: token c0 + s
-    // recompute the chunk's states: slot s holds the state before token c0 + s
-    float S[C::RPT];
+  auto step = [&](const O& op, int cc) {
+    const int64_t ch = bh * nc + cc;
 #pragma unroll
-    for (int i = 0; i < C::RPT; ++i) S[i] = ck[((int64_t)c * D + r0 + i) * D + j];
-    {
-      TokRaw<T, C::RPT> ring[C::PF];  // slot u: the token c0 + s with s % PF == u
+    for (int x = 0; x < O::DTW; ++x)
 #pragma unroll
-      for (int u = 0; u < C::PF; ++u) load_tok<T, D, false>(ring[u], kh, kh, vh, nullptr, c0 + u, r0, j);
-      for (int s0 = 0; s0 < CHUNK; s0 += C::PF) {
+      for (int n = 0; n < O::NV; ++n)
 #pragma unroll
-        for (int u = 0; u < C::PF; ++u) {
-          const int s = s0 + u, tt = c0 + s;
-          store_state<C::RPT>(sc + (int64_t)s * C::NT * C::RPT, S);
-          // (token c0 + 63 runs too, without a branch; its end state is not used)
-          const TokIn<C::RPT> cur = tok_f32<T, C::RPT, false>(ring[u]);
-          load_tok<T, D, false>(ring[u], kh, kh, vh, nullptr, c0 + min(s + C::PF, CHUNK - 1), r0, j);
-          gdn_fwd_token<D>(S, cur, lane_bcast(al_c, s), lane_bcast(be_c, s));
+        for (int i = 0; i < 4; ++i) {
+          const int dk = 16 * (w * O::DTW + x) + 4 * g + i;
+          g_out[(ch * D + dk) * D + dv0 + 16 * n + c] = from_f32<T>(sm[x][n][i]);
         }
+    Frag<T> bg[O::KF][O::NV];
+#pragma unroll
+    for (int ks = 0; ks < O::KF; ++ks)
+#pragma unroll
+      for (int n = 0; n < O::NV; ++n) bg[ks][n] = load8<T>(&Gp[sb][(16 * n + c) * SPP + 32 * ks + 8 * g]);
+    f32x4 z[O::NV], xa[O::NV];
+#pragma unroll
+    for (int n = 0; n < O::NV; ++n) {
+      z[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+      xa[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int ks = 0; ks < O::KF; ++ks)
+#pragma unroll
+      for (int n = 0; n < O::NV; ++n) mma(z[n], op.ka[ks], bg[ks][n]);
+    Frag<T> bdo[2][O::NV], bdg[2][O::NV];
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+      for (int n = 0; n < O::NV; ++n)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float dv = op.dov[k2][n][j];
+          const float gm_ = j < 4 ? op.gk[k2][0][j] : op.gk[k2][1][j - 4];
+          frag_set(bdo[k2][n], j, dv);
+          frag_set(bdg[k2][n], j, dv * gm_);
+        }
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+      for (int n = 0; n < O::NV; ++n) mma(xa[n], op.pt[k2], bdo[k2][n]);
+    const bool lin = op.route == 1;
+    const float gce = lin ? op.gC : 1.f;
+    f32x4 du[O::NV];
+#pragma unroll
+    for (int n = 0; n < O::NV; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) du[n][i] = xa[n][i] + (lin ? op.ek[i] * z[n][i] : 0.f);
+#pragma unroll
+    for (int n = 0; n < O::NV; ++n) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        bw.du[(bh * L + (int64_t)cc * CHUNK + 16 * w + 4 * g + i) * D + dv0 + 16 * n + c] = from_f32<T>(du[n][i]);
+      st4<T>(&Ug[kg_index<URL>(4 * w + g, 16 * n + c)], du[n][0], du[n][1], du[n][2], du[n][3]);
+    }
+    lds_barrier();
+    Frag<T> bu[2][O::NV];
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+      for (int n = 0; n < O::NV; ++n)
+        bu[k2][n] = ld4x2<T>(&Ug[kg_index<URL>(8 * k2 + g, 16 * n + c)], &Ug[kg_index<URL>(8 * k2 + 4 + g, 16 * n + c)]);
+#pragma unroll
+    for (int x = 0; x < O::DTW; ++x)
+#pragma unroll
+      for (int n = 0; n < O::NV; ++n) {
+        f32x4 acc = sm[x][n] * gce;
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          mma(acc, op.qt[x][k2], bdg[k2][n]);
+          mma(acc, op.wt[x][k2], bu[k2][n]);
+        }
+        sm[x][n] = acc;
       }
-    }
-    // the linear gate's derivative (the chunk's end state committed as
-    // S_start + h (S_end - S_start)): <d loss / d carried state after the
-    // chunk, S_end - S_start>, this group's columns; S holds S_end here
-    if (gate_p) {
-      float pg = 0.f;
-#pragma unroll
-      for (int i = 0; i < C::RPT; ++i) pg += Gc[i] * (S[i] - ck[((int64_t)c * D + r0 + i) * D + j]);
-      pg = wave_sum64(pg);
-      if (lane == 0) gate_p[(int64_t)bid_x() * nc + c] = pg;
-    }
-    // (this thread's scratch stores complete before the sweep reads them back)
-    __syncthreads();
-    const bool lin = rt[c] == kRouteLinear;
-    float Gm[C::RPT];
-#pragma unroll
-    for (int i = 0; i < C::RPT; ++i) Gm[i] = lin ? Gc[i] : 0.f;
-    // inputs and S_{t-1}, PFB tokens ahead; the sweep runs backward: step r is
-    // token c0 + 63 - r, in slot r % PFB
-    TokRaw<T, C::RPT> ring[C::PFB];
-    float ringS[C::PFB][C::RPT];
-#pragma unroll
-    for (int u = 0; u < C::PFB; ++u) {
-      load_tok<T, D, true>(ring[u], kh, qh, vh, doh, c0 + CHUNK - 1 - u, r0, j);
-      load_state<C::RPT>(ringS[u], sc + (int64_t)(CHUNK - 1 - u) * C::NT * C::RPT);
-    }
-    for (int r00 = 0; r00 < CHUNK; r00 += C::PFB) {
-#pragma unroll
-      for (int u = 0; u < C::PFB; ++u) {
-        const int rs = r00 + u, s = CHUNK - 1 - rs, tt = c0 + s;
-        const TokIn<C::RPT> x = tok_f32<T, C::RPT, true>(ring[u]);
-        float Sp[C::RPT];
-#pragma unroll
-        for (int i = 0; i < C::RPT; ++i) Sp[i] = ringS[u][i];
-        // the token PFB steps on, clamped to the chunk's first (unconditional)
-        load_tok<T, D, true>(ring[u], kh, qh, vh, doh, c0 + max(s - C::PFB, 0), r0, j);
-        load_state<C::RPT>(ringS[u], sc + (int64_t)max(s - C::PFB, 0) * C::NT * C::RPT);
-        float pa[4] = {0.f, 0.f, 0.f, 0.f}, pw[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int i = 0; i < C::RPT; ++i) {
-          Gm[i] += x.q[i] * x.d_o;  // o_t = S_t^T q_t
-          pa[i & 3] += Sp[i] * x.k[i];
-          pw[i & 3] += Gm[i] * x.k[i];
-        }
-        const float a = col_sum<C::CW>((pa[0] + pa[1]) + (pa[2] + pa[3]));
-        const float w = col_sum<C::CW>((pw[0] + pw[1]) + (pw[2] + pw[3]));
-        const float al = lane_bcast(al_c, s), be = lane_bcast(be_c, s), vj = x.v, doj = x.d_o;
-        const float cv = be * vj - al * be * a, cw = al * be * w;
-        float pal = 0.f, rv[NV];
-#pragma unroll
-        for (int i = 0; i < C::RPT; ++i) {
-          const float ki = x.k[i];
-          const float erased = Sp[i] - be * ki * a;
-          rv[i] = (al * erased + be * ki * vj) * doj;  // this column's share of dq = S_t d_o
-          rv[C::RPT + i] = Gm[i] * cv - cw * Sp[i];    // and of dk
-          pal += Gm[i] * erased;
-          Gm[i] = al * (Gm[i] - be * ki * w);  // the gradient of S_{t-1}
-        }
-        group_reduce_scatter<C::CW, NV>(rv, jl);
-        const int64_t tok = tok0 + tt;
-        float* dst = dqk_p + (tok * C::NCG + cg) * D + rq0;
-        if constexpr (VPL % 4 == 0) {
-#pragma unroll
-          for (int h = 0; h < VPL; h += 4) *(float4*)(dst + h) = make_float4(rv[h], rv[h + 1], rv[h + 2], rv[h + 3]);
-        } else {
-#pragma unroll
-          for (int h = 0; h < VPL; h += 2) *(float2*)(dst + h) = make_float2(rv[h], rv[h + 1]);
-        }
-        float pbe = (rg == 0) ? w * (vj - al * a) : 0.f;
-        pal = wave_sum64(pal);
-        pbe = wave_sum64(pbe);
-        if (lane < 2) dab_p[(tok * C::NCG + cg) * 2 + lane] = lane ? pbe : pal;  // this group's partials
-        if (rg == 0) dv[tok * D + j] = be * w;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < C::RPT; ++i) Gc[i] = Gm[i] + (lin ? 0.f : Gc[i]);
+    write_g(sb ^ 1);
+    sb ^= 1;
+    lds_barrier();
+  };
+
+  O ops[2];
+  bwd_scan_load<T, D, DVT>(ops[0], bw, kh, doh, rt, bh, nc, nc - 1, dv0);
+  int cc = nc - 1;
+  for (; cc >= 1; cc -= 2) {
+    bwd_scan_load<T, D, DVT>(ops[1], bw, kh, doh, rt, bh, nc, cc - 1, dv0);
+    step(ops[0], cc);
+    bwd_scan_load<T, D, DVT>(ops[0], bw, kh, doh, rt, bh, nc, cc >= 2 ? cc - 2 : 0, dv0);
+    step(ops[1], cc - 1);
   }
+  if (cc == 0) step(ops[0], 0);
   if (dS_init) {
 #pragma unroll
-    for (int i = 0; i < C::RPT; ++i) dS_init[((int64_t)bh * D + r0 + i) * D + j] = Gc[i];
+    for (int x = 0; x < O::DTW; ++x)
+#pragma unroll
+      for (int n = 0; n < O::NV; ++n)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int dk = 16 * (w * O::DTW + x) + 4 * g + i;
+          dS_init[(bh * D + dk) * D + dv0 + 16 * n + c] = sm[x][n][i];
+        }
   }
 }
 
-// dq, dk, dalpha, dbeta: the NCG groups' partials added in group order
-// (dalpha and dbeta interleaved).  Threads [0, ntok D/4) take 4 consecutive
-// rows of one token's dq and dk (16-byte loads from the workspace; scalar
-// stores, the outputs carrying no alignment promise); threads
-// [ntok D/4, ntok D/4 + ntok) take one token's dalpha and dbeta.
-template <int D>
-__global__ void __launch_bounds__(256) k_gdn_bwd_reduce(const float* __restrict__ dq_p, const float* __restrict__ dk_p,
-                                                        const float* __restrict__ dab_p, float* __restrict__ dq,
-                                                        float* __restrict__ dk, float* __restrict__ dalpha,
-                                                        float* __restrict__ dbeta, int64_t ntok) {
-  constexpr int NCG = GdnBwdCfg<D>::NCG;
-  static_assert(NCG % 2 == 0 && D % 4 == 0, "whole 16-byte partial vectors");
-  const int64_t gid = (int64_t)bid_x() * 256 + tid_x();
-  const int64_t nvec = ntok * (D / 4);
-  if (gid < nvec) {
-    const int64_t tok = gid / (D / 4);
-    const int i = (int)(gid % (D / 4)) * 4;
-    float sq[4] = {0.f, 0.f, 0.f, 0.f}, sk[4] = {0.f, 0.f, 0.f, 0.f};
+// ------------------------------------------------------- per-chunk gradients
+template <typename T, int D>
+struct BwdChunkCfg {
+  static constexpr int CT = D / 64;  // 16-column tiles per wave of a 64 x D product
+  static constexpr int KV = D / 32;  // contraction steps over D
+  static constexpr int PM = 68;      // pitch of the fp32 64 x 64 matrices (16-byte rows)
+  static constexpr int PT = D + 16 / (int)sizeof(T);
+  // U, dU and K staged in LDS (else read from global memory)
+  static constexpr bool FIT = sizeof(T) == 2 || D == 64;
+  static constexpr int M_BYTES = CHUNK * PM * 4;
+  static constexpr int T_BYTES = CHUNK * PT * (int)sizeof(T);
+  static constexpr int OFF_TL = 0, OFF_AL = M_BYTES, OFF_FL = 2 * M_BYTES, OFF_ML = 3 * M_BYTES;
+  static constexpr int OFF_X1 = 4 * M_BYTES;
+  static constexpr int OFF_UL = OFF_X1 + T_BYTES;
+  static constexpr int OFF_DUL = OFF_UL + (FIT ? T_BYTES : 0);
+  static constexpr int OFF_KL = OFF_DUL + (FIT ? T_BYTES : 0);
+  static constexpr int OFF_VEC = OFF_KL + (FIT ? T_BYTES : 0);
+  // g2, gamma, e, beta, beta gamma, alpha; partial row sums pbeta, pgam,
+  // pts, cdg [4][64]; rdg, rbeta [64]; red [4]
+  static constexpr int VEC_FLOATS = 6 * 64 + 4 * 4 * 64 + 2 * 64 + 4;
+  static constexpr int LDS = OFF_VEC + VEC_FLOATS * 4;
+  static_assert(LDS <= 160 * 1024, "LDS");
+};
+
+template <typename T, typename Fn>
+__device__ __forceinline__ Frag<T> frag_fn(Fn fn) {
+  Frag<T> f;
 #pragma unroll
-    for (int cg = 0; cg < NCG; ++cg) {
-      const float4 a = *(const float4*)(dq_p + (tok * NCG + cg) * D + i);
-      const float4 c = *(const float4*)(dk_p + (tok * NCG + cg) * D + i);
-      sq[0] += a.x; sq[1] += a.y; sq[2] += a.z; sq[3] += a.w;
-      sk[0] += c.x; sk[1] += c.y; sk[2] += c.z; sk[3] += c.w;
-    }
+  for (int j = 0; j < 8; ++j) frag_set(f, j, fn(j));
+  return f;
+}
+template <typename T>
+__device__ __forceinline__ Frag<T> frag_f32(const float* p) {  // 8 contiguous fp32 (16-byte aligned)
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
+  Frag<T> f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      dq[tok * D + i + r] = sq[r];
-      dk[tok * D + i + r] = sk[r];
-    }
-  } else if (gid < nvec + ntok) {
-    const int64_t tok = gid - nvec;
-    float sa = 0.f, sb = 0.f;
-#pragma unroll
-    for (int x = 0; x < NCG; x += 2) {  // groups x and x + 1
-      const float4 a = *(const float4*)(dab_p + (tok * NCG + x) * 2);
-      sa += a.x;
-      sb += a.y;
-      sa += a.z;
-      sb += a.w;
-    }
-    dalpha[tok] = sa;
-    dbeta[tok] = sb;
+  for (int j = 0; j < 4; ++j) {
+    frag_set(f, j, a[j]);
+    frag_set(f, 4 + j, b[j]);
   }
+  return f;
+}
+// sum over the 16 lanes of a row group; lane c = 0 of group g writes the 4
+// rows base + 4g + i
+__device__ __forceinline__ void row_partials(const f32x4& v, float* dst, int g, int c) {
+  f32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = dpp_group_sum<16>(v[i]);
+  if (c == 0) *reinterpret_cast<f32x4*>(dst + 4 * g) = r;
 }
 
-// the linear gates' derivative: the column groups' partials added in order
-__global__ void __launch_bounds__(256) k_gdn_bwd_gate_reduce(const float* __restrict__ gate_p,
-                                                             float* __restrict__ dgate, int ncg, int nc, int64_t n) {
-  const int64_t i = (int64_t)bid_x() * 256 + tid_x();  // (bh, c)
-  if (i >= n) return;
-  const int64_t bh = i / nc, c = i % nc;
-  float s = 0.f;
-  for (int cg = 0; cg < ncg; ++cg) s += gate_p[(bh * ncg + cg) * nc + c];
-  dgate[i] = s;
+// One workgroup per chunk-head.  Wave w owns row tile w of the 64 x 64
+// products (rows t = 16w + 4g + i) and columns 16 (CT w + ct) + c of the
+// 64 x D products (all four row tiles).  All contractions use the row map
+// (8g + j), operands from LDS, or from global memory where they are read
+// once (dO, the S0 / Gc fragments).
+template <typename T, int D>
+__global__ void __launch_bounds__(256, 1)
+    k_gdn_bwd_chunk(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+                    const float* __restrict__ alpha, const float* __restrict__ beta, const float* __restrict__ d_o,
+                    const int32_t* __restrict__ route, GdnBwdWs<T, D> bw, const T* __restrict__ s0,
+                    const T* __restrict__ u, const T* __restrict__ gst, float* __restrict__ dq,
+                    float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ dalpha,
+                    float* __restrict__ dbeta, float* __restrict__ dgate, int H, int L, int G) {
+  using C = BwdChunkCfg<T, D>;
+  constexpr int CT = C::CT, KV = C::KV, PM = C::PM, PT = C::PT;
+  extern __shared__ __align__(16) unsigned char lds[];
+  float* Tl = (float*)(lds + C::OFF_TL);
+  float* Al = (float*)(lds + C::OFF_AL);  // A (decayed), then dT, then E
+  float* Fl = (float*)(lds + C::OFF_FL);
+  float* Ml = (float*)(lds + C::OFF_ML);
+  T* X1 = (T*)(lds + C::OFF_X1);          // TdU, then VmR
+  float* vec = (float*)(lds + C::OFF_VEC);
+  float* g2 = vec;
+  float* gam = vec + 64;
+  float* ekv = vec + 128;
+  float* bet = vec + 192;
+  float* bgm = vec + 256;
+  float* alp = vec + 320;
+  float* pbeta = vec + 384;
+  float* pgam = pbeta + 256;
+  float* pts = pgam + 256;
+  float* cdg = pts + 256;
+  float* rdg = cdg + 256;
+  float* rbeta = rdg + 64;
+  float* red = rbeta + 64;
+
+  const int nc = L / CHUNK;
+  const int64_t ch = bid_x();
+  const int64_t bh = ch / nc;
+  const int cc = (int)(ch % nc);
+  const int b = (int)(bh / H), h = (int)(bh % H);
+  const int grp = (G == 1) ? 0 : h;
+  const bool lin = route[((int64_t)b * G + grp) * nc + cc] == 1;
+  const int64_t tok0 = bh * L + (int64_t)cc * CHUNK;
+  const int t = tid_x(), lane = lane_id(), w = wave_id();
+  const int g = lane >> 4, c = lane & 15;
+
+  const T* qc = q + tok0 * D;
+  const T* kc = k + tok0 * D;
+  const T* vc = v + tok0 * D;
+  const float* doc = d_o + tok0 * D;
+  const T* uc = u + tok0 * D;
+  const T* duc = bw.du + tok0 * D;
+  // U, dU, K rows: LDS copies (pitch PT) or global memory (pitch D)
+  const T* Ub = C::FIT ? (const T*)(lds + C::OFF_UL) : uc;
+  const T* dUb = C::FIT ? (const T*)(lds + C::OFF_DUL) : duc;
+  const T* Kb = C::FIT ? (const T*)(lds + C::OFF_KL) : kc;
+  constexpr int UP = C::FIT ? PT : D;
+
+  // ---- phase 0: decays, staging, the S0^T / Gc^T fragments
+  if (w == 0) {
+    const float a = alpha[tok0 + lane];
+    const float bt = beta[tok0 + lane];
+    float s = __builtin_amdgcn_logf(a);
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float o = __shfl_up(s, off, 64);
+      if (lane >= off) s += o;
+    }
+    const float gC = __shfl(s, 63, 64);
+    const float gm_ = __builtin_amdgcn_exp2f(s);
+    g2[lane] = s;
+    gam[lane] = gm_;
+    ekv[lane] = __builtin_amdgcn_exp2f(gC - s);
+    bet[lane] = bt;
+    bgm[lane] = bt * gm_;
+    alp[lane] = a;
+  }
+  for (int e = t; e < CHUNK * CHUNK / 4; e += 256)
+    *reinterpret_cast<f32x4*>(Tl + (e >> 4) * PM + (e & 15) * 4) =
+        *reinterpret_cast<const f32x4*>(bw.tm + ch * CHUNK * CHUNK + e * 4);
+  if constexpr (C::FIT) {
+    constexpr int PER = 16 / (int)sizeof(T), NP = CHUNK * D / PER;
+    T* Ul = (T*)(lds + C::OFF_UL);
+    T* dUl = (T*)(lds + C::OFF_DUL);
+    T* Kl = (T*)(lds + C::OFF_KL);
+    for (int e = t; e < NP; e += 256) {
+      const int r = e / (D / PER), cl = (e % (D / PER)) * PER;
+      *reinterpret_cast<f32x4*>(Ul + r * PT + cl) = *reinterpret_cast<const f32x4*>(uc + r * D + cl);
+      *reinterpret_cast<f32x4*>(dUl + r * PT + cl) = *reinterpret_cast<const f32x4*>(duc + r * D + cl);
+      *reinterpret_cast<f32x4*>(Kl + r * PT + cl) = *reinterpret_cast<const f32x4*>(kc + r * D + cl);
+    }
+  }
+  // S0^T and Gc^T B fragments of this wave's columns: column d = 16 (CT w +
+  // ct) + c, contraction over v = 32 kv + 8g + j (contiguous rows of S0, Gc)
+  Frag<T> s0f[CT][KV], gf[CT][KV];
+  float sg = 0.f;
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+    for (int kv = 0; kv < KV; ++kv) {
+      const int64_t off = (ch * D + 16 * (CT * w + ct) + c) * D + 32 * kv + 8 * g;
+      s0f[ct][kv] = load8<T>(s0 + off);
+      gf[ct][kv] = load8<T>(gst + off);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sg += to_f32(frag_get<T>(s0f[ct][kv], j)) * to_f32(frag_get<T>(gf[ct][kv], j));
+    }
+  sg = wave_sum64(sg);
+  if (lane == 0) red[w] = sg;
+  __syncthreads();
+
+  // ---- phase 1 (row tile w): A, P, dP
+  f32x4 akk[4], apq[4], dpa[4];
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) {
+    akk[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    apq[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    dpa[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int kv = 0; kv < KV; ++kv) {
+    const Frag<T> ak = load8<T>(Kb + (16 * w + c) * UP + 32 * kv + 8 * g);
+    const Frag<T> aq = load8<T>(qc + (16 * w + c) * D + 32 * kv + 8 * g);
+    const Frag<T> ad = frag_f32<T>(doc + (16 * w + c) * D + 32 * kv + 8 * g);
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      const Frag<T> bk = load8<T>(Kb + (16 * ct + c) * UP + 32 * kv + 8 * g);
+      const Frag<T> bu = load8<T>(Ub + (16 * ct + c) * UP + 32 * kv + 8 * g);
+      mma(akk[ct], ak, bk);
+      mma(apq[ct], aq, bk);
+      mma(dpa[ct], ad, bu);
+    }
+  }
+  {
+    f32x4 rsum = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      float csum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * w + 4 * g + i, s = 16 * ct + c;
+        const float gmx = __builtin_amdgcn_exp2f(g2[r] - g2[s]);
+        Al[r * PM + s] = (s < r) ? gmx * akk[ct][i] : 0.f;
+        const float p = (s <= r) ? gmx * apq[ct][i] : 0.f;
+        const float dp = (s <= r) ? dpa[ct][i] : 0.f;
+        Fl[r * PM + s] = dp * gmx;
+        rsum[i] += dp * p;
+        csum += dp * p;
+      }
+      csum = group4_sum(csum);
+      if (g == 0) cdg[w * 64 + 16 * ct + c] = csum;
+    }
+    row_partials(rsum, rdg + 16 * w, g, c);
+  }
+  __syncthreads();
+
+  // ---- phase 2 (columns of wave w): dO S0^T, U Gc^T, T^T dU, A U, TdU S0^T
+  f32x4 dqa[4][CT], dka[4][CT];
+  f32x4 vb[4], vg[4];  // per-row partial sums for dbeta, dgamma
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    vb[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    vg[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  {
+    f32x4 vt[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      f32x4 dos[CT], ug[CT];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        dos[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+        ug[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int kv = 0; kv < KV; ++kv) {
+        const Frag<T> ad = frag_f32<T>(doc + (16 * rt + c) * D + 32 * kv + 8 * g);
+        const Frag<T> au = load8<T>(Ub + (16 * rt + c) * UP + 32 * kv + 8 * g);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          mma(dos[ct], ad, s0f[ct][kv]);
+          mma(ug[ct], au, gf[ct][kv]);
+        }
+      }
+      vt[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        const int col = 16 * (CT * w + ct) + c;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * rt + 4 * g + i;
+          const float qv = to_f32(qc[r * D + col]);
+          const float kv_ = to_f32(Kb[r * UP + col]);
+          dqa[rt][ct][i] = gam[r] * dos[ct][i];
+          dka[rt][ct][i] = lin ? ekv[r] * ug[ct][i] : 0.f;
+          vg[rt][i] += qv * dos[ct][i];
+          vt[rt][i] += ekv[r] * kv_ * ug[ct][i];
+        }
+      }
+    }
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) row_partials(vt[rt], pts + w * 64 + 16 * rt, g, c);
+  }
+  // TdU = T^T dU -> dv, X1;  A U -> VmR (held until X1 is free)
+  f32x4 vmr[4][CT];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    f32x4 tdu[CT], au[CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      tdu[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+      au[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      const int t0 = 32 * k2 + 8 * g;
+      const Frag<T> at = frag_fn<T>([&](int j) { return Tl[(t0 + j) * PM + 16 * rt + c]; });
+      const Frag<T> aa = frag_f32<T>(Al + (16 * rt + c) * PM + t0);
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        const int col = 16 * (CT * w + ct) + c;
+        const Frag<T> bdu = frag_fn<T>([&](int j) { return to_f32(dUb[(t0 + j) * UP + col]); });
+        const Frag<T> bu = frag_fn<T>([&](int j) { return to_f32(Ub[(t0 + j) * UP + col]); });
+        mma(tdu[ct], at, bdu);
+        mma(au[ct], aa, bu);
+      }
+    }
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      const int col = 16 * (CT * w + ct) + c;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rt + 4 * g + i;
+        dv[(tok0 + r) * D + col] = bet[r] * tdu[ct][i];
+        vb[rt][i] += to_f32(vc[r * D + col]) * tdu[ct][i];
+        X1[r * PT + col] = from_f32<T>(tdu[ct][i]);
+        vmr[rt][ct][i] = to_f32(Ub[r * UP + col]) + bet[r] * au[ct][i];
+      }
+    }
+  }
+  __syncthreads();
+  // TdW = -TdU S0^T
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    f32x4 tw[CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) tw[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kv = 0; kv < KV; ++kv) {
+      const Frag<T> ax = load8<T>(X1 + (16 * rt + c) * PT + 32 * kv + 8 * g);
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) mma(tw[ct], ax, s0f[ct][kv]);
+    }
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      const int col = 16 * (CT * w + ct) + c;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rt + 4 * g + i;
+        const float tdw = -tw[ct][i];
+        const float kw = to_f32(Kb[r * UP + col]) * tdw;
+        dka[rt][ct][i] += bgm[r] * tdw;
+        vb[rt][i] += gam[r] * kw;
+        vg[rt][i] += bet[r] * kw;
+      }
+    }
+  }
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    row_partials(vb[rt], pbeta + w * 64 + 16 * rt, g, c);
+    row_partials(vg[rt], pgam + w * 64 + 16 * rt, g, c);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) X1[(16 * rt + 4 * g + i) * PT + 16 * (CT * w + ct) + c] = from_f32<T>(vmr[rt][ct][i]);
+  __syncthreads();
+
+  // ---- phase 3 (row tile w): dT = dU VmR^T, M1 = T^T dT, dM = -M1 T^T
+  {
+    f32x4 dta[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) dta[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kv = 0; kv < KV; ++kv) {
+      const Frag<T> a = load8<T>(dUb + (16 * w + c) * UP + 32 * kv + 8 * g);
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) mma(dta[ct], a, load8<T>(X1 + (16 * ct + c) * PT + 32 * kv + 8 * g));
+    }
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Al[(16 * w + 4 * g + i) * PM + 16 * ct + c] = dta[ct][i];
+  }
+  __syncthreads();
+  {
+    f32x4 m1[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) m1[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      const int t0 = 32 * k2 + 8 * g;
+      const Frag<T> a = frag_fn<T>([&](int j) { return Tl[(t0 + j) * PM + 16 * w + c]; });
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+        mma(m1[ct], a, frag_fn<T>([&](int j) { return Al[(t0 + j) * PM + 16 * ct + c]; }));
+    }
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Ml[(16 * w + 4 * g + i) * PM + 16 * ct + c] = m1[ct][i];
+  }
+  __syncthreads();
+  {
+    f32x4 dma[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) dma[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      const int k0 = 32 * k2 + 8 * g;
+      const Frag<T> a = frag_f32<T>(Ml + (16 * w + c) * PM + k0);
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) mma(dma[ct], a, frag_f32<T>(Tl + (16 * ct + c) * PM + k0));
+    }
+    f32x4 rb = f32x4{0.f, 0.f, 0.f, 0.f}, rg = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      float csum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * w + 4 * g + i, s = 16 * ct + c;
+        const float gmx = __builtin_amdgcn_exp2f(g2[r] - g2[s]);
+        const float adec = (s < r) ? gmx * akk[ct][i] : 0.f;
+        const float dm = (s < r) ? -dma[ct][i] : 0.f;
+        const float da = bet[r] * dm;
+        rb[i] += dm * adec;
+        rg[i] += da * adec;
+        csum += da * adec;
+        Al[r * PM + s] = da * gmx;  // E
+      }
+      csum = group4_sum(csum);
+      if (g == 0) cdg[w * 64 + 16 * ct + c] += csum;
+    }
+    f32x4 r1, r2;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      r1[i] = dpp_group_sum<16>(rb[i]);
+      r2[i] = dpp_group_sum<16>(rg[i]);
+    }
+    if (c == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        rbeta[16 * w + 4 * g + i] = r1[i];
+        rdg[16 * w + 4 * g + i] += r2[i];
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- phase 4 (columns of wave w): E K, E^T K, F K, F^T Q; store dq, dk
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      const int t0 = 32 * k2 + 8 * g;
+      const Frag<T> ae = frag_f32<T>(Al + (16 * rt + c) * PM + t0);
+      const Frag<T> aet = frag_fn<T>([&](int j) { return Al[(t0 + j) * PM + 16 * rt + c]; });
+      const Frag<T> af = frag_f32<T>(Fl + (16 * rt + c) * PM + t0);
+      const Frag<T> aft = frag_fn<T>([&](int j) { return Fl[(t0 + j) * PM + 16 * rt + c]; });
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        const int col = 16 * (CT * w + ct) + c;
+        const Frag<T> bk = frag_fn<T>([&](int j) { return to_f32(Kb[(t0 + j) * UP + col]); });
+        const Frag<T> bq = frag_fn<T>([&](int j) { return to_f32(qc[(t0 + j) * D + col]); });
+        mma(dka[rt][ct], ae, bk);
+        mma(dka[rt][ct], aet, bk);
+        mma(dqa[rt][ct], af, bk);
+        mma(dka[rt][ct], aft, bq);
+      }
+    }
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      const int col = 16 * (CT * w + ct) + c;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t o = (tok0 + 16 * rt + 4 * g + i) * D + col;
+        dq[o] = dqa[rt][ct][i];
+        dk[o] = dka[rt][ct][i];
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- phase 5 (wave 0, lane = token): dbeta, d log-decay, dalpha, gate
+  if (w == 0) {
+    const int r = lane;
+    float db_ = rbeta[r], dgm = 0.f, ts = 0.f, cd = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) {
+      db_ += pbeta[ww * 64 + r];
+      dgm += pgam[ww * 64 + r];
+      ts += pts[ww * 64 + r];
+      cd += cdg[ww * 64 + r];
+    }
+    const float sgt = red[0] + red[1] + red[2] + red[3];
+    const float tsum = wave_sum64(ts);
+    float dg = rdg[r] - cd + gam[r] * dgm - (lin ? ts : 0.f);
+    if (r == CHUNK - 1 && lin) dg += tsum + gam[CHUNK - 1] * sgt;
+    // d log alpha_r = sum over t >= r of dg_t
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float o = __shfl_down(dg, off, 64);
+      if (lane + off < 64) dg += o;
+    }
+    dalpha[tok0 + r] = dg / alp[r];
+    dbeta[tok0 + r] = db_;
+    if (dgate && lane == 0) dgate[bh * nc + cc] = (gam[CHUNK - 1] - 1.f) * sgt + tsum;
+  }
 }
 
 template <typename T, int D>
@@ -443,41 +940,35 @@ hipError_t launch_gdn_backward(const T* q, const T* k, const T* v, const float* 
                                const int32_t* route, const float* S_init, const float* d_o, const float* dS_final,
                                float* dq, float* dk, float* dv, float* dalpha, float* dbeta, float* dS_init,
                                float* dgate, void* ws, int B, int H, int L, int G, hipStream_t st) {
-  using C = GdnBwdCfg<D>;
   const int nc = L / CHUNK;
-  const int64_t ntok = (int64_t)B * H * L;
-  float* ckpt = (float*)ws;
-  float* scratch = ckpt + (size_t)B * H * nc * D * D;
-  float* dq_p = scratch + (size_t)B * H * CHUNK * D * D;
-  float* dk_p = dq_p + (size_t)ntok * C::NCG * D;
-  float* dab_p = dk_p + (size_t)ntok * C::NCG * D;  // ntok x NCG x (dalpha, dbeta)
-  float* gate_p = dab_p + (size_t)ntok * C::NCG * 2;  // [B H][NCG][Nc]
-  const size_t lds = 0;
-  const unsigned grid = (unsigned)(B * H * C::NCG);
-  hipLaunchKernelGGL((k_gdn_bwd_ckpt<T, D>), dim3(grid), dim3(C::NT), lds, st, k, v, alpha, beta, route, S_init,
-                     ckpt, H, L, G);
-  hipError_t e = hipGetLastError();
+  const int64_t nch = (int64_t)B * H * nc;
+  const size_t rb = region_bytes<T, D>(nch);
+  char* p = (char*)ws + rb;
+  T* s0 = (T*)p;  p += al256((size_t)nch * D * D * sizeof(T));
+  T* u = (T*)p;   p += al256((size_t)nch * CHUNK * D * sizeof(T));
+  T* gst = (T*)p;
+  hipError_t e = launch_gdn_states<T, D>(q, k, v, alpha, beta, route, S_init, s0, u, ws, B, H, L, G, st);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_gdn_bwd<T, D>), dim3(grid), dim3(C::NT), lds, st, q, k, v, alpha, beta, route, d_o,
-                     dS_final, ckpt, scratch, dq_p, dk_p, dab_p, dv, dS_init, dgate ? gate_p : nullptr, H, L, G);
+  GdnBwdWs<T, D> bw = carve_bwd<T, D>(ws, nch);
+  using PC = BwdPrepCfg<T, D>;
+  if ((e = set_lds_limit((const void*)k_gdn_bwd_prep<T, D>, PC::LDS)) != hipSuccess) return e;
+  hipLaunchKernelGGL((k_gdn_bwd_prep<T, D>), dim3((unsigned)nch), dim3(256), PC::LDS, st, q, k, alpha, beta, bw, L);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (dgate) {
-    const int64_t n = (int64_t)B * H * nc;
-    hipLaunchKernelGGL(k_gdn_bwd_gate_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, gate_p, dgate,
-                       C::NCG, nc, n);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
-  const int64_t threads = ntok * (D / 4) + ntok;
-  hipLaunchKernelGGL((k_gdn_bwd_reduce<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, dq_p, dk_p,
-                     dab_p, dq, dk, dalpha, dbeta, ntok);
+  hipLaunchKernelGGL((k_gdn_bwd_scan<T, D, BWD_DVT>), dim3((unsigned)(B * H * (D / BWD_DVT))), dim3(256), 0, st, k,
+                     d_o, route, bw, dS_final, gst, dS_init, H, L, G);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  using CC = BwdChunkCfg<T, D>;
+  if ((e = set_lds_limit((const void*)k_gdn_bwd_chunk<T, D>, CC::LDS)) != hipSuccess) return e;
+  hipLaunchKernelGGL((k_gdn_bwd_chunk<T, D>), dim3((unsigned)nch), dim3(256), CC::LDS, st, q, k, v, alpha, beta, d_o,
+                     route, bw, (const T*)s0, (const T*)u, (const T*)gst, dq, dk, dv, dalpha, dbeta, dgate, H, L, G);
   return hipGetLastError();
 }
 
-#define INST(T, D)                                                                                                \
-  template hipError_t launch_gdn_backward<T, D>(const T*, const T*, const T*, const float*, const float*,         \
-                                                const int32_t*, const float*, const float*, const float*, float*, \
-                                                float*, float*, float*, float*, float*, float*, void*, int, int, int, int, \
-                                                hipStream_t);
+#define INST(T, D)                                                                                                  \
+  template hipError_t launch_gdn_backward<T, D>(const T*, const T*, const T*, const float*, const float*,           \
+                                                const int32_t*, const float*, const float*, const float*, float*,   \
+                                                float*, float*, float*, float*, float*, float*, void*, int, int,    \
+                                                int, int, hipStream_t);
 INST(float, 64)
 INST(float, 128)
 INST(bf16, 64)

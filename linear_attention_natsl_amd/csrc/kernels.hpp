@@ -121,9 +121,15 @@ hipError_t launch_nha(const T* q, const T* k, const T* v, const float* gate, int
                       int L, int window, float scale, hipStream_t st, void (*prof)(int, hipStream_t, int));
 
 size_t gdn_ws_bytes(int io_is_bf16, int D, int64_t nch);
-// Gated DeltaNet branch gradient (per-token reverse sweep): ws holds the
-// chunk-start states [B, H, Nc, D, D] and a per-(b, h) chunk of token states
-size_t gdn_bwd_ws_bytes(int B, int H, int L, int D);
+// Gated DeltaNet branch gradient (chunk form): ws holds the chunk preps'
+// region, then every chunk's start state S0, U and carried gradient
+size_t gdn_bwd_ws_bytes(int io_is_bf16, int B, int H, int L, int D);
+// the forward in state mode: every chunk's start state s0 [B, H, Nc, D, D]
+// and U [B, H, L, D] (io dtype), no outputs; ws as launch_gdn's
+template <typename T, int D>
+hipError_t launch_gdn_states(const T* q, const T* k, const T* v, const float* alpha, const float* beta,
+                             const int32_t* route, const float* S_init, T* s0, T* u, void* ws, int B, int H, int L,
+                             int G, hipStream_t st);
 template <typename T, int D>
 hipError_t launch_gdn_backward(const T* q, const T* k, const T* v, const float* alpha, const float* beta,
                                const int32_t* route, const float* S_init, const float* d_o, const float* dS_final,

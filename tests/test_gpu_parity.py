@@ -460,15 +460,18 @@ def test_softmax_backward_parity(io, D, L, q_scale, per_head):
 @pytest.mark.parametrize("io,D,L,per_head,alpha", [("f32", 64, 256, False, (0.9, 0.999)),
                                                    ("f32", 128, 320, False, (0.995, 1.0)),
                                                    ("bf16", 128, 384, True, (0.9, 0.999)),
-                                                   ("bf16", 64, 448, False, (0.995, 1.0))])
+                                                   ("bf16", 64, 448, False, (0.995, 1.0)),
+                                                   ("bf16", 128, 8192, False, (0.995, 1.0))])
 def test_gdn_backward_parity(io, D, L, per_head, alpha):
     """Gradient of the Gated DeltaNet branch through the rollback (q, k, v,
     alpha, beta and the initial state, with upstream gradients on the outputs
     and on the final carried state) against the oracle's exact derivative.
     Mixed routes, so both the commit and the restore paths carry gradient;
-    alpha ~ U(0.995, 1) keeps gradients flowing many chunks back.  Each
-    gradient within 1e-4 of its largest magnitude (the kernel works in fp32
-    on the same inputs)."""
+    alpha ~ U(0.995, 1) keeps gradients flowing many chunks back.  fp32:
+    each gradient within 1e-4 of its largest magnitude; bf16: within 2e-2
+    (the chunk form's matrix products take bf16 operands with fp32
+    accumulation, as the forward's do: about ten bf16 roundings of the
+    largest term)."""
     B, H = 2, 2
     G = H if per_head else 1
     wl, inp = small_case(io, B=B, H=H, L=L, D=D, alpha=alpha, seed=81)
@@ -487,10 +490,12 @@ def test_gdn_backward_parity(io, D, L, per_head, alpha):
     torch.cuda.synchronize()
     ref = O.gdn_branch_backward(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], r, d_o, S_init=S0,
                                 dS_final=dS)
+    tol = 1e-4 if io == "f32" else 2e-2
+    errs = {}
     for name, g, rf in zip(("dq", "dk", "dv", "dalpha", "dbeta", "dS_init"), got, ref):
-        e = maxerr(host(g), rf) / max(1.0, np.abs(rf).max())
-        say(f"  {name}: rel err {e:.2e} (max |ref| {np.abs(rf).max():.2e})")
-        assert e <= 1e-4, name
+        errs[name] = maxerr(host(g), rf) / max(1.0, np.abs(rf).max())
+        say(f"  {name}: rel err {errs[name]:.2e} (max |ref| {np.abs(rf).max():.2e})")
+    assert all(e <= tol for e in errs.values()), errs
 
 
 @pytest.mark.parametrize("io,branch,D,per_head,gains", [("f32", "f32", 64, False, False),

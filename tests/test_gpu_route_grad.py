@@ -66,8 +66,9 @@ def test_softmax_gate_gradient(io, D, L, per_head, q_scale):
 
 @pytest.mark.parametrize("io,D,L,per_head", [("f32", 64, 256, False), ("bf16", 128, 384, True)])
 def test_gdn_gate_gradient(io, D, L, per_head):
-    """Every chunk's linear-gate derivative against the oracle; the other
-    gradients are bit-identical with and without it."""
+    """Every chunk's linear-gate derivative against the oracle (fp32 within
+    1e-4 of the largest magnitude, bf16 within 2e-2: bf16 matrix operands);
+    the other gradients are bit-identical with and without it."""
     B, H = 2, 2
     G = H if per_head else 1
     wl, inp = case(io, B, H, L, D, seed=93, alpha=(0.995, 1.0))
@@ -89,7 +90,7 @@ def test_gdn_gate_gradient(io, D, L, per_head):
                                     dS_final=dS, with_gate=True)
     e = rel(host(got[6]), ref)
     say(f"  dgate rel err {e:.3e} (max |ref| {np.abs(ref).max():.3e})")
-    assert e <= 1e-4
+    assert e <= (1e-4 if io == "f32" else 2e-2)
 
 
 @pytest.mark.parametrize("io,d,G,H,L", [("f32", 64, 1, 2, 320), ("bf16", 2048, 1, 4, 512), ("f32", 256, 4, 4, 256)])
