@@ -32,7 +32,7 @@
 //                        S0 and U, bf16 or fp32 as the io dtype
 //   k_gdn_bwd_prep       one workgroup per chunk-head: T, and the fragment
 //                        copies of P^T, -W^T and Q^T the reverse scan reads
-//   k_gdn_bwd_scan       one workgroup per (head, 32-column slice), chunks in
+//   k_gdn_bwd_scan       one workgroup per (head, 16-column slice), chunks in
 //                        reverse: Gc and dU of every chunk, and dS_init
 //   k_gdn_bwd_chunk      one workgroup per chunk-head: dq, dk, dv, dalpha,
 //                        dbeta and the gate derivative
@@ -44,7 +44,7 @@
 
 namespace natsl {
 
-constexpr int BWD_DVT = 32;  // state columns per reverse-scan workgroup
+constexpr int BWD_DVT = 16;  // state columns per reverse-scan workgroup
 constexpr int GM_FLOATS = 144;  // gamma[64], gamma_C at 64, exp(g_C - g)[64] at 80
 
 template <typename T, int D>
@@ -715,42 +715,53 @@ __global__ void __launch_bounds__(256, 1)
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) row_partials(vt[rt], pts + w * 64 + 16 * rt, g, c);
   }
-  // TdU = T^T dU -> dv, X1;  A U -> VmR (held until X1 is free)
+  // TdU = T^T dU -> dv, X1;  A U -> VmR (held until X1 is free).  The B
+  // fragments (columns of dU and U) do not depend on the row tile.
   f32x4 vmr[4][CT];
+  {
+    f32x4 tdu[4][CT], au[4][CT];
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
-    f32x4 tdu[CT], au[CT];
+    for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-      tdu[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-      au[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+      for (int ct = 0; ct < CT; ++ct) {
+        tdu[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+        au[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
       const int t0 = 32 * k2 + 8 * g;
-      const Frag<T> at = frag_fn<T>([&](int j) { return Tl[(t0 + j) * PM + 16 * rt + c]; });
-      const Frag<T> aa = frag_f32<T>(Al + (16 * rt + c) * PM + t0);
+      Frag<T> bdu[CT], bu[CT];
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
         const int col = 16 * (CT * w + ct) + c;
-        const Frag<T> bdu = frag_fn<T>([&](int j) { return to_f32(dUb[(t0 + j) * UP + col]); });
-        const Frag<T> bu = frag_fn<T>([&](int j) { return to_f32(Ub[(t0 + j) * UP + col]); });
-        mma(tdu[ct], at, bdu);
-        mma(au[ct], aa, bu);
+        bdu[ct] = frag_fn<T>([&](int j) { return to_f32(dUb[(t0 + j) * UP + col]); });
+        bu[ct] = frag_fn<T>([&](int j) { return to_f32(Ub[(t0 + j) * UP + col]); });
+      }
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const Frag<T> at = frag_fn<T>([&](int j) { return Tl[(t0 + j) * PM + 16 * rt + c]; });
+        const Frag<T> aa = frag_f32<T>(Al + (16 * rt + c) * PM + t0);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          mma(tdu[rt][ct], at, bdu[ct]);
+          mma(au[rt][ct], aa, bu[ct]);
+        }
       }
     }
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-      const int col = 16 * (CT * w + ct) + c;
+    for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * rt + 4 * g + i;
-        dv[(tok0 + r) * D + col] = bet[r] * tdu[ct][i];
-        vb[rt][i] += to_f32(vc[r * D + col]) * tdu[ct][i];
-        X1[r * PT + col] = from_f32<T>(tdu[ct][i]);
-        vmr[rt][ct][i] = to_f32(Ub[r * UP + col]) + bet[r] * au[ct][i];
+      for (int ct = 0; ct < CT; ++ct) {
+        const int col = 16 * (CT * w + ct) + c;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * rt + 4 * g + i;
+          dv[(tok0 + r) * D + col] = bet[r] * tdu[rt][ct][i];
+          vb[rt][i] += to_f32(vc[r * D + col]) * tdu[rt][ct][i];
+          X1[r * PT + col] = from_f32<T>(tdu[rt][ct][i]);
+          vmr[rt][ct][i] = to_f32(Ub[r * UP + col]) + bet[r] * au[rt][ct][i];
+        }
       }
-    }
   }
   __syncthreads();
   // TdW = -TdU S0^T
@@ -874,27 +885,35 @@ __global__ void __launch_bounds__(256, 1)
   }
   __syncthreads();
 
-  // ---- phase 4 (columns of wave w): E K, E^T K, F K, F^T Q; store dq, dk
+  // ---- phase 4 (columns of wave w): E K, E^T K, F K, F^T Q; store dq, dk.
+  // The B fragments (columns of K and Q) do not depend on the row tile.
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
+  for (int k2 = 0; k2 < 2; ++k2) {
+    const int t0 = 32 * k2 + 8 * g;
+    Frag<T> bk[CT], bq[CT];
 #pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2) {
-      const int t0 = 32 * k2 + 8 * g;
+    for (int ct = 0; ct < CT; ++ct) {
+      const int col = 16 * (CT * w + ct) + c;
+      bk[ct] = frag_fn<T>([&](int j) { return to_f32(Kb[(t0 + j) * UP + col]); });
+      bq[ct] = frag_fn<T>([&](int j) { return to_f32(qc[(t0 + j) * D + col]); });
+    }
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
       const Frag<T> ae = frag_f32<T>(Al + (16 * rt + c) * PM + t0);
       const Frag<T> aet = frag_fn<T>([&](int j) { return Al[(t0 + j) * PM + 16 * rt + c]; });
       const Frag<T> af = frag_f32<T>(Fl + (16 * rt + c) * PM + t0);
       const Frag<T> aft = frag_fn<T>([&](int j) { return Fl[(t0 + j) * PM + 16 * rt + c]; });
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
-        const int col = 16 * (CT * w + ct) + c;
-        const Frag<T> bk = frag_fn<T>([&](int j) { return to_f32(Kb[(t0 + j) * UP + col]); });
-        const Frag<T> bq = frag_fn<T>([&](int j) { return to_f32(qc[(t0 + j) * D + col]); });
-        mma(dka[rt][ct], ae, bk);
-        mma(dka[rt][ct], aet, bk);
-        mma(dqa[rt][ct], af, bk);
-        mma(dka[rt][ct], aft, bq);
+        mma(dka[rt][ct], ae, bk[ct]);
+        mma(dka[rt][ct], aet, bk[ct]);
+        mma(dqa[rt][ct], af, bk[ct]);
+        mma(dka[rt][ct], aft, bq[ct]);
       }
     }
+  }
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
       const int col = 16 * (CT * w + ct) + c;
@@ -905,7 +924,6 @@ __global__ void __launch_bounds__(256, 1)
         dk[o] = dka[rt][ct][i];
       }
     }
-  }
   __syncthreads();
 
   // ---- phase 5 (wave 0, lane = token): dbeta, d log-decay, dalpha, gate
