@@ -856,7 +856,8 @@ def achievable_peaks():
 
 PROFILE_BASE = "python3 bench.py --steps 10 --warmup 2 --no-cpu --no-calib --no-alone --decode-steps 20 --profile-copy"
 PROFILE_PARTS = {  # part -> bench.py command profiled (one rocprofv3 run per pass)
-    "headline": PROFILE_BASE + " --only headline",
+    "headline": PROFILE_BASE + " --only headline --no-extras",
+    "gradients": PROFILE_BASE + " --only headline --no-decode",
     "prefill": PROFILE_BASE + " --only prefill",
     "degen_sm": PROFILE_BASE + " --only degen_sm",
     "degen_lin": PROFILE_BASE + " --only degen_lin",
@@ -869,18 +870,21 @@ PROFILE_PASSES = {  # pass -> rocprofv3 options
     "mfma": "--pmc MfmaUtil MfmaFlopsBF16 SQ_BUSY_CU_CYCLES GRBM_GUI_ACTIVE",
 }
 KERNEL_NAMES = [  # substring of the kernel symbol -> short name
-    ("k_softmax_v2", "softmax_masked"), ("k_route", "route"), ("k_compact", "compact"), ("k_gdn_prep", "gdn_prep"),
-    ("k_gdn_scan", "gdn_scan"), ("k_mergeI", "merge"), ("k_decode_route", "decode_route"),
+    ("k_softmax_v2", "softmax_masked"), ("k_route_bwd_x", "route_bwd_x"), ("k_route_bwd_w_final", "route_bwd_w_final"),
+    ("k_route_bwd_w", "route_bwd_w"), ("k_route", "route"), ("k_compact", "compact"), ("k_gdn_prep", "gdn_prep"),
+    ("k_gdn_scan_headIDF16bLi4ELi2ELb1", "gdn_state_scan"), ("k_gdn_scan_head<__bf16, 4, 2, true>", "gdn_state_scan"),
+    ("k_gdn_scan", "gdn_scan"), ("k_gdn_bwd_prep", "gdn_bwd_prep"), ("k_gdn_bwd_scan", "gdn_bwd_scan"),
+    ("k_gdn_bwd_chunk", "gdn_bwd_chunk"), ("k_mergeI", "merge"), ("k_decode_route", "decode_route"),
     ("k_decode_gdn", "decode_gdn"), ("k_decode_attn", "decode_attn"), ("k_decode_combine", "decode_combine"),
     ("k_decode_commit", "decode_commit"), ("k_handoff_state", "handoff_state"), ("k_handoff_kv", "handoff_kv"),
     ("k_sm_bwd_delta", "sm_bwd_delta"), ("k_sm_bwd_dq", "sm_bwd_dq"), ("k_sm_bwd_dkdv", "sm_bwd_dkdv"),
-    ("k_gdn_bwd_ckpt", "gdn_bwd_ckpt"), ("k_gdn_bwdI", "gdn_bwd"), ("k_gdn_bwd_reduce", "gdn_bwd_reduce"),
     ("k_merge_bwd_reduce", "merge_bwd_reduce"), ("k_merge_bwd_final", "merge_bwd_final"), ("k_merge_bwdI", "merge_bwd"),
     ("k_softmax_masked", "nha_window"), ("k_nha_chunk", "nha_chunk"), ("k_nha_scan", "nha_scan"),
     ("k_nha_slots", "nha_slots"),
     ("AUnaryFunctor<float, float", "calib_mul_256MiB"), ("Cijk_", "calib_gemm_bf16_4096"),
 ]
-MFMA_KERNELS = ("softmax_masked", "gdn_prep", "gdn_scan", "sm_bwd_dq", "sm_bwd_dkdv", "calib_gemm_bf16_4096")
+MFMA_KERNELS = ("softmax_masked", "gdn_prep", "gdn_scan", "sm_bwd_dq", "sm_bwd_dkdv", "gdn_bwd_prep", "gdn_bwd_scan",
+                "gdn_bwd_chunk", "gdn_state_scan", "calib_gemm_bf16_4096")
 
 
 def profile_commands(part):
