@@ -975,7 +975,7 @@ def summarize_profiles(d):
                   "| kernel | calls | avg us | min us | max us | HBM read MB/launch | HBM write MB/launch | MfmaUtil % "
                   "| executed bf16 MFMA TFLOP/s |",
                   "|---|---|---|---|---|---|---|---|---|"]
-        for _, n in KERNEL_NAMES:
+        for n in dict.fromkeys(n for _, n in KERNEL_NAMES):
             if n in stats:
                 st = stats[n]
                 mu, fl = mf(n, "MfmaUtil"), mf(n, "MfmaFlopsBF16")
