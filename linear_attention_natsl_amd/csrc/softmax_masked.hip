@@ -1047,6 +1047,277 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) k_sm_bwd_dkdv(con
   }
 }
 
+// bf16, D = 128: dQ with the key tiles streamed straight from global memory
+// into a 2-stage LDS ring (global_load_lds_dwordx4, one tile ahead); K rows
+// carry the forward's V swizzle (row reads for S^T = K Q^T, transposed reads
+// for dQ^T += K^T dS^T), V rows its K swizzle (row reads for dP^T = V dO^T).
+// The tile list sits in LDS so that its reads stay out of the vector-memory
+// counter.  Up to DQ2_LIST visible key tiles (L <= 262144).
+constexpr int DQ2_TILE = 2 * CHUNK * 128 * 2;
+constexpr int DQ2_LIST = 4096;
+constexpr int DQ2_LDS = 2 * DQ2_TILE + 4 * DQ2_LIST;
+__global__ void __launch_bounds__(256, 2)
+    k_sm_bwd_dq2(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+                 const bf16* __restrict__ d_o, const int32_t* __restrict__ sel_idx,
+                 const int32_t* __restrict__ nsel_before, const float* __restrict__ lse,
+                 const float* __restrict__ delta, float* __restrict__ dq, int H, int L, int G, float scale) {
+  constexpr int D = 128;
+  extern __shared__ __align__(16) unsigned char lds[];
+  int32_t* sel_l = reinterpret_cast<int32_t*>(lds + 2 * DQ2_TILE);
+  const int nc = L / CHUNK;
+  const int BH = (int)(grid_dim_x() / nc);
+  const int p = bid_x();
+  const int qc = nc - 1 - p / BH;  // later query chunks see more keys: first
+  const int bh = p % BH;
+  const int b = bh / H, h = bh % H;
+  const int grp = (G == 1) ? 0 : h;
+  const int32_t* sel = sel_idx + ((int64_t)b * G + grp) * nc;
+  const int nsb = nsel_before[((int64_t)b * G + grp) * (nc + 1) + qc];
+  const int lane = lane_id(), w = wave_id();
+  const int g = lane >> 4, c = lane & 15;
+  const int64_t head_off = (int64_t)bh * L * D;
+  const int64_t tok = (int64_t)qc * CHUNK + 16 * w + c;
+  Frag<bf16> qf[4], df[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    qf[ks] = load8<bf16>(q + head_off + tok * D + 32 * ks + 8 * g);
+    df[ks] = load8<bf16>(d_o + head_off + tok * D + 32 * ks + 8 * g);
+  }
+  const float lse2 = lse[(int64_t)bh * L + tok] * LOG2E;
+  const float dlt = delta[(int64_t)bh * L + tok];
+  for (int i = tid_x(); i < nsb; i += 256) sel_l[i] = sel[i];
+  if (tid_x() == 0) sel_l[nsb] = qc;
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): nothing of ours outstanding before the ring starts
+  __syncthreads();
+  const float scale_log2 = scale * LOG2E;
+  const int qrow = 16 * w + c;
+  f32x4 acc[D / 16];
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nt = nsb + 1;
+  auto issue = [&](int it) {
+    const int kc = sel_l[it];
+    unsigned char* st = lds + (it & 1) * DQ2_TILE;
+    const bf16* kg = k + head_off + (int64_t)kc * CHUNK * D;
+    const bf16* vg = v + head_off + (int64_t)kc * CHUNK * D;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e0 = w * 256 + i * 64;
+      const int e = e0 + lane, r = e >> 4, sl = e & 15;
+      gload_lds16(kg + r * D + sm2_vslot(r, sl) * 8, st + e0 * 16);
+      gload_lds16(vg + r * D + sm2_kslot(r, sl) * 8, st + CHUNK * D * 2 + e0 * 16);
+    }
+  };
+  issue(0);
+  for (int it = 0; it < nt; ++it) {
+    const bool diag = it == nsb;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // this tile's loads have landed
+    lds_barrier();                       // ... for every wave; every wave is done with tile it - 1
+    if (it + 1 < nt) issue(it + 1);
+    const unsigned char* st = lds + opaque_sgpr((it & 1) * DQ2_TILE);
+    const unsigned char* ks_l = st;
+    const unsigned char* vs_l = st + CHUNK * D * 2;
+    f32x4 s_[4], dp[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) s_[kt] = dp[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const int r = 16 * kt + c;
+        mma(s_[kt], *reinterpret_cast<const Frag<bf16>*>(ks_l + r * 256 + sm2_vslot(r, 4 * ks + g) * 16), qf[ks]);
+        mma(dp[kt], *reinterpret_cast<const Frag<bf16>*>(vs_l + r * 256 + sm2_kslot(r, 4 * ks + g) * 16), df[ks]);
+      }
+    // dS^T = P^T (dP^T - delta), packed as the B operand (keys in accumulator order)
+    Frag<bf16> dsf[2];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool vis = !diag || (16 * kt + 4 * g + i) <= qrow;
+        const float pp = vis ? __builtin_amdgcn_exp2f(fmaf(s_[kt][i], scale_log2, -lse2)) : 0.f;
+        frag_set(dsf[kt >> 1], 4 * (kt & 1) + i, pp * (dp[kt][i] - dlt));
+      }
+    // dQ^T += K^T dS^T: K^T fragments by transposed reads (rows d = 16 dt + c,
+    // keys 32 k2 + 4g + j and 32 k2 + 16 + 4g + j)
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      const int r0 = 32 * k2 + 4 * g + (c >> 2), r1 = r0 + 16;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) {
+        const int colq = (16 * dt + 4 * (c & 3)) >> 3;
+        const int half = (c & 1) * 8;
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4i16*)(ks_l + r0 * 256 + sm2_vslot(r0, colq) * 16 + half));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4i16*)(ks_l + r1 * 256 + sm2_vslot(r1, colq) * 16 + half));
+        Frag<bf16> a;
+        a.v = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        mma(acc[dt], a, dsf[k2]);
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // no load may still be in flight into LDS at the end
+  float* out = dq + head_off + tok * D;
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) {
+    f32x4 r = acc[dt] * scale;
+    *reinterpret_cast<f32x4*>(out + 16 * dt + 4 * g) = r;
+  }
+}
+
+// bf16, D = 128: the same products with Q and dO streamed straight from
+// global memory into an NSTG-stage LDS ring (global_load_lds_dwordx4, one
+// tile ahead), rows stored with the forward's V swizzle (chunk q of row r at
+// slot q ^ ((r & 7) << 1)): row reads give the A operands of S = Q K^T and
+// dP = dO V^T, transposed reads (ds_read_b64_tr_b16) the A operands of
+// dV^T += dO^T P and dK^T += Q^T dS.  One barrier per query chunk, no
+// register staging; lse and delta of the chunk ride in the same ring.
+constexpr int DK2_STAGES = 2;
+constexpr int DK2_TILE = 2 * CHUNK * 128 * 2 + 1024;  // Q, dO rows; lse, delta (+ two scratch slots)
+constexpr int DK2_LDS = DK2_STAGES * DK2_TILE + 16;
+__global__ void __launch_bounds__(256, 2)
+    k_sm_bwd_dkdv2(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+                   const bf16* __restrict__ d_o, const int32_t* __restrict__ nsel_before,
+                   const float* __restrict__ lse, const float* __restrict__ delta, float* __restrict__ dk,
+                   float* __restrict__ dv, int H, int L, int G, float scale, float* __restrict__ dgate) {
+  constexpr int D = 128;
+  extern __shared__ __align__(16) unsigned char lds[];
+  float* red = reinterpret_cast<float*>(lds + DK2_STAGES * DK2_TILE);
+  const int nc = L / CHUNK;
+  const int BH = (int)(grid_dim_x() / nc);
+  const int p = bid_x();
+  const int kc = p / BH;  // earlier key chunks are seen by more queries: first
+  const int bh = p % BH;
+  const int b = bh / H, h = bh % H;
+  const int grp = (G == 1) ? 0 : h;
+  const int32_t* nsbp = nsel_before + ((int64_t)b * G + grp) * (nc + 1);
+  const bool kc_sm = nsbp[kc + 1] > nsbp[kc];
+  const int qlast = (kc_sm || dgate) ? nc - 1 : kc;
+  const int ntl = qlast - kc + 1;
+  float gsum = 0.f;
+  const int lane = lane_id(), w = wave_id();
+  const int g = lane >> 4, c = lane & 15;
+  const int64_t head_off = (int64_t)bh * L * D;
+  const int64_t key = (int64_t)kc * CHUNK + 16 * w + c;
+  Frag<bf16> kf[4], vf[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    kf[ks] = load8<bf16>(k + head_off + key * D + 32 * ks + 8 * g);
+    vf[ks] = load8<bf16>(v + head_off + key * D + 32 * ks + 8 * g);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): nothing of ours outstanding before the ring starts
+  const float scale_log2 = scale * LOG2E;
+  const int kcol = 16 * w + c;
+  f32x4 adk[D / 16], adv[D / 16];
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) adk[dt] = adv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // tile j (query chunk kc + j) -> stage j % DK2_STAGES: per wave 4 + 4
+  // row-block loads and one 256-byte vector load (waves 0 / 1: lse / delta,
+  // waves 2 / 3 the same into scratch slots, so every wave counts 9 loads)
+  auto issue = [&](int j) {
+    const int qcx = kc + j;
+    unsigned char* st = lds + (j % DK2_STAGES) * DK2_TILE;
+    const bf16* qg = q + head_off + (int64_t)qcx * CHUNK * D;
+    const bf16* dg = d_o + head_off + (int64_t)qcx * CHUNK * D;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e0 = w * 256 + i * 64;
+      const int e = e0 + lane, r = e >> 4, sl = e & 15;
+      gload_lds16(qg + r * D + sm2_vslot(r, sl) * 8, st + e0 * 16);
+      gload_lds16(dg + r * D + sm2_vslot(r, sl) * 8, st + CHUNK * D * 2 + e0 * 16);
+    }
+    const float* src = ((w & 1) ? delta : lse) + (int64_t)bh * L + (int64_t)qcx * CHUNK + 4 * (lane & 15);
+    if (lane < 16) gload_lds16(src, st + 2 * CHUNK * D * 2 + w * 256);
+  };
+  __syncthreads();
+  issue(0);
+  for (int j = 0; j < ntl; ++j) {
+    const int qcx = kc + j;
+    const bool diag = qcx == kc;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // this tile's loads have landed (vmcnt(0))
+    lds_barrier();                       // ... for every wave; every wave is done with tile j - 1
+    if (j + 1 < ntl) issue(j + 1);       // into the stage tile j - 1 used
+    const unsigned char* st = lds + opaque_sgpr((j % DK2_STAGES) * DK2_TILE);
+    const unsigned char* qs_l = st;
+    const unsigned char* ds_l = st + CHUNK * D * 2;
+    const float* lse_s = reinterpret_cast<const float*>(st + 2 * CHUNK * D * 2);
+    const float* dlt_s = lse_s + CHUNK;
+    f32x4 pm[4], dsm[4];
+#pragma unroll
+    for (int qt = 0; qt < 4; ++qt) {
+      f32x4 s_ = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+      const int r = 16 * qt + c;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int off = r * 256 + sm2_vslot(r, 4 * ks + g) * 16;
+        mma(s_, *reinterpret_cast<const Frag<bf16>*>(qs_l + off), kf[ks]);
+        mma(dp, *reinterpret_cast<const Frag<bf16>*>(ds_l + off), vf[ks]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int qrow = 16 * qt + 4 * g + i;
+        const bool vis = !diag || kcol <= qrow;
+        const float pp = vis ? __builtin_amdgcn_exp2f(fmaf(s_[i], scale_log2, -lse_s[qrow] * LOG2E)) : 0.f;
+        pm[qt][i] = pp;
+        dsm[qt][i] = pp * (dp[i] - dlt_s[qrow]);
+        if (!diag) gsum += dsm[qt][i];
+      }
+    }
+    if (!diag && !kc_sm) continue;  // only the gate's sum: these keys are not visible in the forward
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      Frag<bf16> pf, dsf;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        frag_set(pf, jj, pm[2 * k2][jj]);
+        frag_set(pf, 4 + jj, pm[2 * k2 + 1][jj]);
+        frag_set(dsf, jj, dsm[2 * k2][jj]);
+        frag_set(dsf, 4 + jj, dsm[2 * k2 + 1][jj]);
+      }
+      // dO^T and Q^T fragments (rows d = 16 dt + c, queries 32 k2 + 4g + j
+      // and 32 k2 + 16 + 4g + j) by transposed reads: lane c of group g reads
+      // row 32 k2 + 4g + c / 4 (+16), columns 16 dt + 4 (c % 4) .. +3
+      const int r0 = 32 * k2 + 4 * g + (c >> 2), r1 = r0 + 16;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) {
+        const int colq = (16 * dt + 4 * (c & 3)) >> 3;
+        const int half = (c & 1) * 8;
+        const int o0 = r0 * 256 + sm2_vslot(r0, colq) * 16 + half, o1 = r1 * 256 + sm2_vslot(r1, colq) * 16 + half;
+        Frag<bf16> ad, aq;
+        {
+          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(ds_l + o0));
+          const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(ds_l + o1));
+          ad.v = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+        {
+          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(qs_l + o0));
+          const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(qs_l + o1));
+          aq.v = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+        mma(adv[dt], ad, pf);
+        mma(adk[dt], aq, dsf);
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // no load may still be in flight into LDS at the end
+  float* okr = dk + head_off + key * D;
+  float* ovr = dv + head_off + key * D;
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) {
+    f32x4 r = adk[dt] * scale;
+    *reinterpret_cast<f32x4*>(okr + 16 * dt + 4 * g) = r;
+    *reinterpret_cast<f32x4*>(ovr + 16 * dt + 4 * g) = adv[dt];
+  }
+  if (dgate) {  // the wave sums, then the 4 waves in order (deterministic)
+    gsum = wave_sum64(gsum);
+    if (lane == 0) red[w] = gsum;
+    __syncthreads();
+    if (tid_x() == 0) dgate[(int64_t)bh * nc + kc] = (red[0] + red[1]) + (red[2] + red[3]);
+  }
+}
+
 size_t sm_bwd_ws_bytes(int B, int H, int L) { return (size_t)B * H * L * sizeof(float); }
 
 template <typename T, typename To, int D>
@@ -1071,11 +1342,23 @@ hipError_t launch_softmax_backward(const T* q, const T* k, const T* v, const int
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t grid = (int64_t)B * H * nc;
-  hipLaunchKernelGGL((k_sm_bwd_dq<T, D>), dim3((unsigned)grid), dim3(256), LDS_DQ, st, q, k, v, d_o, sel_idx,
-                     nsel_before, lse, delta, dq, H, L, G, scale);
+  if (sizeof(T) == 2 && D == 128 && nc <= DQ2_LIST) {
+    if ((e = set_lds_limit((const void*)k_sm_bwd_dq2, DQ2_LDS)) != hipSuccess) return e;
+    hipLaunchKernelGGL(k_sm_bwd_dq2, dim3((unsigned)grid), dim3(256), DQ2_LDS, st, (const bf16*)q, (const bf16*)k,
+                       (const bf16*)v, (const bf16*)d_o, sel_idx, nsel_before, lse, delta, dq, H, L, G, scale);
+  } else {
+    hipLaunchKernelGGL((k_sm_bwd_dq<T, D>), dim3((unsigned)grid), dim3(256), LDS_DQ, st, q, k, v, d_o, sel_idx,
+                       nsel_before, lse, delta, dq, H, L, G, scale);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((k_sm_bwd_dkdv<T, D>), dim3((unsigned)grid), dim3(256), LDS_DKDV, st, q, k, v, d_o,
-                     nsel_before, lse, delta, dk, dv, H, L, G, scale, dgate);
+  if constexpr (sizeof(T) == 2 && D == 128) {
+    if ((e = set_lds_limit((const void*)k_sm_bwd_dkdv2, DK2_LDS)) != hipSuccess) return e;
+    hipLaunchKernelGGL(k_sm_bwd_dkdv2, dim3((unsigned)grid), dim3(256), DK2_LDS, st, (const bf16*)q, (const bf16*)k,
+                       (const bf16*)v, (const bf16*)d_o, nsel_before, lse, delta, dk, dv, H, L, G, scale, dgate);
+  } else {
+    hipLaunchKernelGGL((k_sm_bwd_dkdv<T, D>), dim3((unsigned)grid), dim3(256), LDS_DKDV, st, q, k, v, d_o,
+                       nsel_before, lse, delta, dk, dv, H, L, G, scale, dgate);
+  }
   return hipGetLastError();
 }
 
