@@ -388,6 +388,9 @@ __global__ void __launch_bounds__(256, 2)
 // 16-bit values across each group of 16 lanes.
 // One workgroup = 8 waves = 4 chunks; waves 2m and 2m+1 own the 64 queries of
 // chunk c0 + m (32 each), so register use matches the kernel above.
+// Window mode (win > 0 chunks, no routes): the key tiles are chunks c0 - win
+// .. c0 + 3, newest first, so that every query's first visible tile is its
+// own (causal) chunk; chunk c - win keeps only keys past the query's offset.
 constexpr int SM2_STAGES = 4;
 constexpr int SM2_TILE_BYTES = 2 * CHUNK * 128 * 2;  // K + V, bf16, D = 128
 constexpr int SM2_LIST = 4096;  // key-tile list entries (prefix tiles + softmax chunks + own chunks)
@@ -403,7 +406,7 @@ __global__ void __launch_bounds__(512, 1)
                  const int32_t* __restrict__ sel_idx, const int32_t* __restrict__ nsel_before,
                  To* __restrict__ o_sm, float* __restrict__ lse, int H, int L, int G, float scale_log2,
                  const bf16* __restrict__ pre_k, const bf16* __restrict__ pre_v, const int32_t* __restrict__ pnc,
-                 int pcap, const float* __restrict__ w_mix, int64_t wmix_hs, float* __restrict__ mixd) {
+                 int pcap, const float* __restrict__ w_mix, int64_t wmix_hs, float* __restrict__ mixd, int win) {
   constexpr int D = 128;
   extern __shared__ __align__(16) unsigned char lds[];
   int32_t* sel_l = reinterpret_cast<int32_t*>(lds + SM2_STAGES * SM2_TILE_BYTES);
@@ -423,19 +426,24 @@ __global__ void __launch_bounds__(512, 1)
   }
   const int b = bh / H, h = bh % H;
   const int grp = (G == 1) ? 0 : h;
-  const int32_t* sel = sel_idx + ((int64_t)b * G + grp) * nc;
-  const int32_t* nsbp = nsel_before + ((int64_t)b * G + grp) * (nc + 1);
   const int c0 = 4 * qblk;
   const int nown = min(4, nc - c0);
   // key tiles: the prefix cache's rows (npre tiles), the softmax chunks
   // before c0, then the block's own chunks
   // (rows of a cache that overflowed were never written: at most cap rows)
-  const int npre = pnc ? min(pnc[(int64_t)b * G + grp], pcap) / CHUNK : 0;
-  const int nsel = nsbp[c0];
-  const int nsb = npre + nsel;
-  const int ntiles = nsb + nown;
-  int sm_bits = 0;
-  for (int j = 0; j < nown; ++j) sm_bits |= (nsbp[c0 + j + 1] > nsbp[c0 + j]) ? (1 << j) : 0;
+  int npre = 0, nsel = 0, nsb = 0, ntiles, sm_bits = 0;
+  const int32_t* sel = nullptr;
+  if (win > 0) {
+    ntiles = c0 + nown - max(0, c0 - win);
+  } else {
+    sel = sel_idx + ((int64_t)b * G + grp) * nc;
+    const int32_t* nsbp = nsel_before + ((int64_t)b * G + grp) * (nc + 1);
+    npre = pnc ? min(pnc[(int64_t)b * G + grp], pcap) / CHUNK : 0;
+    nsel = nsbp[c0];
+    nsb = npre + nsel;
+    ntiles = nsb + nown;
+    for (int j = 0; j < nown; ++j) sm_bits |= (nsbp[c0 + j + 1] > nsbp[c0 + j]) ? (1 << j) : 0;
+  }
 
   const int lane = lane_id(), w = wave_id();
   const int g = lane >> 4, c = lane & 15;
@@ -447,9 +455,13 @@ __global__ void __launch_bounds__(512, 1)
 
   // tile list in LDS (keeps its reads out of the vector-memory counter):
   // prefix tile j is stored as -1 - j
-  for (int i = tid_x(); i < npre; i += 512) sel_l[i] = -1 - i;
-  for (int i = tid_x(); i < nsel; i += 512) sel_l[npre + i] = sel[i];
-  for (int i = tid_x(); i < nown; i += 512) sel_l[nsb + i] = c0 + i;
+  if (win > 0) {
+    for (int i = tid_x(); i < ntiles; i += 512) sel_l[i] = c0 + nown - 1 - i;  // newest first
+  } else {
+    for (int i = tid_x(); i < npre; i += 512) sel_l[i] = -1 - i;
+    for (int i = tid_x(); i < nsel; i += 512) sel_l[npre + i] = sel[i];
+    for (int i = tid_x(); i < nown; i += 512) sel_l[nsb + i] = c0 + i;
+  }
   const int64_t pre_off = (int64_t)bh * pcap * D;
 
   Frag<bf16> qf[2][4];
@@ -505,7 +517,10 @@ __global__ void __launch_bounds__(512, 1)
     if (it + SM2_STAGES - 1 < ntiles) issue(it + SM2_STAGES - 1);  // into the stage read last iteration
 
     int mode;
-    if (it < nsb) {
+    if (win > 0) {
+      const int dm = mch - (nown - 1 - it);  // query chunk - key chunk
+      mode = dm < 0 ? MODE_SKIP : dm == 0 ? MODE_DIAG : dm < win ? MODE_FULL : dm == win ? MODE_WSTART : MODE_SKIP;
+    } else if (it < nsb) {
       mode = MODE_FULL;
     } else {
       const int j = it - nsb;
@@ -568,6 +583,14 @@ __global__ void __launch_bounds__(512, 1)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             if ((16 * kt + 4 * g + i) > qrow_base + 16 * qs + c) s[kt][qs][i] = -INFINITY;
+    } else if (mode == MODE_WSTART) {  // only keys past the window's start
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if ((16 * kt + 4 * g + i) <= qrow_base + 16 * qs + c) s[kt][qs][i] = -INFINITY;
     }
     // tile max per query (its 4 lane groups hold 16 keys each), one rescale
     // decision for the wave
@@ -681,7 +704,7 @@ hipError_t launch_softmax_masked(const T* q, const T* k, const T* v, const int32
       hipLaunchKernelGGL(k_softmax_v2<To>, dim3((unsigned)grid), dim3(512), SM2_LDS, st, (const bf16*)q,
                          (const bf16*)k, (const bf16*)v, sel_idx, nsel_before, o_sm, lse, H, L, G, scale * LOG2E,
                          (const bf16*)pre.k, (const bf16*)pre.v, pre.n_committed, pre.cap, mix.w_mix, mix.hs,
-                         mix.w_mix ? mix.d : nullptr);
+                         mix.w_mix ? mix.d : nullptr, 0);
       e = hipGetLastError();
       if (e == hipSuccess && mix.done) *mix.done = mix.w_mix && mix.d;
       return e;
@@ -703,9 +726,21 @@ hipError_t launch_softmax_window(const T* q, const T* k, const T* v, To* o, floa
                                  int win_chunks, float scale, hipStream_t st) {
   using C = SmCfg<T, D>;
   if (win_chunks < 1) return hipErrorInvalidValue;
+  const int nc = L / CHUNK;
+  if constexpr (sizeof(T) == 2 && D == 128) {
+    if (min(nc, win_chunks + 4) <= SM2_LIST) {  // the fast kernel's tile list holds the window
+      const hipError_t e = set_lds_limit((const void*)k_softmax_v2<To>, SM2_LDS);
+      if (e != hipSuccess) return e;
+      const int64_t grid = (int64_t)B * H * ((nc + 3) / 4);
+      hipLaunchKernelGGL(k_softmax_v2<To>, dim3((unsigned)grid), dim3(512), SM2_LDS, st, (const bf16*)q,
+                         (const bf16*)k, (const bf16*)v, (const int32_t*)nullptr, (const int32_t*)nullptr, o, lse, H,
+                         L, 1, scale * LOG2E, (const bf16*)nullptr, (const bf16*)nullptr, (const int32_t*)nullptr, 0,
+                         (const float*)nullptr, (int64_t)0, (float*)nullptr, win_chunks);
+      return hipGetLastError();
+    }
+  }
   const hipError_t ea = set_lds_limit((const void*)k_softmax_masked<T, To, D>, C::LDS_BYTES);
   if (ea != hipSuccess) return ea;
-  const int nc = L / CHUNK;
   const int64_t grid = (int64_t)B * H * ((nc + 1) / 2);
   hipLaunchKernelGGL((k_softmax_masked<T, To, D>), dim3((unsigned)grid), dim3(256), C::LDS_BYTES, st, q, k, v,
                      (const int32_t*)nullptr, (const int32_t*)nullptr, o, lse, H, L, 1, scale * LOG2E,
