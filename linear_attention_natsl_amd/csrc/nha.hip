@@ -33,6 +33,41 @@
 
 namespace natsl {
 
+template <typename T, typename Fn>
+__device__ __forceinline__ Frag<T> frag_fn_nha(Fn fn) {
+  Frag<T> f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) frag_set(f, j, fn(j));
+  return f;
+}
+// 4 + 4 contiguous elements (two key groups of one column) -> one fragment
+template <typename T> __device__ __forceinline__ Frag<T> ld4x2_nha(const T* p0, const T* p1);
+template <> __device__ __forceinline__ Frag<bf16> ld4x2_nha<bf16>(const bf16* p0, const bf16* p1) {
+  const bf16x4 a = *reinterpret_cast<const bf16x4*>(p0);
+  const bf16x4 b = *reinterpret_cast<const bf16x4*>(p1);
+  Frag<bf16> f;
+  f.v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return f;
+}
+template <> __device__ __forceinline__ Frag<float> ld4x2_nha<float>(const float* p0, const float* p1) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p0);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(p1);
+  Frag<float> f;
+  f.v[0] = a[0]; f.v[1] = a[1]; f.v[2] = a[2]; f.v[3] = a[3];
+  f.v[4] = b[0]; f.v[5] = b[1]; f.v[6] = b[2]; f.v[7] = b[3];
+  return f;
+}
+// 4 values of one column (a key group) -> 4 contiguous elements
+template <typename T> __device__ __forceinline__ void st4(T* p, float a, float b, float c, float d);
+template <> __device__ __forceinline__ void st4<bf16>(bf16* p, float a, float b, float c, float d) {
+  const bf16x4 v4 = {(bf16)a, (bf16)b, (bf16)c, (bf16)d};
+  *reinterpret_cast<bf16x4*>(p) = v4;
+}
+template <> __device__ __forceinline__ void st4<float>(float* p, float a, float b, float c, float d) {
+  const f32x4 v4 = {a, b, c, d};
+  *reinterpret_cast<f32x4*>(p) = v4;
+}
+
 // per (b, h, chunk e < ne): the slots' change over the chunk and its decay
 template <typename T, int D, int M>
 __global__ void __launch_bounds__(256) k_nha_chunk(const T* __restrict__ k, const T* __restrict__ v,
@@ -134,30 +169,62 @@ __global__ void __launch_bounds__(256) k_nha_scan(NhaWs ws, int BH, int ne) {
 }
 
 // per (b, h, query chunk c): slot scores, one softmax with the window, the
-// slot read-out and the merge.  o_w / lse_w: the window's normalised output
-// and natural-log logsumexp (NULL: empty window, w = 0).
+// slot read-out and the merge, on the matrix cores where the work is a
+// product.  o_w / lse_w: the window's normalised output and natural-log
+// logsumexp (NULL: empty window, w = 0).  With Gamma[j][i] = prod_{r<=j}
+// a_r[i] over chunk e's tokens and P the slot weights of the softmax:
+//   X = Q [K~_e; K_e]^T                       (matrix cores)
+//   z_j[i] by the recurrence over chunk e's tokens, softmax      (vector)
+//   R[j][s] = sum_i P[j][i] (1 - a_s[i]) prod_{s<r<=j} a_r[i]   (vector, s <= j)
+//   O = (P * Gamma) V~_e + R V_e + w_win o_w                    (matrix cores)
+// R and Gamma come from running products (gates of exactly 0 or 1 stay exact).
+// The slot states (fp32) enter the bf16 products as hi + lo parts.
+template <typename T, int D, int M>
+struct NhaSlotCfg {
+  static constexpr int MP = M < 32 ? 32 : M;        // slots padded to the 32-deep contraction
+  static constexpr int P = D + 16 / (int)sizeof(T);  // row pitch (elements)
+  static constexpr int RL = kg_row<T, D>();
+  static constexpr int KGB = 16 * RL * 4 * (int)sizeof(T);         // key groups of 64 rows
+  static constexpr int KGBM = (MP / 4) * RL * 4 * (int)sizeof(T);  // key groups of MP rows
+  static constexpr bool SPLIT = sizeof(T) == 2;
+  // region 0: Q rows, [K~_e hi; K_e] rows, K~_e lo rows (scores); then the
+  // key groups of V_e and of V~_e hi / lo (read-out)
+  static constexpr int R0A = (CHUNK + M + CHUNK + (SPLIT ? M : 0)) * P * (int)sizeof(T);
+  static constexpr int R0B = KGB + KGBM * (SPLIT ? 2 : 1);
+  static constexpr int R0 = ((R0A > R0B ? R0A : R0B) + 15) & ~15;
+  static constexpr int OFF_A = R0;                        // fp32 [64][M] gates of chunk e
+  static constexpr int OFF_XS = OFF_A + CHUNK * M * 4;    // fp32 [64 j][M] X's slot part, P, P * Gamma
+  static constexpr int OFF_QK = OFF_XS + CHUNK * M * 4;   // fp32 [64 s][64 j] q_j.k_s, then R [64 j][64 s]
+  static constexpr int OFF_WW = OFF_QK + CHUNK * CHUNK * 4;
+  static constexpr int LDS = OFF_WW + CHUNK * 4;
+  static_assert(LDS <= 160 * 1024, "LDS");
+};
+
 template <typename T, typename To, int D, int M>
 __global__ void __launch_bounds__(256) k_nha_slots(const T* __restrict__ q, const T* __restrict__ k,
                                                    const T* __restrict__ v, const float* __restrict__ gate,
                                                    NhaWs ws, const float* __restrict__ o_w,
                                                    const float* __restrict__ lse_w, To* __restrict__ out, int L,
                                                    int nw, int ne, float scale) {
-  constexpr int DP = D + 4;           // padded LDS row (16-byte aligned, rows spread over the banks)
-  constexpr int NCOL = M + CHUNK;     // columns of the score products: M slots, then the chunk's 64 keys
-  constexpr int TPC = 256 / D, SPT = M / TPC;
-  extern __shared__ __align__(16) float sh[];
-  float* Qs = sh;                     // [64][DP]   queries
-  float* KC = Qs + CHUNK * DP;        // [NCOL][DP] slot keys K~_e, then chunk e's keys
-  float* A = KC + NCOL * DP;          // [64][M]    gates of chunk e's tokens
-  float* XS = A + CHUNK * M;          // [64 j][M]  q_j.K~_e[i], then P[j][i]
-  float* QKT = XS + CHUNK * M;        // [64 s][64 j] q_j.k_s (transposed: a step s reads its queries' row)
-  float* WW = QKT + CHUNK * CHUNK;    // [64] the window's weight per query
+  using C = NhaSlotCfg<T, D, M>;
+  constexpr int P = C::P, KF = D / 32, NCT = (M + CHUNK) / 16, MS = M / 16;
+  extern __shared__ __align__(16) unsigned char lds[];
+  T* Qs = reinterpret_cast<T*>(lds);
+  T* KS = Qs + CHUNK * P;       // M slot rows (hi), then chunk e's 64 key rows
+  T* KL = KS + (M + CHUNK) * P;  // M slot rows (lo)
+  T* Vg = reinterpret_cast<T*>(lds);
+  T* VTh = reinterpret_cast<T*>(lds + C::KGB);
+  T* VTl = reinterpret_cast<T*>(lds + C::KGB + C::KGBM);
+  float* A = reinterpret_cast<float*>(lds + C::OFF_A);
+  float* XS = reinterpret_cast<float*>(lds + C::OFF_XS);
+  float* QK = reinterpret_cast<float*>(lds + C::OFF_QK);
+  float* WW = reinterpret_cast<float*>(lds + C::OFF_WW);
   const int nc = L / CHUNK;
   const int64_t bh = bid_x() / nc;
-  const int c = bid_x() % nc;
-  const int e = c - nw;
+  const int qc = bid_x() % nc;
+  const int e = qc - nw;
   const int tid = tid_x();
-  const int64_t row0 = bh * L + (int64_t)c * CHUNK;
+  const int64_t row0 = bh * L + (int64_t)qc * CHUNK;
   if (e < 0) {  // no token has left the window yet: the window's result stands
     constexpr int NO = CHUNK * D / 4 / 256;
     f32x4 ov[NO];
@@ -171,74 +238,122 @@ __global__ void __launch_bounds__(256) k_nha_slots(const T* __restrict__ q, cons
     return;
   }
   const int64_t erow0 = bh * L + (int64_t)e * CHUNK;
-  // ---- stage q (chunk c), K~_e and chunk e's keys, chunk e's gates: every
-  // load of the thread is issued before the first LDS store (a load, then its
-  // store, one after the other kept a single load in flight per wave)
+  const int lane = lane_id(), w = wave_id();
+  const int g = lane >> 4, c = lane & 15;
+  const float* Ske = ws.Sk + (bh * ne + e) * M * D;
+  const float* Sve = ws.Sv + (bh * ne + e) * M * D;
+
+  // ---- staging: every load is issued before the first LDS store; the read-
+  // out's operands (V_e rows, V~_e rows) are loaded now and stored after the
+  // score products
+  constexpr int NQ = CHUNK * D / 8 / 256;          // 8-element pieces of q, k per thread
+  constexpr int NSK = (M * D / 8 + 255) / 256;     // 8-float pieces of K~_e per thread
+  constexpr int NA = (CHUNK * M / 4 + 255) / 256;  // 4-float pieces of the gates per thread
+  constexpr int VT = (CHUNK / 4) * (D / 8);        // (key group, 8 columns) tasks of V_e
+  constexpr int ST = (C::MP / 4) * (D / 8);        // ... of V~_e (rows past M are zero)
+  static_assert(VT <= 256 && ST <= 256, "one task per thread");
+  const int vkg = tid / (D / 8), vcol = (tid % (D / 8)) * 8;
+  Frag<T> vr[4];
+  float sr[4][8];
   {
-    constexpr int NQ = CHUNK * D / 8 / 256;  // 8-element pieces of q and of k per thread
-    constexpr int NS = M * D / 4 / 256;      // 4-float pieces of K~_e per thread
-    constexpr int NA = CHUNK * M / 4 / 256;  // 4-float pieces of the gates per thread
-    float qv[NQ][8], kv[NQ][8];
-    f32x4 sv[NS], av[NA];
-    const float* Ske = ws.Sk + (bh * ne + e) * M * D;
+    Frag<T> qv[NQ], kv[NQ];
+    float skv[NSK][8];
+    f32x4 av[NA];
 #pragma unroll
     for (int u = 0; u < NQ; ++u) {
       const int x = tid + 256 * u, r = x / (D / 8), col = (x % (D / 8)) * 8;
-      load8f<T>(q + (row0 + r) * D + col, qv[u]);
-      load8f<T>(k + (erow0 + r) * D + col, kv[u]);
+      qv[u] = load8<T>(q + (row0 + r) * D + col);
+      kv[u] = load8<T>(k + (erow0 + r) * D + col);
     }
 #pragma unroll
-    for (int u = 0; u < NS; ++u) {
-      const int x = tid + 256 * u, r = x / (D / 4), col = (x % (D / 4)) * 4;
-      sv[u] = *reinterpret_cast<const f32x4*>(Ske + r * D + col);
-    }
-#pragma unroll
-    for (int u = 0; u < NA; ++u) av[u] = *reinterpret_cast<const f32x4*>(gate + erow0 * M + 4 * (tid + 256 * u));
-#pragma unroll
-    for (int u = 0; u < NQ; ++u) {
+    for (int u = 0; u < NSK; ++u) {
       const int x = tid + 256 * u, r = x / (D / 8), col = (x % (D / 8)) * 8;
-      *reinterpret_cast<f32x4*>(Qs + r * DP + col) = f32x4{qv[u][0], qv[u][1], qv[u][2], qv[u][3]};
-      *reinterpret_cast<f32x4*>(Qs + r * DP + col + 4) = f32x4{qv[u][4], qv[u][5], qv[u][6], qv[u][7]};
-      *reinterpret_cast<f32x4*>(KC + (M + r) * DP + col) = f32x4{kv[u][0], kv[u][1], kv[u][2], kv[u][3]};
-      *reinterpret_cast<f32x4*>(KC + (M + r) * DP + col + 4) = f32x4{kv[u][4], kv[u][5], kv[u][6], kv[u][7]};
-    }
+      if (x < M * D / 8) {
+        const f32x4 lo4 = *reinterpret_cast<const f32x4*>(Ske + r * D + col);
+        const f32x4 hi4 = *reinterpret_cast<const f32x4*>(Ske + r * D + col + 4);
 #pragma unroll
-    for (int u = 0; u < NS; ++u) {
-      const int x = tid + 256 * u, r = x / (D / 4), col = (x % (D / 4)) * 4;
-      *reinterpret_cast<f32x4*>(KC + r * DP + col) = sv[u];
-    }
-#pragma unroll
-    for (int u = 0; u < NA; ++u) *reinterpret_cast<f32x4*>(A + 4 * (tid + 256 * u)) = av[u];
-  }
-  __syncthreads();
-  // ---- X = Q [K~_e; K_e]^T (64 x NCOL): a 4 x (NCOL / 64) tile per thread
-  {
-    constexpr int CPT = NCOL / 16;  // columns per thread
-    const int rg = tid / 16, cg = tid % 16;  // rows 4 rg .. 4 rg + 3; columns cg + 16 u
-    float acc[4][CPT];
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int u = 0; u < CPT; ++u) acc[a][u] = 0.f;
-    for (int d0 = 0; d0 < D; d0 += 4) {
-      f32x4 qv[4];
-#pragma unroll
-      for (int a = 0; a < 4; ++a) qv[a] = *reinterpret_cast<const f32x4*>(Qs + (4 * rg + a) * DP + d0);
-#pragma unroll
-      for (int u = 0; u < CPT; ++u) {
-        const f32x4 kv = *reinterpret_cast<const f32x4*>(KC + (cg + 16 * u) * DP + d0);
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-          acc[a][u] = fmaf(qv[a][0], kv[0], fmaf(qv[a][1], kv[1], fmaf(qv[a][2], kv[2], fmaf(qv[a][3], kv[3], acc[a][u]))));
+        for (int jj = 0; jj < 4; ++jj) {
+          skv[u][jj] = lo4[jj];
+          skv[u][4 + jj] = hi4[jj];
+        }
       }
     }
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int u = 0; u < NA; ++u) {
+      const int x = tid + 256 * u;
+      if (x < CHUNK * M / 4) av[u] = *reinterpret_cast<const f32x4*>(gate + erow0 * M + 4 * x);
+    }
+    if (tid < VT) {
 #pragma unroll
-      for (int u = 0; u < CPT; ++u) {
-        const int col = cg + 16 * u, j = 4 * rg + a;
-        if (u < M / 16) XS[j * M + col] = acc[a][u];
-        else QKT[(col - M) * CHUNK + j] = acc[a][u];
+      for (int i = 0; i < 4; ++i) vr[i] = load8<T>(v + (erow0 + 4 * vkg + i) * D + vcol);
+    }
+    if (tid < ST) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * vkg + i;
+        if (r < M) {
+          const f32x4 lo4 = *reinterpret_cast<const f32x4*>(Sve + r * D + vcol);
+          const f32x4 hi4 = *reinterpret_cast<const f32x4*>(Sve + r * D + vcol + 4);
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            sr[i][jj] = lo4[jj];
+            sr[i][4 + jj] = hi4[jj];
+          }
+        } else {
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) sr[i][jj] = 0.f;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) {
+      const int x = tid + 256 * u, r = x / (D / 8), col = (x % (D / 8)) * 8;
+      store8<T>(Qs + r * P + col, qv[u]);
+      store8<T>(KS + (M + r) * P + col, kv[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < NSK; ++u) {
+      const int x = tid + 256 * u, r = x / (D / 8), col = (x % (D / 8)) * 8;
+      if (x < M * D / 8) {
+        Frag<T> hi, lo;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          frag_set(hi, jj, skv[u][jj]);
+          frag_set(lo, jj, skv[u][jj] - to_f32(frag_get<T>(hi, jj)));
+        }
+        store8<T>(KS + r * P + col, hi);
+        if constexpr (C::SPLIT) store8<T>(KL + r * P + col, lo);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NA; ++u) {
+      const int x = tid + 256 * u;
+      if (x < CHUNK * M / 4) *reinterpret_cast<f32x4*>(A + 4 * x) = av[u];
+    }
+  }
+  __syncthreads();
+  // ---- X = Q [K~_e; K_e]^T: wave w takes query rows 16w .. 16w+15
+  {
+    f32x4 acc[NCT];
+#pragma unroll
+    for (int n = 0; n < NCT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KF; ++ks) {
+      const Frag<T> a = load8<T>(Qs + (16 * w + c) * P + 32 * ks + 8 * g);
+#pragma unroll
+      for (int n = 0; n < NCT; ++n) {
+        mma(acc[n], a, load8<T>(KS + (16 * n + c) * P + 32 * ks + 8 * g));
+        if constexpr (C::SPLIT)
+          if (n < MS) mma(acc[n], a, load8<T>(KL + (16 * n + c) * P + 32 * ks + 8 * g));
+      }
+    }
+#pragma unroll
+    for (int n = 0; n < NCT; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = 16 * w + 4 * g + i;
+        if (n < MS) XS[j * M + 16 * n + c] = acc[n][i];
+        else QK[(16 * (n - MS) + c) * CHUNK + j] = acc[n][i];
       }
   }
   __syncthreads();
@@ -252,13 +367,12 @@ __global__ void __launch_bounds__(256) k_nha_slots(const T* __restrict__ q, cons
     constexpr int NG = 256 / M, JPG = CHUNK / NG;  // JPG = M / 4 queries per group
     const int i = tid % M, grp = tid / M;
     const int jb = grp * JPG;
-    const int lane = lane_id();
     float y[JPG], z[JPG];
 #pragma unroll
     for (int u = 0; u < JPG; ++u) y[u] = XS[(jb + u) * M + i];
     for (int st = 0; st < jb; ++st) {  // tokens before the group's first query: every query takes them
       const float a = A[st * M + i], b = 1.f - a;
-      const float* qk = QKT + st * CHUNK + jb;
+      const float* qk = QK + st * CHUNK + jb;
 #pragma unroll
       for (int u = 0; u < JPG; u += 4) {
         const f32x4 v4 = *reinterpret_cast<const f32x4*>(qk + u);
@@ -270,7 +384,7 @@ __global__ void __launch_bounds__(256) k_nha_slots(const T* __restrict__ q, cons
     for (int u0 = 0; u0 < JPG; ++u0) {  // token jb + u0: queries jb + u0 .. take it, query jb + u0 is done
       const int st = jb + u0;
       const float a = A[st * M + i], b = 1.f - a;
-      const float* qk = QKT + st * CHUNK + jb;
+      const float* qk = QK + st * CHUNK + jb;
 #pragma unroll
       for (int u = u0; u < JPG; ++u) y[u] = fmaf(a, y[u], b * qk[u]);
       z[u0] = y[u0];
@@ -297,45 +411,102 @@ __global__ void __launch_bounds__(256) k_nha_slots(const T* __restrict__ q, cons
     }
   }
   __syncthreads();
-  // ---- read-out: V~ rolled forward over chunk e's tokens, thread (column d,
-  // slots part * SPT ..) keeps its slot values in registers
-  {
-    const int d = tid / TPC, part = tid % TPC;
-    const float* Sve = ws.Sv + (bh * ne + e) * M * D + d;
-    float vt[SPT];
+  // ---- read-out operands: V_e and V~_e (hi, lo) as key groups (4 rows of a
+  // column contiguous) into region 0, free since the score products
+  if (tid < VT) {
 #pragma unroll
-    for (int u = 0; u < SPT; ++u) vt[u] = Sve[(int64_t)(part * SPT + u) * D];
-    const T* vc = v + erow0 * D + d;
-    const float* owc = o_w ? o_w + row0 * D + d : nullptr;
-    // v and o_w of the next PF tokens in flight (unconditional loads at
-    // clamped rows, so that the compiler does not wait for each right away)
-    constexpr int PF = 8;
-    float vr[PF], owr[PF];
+    for (int jj = 0; jj < 8; ++jj)
+      st4<T>(Vg + kg_index<C::RL>(vkg, vcol + jj), to_f32(frag_get<T>(vr[0], jj)), to_f32(frag_get<T>(vr[1], jj)),
+             to_f32(frag_get<T>(vr[2], jj)), to_f32(frag_get<T>(vr[3], jj)));
+  }
+  if (tid < ST) {
 #pragma unroll
-    for (int u = 0; u < PF; ++u) {
-      vr[u] = to_f32(vc[(int64_t)u * D]);
-      owr[u] = owc ? owc[(int64_t)u * D] : 0.f;
+    for (int jj = 0; jj < 8; ++jj) {
+      float hv[4], lv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        hv[i] = to_f32(from_f32<T>(sr[i][jj]));
+        lv[i] = sr[i][jj] - hv[i];
+      }
+      st4<T>(VTh + kg_index<C::RL>(vkg, vcol + jj), hv[0], hv[1], hv[2], hv[3]);
+      if constexpr (C::SPLIT) st4<T>(VTl + kg_index<C::RL>(vkg, vcol + jj), lv[0], lv[1], lv[2], lv[3]);
     }
-    for (int j0 = 0; j0 < CHUNK; j0 += PF) {
+  }
+  // R[j][s] = sum_i P[j][i] (1 - a_s[i]) prod_{s<r<=j} a_r[i]: thread (s,
+  // quarter of the slots) keeps its running weights in registers over j; the
+  // four quarters of a token sit in adjacent lanes and are added by DPP
+  {
+    constexpr int SPQ = M / 4;
+    const int s = tid >> 2, part = tid & 3, i0 = part * SPQ;
+    static_assert(SPQ % 4 == 0, "whole float4 pieces");
+    float cw[SPQ];
 #pragma unroll
-      for (int u = 0; u < PF; ++u) {
-        const int j = j0 + u;
-        const float vj = vr[u], ow = owr[u];
-        const int jn = min(j + PF, CHUNK - 1);
-        vr[u] = to_f32(vc[(int64_t)jn * D]);
-        if (owc) owr[u] = owc[(int64_t)jn * D];
-        const float* aj = A + j * M + part * SPT;
-        const float* pj = XS + j * M + part * SPT;
-        float acc = 0.f;
+    for (int u = 0; u < SPQ; ++u) cw[u] = 1.f - A[s * M + i0 + u];
+    for (int j = 0; j < CHUNK; ++j) {
+      // branch-free (a guarded multiply became one exec-masked branch and
+      // one LDS round trip per slot); four partial sums for the dot product
+      const bool later = j > s;
+      float ra[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int w = 0; w < SPT; ++w) {
-          const float a = aj[w];
-          vt[w] = fmaf(a, vt[w], (1.f - a) * vj);
-          acc = fmaf(pj[w], vt[w], acc);
+      for (int u4 = 0; u4 < SPQ / 4; ++u4) {
+        const f32x4 a4 = *reinterpret_cast<const f32x4*>(A + j * M + i0 + 4 * u4);
+        const f32x4 p4 = *reinterpret_cast<const f32x4*>(XS + j * M + i0 + 4 * u4);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const int u = 4 * u4 + x;
+          cw[u] *= later ? a4[x] : 1.f;
+          ra[x] = fmaf(p4[x], cw[u], ra[x]);
         }
+      }
+      float r = (ra[0] + ra[1]) + (ra[2] + ra[3]);
+      r += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(r), 0xB1, 0xF, 0xF, true));  // quad_perm 1,0,3,2
+      r += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(r), 0x4E, 0xF, 0xF, true));  // quad_perm 2,3,0,1
+      if (part == 0) QK[j * CHUNK + s] = (j >= s) ? r : 0.f;
+    }
+  }
+  __syncthreads();
+  // P * Gamma, in place (slot i's running product over the chunk's tokens)
+  if (tid < M) {
+    float gm = 1.f;
+    for (int j = 0; j < CHUNK; ++j) {
+      gm *= A[j * M + tid];
+      XS[j * M + tid] *= gm;
+    }
+  }
+  __syncthreads();
+  // ---- O = (P * Gamma) V~_e + R V_e + w_win o_w: wave w takes rows 16w ..
+  {
+    constexpr int MK = C::MP / 32;
+    Frag<T> ar[2], ap[MK];
 #pragma unroll
-        for (int msk = 1; msk < TPC; msk <<= 1) acc += __shfl_xor(acc, msk, 64);
-        if (part == 0) out[(row0 + j) * D + d] = from_f32<To>(fmaf(WW[j], ow, acc));
+    for (int k2 = 0; k2 < 2; ++k2)
+      ar[k2] = frag_fn_nha<T>([&](int jj) { return QK[(16 * w + c) * CHUNK + 32 * k2 + kmap_acc(g, jj)]; });
+#pragma unroll
+    for (int kk = 0; kk < MK; ++kk)
+      ap[kk] = frag_fn_nha<T>([&](int jj) {
+        const int i = 32 * kk + kmap_acc(g, jj);
+        return i < M ? XS[(16 * w + c) * M + i] : 0.f;
+      });
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2)
+        mma(acc, ar[k2], ld4x2_nha<T>(Vg + kg_index<C::RL>(8 * k2 + g, 16 * dt + c),
+                                      Vg + kg_index<C::RL>(8 * k2 + 4 + g, 16 * dt + c)));
+#pragma unroll
+      for (int kk = 0; kk < MK; ++kk) {
+        mma(acc, ap[kk], ld4x2_nha<T>(VTh + kg_index<C::RL>(8 * kk + g, 16 * dt + c),
+                                      VTh + kg_index<C::RL>(8 * kk + 4 + g, 16 * dt + c)));
+        if constexpr (C::SPLIT)
+          mma(acc, ap[kk], ld4x2_nha<T>(VTl + kg_index<C::RL>(8 * kk + g, 16 * dt + c),
+                                        VTl + kg_index<C::RL>(8 * kk + 4 + g, 16 * dt + c)));
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = 16 * w + 4 * g + i, d = 16 * dt + c;
+        const float ow = o_w ? o_w[(row0 + j) * D + d] : 0.f;
+        out[(row0 + j) * D + d] = from_f32<To>(fmaf(WW[j], ow, acc[i]));
       }
     }
   }
@@ -378,9 +549,9 @@ hipError_t launch_nha_m(const T* q, const T* k, const T* v, const float* gate, i
   }
   const float* ow = nw > 0 ? o_w : nullptr;
   const float* lw = nw > 0 ? lse_w : nullptr;
-  const size_t lds = (size_t)(CHUNK * (D + 4) + (M + CHUNK) * (D + 4) + CHUNK * M + CHUNK * M + CHUNK * CHUNK + CHUNK) * 4;
 #define NHA_M(MM)                                                                                                  \
   do {                                                                                                             \
+    const size_t lds = NhaSlotCfg<T, D, MM>::LDS;                                                                  \
     if ((e = set_lds_limit((const void*)k_nha_slots<T, To, D, MM>, (int)lds)) != hipSuccess) return e;            \
     if (prof) prof(KID_NHA_CHUNK, st, 0);                                                                          \
     hipLaunchKernelGGL((k_nha_chunk<T, D, MM>), dim3((unsigned)(BH * ne)), dim3(256), 0, st, k, v, gate, ws, L,     \
