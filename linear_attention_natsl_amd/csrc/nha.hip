@@ -68,21 +68,59 @@ template <> __device__ __forceinline__ void st4<float>(float* p, float a, float 
   *reinterpret_cast<f32x4*>(p) = v4;
 }
 
-// per (b, h, chunk e < ne): the slots' change over the chunk and its decay
+// per (b, h, chunk e < ne): the slots' change over the chunk and its decay.
+// The weights W[s][i] = (1 - a_s[i]) prod_{s<r<64} a_r[i] come from suffix
+// products (one thread per slot); dK = W^T K_e and dV = W^T V_e are matrix-
+// core products (W as bf16 hi + lo parts for bf16 io), K_e and V_e staged as
+// key groups (4 tokens of a column contiguous).
 template <typename T, int D, int M>
 __global__ void __launch_bounds__(256) k_nha_chunk(const T* __restrict__ k, const T* __restrict__ v,
                                                    const float* __restrict__ gate, NhaWs ws, int L, int ne) {
-  constexpr int TPC = 256 / D;   // threads per column
-  constexpr int SPT = M / TPC;   // slots per thread
-  __shared__ float wg[CHUNK][M];  // gates, then the weights (1 - a_s) prod_{s<r<64} a_r
-  const int nc = L / CHUNK;
+  constexpr int RL = kg_row<T, D>();
+  constexpr bool SPLIT = sizeof(T) == 2;
+  __shared__ __align__(16) float wg[CHUNK][M];  // gates, then the weights
+  __shared__ __align__(16) T Kg[(CHUNK / 4) * RL * 4];
+  __shared__ __align__(16) T Vg[(CHUNK / 4) * RL * 4];
   const int64_t bh = bid_x() / ne;
   const int e = bid_x() % ne;
-  const int tid = tid_x();
-  const float* gc = gate + (bh * L + (int64_t)e * CHUNK) * M;
-  for (int x = tid; x < CHUNK * M; x += 256) wg[x / M][x % M] = gc[x];
+  const int tid = tid_x(), lane = lane_id(), w = wave_id();
+  const int g = lane >> 4, c = lane & 15;
+  const int64_t row0 = bh * L + (int64_t)e * CHUNK;
+  constexpr int NA = (CHUNK * M / 4 + 255) / 256;
+  constexpr int VT = (CHUNK / 4) * (D / 8);
+  static_assert(VT <= 256, "one task per thread");
+  const int kg = tid / (D / 8), col = (tid % (D / 8)) * 8;
+  {
+    f32x4 av[NA];
+    Frag<T> kr[4], vr[4];
+#pragma unroll
+    for (int u = 0; u < NA; ++u) {
+      const int x = tid + 256 * u;
+      if (x < CHUNK * M / 4) av[u] = *reinterpret_cast<const f32x4*>(gate + row0 * M + 4 * x);
+    }
+    if (tid < VT) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        kr[i] = load8<T>(k + (row0 + 4 * kg + i) * D + col);
+        vr[i] = load8<T>(v + (row0 + 4 * kg + i) * D + col);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NA; ++u) {
+      const int x = tid + 256 * u;
+      if (x < CHUNK * M / 4) *reinterpret_cast<f32x4*>(&wg[0][0] + 4 * x) = av[u];
+    }
+    if (tid < VT) {
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        st4<T>(Kg + kg_index<RL>(kg, col + jj), to_f32(frag_get<T>(kr[0], jj)), to_f32(frag_get<T>(kr[1], jj)),
+               to_f32(frag_get<T>(kr[2], jj)), to_f32(frag_get<T>(kr[3], jj)));
+        st4<T>(Vg + kg_index<RL>(kg, col + jj), to_f32(frag_get<T>(vr[0], jj)), to_f32(frag_get<T>(vr[1], jj)),
+               to_f32(frag_get<T>(vr[2], jj)), to_f32(frag_get<T>(vr[3], jj)));
+      }
+    }
+  }
   __syncthreads();
-  float* G = ws.G + (bh * ne + e) * M;
   if (tid < M) {
     float suf = 1.f;
     for (int s = CHUNK - 1; s >= 0; --s) {
@@ -90,45 +128,33 @@ __global__ void __launch_bounds__(256) k_nha_chunk(const T* __restrict__ k, cons
       wg[s][tid] = (1.f - a) * suf;
       suf *= a;
     }
-    G[tid] = suf;
+    ws.G[(bh * ne + e) * M + tid] = suf;
   }
   __syncthreads();
-  const int d = tid / TPC, part = tid % TPC;
-  const T* kc = k + (bh * L + (int64_t)e * CHUNK) * D + d;
-  const T* vc = v + (bh * L + (int64_t)e * CHUNK) * D + d;
-  float ak[SPT], av[SPT];
+  // tiles (K or V, 16 slots, 16 columns), wave w takes tiles w, w + 4, ...
+  constexpr int RT = M / 16, CT = D / 16, NTL = 2 * RT * CT;
+  for (int t = w; t < NTL; t += 4) {
+    const int which = t / (RT * CT), rem = t % (RT * CT), rt = rem / CT, ct = rem % CT;
+    const T* Xg = which ? Vg : Kg;
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int u = 0; u < SPT; ++u) ak[u] = av[u] = 0.f;
-  constexpr int PF = 8;  // tokens of k and v in flight (clamped, unconditional loads)
-  float kr[PF], vr[PF];
+    for (int k2 = 0; k2 < 2; ++k2) {
+      Frag<T> ah, al;
 #pragma unroll
-  for (int u = 0; u < PF; ++u) {
-    kr[u] = to_f32(kc[(int64_t)u * D]);
-    vr[u] = to_f32(vc[(int64_t)u * D]);
-  }
-  for (int s0 = 0; s0 < CHUNK; s0 += PF) {
-#pragma unroll
-    for (int x = 0; x < PF; ++x) {
-      const int s = s0 + x, sn = min(s + PF, CHUNK - 1);
-      const float ks = kr[x], vs = vr[x];
-      kr[x] = to_f32(kc[(int64_t)sn * D]);
-      vr[x] = to_f32(vc[(int64_t)sn * D]);
-#pragma unroll
-      for (int u = 0; u < SPT; ++u) {
-        const float w = wg[s][part * SPT + u];
-        ak[u] = fmaf(w, ks, ak[u]);
-        av[u] = fmaf(w, vs, av[u]);
+      for (int jj = 0; jj < 8; ++jj) {
+        const float x = wg[32 * k2 + kmap_acc(g, jj)][16 * rt + c];
+        frag_set(ah, jj, x);
+        frag_set(al, jj, x - to_f32(frag_get<T>(ah, jj)));
       }
+      const Frag<T> bx = ld4x2_nha<T>(Xg + kg_index<RL>(8 * k2 + g, 16 * ct + c),
+                                      Xg + kg_index<RL>(8 * k2 + 4 + g, 16 * ct + c));
+      mma(acc, ah, bx);
+      if constexpr (SPLIT) mma(acc, al, bx);
     }
-  }
-  float* dk = ws.Sk + ((bh * ne + e) * M) * D + d;
-  float* dv = ws.Sv + ((bh * ne + e) * M) * D + d;
+    float* S = (which ? ws.Sv : ws.Sk) + (bh * ne + e) * M * D;
 #pragma unroll
-  for (int u = 0; u < SPT; ++u) {
-    dk[(int64_t)(part * SPT + u) * D] = ak[u];
-    dv[(int64_t)(part * SPT + u) * D] = av[u];
+    for (int i = 0; i < 4; ++i) S[(16 * rt + 4 * g + i) * D + 16 * ct + c] = acc[i];
   }
-  (void)nc;
 }
 
 // chunk-start slot states, in place: entry e holds the chunk's change on
