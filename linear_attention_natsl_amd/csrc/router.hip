@@ -76,7 +76,7 @@ template <typename T>
 __global__ void __launch_bounds__(1024, 2) k_route_wide(const T* __restrict__ x, const float* __restrict__ w,
                                                      const float* __restrict__ bsc, int L, int d, int G, int nc,
                                                      int32_t* __restrict__ route_out, float* __restrict__ scores) {
-  extern __shared__ float s_part[];  // [RS][d] partial sums, then the mean [d] and 2G scores
+  extern __shared__ float s_part[];  // [RS][d] partial sums, then the mean [d] and 2G scores; W_score [d][2G]
   const int c = bid_x(), b = bid_y();
   const int tid = tid_x();
   const int ncg = d >> 3;          // column groups
@@ -84,6 +84,20 @@ __global__ void __launch_bounds__(1024, 2) k_route_wide(const T* __restrict__ x,
   const int rows = CHUNK / rs;     // rows per thread
   const int cg = tid % ncg, sl = tid / ncg;
   const T* xc = x + ((int64_t)b * L + (int64_t)c * CHUNK + (int64_t)sl * rows) * d + cg * 8;
+  // W_score goes to LDS (when it fits, 16 KiB at G = 1): its loads are issued
+  // first and stored while the chunk's rows are in flight, so the scores do
+  // not wait on one global load per step
+  const int nw4 = d * 2 * G / 4;
+  float* s_w = s_part + ((rs * d + d + 2 * G + 3) & ~3);
+  const bool w_lds = nw4 <= 4 * 1024 && ((uintptr_t)w & 15) == 0;
+  f32x4 wreg[4];
+  if (w_lds) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int x4 = tid + 1024 * u;
+      if (x4 < nw4) wreg[u] = *reinterpret_cast<const f32x4*>(w + 4 * x4);
+    }
+  }
   float acc[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = 0.f;
@@ -104,6 +118,13 @@ __global__ void __launch_bounds__(1024, 2) k_route_wide(const T* __restrict__ x,
   float* mine = s_part + sl * d + cg * 8;
 #pragma unroll
   for (int j = 0; j < 8; ++j) mine[j] = acc[j];
+  if (w_lds) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int x4 = tid + 1024 * u;
+      if (x4 < nw4) *reinterpret_cast<f32x4*>(s_w + 4 * x4) = wreg[u];
+    }
+  }
   __syncthreads();
   float* s_mean = s_part + rs * d;
   for (int col = tid; col < d; col += 1024) {
@@ -113,9 +134,11 @@ __global__ void __launch_bounds__(1024, 2) k_route_wide(const T* __restrict__ x,
   }
   __syncthreads();
   const int lane = lane_id(), wv = wave_id();
+  const float* wsrc = w_lds ? s_w : w;
   for (int o = wv; o < 2 * G; o += 16) {
     float p = 0.f;
-    for (int j = lane; j < d; j += 64) p += s_mean[j] * w[(int64_t)j * 2 * G + o];
+#pragma unroll 8
+    for (int j = lane; j < d; j += 64) p += s_mean[j] * wsrc[(int64_t)j * 2 * G + o];
     p = wave_sum64(p);
     if (bsc) p += bsc[o];
     if (lane == 0) s_mean[d + o] = p;
@@ -373,7 +396,8 @@ hipError_t launch_route(const T* x, const float* w, const float* bsc, int B, int
   const bool pow2 = (d & (d - 1)) == 0;
   if (pow2 && d >= 512 && d <= 8192) {
     const int rs = 8192 / d;
-    const size_t lds = (size_t)(rs * d + d + 2 * G) * sizeof(float);
+    const size_t nw = (size_t)d * 2 * G;
+    const size_t lds = (size_t)(rs * d + d + 2 * G + 3 + (nw <= 4 * 1024 * 4 ? nw : 0)) * sizeof(float);
     if (lds <= (size_t)LDS_MAX_BYTES) {
       const hipError_t e = set_lds_limit((const void*)k_route_wide<T>, (int)lds);
       if (e != hipSuccess) return e;
