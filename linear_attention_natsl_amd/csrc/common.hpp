@@ -108,6 +108,43 @@ template <typename T> __device__ __forceinline__ void load8f(const T* p, float* 
   for (int j = 0; j < 8; ++j) o[j] = to_f32(frag_get<T>(f, j));
 }
 
+// two 4-element pieces (e.g. two key groups of one column) -> one fragment
+template <typename T> __device__ __forceinline__ Frag<T> ld4x2(const T* p0, const T* p1);
+template <> __device__ __forceinline__ Frag<bf16> ld4x2<bf16>(const bf16* p0, const bf16* p1) {
+  bf16x4 a = *reinterpret_cast<const bf16x4*>(p0);
+  bf16x4 b = *reinterpret_cast<const bf16x4*>(p1);
+  Frag<bf16> f;
+  f.v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return f;
+}
+template <> __device__ __forceinline__ Frag<float> ld4x2<float>(const float* p0, const float* p1) {
+  f32x4 a = *reinterpret_cast<const f32x4*>(p0);
+  f32x4 b = *reinterpret_cast<const f32x4*>(p1);
+  Frag<float> f;
+  f.v[0] = a[0]; f.v[1] = a[1]; f.v[2] = a[2]; f.v[3] = a[3];
+  f.v[4] = b[0]; f.v[5] = b[1]; f.v[6] = b[2]; f.v[7] = b[3];
+  return f;
+}
+// 4 values -> 4 contiguous elements (e.g. one key group of a column)
+template <typename T> __device__ __forceinline__ void st4(T* p, float a, float b, float c, float d);
+template <> __device__ __forceinline__ void st4<bf16>(bf16* p, float a, float b, float c, float d) {
+  bf16x4 v = {(bf16)a, (bf16)b, (bf16)c, (bf16)d};
+  *reinterpret_cast<bf16x4*>(p) = v;
+}
+template <> __device__ __forceinline__ void st4<float>(float* p, float a, float b, float c, float d) {
+  f32x4 v = {a, b, c, d};
+  *reinterpret_cast<f32x4*>(p) = v;
+}
+
+// a fragment from a function of the element index (scattered reads)
+template <typename T, typename Fn>
+__device__ __forceinline__ Frag<T> frag_fn(Fn fn) {
+  Frag<T> f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) frag_set(f, j, fn(j));
+  return f;
+}
+
 __device__ __forceinline__ int kmap_acc(int g, int j) { return (j < 4) ? (4 * g + j) : (16 + 4 * g + (j - 4)); }
 
 // "Key-group" LDS layout for an operand whose contraction index runs over

@@ -485,13 +485,6 @@ struct BwdChunkCfg {
   static_assert(LDS <= 160 * 1024, "LDS");
 };
 
-template <typename T, typename Fn>
-__device__ __forceinline__ Frag<T> frag_fn(Fn fn) {
-  Frag<T> f;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) frag_set(f, j, fn(j));
-  return f;
-}
 template <typename T>
 __device__ __forceinline__ Frag<T> frag_f32(const float* p) {  // 8 contiguous fp32 (16-byte aligned)
   const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);

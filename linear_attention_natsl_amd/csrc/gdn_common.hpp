@@ -64,32 +64,6 @@ static GdnWs<T, D> carve(void* ws, int64_t nch) {
   return w;
 }
 
-template <typename T> __device__ __forceinline__ Frag<T> ld4x2(const T* p0, const T* p1);
-template <> __device__ __forceinline__ Frag<bf16> ld4x2<bf16>(const bf16* p0, const bf16* p1) {
-  bf16x4 a = *reinterpret_cast<const bf16x4*>(p0);
-  bf16x4 b = *reinterpret_cast<const bf16x4*>(p1);
-  Frag<bf16> f;
-  f.v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-  return f;
-}
-template <> __device__ __forceinline__ Frag<float> ld4x2<float>(const float* p0, const float* p1) {
-  f32x4 a = *reinterpret_cast<const f32x4*>(p0);
-  f32x4 b = *reinterpret_cast<const f32x4*>(p1);
-  Frag<float> f;
-  f.v[0] = a[0]; f.v[1] = a[1]; f.v[2] = a[2]; f.v[3] = a[3];
-  f.v[4] = b[0]; f.v[5] = b[1]; f.v[6] = b[2]; f.v[7] = b[3];
-  return f;
-}
-template <typename T> __device__ __forceinline__ void st4(T* p, float a, float b, float c, float d);
-template <> __device__ __forceinline__ void st4<bf16>(bf16* p, float a, float b, float c, float d) {
-  bf16x4 v = {(bf16)a, (bf16)b, (bf16)c, (bf16)d};
-  *reinterpret_cast<bf16x4*>(p) = v;
-}
-template <> __device__ __forceinline__ void st4<float>(float* p, float a, float b, float c, float d) {
-  f32x4 v = {a, b, c, d};
-  *reinterpret_cast<f32x4*>(p) = v;
-}
-
 // The scan runs one workgroup per head for bf16 with D = 128, and one per
 // (head, 32-column slice) otherwise; the two read -W in different orders.
 template <typename T, int D> constexpr bool scan_head_form() { return sizeof(T) == 2 && D == 128; }

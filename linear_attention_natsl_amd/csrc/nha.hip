@@ -33,41 +33,6 @@
 
 namespace natsl {
 
-template <typename T, typename Fn>
-__device__ __forceinline__ Frag<T> frag_fn_nha(Fn fn) {
-  Frag<T> f;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) frag_set(f, j, fn(j));
-  return f;
-}
-// 4 + 4 contiguous elements (two key groups of one column) -> one fragment
-template <typename T> __device__ __forceinline__ Frag<T> ld4x2_nha(const T* p0, const T* p1);
-template <> __device__ __forceinline__ Frag<bf16> ld4x2_nha<bf16>(const bf16* p0, const bf16* p1) {
-  const bf16x4 a = *reinterpret_cast<const bf16x4*>(p0);
-  const bf16x4 b = *reinterpret_cast<const bf16x4*>(p1);
-  Frag<bf16> f;
-  f.v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-  return f;
-}
-template <> __device__ __forceinline__ Frag<float> ld4x2_nha<float>(const float* p0, const float* p1) {
-  const f32x4 a = *reinterpret_cast<const f32x4*>(p0);
-  const f32x4 b = *reinterpret_cast<const f32x4*>(p1);
-  Frag<float> f;
-  f.v[0] = a[0]; f.v[1] = a[1]; f.v[2] = a[2]; f.v[3] = a[3];
-  f.v[4] = b[0]; f.v[5] = b[1]; f.v[6] = b[2]; f.v[7] = b[3];
-  return f;
-}
-// 4 values of one column (a key group) -> 4 contiguous elements
-template <typename T> __device__ __forceinline__ void st4(T* p, float a, float b, float c, float d);
-template <> __device__ __forceinline__ void st4<bf16>(bf16* p, float a, float b, float c, float d) {
-  const bf16x4 v4 = {(bf16)a, (bf16)b, (bf16)c, (bf16)d};
-  *reinterpret_cast<bf16x4*>(p) = v4;
-}
-template <> __device__ __forceinline__ void st4<float>(float* p, float a, float b, float c, float d) {
-  const f32x4 v4 = {a, b, c, d};
-  *reinterpret_cast<f32x4*>(p) = v4;
-}
-
 // per (b, h, chunk e < ne): the slots' change over the chunk and its decay.
 // The weights W[s][i] = (1 - a_s[i]) prod_{s<r<64} a_r[i] come from suffix
 // products (one thread per slot); dK = W^T K_e and dV = W^T V_e are matrix-
@@ -146,7 +111,7 @@ __global__ void __launch_bounds__(256) k_nha_chunk(const T* __restrict__ k, cons
         frag_set(ah, jj, x);
         frag_set(al, jj, x - to_f32(frag_get<T>(ah, jj)));
       }
-      const Frag<T> bx = ld4x2_nha<T>(Xg + kg_index<RL>(8 * k2 + g, 16 * ct + c),
+      const Frag<T> bx = ld4x2<T>(Xg + kg_index<RL>(8 * k2 + g, 16 * ct + c),
                                       Xg + kg_index<RL>(8 * k2 + 4 + g, 16 * ct + c));
       mma(acc, ah, bx);
       if constexpr (SPLIT) mma(acc, al, bx);
@@ -506,10 +471,10 @@ __global__ void __launch_bounds__(256) k_nha_slots(const T* __restrict__ q, cons
     Frag<T> ar[2], ap[MK];
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2)
-      ar[k2] = frag_fn_nha<T>([&](int jj) { return QK[(16 * w + c) * CHUNK + 32 * k2 + kmap_acc(g, jj)]; });
+      ar[k2] = frag_fn<T>([&](int jj) { return QK[(16 * w + c) * CHUNK + 32 * k2 + kmap_acc(g, jj)]; });
 #pragma unroll
     for (int kk = 0; kk < MK; ++kk)
-      ap[kk] = frag_fn_nha<T>([&](int jj) {
+      ap[kk] = frag_fn<T>([&](int jj) {
         const int i = 32 * kk + kmap_acc(g, jj);
         return i < M ? XS[(16 * w + c) * M + i] : 0.f;
       });
@@ -518,14 +483,14 @@ __global__ void __launch_bounds__(256) k_nha_slots(const T* __restrict__ q, cons
       f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2)
-        mma(acc, ar[k2], ld4x2_nha<T>(Vg + kg_index<C::RL>(8 * k2 + g, 16 * dt + c),
+        mma(acc, ar[k2], ld4x2<T>(Vg + kg_index<C::RL>(8 * k2 + g, 16 * dt + c),
                                       Vg + kg_index<C::RL>(8 * k2 + 4 + g, 16 * dt + c)));
 #pragma unroll
       for (int kk = 0; kk < MK; ++kk) {
-        mma(acc, ap[kk], ld4x2_nha<T>(VTh + kg_index<C::RL>(8 * kk + g, 16 * dt + c),
+        mma(acc, ap[kk], ld4x2<T>(VTh + kg_index<C::RL>(8 * kk + g, 16 * dt + c),
                                       VTh + kg_index<C::RL>(8 * kk + 4 + g, 16 * dt + c)));
         if constexpr (C::SPLIT)
-          mma(acc, ap[kk], ld4x2_nha<T>(VTl + kg_index<C::RL>(8 * kk + g, 16 * dt + c),
+          mma(acc, ap[kk], ld4x2<T>(VTl + kg_index<C::RL>(8 * kk + g, 16 * dt + c),
                                         VTl + kg_index<C::RL>(8 * kk + 4 + g, 16 * dt + c)));
       }
 #pragma unroll

@@ -44,23 +44,6 @@ struct SmCfg {
   static constexpr int VT = (VTASKS + 255) / 256;
 };
 
-template <typename T> __device__ __forceinline__ Frag<T> load4x2(const T* p0, const T* p1);
-template <> __device__ __forceinline__ Frag<bf16> load4x2<bf16>(const bf16* p0, const bf16* p1) {
-  bf16x4 a = *reinterpret_cast<const bf16x4*>(p0);
-  bf16x4 b = *reinterpret_cast<const bf16x4*>(p1);
-  Frag<bf16> f;
-  f.v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-  return f;
-}
-template <> __device__ __forceinline__ Frag<float> load4x2<float>(const float* p0, const float* p1) {
-  f32x4 a = *reinterpret_cast<const f32x4*>(p0);
-  f32x4 b = *reinterpret_cast<const f32x4*>(p1);
-  Frag<float> f;
-  f.v[0] = a[0]; f.v[1] = a[1]; f.v[2] = a[2]; f.v[3] = a[3];
-  f.v[4] = b[0]; f.v[5] = b[1]; f.v[6] = b[2]; f.v[7] = b[3];
-  return f;
-}
-
 // store 4 elements (one per token of a key group) for one column
 template <typename T> __device__ __forceinline__ void store_col4(T* p, T a, T b, T c, T d);
 template <> __device__ __forceinline__ void store_col4<bf16>(bf16* p, bf16 a, bf16 b, bf16 c, bf16 d) {
@@ -340,7 +323,7 @@ __global__ void __launch_bounds__(256, 2)
       for (int dt = 0; dt < D / 16; ++dt)
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
-          const Frag<T> a = load4x2<T>(vs_lds + kg_index<C::VRL>(8 * k2 + g, 16 * dt + c),
+          const Frag<T> a = ld4x2<T>(vs_lds + kg_index<C::VRL>(8 * k2 + g, 16 * dt + c),
                                        vs_lds + kg_index<C::VRL>(8 * k2 + 4 + g, 16 * dt + c));
 #pragma unroll
           for (int qs = 0; qs < 2; ++qs) mma(o[dt][qs], a, pf[qs][k2]);
@@ -941,7 +924,7 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) k_sm_bwd_dq(const
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
         const T* kg = kbuf + C::KTILE;
-        const Frag<T> a = load4x2<T>(kg + kg_index<C::VRL>(8 * k2 + g, 16 * dt + c),
+        const Frag<T> a = ld4x2<T>(kg + kg_index<C::VRL>(8 * k2 + g, 16 * dt + c),
                                      kg + kg_index<C::VRL>(8 * k2 + 4 + g, 16 * dt + c));
         mma(acc[dt], a, dsf[k2]);
       }
@@ -1058,9 +1041,9 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) k_sm_bwd_dkdv(con
       for (int dt = 0; dt < D / 16; ++dt) {
         const T* dgk = qbuf + C::KTILE;  // dO key groups
         const T* qgk = dbuf + C::KTILE;  // Q key groups
-        mma(adv[dt], load4x2<T>(dgk + kg_index<C::VRL>(8 * k2 + g, 16 * dt + c),
+        mma(adv[dt], ld4x2<T>(dgk + kg_index<C::VRL>(8 * k2 + g, 16 * dt + c),
                                 dgk + kg_index<C::VRL>(8 * k2 + 4 + g, 16 * dt + c)), pf);
-        mma(adk[dt], load4x2<T>(qgk + kg_index<C::VRL>(8 * k2 + g, 16 * dt + c),
+        mma(adk[dt], ld4x2<T>(qgk + kg_index<C::VRL>(8 * k2 + g, 16 * dt + c),
                                 qgk + kg_index<C::VRL>(8 * k2 + 4 + g, 16 * dt + c)), dsf);
       }
     }
