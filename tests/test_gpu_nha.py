@@ -38,6 +38,7 @@ def run(inp, B, H, L, D, window):
     ("bf16", 128, 16, 704, 64, 4.0),   # sharp attention: a misplaced key or slot shows
     ("bf16", 64, 32, 384, 128, 1.0),
     ("bf16", 128, 64, 448, 0, 1.0),
+    ("f32", 128, 64, 320, 128, 1.0),   # the largest LDS footprint of the slot and chunk kernels
 ])
 def test_nha_matches_oracle(io, D, m, L, window, q_scale):
     B, H = 2, 2

@@ -461,7 +461,9 @@ def test_softmax_backward_parity(io, D, L, q_scale, per_head):
                                                    ("f32", 128, 320, False, (0.995, 1.0)),
                                                    ("bf16", 128, 384, True, (0.9, 0.999)),
                                                    ("bf16", 64, 448, False, (0.995, 1.0)),
-                                                   ("bf16", 128, 8192, False, (0.995, 1.0))])
+                                                   ("bf16", 128, 8192, False, (0.995, 1.0)),
+                                                   ("bf16", 128, 64, False, (0.9, 0.999)),
+                                                   ("f32", 64, 128, True, (0.9, 0.999))])
 def test_gdn_backward_parity(io, D, L, per_head, alpha):
     """Gradient of the Gated DeltaNet branch through the rollback (q, k, v,
     alpha, beta and the initial state, with upstream gradients on the outputs
