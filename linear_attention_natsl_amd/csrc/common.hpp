@@ -49,6 +49,25 @@ __device__ __forceinline__ void mma(f32x4& c, const Frag<float>& a, const Frag<f
   for (int j = 0; j < 8; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[j], b.v[j], c, 0, 0, 0);
 }
 
+// f when keep, else a zero fragment: a selection, never a product, so that a
+// non-finite fragment cannot survive as 0 * inf
+__device__ __forceinline__ Frag<bf16> frag_select(bool keep, const Frag<bf16>& f) {
+  typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+  const u32x4_t u = __builtin_bit_cast(u32x4_t, f.v);
+  u32x4_t r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) r[j] = keep ? u[j] : 0u;
+  Frag<bf16> o;
+  o.v = __builtin_bit_cast(bf16x8, r);
+  return o;
+}
+__device__ __forceinline__ Frag<float> frag_select(bool keep, const Frag<float>& f) {
+  Frag<float> o;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) o.v[j] = keep ? f.v[j] : 0.f;
+  return o;
+}
+
 template <typename T> __device__ __forceinline__ T frag_get(const Frag<T>& f, int j);
 template <> __device__ __forceinline__ bf16 frag_get<bf16>(const Frag<bf16>& f, int j) { return f.v[j]; }
 template <> __device__ __forceinline__ float frag_get<float>(const Frag<float>& f, int j) { return f.v[j]; }

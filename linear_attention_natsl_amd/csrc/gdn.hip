@@ -401,9 +401,11 @@ __global__ void __launch_bounds__(256, 1)
   lds_barrier();
 
   // One chunk.  Branch-free: for a softmax-routed chunk the state update runs
-  // with decay 1 and a zero scaled U, which leaves S bit-identical (x*1 + 0),
-  // so every prefetched operand is consumed unconditionally (a use inside a
-  // branch lets the compiler sink the load into it, defeating the prefetch).
+  // with decay 1 and zero operands (U scaled to zero and K^T replaced by zero
+  // by selection, not by multiplication, so that a non-finite U or K cannot
+  // leak in as 0 * inf), which leaves S bit-identical (x*1 + 0*0), so every
+  // prefetched operand is consumed unconditionally (a use inside a branch
+  // lets the compiler sink the load into it, defeating the prefetch).
   auto step = [&](const ScanOps<T, D, DVT>& op, int cc) {
     if constexpr (ST) {
 #pragma unroll
@@ -437,14 +439,13 @@ __global__ void __launch_bounds__(256, 1)
       }
     const bool lin = op.route == 1;
     const float gce = lin ? op.gC : 1.f;
-    f32x4 eks;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) eks[i] = lin ? op.ek[i] : 0.f;
 #pragma unroll
     for (int n = 0; n < O::NV; ++n) {
+      f32x4 ue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ue[i] = lin ? u[n][i] * op.ek[i] : 0.f;
       st4<T>(&Up[kg_index<URL>(4 * w + g, 16 * n + c)], u[n][0], u[n][1], u[n][2], u[n][3]);
-      st4<T>(&Ue[kg_index<URL>(4 * w + g, 16 * n + c)], u[n][0] * eks[0], u[n][1] * eks[1], u[n][2] * eks[2],
-             u[n][3] * eks[3]);
+      st4<T>(&Ue[kg_index<URL>(4 * w + g, 16 * n + c)], ue[0], ue[1], ue[2], ue[3]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) oa[n][i] *= op.gam[i];
     }
@@ -479,7 +480,7 @@ __global__ void __launch_bounds__(256, 1)
       for (int n = 0; n < O::NV; ++n) {
         f32x4 acc = sm[x][n] * gce;
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) mma(acc, op.kt[x][k2], be[k2][n]);
+        for (int k2 = 0; k2 < 2; ++k2) mma(acc, frag_select(lin, op.kt[x][k2]), be[k2][n]);
         sm[x][n] = acc;
       }
     write_state(sb ^ 1);
@@ -847,8 +848,10 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW)
       }
       fence();
     }
-    // branch-free rollback: a softmax-routed chunk updates with decay 1 and a
-    // zero scaled U, which leaves S bit-identical
+    // branch-free rollback: a softmax-routed chunk updates with decay 1 and
+    // zero operands (scaled U and K^T both replaced by zero by selection, so
+    // that a non-finite U or K cannot leak in as 0 * inf), which leaves S
+    // bit-identical
     const float gce = lin ? gm[64] : 1.f;
     Frag<bf16> bu[2][NV], be[2][NV];
 #pragma unroll
@@ -915,7 +918,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW)
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
-        for (int nn = 0; nn < NV; ++nn) mma(sm[dt][nn], fk[dt % 3][k2], be[k2][nn]);
+        for (int nn = 0; nn < NV; ++nn) mma(sm[dt][nn], frag_select(lin, fk[dt % 3][k2]), be[k2][nn]);
       fence();
     }
   };
