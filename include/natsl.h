@@ -32,8 +32,9 @@
  *     enqueue, so concurrent forwards never share them, (b) a record of the
  *     kernels whose LDS limit has been raised, guarded by a mutex, and (c)
  *     the natsl_profile_* timing records, guarded by a mutex (timing several
- *     threads at once mixes their records), and (d) the scratch array of
- *     natsl_decode_step_noalloc (see there).  Calls whose device buffers
+ *     threads at once mixes their records), (d) the scratch array of
+ *     natsl_decode_step_noalloc (see there), and (e) the level of the
+ *     natsl_set_sync_check debug mode (atomic).  Calls whose device buffers
  *     overlap must be ordered by the caller (same stream, or events);
  *   - every call validates its arguments on the host BEFORE enqueueing any
  *     work; on failure nothing is enqueued, a status != NATSL_OK is
@@ -43,7 +44,9 @@
  *   - tensors are dense row-major with the shapes given; io tensors (x, q, k,
  *     v, out) hold the io dtype of natsl_dims, alpha/beta/weights are fp32;
  *   - supported: Dk == Dv in {64, 128}, chunk == 64, L % 64 == 0, L >= 64,
- *     B * H * L < 2^31, route_groups G in {1, H}, H <= 1024, d_model % 8 == 0
+ *     B * H * L <= 2^28 (so that every launch's work-item count stays
+ *     below 2^32; q, k, v and out alone take 256 GiB at that bound),
+ *     route_groups G in {1, H}, H <= 1024, d_model % 8 == 0
  *     and 8 <= d_model <= 32768 (where d_model is used).  The Gated DeltaNet
  *     branch (natsl_gdn_chunk, natsl_forward) with bf16 io and D = 128 takes
  *     at most 15232 chunks per sequence (L <= 974848); a longer L is
@@ -71,7 +74,16 @@ typedef enum {
   NATSL_ERR_CAPACITY = 5      /* host-visible capacity problem (decode)     */
 } natsl_status;
 
-typedef enum { NATSL_F32 = 0, NATSL_BF16 = 1 } natsl_dtype;
+typedef enum {
+  NATSL_F32 = 0,
+  NATSL_BF16 = 1,
+  /* Not dtypes: these two make natsl_dtype a full 32-bit signed integer in C
+   * and in C++, so that any int a caller stores in a dtype field is a value of
+   * the type (the library then rejects it with NATSL_ERR_INVALID_ARG) rather
+   * than undefined behaviour in the library's C++. */
+  NATSL_DTYPE_MIN_ = -2147483647 - 1,
+  NATSL_DTYPE_MAX_ = 2147483647
+} natsl_dtype;
 
 enum { NATSL_ROUTE_SOFTMAX = 0, NATSL_ROUTE_LINEAR = 1 };
 
@@ -405,7 +417,8 @@ typedef struct {
  * its rows are dropped.  The cache (natsl_decode_cache) is read and updated
  * in place on the device; args' tensors are read, out / route_out / the dbg
  * outputs written.  Errors: NATSL_ERR_INVALID_ARG (NULL tensor, cap < 1),
- * NATSL_ERR_UNSUPPORTED (dims), NATSL_ERR_WORKSPACE, all before anything is
+ * NATSL_ERR_UNSUPPORTED (dims; cap above 2^30; B * H * ceil(cap / 1024) at
+ * or above 2^24, the attention's workgroup count), NATSL_ERR_WORKSPACE, all before anything is
  * enqueued; NATSL_ERR_DEVICE for a failed launch.  The new row is written at index n_committed + n_open;
  * if that index is >= cap the row is not written and *err_flag is set to 1
  * (checked by the caller after the step; counters still advance).
@@ -506,6 +519,23 @@ natsl_status natsl_nha_workspace_size(const natsl_dims* dims, int slots, int win
 natsl_status natsl_nha_attention(const natsl_dims* dims, const void* q, const void* k, const void* v,
                                  const float* slot_gate, int slots, int window, void* out, void* ws,
                                  size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Synchronous-check debug mode (not part of the method; for finding which call
+ * raised a device error).  level 0: off (the default).  level 1: every entry
+ * point that enqueues work waits for `stream` before it returns, and the first
+ * error the HIP runtime reports there becomes NATSL_ERR_DEVICE whose message
+ * names the entry point.  level 2: as 1, and the entry point's name is written
+ * to stderr (flushed) before the wait, so that a fault which ends the process
+ * still names the call.  A stream under graph capture is never waited for.
+ * Without a call to natsl_set_sync_check the level is read once, at the first
+ * call that needs it, from the environment variable NATSL_SYNC_CHECK ("1" or
+ * "2"; unset, empty or "0" is off).  The level is process-wide; calls on other
+ * threads see a change at their next entry.  natsl_set_sync_check returns
+ * NATSL_ERR_INVALID_ARG for a level outside 0..2 and changes nothing then.
+ */
+natsl_status natsl_set_sync_check(int level);
+int natsl_get_sync_check(void);
 
 /*
  * Kernel timing for measurement: when enabled, every kernel the library

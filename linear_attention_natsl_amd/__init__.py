@@ -28,7 +28,7 @@ EXPORTS = ["natsl_version", "natsl_last_error", "natsl_workspace_size", "natsl_r
            "natsl_softmax_masked", "natsl_merge", "natsl_forward", "natsl_decode_step",
            "natsl_decode_handoff", "natsl_softmax_masked_backward", "natsl_gdn_backward", "natsl_merge_backward",
            "natsl_decode_step_noalloc", "natsl_route_backward", "natsl_nha_workspace_size", "natsl_nha_attention", "natsl_profile_enable", "natsl_profile_reset", "natsl_profile_read",
-           "natsl_profile_select"]
+           "natsl_profile_select", "natsl_set_sync_check", "natsl_get_sync_check"]
 DECODE_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
@@ -103,13 +103,17 @@ def lib():
         L.natsl_profile_enable.argtypes = [C.c_int]
         L.natsl_profile_read.argtypes = [C.c_char_p, C.POINTER(C.c_int), C.POINTER(C.c_double)]
         L.natsl_profile_select.argtypes = [C.c_char_p]
+        L.natsl_set_sync_check.argtypes = [C.c_int]
+        L.natsl_get_sync_check.argtypes = []
+        L.natsl_get_sync_check.restype = C.c_int
         for name in ("natsl_workspace_size", "natsl_route", "natsl_gdn_chunk", "natsl_softmax_masked",
                      "natsl_merge", "natsl_forward", "natsl_decode_step", "natsl_decode_step_noalloc",
                      "natsl_nha_workspace_size", "natsl_nha_attention", "natsl_route_backward",
                      "natsl_decode_handoff",
                      "natsl_softmax_masked_backward", "natsl_gdn_backward", "natsl_merge_backward",
                      "natsl_profile_enable",
-                     "natsl_profile_reset", "natsl_profile_read", "natsl_profile_select"):
+                     "natsl_profile_reset", "natsl_profile_read", "natsl_profile_select",
+                     "natsl_set_sync_check"):
             getattr(L, name).restype = st
         _lib = L
     return _lib
@@ -521,6 +525,16 @@ def decode_handoff(dm: Dims, route, k, v, S_final, state: DecodeState, append=Fa
 
 def profile_enable(on=True):
     _check(lib().natsl_profile_enable(1 if on else 0))
+
+
+def set_sync_check(level):
+    """Debug mode: 0 off, 1 each call waits for its stream and reports the
+    first device error by entry point, 2 also names the call on stderr first."""
+    _check(lib().natsl_set_sync_check(int(level)))
+
+
+def get_sync_check():
+    return lib().natsl_get_sync_check()
 
 
 def profile_reset():

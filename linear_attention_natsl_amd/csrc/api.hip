@@ -5,8 +5,10 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 #include <set>
 #include <string>
@@ -58,6 +60,41 @@ natsl_status ok() {
 }
 natsl_status dev_fail(hipError_t e, const char* where) {
   return fail(NATSL_ERR_DEVICE, "%s: %s", where, hipGetErrorString(e));
+}
+
+// ------------------------------------------------------------- sync check ----
+// Debug mode.  Level 1: every entry point that enqueues work waits for its
+// stream before it returns and turns the first error the runtime reports into
+// NATSL_ERR_DEVICE naming the entry point.  Level 2 also writes the entry
+// point's name to stderr (flushed) before the wait, so that a fault which ends
+// the process still names the call that raised it.  A stream under graph
+// capture is not waited for.  The level comes from natsl_set_sync_check, else
+// from NATSL_SYNC_CHECK in the environment at the first call ("1", "2").
+std::atomic<int> g_sync_level{-1};
+int sync_level() {
+  int v = g_sync_level.load(std::memory_order_acquire);
+  if (v >= 0) return v;
+  const char* s = getenv("NATSL_SYNC_CHECK");
+  int want = 0;
+  if (s && s[0] && strcmp(s, "0") != 0) want = strcmp(s, "2") == 0 ? 2 : 1;
+  int expect = -1;
+  g_sync_level.compare_exchange_strong(expect, want, std::memory_order_acq_rel);
+  return g_sync_level.load(std::memory_order_acquire);
+}
+natsl_status done(hipStream_t st, const char* where) {
+  const int lv = sync_level();
+  if (lv > 0) {
+    if (lv > 1) {
+      fprintf(stderr, "natsl sync check: %s\n", where);
+      fflush(stderr);
+    }
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(st, &cs);
+    if (e == hipSuccess && cs == hipStreamCaptureStatusNone) e = hipStreamSynchronize(st);
+    if (e == hipSuccess) e = hipGetLastError();
+    if (e != hipSuccess) return fail(NATSL_ERR_DEVICE, "%s (sync check): %s", where, hipGetErrorString(e));
+  }
+  return ok();
 }
 
 size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -155,8 +192,10 @@ natsl_status check_dims(const natsl_dims* d, bool need_L, bool need_dmodel) {
     return fail(NATSL_ERR_UNSUPPORTED, "route_groups %d not in {1, H=%d}", d->route_groups, d->H);
   if (need_L) {
     if (d->L < 64 || d->L % 64 != 0) return fail(NATSL_ERR_UNSUPPORTED, "L=%d must be a positive multiple of 64", d->L);
-    if ((int64_t)d->B * d->H * d->L > ((int64_t)1 << 31) - 1)
-      return fail(NATSL_ERR_UNSUPPORTED, "B*H*L too large");
+    // keeps every launch's work-item count (e.g. one 256-lane workgroup per
+    // chunk-head, 1024 lanes per chunk in the router) below 2^32
+    if ((int64_t)d->B * d->H * d->L > ((int64_t)1 << 28))
+      return fail(NATSL_ERR_UNSUPPORTED, "B*H*L = %lld above 2^28", (long long)d->B * d->H * d->L);
   }
   if (need_dmodel) {
     // the router keeps the chunk mean (d_model floats) and 2G scores in LDS
@@ -369,6 +408,8 @@ natsl_status natsl_workspace_size(int entry, const natsl_dims* dims, size_t* byt
     case NATSL_ENTRY_DECODE_STEP:
       CHECK(check_dims(dims, false, false));
       if (dims->L < 1) return fail(NATSL_ERR_INVALID_ARG, "decode: dims->L must hold the cache capacity");
+      if (const char* why = decode_dims_problem(dims->B, dims->H, dims->L))
+        return fail(NATSL_ERR_UNSUPPORTED, "decode: %s", why);
       *bytes = decode_ws_bytes(dims->B, dims->H, dims->route_groups, dims->Dk, dims->L);
       return ok();
     case NATSL_ENTRY_SOFTMAX_BACKWARD:
@@ -411,7 +452,7 @@ natsl_status natsl_route(const natsl_dims* dims, const void* x, const float* w_s
   NEED(nsel_before, "nsel_before");
   hipError_t e = do_route(dims, x, w_score, b_score, route_in, route_out, sel_idx, nsel_before, scores, stream);
   if (e != hipSuccess) return dev_fail(e, "natsl_route");
-  return ok();
+  return done(stream, "natsl_route");
 }
 
 natsl_status natsl_gdn_chunk(const natsl_dims* dims, const void* q, const void* k, const void* v,
@@ -433,7 +474,7 @@ natsl_status natsl_gdn_chunk(const natsl_dims* dims, const void* q, const void* 
   CHECK(check_ws(ws, ws_bytes, need));
   hipError_t e = do_gdn(dims, q, k, v, alpha, beta, route, S_init, o_gdn, o_dtype, S_final, ws, stream);
   if (e != hipSuccess) return dev_fail(e, "natsl_gdn_chunk");
-  return ok();
+  return done(stream, "natsl_gdn_chunk");
 }
 
 natsl_status natsl_softmax_masked(const natsl_dims* dims, const void* q, const void* k, const void* v,
@@ -452,7 +493,7 @@ natsl_status natsl_softmax_masked(const natsl_dims* dims, const void* q, const v
   if (o_dtype != NATSL_F32 && o_dtype != NATSL_BF16) return fail(NATSL_ERR_INVALID_ARG, "bad o_dtype");
   hipError_t e = do_softmax(dims, q, k, v, sel_idx, nsel_before, o_sm, o_dtype, lse, stream);
   if (e != hipSuccess) return dev_fail(e, "natsl_softmax_masked");
-  return ok();
+  return done(stream, "natsl_softmax_masked");
 }
 
 natsl_status natsl_merge(const natsl_dims* dims, const void* q, const void* o_sm, const void* o_gdn,
@@ -469,7 +510,7 @@ natsl_status natsl_merge(const natsl_dims* dims, const void* q, const void* o_sm
   if (w_mix_head_stride < 0) return fail(NATSL_ERR_INVALID_ARG, "negative w_mix head stride");
   hipError_t e = do_merge(dims, q, o_sm, o_gdn, branch_dtype, w_mix, w_mix_head_stride, g_sm, g_lin, out, stream);
   if (e != hipSuccess) return dev_fail(e, "natsl_merge");
-  return ok();
+  return done(stream, "natsl_merge");
 }
 
 natsl_status natsl_forward(const natsl_dims* dims, const natsl_forward_args* a, void* ws, size_t ws_bytes,
@@ -553,7 +594,7 @@ natsl_status natsl_forward(const natsl_dims* dims, const natsl_forward_args* a, 
   e = do_merge(dims, a->q, o_sm, o_gd, a->branch_dtype, a->w_mix, a->w_mix_head_stride, a->g_sm, a->g_lin, a->out,
                stream, mix_done ? w.mixd : nullptr);
   if (e != hipSuccess) return dev_fail(e, "natsl_forward/merge");
-  return ok();
+  return done(stream, "natsl_forward");
 }
 
 namespace {
@@ -575,6 +616,7 @@ natsl_status decode_step_impl(const natsl_dims* dims, const natsl_decode_cache* 
   NEED(c->x_sum, "x_sum");
   NEED(c->err_flag, "err_flag");
   if (c->cap < 1) return fail(NATSL_ERR_INVALID_ARG, "cache capacity %d", c->cap);
+  if (const char* why = decode_dims_problem(dims->B, dims->H, c->cap)) return fail(NATSL_ERR_UNSUPPORTED, "decode: %s", why);
   NEED(a->x, "x");
   NEED(a->q, "q");
   NEED(a->k, "k");
@@ -635,7 +677,7 @@ natsl_status decode_step_impl(const natsl_dims* dims, const natsl_decode_cache* 
   else
     e = dims->Dk == 64 ? launch_decode<float, 64>(L, ws, stream, prof) : launch_decode<float, 128>(L, ws, stream, prof);
   if (e != hipSuccess) return dev_fail(e, noalloc ? "natsl_decode_step_noalloc" : "natsl_decode_step");
-  return ok();
+  return done(stream, noalloc ? "natsl_decode_step_noalloc" : "natsl_decode_step");
 }
 }  // namespace
 
@@ -690,7 +732,7 @@ natsl_status natsl_softmax_masked_backward(const natsl_dims* dims, const void* q
                                                          dk, dv, dgate, ws, B, H, L, G, sc, stream);
   if (prof) prof(KID_SOFTMAX_BWD, stream, 1);
   if (e != hipSuccess) return dev_fail(e, "natsl_softmax_masked_backward");
-  return ok();
+  return done(stream, "natsl_softmax_masked_backward");
 }
 
 natsl_status natsl_gdn_backward(const natsl_dims* dims, const void* q, const void* k, const void* v,
@@ -734,7 +776,7 @@ natsl_status natsl_gdn_backward(const natsl_dims* dims, const void* q, const voi
                                                          dbeta, dS_init, dgate, ws, B, H, L, G, stream);
   if (prof) prof(KID_GDN_BWD, stream, 1);
   if (e != hipSuccess) return dev_fail(e, "natsl_gdn_backward");
-  return ok();
+  return done(stream, "natsl_gdn_backward");
 }
 
 natsl_status natsl_merge_backward(const natsl_dims* dims, const void* q, const void* o_sm, const void* o_gdn,
@@ -774,7 +816,7 @@ natsl_status natsl_merge_backward(const natsl_dims* dims, const void* q, const v
                                            dw_mix, dg_sm, dg_lin, ws, stream);
   if (prof) prof(KID_MERGE_BWD, stream, 1);
   if (e != hipSuccess) return dev_fail(e, "natsl_merge_backward");
-  return ok();
+  return done(stream, "natsl_merge_backward");
 }
 
 natsl_status natsl_decode_handoff(const natsl_dims* dims, const int32_t* route, const void* k, const void* v,
@@ -824,7 +866,7 @@ natsl_status natsl_decode_handoff(const natsl_dims* dims, const int32_t* route, 
   const hipError_t e = dims->io == NATSL_BF16 ? launch_handoff<bf16>(L, ws, stream) : launch_handoff<float>(L, ws, stream);
   if (prof) prof(KID_HANDOFF, stream, 1);
   if (e != hipSuccess) return dev_fail(e, "natsl_decode_handoff");
-  return ok();
+  return done(stream, "natsl_decode_handoff");
 }
 
 natsl_status natsl_route_backward(const natsl_dims* dims, const void* x, const float* w_score, const float* scores,
@@ -850,7 +892,7 @@ natsl_status natsl_route_backward(const natsl_dims* dims, const void* x, const f
                                          stream);
   if (prof) prof(KID_ROUTE_BWD, stream, 1);
   if (e != hipSuccess) return dev_fail(e, "natsl_route_backward");
-  return ok();
+  return done(stream, "natsl_route_backward");
 }
 
 natsl_status natsl_nha_workspace_size(const natsl_dims* dims, int slots, int window, size_t* bytes) {
@@ -893,8 +935,16 @@ natsl_status natsl_nha_attention(const natsl_dims* dims, const void* q, const vo
                                                        slots, (float*)out, ws, B, H, L, window, sc, stream, prof);
   if (prof) prof(KID_NHA, stream, 1);
   if (e != hipSuccess) return dev_fail(e, "natsl_nha_attention");
+  return done(stream, "natsl_nha_attention");
+}
+
+natsl_status natsl_set_sync_check(int level) {
+  if (level < 0 || level > 2) return fail(NATSL_ERR_INVALID_ARG, "sync check level %d (0, 1 or 2)", level);
+  g_sync_level.store(level, std::memory_order_release);
   return ok();
 }
+
+int natsl_get_sync_check(void) { return sync_level(); }
 
 natsl_status natsl_profile_enable(int on) {
   std::lock_guard<std::mutex> lk(g_prof_mu);

@@ -153,7 +153,8 @@ __global__ void __launch_bounds__(256) k_decode_attn(const T* __restrict__ q, co
   constexpr int NGRP = 4 * GPW;     // row groups per workgroup
   __shared__ float red_o[NGRP][D];
   __shared__ float red_m[NGRP], red_l[NGRP];
-  const int s = bid_x(), bh = bid_y(), b = bh / H, h = bh % H;
+  const unsigned bid = (unsigned)bid_x();  // (split, b * H + h) flattened, split fastest
+  const int s = (int)(bid % (unsigned)nsplit), bh = (int)(bid / (unsigned)nsplit), b = bh / H, h = bh % H;
   const int grp = (G == 1) ? 0 : h;
   // rows actually present (after a capacity error the counters run past cap)
   const int n = min(n_committed[b * G + grp] + n_open[b], cap);
@@ -353,9 +354,17 @@ hipError_t decode_scratch_address(void** out) {
   return hipSuccess;
 }
 
+const char* decode_dims_problem(int B, int H, int cap) {
+  if (cap < 1 || cap > (1 << 30)) return "cache capacity must lie in [1, 2^30]";
+  // the attention grid has one 256-lane workgroup per (split, b, h)
+  if ((int64_t)B * H * ((cap + DEC_SPLIT - 1) / DEC_SPLIT) >= ((int64_t)1 << 24))
+    return "B * H * ceil(capacity / 1024) must stay below 2^24";
+  return nullptr;
+}
+
 size_t decode_ws_bytes(int B, int H, int G, int D, int cap) {
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  const size_t nsplit = (size_t)(cap + DEC_SPLIT - 1) / DEC_SPLIT;
+  const size_t nsplit = ((size_t)cap + DEC_SPLIT - 1) / DEC_SPLIT;
   return al((size_t)B * G * 4) + al((size_t)B * H * D * 4) + al((size_t)B * H * nsplit * D * 4) +
          al((size_t)B * H * nsplit * 2 * 4);
 }
@@ -383,7 +392,7 @@ hipError_t launch_decode(const DecodeLaunch& a, void* wsp, hipStream_t st,
   LAUNCH_CHECK(KID_DECODE_GDN, (k_decode_gdn<T, D>), dim3(a.B * a.H), dim3(256), 0, st, (const T*)a.q,
                (const T*)a.k, (const T*)a.v, a.alpha, a.beta, a.S_carry, a.S_work, a.n_open, dec, a.H,
                a.G, o_gdn);
-  LAUNCH_CHECK(KID_DECODE_ATTN, (k_decode_attn<T, D>), dim3(nsplit, a.B * a.H), dim3(256), 0, st,
+  LAUNCH_CHECK(KID_DECODE_ATTN, (k_decode_attn<T, D>), dim3((unsigned)(nsplit * a.B * a.H)), dim3(256), 0, st,
                (const T*)a.q, (const T*)a.k_cache, (const T*)a.v_cache, a.cap, a.n_committed, a.n_open,
                a.H, a.G, a.scale * LOG2E, nsplit, part_o, part_ml);
   LAUNCH_CHECK(KID_DECODE_COMBINE, (k_decode_combine<T, D>), dim3(a.B * a.H), dim3(D), 0, st,

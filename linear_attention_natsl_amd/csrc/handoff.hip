@@ -56,7 +56,8 @@ __global__ void __launch_bounds__(256) k_handoff_kv(const T* __restrict__ k, con
                                                     T* __restrict__ v_cache, int32_t* __restrict__ err_flag,
                                                     const int32_t* __restrict__ base_rows,
                                                     const int32_t* __restrict__ n_open) {
-  const int pos = bid_x(), bh = bid_y();
+  const unsigned bid = (unsigned)bid_x();  // (list position, b * H + h) flattened, position fastest
+  const int pos = (int)(bid % (unsigned)nc), bh = (int)(bid / (unsigned)nc);
   const int b = bh / H, h = bh % H, g = (G == 1) ? 0 : h;
   const int64_t bg = (int64_t)b * G + g;
   if (pos >= nsel_before[bg * (nc + 1) + nc]) return;
@@ -108,7 +109,7 @@ hipError_t launch_handoff(const HandoffLaunch& a, void* ws, hipStream_t st) {
     return hipGetLastError();
   };
   auto rows = [&]() {
-    hipLaunchKernelGGL(k_handoff_kv<T>, dim3(nc, a.B * a.H), dim3(256), 0, st, (const T*)a.k, (const T*)a.v, sel,
+    hipLaunchKernelGGL(k_handoff_kv<T>, dim3((unsigned)(nc * a.B * a.H)), dim3(256), 0, st, (const T*)a.k, (const T*)a.v, sel,
                        nsb, a.H, a.G, a.L, a.D, nc, a.cap, (T*)a.k_cache, (T*)a.v_cache, a.err_flag,
                        a.append ? (const int32_t*)a.n_committed : nullptr, (const int32_t*)a.n_open);
     return hipGetLastError();

@@ -155,6 +155,8 @@ struct DecodeLaunch {
   float *o_sm_dbg, *o_gdn_dbg;
 };
 size_t decode_ws_bytes(int B, int H, int G, int D, int cap);
+// nullptr if a decode step supports these sizes, else why not
+const char* decode_dims_problem(int B, int H, int cap);
 // the allocation-free decode step's scratch: a DECODE_SCRATCH_BYTES array per
 // device, 256-byte aligned; its device address on the current device
 constexpr size_t DECODE_SCRATCH_BYTES = (size_t)16 << 20;

@@ -28,7 +28,8 @@ __global__ void __launch_bounds__(256) k_route(const T* __restrict__ x, const fl
                                                int nc, int32_t* __restrict__ route_out,
                                                float* __restrict__ scores) {
   extern __shared__ float s_mean[];  // [d]
-  const int c = bid_x(), b = bid_y();
+  const unsigned bid = (unsigned)bid_x();  // one-dimensional grid: chunk fastest
+  const int c = (int)(bid % (unsigned)nc), b = (int)(bid / (unsigned)nc);
   const T* xc = x + ((int64_t)b * L + (int64_t)c * CHUNK) * d;
   for (int col0 = tid_x() * 8; col0 < d; col0 += 256 * 8) {
     float acc[8];
@@ -77,7 +78,8 @@ __global__ void __launch_bounds__(1024, 2) k_route_wide(const T* __restrict__ x,
                                                      const float* __restrict__ bsc, int L, int d, int G, int nc,
                                                      int32_t* __restrict__ route_out, float* __restrict__ scores) {
   extern __shared__ float s_part[];  // [RS][d] partial sums, then the mean [d] and 2G scores; W_score [d][2G]
-  const int c = bid_x(), b = bid_y();
+  const unsigned bid = (unsigned)bid_x();  // one-dimensional grid: chunk fastest
+  const int c = (int)(bid % (unsigned)nc), b = (int)(bid / (unsigned)nc);
   const int tid = tid_x();
   const int ncg = d >> 3;          // column groups
   const int rs = 1024 / ncg;       // row slices (1 .. 64 ... capped below)
@@ -213,7 +215,8 @@ __global__ void __launch_bounds__(256) k_route_bwd_x(const T* __restrict__ x, co
                                                      int nc, float* __restrict__ ds, float* __restrict__ pooled,
                                                      float* __restrict__ dx) {
   extern __shared__ float s_ds[];  // [G][2]
-  const int c = bid_x(), b = bid_y(), z = (int)__builtin_amdgcn_workgroup_id_z();
+  const unsigned bid = (unsigned)bid_x();  // (chunk, batch) flattened, chunk fastest; z: column block
+  const int c = (int)(bid % (unsigned)nc), b = (int)(bid / (unsigned)nc), z = (int)__builtin_amdgcn_workgroup_id_z();
   const int col = (z * 256 + tid_x()) * 8;
   // the gate sums' loads are issued first, the x rows' next; the barrier
   // before dx waits for both
@@ -369,7 +372,7 @@ hipError_t launch_route_backward(const T* x, const float* w, const float* scores
   float* ds = (float*)wsp;
   float* pooled = (float*)((char*)wsp + al((size_t)B * G * nc * 2 * 4));
   float* part = (float*)((char*)pooled + al((size_t)B * nc * d * 4));
-  hipLaunchKernelGGL(k_route_bwd_x<T>, dim3(nc, B, (d + 2047) / 2048), dim3(256), (size_t)G * 2 * sizeof(float), st,
+  hipLaunchKernelGGL(k_route_bwd_x<T>, dim3((unsigned)(nc * B), 1, (d + 2047) / 2048), dim3(256), (size_t)G * 2 * sizeof(float), st,
                      x, w, scores, dg_sm, dg_lin, L, d, H, G, nc, ds, pooled, dx);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -401,13 +404,13 @@ hipError_t launch_route(const T* x, const float* w, const float* bsc, int B, int
     if (lds <= (size_t)LDS_MAX_BYTES) {
       const hipError_t e = set_lds_limit((const void*)k_route_wide<T>, (int)lds);
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL(k_route_wide<T>, dim3(nc, B), dim3(1024), lds, st, x, w, bsc, L, d, G, nc, route_out,
+      hipLaunchKernelGGL(k_route_wide<T>, dim3((unsigned)(nc * B)), dim3(1024), lds, st, x, w, bsc, L, d, G, nc, route_out,
                          scores);
       return hipGetLastError();
     }
   }
   const size_t lds = (size_t)(d + 2 * G) * sizeof(float);
-  hipLaunchKernelGGL(k_route<T>, dim3(nc, B), dim3(256), lds, st, x, w, bsc, L, d, G, nc, route_out,
+  hipLaunchKernelGGL(k_route<T>, dim3((unsigned)(nc * B)), dim3(256), lds, st, x, w, bsc, L, d, G, nc, route_out,
                      scores);
   return hipGetLastError();
 }

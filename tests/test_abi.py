@@ -287,3 +287,34 @@ def test_decode_noalloc_rejects_oversized_before_enqueue(L):
     assert L.natsl_decode_step_noalloc(C.byref(d), C.byref(c), C.byref(a), None) == 3
     assert b"16777216" in L.natsl_last_error()
     assert L.natsl_decode_step_noalloc(C.byref(d), None, C.byref(a), None) == 1
+
+
+def test_sync_check_level(L):
+    """The synchronous-check debug level is host state: 0..2 are accepted and
+    read back, anything else is INVALID_ARG and changes nothing; without a
+    call, NATSL_SYNC_CHECK in the environment sets it (read in a fresh
+    process)."""
+    import subprocess
+    import sys
+    try:
+        assert L.natsl_set_sync_check(3) == 1 and b"sync check level" in L.natsl_last_error()
+        assert L.natsl_set_sync_check(-1) == 1
+        for lv in (1, 2, 0):
+            assert L.natsl_set_sync_check(lv) == 0 and L.natsl_get_sync_check() == lv
+        N.set_sync_check(1)
+        assert N.get_sync_check() == 1
+        with pytest.raises(N.NatslError):
+            N.set_sync_check(7)
+        assert N.get_sync_check() == 1
+    finally:
+        N.set_sync_check(0)
+    code = "import linear_attention_natsl_amd as N; print(N.get_sync_check())"
+    for env_val, want in (("2", 2), ("1", 1), ("yes", 1), ("0", 0), ("", 0), (None, 0)):
+        env = dict(os.environ)
+        env.pop("NATSL_SYNC_CHECK", None)
+        if env_val is not None:
+            env["NATSL_SYNC_CHECK"] = env_val
+        r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, cwd=ROOT,
+                           timeout=300)
+        assert r.returncode == 0, r.stderr[-2000:]
+        assert r.stdout.strip().splitlines()[-1] == str(want), (env_val, r.stdout)

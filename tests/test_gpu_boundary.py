@@ -150,3 +150,43 @@ def test_softmax_long_tile_list_kernel_bf16_d128():
     el = maxerr(rmsn(host(f1.o_gdn)), ref["n_lin"][:, :, L0:])
     say(f"  out {eo:.3e} n_sm {es:.3e} n_lin {el:.3e}")
     assert max(eo, es, el) <= TOL_BF16
+
+
+def test_sync_check_mode_forward_and_decode(capfd):
+    """Synchronous-check debug mode: with level 1 the forward and a decode
+    step wait for their stream and succeed with results bit-identical to
+    level 0; level 2 also names each entry point on stderr before its wait."""
+    B, H, L, D, d = 1, 4, 1024, 128, 256
+    wl, inp = case(B, H, L, D, d, 83)
+    t = prefill_tensors(inp)
+    dm = N.dims(B, H, L, D, d, N.BF16)
+    f = N.Forward(dm, want_state=True)
+    args = (t["x"], t["q"], t["k"], t["v"], t["alpha"], t["beta"], t["w_score"], t["w_mix"])
+    try:
+        say("[boundary] sync check: level 0 reference")
+        N.set_sync_check(0)
+        f(*args, b_score=t["b_score"])
+        torch.cuda.synchronize()
+        ref = (f.out.clone(), f.route.clone(), f.S_final.clone())
+        for lv in (1, 2):
+            say(f"[boundary] sync check: level {lv}")
+            f.out.zero_()
+            N.set_sync_check(lv)
+            f(*args, b_score=t["b_score"])
+            # no synchronize here: level >= 1 has already waited for the stream
+            assert torch.equal(f.out, ref[0]) and torch.equal(f.route, ref[1]) and torch.equal(f.S_final, ref[2])
+        err = capfd.readouterr().err
+        assert "natsl sync check: natsl_forward" in err
+        st = N.DecodeState(B, H, D, d, cap=256)
+        dd = N.dims(B, H, 256, D, d, N.BF16)
+        step = N.Decode(dd, st)
+        g = torch.Generator().manual_seed(5)
+        mk = lambda *s: torch.randn(*s, generator=g).to("cuda")
+        x, q, k, v = (mk(B, d).bfloat16(), mk(B, H, D).bfloat16(), mk(B, H, D).bfloat16(), mk(B, H, D).bfloat16())
+        alpha = torch.full((B, H), 0.95, device="cuda")
+        beta = torch.full((B, H), 0.5, device="cuda")
+        step(x, q, k, v, alpha, beta, t["w_score"], t["w_mix"])
+        assert "natsl sync check: natsl_decode_step" in capfd.readouterr().err
+        assert torch.isfinite(step.out.float()).all()
+    finally:
+        N.set_sync_check(0)
