@@ -44,10 +44,8 @@
 namespace natsl {
 
 size_t gdn_ws_bytes(int io_is_bf16, int D, int64_t nch) {
-  const size_t ts = io_is_bf16 ? 2 : 4;
-  const size_t per = (size_t)CHUNK * D * ts + (size_t)CHUNK * D * 4 + (size_t)D * CHUNK * ts +
-                     2 * (size_t)CHUNK * CHUNK * ts + 144 * 4;
-  return per * (size_t)nch + 5 * 256;
+  if (io_is_bf16) return D == 64 ? carve_bytes<bf16, 64>(nch) : carve_bytes<bf16, 128>(nch);
+  return D == 64 ? carve_bytes<float, 64>(nch) : carve_bytes<float, 128>(nch);
 }
 
 // ---------------------------------------------------------------- prep ----
@@ -182,7 +180,7 @@ __global__ void __launch_bounds__(256, (GdnCfg<T, D>::ALIAS ? 3 : 2))
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
       if constexpr (scan_head_form<T, D>()) {
-        store8<T>(ws.pm + ch * C::PM + (w * 2 + k2) * 512 + lane * 8, ph[k2]);  // first half of the chunk's slot
+        store8<T>(ws.pm + ch * C::PM + (w * 2 + k2) * 512 + lane * 8, ph[k2]);
       } else {
         store8<T>(ws.pm + (((ch * 4 + w) * 2 + k2) * 2 + 0) * 512 + lane * 8, ph[k2]);
         store8<T>(ws.pm + (((ch * 4 + w) * 2 + k2) * 2 + 1) * 512 + lane * 8, pl[k2]);

@@ -30,14 +30,16 @@
 // Launches (one stream):
 //   k_gdn_prep + scan    the forward in state mode (gdn.hip): every chunk's
 //                        S0 and U, bf16 or fp32 as the io dtype
-//   k_gdn_bwd_prep       one workgroup per chunk-head: T, and the fragment
-//                        copies of P^T, -W^T and Q^T the reverse scan reads
+//   k_gdn_bwd_prep       one workgroup per chunk-head: the fragment copies of
+//                        P^T and -W^T the reverse scan reads
 //   k_gdn_bwd_scan       one workgroup per (head, 16-column slice), chunks in
-//                        reverse: Gc and dU of every chunk, and dS_init
-//   k_gdn_bwd_chunk      one workgroup per chunk-head: dq, dk, dv, dalpha,
-//                        dbeta and the gate derivative
-// The backward prep's outputs reuse the forward prep's workspace, which is
-// dead once the state scan is done.
+//                        reverse: Gc of every chunk, and dS_init
+//   k_gdn_bwd_chunk      one workgroup per chunk-head: T again (as the preps
+//                        compute it) and dU = P^T dO + [committed] K~ Gc, then
+//                        dq, dk, dv, dalpha, dbeta and the gate derivative
+// Workspace: every chunk's S0 and U, then one region that holds the forward
+// prep's output while the state scan runs and, once it is dead, the backward
+// prep's output and every chunk's Gc.
 #include "common.hpp"
 #include "gdn_common.hpp"
 #include "kernels.hpp"
@@ -51,49 +53,46 @@ template <typename T, int D>
 struct GdnBwdWs {
   T* pt;      // [nch][4 rs][2 k2][64][8]  P^T A fragments (rows s, contraction t, accumulator-shaped map)
   T* wtn;     // [nch][D/16][2 k2][64][8]  -W^T A fragments (rows d, contraction s)
-  T* qt;      // [nch][D/16][2 k2][64][8]  Q^T A fragments (rows d, contraction t)
-  float* tm;  // [nch][64][64]             T = (I + diag(b) A)^-1
   float* gm;  // [nch][GM_FLOATS]
-  T* du;      // [B, H, L, D]              dU of every chunk
+  T* gst;     // [nch][D][D]               Gc of every chunk (the carried gradient after it)
 };
 
 static inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// workspace: [S0 of every chunk][U of every chunk][region], where the region
+// holds the forward prep's output (live during the state scan) or, after it,
+// the backward prep's output followed by Gc
 template <typename T, int D>
-static size_t bwd_region_bytes(int64_t nch) {
-  const size_t n = (size_t)nch;
-  return al256(n * CHUNK * CHUNK * sizeof(T)) + 2 * al256(n * CHUNK * D * sizeof(T)) +
-         al256(n * CHUNK * CHUNK * 4) + al256(n * GM_FLOATS * 4) + al256(n * CHUNK * D * sizeof(T));
-}
-
-template <typename T, int D>
-static GdnBwdWs<T, D> carve_bwd(void* ws, int64_t nch) {
-  const size_t n = (size_t)nch;
-  char* p = (char*)ws;
-  GdnBwdWs<T, D> w;
-  w.pt = (T*)p;  p += al256(n * CHUNK * CHUNK * sizeof(T));
-  w.wtn = (T*)p; p += al256(n * CHUNK * D * sizeof(T));
-  w.qt = (T*)p;  p += al256(n * CHUNK * D * sizeof(T));
-  w.tm = (float*)p; p += al256(n * CHUNK * CHUNK * 4);
-  w.gm = (float*)p; p += al256(n * GM_FLOATS * 4);
-  w.du = (T*)p;
-  return w;
-}
-
-// workspace: [forward prep / backward prep region][S0 per chunk][U][Gc per chunk]
-template <typename T, int D>
-static size_t region_bytes(int64_t nch) {
-  const size_t f = al256(gdn_ws_bytes(sizeof(T) == 2, D, nch)), b = al256(bwd_region_bytes<T, D>(nch));
-  return f > b ? f : b;
-}
+struct BwdLayout {
+  size_t s0, u, region, pt, wtn, gm, gst, total;
+  explicit BwdLayout(int64_t nch) {
+    const size_t n = (size_t)nch;
+    s0 = 0;
+    u = al256(n * D * D * sizeof(T));
+    region = u + al256(n * CHUNK * D * sizeof(T));
+    pt = region;
+    wtn = pt + al256(n * CHUNK * CHUNK * sizeof(T));
+    gm = wtn + al256(n * CHUNK * D * sizeof(T));
+    gst = gm + al256(n * GM_FLOATS * 4);
+    const size_t bwd_end = gst + al256(n * D * D * sizeof(T));
+    const size_t fwd_end = region + al256(carve_bytes<T, D>(nch));
+    total = bwd_end > fwd_end ? bwd_end : fwd_end;
+  }
+  GdnBwdWs<T, D> carve(void* ws) const {
+    char* p = (char*)ws;
+    GdnBwdWs<T, D> w;
+    w.pt = (T*)(p + pt);
+    w.wtn = (T*)(p + wtn);
+    w.gm = (float*)(p + gm);
+    w.gst = (T*)(p + gst);
+    return w;
+  }
+};
 
 size_t gdn_bwd_ws_bytes(int io_is_bf16, int B, int H, int L, int D) {
   const int64_t nch = (int64_t)B * H * (L / CHUNK);
-  const size_t ts = io_is_bf16 ? 2 : 4;
-  size_t r;
-  if (io_is_bf16) r = D == 64 ? region_bytes<bf16, 64>(nch) : region_bytes<bf16, 128>(nch);
-  else r = D == 64 ? region_bytes<float, 64>(nch) : region_bytes<float, 128>(nch);
-  return r + 2 * al256((size_t)nch * D * D * ts) + al256((size_t)nch * CHUNK * D * ts);
+  if (io_is_bf16) return D == 64 ? BwdLayout<bf16, 64>(nch).total : BwdLayout<bf16, 128>(nch).total;
+  return D == 64 ? BwdLayout<float, 64>(nch).total : BwdLayout<float, 128>(nch).total;
 }
 
 // ------------------------------------------------------------ backward prep
@@ -102,7 +101,7 @@ struct BwdPrepCfg {
   static constexpr int RL = kg_row<T, D>();
   static constexpr int KG_BYTES = 16 * RL * 4 * (int)sizeof(T);
   static constexpr int LTP = CHUNK + 1;
-  static constexpr int OFF_KG = 0, OFF_QG = KG_BYTES, OFF_LT = 2 * KG_BYTES;
+  static constexpr int OFF_KG = 0, OFF_LT = KG_BYTES;
   static constexpr int OFF_RS = OFF_LT + CHUNK * LTP * 4;
   static constexpr int OFF_GL = OFF_RS + 3 * 16 * 17 * 4;
   static constexpr int LDS = OFF_GL + 3 * CHUNK * 4;
@@ -121,7 +120,6 @@ __global__ void __launch_bounds__(256) k_gdn_bwd_prep(const T* __restrict__ q, c
   using C = BwdPrepCfg<T, D>;
   extern __shared__ __align__(16) unsigned char lds[];
   T* Kg = (T*)(lds + C::OFF_KG);
-  T* Qg = (T*)(lds + C::OFF_QG);
   float* LT = (float*)(lds + C::OFF_LT);
   float* Rs = (float*)(lds + C::OFF_RS);
   float* gl = (float*)(lds + C::OFF_GL);  // cumulative log2 decay
@@ -138,13 +136,10 @@ __global__ void __launch_bounds__(256) k_gdn_bwd_prep(const T* __restrict__ q, c
   constexpr int TASKS = (CHUNK / 4) * (D / 8);
   static_assert(TASKS <= 256, "one task per thread");
   const int kg = t / (D / 8), col = (t % (D / 8)) * 8;
-  Frag<T> kr[4], qr[4];
+  Frag<T> kr[4];
   if (t < TASKS) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      kr[i] = load8<T>(k + (tok0 + 4 * kg + i) * D + col);
-      qr[i] = load8<T>(q + (tok0 + 4 * kg + i) * D + col);
-    }
+    for (int i = 0; i < 4; ++i) kr[i] = load8<T>(k + (tok0 + 4 * kg + i) * D + col);
   }
   Frag<T> ka[C::KF], qa[C::KF];
 #pragma unroll
@@ -174,8 +169,6 @@ __global__ void __launch_bounds__(256) k_gdn_bwd_prep(const T* __restrict__ q, c
     for (int j = 0; j < 8; ++j) {
       st4<T>(Kg + kg_index<C::RL>(kg, col + j), to_f32(frag_get<T>(kr[0], j)), to_f32(frag_get<T>(kr[1], j)),
              to_f32(frag_get<T>(kr[2], j)), to_f32(frag_get<T>(kr[3], j)));
-      st4<T>(Qg + kg_index<C::RL>(kg, col + j), to_f32(frag_get<T>(qr[0], j)), to_f32(frag_get<T>(qr[1], j)),
-             to_f32(frag_get<T>(qr[2], j)), to_f32(frag_get<T>(qr[3], j)));
     }
   }
   __syncthreads();
@@ -210,7 +203,6 @@ __global__ void __launch_bounds__(256) k_gdn_bwd_prep(const T* __restrict__ q, c
   }
   __syncthreads();
   lt_inverse64<C::LTP>(LT, Rs);
-  for (int e = t; e < CHUNK * CHUNK; e += 256) bw.tm[ch * CHUNK * CHUNK + e] = LT[(e >> 6) * C::LTP + (e & 63)];
 
   // W = T diag(b gamma) K, rows 16w .. 16w+15 (T split into bf16 hi + lo)
   constexpr bool SPLIT = sizeof(T) == 2;
@@ -240,12 +232,6 @@ __global__ void __launch_bounds__(256) k_gdn_bwd_prep(const T* __restrict__ q, c
   for (int n = 0; n < C::NT; ++n)
     st4<T>(bw.wtn + ((ch * C::NT + n) * 2 + kb) * 512 + lane * 8 + hb * 4, -wa[n][0], -wa[n][1], -wa[n][2],
            -wa[n][3]);
-  // Q^T fragments (rows d, tokens in the accumulator-shaped map)
-  for (int f = w; f < C::NT * 2; f += 4) {
-    const int n = f >> 1, k2 = f & 1;
-    store8<T>(bw.qt + ((ch * C::NT + n) * 2 + k2) * 512 + lane * 8,
-              ld4x2<T>(Qg + kg_index<C::RL>(8 * k2 + g, 16 * n + c), Qg + kg_index<C::RL>(8 * k2 + 4 + g, 16 * n + c)));
-  }
 }
 
 // -------------------------------------------------------------- reverse scan
@@ -255,7 +241,12 @@ struct BwdScanOps {
   Frag<T> ka[KF];      // K rows 16w + c (contraction d, contiguous)
   Frag<T> pt[2];       // P^T, row tile w
   Frag<T> wt[DTW][2];  // -W^T, d tiles DTW w + x
-  Frag<T> qt[DTW][2];  // Q^T, d tiles DTW w + x
+  // Q^T (rows d, tokens in the accumulator-shaped map).  bf16, D = 128: the
+  // chunk's Q rows, 16 bytes per piece (pieces tid + 256 i), for the
+  // transposed LDS reads; otherwise the fragments gathered from q directly
+  static constexpr bool QTR = sizeof(T) == 2 && D == 128;
+  bf16x8 qv[QTR ? 4 : 1];
+  Frag<T> qt[QTR ? 1 : DTW][2];
   float dov[2][NV][8]; // d_o at tokens 32 k2 + kmap_acc(g, j), columns dv0 + 16 n + c
   f32x4 gk[2][2];      // gamma at tokens 32 k2 + 4g + i and 32 k2 + 16 + 4g + i
   f32x4 ek;            // exp(g_C - g) at rows 16w + 4g + i
@@ -265,13 +256,28 @@ struct BwdScanOps {
 
 template <typename T, int D, int DVT>
 __device__ __forceinline__ void bwd_scan_load(BwdScanOps<T, D, DVT>& op, const GdnBwdWs<T, D>& bw, const T* kh,
-                                              const float* doh, const int32_t* rt, int64_t bh, int nc, int cc,
-                                              int dv0) {
+                                              const T* qh, const float* doh, const int32_t* rt, int64_t bh, int nc,
+                                              int cc, int dv0) {
   using O = BwdScanOps<T, D, DVT>;
   constexpr int NT = D / 16;
   const int lane = lane_id(), w = wave_id();
   const int g = lane >> 4, c = lane & 15;
   const int64_t ch = bh * nc + cc;
+  if constexpr (O::QTR) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = tid_x() + 256 * i;
+      op.qv[i] = *reinterpret_cast<const bf16x8*>(qh + ((int64_t)cc * CHUNK + (e >> 4)) * D + 8 * (e & 15));
+    }
+  } else {
+#pragma unroll
+    for (int x = 0; x < O::DTW; ++x)
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          op.qt[x][k2].v[j] = qh[((int64_t)cc * CHUNK + 32 * k2 + kmap_acc(g, j)) * D + 16 * (O::DTW * w + x) + c];
+  }
 #pragma unroll
   for (int ks = 0; ks < O::KF; ++ks) op.ka[ks] = load8<T>(kh + ((int64_t)cc * CHUNK + 16 * w + c) * D + 32 * ks + 8 * g);
 #pragma unroll
@@ -282,7 +288,6 @@ __device__ __forceinline__ void bwd_scan_load(BwdScanOps<T, D, DVT>& op, const G
     for (int k2 = 0; k2 < 2; ++k2) {
       const int dt = O::DTW * w + x;
       op.wt[x][k2] = load8<T>(bw.wtn + ((ch * NT + dt) * 2 + k2) * 512 + lane * 8);
-      op.qt[x][k2] = load8<T>(bw.qt + ((ch * NT + dt) * 2 + k2) * 512 + lane * 8);
     }
 #pragma unroll
   for (int k2 = 0; k2 < 2; ++k2)
@@ -305,12 +310,15 @@ __device__ __forceinline__ void bwd_scan_load(BwdScanOps<T, D, DVT>& op, const G
 // One workgroup per (b, h, DVT-column slice of Dv), chunks in reverse.  The
 // fp32 carried gradient lives in registers (rows d = 16 (DTW w + x) + 4g + i,
 // columns dv0 + 16 n + c), a T copy transposed in LDS feeds K Gc; dU goes
-// through LDS key groups into -W^T dU.  Per chunk: Gc -> workspace, then
-//   Z = K Gc;  dU = P^T dO + [committed] diag(e) Z -> workspace
+// through LDS key groups into -W^T dU, and (bf16, D = 128) the chunk's Q rows
+// (loaded with the chunk's other operands, one chunk ahead) through LDS into
+// Q^T by transposed reads.  Per chunk: Gc -> workspace, then
+//   Z = K Gc;  dU = P^T dO + [committed] diag(e) Z
 //   Gc <- [committed ? gamma_C : 1] Gc + Q^T (gamma dO) + (-W^T) dU.
 template <typename T, int D, int DVT>
 __global__ void __launch_bounds__(256, 1)
-    k_gdn_bwd_scan(const T* __restrict__ k, const float* __restrict__ d_o, const int32_t* __restrict__ route,
+    k_gdn_bwd_scan(const T* __restrict__ q, const T* __restrict__ k, const float* __restrict__ d_o,
+                   const int32_t* __restrict__ route,
                    GdnBwdWs<T, D> bw, const float* __restrict__ dS_final, T* __restrict__ g_out,
                    float* __restrict__ dS_init, int H, int L, int G) {
   using O = BwdScanOps<T, D, DVT>;
@@ -318,6 +326,9 @@ __global__ void __launch_bounds__(256, 1)
   __shared__ __align__(16) T Gp[2][DVT * SPP];
   constexpr int URL = kg_row<T, DVT>();
   __shared__ __align__(16) T Ug[(CHUNK / 4) * URL * 4];
+  // Q rows of the chunk (bf16, D = 128): 16-byte piece q of row r at slot
+  // q ^ ((r & 7) << 1), which keeps the transposed reads conflict-free
+  __shared__ __align__(16) unsigned char Qs[O::QTR ? CHUNK * 256 : 16];
 
   const int nc = L / CHUNK;
   const int nvt = D / DVT;
@@ -332,6 +343,7 @@ __global__ void __launch_bounds__(256, 1)
   const int32_t* rt = route + ((int64_t)b * G + grp) * nc;
   const int dv0 = vt * DVT;
   const T* kh = k + bh * L * D;
+  const T* qh = q + bh * L * D;
   const float* doh = d_o + bh * L * D;
   const int lane = lane_id(), w = wave_id();
   const int g = lane >> 4, c = lane & 15;
@@ -360,6 +372,15 @@ __global__ void __launch_bounds__(256, 1)
 
   auto step = [&](const O& op, int cc) {
     const int64_t ch = bh * nc + cc;
+    // Q rows -> LDS (the previous chunk's reads of Qs ended before its last
+    // barrier; the barrier after the dU stores publishes these)
+    if constexpr (O::QTR) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = tid_x() + 256 * i, r = e >> 4;
+        *reinterpret_cast<bf16x8*>(Qs + r * 256 + (((e & 15) ^ ((r & 7) << 1)) * 16)) = op.qv[i];
+      }
+    }
 #pragma unroll
     for (int x = 0; x < O::DTW; ++x)
 #pragma unroll
@@ -408,12 +429,7 @@ __global__ void __launch_bounds__(256, 1)
 #pragma unroll
       for (int i = 0; i < 4; ++i) du[n][i] = xa[n][i] + (lin ? op.ek[i] * z[n][i] : 0.f);
 #pragma unroll
-    for (int n = 0; n < O::NV; ++n) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        bw.du[(bh * L + (int64_t)cc * CHUNK + 16 * w + 4 * g + i) * D + dv0 + 16 * n + c] = from_f32<T>(du[n][i]);
-      st4<T>(&Ug[kg_index<URL>(4 * w + g, 16 * n + c)], du[n][0], du[n][1], du[n][2], du[n][3]);
-    }
+    for (int n = 0; n < O::NV; ++n) st4<T>(&Ug[kg_index<URL>(4 * w + g, 16 * n + c)], du[n][0], du[n][1], du[n][2], du[n][3]);
     lds_barrier();
     Frag<T> bu[2][O::NV];
 #pragma unroll
@@ -421,6 +437,26 @@ __global__ void __launch_bounds__(256, 1)
 #pragma unroll
       for (int n = 0; n < O::NV; ++n)
         bu[k2][n] = ld4x2<T>(&Ug[kg_index<URL>(8 * k2 + g, 16 * n + c)], &Ug[kg_index<URL>(8 * k2 + 4 + g, 16 * n + c)]);
+    // Q^T A fragments (rows d, tokens in the accumulator-shaped map): lane c
+    // of group g reads rows 32 k2 + 4g + c / 4 and +16, columns 16 dt + 4 (c % 4) .. +3
+    Frag<T> qt[O::DTW][2];
+#pragma unroll
+    for (int x = 0; x < O::DTW; ++x)
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        if constexpr (O::QTR) {
+          const int dt = O::DTW * w + x;
+          const int colq = (16 * dt + 4 * (c & 3)) >> 3, half = (c & 1) * 8;
+          const int r0 = 32 * k2 + 4 * g + (c >> 2), r1 = r0 + 16;
+          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4i16*)(Qs + r0 * 256 + ((colq ^ ((r0 & 7) << 1)) * 16) + half));
+          const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4i16*)(Qs + r1 * 256 + ((colq ^ ((r1 & 7) << 1)) * 16) + half));
+          qt[x][k2].v = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        } else {
+          qt[x][k2] = op.qt[x][k2];
+        }
+      }
 #pragma unroll
     for (int x = 0; x < O::DTW; ++x)
 #pragma unroll
@@ -428,7 +464,7 @@ __global__ void __launch_bounds__(256, 1)
         f32x4 acc = sm[x][n] * gce;
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
-          mma(acc, op.qt[x][k2], bdg[k2][n]);
+          mma(acc, qt[x][k2], bdg[k2][n]);
           mma(acc, op.wt[x][k2], bu[k2][n]);
         }
         sm[x][n] = acc;
@@ -439,12 +475,12 @@ __global__ void __launch_bounds__(256, 1)
   };
 
   O ops[2];
-  bwd_scan_load<T, D, DVT>(ops[0], bw, kh, doh, rt, bh, nc, nc - 1, dv0);
+  bwd_scan_load<T, D, DVT>(ops[0], bw, kh, qh, doh, rt, bh, nc, nc - 1, dv0);
   int cc = nc - 1;
   for (; cc >= 1; cc -= 2) {
-    bwd_scan_load<T, D, DVT>(ops[1], bw, kh, doh, rt, bh, nc, cc - 1, dv0);
+    bwd_scan_load<T, D, DVT>(ops[1], bw, kh, qh, doh, rt, bh, nc, cc - 1, dv0);
     step(ops[0], cc);
-    bwd_scan_load<T, D, DVT>(ops[0], bw, kh, doh, rt, bh, nc, cc >= 2 ? cc - 2 : 0, dv0);
+    bwd_scan_load<T, D, DVT>(ops[0], bw, kh, qh, doh, rt, bh, nc, cc >= 2 ? cc - 2 : 0, dv0);
     step(ops[1], cc - 1);
   }
   if (cc == 0) step(ops[0], 0);
@@ -468,16 +504,18 @@ struct BwdChunkCfg {
   static constexpr int KV = D / 32;  // contraction steps over D
   static constexpr int PM = 68;      // pitch of the fp32 64 x 64 matrices (16-byte rows)
   static constexpr int PT = D + 16 / (int)sizeof(T);
-  // U, dU and K staged in LDS (else read from global memory)
+  // U and K staged in LDS (else read from global memory); dU is computed
+  // here and always lives in LDS
   static constexpr bool FIT = sizeof(T) == 2 || D == 64;
   static constexpr int M_BYTES = CHUNK * PM * 4;
   static constexpr int T_BYTES = CHUNK * PT * (int)sizeof(T);
   static constexpr int OFF_TL = 0, OFF_AL = M_BYTES, OFF_FL = 2 * M_BYTES, OFF_ML = 3 * M_BYTES;
   static constexpr int OFF_X1 = 4 * M_BYTES;
-  static constexpr int OFF_UL = OFF_X1 + T_BYTES;
-  static constexpr int OFF_DUL = OFF_UL + (FIT ? T_BYTES : 0);
-  static constexpr int OFF_KL = OFF_DUL + (FIT ? T_BYTES : 0);
+  static constexpr int OFF_DUL = OFF_X1 + T_BYTES;
+  static constexpr int OFF_UL = OFF_DUL + T_BYTES;
+  static constexpr int OFF_KL = OFF_UL + (FIT ? T_BYTES : 0);
   static constexpr int OFF_VEC = OFF_KL + (FIT ? T_BYTES : 0);
+  static_assert(3 * 16 * 17 * 4 <= T_BYTES, "the inverse's scratch fits in X1");
   // g2, gamma, e, beta, beta gamma, alpha; partial row sums pbeta, pgam,
   // pts, cdg [4][64]; rdg, rbeta [64]; red [4]
   static constexpr int VEC_FLOATS = 6 * 64 + 4 * 4 * 64 + 2 * 64 + 4;
@@ -509,13 +547,15 @@ __device__ __forceinline__ void row_partials(const f32x4& v, float* dst, int g, 
 // products (rows t = 16w + 4g + i) and columns 16 (CT w + ct) + c of the
 // 64 x D products (all four row tiles).  All contractions use the row map
 // (8g + j), operands from LDS, or from global memory where they are read
-// once (dO, the S0 / Gc fragments).
+// once (dO, the S0 / Gc fragments).  T and dU are computed here rather than
+// stored by the preps and the reverse scan: T by the preps' own steps (so
+// the same values), dU from the reverse scan's bf16 operands.
 template <typename T, int D>
 __global__ void __launch_bounds__(256, 1)
     k_gdn_bwd_chunk(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                     const float* __restrict__ alpha, const float* __restrict__ beta, const float* __restrict__ d_o,
                     const int32_t* __restrict__ route, GdnBwdWs<T, D> bw, const T* __restrict__ s0,
-                    const T* __restrict__ u, const T* __restrict__ gst, float* __restrict__ dq,
+                    const T* __restrict__ u, float* __restrict__ dq,
                     float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ dalpha,
                     float* __restrict__ dbeta, float* __restrict__ dgate, int H, int L, int G) {
   using C = BwdChunkCfg<T, D>;
@@ -557,10 +597,11 @@ __global__ void __launch_bounds__(256, 1)
   const T* vc = v + tok0 * D;
   const float* doc = d_o + tok0 * D;
   const T* uc = u + tok0 * D;
-  const T* duc = bw.du + tok0 * D;
-  // U, dU, K rows: LDS copies (pitch PT) or global memory (pitch D)
+  const T* gst = bw.gst;
+  // U, K rows: LDS copies (pitch PT) or global memory (pitch D); dU rows in LDS (pitch PT)
   const T* Ub = C::FIT ? (const T*)(lds + C::OFF_UL) : uc;
-  const T* dUb = C::FIT ? (const T*)(lds + C::OFF_DUL) : duc;
+  T* dUl = (T*)(lds + C::OFF_DUL);
+  const T* dUb = dUl;
   const T* Kb = C::FIT ? (const T*)(lds + C::OFF_KL) : kc;
   constexpr int UP = C::FIT ? PT : D;
 
@@ -583,18 +624,13 @@ __global__ void __launch_bounds__(256, 1)
     bgm[lane] = bt * gm_;
     alp[lane] = a;
   }
-  for (int e = t; e < CHUNK * CHUNK / 4; e += 256)
-    *reinterpret_cast<f32x4*>(Tl + (e >> 4) * PM + (e & 15) * 4) =
-        *reinterpret_cast<const f32x4*>(bw.tm + ch * CHUNK * CHUNK + e * 4);
   if constexpr (C::FIT) {
     constexpr int PER = 16 / (int)sizeof(T), NP = CHUNK * D / PER;
     T* Ul = (T*)(lds + C::OFF_UL);
-    T* dUl = (T*)(lds + C::OFF_DUL);
     T* Kl = (T*)(lds + C::OFF_KL);
     for (int e = t; e < NP; e += 256) {
       const int r = e / (D / PER), cl = (e % (D / PER)) * PER;
       *reinterpret_cast<f32x4*>(Ul + r * PT + cl) = *reinterpret_cast<const f32x4*>(uc + r * D + cl);
-      *reinterpret_cast<f32x4*>(dUl + r * PT + cl) = *reinterpret_cast<const f32x4*>(duc + r * D + cl);
       *reinterpret_cast<f32x4*>(Kl + r * PT + cl) = *reinterpret_cast<const f32x4*>(kc + r * D + cl);
     }
   }
@@ -616,7 +652,7 @@ __global__ void __launch_bounds__(256, 1)
   if (lane == 0) red[w] = sg;
   __syncthreads();
 
-  // ---- phase 1 (row tile w): A, P, dP
+  // ---- phase 1 (row tile w): A, L = diag(b) A (-> Tl), P (-> Ml), dP
   f32x4 akk[4], apq[4], dpa[4];
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) {
@@ -648,7 +684,9 @@ __global__ void __launch_bounds__(256, 1)
         const int r = 16 * w + 4 * g + i, s = 16 * ct + c;
         const float gmx = __builtin_amdgcn_exp2f(g2[r] - g2[s]);
         Al[r * PM + s] = (s < r) ? gmx * akk[ct][i] : 0.f;
+        Tl[r * PM + s] = (s < r) ? bet[r] * gmx * akk[ct][i] : 0.f;  // as the preps form it
         const float p = (s <= r) ? gmx * apq[ct][i] : 0.f;
+        Ml[r * PM + s] = p;
         const float dp = (s <= r) ? dpa[ct][i] : 0.f;
         Fl[r * PM + s] = dp * gmx;
         rsum[i] += dp * p;
@@ -660,6 +698,50 @@ __global__ void __launch_bounds__(256, 1)
     row_partials(rsum, rdg + 16 * w, g, c);
   }
   __syncthreads();
+
+  // ---- phase 1b (columns of wave w): dU = P^T dO + [committed] diag(e) K Gc
+  // -> dUl, the reverse scan's dU from the same bf16 operands (dO rounded to
+  // T, Gc as stored); then T = (I + L)^-1 in place in Tl, whose barriers also
+  // publish dUl
+  // (one 16-column tile at a time: 32 accumulator registers)
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    const int col = 16 * (CT * w + ct) + c;
+    f32x4 dua[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) dua[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      const int s0_ = 32 * k2 + 8 * g;
+      const Frag<T> bdo = frag_fn<T>([&](int j) { return doc[(s0_ + j) * D + col]; });
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+        mma(dua[rt], frag_fn<T>([&](int j) { return Ml[(s0_ + j) * PM + 16 * rt + c]; }), bdo);
+    }
+    if (lin) {
+      f32x4 kga[4];
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) kga[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kv = 0; kv < KV; ++kv) {
+        const int d0 = 32 * kv + 8 * g;
+        const Frag<T> bgc = frag_fn<T>([&](int j) { return to_f32(gst[(ch * D + d0 + j) * D + col]); });
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) mma(kga[rt], load8<T>(Kb + (16 * rt + c) * UP + 32 * kv + 8 * g), bgc);
+      }
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dua[rt][i] += ekv[16 * rt + 4 * g + i] * kga[rt][i];
+    }
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dUl[(16 * rt + 4 * g + i) * PT + col] = from_f32<T>(dua[rt][i]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  lt_inverse64<PM>(Tl, (float*)X1);
 
   // ---- phase 2 (columns of wave w): dO S0^T, U Gc^T, T^T dU, A U, TdU S0^T
   f32x4 dqa[4][CT], dka[4][CT];
@@ -727,7 +809,7 @@ __global__ void __launch_bounds__(256, 1)
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
         const int col = 16 * (CT * w + ct) + c;
-        bdu[ct] = frag_fn<T>([&](int j) { return to_f32(dUb[(t0 + j) * UP + col]); });
+        bdu[ct] = frag_fn<T>([&](int j) { return to_f32(dUb[(t0 + j) * PT + col]); });
         bu[ct] = frag_fn<T>([&](int j) { return to_f32(Ub[(t0 + j) * UP + col]); });
       }
 #pragma unroll
@@ -804,7 +886,7 @@ __global__ void __launch_bounds__(256, 1)
     for (int ct = 0; ct < 4; ++ct) dta[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kv = 0; kv < KV; ++kv) {
-      const Frag<T> a = load8<T>(dUb + (16 * w + c) * UP + 32 * kv + 8 * g);
+      const Frag<T> a = load8<T>(dUb + (16 * w + c) * PT + 32 * kv + 8 * g);
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) mma(dta[ct], a, load8<T>(X1 + (16 * ct + c) * PT + 32 * kv + 8 * g));
     }
@@ -953,25 +1035,24 @@ hipError_t launch_gdn_backward(const T* q, const T* k, const T* v, const float* 
                                float* dgate, void* ws, int B, int H, int L, int G, hipStream_t st) {
   const int nc = L / CHUNK;
   const int64_t nch = (int64_t)B * H * nc;
-  const size_t rb = region_bytes<T, D>(nch);
-  char* p = (char*)ws + rb;
-  T* s0 = (T*)p;  p += al256((size_t)nch * D * D * sizeof(T));
-  T* u = (T*)p;   p += al256((size_t)nch * CHUNK * D * sizeof(T));
-  T* gst = (T*)p;
-  hipError_t e = launch_gdn_states<T, D>(q, k, v, alpha, beta, route, S_init, s0, u, ws, B, H, L, G, st);
+  const BwdLayout<T, D> lay(nch);
+  T* s0 = (T*)((char*)ws + lay.s0);
+  T* u = (T*)((char*)ws + lay.u);
+  hipError_t e = launch_gdn_states<T, D>(q, k, v, alpha, beta, route, S_init, s0, u, (char*)ws + lay.region, B, H, L,
+                                         G, st);
   if (e != hipSuccess) return e;
-  GdnBwdWs<T, D> bw = carve_bwd<T, D>(ws, nch);
+  GdnBwdWs<T, D> bw = lay.carve(ws);
   using PC = BwdPrepCfg<T, D>;
   if ((e = set_lds_limit((const void*)k_gdn_bwd_prep<T, D>, PC::LDS)) != hipSuccess) return e;
   hipLaunchKernelGGL((k_gdn_bwd_prep<T, D>), dim3((unsigned)nch), dim3(256), PC::LDS, st, q, k, alpha, beta, bw, L);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((k_gdn_bwd_scan<T, D, BWD_DVT>), dim3((unsigned)(B * H * (D / BWD_DVT))), dim3(256), 0, st, k,
-                     d_o, route, bw, dS_final, gst, dS_init, H, L, G);
+  hipLaunchKernelGGL((k_gdn_bwd_scan<T, D, BWD_DVT>), dim3((unsigned)(B * H * (D / BWD_DVT))), dim3(256), 0, st, q,
+                     k, d_o, route, bw, dS_final, bw.gst, dS_init, H, L, G);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   using CC = BwdChunkCfg<T, D>;
   if ((e = set_lds_limit((const void*)k_gdn_bwd_chunk<T, D>, CC::LDS)) != hipSuccess) return e;
   hipLaunchKernelGGL((k_gdn_bwd_chunk<T, D>), dim3((unsigned)nch), dim3(256), CC::LDS, st, q, k, v, alpha, beta, d_o,
-                     route, bw, (const T*)s0, (const T*)u, (const T*)gst, dq, dk, dv, dalpha, dbeta, dgate, H, L, G);
+                     route, bw, (const T*)s0, (const T*)u, dq, dk, dv, dalpha, dbeta, dgate, H, L, G);
   return hipGetLastError();
 }
 

@@ -33,11 +33,13 @@ struct GdnCfg {
   static constexpr int OFF_GL = ALIAS ? OFF_LT + CHUNK * LTP * 4 : OFF_RS + RS_BYTES;
   static constexpr int PREP_LDS = OFF_GL + 3 * CHUNK * 4;
   static_assert(!ALIAS || 3 * PREP_LDS <= 160 * 1024, "three prep workgroups per CU");
-  // per chunk-head workspace (elements)
+  // per chunk-head workspace (elements).  The head-form scan (bf16, D = 128)
+  // reads K itself and takes P in bf16: no K^T copy, no P remainder.
+  static constexpr bool HEAD = sizeof(T) == 2 && D == 128;
   static constexpr int64_t WN = (int64_t)CHUNK * D;   // T
   static constexpr int64_t UT = (int64_t)CHUNK * D;   // float
-  static constexpr int64_t KT = (int64_t)D * CHUNK;   // T
-  static constexpr int64_t PM = 2 * (int64_t)CHUNK * CHUNK;  // T: hi and lo parts
+  static constexpr int64_t KT = HEAD ? 0 : (int64_t)D * CHUNK;                 // T
+  static constexpr int64_t PM = (HEAD ? 1 : 2) * (int64_t)CHUNK * CHUNK;       // T: P, and its remainder
   static constexpr int64_t GM = 144;  // float: gamma[64], gamma_C at 64, exp(g_C - g)[64] at 80
 };
 
@@ -50,6 +52,8 @@ struct GdnWs {
   float* gm;
 };
 
+// The chunk prep's workspace for nch chunk-heads: carve() lays it out (from
+// a 256-byte aligned base), carve_bytes() is its size.
 template <typename T, int D>
 static GdnWs<T, D> carve(void* ws, int64_t nch) {
   using C = GdnCfg<T, D>;
@@ -58,10 +62,17 @@ static GdnWs<T, D> carve(void* ws, int64_t nch) {
   GdnWs<T, D> w;
   w.wn = (T*)p; p += al(C::WN * nch * sizeof(T));
   w.ut = (float*)p; p += al(C::UT * nch * sizeof(float));
-  w.kt = (T*)p; p += al(C::KT * nch * sizeof(T));
+  w.kt = C::KT ? (T*)p : nullptr; p += al(C::KT * nch * sizeof(T));
   w.pm = (T*)p; p += al(C::PM * nch * sizeof(T));
   w.gm = (float*)p;
   return w;
+}
+template <typename T, int D>
+static size_t carve_bytes(int64_t nch) {
+  using C = GdnCfg<T, D>;
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  return al(C::WN * nch * sizeof(T)) + al(C::UT * nch * sizeof(float)) + al(C::KT * nch * sizeof(T)) +
+         al(C::PM * nch * sizeof(T)) + al(C::GM * nch * sizeof(float));
 }
 
 // The scan runs one workgroup per head for bf16 with D = 128, and one per
