@@ -50,7 +50,7 @@ size_t gdn_ws_bytes(int io_is_bf16, int D, int64_t nch) {
 
 // ---------------------------------------------------------------- prep ----
 template <typename T, int D>
-__global__ void __launch_bounds__(256, (GdnCfg<T, D>::ALIAS ? 3 : 2))
+__global__ void __launch_bounds__(256, (GdnCfg<T, D>::PREP_WGS))
     k_gdn_prep(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                const float* __restrict__ alpha, const float* __restrict__ beta, GdnWs<T, D> ws,
                int L) {
@@ -191,7 +191,14 @@ __global__ void __launch_bounds__(256, (GdnCfg<T, D>::ALIAS ? 3 : 2))
 
   lt_inverse64<C::LTP>(LT, Rs);
 
-  if constexpr (C::ALIAS) {  // the inverse's scratch is dead (barrier above)
+  // this lane's T values: row 16w + c, columns 32 k2 + kmap_acc(g, j)
+  float tvr[2][8];
+#pragma unroll
+  for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) tvr[k2][j] = LT[(16 * w + c) * C::LTP + 32 * k2 + kmap_acc(g, j)];
+  if constexpr (C::ALIAS) {  // the key-group copies overwrite the inverse's scratch and T
+    __syncthreads();
     store_kv_groups();
     __syncthreads();
   }
@@ -206,11 +213,10 @@ __global__ void __launch_bounds__(256, (GdnCfg<T, D>::ALIAS ? 3 : 2))
 #pragma unroll
   for (int k2 = 0; k2 < 2; ++k2) {
     Frag<T> a1, a2, a1l, a2l;
-    const float* trow = LT + (16 * w + c) * C::LTP;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int tk = 32 * k2 + kmap_acc(g, j);
-      const float tv = trow[tk];
+      const float tv = tvr[k2][j];
       const float x1 = tv * bl[tk], x2 = tv * gbl[tk];
       frag_set(a1, j, x1);
       frag_set(a2, j, x2);

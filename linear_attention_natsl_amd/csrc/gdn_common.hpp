@@ -15,24 +15,29 @@ struct GdnCfg {
   static constexpr int KF = D / 32;
   static constexpr int NT = D / 16;                     // 16-wide column tiles of D
   // LDS layout of the prep kernel (bytes).  The bf16, D = 128 form (the one
-  // the head-form scan reads) keeps the K rows, the inverse's block scratch
-  // and the K / V key-group copies in one region, live one after the other
-  // (K and V wait in registers until the inverse is done), so that three
-  // workgroups fit in a CU's 160 KiB instead of two.
+  // the head-form scan reads) keeps its buffers live one after the other in
+  // one region: the K rows and L / T (products and inverse), the inverse's
+  // block scratch over the dead K rows, then the K / V key-group copies over
+  // everything (K and V wait in registers until the inverse is done, and each
+  // lane holds the 16 values of T it needs in registers by then), so that four
+  // workgroups fit in a CU's 160 KiB.
   static constexpr bool ALIAS = sizeof(T) == 2 && D == 128;
   static constexpr int RL = kg_row<T, D>();             // padded key-group row (columns)
   static constexpr int KS_BYTES = CHUNK * KP * (int)sizeof(T);
   static constexpr int KG_BYTES = 16 * RL * 4 * (int)sizeof(T);
+  static constexpr int LT_BYTES = CHUNK * LTP * 4;
   static constexpr int RS_BYTES = 3 * 16 * 17 * 4;
   static constexpr int OFF_KS = 0;
   static constexpr int OFF_KG = ALIAS ? 0 : OFF_KS + KS_BYTES;
   static constexpr int OFF_VG = OFF_KG + KG_BYTES;
-  static constexpr int R0_END = ALIAS ? (KS_BYTES > 2 * KG_BYTES ? KS_BYTES : 2 * KG_BYTES) : OFF_VG + KG_BYTES;
-  static constexpr int OFF_LT = R0_END;
-  static constexpr int OFF_RS = ALIAS ? 0 : OFF_LT + CHUNK * LTP * 4;
-  static constexpr int OFF_GL = ALIAS ? OFF_LT + CHUNK * LTP * 4 : OFF_RS + RS_BYTES;
+  static constexpr int OFF_LT = ALIAS ? KS_BYTES : OFF_VG + KG_BYTES;
+  static constexpr int OFF_RS = ALIAS ? 0 : OFF_LT + LT_BYTES;
+  static constexpr int OFF_GL = ALIAS ? (OFF_LT + LT_BYTES > 2 * KG_BYTES ? OFF_LT + LT_BYTES : 2 * KG_BYTES)
+                                      : OFF_RS + RS_BYTES;
   static constexpr int PREP_LDS = OFF_GL + 3 * CHUNK * 4;
-  static_assert(!ALIAS || 3 * PREP_LDS <= 160 * 1024, "three prep workgroups per CU");
+  static constexpr int PREP_WGS = ALIAS ? 4 : 2;        // workgroups per CU the launch bounds ask for
+  static_assert(!ALIAS || (KS_BYTES % 16 == 0 && RS_BYTES <= KS_BYTES), "layout");
+  static_assert(!ALIAS || PREP_WGS * PREP_LDS <= 160 * 1024, "four prep workgroups per CU");
   // per chunk-head workspace (elements).  The head-form scan (bf16, D = 128)
   // reads K itself and takes P in bf16: no K^T copy, no P remainder.
   static constexpr bool HEAD = sizeof(T) == 2 && D == 128;
