@@ -969,7 +969,8 @@ def summarize_profiles(d):
                          f"tokens/s)" + (f" and {bench_line['decode']['ms_per_step']} ms per decode step"
                                           if "decode" in bench_line else "") + " in the traced run.")
         for k, v in bench_line.get("configs", {}).items():
-            lines.append(f"bench.py reported for `{k}`: {v.get('ms_per_step')} ms per step ({v.get('value'):.0f} "
+            ms = v.get("ms_per_step", v.get("ms_per_call_median"))
+            lines.append(f"bench.py reported for `{k}`: {ms} ms per step ({v.get('value'):.0f} "
                          f"tokens/s) in the traced run.")
         lines += ["bench.py first runs each step untimed for 0.3 s (clock settle), so the dispatch counts include "
                   "those steps.", "",
