@@ -232,9 +232,10 @@ natsl_status natsl_softmax_masked_backward(const natsl_dims* dims, const void* q
  *                  state after chunk c written S_start + h (S_end - S_start)):
  *                  <d loss / d carried state after c, S_end - S_start>
  *   ws             workspace of natsl_workspace_size(NATSL_ENTRY_GDN_BACKWARD):
- *                  the chunk preps, and every chunk's S0, U and Gc in the io
- *                  dtype (about 1.35 GB for B = 1, H = 16, L = 32768, D = 128
- *                  bf16)
+ *                  every chunk's S0 and U in the io dtype, then one region
+ *                  used in turn by the forward chunk prep and by the backward
+ *                  prep's output plus every chunk's Gc (about 0.88 GB for
+ *                  B = 1, H = 16, L = 32768, D = 128 bf16)
  * Every output is written, not accumulated; results are deterministic.  The
  * matrix products take io-dtype operands (bf16 for bf16 io) with fp32
  * accumulation.  The bf16 D = 128 form has natsl_gdn_chunk's sequence-length
