@@ -580,6 +580,16 @@ constexpr int SCH_ROUTE = 2 * SCH_STAGE;
 constexpr int SCH_MAX_NC = (LDS_MAX_BYTES - SCH_ROUTE) & ~15;
 constexpr int SCH_NW = 4;              // waves per workgroup
 constexpr int SCH_NSPLIT = 2;          // workgroups per head
+// One workgroup of eight waves per head (for many heads, where two
+// workgroups per head would hold most of the GPU): its 32 KiB of U~ columns
+// would not fit in both stages, so the stages hold no U~ and one U~ buffer
+// follows them, refilled for the next chunk once every wave has read its
+// columns.
+constexpr int SCH1_NW = 8;
+constexpr int SCH1_GM = SCH_UT;        // the decays right after K
+constexpr int SCH1_STAGE = SCH1_GM + 576;
+constexpr int SCH1_UT = 2 * SCH1_STAGE;
+static_assert(SCH1_UT + 32768 <= SCH_ROUTE, "the one-workgroup layout ends before the route bytes");
 // (every wave reads all 64 KiB of shared operands from LDS per chunk, so LDS
 // traffic per CU grows with the waves per workgroup: two workgroups of four
 // waves per head halve it against one of eight, at the price of loading the
@@ -613,6 +623,10 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW)
   constexpr int NV = D / (16 * NW * NSPLIT);  // 16-column state tiles per wave
   static_assert(NV >= 1 && NW >= 4, "the Q swizzle assumes 4 KiB-aligned load groups");
   constexpr int NB = 16 / NW;        // 1 KiB blocks of each 16 KiB operand per wave
+  constexpr bool UT1 = NSPLIT == 1;  // one U~ buffer after the stages (see SCH1_*)
+  constexpr int STAGE = UT1 ? SCH1_STAGE : SCH_STAGE;
+  constexpr int OFF_GM = UT1 ? SCH1_GM : SCH_GM;
+  static_assert(!UT1 || 4 * NV * NW * 1024 == 32768, "one U~ buffer of 32 KiB");
   using C = GdnCfg<bf16, D>;
   extern __shared__ __align__(16) unsigned char lds[];
   unsigned char* rl = lds + SCH_ROUTE;  // one route byte per chunk
@@ -670,20 +684,21 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW)
   const int qr = 4 * w + (lane >> 4);
   const uint32_t off_q = (uint32_t)(w * 1024 + (lane >> 4) * 256 + (((lane & 15) ^ (qr & 15)) * 16));
   const uint32_t off_k = (uint32_t)(w * 1024 + (lane >> 4) * 256 + (((lane & 15) ^ ((qr & 7) << 1)) * 16));
-  constexpr int GMW = 36 / NW;  // 16-byte pieces of the 576 decay bytes per wave
-  static_assert(36 % NW == 0, "decays split evenly over the waves");
+  constexpr int GMW = (36 + NW - 1) / NW;  // 16-byte pieces of the 576 decay bytes per wave (fewer for the last)
+  static_assert((NW - 1) * GMW < 36, "every wave loads a piece of the decays (one DMA operation each)");
   // op 0: -W, 1: Q, 2: P (8 KiB) and the decays, 3: K, 4: this
   // workgroup's U~ columns ([rt][16-column tile] blocks)
   auto load_part = [&](int cc, int st, int op) {
     const int64_t ch = bh * nc + cc;
-    unsigned char* sb = lds + opaque_sgpr(st * SCH_STAGE);
+    unsigned char* sb = lds + opaque_sgpr(st * STAGE);
     if (op == 4) {
       const unsigned char* ub = reinterpret_cast<const unsigned char*>(ws.ut + ch * 4 * C::NT * 256);
 #pragma unroll
       for (int i = 0; i < 4 * NV; ++i) {
         const int j = NW * i + w;  // block: row tile j / (NV NW), local column tile j % (NV NW)
         const int rt = j / (NV * NW), tl = j % (NV * NW);
-        gload_lds16_s(ub + (rt * C::NT + NV * NW * part + tl) * 1024, (uint32_t)(lane * 16), sb + SCH_UT + j * 1024);
+        gload_lds16_s(ub + (rt * C::NT + NV * NW * part + tl) * 1024, (uint32_t)(lane * 16),
+                      (UT1 ? lds + SCH1_UT : sb + SCH_UT) + j * 1024);
       }
       return;
     }
@@ -709,9 +724,9 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW)
 #pragma unroll
     for (int i = 0; i < NB; ++i)
       if (i < nb) gload_lds16_s(src + i * NW * 1024, off, sb + dst + (NW * i + w) * 1024);
-    if (op == 2 && lane < GMW)  // 576 bytes of decays, a share per wave
+    if (op == 2 && lane < GMW && w * GMW + lane < 36)  // 576 bytes of decays, a share per wave
       gload_lds16_s(reinterpret_cast<const unsigned char*>(ws.gm + ch * C::GM) + w * GMW * 16, (uint32_t)(lane * 16),
-                    sb + SCH_GM + w * GMW * 16);
+                    sb + OFF_GM + w * GMW * 16);
   };
   // DMA operations a wave issues per part
   constexpr int N_W = NB, N_Q = NB, N_U = 4 * NV, N_P = NB / 2 + 1, N_KT = NB;
@@ -804,18 +819,24 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW)
   auto step = [&](int cc, int st, f32x4 (&o)[4][NV], f32x4 (&o_prev)[4][NV]) {
     wait_vmcnt<N_KT>();  // all of chunk cc's operands but K^T (and older stores) are in
     lds_barrier();       // ... for every wave; every wave is done with chunk cc - 1
-    const unsigned char* sb = lds + opaque_sgpr(st * SCH_STAGE);
+    const unsigned char* sb = lds + opaque_sgpr(st * STAGE);
+    const unsigned char* ub = UT1 ? lds + SCH1_UT : sb + SCH_UT;
     f32x4 u[4][NV];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
       for (int nn = 0; nn < NV; ++nn)
-        u[rt][nn] = *reinterpret_cast<const f32x4*>(sb + SCH_UT + ((rt * NV * NW + NV * w + nn) * 64 + lane) * 16);
+        u[rt][nn] = *reinterpret_cast<const f32x4*>(ub + ((rt * NV * NW + NV * w + nn) * 64 + lane) * 16);
+    const bool more = cc + 1 < nc;
+    if constexpr (UT1) lds_barrier();  // every wave holds its U~ columns: the one buffer may be refilled
     if (cc > 0) store_o(cc - 1, o_prev);  // outputs of chunk cc - 1 (state mode: its U)
     if constexpr (ST) store_state(cc);
-    const bool more = cc + 1 < nc;
+    // (one buffer: chunk cc + 1's U~ goes first, after the stores, so that the
+    // K^T wait below, which counts the operand loads issued after K^T but not
+    // the stores, leaves it in flight)
+    if (UT1 && more) load_part(cc + 1, st ^ 1, 4);
     if (more) load_part(cc + 1, st ^ 1, 0);
-    const float* gm = reinterpret_cast<const float*>(sb + SCH_GM);
+    const float* gm = reinterpret_cast<const float*>(sb + OFF_GM);
     const bool lin = rl[cc] == 1;
 
     // state B operand, contraction over d
@@ -842,7 +863,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW)
       if (s_ + 2 < 16) read_wq(sb, s_ + 2, fw[(s_ + 2) % 3], fq[(s_ + 2) % 3]);
       if (s_ == 13) read_p(sb, 0, fp[0]);
       if (more && s_ == 3) load_part(cc + 1, st ^ 1, 1);
-      if (more && s_ == 7) load_part(cc + 1, st ^ 1, 4);
+      if (!UT1 && more && s_ == 7) load_part(cc + 1, st ^ 1, 4);
       if (more && s_ == 11) load_part(cc + 1, st ^ 1, 2);
       fence();
 #pragma unroll
@@ -972,8 +993,16 @@ hipError_t launch_gdn(const T* q, const T* k, const T* v, const float* alpha, co
   if (nc > gdn_max_chunks(sizeof(T) == 2, D)) return hipErrorInvalidValue;
   hipError_t e = set_lds_limit((const void*)k_gdn_prep<T, D>, C::PREP_LDS);
   if (e != hipSuccess) return e;
+  // the head-form scan: two workgroups per head, or one of eight waves when
+  // two per head would not fit the GPU at once (256 CUs, one scan workgroup
+  // each).  The one-workgroup form is slower per chunk (every wave reads all
+  // shared operands, for half the state columns); at 64 heads it freed CUs
+  // that sped the softmax branch by 10%, but the longer scan then bounded
+  // the step (B = 4, H = 16, L = 4096: 0.424 vs 0.419 ms)
+  const bool one_wg = (int64_t)B * H >= 128;
   if constexpr (scan_head_form<T, D>()) {
-    e = set_lds_limit((const void*)k_gdn_scan_head<To, SCH_NW, SCH_NSPLIT, false>, SCH_ROUTE + SCH_MAX_NC);
+    e = one_wg ? set_lds_limit((const void*)k_gdn_scan_head<To, SCH1_NW, 1, false>, SCH_ROUTE + SCH_MAX_NC)
+               : set_lds_limit((const void*)k_gdn_scan_head<To, SCH_NW, SCH_NSPLIT, false>, SCH_ROUTE + SCH_MAX_NC);
     if (e != hipSuccess) return e;
   }
   const int64_t nch = (int64_t)B * H * nc;
@@ -997,9 +1026,14 @@ hipError_t launch_gdn(const T* q, const T* k, const T* v, const float* alpha, co
   if (prof) prof(KID_GDN_SCAN, st_scan, 0);
   if constexpr (scan_head_form<T, D>()) {
     const size_t lds = SCH_ROUTE + ((size_t)nc + 15) / 16 * 16;
-    hipLaunchKernelGGL((k_gdn_scan_head<To, SCH_NW, SCH_NSPLIT, false>), dim3((unsigned)(B * H * SCH_NSPLIT)),
-                       dim3(64 * SCH_NW), lds, st_scan, (const bf16*)q, (const bf16*)k, route, ws, S_init, o_gdn,
-                       S_final, (bf16*)nullptr, H, L, G);
+    if (one_wg)
+      hipLaunchKernelGGL((k_gdn_scan_head<To, SCH1_NW, 1, false>), dim3((unsigned)(B * H)), dim3(64 * SCH1_NW), lds,
+                         st_scan, (const bf16*)q, (const bf16*)k, route, ws, S_init, o_gdn, S_final, (bf16*)nullptr,
+                         H, L, G);
+    else
+      hipLaunchKernelGGL((k_gdn_scan_head<To, SCH_NW, SCH_NSPLIT, false>), dim3((unsigned)(B * H * SCH_NSPLIT)),
+                         dim3(64 * SCH_NW), lds, st_scan, (const bf16*)q, (const bf16*)k, route, ws, S_init, o_gdn,
+                         S_final, (bf16*)nullptr, H, L, G);
   } else {
     hipLaunchKernelGGL((k_gdn_scan<T, To, D, DVT, SCAN_NS, false>), dim3((unsigned)(B * H * (D / DVT))), dim3(256),
                        0, st_scan, q, route, ws, S_init, o_gdn, S_final, (T*)nullptr, H, L, G);

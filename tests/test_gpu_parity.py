@@ -142,6 +142,35 @@ def test_gdn_chunk_parity(io, D, L, alpha):
     assert es <= (1e-4 if io == "f32" else 3e-2)
 
 
+@pytest.mark.parametrize("per_head", [False, True])
+def test_gdn_chunk_many_heads(per_head):
+    """B * H = 128 heads: the bf16 D = 128 scan then runs one workgroup of
+    eight waves per head (its U~ through one LDS buffer) instead of two of
+    four.  Five chunks (an odd count), slow decay and an initial state; with
+    per-head routes every head commits a different chunk set."""
+    B, H, L, D = 8, 16, 320, 128
+    wl, inp = small_case("bf16", B=B, H=H, L=L, D=D, alpha=(0.995, 1.0), seed=14)
+    nc = L // 64
+    rng = np.random.default_rng(5)
+    if per_head:
+        r = (rng.random((B, H, nc)) < 0.5).astype(np.int32)
+    else:
+        r = np.broadcast_to(inp["plan"], (B, 1, nc)).copy()
+    G = H if per_head else 1
+    say(f"[gdn many heads] B={B} H={H} L={L} per_head={per_head}")
+    S0 = (rng.standard_normal((B, H, D, D)) / np.sqrt(D)).astype(np.float32)
+    dm = N.dims(B, H, L, D, wl.d, io_code(inp), groups=G)
+    o, Sf = N.gdn_chunk(dm, dev(inp["q"], "bf16"), dev(inp["k"], "bf16"), dev(inp["v"], "bf16"), dev(inp["alpha"]),
+                        dev(inp["beta"]), dev(r), S_init=dev(S0))
+    torch.cuda.synchronize()
+    ref, Sref = O.gdn_branch(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], r, S_init=S0)
+    e = maxerr(rmsn(host(o)), rmsn(ref))
+    es = maxerr(host(Sf), Sref) / max(1.0, np.abs(Sref).max())
+    say(f"  n_lin err {e:.3e}  S_final rel {es:.3e}")
+    assert e <= TOL_BF16
+    assert es <= 3e-2
+
+
 @pytest.mark.parametrize("io,branch,D", [("f32", "f32", 64), ("bf16", "bf16", 128), ("bf16", "f32", 128),
                                          ("f32", "bf16", 128)])
 def test_merge_parity(io, branch, D):
