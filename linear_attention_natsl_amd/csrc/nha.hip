@@ -14,7 +14,7 @@
 // With w = 64 nw, the queries of chunk c take their evictions from chunk
 // e = c - nw: query 64 c + j sees the slots after tokens 64 e .. 64 e + j have
 // entered.  Four launches:
-//   window attention  the generic softmax kernel in window mode (o_w, lse_w);
+//   window attention  the softmax kernel in window mode (o_w, lse_w);
 //   k_nha_chunk       per chunk e: the slots' change over its 64 tokens,
 //                     dK[i] = sum_s a(s..63] (1 - a_s) k_s (and dV), and the
 //                     chunk's decay G[i] = prod_s a_s[i];
@@ -178,31 +178,34 @@ struct NhaSlotCfg {
   static constexpr int KGB = 16 * RL * 4 * (int)sizeof(T);         // key groups of 64 rows
   static constexpr int KGBM = (MP / 4) * RL * 4 * (int)sizeof(T);  // key groups of MP rows
   static constexpr bool SPLIT = sizeof(T) == 2;
-  // region 0: Q rows, [K~_e hi; K_e] rows, K~_e lo rows (scores); then the
-  // key groups of V_e and of V~_e hi / lo (read-out)
-  static constexpr int R0A = (CHUNK + M + CHUNK + (SPLIT ? M : 0)) * P * (int)sizeof(T);
-  static constexpr int R0B = KGB + KGBM * (SPLIT ? 2 : 1);
-  static constexpr int R0 = ((R0A > R0B ? R0A : R0B) + 15) & ~15;
-  static constexpr int OFF_A = R0;                        // fp32 [64][M] gates of chunk e
-  static constexpr int OFF_XS = OFF_A + CHUNK * M * 4;    // fp32 [64 j][M] X's slot part, P, P * Gamma
-  static constexpr int OFF_QK = OFF_XS + CHUNK * M * 4;   // fp32 [64 s][64 j] q_j.k_s, then R [64 j][64 s]
-  static constexpr int OFF_WW = OFF_QK + CHUNK * CHUNK * 4;
+  // One region serves three phases in turn (Q stays in registers, each
+  // wave's 16 rows): (1) the score products' [K~_e hi; K_e] and K~_e lo
+  // rows; (2) fp32 [64][*] arrays: the gates of chunk e, X's slot part / P /
+  // P * Gamma, and q_j.k_s / R; (3) the read-out's key groups of V_e and of
+  // V~_e hi / lo.  So two workgroups fit in a CU.
+  static constexpr int RK = (M + CHUNK + (SPLIT ? M : 0)) * P * (int)sizeof(T);
+  static constexpr int OFF_A = 0;                       // fp32 [64][M] gates of chunk e
+  static constexpr int OFF_XS = CHUNK * M * 4;          // fp32 [64 j][M] X's slot part, P, P * Gamma
+  static constexpr int OFF_QK = 2 * CHUNK * M * 4;      // fp32 [64 s][64 j] q_j.k_s, then R [64 j][64 s]
+  static constexpr int RS = OFF_QK + CHUNK * CHUNK * 4;
+  static constexpr int RV = KGB + KGBM * (SPLIT ? 2 : 1);
+  static constexpr int R1 = RK > RS ? RK : RS;
+  static constexpr int OFF_WW = (((R1 > RV ? R1 : RV) + 15) & ~15);  // fp32 [64] the window's weights
   static constexpr int LDS = OFF_WW + CHUNK * 4;
-  static_assert(LDS <= 160 * 1024, "LDS");
+  static_assert(2 * LDS <= 160 * 1024, "two workgroups per CU");
 };
 
 template <typename T, typename To, int D, int M>
-__global__ void __launch_bounds__(256) k_nha_slots(const T* __restrict__ q, const T* __restrict__ k,
-                                                   const T* __restrict__ v, const float* __restrict__ gate,
-                                                   NhaWs ws, const float* __restrict__ o_w,
-                                                   const float* __restrict__ lse_w, To* __restrict__ out, int L,
-                                                   int nw, int ne, float scale) {
+__global__ void __launch_bounds__(256, 2) k_nha_slots(const T* __restrict__ q, const T* __restrict__ k,
+                                                      const T* __restrict__ v, const float* __restrict__ gate,
+                                                      NhaWs ws, const float* __restrict__ o_w,
+                                                      const float* __restrict__ lse_w, To* __restrict__ out, int L,
+                                                      int nw, int ne, float scale) {
   using C = NhaSlotCfg<T, D, M>;
   constexpr int P = C::P, KF = D / 32, NCT = (M + CHUNK) / 16, MS = M / 16;
   extern __shared__ __align__(16) unsigned char lds[];
-  T* Qs = reinterpret_cast<T*>(lds);
-  T* KS = Qs + CHUNK * P;       // M slot rows (hi), then chunk e's 64 key rows
-  T* KL = KS + (M + CHUNK) * P;  // M slot rows (lo)
+  T* KS = reinterpret_cast<T*>(lds);  // M slot rows (hi), then chunk e's 64 key rows
+  T* KL = KS + (M + CHUNK) * P;       // M slot rows (lo)
   T* Vg = reinterpret_cast<T*>(lds);
   T* VTh = reinterpret_cast<T*>(lds + C::KGB);
   T* VTl = reinterpret_cast<T*>(lds + C::KGB + C::KGBM);
@@ -234,26 +237,19 @@ __global__ void __launch_bounds__(256) k_nha_slots(const T* __restrict__ q, cons
   const float* Ske = ws.Sk + (bh * ne + e) * M * D;
   const float* Sve = ws.Sv + (bh * ne + e) * M * D;
 
-  // ---- staging: every load is issued before the first LDS store; the read-
-  // out's operands (V_e rows, V~_e rows) are loaded now and stored after the
-  // score products
-  constexpr int NQ = CHUNK * D / 8 / 256;          // 8-element pieces of q, k per thread
+  // ---- phase 1: the score products' rows; Q as this wave's A fragments and
+  // the gates stay in registers until the rows are dead
+  constexpr int NQ = CHUNK * D / 8 / 256;          // 8-element pieces of k per thread
   constexpr int NSK = (M * D / 8 + 255) / 256;     // 8-float pieces of K~_e per thread
   constexpr int NA = (CHUNK * M / 4 + 255) / 256;  // 4-float pieces of the gates per thread
-  constexpr int VT = (CHUNK / 4) * (D / 8);        // (key group, 8 columns) tasks of V_e
-  constexpr int ST = (C::MP / 4) * (D / 8);        // ... of V~_e (rows past M are zero)
-  static_assert(VT <= 256 && ST <= 256, "one task per thread");
-  const int vkg = tid / (D / 8), vcol = (tid % (D / 8)) * 8;
-  Frag<T> vr[4];
-  float sr[4][8];
+  Frag<T> qa[KF];
+  f32x4 av[NA];
   {
-    Frag<T> qv[NQ], kv[NQ];
+    Frag<T> kv[NQ];
     float skv[NSK][8];
-    f32x4 av[NA];
 #pragma unroll
     for (int u = 0; u < NQ; ++u) {
       const int x = tid + 256 * u, r = x / (D / 8), col = (x % (D / 8)) * 8;
-      qv[u] = load8<T>(q + (row0 + r) * D + col);
       kv[u] = load8<T>(k + (erow0 + r) * D + col);
     }
 #pragma unroll
@@ -270,36 +266,15 @@ __global__ void __launch_bounds__(256) k_nha_slots(const T* __restrict__ q, cons
       }
     }
 #pragma unroll
+    for (int ks = 0; ks < KF; ++ks) qa[ks] = load8<T>(q + (row0 + 16 * w + c) * D + 32 * ks + 8 * g);
+#pragma unroll
     for (int u = 0; u < NA; ++u) {
       const int x = tid + 256 * u;
       if (x < CHUNK * M / 4) av[u] = *reinterpret_cast<const f32x4*>(gate + erow0 * M + 4 * x);
     }
-    if (tid < VT) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) vr[i] = load8<T>(v + (erow0 + 4 * vkg + i) * D + vcol);
-    }
-    if (tid < ST) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 4 * vkg + i;
-        if (r < M) {
-          const f32x4 lo4 = *reinterpret_cast<const f32x4*>(Sve + r * D + vcol);
-          const f32x4 hi4 = *reinterpret_cast<const f32x4*>(Sve + r * D + vcol + 4);
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            sr[i][jj] = lo4[jj];
-            sr[i][4 + jj] = hi4[jj];
-          }
-        } else {
-#pragma unroll
-          for (int jj = 0; jj < 8; ++jj) sr[i][jj] = 0.f;
-        }
-      }
-    }
 #pragma unroll
     for (int u = 0; u < NQ; ++u) {
       const int x = tid + 256 * u, r = x / (D / 8), col = (x % (D / 8)) * 8;
-      store8<T>(Qs + r * P + col, qv[u]);
       store8<T>(KS + (M + r) * P + col, kv[u]);
     }
 #pragma unroll
@@ -316,11 +291,6 @@ __global__ void __launch_bounds__(256) k_nha_slots(const T* __restrict__ q, cons
         if constexpr (C::SPLIT) store8<T>(KL + r * P + col, lo);
       }
     }
-#pragma unroll
-    for (int u = 0; u < NA; ++u) {
-      const int x = tid + 256 * u;
-      if (x < CHUNK * M / 4) *reinterpret_cast<f32x4*>(A + 4 * x) = av[u];
-    }
   }
   __syncthreads();
   // ---- X = Q [K~_e; K_e]^T: wave w takes query rows 16w .. 16w+15
@@ -330,14 +300,14 @@ __global__ void __launch_bounds__(256) k_nha_slots(const T* __restrict__ q, cons
     for (int n = 0; n < NCT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KF; ++ks) {
-      const Frag<T> a = load8<T>(Qs + (16 * w + c) * P + 32 * ks + 8 * g);
 #pragma unroll
       for (int n = 0; n < NCT; ++n) {
-        mma(acc[n], a, load8<T>(KS + (16 * n + c) * P + 32 * ks + 8 * g));
+        mma(acc[n], qa[ks], load8<T>(KS + (16 * n + c) * P + 32 * ks + 8 * g));
         if constexpr (C::SPLIT)
-          if (n < MS) mma(acc[n], a, load8<T>(KL + (16 * n + c) * P + 32 * ks + 8 * g));
+          if (n < MS) mma(acc[n], qa[ks], load8<T>(KL + (16 * n + c) * P + 32 * ks + 8 * g));
       }
     }
+    __syncthreads();  // every wave is done with the rows: phase 2's arrays take the region
 #pragma unroll
     for (int n = 0; n < NCT; ++n)
 #pragma unroll
@@ -346,6 +316,11 @@ __global__ void __launch_bounds__(256) k_nha_slots(const T* __restrict__ q, cons
         if (n < MS) XS[j * M + 16 * n + c] = acc[n][i];
         else QK[(16 * (n - MS) + c) * CHUNK + j] = acc[n][i];
       }
+#pragma unroll
+    for (int u = 0; u < NA; ++u) {
+      const int x = tid + 256 * u;
+      if (x < CHUNK * M / 4) *reinterpret_cast<f32x4*>(A + 4 * x) = av[u];
+    }
   }
   __syncthreads();
   // ---- slot scores: lane group grp (M lanes, lane i = slot i) takes the
@@ -402,25 +377,34 @@ __global__ void __launch_bounds__(256) k_nha_slots(const T* __restrict__ q, cons
     }
   }
   __syncthreads();
-  // ---- read-out operands: V_e and V~_e (hi, lo) as key groups (4 rows of a
-  // column contiguous) into region 0, free since the score products
+  // the read-out's V_e and V~_e rows: loaded now (the R loop hides their
+  // latency), stored as key groups once phase 2's arrays are dead
+  constexpr int VT = (CHUNK / 4) * (D / 8);  // (key group, 8 columns) tasks of V_e
+  constexpr int ST = (C::MP / 4) * (D / 8);  // ... of V~_e (rows past M are zero)
+  static_assert(VT <= 256 && ST <= 256, "one task per thread");
+  const int vkg = tid / (D / 8), vcol = (tid % (D / 8)) * 8;
+  Frag<T> vr[4];
+  float sr[4][8];
   if (tid < VT) {
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj)
-      st4<T>(Vg + kg_index<C::RL>(vkg, vcol + jj), to_f32(frag_get<T>(vr[0], jj)), to_f32(frag_get<T>(vr[1], jj)),
-             to_f32(frag_get<T>(vr[2], jj)), to_f32(frag_get<T>(vr[3], jj)));
+    for (int i = 0; i < 4; ++i) vr[i] = load8<T>(v + (erow0 + 4 * vkg + i) * D + vcol);
   }
   if (tid < ST) {
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      float hv[4], lv[4];
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * vkg + i;
+      if (r < M) {
+        const f32x4 lo4 = *reinterpret_cast<const f32x4*>(Sve + r * D + vcol);
+        const f32x4 hi4 = *reinterpret_cast<const f32x4*>(Sve + r * D + vcol + 4);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        hv[i] = to_f32(from_f32<T>(sr[i][jj]));
-        lv[i] = sr[i][jj] - hv[i];
+        for (int jj = 0; jj < 4; ++jj) {
+          sr[i][jj] = lo4[jj];
+          sr[i][4 + jj] = hi4[jj];
+        }
+      } else {
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) sr[i][jj] = 0.f;
       }
-      st4<T>(VTh + kg_index<C::RL>(vkg, vcol + jj), hv[0], hv[1], hv[2], hv[3]);
-      if constexpr (C::SPLIT) st4<T>(VTl + kg_index<C::RL>(vkg, vcol + jj), lv[0], lv[1], lv[2], lv[3]);
     }
   }
   // R[j][s] = sum_i P[j][i] (1 - a_s[i]) prod_{s<r<=j} a_r[i]: thread (s,
@@ -465,40 +449,61 @@ __global__ void __launch_bounds__(256) k_nha_slots(const T* __restrict__ q, cons
     }
   }
   __syncthreads();
-  // ---- O = (P * Gamma) V~_e + R V_e + w_win o_w: wave w takes rows 16w ..
-  {
-    constexpr int MK = C::MP / 32;
-    Frag<T> ar[2], ap[MK];
+  // ---- O = (P * Gamma) V~_e + R V_e + w_win o_w: wave w takes rows 16w ..;
+  // its R and P * Gamma fragments go to registers before phase 3 takes the region
+  constexpr int MK = C::MP / 32;
+  Frag<T> ar[2], ap[MK];
 #pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2)
-      ar[k2] = frag_fn<T>([&](int jj) { return QK[(16 * w + c) * CHUNK + 32 * k2 + kmap_acc(g, jj)]; });
+  for (int k2 = 0; k2 < 2; ++k2)
+    ar[k2] = frag_fn<T>([&](int jj) { return QK[(16 * w + c) * CHUNK + 32 * k2 + kmap_acc(g, jj)]; });
 #pragma unroll
-    for (int kk = 0; kk < MK; ++kk)
-      ap[kk] = frag_fn<T>([&](int jj) {
-        const int i = 32 * kk + kmap_acc(g, jj);
-        return i < M ? XS[(16 * w + c) * M + i] : 0.f;
-      });
+  for (int kk = 0; kk < MK; ++kk)
+    ap[kk] = frag_fn<T>([&](int jj) {
+      const int i = 32 * kk + kmap_acc(g, jj);
+      return i < M ? XS[(16 * w + c) * M + i] : 0.f;
+    });
+  __syncthreads();
+  // V_e and V~_e (hi, lo) as key groups (4 rows of a column contiguous)
+  if (tid < VT) {
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) {
-      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int jj = 0; jj < 8; ++jj)
+      st4<T>(Vg + kg_index<C::RL>(vkg, vcol + jj), to_f32(frag_get<T>(vr[0], jj)), to_f32(frag_get<T>(vr[1], jj)),
+             to_f32(frag_get<T>(vr[2], jj)), to_f32(frag_get<T>(vr[3], jj)));
+  }
+  if (tid < ST) {
 #pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2)
-        mma(acc, ar[k2], ld4x2<T>(Vg + kg_index<C::RL>(8 * k2 + g, 16 * dt + c),
-                                      Vg + kg_index<C::RL>(8 * k2 + 4 + g, 16 * dt + c)));
-#pragma unroll
-      for (int kk = 0; kk < MK; ++kk) {
-        mma(acc, ap[kk], ld4x2<T>(VTh + kg_index<C::RL>(8 * kk + g, 16 * dt + c),
-                                      VTh + kg_index<C::RL>(8 * kk + 4 + g, 16 * dt + c)));
-        if constexpr (C::SPLIT)
-          mma(acc, ap[kk], ld4x2<T>(VTl + kg_index<C::RL>(8 * kk + g, 16 * dt + c),
-                                        VTl + kg_index<C::RL>(8 * kk + 4 + g, 16 * dt + c)));
-      }
+    for (int jj = 0; jj < 8; ++jj) {
+      float hv[4], lv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int j = 16 * w + 4 * g + i, d = 16 * dt + c;
-        const float ow = o_w ? o_w[(row0 + j) * D + d] : 0.f;
-        out[(row0 + j) * D + d] = from_f32<To>(fmaf(WW[j], ow, acc[i]));
+        hv[i] = to_f32(from_f32<T>(sr[i][jj]));
+        lv[i] = sr[i][jj] - hv[i];
       }
+      st4<T>(VTh + kg_index<C::RL>(vkg, vcol + jj), hv[0], hv[1], hv[2], hv[3]);
+      if constexpr (C::SPLIT) st4<T>(VTl + kg_index<C::RL>(vkg, vcol + jj), lv[0], lv[1], lv[2], lv[3]);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) {
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+      mma(acc, ar[k2], ld4x2<T>(Vg + kg_index<C::RL>(8 * k2 + g, 16 * dt + c),
+                                    Vg + kg_index<C::RL>(8 * k2 + 4 + g, 16 * dt + c)));
+#pragma unroll
+    for (int kk = 0; kk < MK; ++kk) {
+      mma(acc, ap[kk], ld4x2<T>(VTh + kg_index<C::RL>(8 * kk + g, 16 * dt + c),
+                                    VTh + kg_index<C::RL>(8 * kk + 4 + g, 16 * dt + c)));
+      if constexpr (C::SPLIT)
+        mma(acc, ap[kk], ld4x2<T>(VTl + kg_index<C::RL>(8 * kk + g, 16 * dt + c),
+                                      VTl + kg_index<C::RL>(8 * kk + 4 + g, 16 * dt + c)));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = 16 * w + 4 * g + i, d = 16 * dt + c;
+      const float ow = o_w ? o_w[(row0 + j) * D + d] : 0.f;
+      out[(row0 + j) * D + d] = from_f32<To>(fmaf(WW[j], ow, acc[i]));
     }
   }
 }
