@@ -22,16 +22,18 @@
 //               Q K^T on MFMA, the 64x64 unit-lower-triangular inverse T in
 //               LDS (fp32: 16x16 diagonal blocks by forward substitution, then
 //               block rows), T diag(b) V and T diag(b gamma) K on MFMA; writes
-//               -W, U~, K^T, P and the per-token decays in exactly the
-//               per-lane fragment order the scan consumes (every scan load is
-//               16 B per lane, 1 KiB contiguous per wave).  T diag(b) and
+//               -W, U~, P, the per-token decays and (except for the head form,
+//               which reads K itself) K^T in exactly the per-lane fragment
+//               order the scan consumes (every scan load is 16 B per lane,
+//               1 KiB contiguous per wave).  T diag(b) and
 //               T diag(b gamma) are split into bf16 hi + lo parts for their
 //               products, so neither is rounded to bf16 precision; P is
 //               stored as hi + lo except for the bf16 head-form scan, which
 //               takes P in bf16 like -W and U; K^T stays exact (its
 //               exp(g_C - g) scale is applied to U in fp32 by the scan).
-//   k_gdn_scan  one workgroup per (b, h, 32-column slice of Dv), sequential
-//               over chunks.  Columns of S evolve independently under the
+//   k_gdn_scan_head (bf16, D = 128) and k_gdn_scan (otherwise): the scan,
+//               sequential over chunks (see each kernel).  k_gdn_scan takes
+//               one workgroup per (b, h, 32-column slice of Dv).  Columns of S evolve independently under the
 //               delta rule, so slicing Dv needs no communication.  The fp32
 //               master state lives in registers, a bf16 copy in LDS feeds the
 //               MFMAs; the next chunk's operands are loaded while the current
