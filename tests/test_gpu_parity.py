@@ -770,6 +770,43 @@ def test_decode_groups_per_head_mix(io, D):
             assert np.array_equal(kc[b, h, :n], cache["k"][b, h, :n]), (b, h)
 
 
+def test_chunked_prefill_long_tile_list():
+    """bf16 D = 128 prefill segment over a decode cache of 4096 chunks of
+    capacity: the segment's key-tile list (the cache's chunks + its own) no
+    longer fits the fast softmax kernel's 4096-entry LDS list, so the launch
+    takes the generic kernel, which reads the chunk list from global memory.
+    Outputs match the oracle and the one-shot prefill to the bf16 tolerance,
+    routes and final state match the one-shot prefill bit for bit."""
+    B, H, L, L1, D = 1, 2, 576, 320, 128
+    cap = 4096 * 64
+    wl, inp = small_case("bf16", B=B, H=H, L=L, D=D, seed=79, sm_frac=0.5)
+    d = wl.d
+    say(f"[chunked prefill, long tile list] cap={cap}")
+    seg = lambda a, lo, hi: {k: ((val[:, lo:hi] if k == "x" else val[:, :, lo:hi])
+                                 if k in ("x", "q", "k", "v", "alpha", "beta") else val) for k, val in a.items()}
+    s1, s2 = seg(inp, 0, L1), seg(inp, L1, L)
+    full = run_forward(inp, d, B, H, L, D)
+    f1 = run_forward(s1, d, B, H, L1, D)
+    st = N.DecodeState(B, H, D, d, cap, io=torch.bfloat16)
+    t1 = prefill_tensors(s1)
+    N.decode_handoff(N.dims(B, H, L1, D, d, io_code(inp)), f1.route, t1["k"], t1["v"], f1.S_final, st)
+    dm2 = N.dims(B, H, L - L1, D, d, io_code(inp))
+    f2 = N.Forward(dm2, debug=True, want_state=True)
+    t2 = prefill_tensors(s2)
+    f2(t2["x"], t2["q"], t2["k"], t2["v"], t2["alpha"], t2["beta"], t2["w_score"], t2["w_mix"],
+       b_score=t2["b_score"], g_sm=t2["g_sm"], g_lin=t2["g_lin"], prefix=st)
+    torch.cuda.synchronize()
+    assert int(st.err.item()) == 0
+    assert torch.equal(f2.route, full.route[:, :, L1 // 64:])
+    assert torch.equal(f2.S_final, full.S_final)
+    ref = O.forward(inp["x"], inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["w_score"],
+                    inp["w_mix"], inp["b_score"], inp["g_sm"], inp["g_lin"])
+    e = maxerr(host(f2.out), ref["out"][:, :, L1:])
+    e_full = maxerr(host(f2.out), host(full.out)[:, :, L1:])
+    say(f"  segment out err vs oracle {e:.3e}, vs one-shot {e_full:.3e}")
+    assert e <= TOL_BF16 and e_full <= TOL_BF16
+
+
 @pytest.mark.parametrize("io,D,per_head", [("f32", 64, False), ("bf16", 128, False), ("bf16", 128, True)])
 def test_chunked_prefill_equals_one_shot(io, D, per_head):
     """Chunked prefill: forward over the first 320 tokens, handoff, forward
