@@ -36,6 +36,7 @@ def run(inp, B, H, L, D, window):
     ("bf16", 128, 64, 640, 256, 1.0),
     ("bf16", 128, 64, 576, 576, 1.0),  # window covers the sequence: causal attention
     ("bf16", 128, 16, 704, 64, 4.0),   # sharp attention: a misplaced key or slot shows
+    ("bf16", 128, 32, 512, 192, 2.0),  # 32 slots at bf16 D = 128, a three-chunk window
     ("bf16", 64, 32, 384, 128, 1.0),
     ("bf16", 128, 64, 448, 0, 1.0),
     ("f32", 128, 64, 320, 128, 1.0),   # the largest LDS footprint of the slot and chunk kernels
