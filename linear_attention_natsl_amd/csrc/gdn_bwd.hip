@@ -625,13 +625,24 @@ __global__ void __launch_bounds__(256, 1)
     alp[lane] = a;
   }
   if constexpr (C::FIT) {
-    constexpr int PER = 16 / (int)sizeof(T), NP = CHUNK * D / PER;
+    // a fixed trip count, so that every load is in flight before the first
+    // LDS store (one workgroup per CU: nothing else hides their latency)
+    constexpr int PER = 16 / (int)sizeof(T), NP = CHUNK * D / PER, NI = NP / 256;
+    static_assert(NP % 256 == 0, "staging loop");
     T* Ul = (T*)(lds + C::OFF_UL);
     T* Kl = (T*)(lds + C::OFF_KL);
-    for (int e = t; e < NP; e += 256) {
-      const int r = e / (D / PER), cl = (e % (D / PER)) * PER;
-      *reinterpret_cast<f32x4*>(Ul + r * PT + cl) = *reinterpret_cast<const f32x4*>(uc + r * D + cl);
-      *reinterpret_cast<f32x4*>(Kl + r * PT + cl) = *reinterpret_cast<const f32x4*>(kc + r * D + cl);
+    f32x4 us[NI], ks[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int e = t + 256 * i, r = e / (D / PER), cl = (e % (D / PER)) * PER;
+      us[i] = *reinterpret_cast<const f32x4*>(uc + r * D + cl);
+      ks[i] = *reinterpret_cast<const f32x4*>(kc + r * D + cl);
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int e = t + 256 * i, r = e / (D / PER), cl = (e % (D / PER)) * PER;
+      *reinterpret_cast<f32x4*>(Ul + r * PT + cl) = us[i];
+      *reinterpret_cast<f32x4*>(Kl + r * PT + cl) = ks[i];
     }
   }
   // S0^T and Gc^T B fragments of this wave's columns: column d = 16 (CT w +
