@@ -1065,97 +1065,175 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) k_sm_bwd_dkdv(con
   }
 }
 
-// bf16, D = 128: dQ with the key tiles streamed straight from global memory
-// into a 2-stage LDS ring (global_load_lds_dwordx4, one tile ahead); K rows
-// carry the forward's V swizzle (row reads for S^T = K Q^T, transposed reads
-// for dQ^T += K^T dS^T), V rows its K swizzle (row reads for dP^T = V dO^T).
-// The tile list sits in LDS so that its reads stay out of the vector-memory
-// counter.  Up to DQ2_LIST visible key tiles (L <= 262144).
-constexpr int DQ2_TILE = 2 * CHUNK * 128 * 2;
-constexpr int DQ2_LIST = 4096;
-constexpr int DQ2_LDS = 2 * DQ2_TILE + 4 * DQ2_LIST;
-__global__ void __launch_bounds__(256, 2)
+// bf16, D = 128: dQ on the forward kernel's layout.  8 waves own 4 query
+// chunks (waves 2m, 2m + 1: 32 queries each of chunk c0 + m); the key tiles
+// (the softmax chunks before the block, then its own chunks) stream through
+// the 4-stage direct-to-LDS ring three tiles ahead; blocks run longest-first
+// and XCD-aware.  K rows carry the V swizzle (row reads for S^T = K Q^T,
+// transposed reads for dQ^T += K^T dS^T), V rows the K swizzle (row reads for
+// dP^T = V dO^T).  The tile list sits in LDS so that its reads stay out of
+// the vector-memory counter (up to SM2_LIST tiles).  (This layout replaced
+// one workgroup of 4 waves per query chunk, 16 queries per wave and a 2-stage
+// ring: same tiles in the same order per query, bit-identical, 17% faster.)
+__global__ void __launch_bounds__(512, 1)
     k_sm_bwd_dq2(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
                  const bf16* __restrict__ d_o, const int32_t* __restrict__ sel_idx,
                  const int32_t* __restrict__ nsel_before, const float* __restrict__ lse,
                  const float* __restrict__ delta, float* __restrict__ dq, int H, int L, int G, float scale) {
   constexpr int D = 128;
   extern __shared__ __align__(16) unsigned char lds[];
-  int32_t* sel_l = reinterpret_cast<int32_t*>(lds + 2 * DQ2_TILE);
+  int32_t* sel_l = reinterpret_cast<int32_t*>(lds + SM2_STAGES * SM2_TILE_BYTES);
   const int nc = L / CHUNK;
-  const int BH = (int)(grid_dim_x() / nc);
+  const int nb = (nc + 3) / 4;
+  const int BH = (int)(grid_dim_x() / nb);
   const int p = bid_x();
-  const int qc = nc - 1 - p / BH;  // later query chunks see more keys: first
-  const int bh = p % BH;
+  int qblk, bh;
+  if ((BH & 7) == 0) {
+    const int xcd = p & 7, slot = p >> 3, hpx = BH >> 3;
+    qblk = nb - 1 - slot / hpx;
+    bh = (slot % hpx) * 8 + xcd;
+  } else {
+    qblk = nb - 1 - p / BH;
+    bh = p % BH;
+  }
   const int b = bh / H, h = bh % H;
   const int grp = (G == 1) ? 0 : h;
+  const int c0 = 4 * qblk;
+  const int nown = min(4, nc - c0);
   const int32_t* sel = sel_idx + ((int64_t)b * G + grp) * nc;
-  const int nsb = nsel_before[((int64_t)b * G + grp) * (nc + 1) + qc];
+  const int32_t* nsbp = nsel_before + ((int64_t)b * G + grp) * (nc + 1);
+  const int nsb = nsbp[c0];
+  const int ntiles = nsb + nown;
+  int sm_bits = 0;
+  for (int j = 0; j < nown; ++j) sm_bits |= (nsbp[c0 + j + 1] > nsbp[c0 + j]) ? (1 << j) : 0;
+
   const int lane = lane_id(), w = wave_id();
   const int g = lane >> 4, c = lane & 15;
+  const int mch = w >> 1;  // chunk of this wave within the block
+  const bool active = mch < nown;
   const int64_t head_off = (int64_t)bh * L * D;
-  const int64_t tok = (int64_t)qc * CHUNK + 16 * w + c;
-  Frag<bf16> qf[4], df[4];
+  const bf16* kh = k + head_off;
+  const bf16* vh = v + head_off;
+  for (int i = tid_x(); i < nsb; i += 512) sel_l[i] = sel[i];
+  for (int i = tid_x(); i < nown; i += 512) sel_l[nsb + i] = c0 + i;
+
+  Frag<bf16> qf[2][4], df[2][4];
+  float lse2[2], dlt[2];
+  const int qtok0 = (c0 + (active ? mch : 0)) * CHUNK + 32 * (w & 1);
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    qf[ks] = load8<bf16>(q + head_off + tok * D + 32 * ks + 8 * g);
-    df[ks] = load8<bf16>(d_o + head_off + tok * D + 32 * ks + 8 * g);
+  for (int qs = 0; qs < 2; ++qs) {
+    const int64_t tok = qtok0 + 16 * qs + c;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      qf[qs][ks] = load8<bf16>(q + head_off + tok * D + 32 * ks + 8 * g);
+      df[qs][ks] = load8<bf16>(d_o + head_off + tok * D + 32 * ks + 8 * g);
+    }
+    lse2[qs] = lse[(int64_t)bh * L + tok] * LOG2E;
+    dlt[qs] = delta[(int64_t)bh * L + tok];
   }
-  const float lse2 = lse[(int64_t)bh * L + tok] * LOG2E;
-  const float dlt = delta[(int64_t)bh * L + tok];
-  for (int i = tid_x(); i < nsb; i += 256) sel_l[i] = sel[i];
-  if (tid_x() == 0) sel_l[nsb] = qc;
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): nothing of ours outstanding before the ring starts
   __syncthreads();
-  const float scale_log2 = scale * LOG2E;
-  const int qrow = 16 * w + c;
-  f32x4 acc[D / 16];
-#pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int nt = nsb + 1;
+
+  // tile `it` -> stage it % STAGES: 2 K + 2 V 16-byte loads per thread
   auto issue = [&](int it) {
     const int kc = sel_l[it];
-    unsigned char* st = lds + (it & 1) * DQ2_TILE;
-    const bf16* kg = k + head_off + (int64_t)kc * CHUNK * D;
-    const bf16* vg = v + head_off + (int64_t)kc * CHUNK * D;
+    unsigned char* st = lds + (it % SM2_STAGES) * SM2_TILE_BYTES;
+    const bf16* kg = kh + (int64_t)kc * CHUNK * D;
+    const bf16* vg = vh + (int64_t)kc * CHUNK * D;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e0 = w * 256 + i * 64;
+    for (int i = 0; i < 2; ++i) {
+      const int e0 = w * 128 + i * 64;  // first 16-byte chunk of this wave instruction
       const int e = e0 + lane, r = e >> 4, sl = e & 15;
       gload_lds16(kg + r * D + sm2_vslot(r, sl) * 8, st + e0 * 16);
       gload_lds16(vg + r * D + sm2_kslot(r, sl) * 8, st + CHUNK * D * 2 + e0 * 16);
     }
   };
-  issue(0);
-  for (int it = 0; it < nt; ++it) {
-    const bool diag = it == nsb;
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // this tile's loads have landed
-    lds_barrier();                       // ... for every wave; every wave is done with tile it - 1
-    if (it + 1 < nt) issue(it + 1);
-    const unsigned char* st = lds + opaque_sgpr((it & 1) * DQ2_TILE);
+  const float scale_log2 = scale * LOG2E;
+  const int qrow_base = 32 * (w & 1);
+  f32x4 acc[D / 16][2];
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) acc[dt][qs] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < SM2_STAGES - 1; ++j)
+    if (j < ntiles) issue(j);
+  for (int it = 0; it < ntiles; ++it) {
+    wait_vm(4 * (min(it + SM2_STAGES - 2, ntiles - 1) - it));  // this tile's loads have landed
+    lds_barrier();                                              // ... for every wave
+    if (it + SM2_STAGES - 1 < ntiles) issue(it + SM2_STAGES - 1);  // into the stage read last iteration
+    int mode;
+    if (it < nsb) {
+      mode = MODE_FULL;
+    } else {
+      const int j = it - nsb;
+      mode = (j == mch) ? MODE_DIAG : (j < mch && ((sm_bits >> j) & 1)) ? MODE_FULL : MODE_SKIP;
+    }
+    if (!active) mode = MODE_SKIP;
+    if (mode == MODE_SKIP) continue;
+
+    const unsigned char* st = lds + (it % SM2_STAGES) * SM2_TILE_BYTES;
     const unsigned char* ks_l = st;
     const unsigned char* vs_l = st + CHUNK * D * 2;
-    f32x4 s_[4], dp[4];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) s_[kt] = dp[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        const int r = 16 * kt + c;
-        mma(s_[kt], *reinterpret_cast<const Frag<bf16>*>(ks_l + r * 256 + sm2_vslot(r, 4 * ks + g) * 16), qf[ks]);
-        mma(dp[kt], *reinterpret_cast<const Frag<bf16>*>(vs_l + r * 256 + sm2_kslot(r, 4 * ks + g) * 16), df[ks]);
-      }
-    // dS^T = P^T (dP^T - delta), packed as the B operand (keys in accumulator order)
-    Frag<bf16> dsf[2];
+    f32x4 s_[4][2], dp[4][2];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool vis = !diag || (16 * kt + 4 * g + i) <= qrow;
-        const float pp = vis ? __builtin_amdgcn_exp2f(fmaf(s_[kt][i], scale_log2, -lse2)) : 0.f;
-        frag_set(dsf[kt >> 1], 4 * (kt & 1) + i, pp * (dp[kt][i] - dlt));
-      }
+      for (int qs = 0; qs < 2; ++qs) s_[kt][qs] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // S^T = K Q^T, the K fragments in two halves of the contraction
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      Frag<bf16> ka[2][4];
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          const int r = 16 * kt + c, ks = 2 * hf + k;
+          ka[k][kt] = *reinterpret_cast<const Frag<bf16>*>(ks_l + r * 256 + sm2_vslot(r, 4 * ks + g) * 16);
+        }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int qs = 0; qs < 2; ++qs) mma(s_[kt][qs], ka[k][kt], qf[qs][2 * hf + k]);
+    }
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs) dp[kt][qs] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // dP^T = V dO^T, the V fragments in two halves of the contraction
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      Frag<bf16> va[2][4];
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          const int r = 16 * kt + c, ks = 2 * hf + k;
+          va[k][kt] = *reinterpret_cast<const Frag<bf16>*>(vs_l + r * 256 + sm2_kslot(r, 4 * ks + g) * 16);
+        }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int qs = 0; qs < 2; ++qs) mma(dp[kt][qs], va[k][kt], df[qs][2 * hf + k]);
+    }
+    // dS^T = P^T (dP^T - delta), packed as the B operand (keys in accumulator order)
+    Frag<bf16> dsf[2][2];
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool vis = mode != MODE_DIAG || (16 * kt + 4 * g + i) <= qrow_base + 16 * qs + c;
+          const float pp = vis ? __builtin_amdgcn_exp2f(fmaf(s_[kt][qs][i], scale_log2, -lse2[qs])) : 0.f;
+          frag_set(dsf[qs][kt >> 1], 4 * (kt & 1) + i, pp * (dp[kt][qs][i] - dlt[qs]));
+        }
     // dQ^T += K^T dS^T: K^T fragments by transposed reads (rows d = 16 dt + c,
     // keys 32 k2 + 4g + j and 32 k2 + 16 + 4g + j)
 #pragma unroll
@@ -1171,16 +1249,21 @@ __global__ void __launch_bounds__(256, 2)
             (__attribute__((address_space(3))) v4i16*)(ks_l + r1 * 256 + sm2_vslot(r1, colq) * 16 + half));
         Frag<bf16> a;
         a.v = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        mma(acc[dt], a, dsf[k2]);
+#pragma unroll
+        for (int qs = 0; qs < 2; ++qs) mma(acc[dt][qs], a, dsf[qs][k2]);
       }
     }
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // no load may still be in flight into LDS at the end
-  float* out = dq + head_off + tok * D;
+  if (!active) return;
 #pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) {
-    f32x4 r = acc[dt] * scale;
-    *reinterpret_cast<f32x4*>(out + 16 * dt + 4 * g) = r;
+  for (int qs = 0; qs < 2; ++qs) {
+    float* out = dq + head_off + (int64_t)(qtok0 + 16 * qs + c) * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      f32x4 r = acc[dt][qs] * scale;
+      *reinterpret_cast<f32x4*>(out + 16 * dt + 4 * g) = r;
+    }
   }
 }
 
@@ -1360,10 +1443,11 @@ hipError_t launch_softmax_backward(const T* q, const T* k, const T* v, const int
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t grid = (int64_t)B * H * nc;
-  if (sizeof(T) == 2 && D == 128 && nc <= DQ2_LIST) {
-    if ((e = set_lds_limit((const void*)k_sm_bwd_dq2, DQ2_LDS)) != hipSuccess) return e;
-    hipLaunchKernelGGL(k_sm_bwd_dq2, dim3((unsigned)grid), dim3(256), DQ2_LDS, st, (const bf16*)q, (const bf16*)k,
-                       (const bf16*)v, (const bf16*)d_o, sel_idx, nsel_before, lse, delta, dq, H, L, G, scale);
+  if (sizeof(T) == 2 && D == 128 && nc <= SM2_LIST) {
+    if ((e = set_lds_limit((const void*)k_sm_bwd_dq2, SM2_LDS)) != hipSuccess) return e;
+    hipLaunchKernelGGL(k_sm_bwd_dq2, dim3((unsigned)((int64_t)B * H * ((nc + 3) / 4))), dim3(512), SM2_LDS, st,
+                       (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)d_o, sel_idx, nsel_before, lse,
+                       delta, dq, H, L, G, scale);
   } else {
     hipLaunchKernelGGL((k_sm_bwd_dq<T, D>), dim3((unsigned)grid), dim3(256), LDS_DQ, st, q, k, v, d_o, sel_idx,
                        nsel_before, lse, delta, dq, H, L, G, scale);
