@@ -451,15 +451,18 @@ def test_decode_steps_match_oracle(io, D):
     assert int(st.err.item()) == 0
 
 
-@pytest.mark.parametrize("io,D,L,q_scale,per_head", [("f32", 64, 256, 1.0, False), ("f32", 128, 320, 1.0, False),
-                                                      ("bf16", 128, 640, 1.0, False), ("bf16", 128, 576, 8.0, False),
-                                                      ("bf16", 64, 448, 1.0, True)])
-def test_softmax_backward_parity(io, D, L, q_scale, per_head):
+@pytest.mark.parametrize("io,D,L,q_scale,per_head,H", [("f32", 64, 256, 1.0, False, 2), ("f32", 128, 320, 1.0, False, 2),
+                                                        ("bf16", 128, 640, 1.0, False, 2),
+                                                        ("bf16", 128, 576, 8.0, False, 2),
+                                                        ("bf16", 64, 448, 1.0, True, 2),
+                                                        ("bf16", 128, 448, 2.0, True, 4)])
+def test_softmax_backward_parity(io, D, L, q_scale, per_head, H):
     """Gradient of the softmax branch against the oracle's derivative, from
     the GPU forward's o and lse; the error is taken relative to each
     gradient's largest magnitude (bf16: P and dS are rounded to bf16 for the
-    matrix cores, and o is the bf16 forward output)."""
-    B, H = 2, 2
+    matrix cores, and o is the bf16 forward output).  B * H = 8 takes the
+    kernels' XCD-aware block order; 7 chunks leave a ragged last block of 4."""
+    B = 2
     wl, inp = small_case(io, B=B, H=H, L=L, D=D, q_scale=q_scale, seed=81)
     G = H if per_head else 1
     nc = L // 64
