@@ -170,6 +170,42 @@ __global__ void __launch_bounds__(256) k_nha_scan(NhaWs ws, int BH, int ne) {
 //   O = (P * Gamma) V~_e + R V_e + w_win o_w                    (matrix cores)
 // R and Gamma come from running products (gates of exactly 0 or 1 stay exact).
 // The slot states (fp32) enter the bf16 products as hi + lo parts.
+// max / sum over aligned groups of M = 16, 32 or 64 lanes, in registers:
+// the 16-lane rows by DPP (quad swaps, then the half-row and row mirrors),
+// then the gfx950 row swaps (permlane16: rows 0-1 and 2-3; permlane32: rows
+// 0-2 and 1-3); the result is in every lane of the group
+template <int M>
+__device__ __forceinline__ float lane_group_max(float x) {
+  static_assert(M == 16 || M == 32 || M == 64, "groups of 16, 32 or 64 lanes");
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true)));   // quad_perm 1,0,3,2
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true)));   // quad_perm 2,3,0,1
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, true)));  // row_half_mirror
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, true)));  // row_mirror
+  if constexpr (M >= 32) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+  if constexpr (M == 64) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+  return x;
+}
+template <int M>
+__device__ __forceinline__ float lane_group_sum(float x) {
+  static_assert(M == 16 || M == 32 || M == 64, "groups of 16, 32 or 64 lanes");
+  x = dpp_group_sum<16>(x);
+  if constexpr (M >= 32) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  if constexpr (M == 64) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  return x;
+}
+
 template <typename T, int D, int M>
 struct NhaSlotCfg {
   static constexpr int MP = M < 32 ? 32 : M;        // slots padded to the 32-deep contraction
@@ -336,6 +372,7 @@ __global__ void __launch_bounds__(256, 2) k_nha_slots(const T* __restrict__ q, c
     float y[JPG], z[JPG];
 #pragma unroll
     for (int u = 0; u < JPG; ++u) y[u] = XS[(jb + u) * M + i];
+#pragma unroll 4
     for (int st = 0; st < jb; ++st) {  // tokens before the group's first query: every query takes them
       const float a = A[st * M + i], b = 1.f - a;
       const float* qk = QK + st * CHUNK + jb;
@@ -361,14 +398,9 @@ __global__ void __launch_bounds__(256, 2) k_nha_slots(const T* __restrict__ q, c
       const int j = jb + u;
       const float zz = scale * z[u];
       const float lw = lse_w ? lse_w[row0 + j] : -INFINITY;
-      float mx = zz;
-#pragma unroll
-      for (int msk = M / 2; msk >= 1; msk >>= 1) mx = fmaxf(mx, __shfl_xor(mx, msk, 64));
-      mx = fmaxf(mx, lw);
+      const float mx = fmaxf(lane_group_max<M>(zz), lw);
       const float p = __expf(zz - mx);
-      float den = p;
-#pragma unroll
-      for (int msk = M / 2; msk >= 1; msk >>= 1) den += __shfl_xor(den, msk, 64);
+      float den = lane_group_sum<M>(p);
       const float pw = __expf(lw - mx);  // 0 for an empty window
       den += pw;
       const float inv = 1.f / den;
@@ -417,7 +449,12 @@ __global__ void __launch_bounds__(256, 2) k_nha_slots(const T* __restrict__ q, c
     float cw[SPQ];
 #pragma unroll
     for (int u = 0; u < SPQ; ++u) cw[u] = 1.f - A[s * M + i0 + u];
-    for (int j = 0; j < CHUNK; ++j) {
+    // R[j][s] = 0 for j < s: wave w (tokens 16w .. 16w + 15) starts at j = 16w
+    const int j0 = 16 * w;
+    if (part == 0)
+      for (int j = 0; j < j0; ++j) QK[j * CHUNK + s] = 0.f;
+#pragma unroll 4
+    for (int j = j0; j < CHUNK; ++j) {
       // branch-free (a guarded multiply became one exec-masked branch and
       // one LDS round trip per slot); four partial sums for the dot product
       const bool later = j > s;
