@@ -1267,17 +1267,22 @@ __global__ void __launch_bounds__(512, 1)
   }
 }
 
-// bf16, D = 128: the same products with Q and dO streamed straight from
-// global memory into an NSTG-stage LDS ring (global_load_lds_dwordx4, one
-// tile ahead), rows stored with the forward's V swizzle (chunk q of row r at
-// slot q ^ ((r & 7) << 1)): row reads give the A operands of S = Q K^T and
+// bf16, D = 128: dK and dV with one workgroup of 2 waves per key chunk, 32
+// keys per wave (two 16-key sub-tiles, so every Q or dO fragment read from
+// LDS feeds two products; one wave per SIMD with 512 registers, two
+// workgroups per CU), the query chunks' Q and dO streamed straight from
+// global memory into a 2-stage LDS ring (global_load_lds_dwordx4, one tile
+// ahead), rows stored with the forward's V swizzle (chunk q of row r at slot
+// q ^ ((r & 7) << 1)): row reads give the A operands of S = Q K^T and
 // dP = dO V^T, transposed reads (ds_read_b64_tr_b16) the A operands of
 // dV^T += dO^T P and dK^T += Q^T dS.  One barrier per query chunk, no
 // register staging; lse and delta of the chunk ride in the same ring.
+// (4 waves of 16 keys each, two per SIMD, read twice the LDS per product and
+// were 3% slower for the whole gradient; the per-key arithmetic is the same.)
 constexpr int DK2_STAGES = 2;
-constexpr int DK2_TILE = 2 * CHUNK * 128 * 2 + 1024;  // Q, dO rows; lse, delta (+ two scratch slots)
+constexpr int DK2_TILE = 2 * CHUNK * 128 * 2 + 1024;  // Q, dO rows; lse, delta (+ two spare slots)
 constexpr int DK2_LDS = DK2_STAGES * DK2_TILE + 16;
-__global__ void __launch_bounds__(256, 2)
+__global__ void __launch_bounds__(128, 1)
     k_sm_bwd_dkdv2(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
                    const bf16* __restrict__ d_o, const int32_t* __restrict__ nsel_before,
                    const float* __restrict__ lse, const float* __restrict__ delta, float* __restrict__ dk,
@@ -1300,31 +1305,34 @@ __global__ void __launch_bounds__(256, 2)
   const int lane = lane_id(), w = wave_id();
   const int g = lane >> 4, c = lane & 15;
   const int64_t head_off = (int64_t)bh * L * D;
-  const int64_t key = (int64_t)kc * CHUNK + 16 * w + c;
-  Frag<bf16> kf[4], vf[4];
+  // wave w owns keys 32 w .. 32 w + 31 of the chunk, as two 16-key sub-tiles kq
+  Frag<bf16> kf[2][4], vf[2][4];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    kf[ks] = load8<bf16>(k + head_off + key * D + 32 * ks + 8 * g);
-    vf[ks] = load8<bf16>(v + head_off + key * D + 32 * ks + 8 * g);
-  }
+  for (int kq = 0; kq < 2; ++kq)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int64_t key = (int64_t)kc * CHUNK + 32 * w + 16 * kq + c;
+      kf[kq][ks] = load8<bf16>(k + head_off + key * D + 32 * ks + 8 * g);
+      vf[kq][ks] = load8<bf16>(v + head_off + key * D + 32 * ks + 8 * g);
+    }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): nothing of ours outstanding before the ring starts
   const float scale_log2 = scale * LOG2E;
-  const int kcol = 16 * w + c;
-  f32x4 adk[D / 16], adv[D / 16];
+  f32x4 adk[2][D / 16], adv[2][D / 16];
 #pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) adk[dt] = adv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int kq = 0; kq < 2; ++kq)
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) adk[kq][dt] = adv[kq][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // tile j (query chunk kc + j) -> stage j % DK2_STAGES: per wave 4 + 4
-  // row-block loads and one 256-byte vector load (waves 0 / 1: lse / delta,
-  // waves 2 / 3 the same into scratch slots, so every wave counts 9 loads)
+  // tile j (query chunk kc + j) -> stage j % DK2_STAGES: per wave 8 + 8
+  // row-block loads and one 256-byte vector load (wave 0: lse, wave 1: delta)
   auto issue = [&](int j) {
     const int qcx = kc + j;
     unsigned char* st = lds + (j % DK2_STAGES) * DK2_TILE;
     const bf16* qg = q + head_off + (int64_t)qcx * CHUNK * D;
     const bf16* dg = d_o + head_off + (int64_t)qcx * CHUNK * D;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e0 = w * 256 + i * 64;
+    for (int i = 0; i < 8; ++i) {
+      const int e0 = w * 512 + i * 64;
       const int e = e0 + lane, r = e >> 4, sl = e & 15;
       gload_lds16(qg + r * D + sm2_vslot(r, sl) * 8, st + e0 * 16);
       gload_lds16(dg + r * D + sm2_vslot(r, sl) * 8, st + CHUNK * D * 2 + e0 * 16);
@@ -1345,38 +1353,48 @@ __global__ void __launch_bounds__(256, 2)
     const unsigned char* ds_l = st + CHUNK * D * 2;
     const float* lse_s = reinterpret_cast<const float*>(st + 2 * CHUNK * D * 2);
     const float* dlt_s = lse_s + CHUNK;
-    f32x4 pm[4], dsm[4];
+    f32x4 pm[2][4], dsm[2][4];
 #pragma unroll
     for (int qt = 0; qt < 4; ++qt) {
-      f32x4 s_ = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+      f32x4 s_[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      f32x4 dp[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
       const int r = 16 * qt + c;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const int off = r * 256 + sm2_vslot(r, 4 * ks + g) * 16;
-        mma(s_, *reinterpret_cast<const Frag<bf16>*>(qs_l + off), kf[ks]);
-        mma(dp, *reinterpret_cast<const Frag<bf16>*>(ds_l + off), vf[ks]);
+        const Frag<bf16> aq = *reinterpret_cast<const Frag<bf16>*>(qs_l + off);
+        const Frag<bf16> ad = *reinterpret_cast<const Frag<bf16>*>(ds_l + off);
+#pragma unroll
+        for (int kq = 0; kq < 2; ++kq) {
+          mma(s_[kq], aq, kf[kq][ks]);
+          mma(dp[kq], ad, vf[kq][ks]);
+        }
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int qrow = 16 * qt + 4 * g + i;
-        const bool vis = !diag || kcol <= qrow;
-        const float pp = vis ? __builtin_amdgcn_exp2f(fmaf(s_[i], scale_log2, -lse_s[qrow] * LOG2E)) : 0.f;
-        pm[qt][i] = pp;
-        dsm[qt][i] = pp * (dp[i] - dlt_s[qrow]);
-        if (!diag) gsum += dsm[qt][i];
-      }
+      for (int kq = 0; kq < 2; ++kq)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int qrow = 16 * qt + 4 * g + i;
+          const bool vis = !diag || 32 * w + 16 * kq + c <= qrow;
+          const float pp = vis ? __builtin_amdgcn_exp2f(fmaf(s_[kq][i], scale_log2, -lse_s[qrow] * LOG2E)) : 0.f;
+          pm[kq][qt][i] = pp;
+          dsm[kq][qt][i] = pp * (dp[kq][i] - dlt_s[qrow]);
+          if (!diag) gsum += dsm[kq][qt][i];
+        }
     }
     if (!diag && !kc_sm) continue;  // only the gate's sum: these keys are not visible in the forward
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
-      Frag<bf16> pf, dsf;
+      Frag<bf16> pf[2], dsf[2];
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        frag_set(pf, jj, pm[2 * k2][jj]);
-        frag_set(pf, 4 + jj, pm[2 * k2 + 1][jj]);
-        frag_set(dsf, jj, dsm[2 * k2][jj]);
-        frag_set(dsf, 4 + jj, dsm[2 * k2 + 1][jj]);
-      }
+      for (int kq = 0; kq < 2; ++kq)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          frag_set(pf[kq], jj, pm[kq][2 * k2][jj]);
+          frag_set(pf[kq], 4 + jj, pm[kq][2 * k2 + 1][jj]);
+          frag_set(dsf[kq], jj, dsm[kq][2 * k2][jj]);
+          frag_set(dsf[kq], 4 + jj, dsm[kq][2 * k2 + 1][jj]);
+        }
       // dO^T and Q^T fragments (rows d = 16 dt + c, queries 32 k2 + 4g + j
       // and 32 k2 + 16 + 4g + j) by transposed reads: lane c of group g reads
       // row 32 k2 + 4g + c / 4 (+16), columns 16 dt + 4 (c % 4) .. +3
@@ -1397,25 +1415,32 @@ __global__ void __launch_bounds__(256, 2)
           const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(qs_l + o1));
           aq.v = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         }
-        mma(adv[dt], ad, pf);
-        mma(adk[dt], aq, dsf);
+#pragma unroll
+        for (int kq = 0; kq < 2; ++kq) {
+          mma(adv[kq][dt], ad, pf[kq]);
+          mma(adk[kq][dt], aq, dsf[kq]);
+        }
       }
     }
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // no load may still be in flight into LDS at the end
-  float* okr = dk + head_off + key * D;
-  float* ovr = dv + head_off + key * D;
 #pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) {
-    f32x4 r = adk[dt] * scale;
-    *reinterpret_cast<f32x4*>(okr + 16 * dt + 4 * g) = r;
-    *reinterpret_cast<f32x4*>(ovr + 16 * dt + 4 * g) = adv[dt];
+  for (int kq = 0; kq < 2; ++kq) {
+    const int64_t key = (int64_t)kc * CHUNK + 32 * w + 16 * kq + c;
+    float* okr = dk + head_off + key * D;
+    float* ovr = dv + head_off + key * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      f32x4 r = adk[kq][dt] * scale;
+      *reinterpret_cast<f32x4*>(okr + 16 * dt + 4 * g) = r;
+      *reinterpret_cast<f32x4*>(ovr + 16 * dt + 4 * g) = adv[kq][dt];
+    }
   }
-  if (dgate) {  // the wave sums, then the 4 waves in order (deterministic)
+  if (dgate) {  // the wave sums, then the 2 waves in order (deterministic)
     gsum = wave_sum64(gsum);
     if (lane == 0) red[w] = gsum;
     __syncthreads();
-    if (tid_x() == 0) dgate[(int64_t)bh * nc + kc] = (red[0] + red[1]) + (red[2] + red[3]);
+    if (tid_x() == 0) dgate[(int64_t)bh * nc + kc] = red[0] + red[1];
   }
 }
 
@@ -1455,7 +1480,7 @@ hipError_t launch_softmax_backward(const T* q, const T* k, const T* v, const int
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if constexpr (sizeof(T) == 2 && D == 128) {
     if ((e = set_lds_limit((const void*)k_sm_bwd_dkdv2, DK2_LDS)) != hipSuccess) return e;
-    hipLaunchKernelGGL(k_sm_bwd_dkdv2, dim3((unsigned)grid), dim3(256), DK2_LDS, st, (const bf16*)q, (const bf16*)k,
+    hipLaunchKernelGGL(k_sm_bwd_dkdv2, dim3((unsigned)grid), dim3(128), DK2_LDS, st, (const bf16*)q, (const bf16*)k,
                        (const bf16*)v, (const bf16*)d_o, nsel_before, lse, delta, dk, dv, H, L, G, scale, dgate);
   } else {
     hipLaunchKernelGGL((k_sm_bwd_dkdv<T, D>), dim3((unsigned)grid), dim3(256), LDS_DKDV, st, q, k, v, d_o,
