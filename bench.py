@@ -254,25 +254,36 @@ def time_gdn_backward(N, dm, t, wl, route, reps=3):
     (K Gc, P^T dO, Q^T dO, W^T dU) and the chunk gradients (A, P, dP, dO S0^T,
     U Gc^T, TdU S0^T, T^T dU, A U, dT, T^T dT T^T, E K, E^T K, F K, F^T Q).
     Two of its five launches are sequential over the 512 chunks, so it is
-    latency-bound, not set against a roofline."""
+    latency-bound, not set against a roofline.  Timed in both workspace
+    layouts: the default (one region shared by the two sweeps, run one after
+    the other) and the overlapping one (the sweeps at the same time on two
+    streams)."""
     import torch
     d_o = torch.randn(t["q"].shape, dtype=torch.float32, device=t["q"].device)
-    N.gdn_backward(dm, t["q"], t["k"], t["v"], t["alpha"], t["beta"], route, d_o)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        N.gdn_backward(dm, t["q"], t["k"], t["v"], t["alpha"], t["beta"], route, d_o)
-    e1.record()
-    torch.cuda.synchronize()
-    us = 1000.0 * e0.elapsed_time(e1) / reps
+
+    def timed(overlap):
+        N.gdn_backward(dm, t["q"], t["k"], t["v"], t["alpha"], t["beta"], route, d_o, overlap=overlap)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            N.gdn_backward(dm, t["q"], t["k"], t["v"], t["alpha"], t["beta"], route, d_o, overlap=overlap)
+        e1.record()
+        torch.cuda.synchronize()
+        return 1000.0 * e0.elapsed_time(e1) / reps
+
+    us, us_ov = timed(False), timed(True)
     C, D = 64, wl.D
     flops = (36 * C * C * D + 16 * C * D * D + 4 * C ** 3) * wl.B * wl.H * (wl.L // C)
     tf = flops / (us * 1e-6) / 1e12
     ws = N.workspace_size(N.ENTRY_GDN_BACKWARD, dm)
+    ws_ov = N.workspace_size(N.ENTRY_GDN_BACKWARD_OVERLAP, dm)
     return dict(workload=f"gradient of the Gated DeltaNet branch on the {wl.name} prefill (chunk form)",
                 us=round(us, 1), flops=flops, tflops=round(tf, 1), frac_bf16_mfma=round(tf / PEAK_BF16_TFLOPS, 4),
-                workspace_bytes=int(ws), note="latency-bound: two sequential sweeps over the chunks")
+                workspace_bytes=int(ws), note="latency-bound: two sequential sweeps over the chunks",
+                overlap=dict(us=round(us_ov, 1), workspace_bytes=int(ws_ov),
+                             note="the same gradient with the larger workspace layout: the state scan and the "
+                                  "reverse scan at the same time on two streams (bit-identical results)"))
 
 
 def time_merge_backward(N, dm, t, wl, reps=5):

@@ -99,7 +99,8 @@ enum {
   NATSL_ENTRY_SOFTMAX_BACKWARD = 7,
   NATSL_ENTRY_GDN_BACKWARD = 8,
   NATSL_ENTRY_MERGE_BACKWARD = 9,
-  NATSL_ENTRY_ROUTE_BACKWARD = 10
+  NATSL_ENTRY_ROUTE_BACKWARD = 10,
+  NATSL_ENTRY_GDN_BACKWARD_OVERLAP = 11  /* natsl_gdn_backward's larger, overlapping layout */
 };
 
 typedef struct {
@@ -235,7 +236,13 @@ natsl_status natsl_softmax_masked_backward(const natsl_dims* dims, const void* q
  *                  every chunk's S0 and U in the io dtype, then one region
  *                  used in turn by the forward chunk prep and by the backward
  *                  prep's output plus every chunk's Gc (about 0.88 GB for
- *                  B = 1, H = 16, L = 32768, D = 128 bf16)
+ *                  B = 1, H = 16, L = 32768, D = 128 bf16).  A workspace of at
+ *                  least natsl_workspace_size(NATSL_ENTRY_GDN_BACKWARD_OVERLAP)
+ *                  (about 1.35 GB there) gives the two uses regions of their
+ *                  own, and the call then runs the forward's state scan and
+ *                  the reverse scan at the same time on a library helper
+ *                  stream (forked from and joined back into `stream` within
+ *                  the call); the results are bit-identical either way
  * Every output is written, not accumulated; results are deterministic.  The
  * matrix products take io-dtype operands (bf16 for bf16 io) with fp32
  * accumulation.  The bf16 D = 128 form has natsl_gdn_chunk's sequence-length

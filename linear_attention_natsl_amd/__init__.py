@@ -21,7 +21,7 @@ F32, BF16 = 0, 1
 ROUTE_SOFTMAX, ROUTE_LINEAR = 0, 1
 ENTRY_ROUTE, ENTRY_GDN_CHUNK, ENTRY_SOFTMAX_MASKED, ENTRY_MERGE, ENTRY_FORWARD, ENTRY_DECODE_STEP, \
     ENTRY_DECODE_HANDOFF, ENTRY_SOFTMAX_BACKWARD, ENTRY_GDN_BACKWARD, ENTRY_MERGE_BACKWARD, \
-    ENTRY_ROUTE_BACKWARD = range(11)
+    ENTRY_ROUTE_BACKWARD, ENTRY_GDN_BACKWARD_OVERLAP = range(12)
 STATUS = {0: "NATSL_OK", 1: "NATSL_ERR_INVALID_ARG", 2: "NATSL_ERR_UNSUPPORTED",
           3: "NATSL_ERR_WORKSPACE", 4: "NATSL_ERR_DEVICE", 5: "NATSL_ERR_CAPACITY"}
 EXPORTS = ["natsl_version", "natsl_last_error", "natsl_workspace_size", "natsl_route", "natsl_gdn_chunk",
@@ -431,11 +431,13 @@ def softmax_masked_backward(dm: Dims, q, k, v, sel_idx, nsel_before, o_sm, lse, 
 
 
 def gdn_backward(dm: Dims, q, k, v, alpha, beta, route_bgc, d_o, S_init=None, dS_final=None, want_dS_init=True,
-                 stream=None, want_gate=False):
+                 stream=None, want_gate=False, overlap=False):
     """Gradient of the Gated DeltaNet branch through the rollback: returns fp32
     (dq, dk, dv, dalpha, dbeta, dS_init).  q, k, v, alpha, beta, route_bgc and
     S_init are the forward's inputs (gdn_chunk), d_o the fp32 upstream gradient
-    of o_gdn, dS_final that of the final carried state (None: zero)."""
+    of o_gdn, dS_final that of the final carried state (None: zero).  overlap:
+    pass the larger workspace of ENTRY_GDN_BACKWARD_OVERLAP, with which the
+    library runs its two sweeps at the same time (same results)."""
     io, qs, ts = _io_t(dm), (dm.B, dm.H, dm.L, dm.Dk), (dm.B, dm.H, dm.L)
     ss = (dm.B, dm.H, dm.Dk, dm.Dv)
     dq = torch.empty(qs, dtype=torch.float32, device=q.device)
@@ -444,7 +446,7 @@ def gdn_backward(dm: Dims, q, k, v, alpha, beta, route_bgc, d_o, S_init=None, dS
     db = torch.empty_like(da)
     dS0 = torch.empty(ss, dtype=torch.float32, device=q.device) if want_dS_init else None
     dg = torch.empty(dm.B, dm.H, dm.L // 64, dtype=torch.float32, device=q.device) if want_gate else None
-    ws_bytes = workspace_size(ENTRY_GDN_BACKWARD, dm)
+    ws_bytes = workspace_size(ENTRY_GDN_BACKWARD_OVERLAP if overlap else ENTRY_GDN_BACKWARD, dm)
     ws = workspace(ws_bytes, q.device)
     _check(lib().natsl_gdn_backward(
         C.byref(dm), _p(q, io, "q", qs), _p(k, io, "k", qs), _p(v, io, "v", qs),

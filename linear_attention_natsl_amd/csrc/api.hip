@@ -421,9 +421,11 @@ natsl_status natsl_workspace_size(int entry, const natsl_dims* dims, size_t* byt
       *bytes = handoff_ws_bytes(dims->B, dims->route_groups, nchunks(dims));
       return ok();
     case NATSL_ENTRY_GDN_BACKWARD:
+    case NATSL_ENTRY_GDN_BACKWARD_OVERLAP:
       CHECK(check_dims(dims, true, false));
       CHECK(check_gdn_len(dims));
-      *bytes = gdn_bwd_ws_bytes(dims->io == NATSL_BF16, dims->B, dims->H, dims->L, dims->Dk);
+      *bytes = gdn_bwd_ws_bytes(dims->io == NATSL_BF16, dims->B, dims->H, dims->L, dims->Dk,
+                                entry == NATSL_ENTRY_GDN_BACKWARD_OVERLAP);
       return ok();
     case NATSL_ENTRY_MERGE_BACKWARD:
       CHECK(check_dims(dims, true, false));
@@ -755,7 +757,17 @@ natsl_status natsl_gdn_backward(const natsl_dims* dims, const void* q, const voi
   NEED(dalpha, "dalpha");
   NEED(dbeta, "dbeta");
   CHECK(check_gdn_len(dims));
-  CHECK(check_ws(ws, ws_bytes, gdn_bwd_ws_bytes(dims->io == NATSL_BF16, dims->B, dims->H, dims->L, dims->Dk)));
+  const bool bf = dims->io == NATSL_BF16;
+  CHECK(check_ws(ws, ws_bytes, gdn_bwd_ws_bytes(bf, dims->B, dims->H, dims->L, dims->Dk, false)));
+  // a workspace of the overlap layout's size: the two sweeps on two streams
+  GdnBwdOverlap ov;
+  HelperPool<Helper>::Lease lease;
+  if (ws_bytes >= gdn_bwd_ws_bytes(bf, dims->B, dims->H, dims->L, dims->Dk, true)) {
+    CHECK(acquire_helper(&lease));
+    ov.aux = lease.ctx->aux;
+    ov.fork = lease.ctx->fork;
+    ov.join = lease.ctx->join;
+  }
   const int B = dims->B, H = dims->H, L = dims->L, G = dims->route_groups;
   hipError_t e;
   auto prof = prof_fn();
@@ -763,17 +775,17 @@ natsl_status natsl_gdn_backward(const natsl_dims* dims, const void* q, const voi
   if (dims->io == NATSL_BF16)
     e = dims->Dk == 64 ? launch_gdn_backward<bf16, 64>((const bf16*)q, (const bf16*)k, (const bf16*)v, alpha, beta,
                                                        route, S_init, d_o, dS_final, dq, dk, dv, dalpha, dbeta,
-                                                       dS_init, dgate, ws, B, H, L, G, stream)
+                                                       dS_init, dgate, ws, B, H, L, G, stream, ov)
                        : launch_gdn_backward<bf16, 128>((const bf16*)q, (const bf16*)k, (const bf16*)v, alpha, beta,
                                                         route, S_init, d_o, dS_final, dq, dk, dv, dalpha, dbeta,
-                                                        dS_init, dgate, ws, B, H, L, G, stream);
+                                                        dS_init, dgate, ws, B, H, L, G, stream, ov);
   else
     e = dims->Dk == 64 ? launch_gdn_backward<float, 64>((const float*)q, (const float*)k, (const float*)v, alpha,
                                                         beta, route, S_init, d_o, dS_final, dq, dk, dv, dalpha,
-                                                        dbeta, dS_init, dgate, ws, B, H, L, G, stream)
+                                                        dbeta, dS_init, dgate, ws, B, H, L, G, stream, ov)
                        : launch_gdn_backward<float, 128>((const float*)q, (const float*)k, (const float*)v, alpha,
                                                          beta, route, S_init, d_o, dS_final, dq, dk, dv, dalpha,
-                                                         dbeta, dS_init, dgate, ws, B, H, L, G, stream);
+                                                         dbeta, dS_init, dgate, ws, B, H, L, G, stream, ov);
   if (prof) prof(KID_GDN_BWD, stream, 1);
   if (e != hipSuccess) return dev_fail(e, "natsl_gdn_backward");
   return done(stream, "natsl_gdn_backward");

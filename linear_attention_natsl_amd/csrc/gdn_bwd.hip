@@ -61,16 +61,18 @@ static inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // workspace: [S0 of every chunk][U of every chunk][region], where the region
 // holds the forward prep's output (live during the state scan) or, after it,
-// the backward prep's output followed by Gc
+// the backward prep's output followed by Gc.  With `overlap` the two uses get
+// regions of their own, so that the state scan and the reverse scan (which
+// reads neither S0 nor U) can run at the same time on two streams.
 template <typename T, int D>
 struct BwdLayout {
   size_t s0, u, region, pt, wtn, gm, gst, total;
-  explicit BwdLayout(int64_t nch) {
+  BwdLayout(int64_t nch, bool overlap) {
     const size_t n = (size_t)nch;
     s0 = 0;
     u = al256(n * D * D * sizeof(T));
     region = u + al256(n * CHUNK * D * sizeof(T));
-    pt = region;
+    pt = overlap ? region + al256(carve_bytes<T, D>(nch)) : region;
     wtn = pt + al256(n * CHUNK * CHUNK * sizeof(T));
     gm = wtn + al256(n * CHUNK * D * sizeof(T));
     gst = gm + al256(n * GM_FLOATS * 4);
@@ -89,10 +91,11 @@ struct BwdLayout {
   }
 };
 
-size_t gdn_bwd_ws_bytes(int io_is_bf16, int B, int H, int L, int D) {
+size_t gdn_bwd_ws_bytes(int io_is_bf16, int B, int H, int L, int D, bool overlap) {
   const int64_t nch = (int64_t)B * H * (L / CHUNK);
-  if (io_is_bf16) return D == 64 ? BwdLayout<bf16, 64>(nch).total : BwdLayout<bf16, 128>(nch).total;
-  return D == 64 ? BwdLayout<float, 64>(nch).total : BwdLayout<float, 128>(nch).total;
+  if (io_is_bf16)
+    return D == 64 ? BwdLayout<bf16, 64>(nch, overlap).total : BwdLayout<bf16, 128>(nch, overlap).total;
+  return D == 64 ? BwdLayout<float, 64>(nch, overlap).total : BwdLayout<float, 128>(nch, overlap).total;
 }
 
 // ------------------------------------------------------------ backward prep
@@ -1043,23 +1046,48 @@ template <typename T, int D>
 hipError_t launch_gdn_backward(const T* q, const T* k, const T* v, const float* alpha, const float* beta,
                                const int32_t* route, const float* S_init, const float* d_o, const float* dS_final,
                                float* dq, float* dk, float* dv, float* dalpha, float* dbeta, float* dS_init,
-                               float* dgate, void* ws, int B, int H, int L, int G, hipStream_t st) {
+                               float* dgate, void* ws, int B, int H, int L, int G, hipStream_t st,
+                               const GdnBwdOverlap& ov) {
   const int nc = L / CHUNK;
   const int64_t nch = (int64_t)B * H * nc;
-  const BwdLayout<T, D> lay(nch);
+  const bool overlap = ov.aux != nullptr;
+  const BwdLayout<T, D> lay(nch, overlap);
   T* s0 = (T*)((char*)ws + lay.s0);
   T* u = (T*)((char*)ws + lay.u);
-  hipError_t e = launch_gdn_states<T, D>(q, k, v, alpha, beta, route, S_init, s0, u, (char*)ws + lay.region, B, H, L,
-                                         G, st);
-  if (e != hipSuccess) return e;
   GdnBwdWs<T, D> bw = lay.carve(ws);
   using PC = BwdPrepCfg<T, D>;
-  if ((e = set_lds_limit((const void*)k_gdn_bwd_prep<T, D>, PC::LDS)) != hipSuccess) return e;
-  hipLaunchKernelGGL((k_gdn_bwd_prep<T, D>), dim3((unsigned)nch), dim3(256), PC::LDS, st, q, k, alpha, beta, bw, L);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((k_gdn_bwd_scan<T, D, BWD_DVT>), dim3((unsigned)(B * H * (D / BWD_DVT))), dim3(256), 0, st, q,
-                     k, d_o, route, bw, dS_final, bw.gst, dS_init, H, L, G);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipError_t e = set_lds_limit((const void*)k_gdn_bwd_prep<T, D>, PC::LDS);
+  if (e != hipSuccess) return e;
+  // the backward prep and the reverse scan: on the helper stream beside the
+  // forward's state mode (own regions), else after it on st (shared region)
+  hipStream_t sb = overlap ? ov.aux : st;
+  if (overlap) {
+    if ((e = hipEventRecord(ov.fork, st)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(ov.aux, ov.fork, 0)) != hipSuccess) return e;
+  }
+  auto reverse = [&]() -> hipError_t {
+    hipLaunchKernelGGL((k_gdn_bwd_prep<T, D>), dim3((unsigned)nch), dim3(256), PC::LDS, sb, q, k, alpha, beta, bw,
+                       L);
+    hipError_t r = hipGetLastError();
+    if (r != hipSuccess) return r;
+    hipLaunchKernelGGL((k_gdn_bwd_scan<T, D, BWD_DVT>), dim3((unsigned)(B * H * (D / BWD_DVT))), dim3(256), 0, sb, q,
+                       k, d_o, route, bw, dS_final, bw.gst, dS_init, H, L, G);
+    return hipGetLastError();
+  };
+  if (overlap) e = reverse();
+  if (e == hipSuccess)
+    e = launch_gdn_states<T, D>(q, k, v, alpha, beta, route, S_init, s0, u, (char*)ws + lay.region, B, H, L, G, st);
+  if (e == hipSuccess && !overlap) e = reverse();
+  if (overlap) {  // joined also after a failed launch, so that nothing queued outlives the call's stream order
+    const hipError_t ej = hipEventRecord(ov.join, ov.aux);
+    if (ej == hipSuccess) {
+      const hipError_t ew = hipStreamWaitEvent(st, ov.join, 0);
+      if (e == hipSuccess) e = ew;
+    } else if (e == hipSuccess) {
+      e = ej;
+    }
+  }
+  if (e != hipSuccess) return e;
   using CC = BwdChunkCfg<T, D>;
   if ((e = set_lds_limit((const void*)k_gdn_bwd_chunk<T, D>, CC::LDS)) != hipSuccess) return e;
   hipLaunchKernelGGL((k_gdn_bwd_chunk<T, D>), dim3((unsigned)nch), dim3(256), CC::LDS, st, q, k, v, alpha, beta, d_o,
@@ -1071,7 +1099,7 @@ hipError_t launch_gdn_backward(const T* q, const T* k, const T* v, const float* 
   template hipError_t launch_gdn_backward<T, D>(const T*, const T*, const T*, const float*, const float*,           \
                                                 const int32_t*, const float*, const float*, const float*, float*,   \
                                                 float*, float*, float*, float*, float*, float*, void*, int, int,    \
-                                                int, int, hipStream_t);
+                                                int, int, hipStream_t, const GdnBwdOverlap&);
 INST(float, 64)
 INST(float, 128)
 INST(bf16, 64)

@@ -211,6 +211,22 @@ def test_workspace_sizes_monotone(L):
     assert N.workspace_size(N.ENTRY_SOFTMAX_MASKED, N.dims(1, 16, 4096, 128, 2048, N.BF16)) == 0
 
 
+def test_gdn_backward_overlap_workspace(L):
+    """natsl_gdn_backward's overlapping layout gives the forward prep's output
+    and the backward prep's output plus Gc regions of their own: on the long
+    prefill (B 1, H 16, L 32768, bf16 D 128) 0.877 GB shared, 1.352 GB apart
+    (each region 57920 bytes per chunk-head, S0 32768 and U 16384)."""
+    d = N.dims(1, 16, 32768, 128, 2048, N.BF16)
+    a = N.workspace_size(N.ENTRY_GDN_BACKWARD, d)
+    b = N.workspace_size(N.ENTRY_GDN_BACKWARD_OVERLAP, d)
+    nch = 16 * 512
+    assert abs(a - nch * (32768 + 16384 + 57920)) <= 4 * 256
+    assert abs(b - nch * (32768 + 16384 + 2 * 57920)) <= 8 * 256
+    for io, D in ((N.F32, 64), (N.F32, 128), (N.BF16, 64)):
+        d = N.dims(2, 4, 640, D, 256, io)
+        assert N.workspace_size(N.ENTRY_GDN_BACKWARD_OVERLAP, d) > N.workspace_size(N.ENTRY_GDN_BACKWARD, d)
+
+
 def test_last_error_is_thread_local(L):
     L.natsl_route(None, *([None] * 9))
     assert L.natsl_last_error() != b""
