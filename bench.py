@@ -517,6 +517,12 @@ def time_prefill_config(args, N, W, name, route_kind=None):
                                traffic=counters_traffic("softmax_masked", wl_key,
                                                         source_hash("softmax_masked.hip", "common.hpp")),
                                flops_per_launch=r["f_sm"], avg_launch_us=sm_us)
+        chain_us = k["gdn_prep"]["avg_us"] + k["gdn_scan"]["avg_us"]
+        out["critical_path"] = dict(
+            gdn_prep_plus_scan_us=round(chain_us, 1), softmax_us=sm_us, step_us=round(1e6 * step_s, 1),
+            note=f"the branches run on two streams and the merge follows both: the step is bounded by the longer of "
+                 f"the Gated DeltaNet chain (the prep, then {wl.nc} dependent scan steps per (b, h)) and the softmax "
+                 f"launch, each measured while sharing the GPU with the other")
     return out, inp, r["route"]
 
 
