@@ -178,8 +178,13 @@ __global__ void __launch_bounds__(256) k_decode_attn(const T* __restrict__ q, co
     for (int u = 0; u < DEC_UNROLL; ++u) {
       const int r = r0 + u * NGRP;
       const int rr = (r < hi) ? r : lo;  // in-bounds row; masked below
-      kf[u] = load8<T>(kb + (int64_t)rr * D);
-      vf[u] = load8<T>(vb + (int64_t)rr * D);
+      if constexpr (sizeof(T) == 2) {  // each cached row is read once per step: streaming (non-temporal) loads
+        kf[u].v = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(kb + (int64_t)rr * D)));
+        vf[u].v = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(vb + (int64_t)rr * D)));
+      } else {
+        kf[u] = load8<T>(kb + (int64_t)rr * D);
+        vf[u] = load8<T>(vb + (int64_t)rr * D);
+      }
     }
     float sc[DEC_UNROLL];
 #pragma unroll
