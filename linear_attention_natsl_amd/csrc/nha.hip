@@ -61,7 +61,7 @@ __global__ void __launch_bounds__(256) k_nha_chunk(const T* __restrict__ k, cons
 #pragma unroll
     for (int u = 0; u < NA; ++u) {
       const int x = tid + 256 * u;
-      if (x < CHUNK * M / 4) av[u] = *reinterpret_cast<const f32x4*>(gate + row0 * M + 4 * x);
+      if (x < CHUNK * M / 4) av[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(gate + row0 * M + 4 * x));
     }
     if (tid < VT) {
 #pragma unroll
@@ -142,13 +142,13 @@ __global__ void __launch_bounds__(256) k_nha_scan(NhaWs ws, int BH, int ne) {
   for (; e + 8 <= ne; e += 8) {
     float dl[8], g[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      dl[u] = S[(int64_t)(e + u) * PER];
+    for (int u = 0; u < 8; ++u) {  // each entry is read and rewritten once: non-temporal
+      dl[u] = __builtin_nontemporal_load(S + (int64_t)(e + u) * PER);
       g[u] = G[(int64_t)(e + u) * M];
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      S[(int64_t)(e + u) * PER] = state;
+      __builtin_nontemporal_store(state, S + (int64_t)(e + u) * PER);
       state = fmaf(g[u], state, dl[u]);
     }
   }
