@@ -109,7 +109,13 @@ __global__ void __launch_bounds__(1024, 2) k_route_wide(const T* __restrict__ x,
     for (int r = 0; r < rows; r += 8) {
       Frag<T> v[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = load8<T>(xc + (int64_t)min(r + u, rows - 1) * d);
+      for (int u = 0; u < 8; ++u) {  // x is read once, here: non-temporal loads (bf16)
+        const T* px = xc + (int64_t)min(r + u, rows - 1) * d;
+        if constexpr (sizeof(T) == 2)
+          v[u].v = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(px)));
+        else
+          v[u] = load8<T>(px);
+      }
 #pragma unroll
       for (int u = 0; u < 8; ++u)
         if (r + u < rows)
