@@ -255,6 +255,18 @@ __device__ __forceinline__ void gload_lds16_s(const void* gbase, uint32_t voff, 
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(base), "v"(voff), "s"(gs)
                : "memory", "m0");
 }
+// The same, non-temporal: for operands that one kernel reads once, so that
+// streaming them does not displace lines other kernels reuse.
+__device__ __forceinline__ void gload_lds16_s_nt(const void* gbase, uint32_t voff, const void* lds_wave_base) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_wave_base);
+  const uint64_t gp = (uint64_t)(uintptr_t)gbase;
+  const uint32_t ghi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(gp >> 32));
+  const uint32_t glo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)gp);
+  const uint64_t gs = ((uint64_t)ghi << 32) | (uint64_t)glo;
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt" ::"s"(base), "v"(voff), "s"(gs)
+               : "memory", "m0");
+}
 // s_waitcnt until at most N vector memory operations of this wave are
 // outstanding (they complete in issue order); expcnt / lgkmcnt not waited
 template <int N>

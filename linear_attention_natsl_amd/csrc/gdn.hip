@@ -699,8 +699,8 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW)
       for (int i = 0; i < 4 * NV; ++i) {
         const int j = NW * i + w;  // block: row tile j / (NV NW), local column tile j % (NV NW)
         const int rt = j / (NV * NW), tl = j % (NV * NW);
-        gload_lds16_s(ub + (rt * C::NT + NV * NW * part + tl) * 1024, (uint32_t)(lane * 16),
-                      (UT1 ? lds + SCH1_UT : sb + SCH_UT) + j * 1024);
+        gload_lds16_s_nt(ub + (rt * C::NT + NV * NW * part + tl) * 1024, (uint32_t)(lane * 16),
+                         (UT1 ? lds + SCH1_UT : sb + SCH_UT) + j * 1024);
       }
       return;
     }
@@ -725,10 +725,15 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW)
     const int nb = op == 2 ? NB / 2 : NB;  // P: 8 KiB
 #pragma unroll
     for (int i = 0; i < NB; ++i)
-      if (i < nb) gload_lds16_s(src + i * NW * 1024, off, sb + dst + (NW * i + w) * 1024);
+      if (i < nb) {  // the prep's operands (-W, P) are read once, here; q and k also by the softmax branch
+        if (op == 0 || op == 2)
+          gload_lds16_s_nt(src + i * NW * 1024, off, sb + dst + (NW * i + w) * 1024);
+        else
+          gload_lds16_s(src + i * NW * 1024, off, sb + dst + (NW * i + w) * 1024);
+      }
     if (op == 2 && lane < GMW && w * GMW + lane < 36)  // 576 bytes of decays, a share per wave
-      gload_lds16_s(reinterpret_cast<const unsigned char*>(ws.gm + ch * C::GM) + w * GMW * 16, (uint32_t)(lane * 16),
-                    sb + OFF_GM + w * GMW * 16);
+      gload_lds16_s_nt(reinterpret_cast<const unsigned char*>(ws.gm + ch * C::GM) + w * GMW * 16,
+                       (uint32_t)(lane * 16), sb + OFF_GM + w * GMW * 16);
   };
   // DMA operations a wave issues per part
   constexpr int N_W = NB, N_Q = NB, N_U = 4 * NV, N_P = NB / 2 + 1, N_KT = NB;
