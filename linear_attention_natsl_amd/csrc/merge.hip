@@ -246,11 +246,23 @@ __global__ void __launch_bounds__(256) k_merge_bwd_reduce(const float* __restric
   merge_group(g, D, per_head, nblk, H, base, hh, head_only, count);
   const int64_t chunk = (count + kMergeSplit - 1) / kMergeSplit;
   const int64_t n0 = sp * chunk, n1 = min(count, n0 + chunk);
-  float s = 0.f;
-  for (int64_t n = n0 + sb; n < n1; n += 4) {
+  auto slot_of = [&](int64_t n) {
     const int64_t x = head_only ? ((n / blk_per_head) * H + hh) * blk_per_head + n % blk_per_head : n;
-    s += part[x * 3 * D + base + el];
+    return part + x * 3 * D + base + el;
+  };
+  // 16 loads in flight per lane, added in block order (the same order as one
+  // load at a time: the sums do not depend on the unrolling)
+  constexpr int U = 16;
+  float s = 0.f;
+  int64_t n = n0 + sb;
+  for (; n + 4 * (U - 1) < n1; n += 4 * U) {
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = *slot_of(n + 4 * u);
+#pragma unroll
+    for (int u = 0; u < U; ++u) s += v[u];
   }
+  for (; n < n1; n += 4) s += *slot_of(n);
   red[sb][el] = s;
   __syncthreads();
   if (t < 64) part2[(int64_t)bid_x() * 64 + t] = (red[0][t] + red[1][t]) + (red[2][t] + red[3][t]);
