@@ -560,16 +560,20 @@ def test_gdn_backward_overlap_matches_sequential(io, D, per_head):
         assert torch.equal(a, c), name
 
 
-@pytest.mark.parametrize("io,branch,D,per_head,gains", [("f32", "f32", 64, False, False),
-                                                        ("bf16", "bf16", 128, True, True),
-                                                        ("bf16", "f32", 128, False, True)])
-def test_merge_backward_parity(io, branch, D, per_head, gains):
+@pytest.mark.parametrize("io,branch,D,per_head,gains,shape", [("f32", "f32", 64, False, False, (2, 3, 128)),
+                                                              ("bf16", "bf16", 128, True, True, (2, 3, 128)),
+                                                              ("bf16", "f32", 128, False, True, (2, 3, 128)),
+                                                              ("bf16", "bf16", 128, False, True, (1, 2, 70016)),
+                                                              ("bf16", "bf16", 128, True, False, (1, 2, 70016))])
+def test_merge_backward_parity(io, branch, D, per_head, gains, shape):
     """Gradient of the merge (both branch outputs, q through the mixing
     weights, W_mix shared or per head, the gains) against the oracle's exact
     derivative; each within 1e-4 of its largest magnitude (the kernel works in
     fp32 on the same inputs; W_mix and gain gradients are sums over every
-    token, added in a fixed order)."""
-    B, H, L = 2, 3, 128
+    token, added in a fixed order).  The 70016-token cases give the reduce of
+    the blocks' partials long, uneven ranges (8752 blocks over 64 ranges shared,
+    4376 per head), so that both its 16-load rounds and its tail run."""
+    B, H, L = shape
     say(f"[merge backward] io={io} branch={branch} D={D} per_head={per_head} gains={gains}")
     rng = np.random.default_rng(95)
     io_t = torch.bfloat16 if io == "bf16" else torch.float32
