@@ -21,15 +21,16 @@
  *     library never allocates, frees or synchronises device memory;
  *   - scratch memory is a caller-provided workspace whose size comes from
  *     natsl_workspace_size(); it must be 256-byte aligned;
- *   - every call is asynchronous on the caller's stream (natsl_forward forks
- *     work onto a library-owned helper stream of default priority and joins
- *     it back before returning, also when it fails after the fork; the join
- *     is an event wait, not a host synchronisation);
+ *   - every call is asynchronous on the caller's stream (natsl_forward,
+ *     natsl_nha_attention and natsl_gdn_backward with the overlap workspace
+ *     fork work onto a library-owned helper stream of default priority and
+ *     join it back before returning, also when they fail after the fork; the
+ *     join is an event wait, not a host synchronisation);
  *   - threads: every entry point may be called from several host threads at
  *     once, on the same or different streams.  The library keeps no mutable
  *     state between calls except (a) helper streams and their events, which
- *     natsl_forward takes from a per-device pool for the duration of its
- *     enqueue, so concurrent forwards never share them, (b) a record of the
+ *     those calls take from a per-device pool for the duration of their
+ *     enqueue, so concurrent calls never share them, (b) a record of the
  *     kernels whose LDS limit has been raised, guarded by a mutex, and (c)
  *     the natsl_profile_* timing records, guarded by a mutex (timing several
  *     threads at once mixes their records), (d) the scratch array of
@@ -520,6 +521,8 @@ natsl_status natsl_decode_handoff(const natsl_dims* dims, const int32_t* route, 
  *   out         [B, H, L, D] io dtype
  *   ws          natsl_nha_workspace_size bytes (the slots' states at every
  *               chunk start and the window's partial result, fp32)
+ * The window's softmax runs on the helper stream beside the slot-state
+ * kernels (it needs none of them) and is joined before the slots' read-out.
  * Errors: NATSL_ERR_UNSUPPORTED (slots, window or dims), NATSL_ERR_INVALID_ARG,
  * NATSL_ERR_WORKSPACE, before anything is enqueued; NATSL_ERR_DEVICE.
  */

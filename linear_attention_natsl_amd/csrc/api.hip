@@ -760,7 +760,7 @@ natsl_status natsl_gdn_backward(const natsl_dims* dims, const void* q, const voi
   const bool bf = dims->io == NATSL_BF16;
   CHECK(check_ws(ws, ws_bytes, gdn_bwd_ws_bytes(bf, dims->B, dims->H, dims->L, dims->Dk, false)));
   // a workspace of the overlap layout's size: the two sweeps on two streams
-  GdnBwdOverlap ov;
+  SideStream ov;
   HelperPool<Helper>::Lease lease;
   if (ws_bytes >= gdn_bwd_ws_bytes(bf, dims->B, dims->H, dims->L, dims->Dk, true)) {
     CHECK(acquire_helper(&lease));
@@ -930,6 +930,12 @@ natsl_status natsl_nha_attention(const natsl_dims* dims, const void* q, const vo
   NEED(slot_gate, "slot_gate");
   NEED(out, "out");
   CHECK(check_ws(ws, ws_bytes, need));
+  HelperPool<Helper>::Lease lease;
+  CHECK(acquire_helper(&lease));
+  SideStream side;
+  side.aux = lease.ctx->aux;
+  side.fork = lease.ctx->fork;
+  side.join = lease.ctx->join;
   const float sc = eff_scale(dims);
   const int B = dims->B, H = dims->H, L = dims->L;
   hipError_t e;
@@ -937,14 +943,14 @@ natsl_status natsl_nha_attention(const natsl_dims* dims, const void* q, const vo
   if (prof) prof(KID_NHA, stream, 0);
   if (dims->io == NATSL_BF16)
     e = dims->Dk == 64 ? launch_nha<bf16, bf16, 64>((const bf16*)q, (const bf16*)k, (const bf16*)v, slot_gate, slots,
-                                                    (bf16*)out, ws, B, H, L, window, sc, stream, prof)
+                                                    (bf16*)out, ws, B, H, L, window, sc, stream, prof, side)
                        : launch_nha<bf16, bf16, 128>((const bf16*)q, (const bf16*)k, (const bf16*)v, slot_gate,
-                                                     slots, (bf16*)out, ws, B, H, L, window, sc, stream, prof);
+                                                     slots, (bf16*)out, ws, B, H, L, window, sc, stream, prof, side);
   else
     e = dims->Dk == 64 ? launch_nha<float, float, 64>((const float*)q, (const float*)k, (const float*)v, slot_gate,
-                                                      slots, (float*)out, ws, B, H, L, window, sc, stream, prof)
+                                                      slots, (float*)out, ws, B, H, L, window, sc, stream, prof, side)
                        : launch_nha<float, float, 128>((const float*)q, (const float*)k, (const float*)v, slot_gate,
-                                                       slots, (float*)out, ws, B, H, L, window, sc, stream, prof);
+                                                       slots, (float*)out, ws, B, H, L, window, sc, stream, prof, side);
   if (prof) prof(KID_NHA, stream, 1);
   if (e != hipSuccess) return dev_fail(e, "natsl_nha_attention");
   return done(stream, "natsl_nha_attention");

@@ -1047,7 +1047,7 @@ hipError_t launch_gdn_backward(const T* q, const T* k, const T* v, const float* 
                                const int32_t* route, const float* S_init, const float* d_o, const float* dS_final,
                                float* dq, float* dk, float* dv, float* dalpha, float* dbeta, float* dS_init,
                                float* dgate, void* ws, int B, int H, int L, int G, hipStream_t st,
-                               const GdnBwdOverlap& ov) {
+                               const SideStream& ov) {
   const int nc = L / CHUNK;
   const int64_t nch = (int64_t)B * H * nc;
   const bool overlap = ov.aux != nullptr;
@@ -1099,7 +1099,7 @@ hipError_t launch_gdn_backward(const T* q, const T* k, const T* v, const float* 
   template hipError_t launch_gdn_backward<T, D>(const T*, const T*, const T*, const float*, const float*,           \
                                                 const int32_t*, const float*, const float*, const float*, float*,   \
                                                 float*, float*, float*, float*, float*, float*, void*, int, int,    \
-                                                int, int, hipStream_t, const GdnBwdOverlap&);
+                                                int, int, hipStream_t, const SideStream&);
 INST(float, 64)
 INST(float, 128)
 INST(bf16, 64)

@@ -6,6 +6,16 @@
 
 namespace natsl {
 
+// a helper stream and two events (all set or none): work that does not need
+// the caller's stream's other launches runs on it, forked from and joined back
+// into the caller's stream (the GDN gradient: the state scan beside the
+// reverse scan, the workspace laid out for it; Native Hybrid Attention: the
+// window's softmax beside the slot states)
+struct SideStream {
+  hipStream_t aux = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+
 typedef __bf16 bf16;
 
 // kernel ids for the optional launch timing
@@ -118,19 +128,14 @@ struct NhaWs {
 size_t nha_ws_bytes(int B, int H, int L, int D, int M, int window);
 template <typename T, typename To, int D>
 hipError_t launch_nha(const T* q, const T* k, const T* v, const float* gate, int M, To* out, void* ws, int B, int H,
-                      int L, int window, float scale, hipStream_t st, void (*prof)(int, hipStream_t, int));
+                      int L, int window, float scale, hipStream_t st, void (*prof)(int, hipStream_t, int),
+                      const SideStream& side = SideStream());
 
 size_t gdn_ws_bytes(int io_is_bf16, int D, int64_t nch);
 // Gated DeltaNet branch gradient (chunk form): ws holds every chunk's start
 // state S0 and U, then the chunk preps' region(s) and every chunk's carried
 // gradient; `overlap` lays out separate regions for the two sweeps
 size_t gdn_bwd_ws_bytes(int io_is_bf16, int B, int H, int L, int D, bool overlap);
-// a helper stream and two events (both or neither): the state scan and the
-// reverse scan then run at the same time, the workspace laid out for overlap
-struct GdnBwdOverlap {
-  hipStream_t aux = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-};
 // the forward in state mode: every chunk's start state s0 [B, H, Nc, D, D]
 // and U [B, H, L, D] (io dtype), no outputs; ws as launch_gdn's
 template <typename T, int D>
@@ -142,7 +147,7 @@ hipError_t launch_gdn_backward(const T* q, const T* k, const T* v, const float* 
                                const int32_t* route, const float* S_init, const float* d_o, const float* dS_final,
                                float* dq, float* dk, float* dv, float* dalpha, float* dbeta, float* dS_init,
                                float* dgate, void* ws, int B, int H, int L, int G, hipStream_t st,
-                               const GdnBwdOverlap& ov = GdnBwdOverlap());
+                               const SideStream& ov = SideStream());
 template <typename T, typename To, int D>
 hipError_t launch_gdn(const T* q, const T* k, const T* v, const float* alpha, const float* beta,
                       const int32_t* route, const float* S_init, To* o_gdn, float* S_final, void* ws,

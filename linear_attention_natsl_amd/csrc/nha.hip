@@ -555,7 +555,8 @@ size_t nha_ws_bytes(int B, int H, int L, int D, int M, int window) {
 
 template <typename T, typename To, int D>
 hipError_t launch_nha_m(const T* q, const T* k, const T* v, const float* gate, int M, To* out, void* wsp, int B,
-                        int H, int L, int window, float scale, hipStream_t st, void (*prof)(int, hipStream_t, int)) {
+                        int H, int L, int window, float scale, hipStream_t st, void (*prof)(int, hipStream_t, int),
+                        const SideStream& side) {
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   const int nc = L / CHUNK, nw = window / CHUNK;
   const int ne = nc > nw ? nc - nw : 0;
@@ -574,29 +575,44 @@ hipError_t launch_nha_m(const T* q, const T* k, const T* v, const float* gate, i
   ws.G = (float*)p; p += al((size_t)BH * ne * M * 4);
   float* o_w = (float*)p; p += al((size_t)BH * L * D * 4);
   float* lse_w = (float*)p;
+  // the window's softmax needs none of the slot states: with a side stream
+  // it runs there beside the chunk and scan kernels, joined before the slots
+  const bool fork = side.aux != nullptr && nw > 0;
+  const hipStream_t sw = fork ? side.aux : st;
+  if (fork) {
+    if ((e = hipEventRecord(side.fork, st)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(side.aux, side.fork, 0)) != hipSuccess) return e;
+  }
+  auto join = [&](hipError_t err) {  // also after a failed launch: nothing queued outlives the call's order
+    if (!fork) return err;
+    const hipError_t ej = hipEventRecord(side.join, side.aux);
+    const hipError_t ew = ej == hipSuccess ? hipStreamWaitEvent(st, side.join, 0) : ej;
+    return err != hipSuccess ? err : ew;
+  };
   if (nw > 0) {
-    if (prof) prof(KID_NHA_WINDOW, st, 0);
-    e = launch_softmax_window<T, float, D>(q, k, v, o_w, lse_w, B, H, L, nw, scale, st);
-    if (e != hipSuccess) return e;
-    if (prof) prof(KID_NHA_WINDOW, st, 1);
+    if (prof) prof(KID_NHA_WINDOW, sw, 0);
+    e = launch_softmax_window<T, float, D>(q, k, v, o_w, lse_w, B, H, L, nw, scale, sw);
+    if (e != hipSuccess) return join(e);
+    if (prof) prof(KID_NHA_WINDOW, sw, 1);
   }
   const float* ow = nw > 0 ? o_w : nullptr;
   const float* lw = nw > 0 ? lse_w : nullptr;
 #define NHA_M(MM)                                                                                                  \
   do {                                                                                                             \
     const size_t lds = NhaSlotCfg<T, D, MM>::LDS;                                                                  \
-    if ((e = set_lds_limit((const void*)k_nha_slots<T, To, D, MM>, (int)lds)) != hipSuccess) return e;            \
+    if ((e = set_lds_limit((const void*)k_nha_slots<T, To, D, MM>, (int)lds)) != hipSuccess) return join(e);      \
     if (prof) prof(KID_NHA_CHUNK, st, 0);                                                                          \
     hipLaunchKernelGGL((k_nha_chunk<T, D, MM>), dim3((unsigned)(BH * ne)), dim3(256), 0, st, k, v, gate, ws, L,     \
                        ne);                                                                                        \
-    if ((e = hipGetLastError()) != hipSuccess) return e;                                                          \
+    if ((e = hipGetLastError()) != hipSuccess) return join(e);                                                    \
     if (prof) prof(KID_NHA_CHUNK, st, 1);                                                                          \
     const int64_t nthr = BH * 2 * MM * D;                                                                          \
     if (prof) prof(KID_NHA_SCAN, st, 0);                                                                           \
     hipLaunchKernelGGL((k_nha_scan<D, MM>), dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0, st, ws, (int)BH,   \
                        ne);                                                                                        \
-    if ((e = hipGetLastError()) != hipSuccess) return e;                                                          \
+    if ((e = hipGetLastError()) != hipSuccess) return join(e);                                                    \
     if (prof) prof(KID_NHA_SCAN, st, 1);                                                                           \
+    if ((e = join(hipSuccess)) != hipSuccess) return e;                                                            \
     if (prof) prof(KID_NHA_SLOTS, st, 0);                                                                          \
     hipLaunchKernelGGL((k_nha_slots<T, To, D, MM>), dim3((unsigned)(BH * nc)), dim3(256), lds, st, q, k, v, gate,  \
                        ws, ow, lw, out, L, nw, ne, scale);                                                         \
@@ -608,18 +624,20 @@ hipError_t launch_nha_m(const T* q, const T* k, const T* v, const float* gate, i
   if (M == 32) NHA_M(32);
   if (M == 64) NHA_M(64);
 #undef NHA_M
-  return hipErrorInvalidValue;
+  return join(hipErrorInvalidValue);
 }
 
 template <typename T, typename To, int D>
 hipError_t launch_nha(const T* q, const T* k, const T* v, const float* gate, int M, To* out, void* ws, int B, int H,
-                      int L, int window, float scale, hipStream_t st, void (*prof)(int, hipStream_t, int)) {
-  return launch_nha_m<T, To, D>(q, k, v, gate, M, out, ws, B, H, L, window, scale, st, prof);
+                      int L, int window, float scale, hipStream_t st, void (*prof)(int, hipStream_t, int),
+                      const SideStream& side) {
+  return launch_nha_m<T, To, D>(q, k, v, gate, M, out, ws, B, H, L, window, scale, st, prof, side);
 }
 
 #define INST(T, To, D)                                                                                          \
   template hipError_t launch_nha<T, To, D>(const T*, const T*, const T*, const float*, int, To*, void*, int, int, \
-                                           int, int, float, hipStream_t, void (*)(int, hipStream_t, int));
+                                           int, int, float, hipStream_t, void (*)(int, hipStream_t, int), \
+                                           const SideStream&);
 INST(float, float, 64)
 INST(float, float, 128)
 INST(bf16, bf16, 64)
