@@ -568,6 +568,9 @@ def time_nha(args, N, W, reps=10):
     rl = dict(bound=bound, kernel=dom, achieved=round(ach, 1), peak=peak, unit=unit, frac=round(ach / peak, 4),
               traffic=None, avg_launch_us=us)
     rl["flops_per_launch" if unit == "TFLOP/s" else "bytes_per_launch"] = amount
+    if dom == "nha_window":
+        rl["note"] = ("the window's softmax runs on the library's helper stream beside nha_chunk and nha_scan, so "
+                      "its launch shares the GPU with them for part of its duration")
     return dict(workload=f"Native Hybrid Attention: B={B} H={H} L={L} D={D}, {m} slots, window {w} tokens, bf16",
                 value=round(B * L / (med * 1e-3), 1), unit="tokens/s", ms_per_call_median=med,
                 step_stats=dict(flushed=stats, back_to_back=warm),
