@@ -80,6 +80,57 @@ def test_concurrent_forwards_two_threads_two_streams():
     assert not errors, errors
 
 
+def test_concurrent_nha_two_threads_two_streams():
+    """Two host threads call natsl_nha_attention at the same time, each on its
+    own stream with its own inputs and workspace, 8 times each; every output is
+    bit-identical to the same call run alone.  Each call forks its window's
+    softmax onto a helper stream that it takes from the per-device pool for
+    the call, so neither call can wait on the other's events."""
+    B, H, L, D, m, win = 1, 4, 4096, 128, 16, 1024
+    runs = []
+    for seed in (83, 84):
+        inp = W.make_nha(B, H, L, D, m, io="bf16", seed=seed)
+        bf = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda().to(torch.bfloat16)
+        q, k, v = bf(inp["q"]), bf(inp["k"]), bf(inp["v"])
+        gate = torch.from_numpy(np.ascontiguousarray(inp["gate"])).cuda()
+        dm = N.dims(B, H, L, D, 64, N.BF16)
+        ws = N.workspace(N.nha_workspace_size(dm, m, win), q.device)
+        runs.append((dm, q, k, v, gate, ws))
+    say("[boundary] concurrent NHA calls: serial references")
+    refs = []
+    for dm, q, k, v, gate, ws in runs:
+        refs.append(N.nha_attention(dm, q, k, v, gate, win, ws=ws).clone())
+        torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    errors = []
+    barrier = threading.Barrier(2)
+
+    def worker(i):
+        try:
+            dm, q, k, v, gate, ws = runs[i]
+            s = streams[i]
+            barrier.wait()
+            with torch.cuda.stream(s):
+                for it in range(8):
+                    o = N.nha_attention(dm, q, k, v, gate, win, ws=ws, stream=s)
+                    if it % 4 == 3:
+                        s.synchronize()
+                        if not torch.equal(o, refs[i]):
+                            errors.append(f"thread {i} iteration {it}: differs from the serial run")
+        except Exception as e:  # pragma: no cover - reported below
+            errors.append(f"thread {i}: {e!r}")
+
+    say("[boundary] concurrent NHA calls: two threads")
+    th = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for x in th:
+        x.start()
+    for x in th:
+        x.join(timeout=120)
+    assert not any(x.is_alive() for x in th), "a worker thread did not finish"
+    torch.cuda.synchronize()
+    assert not errors, errors
+
+
 def test_forward_128k_tokens_sampled():
     """A 131072-token bf16 D = 128 prefill (2048 chunks: a softmax tile list
     of up to 2048 entries, 2048 route bytes in the scan's LDS), 25% softmax
