@@ -532,7 +532,8 @@ def test_gdn_backward_parity(io, D, L, per_head, alpha):
     assert all(e <= tol for e in errs.values()), errs
 
 
-@pytest.mark.parametrize("io,D,per_head", [("bf16", 128, False), ("bf16", 128, True), ("f32", 64, False)])
+@pytest.mark.parametrize("io,D,per_head", [("bf16", 128, False), ("bf16", 128, True), ("f32", 64, False),
+                                            ("f32", 128, True), ("bf16", 64, False)])
 def test_gdn_backward_overlap_matches_sequential(io, D, per_head):
     """With the overlapping workspace natsl_gdn_backward runs the state scan
     and the reverse scan at the same time on two streams; every output (and
