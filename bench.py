@@ -464,6 +464,12 @@ def time_prefill(args, N, W):
                    layer_frac_of_mfma_peak=round((f_sm + f_gdn) / step_s / 1e12 / PEAK_BF16_TFLOPS, 4),
                    step_stats=dict(flushed=r["per_step"], back_to_back=r["warm_steps"]),
                    kernels=r["kernels"], route_alone=route_alone),
+        critical_path=dict(
+            gdn_prep_plus_scan_us=round(r["kernels"]["gdn_prep"]["avg_us"] + r["kernels"]["gdn_scan"]["avg_us"], 1),
+            softmax_us=sm_us, step_us=round(1e6 * step_s, 1),
+            note=f"the branches run on two streams and the merge follows both: the step is bounded by the longer of "
+                 f"the Gated DeltaNet chain (the prep, then {wl.nc} dependent scan steps per (b, h)) and the softmax "
+                 f"launch, each measured while sharing the GPU with the other"),
         **extras,
     )
     return res, inp, route
