@@ -334,3 +334,23 @@ def test_sync_check_level(L):
                            timeout=300)
         assert r.returncode == 0, r.stderr[-2000:]
         assert r.stdout.strip().splitlines()[-1] == str(want), (env_val, r.stdout)
+
+
+def test_missing_library_fails_loudly():
+    """Without the built library the binding raises (no CPU fallback exists):
+    run in a fresh interpreter whose loader points at a file that is not there."""
+    import subprocess
+    import sys
+    code = ("import linear_attention_natsl_amd as N\n"
+            "N._lib = None\n"
+            "N.LIB_PATH = N.LIB_PATH + '.not_built'\n"
+            "try:\n"
+            "    N.lib()\n"
+            "except RuntimeError as e:\n"
+            "    print('raised:', e)\n"
+            "else:\n"
+            "    print('loaded')\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300, cwd=root)
+    assert r.returncode == 0, r.stderr
+    assert "raised:" in r.stdout and "no fallback" in r.stdout
